@@ -1,0 +1,184 @@
+"""Plain fp64 CPU oracle for the MiniMax-H3 attention step.
+
+TEST INFRASTRUCTURE. Only the tests, the smoke check and the CPU-baseline leg
+of the benchmark may import this package. The HIP library never calls it, and
+it shares no code, table or constant generator with the HIP library: it
+computes its own rotary angles, its own normalisation and its own softmax from
+the definitions, in float64, with NumPy.
+
+What it computes, in the order the pages give (norm, then rotary, then
+attention):
+
+* Q/K RMSNorm per head over the 128 head channels (FastVideo PR #1832,
+  "Summary" and "Preserve H3-specific attention behavior"; TeleFuser PR #37,
+  "2.2 Fuse Q/K RMSNorm, RoPE, and Ulysses Pack", steps 1 and 3).
+* Partial rotary embedding on 96 of the 128 channels, rotate-half pairs
+  (j, j+48) (FastVideo PR #1832, "Preserve H3-specific attention behavior").
+* Dense non-causal softmax attention over BSHD tensors at head_dim 128
+  (FastVideo PR #1832, "Summary"), with keys past a valid length excluded
+  (FastVideo PR #1799, "Implementation": padding masks) and query rows past a
+  valid length set to zero (TeleFuser PR #37, "2.3 Add fixed-valid and
+  valid-only attention modes" and "2.4 Fuse valid-only gather with zero-tail
+  merge").
+
+Readings where the pages are silent (each pinned by a test in tests/):
+per-head norm with one [128] weight shared by all heads, eps inside the square
+root, weight multiplied as given; rotary frequency theta^(-2j/96) over the 96
+rotated channels; 1-D positions 0..S-1; no rounding between steps.
+
+Every function here is pinned by `tests/test_oracle_pins.py` against brute
+force on tiny inputs, closed forms, invariants and torch's CPU float64 SDPA.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+HEAD_DIM = 128
+ROT_DIM = 96            # channels 0..95 are rotated, 96..127 pass through
+HALF = ROT_DIM // 2     # 48 rotate-half pairs (j, j + 48)
+
+
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    """Exact value of bfloat16 bit patterns, as float64 (bf16 is the upper
+    half of an IEEE float32)."""
+    b = np.asarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def rms_norm(x: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
+    """RMSNorm over the last axis (the 128 channels of one head):
+    y_c = x_c / sqrt(mean_c(x_c^2) + eps) * w_c.
+
+    Per-head extent and eps inside the root are readings of "Q/K RMSNorm"
+    (FastVideo PR #1832, "Summary"); the pages print no formula."""
+    x = np.asarray(x, dtype=np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + float(eps)) * np.asarray(w, dtype=np.float64)
+
+
+def rope_inv_freq(theta: float, rot_dim: int = ROT_DIM) -> np.ndarray:
+    """Rotary frequencies theta^(-2j/rot_dim) for pairs j = 0 .. rot_dim/2-1."""
+    j = np.arange(rot_dim // 2, dtype=np.float64)
+    return float(theta) ** (-2.0 * j / rot_dim)
+
+
+def rope_angles(positions, theta: float, rot_dim: int = ROT_DIM) -> np.ndarray:
+    """phi[p, j] = position_p * theta^(-2j/rot_dim), shape [len(positions), rot_dim/2]."""
+    pos = np.asarray(positions, dtype=np.float64)
+    return np.multiply.outer(pos, rope_inv_freq(theta, rot_dim))
+
+
+def apply_rope(y: np.ndarray, positions, theta: float, rot_dim: int = ROT_DIM) -> np.ndarray:
+    """Partial rotary embedding on a [B, S, H, 128] tensor (FastVideo PR #1832,
+    "Preserve H3-specific attention behavior": 96 of 128 channels rotated).
+
+    Pair (a, b) = (y_j, y_{j+48}) at position p rotates by phi = p*theta^(-j/48):
+    y'_j = a cos(phi) - b sin(phi), y'_{j+48} = b cos(phi) + a sin(phi).
+    Channels rot_dim..127 are unchanged."""
+    y = np.asarray(y, dtype=np.float64)
+    half = rot_dim // 2
+    phi = rope_angles(positions, theta, rot_dim)            # [S, half]
+    c = np.cos(phi)[None, :, None, :]                       # broadcast over B and H
+    s = np.sin(phi)[None, :, None, :]
+    a = y[..., :half]
+    b = y[..., half:rot_dim]
+    out = y.copy()
+    out[..., :half] = a * c - b * s
+    out[..., half:rot_dim] = b * c + a * s
+    return out
+
+
+def qk_prologue(q_bits, k_bits, w_q, w_k, eps: float, theta: float | None,
+                norm: bool = True):
+    """The Q/K prologue of the attention step: RMSNorm, then rotary at
+    positions 0..S-1 when `theta` is given. Inputs are bf16 bit patterns
+    [B, S, H, 128]; outputs are exact float64 (no rounding)."""
+    q = bf16_bits_to_f64(q_bits)
+    k = bf16_bits_to_f64(k_bits)
+    if norm:
+        q = rms_norm(q, w_q, eps)
+        k = rms_norm(k, w_k, eps)
+    if theta is not None:
+        q = apply_rope(q, np.arange(q.shape[1]), theta)
+        k = apply_rope(k, np.arange(k.shape[1]), theta)
+    return q, k
+
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
+              q_valid: int | None = None, kv_valid: int | None = None,
+              rows=None, block: int = 256) -> np.ndarray:
+    """Dense non-causal softmax attention on BSHD float64 tensors.
+
+    o_i = sum_{j < kv_valid} softmax_j(scale * q_i . k_j) v_j for i < q_valid,
+    o_i = 0 for i >= q_valid. With `rows`, only those query rows are computed
+    and the result has shape [B, len(rows), H, D]. Query rows are processed
+    `block` at a time so no Sq x Sk score matrix is held."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Sq, H, D = q.shape
+    Sk = k.shape[1]
+    q_valid = Sq if q_valid is None else int(q_valid)
+    kv_valid = Sk if kv_valid is None else int(kv_valid)
+    if kv_valid < 1:
+        raise ValueError("attention needs at least one valid key")
+    row_idx = np.arange(Sq) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.zeros((B, len(row_idx), H, D), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            kh = np.ascontiguousarray(k[b, :kv_valid, h, :])
+            vh = np.ascontiguousarray(v[b, :kv_valid, h, :])
+            for start in range(0, len(row_idx), block):
+                sel = row_idx[start:start + block]
+                live = sel < q_valid
+                if not live.any():
+                    continue
+                qh = q[b, sel[live], h, :]
+                s = (qh @ kh.T) * scale
+                m = s.max(axis=1, keepdims=True)
+                p = np.exp(s - m)
+                o = (p @ vh) / p.sum(axis=1, keepdims=True)
+                dst = np.arange(start, start + len(sel))[live]
+                out[b, dst, h, :] = o
+    return out
+
+
+def forward(q_bits, k_bits, v_bits, w_q, w_k, eps: float, theta: float | None,
+            scale: float, q_valid: int | None = None, kv_valid: int | None = None,
+            norm: bool = True, rows=None) -> np.ndarray:
+    """The whole attention step: prologue on q and k, then attention with v."""
+    qn, kn = qk_prologue(q_bits, k_bits, w_q, w_k, eps, theta, norm=norm)
+    if rows is not None:
+        # Only the sampled query rows are needed; keep their prologue outputs.
+        qn = qn[:, np.asarray(rows, dtype=np.int64)]
+        rows_local = np.arange(qn.shape[1])
+        o = attention(qn, kn, bf16_bits_to_f64(v_bits), scale, None, kv_valid,
+                      rows=rows_local)
+        if q_valid is not None:
+            o[:, np.asarray(rows) >= q_valid] = 0.0
+        return o
+    return attention(qn, kn, bf16_bits_to_f64(v_bits), scale, q_valid, kv_valid)
+
+
+def compare(got_bits_or_f64, ref: np.ndarray) -> dict:
+    """Error metrics of a bf16 (bit patterns) or float result against the
+    fp64 reference: max-abs, relative RMS ||d||_2 / ||ref||_2, and the
+    largest distance in bf16 units in the last place."""
+    got = np.asarray(got_bits_or_f64)
+    if got.dtype == np.uint16:
+        got = bf16_bits_to_f64(got)
+    got = got.astype(np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    d = got - ref
+    nref = float(np.sqrt(np.sum(ref * ref)))
+    rel_rms = float(np.sqrt(np.sum(d * d)) / nref) if nref > 0 else float(np.sqrt(np.sum(d * d)))
+    # bf16 ulp of the reference value: 2^(floor(log2|x|) - 7), smallest normal spacing for 0.
+    a = np.abs(ref)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    ulp = np.where(a > 0, np.exp2(np.maximum(e, -126.0) - 7.0), np.exp2(-133.0))
+    return {
+        "max_abs": float(np.max(np.abs(d))) if d.size else 0.0,
+        "rel_rms": rel_rms,
+        "max_ulp": float(np.max(np.abs(d) / ulp)) if d.size else 0.0,
+        "nonfinite": int(np.size(got) - np.count_nonzero(np.isfinite(got))),
+    }

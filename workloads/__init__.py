@@ -1,0 +1,143 @@
+"""Seeded synthetic workloads for the MiniMax-H3 attention step.
+
+This module only draws random numbers and stores them in the formats the
+library consumes (bf16 bit patterns, fp32 weights). It holds none of the
+method's arithmetic: no normalisation, no rotary angles, no attention. The
+fp64 oracle and the HIP library both receive the arrays it returns, and
+neither imports the other.
+
+The five workloads are the shapes on which the pages run the H3 attention
+step: a tiny smoke case, an 8x32x32 latent grid, a valid-front/padded-tail
+packed sequence (TeleFuser PR #37, "2.3 Add fixed-valid and valid-only
+attention modes"), video-to-text cross-attention (FastVideo PR #1799,
+"Implementation": dense self- and cross-attention) and one GPU's 6-head
+share of the ~104k-row 345-frame packed sequence under Ulysses-8 (SGLang
+PR #37903, "Motivation" table).
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+HEAD_DIM = 128
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    Sq: int
+    Sk: int
+    H: int
+    q_valid: int          # query rows >= q_valid produce zero output
+    kv_valid: int         # keys >= kv_valid are masked out
+    norm: bool            # Q/K RMSNorm on
+    rope: bool            # 96/128 partial rotary embedding on
+    seed: int
+    eps: float = 1e-6
+    theta: float = 1e4
+    description: str = ""
+
+    @property
+    def D(self) -> int:
+        return HEAD_DIM
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(HEAD_DIM))
+
+    def attention_flops(self) -> float:
+        """4 * Sq_valid * Sk_valid * d * H * B: QK^T and PV, 2 flop per MAC."""
+        return 4.0 * self.q_valid * self.kv_valid * HEAD_DIM * self.H * self.B
+
+    def nominal_flops(self) -> float:
+        return 4.0 * self.Sq * self.Sk * HEAD_DIM * self.H * self.B
+
+    def prologue_bytes(self) -> int:
+        """Compulsory HBM bytes of the stand-alone Q/K prologue: read and write
+        q and k in bf16, read the fp32 cos/sin tables (48 pairs per row) when
+        rotary is on, and the two fp32 weight vectors."""
+        qk = 2 * 2 * self.B * (self.Sq + self.Sk) * self.H * HEAD_DIM
+        tables = 2 * 4 * 48 * max(self.Sq, self.Sk) if self.rope else 0
+        return qk + tables + 2 * 4 * HEAD_DIM
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", 1, 512, 512, 2, 512, 512, True, True, 0,
+                     description="B=1 S=512 H=2 d=128, prologue on, no mask"),
+    "mid": Workload("mid", 1, 8192, 8192, 8, 8192, 8192, True, True, 1,
+                    description="B=1 S=8192 (8x32x32 latent grid) H=8, prologue on, no mask"),
+    "padded": Workload("padded", 1, 32768, 32768, 8, 30720, 30720, True, True, 2,
+                       description="B=1 S=32768, first 30720 rows valid, tail masked and zeroed, H=8"),
+    "cross": Workload("cross", 1, 32760, 512, 8, 32760, 300, True, False, 3,
+                      description="B=1 Sq=32760 video queries, Sk=512 text keys (300 valid), H=8, "
+                                  "Q/K RMSNorm, no rotary"),
+    "full": Workload("full", 1, 104448, 104448, 6, 104448, 104448, True, True, 4,
+                     description="B=1 S=104448 packed rows (345 frames at 1344x768), H=6, "
+                                 "prologue on, no mask"),
+}
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (round to nearest, ties to even) and
+    return the 16-bit patterns. NaN inputs map to a quiet NaN."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    rounding_bias = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    out = ((u + rounding_bias) >> np.uint32(16)).astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        out[nan] = np.uint16(0x7FC0)
+    return out
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+@dataclasses.dataclass
+class Inputs:
+    q: np.ndarray        # uint16 bf16 bits [B, Sq, H, 128]
+    k: np.ndarray        # uint16 bf16 bits [B, Sk, H, 128]
+    v: np.ndarray        # uint16 bf16 bits [B, Sk, H, 128]
+    w_q: np.ndarray      # float32 [128], bf16-representable
+    w_k: np.ndarray      # float32 [128], bf16-representable
+
+
+def _normal_bf16(rng: np.random.Generator, shape) -> np.ndarray:
+    return f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
+
+
+def make_inputs(B: int, Sq: int, Sk: int, H: int, seed: int,
+                weight_sigma: float = 0.1) -> Inputs:
+    """Draw q, k, v ~ N(0,1) (float32, then RNE to bf16) and RMSNorm weights
+    1 + weight_sigma*N(0,1) (float64, rounded to bf16-representable values and
+    stored as float32), in that order, from numpy's PCG64 with `seed`."""
+    rng = np.random.default_rng(seed)
+    q = _normal_bf16(rng, (B, Sq, H, HEAD_DIM))
+    k = _normal_bf16(rng, (B, Sk, H, HEAD_DIM))
+    v = _normal_bf16(rng, (B, Sk, H, HEAD_DIM))
+    w = []
+    for _ in range(2):
+        w64 = 1.0 + weight_sigma * rng.standard_normal(HEAD_DIM)
+        w.append(bf16_bits_to_f32(f32_to_bf16_bits(w64.astype(np.float32))))
+    return Inputs(q, k, v, w[0], w[1])
+
+
+def make_workload_inputs(wl: Workload, seed: int | None = None) -> Inputs:
+    return make_inputs(wl.B, wl.Sq, wl.Sk, wl.H, wl.seed if seed is None else seed)
+
+
+def sample_rows(S: int, valid: int, count: int, seed: int, tile: int = 256) -> np.ndarray:
+    """A seeded, sorted subset of query rows for sampled parity at full size.
+    Always includes the first and last row, the last valid row and the rows
+    either side of every `tile` boundary up to `count` draws."""
+    rng = np.random.default_rng(10_000 + seed)
+    must = {0, S - 1, max(valid - 1, 0), min(valid, S - 1)}
+    for t in range(tile, S, tile * max(1, S // (tile * 8))):
+        must.update({t - 1, t})
+    extra = rng.choice(S, size=min(count, S), replace=False)
+    rows = np.array(sorted(set(int(r) for r in must) | set(int(r) for r in extra)), dtype=np.int64)
+    return rows

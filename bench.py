@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""Benchmark of the MiniMax-H3 attention step on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input
+already resident in HBM: the fused Q/K RMSNorm + partial-rotary prologue
+(with the key-major copy of v) and the dense attention forward, through the
+C-ABI (h3attn_forward_stages). The workload is one GPU's 6-head share of the
+104,448-row packed sequence (B=1, S=104448, H=6, d=128, bf16).
+
+Prints one JSON line. `value` is attention TFLOP/s over the whole step
+(4*S^2*d*H flop per step / step time). `roofline` is the attention kernel
+alone, timed with HIP events on the stream it runs on. `cpu_baseline` is the
+fp64 oracle timed on this host on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 matrix-core peak
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+METRIC = "attention fwd TFLOP/s + % bf16 MFMA peak at S=104448,H=6,d=128 (1 GPU)"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_full_traffic.json")
+ATTN_SOURCE = os.path.join(ROOT, "video_dit_dense_amd", "csrc", "attn_fwd.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    with open(ATTN_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary, or None when it is missing or the kernel source changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, inp, target_s: float):
+    """Time the fp64 oracle (as it stands) on one head and a seeded sample of
+    query rows against all keys; scale the row count so the run takes about
+    `target_s` seconds. Reports attention TFLOP/s of that sample."""
+    import numpy as np
+    import oracle
+    import workloads
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max([d.get("num_threads", 1) for d in info if d.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        threads = None
+    q1, k1, v1 = inp.q[:, :, :1].copy(), inp.k[:, :, :1].copy(), inp.v[:, :, :1].copy()
+    theta = wl.theta if wl.rope else None
+
+    def run(n_rows):
+        rows = np.sort(np.random.default_rng(99).choice(wl.q_valid, size=n_rows, replace=False))
+        t0 = time.perf_counter()
+        oracle.forward(q1, k1, v1, inp.w_q, inp.w_k, wl.eps, theta, wl.scale, wl.q_valid, wl.kv_valid,
+                       norm=wl.norm, rows=rows)
+        return time.perf_counter() - t0
+
+    probe_rows = 64
+    t_probe = run(probe_rows)
+    n = int(min(wl.q_valid, max(probe_rows, probe_rows * target_s / max(t_probe, 1e-3))))
+    t = run(n)
+    flops = 4.0 * n * wl.kv_valid * 128 * 1
+    return {
+        "value": flops / t / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads if threads is not None else len(os.sched_getaffinity(0)),
+        "kind": "oracle",
+        "sample": f"fp64 NumPy oracle, head 0 of {wl.H}, {n} of {wl.q_valid} query rows against all "
+                  f"{wl.kv_valid} keys, prologue included, {t:.1f} s wall",
+        "seconds": t,
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="full", help="workload name (default: full)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-baseline duration")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prologue-reps", type=int, default=20)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (no sharding or "
+              "collectives); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import numpy as np  # noqa: F401
+    import torch
+    import workloads
+    from video_dit_dense_amd import h3attn
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    h3attn.load_library()
+    wl = workloads.WORKLOADS[args.workload]
+    log(f"workload {wl.name}: {wl.description}")
+    t0 = time.perf_counter()
+    inp = workloads.make_workload_inputs(wl)
+    log(f"inputs generated in {time.perf_counter() - t0:.1f} s")
+
+    def dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+
+    q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
+    w_q = torch.from_numpy(inp.w_q).to("cuda:0")
+    w_k = torch.from_numpy(inp.w_k).to("cuda:0")
+    cos = sin = None
+    if wl.rope:
+        cos, sin = h3attn.rope_tables(max(wl.Sq, wl.Sk), wl.theta)
+    ws = h3attn.make_workspace(wl.B, wl.Sq, wl.Sk, wl.H)
+    o = torch.empty_like(q)
+
+    def stage(st):
+        h3attn.forward(q, k, v, w_q if wl.norm else None, w_k if wl.norm else None, wl.eps, cos, sin,
+                       q_valid=wl.q_valid, kv_valid=wl.kv_valid, scale=wl.scale, out=o, workspace=ws,
+                       stages=st)
+
+    for _ in range(args.warmup):
+        stage(h3attn.STAGE_PREPARE)
+        stage(h3attn.STAGE_ATTEND)
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        ev[i][0].record()
+        stage(h3attn.STAGE_PREPARE)
+        ev[i][1].record()
+        stage(h3attn.STAGE_ATTEND)
+        ev[i][2].record()
+    end.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+    prep_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    attn_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    attn_avg = sum(attn_ms) / len(attn_ms)
+    prep_avg = sum(prep_ms) / len(prep_ms)
+    flops = wl.attention_flops()
+    log(f"timed {args.steps} steps: {ms_step:.3f} ms/step, attention kernel {attn_avg:.3f} ms "
+        f"(min {min(attn_ms):.3f}, max {max(attn_ms):.3f}), prepare {prep_avg:.3f} ms")
+
+    # Stand-alone prologue (h3attn_qk_prologue, BSHD in, BSHD out), HBM roofline.
+    qo, ko = torch.empty_like(q), torch.empty_like(k)
+    for _ in range(3):
+        h3attn.qk_prologue(q, k, w_q if wl.norm else None, w_k if wl.norm else None, wl.eps, cos, sin, qo, ko)
+    pe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    pe[0].record()
+    for _ in range(args.prologue_reps):
+        h3attn.qk_prologue(q, k, w_q if wl.norm else None, w_k if wl.norm else None, wl.eps, cos, sin, qo, ko)
+    pe[1].record()
+    torch.cuda.synchronize()
+    pro_ms = pe[0].elapsed_time(pe[1]) / args.prologue_reps
+    pro_gbs = wl.prologue_bytes() / (pro_ms * 1e-3) / 1e9
+    log(f"prologue: {pro_ms * 1e3:.1f} us, {pro_gbs:.0f} GB/s")
+
+    achieved = flops / (attn_avg * 1e-3) / 1e12
+    traffic = measured_traffic()
+    result = {
+        "metric": METRIC,
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{wl.name}: B={wl.B} Sq={wl.Sq} Sk={wl.Sk} H={wl.H} d=128 q_valid={wl.q_valid} "
+                        f"kv_valid={wl.kv_valid} norm={wl.norm} rope={'96/128' if wl.rope else 'off'}",
+            "flop_per_step": flops,
+            "step": "prepare (RMSNorm+RoPE prologue, key-major v) + attention forward",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "attn_fwd_kernel",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "avg_ms": round(attn_avg, 4),
+        },
+        "prologue": {
+            "kernel": "qk_prologue_kernel (h3attn_qk_prologue, BSHD)",
+            "bound": "hbm",
+            "avg_us": round(pro_ms * 1e3, 2),
+            "achieved": round(pro_gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(pro_gbs / PEAK_HBM_GBS, 4),
+            "bytes": wl.prologue_bytes(),
+        },
+        "prepare_stage_ms": round(prep_avg, 4),
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (fp64 oracle) ...")
+        result["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
+        log(f"cpu baseline: {result['cpu_baseline']}")
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

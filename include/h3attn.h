@@ -1,0 +1,170 @@
+/*
+ * h3attn: the MiniMax-H3 video-DiT attention step on AMD Instinct MI355X (gfx950).
+ *
+ * The step (FastVideo PR #1832 "Add FlashInfer attention backend support for
+ * MiniMax H3", sections "Summary" and "Preserve H3-specific attention
+ * behavior"; TeleFuser PR #37, section 2.2): per-head RMSNorm of q and k, a
+ * rotary embedding on 96 of the 128 head channels, then dense non-causal
+ * scaled-dot-product attention over BSHD tensors at head_dim 128 in bf16,
+ * with an optional valid front / padded tail (TeleFuser PR #37, sections 2.3
+ * and 2.4; FastVideo PR #1799, section "Implementation", padding masks).
+ *
+ * Conventions shared by every entry point
+ *  - bf16 tensors are passed as uint16_t bit patterns. Every pointer is a
+ *    caller-owned device pointer unless stated otherwise. q, k, v and o are
+ *    dense, contiguous [B, S, H, 128] (BSHD, channel fastest).
+ *  - Every device pointer must be 16-byte aligned.
+ *  - The library allocates no device memory and keeps no pointer after a call
+ *    returns. Work is enqueued asynchronously on `stream` (a hipStream_t
+ *    passed as void*; NULL is the null stream).
+ *  - All arguments are validated before anything is enqueued: when a call
+ *    returns an error, nothing has run and no output was touched.
+ *  - Device faults, like any asynchronous HIP error, surface at the caller's
+ *    next synchronisation, not as a return value.
+ *  - The library runs on gfx950 only. On any other device the call returns
+ *    H3ATTN_ERR_UNSUPPORTED_DEVICE; there is no fallback path.
+ *  - There is no backward pass: the step is inference-only (FastVideo PR
+ *    #1799, section "Failure behavior").
+ */
+#ifndef H3ATTN_H_
+#define H3ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+enum h3attn_status {
+  H3ATTN_OK = 0,
+  H3ATTN_ERR_NULL_POINTER = 1,      /* a required pointer is NULL, or only one of a pair is given */
+  H3ATTN_ERR_BAD_SHAPE = 2,         /* a size is out of range (head_dim != 128, S < 1, valid lengths, table rows) */
+  H3ATTN_ERR_BAD_ALIGNMENT = 3,     /* a pointer is not 16-byte aligned */
+  H3ATTN_ERR_ALIASING = 4,          /* an output overlaps an input (other than an exact in-place prologue) */
+  H3ATTN_ERR_BAD_VALUE = 5,         /* eps, theta or softmax_scale not finite / out of range */
+  H3ATTN_ERR_WORKSPACE = 6,         /* workspace missing or smaller than h3attn_forward_workspace_bytes() */
+  H3ATTN_ERR_UNSUPPORTED_DEVICE = 7,/* the current device is not gfx950, or there is no device */
+  H3ATTN_ERR_HIP = 8                /* a HIP runtime call or a kernel launch failed */
+};
+
+#define H3ATTN_HEAD_DIM 128
+#define H3ATTN_ROPE_DIM 96     /* channels 0..95 are rotated as 48 rotate-half pairs (j, j+48) */
+#define H3ATTN_ROPE_PAIRS 48
+
+/* A static, NUL-terminated description of a status code. Never NULL. */
+const char* h3attn_status_string(int status);
+
+/*
+ * Rotary tables for the 96/128 partial rotary embedding (FastVideo PR #1832,
+ * "Preserve H3-specific attention behavior").
+ *
+ * Writes cos_out[p*48 + j] = cos(phi) and sin_out[p*48 + j] = sin(phi) with
+ * phi = p * theta^(-2j/96), for rows p = 0 .. rows-1 and pairs j = 0..47.
+ * Angles, cosines and sines are evaluated in fp64 on the device and rounded
+ * once to fp32.
+ *   cos_out, sin_out: device fp32 [rows, 48], disjoint, 16-byte aligned.
+ *   rows >= 1; theta finite and > 1.
+ * Errors: NULL_POINTER, BAD_SHAPE (rows < 1), BAD_VALUE (theta), ALIGNMENT,
+ * ALIASING (cos/sin overlap), UNSUPPORTED_DEVICE, HIP.
+ */
+int h3attn_rope_tables(float* cos_out, float* sin_out, int32_t rows, double theta, void* stream);
+
+/*
+ * The fused Q/K prologue: per-head RMSNorm followed by the partial rotary
+ * embedding, rounded once to bf16 (round to nearest even).
+ *
+ * For every (b, s, h) row x of 128 channels of q (weight q_norm_w) and of k
+ * (weight k_norm_w):
+ *   y_c = x_c * (mean_c x_c^2 + eps)^(-1/2) * w_c            (fp32)
+ *   for j in 0..47, (a, b) = (y_j, y_{j+48}), c = cos[s*48+j], n = sin[s*48+j]:
+ *   y_j <- a*c - b*n,  y_{j+48} <- b*c + a*n;  channels 96..127 unchanged.
+ * (TeleFuser PR #37 section 2.2, steps 1 and 3; FastVideo PR #1832,
+ * "Preserve H3-specific attention behavior".)
+ *
+ *   q_in [B,Sq,H,128], k_in [B,Sk,H,128]: device bf16, read only.
+ *   q_out, k_out: device bf16, same shapes. Each may equal its input exactly
+ *     (in place) or be disjoint from every other tensor.
+ *   head_dim: must be 128.
+ *   q_norm_w, k_norm_w: device fp32 [128]; both NULL disables the norm.
+ *   eps: finite, >= 0 (the configurations use 1e-6).
+ *   rope_cos, rope_sin: device fp32 [rope_rows, 48] (see h3attn_rope_tables);
+ *     both NULL disables the rotary embedding; row s serves token s.
+ *   rope_rows: >= max(Sq, Sk) when the rotary embedding is on.
+ * Errors: NULL_POINTER, BAD_SHAPE, BAD_ALIGNMENT, ALIASING, BAD_VALUE,
+ * UNSUPPORTED_DEVICE, HIP.
+ */
+int h3attn_qk_prologue(const uint16_t* q_in, const uint16_t* k_in,
+                       uint16_t* q_out, uint16_t* k_out,
+                       int32_t B, int32_t Sq, int32_t Sk, int32_t H, int32_t head_dim,
+                       const float* q_norm_w, const float* k_norm_w, float eps,
+                       const float* rope_cos, const float* rope_sin, int32_t rope_rows,
+                       void* stream);
+
+/*
+ * Bytes of device workspace h3attn_forward needs for these sizes (the
+ * normalised q and k and a key-major copy of v, each padded to whole tiles).
+ * Returns 0 when a size is < 1 or the result would overflow.
+ */
+size_t h3attn_forward_workspace_bytes(int32_t B, int32_t Sq, int32_t Sk, int32_t H);
+
+/*
+ * The attention step: the prologue above on q and k (when enabled), then dense
+ * non-causal attention
+ *   o_i = sum_{j < kv_valid} softmax_j(softmax_scale * q_i . k_j) v_j   for i < q_valid,
+ *   o_i = 0                                                             for q_valid <= i < Sq,
+ * per (b, h), with QK^T and PV as bf16 matrix-core contractions accumulated
+ * in fp32 and the softmax in fp32. Keys at or past kv_valid are never read.
+ *
+ *   q [B,Sq,H,128], k and v [B,Sk,H,128]: device bf16, read only.
+ *   o [B,Sq,H,128]: device bf16, written in full; disjoint from all inputs
+ *     and from the workspace.
+ *   head_dim: must be 128.
+ *   q_norm_w, k_norm_w, eps: as for h3attn_qk_prologue (both NULL: q and k
+ *     are used as given).
+ *   rope_cos, rope_sin, rope_rows: as for h3attn_qk_prologue (both NULL: no
+ *     rotary embedding; cross-attention uses this).
+ *   q_valid: -1 means Sq; else 0..Sq. Rows >= q_valid are written as +0.0.
+ *   kv_valid: -1 means Sk; else 1..Sk.
+ *   softmax_scale: finite and > 0 (the configurations use 1/sqrt(128)).
+ *   workspace: device memory of at least
+ *     h3attn_forward_workspace_bytes(B, Sq, Sk, H) bytes, 256-byte aligned,
+ *     disjoint from every tensor; its contents on entry do not matter and are
+ *     clobbered. Required.
+ * Errors: NULL_POINTER, BAD_SHAPE, BAD_ALIGNMENT, ALIASING, BAD_VALUE,
+ * WORKSPACE, UNSUPPORTED_DEVICE, HIP.
+ */
+int h3attn_forward(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
+                   int32_t B, int32_t Sq, int32_t Sk, int32_t H, int32_t head_dim,
+                   const float* q_norm_w, const float* k_norm_w, float eps,
+                   const float* rope_cos, const float* rope_sin, int32_t rope_rows,
+                   int32_t q_valid, int32_t kv_valid, float softmax_scale,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * h3attn_forward split into its two stages, for callers that time them
+ * separately or prepare k/v once and attend several times.
+ *   stages & H3ATTN_STAGE_PREPARE: the prologue on q and k and the key-major
+ *     copy of v, written into the workspace (all other tensors read only).
+ *   stages & H3ATTN_STAGE_ATTEND: attention from the prepared workspace into o.
+ * Arguments and errors are those of h3attn_forward; stages must be 1, 2 or 3
+ * (else BAD_VALUE). A call with only H3ATTN_STAGE_ATTEND must follow, in
+ * stream order, a PREPARE call with the same sizes, valid lengths and
+ * workspace; q, k and v are then not read (but must still be valid
+ * pointers, for validation). h3attn_forward(...) equals this with stages = 3.
+ */
+#define H3ATTN_STAGE_PREPARE 1u
+#define H3ATTN_STAGE_ATTEND 2u
+int h3attn_forward_stages(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
+                          int32_t B, int32_t Sq, int32_t Sk, int32_t H, int32_t head_dim,
+                          const float* q_norm_w, const float* k_norm_w, float eps,
+                          const float* rope_cos, const float* rope_sin, int32_t rope_rows,
+                          int32_t q_valid, int32_t kv_valid, float softmax_scale,
+                          void* workspace, size_t workspace_bytes, uint32_t stages, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* H3ATTN_H_ */

@@ -1,0 +1,147 @@
+"""Host-side tests of the C-ABI library: it loads, exports every entry point
+include/h3attn.h declares, and rejects bad arguments before touching the GPU.
+No test here launches a kernel: every fake pointer below sits in a call that
+fails validation (or, with no GPU present, the device gate)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from video_dit_dense_amd import h3attn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "h3attn.h")
+
+OK, NULLP, SHAPE, ALIGN, ALIAS, VALUE, WS, DEVICE, HIP = range(9)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(h3attn_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return h3attn.load_library()
+
+
+def P(x):
+    return ctypes.c_void_p(x)
+
+
+A = 1 << 20   # fake, 16-byte aligned, never dereferenced (validation fails first)
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert names == sorted(h3attn.SIGNATURES)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for s in range(9):
+        msg = h3attn.status_string(s)
+        assert isinstance(msg, str) and msg
+    assert "unknown" in h3attn.status_string(99)
+    assert h3attn.status_string(DEVICE).find("gfx950") >= 0
+
+
+def test_workspace_bytes(lib):
+    # q, k, v each padded to 256 rows, bf16, 128 channels
+    assert lib.h3attn_forward_workspace_bytes(1, 104448, 104448, 6) == 6 * 104448 * 256 * 3
+    assert lib.h3attn_forward_workspace_bytes(2, 1000, 300, 3) == 6 * (1024 + 2 * 512) * 256
+    assert lib.h3attn_forward_workspace_bytes(0, 1, 1, 1) == 0
+    assert lib.h3attn_forward_workspace_bytes(1, -5, 1, 1) == 0
+
+
+def prologue(lib, q=A, k=2 * A, qo=3 * A, ko=4 * A, B=1, Sq=8, Sk=8, H=2, D=128,
+             wq=5 * A, wk=5 * A + 512, eps=1e-6, rc=6 * A, rs=7 * A, rows=8):
+    return lib.h3attn_qk_prologue(P(q), P(k), P(qo), P(ko), B, Sq, Sk, H, D, P(wq), P(wk), eps,
+                                  P(rc), P(rs), rows, None)
+
+
+def test_prologue_validation(lib):
+    assert prologue(lib, q=0) == NULLP
+    assert prologue(lib, ko=0) == NULLP
+    assert prologue(lib, wk=0) == NULLP            # only one weight
+    assert prologue(lib, rs=0) == NULLP            # only one table
+    assert prologue(lib, D=64) == SHAPE
+    assert prologue(lib, H=0) == SHAPE
+    assert prologue(lib, Sq=0) == SHAPE
+    assert prologue(lib, rows=7) == SHAPE          # tables shorter than S
+    assert prologue(lib, eps=float("nan")) == VALUE
+    assert prologue(lib, eps=-1.0) == VALUE
+    assert prologue(lib, q=A + 2) == ALIGN
+    assert prologue(lib, rc=6 * A + 4) == ALIGN
+    assert prologue(lib, qo=2 * A) == ALIAS        # q_out on top of k
+    assert prologue(lib, qo=A + 256) == ALIAS      # partial overlap with q
+    assert prologue(lib, qo=3 * A, ko=3 * A + 256) == ALIAS
+    assert prologue(lib, rs=6 * A + 16) == ALIAS   # cos and sin overlap
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="device gate is checked on a machine without a GPU")
+def test_prologue_device_gate_without_gpu(lib):
+    assert prologue(lib) == DEVICE
+    assert prologue(lib, qo=A, ko=2 * A) == DEVICE     # exact in-place passes validation
+    assert prologue(lib, wq=0, wk=0, rc=0, rs=0, rows=0) == DEVICE
+
+
+def forward(lib, q=A, k=2 * A, v=3 * A, o=4 * A, B=1, Sq=8, Sk=8, H=2, D=128, wq=5 * A, wk=5 * A + 512,
+            eps=1e-6, rc=6 * A, rs=7 * A, rows=8, qv=-1, kvv=-1, scale=0.0883, ws=16 * A, wsb=None):
+    if wsb is None:
+        wsb = lib.h3attn_forward_workspace_bytes(B, Sq, Sk, H) if B > 0 and Sq > 0 and Sk > 0 and H > 0 else 0
+    return lib.h3attn_forward(P(q), P(k), P(v), P(o), B, Sq, Sk, H, D, P(wq), P(wk), eps, P(rc), P(rs), rows,
+                              qv, kvv, scale, P(ws), wsb, None)
+
+
+def test_forward_validation(lib):
+    assert forward(lib, v=0) == NULLP
+    assert forward(lib, o=0) == NULLP
+    assert forward(lib, wq=0) == NULLP
+    assert forward(lib, D=256) == SHAPE
+    assert forward(lib, qv=9) == SHAPE
+    assert forward(lib, qv=-2) == SHAPE
+    assert forward(lib, kvv=0) == SHAPE
+    assert forward(lib, kvv=9) == SHAPE
+    assert forward(lib, B=70000, H=1) == SHAPE
+    assert forward(lib, scale=0.0) == VALUE
+    assert forward(lib, scale=float("inf")) == VALUE
+    assert forward(lib, o=4 * A + 8) == ALIGN
+    assert forward(lib, ws=0) == WS
+    assert forward(lib, wsb=1024) == WS
+    assert forward(lib, ws=16 * A + 16) == ALIGN   # workspace must be 256-byte aligned
+    assert forward(lib, o=A) == ALIAS              # o on top of q
+    assert forward(lib, ws=3 * A) == ALIAS         # workspace on top of v
+    assert forward(lib, rows=4) == SHAPE
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="device gate is checked on a machine without a GPU")
+def test_forward_device_gate_without_gpu(lib):
+    assert forward(lib) == DEVICE
+    assert forward(lib, wq=0, wk=0, rc=0, rs=0, rows=0, qv=0, kvv=1) == DEVICE
+    assert lib.h3attn_rope_tables(P(A), P(2 * A), 16, 1e4, None) == DEVICE
+
+
+def test_rope_tables_validation(lib):
+    assert lib.h3attn_rope_tables(P(0), P(2 * A), 16, 1e4, None) == NULLP
+    assert lib.h3attn_rope_tables(P(A), P(2 * A), 0, 1e4, None) == SHAPE
+    assert lib.h3attn_rope_tables(P(A), P(2 * A), 16, float("nan"), None) == VALUE
+    assert lib.h3attn_rope_tables(P(A), P(2 * A), 16, 0.5, None) == VALUE
+    assert lib.h3attn_rope_tables(P(A + 4), P(2 * A), 16, 1e4, None) == ALIGN
+    assert lib.h3attn_rope_tables(P(A), P(A + 64), 16, 1e4, None) == ALIAS
+
+
+def test_python_wrapper_rejections():
+    q = torch.zeros(1, 8, 2, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        h3attn.forward(q, q, q)
+    with pytest.raises(ValueError, match="GPU"):
+        h3attn.qk_prologue(q, q, None, None)
+    with pytest.raises(ValueError, match="GPU"):
+        h3attn.forward(q.float(), q, q)
+    with pytest.raises(TypeError):
+        h3attn._check_bshd("q", q.numpy())

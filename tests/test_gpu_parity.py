@@ -1,0 +1,248 @@
+"""GPU parity of the HIP path against the fp64 oracle, through the C-ABI.
+
+Bar (spec tolerance on bf16 outputs): max-abs error <= 2e-2 and
+relative RMS error <= 5e-3 against the fp64 oracle on the same seeded inputs.
+The prologue alone is held to a tighter bar: every output within half a
+bf16 ulp of the exact fp64 value (one correct rounding) plus 1e-6 absolute,
+the fp32 error of the rotation where a*cos - b*sin cancels to a small value.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import DevInputs, say, to_dev, to_host, f32_dev
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+MAX_ABS = 2e-2
+REL_RMS = 5e-3
+
+
+@pytest.fixture(scope="module")
+def h3():
+    from video_dit_dense_amd import h3attn
+    h3attn.load_library()
+    return h3attn
+
+
+def run_forward(h3, wl_or_shape, inp, q_valid=None, kv_valid=None, norm=True, rope=True, theta=1e4):
+    d = DevInputs(inp)
+    S_rows = max(d.q.shape[1], d.k.shape[1])
+    cos = sin = None
+    if rope:
+        cos, sin = h3.rope_tables(S_rows, theta)
+    o = h3.forward(d.q, d.k, d.v, d.w_q if norm else None, d.w_k if norm else None, 1e-6, cos, sin,
+                   q_valid=q_valid, kv_valid=kv_valid, scale=1 / math.sqrt(128))
+    torch.cuda.synchronize()
+    return to_host(o)
+
+
+def assert_prologue_rounding(got_bits, ref, label):
+    got = oracle.bf16_bits_to_f64(got_bits)
+    a = np.abs(ref)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    half_ulp = np.where(a > 0, np.exp2(np.maximum(e, -126.0) - 8.0), 0.0)
+    err = np.abs(got - ref)
+    assert np.all(np.isfinite(got)), label
+    assert np.all(err <= half_ulp * (1 + 1e-6) + 1e-6), (label, float((err - half_ulp).max()))
+    assert np.mean(err <= half_ulp * (1 + 1e-6)) > 0.9999, label
+
+
+def check(metrics, label):
+    say(f"{label}: {metrics}")
+    assert metrics["nonfinite"] == 0, label
+    assert metrics["max_abs"] <= MAX_ABS, label
+    assert metrics["rel_rms"] <= REL_RMS, label
+
+
+# ------------------------------------------------------------------ rotary tables
+
+def test_rope_tables_match_oracle_angles(h3):
+    rows = workloads.WORKLOADS["full"].Sq
+    say("rope tables rows", rows)
+    cos, sin = h3.rope_tables(rows, 1e4)
+    torch.cuda.synchronize()
+    phi = oracle.rope_angles(np.arange(rows), 1e4)
+    # Both sides evaluate phi = p * theta^(-j/48) in fp64; their angles may
+    # differ by a few fp64 ulps of phi (<= 5e-11 rad for phi <= 1.1e5), which
+    # matters only where cos/sin pass near zero. Bar: one correct fp32
+    # rounding of the fp64 value plus that absolute slack.
+    for got, ref in ((cos.cpu().numpy(), np.cos(phi)), (sin.cpu().numpy(), np.sin(phi))):
+        half_ulp32 = 0.5 * np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64)
+        err = np.abs(got.astype(np.float64) - ref)
+        assert np.all(err <= half_ulp32 * (1 + 1e-6) + 1e-10)
+        assert np.mean(err <= half_ulp32 * (1 + 1e-6)) > 0.999
+
+
+# ------------------------------------------------------------------------ prologue
+
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+def test_prologue_matches_oracle(h3, name):
+    wl = workloads.WORKLOADS[name]
+    say("prologue", name, wl)
+    inp = workloads.make_workload_inputs(wl)
+    d = DevInputs(inp)
+    cos = sin = None
+    if wl.rope:
+        cos, sin = h3.rope_tables(max(wl.Sq, wl.Sk), wl.theta)
+    qo, ko = h3.qk_prologue(d.q, d.k, d.w_q, d.w_k, wl.eps, cos, sin)
+    torch.cuda.synchronize()
+    qr, kr = oracle.qk_prologue(inp.q, inp.k, inp.w_q, inp.w_k, wl.eps, wl.theta if wl.rope else None)
+    for got, ref, lab in ((to_host(qo), qr, "q"), (to_host(ko), kr, "k")):
+        m = oracle.compare(got, ref)
+        say(f"  {lab}: {m} max|y|={np.abs(ref).max():.3f}")
+        assert_prologue_rounding(got, ref, f"{name} {lab}")
+        assert m["rel_rms"] <= REL_RMS
+        assert m["max_abs"] <= MAX_ABS
+
+
+def test_prologue_in_place_equals_out_of_place(h3):
+    inp = workloads.make_inputs(2, 777, 301, 3, seed=21)
+    d = DevInputs(inp)
+    cos, sin = h3.rope_tables(777)
+    qo, ko = h3.qk_prologue(d.q, d.k, d.w_q, d.w_k, 1e-6, cos, sin)
+    qi, ki = d.q.clone(), d.k.clone()
+    h3.qk_prologue(qi, ki, d.w_q, d.w_k, 1e-6, cos, sin, q_out=qi, k_out=ki)
+    torch.cuda.synchronize()
+    assert torch.equal(qo.view(torch.int16), qi.view(torch.int16))
+    assert torch.equal(ko.view(torch.int16), ki.view(torch.int16))
+
+
+def test_prologue_norm_only_and_rope_only(h3):
+    inp = workloads.make_inputs(1, 130, 70, 2, seed=22)
+    d = DevInputs(inp)
+    cos, sin = h3.rope_tables(130)
+    qo, ko = h3.qk_prologue(d.q, d.k, d.w_q, d.w_k, 1e-6, None, None)
+    qr, kr = oracle.qk_prologue(inp.q, inp.k, inp.w_q, inp.w_k, 1e-6, None)
+    assert_prologue_rounding(to_host(qo), qr, "norm-only q")
+    assert_prologue_rounding(to_host(ko), kr, "norm-only k")
+    qo, ko = h3.qk_prologue(d.q, d.k, None, None, 1e-6, cos, sin)
+    qr, kr = oracle.qk_prologue(inp.q, inp.k, None, None, 1e-6, 1e4, norm=False)
+    assert_prologue_rounding(to_host(qo), qr, "rope-only q")
+    assert_prologue_rounding(to_host(ko), kr, "rope-only k")
+
+
+# ----------------------------------------------------------------------- attention
+
+@pytest.mark.parametrize("name", ["tiny", "mid"])
+def test_forward_full_oracle(h3, name):
+    wl = workloads.WORKLOADS[name]
+    say("forward", name)
+    inp = workloads.make_workload_inputs(wl)
+    got = run_forward(h3, wl, inp, wl.q_valid, wl.kv_valid, wl.norm, wl.rope)
+    ref = oracle.forward(inp.q, inp.k, inp.v, inp.w_q, inp.w_k, wl.eps, wl.theta if wl.rope else None,
+                         wl.scale, wl.q_valid, wl.kv_valid, norm=wl.norm)
+    check(oracle.compare(got, ref), name)
+
+
+@pytest.mark.parametrize("name", ["padded", "cross", "full"])
+def test_forward_sampled_rows(h3, name):
+    """Full-size launch (the configuration the benchmark times); the oracle
+    computes a seeded sample of query rows exactly, including the first and
+    last rows, the valid/tail boundary and rows around block boundaries."""
+    wl = workloads.WORKLOADS[name]
+    say("forward sampled", name)
+    inp = workloads.make_workload_inputs(wl)
+    got = run_forward(h3, wl, inp, wl.q_valid, wl.kv_valid, wl.norm, wl.rope)
+    rows = workloads.sample_rows(wl.Sq, wl.q_valid, 192, wl.seed)
+    ref = oracle.forward(inp.q, inp.k, inp.v, inp.w_q, inp.w_k, wl.eps, wl.theta if wl.rope else None,
+                         wl.scale, wl.q_valid, wl.kv_valid, norm=wl.norm, rows=rows)
+    sel = got[:, rows]
+    check(oracle.compare(sel, ref), f"{name} ({len(rows)} rows)")
+    if wl.q_valid < wl.Sq:
+        assert np.all(got[:, wl.q_valid:] == 0), "tail rows must be +0.0"
+
+
+RAGGED = [
+    # B, Sq, Sk, H, q_valid, kv_valid, norm, rope
+    (2, 1000, 777, 3, 900, 700, True, True),
+    (1, 1, 1, 1, 1, 1, True, True),
+    (1, 33, 65, 2, 33, 65, True, False),
+    (1, 129, 64, 1, 129, 63, False, False),
+    (3, 300, 300, 2, 0, 300, True, True),
+    (1, 513, 1000, 2, 257, 1, True, True),
+    (1, 4096, 129, 4, 4000, 129, False, True),
+]
+
+
+@pytest.mark.parametrize("B,Sq,Sk,H,qv,kvv,norm,rope", RAGGED)
+def test_forward_ragged(h3, B, Sq, Sk, H, qv, kvv, norm, rope):
+    say("ragged", B, Sq, Sk, H, qv, kvv, norm, rope)
+    inp = workloads.make_inputs(B, Sq, Sk, H, seed=Sq * 7 + Sk)
+    got = run_forward(h3, None, inp, qv, kvv, norm, rope)
+    ref = oracle.forward(inp.q, inp.k, inp.v, inp.w_q, inp.w_k, 1e-6, 1e4 if rope else None,
+                         1 / math.sqrt(128), qv, kvv, norm=norm)
+    if qv == 0:
+        assert np.all(got == 0)
+        return
+    check(oracle.compare(got, ref), "ragged")
+    assert np.all(got[:, qv:] == 0)
+
+
+# ---------------------------------------------------------------------- invariants
+
+def test_single_valid_key_returns_its_value_exactly(h3):
+    inp = workloads.make_inputs(1, 700, 300, 2, seed=31)
+    got = run_forward(h3, None, inp, None, 1, True, True)
+    want = np.broadcast_to(inp.v[:, :1], got.shape)
+    assert np.array_equal(got, want)
+
+
+def test_zero_query_gives_exact_mean(h3):
+    rng = np.random.default_rng(32)
+    B, S, H = 1, 384, 2
+    q = np.zeros((B, S, H, 128), dtype=np.uint16)
+    k = workloads.make_inputs(B, S, S, H, seed=33).k
+    vals = rng.integers(-1, 2, size=(B, S, H, 128)).astype(np.float32)
+    v = workloads.f32_to_bf16_bits(vals)
+    inp = workloads.Inputs(q, k, v, np.ones(128, np.float32), np.ones(128, np.float32))
+    got = run_forward(h3, None, inp, None, 256, False, False)
+    mean = vals[:, :256].sum(axis=1, keepdims=True) / 256.0
+    want = workloads.f32_to_bf16_bits(np.broadcast_to(mean, vals.shape).astype(np.float32))
+    assert np.array_equal(got, want)
+
+
+def test_masked_keys_never_read(h3):
+    inp = workloads.make_inputs(1, 520, 512, 2, seed=34)
+    clean = run_forward(h3, None, inp, None, 300, True, True)
+    k = inp.k.copy(); v = inp.v.copy()
+    k[:, 300:] = 0x7FC0                                   # NaN
+    v[:, 300:] = workloads.f32_to_bf16_bits(np.float32(1e4))
+    v[:, 400:] = 0xFF80                                   # -inf
+    pois = run_forward(h3, None, workloads.Inputs(inp.q, k, v, inp.w_q, inp.w_k), None, 300, True, True)
+    assert np.array_equal(clean, pois)
+
+
+def test_tail_queries_are_positive_zero_and_never_read(h3):
+    inp = workloads.make_inputs(1, 1000, 600, 2, seed=35)
+    a = run_forward(h3, None, inp, 700, None, True, True)
+    q = inp.q.copy(); q[:, 700:] = 0x7FC0
+    b = run_forward(h3, None, workloads.Inputs(q, inp.k, inp.v, inp.w_q, inp.w_k), 700, None, True, True)
+    assert np.array_equal(a, b)
+    assert np.all(a[:, 700:] == 0)                        # bit pattern 0x0000 = +0.0
+
+
+def test_permutation_of_keys_and_values(h3):
+    inp = workloads.make_inputs(1, 256, 512, 2, seed=36)
+    a = run_forward(h3, None, inp, None, None, True, False)
+    perm = np.random.default_rng(37).permutation(512)
+    p = workloads.Inputs(inp.q, inp.k[:, perm], inp.v[:, perm], inp.w_q, inp.w_k)
+    b = run_forward(h3, None, p, None, None, True, False)
+    # The running max per tile depends on key order, so P rounds to bf16
+    # differently and a, b are not bitwise equal; both must meet the bar
+    # against the (order-free) oracle of the unpermuted problem.
+    ref = oracle.forward(inp.q, inp.k, inp.v, inp.w_q, inp.w_k, 1e-6, None, 1 / math.sqrt(128))
+    check(oracle.compare(a, ref), "original order")
+    check(oracle.compare(b, ref), "permuted keys/values")
+
+
+def test_repeat_runs_are_bitwise_identical(h3):
+    inp = workloads.make_inputs(1, 2048, 2048, 4, seed=38)
+    a = run_forward(h3, None, inp, 2000, 1999, True, True)
+    b = run_forward(h3, None, inp, 2000, 1999, True, True)
+    assert np.array_equal(a, b)

@@ -1,0 +1,244 @@
+// C-ABI layer of the h3attn library: argument validation, the gfx950 device
+// gate, workspace carving and kernel orchestration. Every check runs before
+// anything is enqueued, so an error return means no work was done.
+#include "h3attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "h3attn_internal.h"
+
+#define H3_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// 0 = unknown, 1 = gfx950, 2 = other architecture.
+std::atomic<int> g_device_kind[kMaxDevices];
+
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return H3ATTN_ERR_UNSUPPORTED_DEVICE;
+  if (dev >= kMaxDevices) return H3ATTN_ERR_UNSUPPORTED_DEVICE;
+  int kind = g_device_kind[dev].load(std::memory_order_relaxed);
+  if (kind == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return H3ATTN_ERR_HIP;
+    kind = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_device_kind[dev].store(kind, std::memory_order_relaxed);
+  }
+  return kind == 1 ? H3ATTN_OK : H3ATTN_ERR_UNSUPPORTED_DEVICE;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+Range range_of(const void* p, size_t bytes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{lo, lo + bytes};
+}
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Element count of a [B, S, H, 128] tensor, or 0 on overflow.
+size_t bshd_bytes(int32_t B, int32_t S, int32_t H) {
+  const unsigned __int128 n = (unsigned __int128)B * (unsigned __int128)S * (unsigned __int128)H * 128u * 2u;
+  if (n > (unsigned __int128)(INT64_MAX / 4)) return 0;
+  return (size_t)n;
+}
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+int status_from(hipError_t e) { return e == hipSuccess ? H3ATTN_OK : H3ATTN_ERR_HIP; }
+
+// Shared validation of the prologue arguments (both entry points).
+int check_prologue_args(int32_t Sq, int32_t Sk, const float* wq, const float* wk, float eps,
+                        const float* rc, const float* rs, int32_t rope_rows) {
+  if ((wq == nullptr) != (wk == nullptr)) return H3ATTN_ERR_NULL_POINTER;
+  if ((rc == nullptr) != (rs == nullptr)) return H3ATTN_ERR_NULL_POINTER;
+  if (wq && !(std::isfinite(eps) && eps >= 0.f)) return H3ATTN_ERR_BAD_VALUE;
+  if (wq && (!aligned16(wq) || !aligned16(wk))) return H3ATTN_ERR_BAD_ALIGNMENT;
+  if (rc) {
+    if (rope_rows < Sq || rope_rows < Sk) return H3ATTN_ERR_BAD_SHAPE;
+    if (!aligned16(rc) || !aligned16(rs)) return H3ATTN_ERR_BAD_ALIGNMENT;
+    const size_t tb = (size_t)rope_rows * h3::kRopePairs * sizeof(float);
+    if (overlap(range_of(rc, tb), range_of(rs, tb))) return H3ATTN_ERR_ALIASING;
+  }
+  return H3ATTN_OK;
+}
+
+struct WorkspaceLayout {
+  int64_t Sq_pad, Sk_pad;
+  size_t q_off, k_off, v_off, total;
+};
+
+bool workspace_layout(int32_t B, int32_t Sq, int32_t Sk, int32_t H, WorkspaceLayout* w) {
+  if (B < 1 || Sq < 1 || Sk < 1 || H < 1) return false;
+  w->Sq_pad = round_up(Sq, h3::kRowPad);
+  w->Sk_pad = round_up(Sk, h3::kRowPad);
+  const unsigned __int128 bh = (unsigned __int128)B * (unsigned __int128)H;
+  const unsigned __int128 qb = bh * (unsigned __int128)w->Sq_pad * 256u;
+  const unsigned __int128 kb = bh * (unsigned __int128)w->Sk_pad * 256u;
+  const unsigned __int128 tot = qb + 2 * kb;
+  if (tot > (unsigned __int128)(INT64_MAX / 4)) return false;
+  w->q_off = 0;
+  w->k_off = (size_t)qb;
+  w->v_off = (size_t)(qb + kb);
+  w->total = (size_t)tot;
+  return true;
+}
+
+}  // namespace
+
+H3_API const char* h3attn_status_string(int status) {
+  switch (status) {
+    case H3ATTN_OK: return "ok";
+    case H3ATTN_ERR_NULL_POINTER: return "a required pointer is NULL (or only one of a pair was given)";
+    case H3ATTN_ERR_BAD_SHAPE: return "a size is out of range (head_dim must be 128; S, H, B >= 1; valid lengths; rotary table rows)";
+    case H3ATTN_ERR_BAD_ALIGNMENT: return "a pointer is not 16-byte aligned (workspace: 256-byte)";
+    case H3ATTN_ERR_ALIASING: return "an output overlaps an input or another output";
+    case H3ATTN_ERR_BAD_VALUE: return "eps, theta or softmax_scale is not finite or out of range";
+    case H3ATTN_ERR_WORKSPACE: return "workspace missing or smaller than h3attn_forward_workspace_bytes()";
+    case H3ATTN_ERR_UNSUPPORTED_DEVICE: return "the current device is not gfx950 (MI355X), or no device is present";
+    case H3ATTN_ERR_HIP: return "a HIP runtime call or kernel launch failed";
+    default: return "unknown h3attn status";
+  }
+}
+
+H3_API int h3attn_rope_tables(float* cos_out, float* sin_out, int32_t rows, double theta, void* stream) {
+  if (!cos_out || !sin_out) return H3ATTN_ERR_NULL_POINTER;
+  if (rows < 1 || (int64_t)rows * h3::kRopePairs > INT32_MAX) return H3ATTN_ERR_BAD_SHAPE;
+  if (!std::isfinite(theta) || !(theta > 1.0)) return H3ATTN_ERR_BAD_VALUE;
+  if (!aligned16(cos_out) || !aligned16(sin_out)) return H3ATTN_ERR_BAD_ALIGNMENT;
+  const size_t tb = (size_t)rows * h3::kRopePairs * sizeof(float);
+  if (overlap(range_of(cos_out, tb), range_of(sin_out, tb))) return H3ATTN_ERR_ALIASING;
+  if (int st = check_device()) return st;
+  return status_from(h3::launch_rope_tables(cos_out, sin_out, rows, theta, (hipStream_t)stream));
+}
+
+H3_API int h3attn_qk_prologue(const uint16_t* q_in, const uint16_t* k_in, uint16_t* q_out, uint16_t* k_out,
+                              int32_t B, int32_t Sq, int32_t Sk, int32_t H, int32_t head_dim,
+                              const float* q_norm_w, const float* k_norm_w, float eps,
+                              const float* rope_cos, const float* rope_sin, int32_t rope_rows,
+                              void* stream) {
+  if (!q_in || !k_in || !q_out || !k_out) return H3ATTN_ERR_NULL_POINTER;
+  if (head_dim != h3::kHeadDim || B < 1 || Sq < 1 || Sk < 1 || H < 1) return H3ATTN_ERR_BAD_SHAPE;
+  const size_t qbytes = bshd_bytes(B, Sq, H), kbytes = bshd_bytes(B, Sk, H);
+  if (qbytes == 0 || kbytes == 0) return H3ATTN_ERR_BAD_SHAPE;
+  if (int st = check_prologue_args(Sq, Sk, q_norm_w, k_norm_w, eps, rope_cos, rope_sin, rope_rows)) return st;
+  if (!aligned16(q_in) || !aligned16(k_in) || !aligned16(q_out) || !aligned16(k_out))
+    return H3ATTN_ERR_BAD_ALIGNMENT;
+  const Range qi = range_of(q_in, qbytes), ki = range_of(k_in, kbytes);
+  const Range qo = range_of(q_out, qbytes), ko = range_of(k_out, kbytes);
+  if (q_out != q_in && (overlap(qo, qi) || overlap(qo, ki))) return H3ATTN_ERR_ALIASING;
+  if (k_out != k_in && (overlap(ko, ki) || overlap(ko, qi))) return H3ATTN_ERR_ALIASING;
+  if (overlap(qo, ko)) return H3ATTN_ERR_ALIASING;
+  if (q_out == q_in && overlap(qi, ki)) return H3ATTN_ERR_ALIASING;
+  if (int st = check_device()) return st;
+
+  const int64_t row = (int64_t)H * h3::kHeadDim;
+  h3::ProTensor tq{q_in, q_out, q_norm_w, (int64_t)Sq * row, row, h3::kHeadDim,
+                   (int64_t)Sq * row, row, h3::kHeadDim, Sq, Sq};
+  h3::ProTensor tk{k_in, k_out, k_norm_w, (int64_t)Sk * row, row, h3::kHeadDim,
+                   (int64_t)Sk * row, row, h3::kHeadDim, Sk, Sk};
+  return status_from(h3::launch_qk_prologue(tq, tk, B, H, eps, rope_cos, rope_sin, (hipStream_t)stream));
+}
+
+H3_API size_t h3attn_forward_workspace_bytes(int32_t B, int32_t Sq, int32_t Sk, int32_t H) {
+  WorkspaceLayout w;
+  if (!workspace_layout(B, Sq, Sk, H, &w)) return 0;
+  return w.total;
+}
+
+H3_API int h3attn_forward(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
+                          int32_t B, int32_t Sq, int32_t Sk, int32_t H, int32_t head_dim,
+                          const float* q_norm_w, const float* k_norm_w, float eps,
+                          const float* rope_cos, const float* rope_sin, int32_t rope_rows,
+                          int32_t q_valid, int32_t kv_valid, float softmax_scale,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  return h3attn_forward_stages(q, k, v, o, B, Sq, Sk, H, head_dim, q_norm_w, k_norm_w, eps, rope_cos,
+                               rope_sin, rope_rows, q_valid, kv_valid, softmax_scale, workspace,
+                               workspace_bytes, H3ATTN_STAGE_PREPARE | H3ATTN_STAGE_ATTEND, stream);
+}
+
+H3_API int h3attn_forward_stages(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
+                                 int32_t B, int32_t Sq, int32_t Sk, int32_t H, int32_t head_dim,
+                                 const float* q_norm_w, const float* k_norm_w, float eps,
+                                 const float* rope_cos, const float* rope_sin, int32_t rope_rows,
+                                 int32_t q_valid, int32_t kv_valid, float softmax_scale,
+                                 void* workspace, size_t workspace_bytes, uint32_t stages, void* stream) {
+  if (!q || !k || !v || !o) return H3ATTN_ERR_NULL_POINTER;
+  if (stages == 0 || stages > (H3ATTN_STAGE_PREPARE | H3ATTN_STAGE_ATTEND)) return H3ATTN_ERR_BAD_VALUE;
+  if (head_dim != h3::kHeadDim || B < 1 || Sq < 1 || Sk < 1 || H < 1) return H3ATTN_ERR_BAD_SHAPE;
+  if ((int64_t)B * H > 65535 || Sq > (1 << 30) || Sk > (1 << 30)) return H3ATTN_ERR_BAD_SHAPE;
+  const size_t qbytes = bshd_bytes(B, Sq, H), kbytes = bshd_bytes(B, Sk, H);
+  if (qbytes == 0 || kbytes == 0) return H3ATTN_ERR_BAD_SHAPE;
+  if (q_valid == -1) q_valid = Sq;
+  if (kv_valid == -1) kv_valid = Sk;
+  if (q_valid < 0 || q_valid > Sq || kv_valid < 1 || kv_valid > Sk) return H3ATTN_ERR_BAD_SHAPE;
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return H3ATTN_ERR_BAD_VALUE;
+  if (int st = check_prologue_args(Sq, Sk, q_norm_w, k_norm_w, eps, rope_cos, rope_sin, rope_rows)) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return H3ATTN_ERR_BAD_ALIGNMENT;
+  WorkspaceLayout wl;
+  if (!workspace_layout(B, Sq, Sk, H, &wl)) return H3ATTN_ERR_BAD_SHAPE;
+  if (!workspace || workspace_bytes < wl.total) return H3ATTN_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return H3ATTN_ERR_BAD_ALIGNMENT;
+  const Range oq = range_of(o, qbytes);
+  const Range ws = range_of(workspace, wl.total);
+  const Range rq = range_of(q, qbytes), rk = range_of(k, kbytes), rv = range_of(v, kbytes);
+  if (overlap(oq, rq) || overlap(oq, rk) || overlap(oq, rv) || overlap(oq, ws)) return H3ATTN_ERR_ALIASING;
+  if (overlap(ws, rq) || overlap(ws, rk) || overlap(ws, rv)) return H3ATTN_ERR_ALIASING;
+  if (q_norm_w) {
+    const Range w1 = range_of(q_norm_w, 512), w2 = range_of(k_norm_w, 512);
+    if (overlap(ws, w1) || overlap(ws, w2) || overlap(oq, w1) || overlap(oq, w2)) return H3ATTN_ERR_ALIASING;
+  }
+  if (rope_cos) {
+    const size_t tb = (size_t)rope_rows * h3::kRopePairs * sizeof(float);
+    const Range c1 = range_of(rope_cos, tb), c2 = range_of(rope_sin, tb);
+    if (overlap(ws, c1) || overlap(ws, c2) || overlap(oq, c1) || overlap(oq, c2)) return H3ATTN_ERR_ALIASING;
+  }
+  if (int st = check_device()) return st;
+
+  hipStream_t s = (hipStream_t)stream;
+  uint16_t* wsb = static_cast<uint16_t*>(workspace);
+  uint16_t* qw = wsb + wl.q_off / 2;
+  uint16_t* kw = wsb + wl.k_off / 2;
+  uint16_t* vt = wsb + wl.v_off / 2;
+  const int64_t row = (int64_t)H * h3::kHeadDim;
+
+  // Prologue into the head-major workspace: rows past the valid length are
+  // zero-filled so the attention kernel can read whole tiles.
+  h3::ProTensor tq{q, qw, q_norm_w, (int64_t)Sq * row, row, h3::kHeadDim,
+                   (int64_t)H * wl.Sq_pad * h3::kHeadDim, h3::kHeadDim, wl.Sq_pad * h3::kHeadDim,
+                   q_valid, (int32_t)wl.Sq_pad};
+  h3::ProTensor tk{k, kw, k_norm_w, (int64_t)Sk * row, row, h3::kHeadDim,
+                   (int64_t)H * wl.Sk_pad * h3::kHeadDim, h3::kHeadDim, wl.Sk_pad * h3::kHeadDim,
+                   kv_valid, (int32_t)wl.Sk_pad};
+  if (stages & H3ATTN_STAGE_PREPARE) {
+    hipError_t e = h3::launch_qk_prologue(tq, tk, B, H, eps, rope_cos, rope_sin, s);
+    if (e != hipSuccess) return H3ATTN_ERR_HIP;
+    e = h3::launch_v_relayout(v, vt, B, Sk, H, kv_valid, (int32_t)wl.Sk_pad, s);
+    if (e != hipSuccess) return H3ATTN_ERR_HIP;
+  }
+  if (!(stages & H3ATTN_STAGE_ATTEND)) return H3ATTN_OK;
+
+  h3::AttnArgs a;
+  a.qw = qw;
+  a.kw = kw;
+  a.vt = vt;
+  a.o = o;
+  a.B = B;
+  a.H = H;
+  a.Sq = Sq;
+  a.Sq_pad = (int32_t)wl.Sq_pad;
+  a.Sk_pad = (int32_t)wl.Sk_pad;
+  a.q_valid = q_valid;
+  a.kv_valid = kv_valid;
+  a.scale_log2e = (float)((double)softmax_scale * 1.4426950408889634);
+  return status_from(h3::launch_attention(a, s));
+}

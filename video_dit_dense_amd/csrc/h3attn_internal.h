@@ -1,0 +1,52 @@
+// Internal launch interface between the C-ABI layer (h3attn_api.cpp) and the
+// gfx950 kernels. Arguments reaching these functions are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace h3 {
+
+constexpr int kHeadDim = 128;
+constexpr int kRopePairs = 48;      // rotate-half pairs (j, j+48), j < 48
+constexpr int kRowPad = 256;        // workspace rows are padded to this multiple
+
+// One tensor handled by the prologue kernel. Strides are in elements and
+// describe a [B, S, H, 128] view (channel stride 1).
+struct ProTensor {
+  const uint16_t* in;
+  uint16_t* out;
+  const float* w;          // RMSNorm weight [128] or nullptr (no norm)
+  int64_t in_sb, in_ss, in_sh;
+  int64_t out_sb, out_ss, out_sh;
+  int32_t S_valid;         // rows s < S_valid are read and transformed
+  int32_t S_out;           // rows S_valid <= s < S_out are written as zeros
+};
+
+// Enqueues the fused RMSNorm + partial-rotary prologue over up to two tensors
+// (t1 may have S_out == 0). rope_cos/rope_sin == nullptr disables rotary.
+hipError_t launch_qk_prologue(const ProTensor& t0, const ProTensor& t1, int32_t B, int32_t H,
+                              float eps, const float* rope_cos, const float* rope_sin,
+                              hipStream_t stream);
+
+// Writes the key-major copy of v used by the attention kernel:
+// vt[(b*H + h)*128 + d][p] = v[b][sigma(p)][h][d] for sigma(p) < kv_valid, else 0,
+// for p < Sk_pad, where sigma swaps bits 2 and 3 of p (see attn_fwd.hip).
+hipError_t launch_v_relayout(const uint16_t* v, uint16_t* vt, int32_t B, int32_t Sk, int32_t H,
+                             int32_t kv_valid, int32_t Sk_pad, hipStream_t stream);
+
+hipError_t launch_rope_tables(float* cos_out, float* sin_out, int32_t rows, double theta,
+                              hipStream_t stream);
+
+struct AttnArgs {
+  const uint16_t* qw;      // [B*H][Sq_pad][128], rows >= q_valid are zero
+  const uint16_t* kw;      // [B*H][Sk_pad][128], rows >= kv_valid are zero
+  const uint16_t* vt;      // [B*H][128][Sk_pad], key-permuted, keys >= kv_valid zero
+  uint16_t* o;             // [B][Sq][H][128]
+  int32_t B, H, Sq, Sq_pad, Sk_pad, q_valid, kv_valid;
+  float scale_log2e;       // softmax_scale * log2(e)
+};
+
+hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);
+
+}  // namespace h3

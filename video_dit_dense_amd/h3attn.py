@@ -1,0 +1,195 @@
+"""ctypes binding of libh3attn.so: argument marshalling only.
+
+Every computation runs in the library's HIP kernels. torch supplies device
+memory (outputs, workspace) and the current stream. There is no CPU path: if
+the library is missing or the device is not gfx950, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libh3attn.so")
+
+HEAD_DIM = 128
+ROPE_PAIRS = 48
+
+STATUS = {
+    0: "OK", 1: "ERR_NULL_POINTER", 2: "ERR_BAD_SHAPE", 3: "ERR_BAD_ALIGNMENT",
+    4: "ERR_ALIASING", 5: "ERR_BAD_VALUE", 6: "ERR_WORKSPACE",
+    7: "ERR_UNSUPPORTED_DEVICE", 8: "ERR_HIP",
+}
+
+# Exported symbols and their C signatures (include/h3attn.h).
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_F = ctypes.c_float
+SIGNATURES = {
+    "h3attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "h3attn_rope_tables": (ctypes.c_int, [_P, _P, _I, ctypes.c_double, _P]),
+    "h3attn_qk_prologue": (ctypes.c_int, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _F, _P, _P, _I, _P]),
+    "h3attn_forward_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
+    "h3attn_forward": (ctypes.c_int, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _F, _P, _P, _I,
+                                      _I, _I, _F, _P, ctypes.c_size_t, _P]),
+    "h3attn_forward_stages": (ctypes.c_int, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _F, _P, _P, _I,
+                                             _I, _I, _F, _P, ctypes.c_size_t, ctypes.c_uint32, _P]),
+}
+
+STAGE_PREPARE = 1
+STAGE_ATTEND = 2
+
+_lib = None
+
+
+class H3AttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({status_string(status)})")
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library once. Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is missing: build it with `python -m video_dit_dense_amd.build` "
+                              "(there is no CPU fallback)")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return load_library().h3attn_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise H3AttnError(status, where)
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check_bshd(name: str, t: torch.Tensor) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if t.dtype != torch.bfloat16:
+        raise ValueError(f"{name} must be bfloat16 (got {t.dtype}); the library is bf16-only")
+    if t.dim() != 4 or t.shape[-1] != HEAD_DIM:
+        raise ValueError(f"{name} must be [B, S, H, {HEAD_DIM}] (got {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous BSHD")
+    if t.requires_grad and torch.is_grad_enabled():
+        raise RuntimeError(f"{name} requires grad: h3attn is inference-only (no backward)")
+
+
+def _check_f32(name: str, t: torch.Tensor | None, numel: int | None = None) -> None:
+    if t is None:
+        return
+    if t.device.type != "cuda" or t.dtype != torch.float32 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 GPU tensor")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must have {numel} elements (got {t.numel()})")
+
+
+def rope_tables(rows: int, theta: float = 1e4, device="cuda") -> tuple[torch.Tensor, torch.Tensor]:
+    """cos/sin tables [rows, 48] (fp32) for the 96/128 partial rotary embedding."""
+    lib = load_library()
+    cos = torch.empty((rows, ROPE_PAIRS), dtype=torch.float32, device=device)
+    sin = torch.empty((rows, ROPE_PAIRS), dtype=torch.float32, device=device)
+    _check(lib.h3attn_rope_tables(_ptr(cos), _ptr(sin), int(rows), float(theta), _stream(cos.device)),
+           "h3attn_rope_tables")
+    return cos, sin
+
+
+def qk_prologue(q: torch.Tensor, k: torch.Tensor, w_q: torch.Tensor | None, w_k: torch.Tensor | None,
+                eps: float = 1e-6, rope_cos: torch.Tensor | None = None, rope_sin: torch.Tensor | None = None,
+                q_out: torch.Tensor | None = None, k_out: torch.Tensor | None = None):
+    """Per-head RMSNorm + 96/128 partial rotary on q and k. Pass q_out=q,
+    k_out=k to run in place. Returns (q_out, k_out)."""
+    lib = load_library()
+    _check_bshd("q", q)
+    _check_bshd("k", k)
+    _check_f32("w_q", w_q, HEAD_DIM)
+    _check_f32("w_k", w_k, HEAD_DIM)
+    _check_f32("rope_cos", rope_cos)
+    _check_f32("rope_sin", rope_sin)
+    B, Sq, H, D = q.shape
+    if k.shape[0] != B or k.shape[2] != H:
+        raise ValueError("q and k must share B and H")
+    q_out = torch.empty_like(q) if q_out is None else q_out
+    k_out = torch.empty_like(k) if k_out is None else k_out
+    _check_bshd("q_out", q_out)
+    _check_bshd("k_out", k_out)
+    rows = 0 if rope_cos is None else rope_cos.shape[0]
+    st = lib.h3attn_qk_prologue(_ptr(q), _ptr(k), _ptr(q_out), _ptr(k_out), B, Sq, k.shape[1], H, D,
+                                _ptr(w_q), _ptr(w_k), float(eps), _ptr(rope_cos), _ptr(rope_sin), rows,
+                                _stream(q.device))
+    _check(st, "h3attn_qk_prologue")
+    return q_out, k_out
+
+
+def workspace_bytes(B: int, Sq: int, Sk: int, H: int) -> int:
+    return int(load_library().h3attn_forward_workspace_bytes(B, Sq, Sk, H))
+
+
+def make_workspace(B: int, Sq: int, Sk: int, H: int, device="cuda") -> torch.Tensor:
+    n = workspace_bytes(B, Sq, Sk, H)
+    if n == 0:
+        raise ValueError("bad sizes for the workspace")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+            w_q: torch.Tensor | None = None, w_k: torch.Tensor | None = None, eps: float = 1e-6,
+            rope_cos: torch.Tensor | None = None, rope_sin: torch.Tensor | None = None,
+            q_valid: int | None = None, kv_valid: int | None = None, scale: float | None = None,
+            out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+            stages: int = STAGE_PREPARE | STAGE_ATTEND) -> torch.Tensor:
+    """The attention step: prologue on q/k (if weights/tables given), then
+    dense non-causal attention with key-padding (kv_valid) and a zeroed query
+    tail (q_valid). Returns o [B, Sq, H, 128] bf16. `stages` selects the
+    prepare and/or attend stage (h3attn_forward_stages); a lone attend stage
+    needs `workspace` from an earlier prepare call with the same arguments."""
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_bshd(name, t)
+    _check_f32("w_q", w_q, HEAD_DIM)
+    _check_f32("w_k", w_k, HEAD_DIM)
+    _check_f32("rope_cos", rope_cos)
+    _check_f32("rope_sin", rope_sin)
+    B, Sq, H, D = q.shape
+    Sk = k.shape[1]
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != H:
+        raise ValueError("k and v must be [B, Sk, H, 128] with q's B and H")
+    o = torch.empty_like(q) if out is None else out
+    _check_bshd("out", o)
+    ws = make_workspace(B, Sq, Sk, H, q.device) if workspace is None else workspace
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    rows = 0 if rope_cos is None else rope_cos.shape[0]
+    if stages != (STAGE_PREPARE | STAGE_ATTEND) and workspace is None:
+        raise ValueError("a single stage needs a caller-kept workspace")
+    st = lib.h3attn_forward_stages(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, Sq, Sk, H, D,
+                                   _ptr(w_q), _ptr(w_k), float(eps), _ptr(rope_cos), _ptr(rope_sin), rows,
+                                   -1 if q_valid is None else int(q_valid),
+                                   -1 if kv_valid is None else int(kv_valid),
+                                   scale, _ptr(ws), ws.numel() * ws.element_size(), int(stages),
+                                   _stream(q.device))
+    _check(st, "h3attn_forward_stages")
+    return o

@@ -16,6 +16,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-fvisibility=hidden",
+    # Scores and activations are finite or -inf: no NaN canonicalisation in max.
+    "-fno-honor-nans",
     # No packed fp32 VALU ops anywhere in device code.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",

@@ -2,7 +2,7 @@
 //
 // Computes, per (b, h) and query row i < q_valid,
 //   o_i = sum_{j < kv_valid} softmax_j(scale * q_i . k_j) v_j
-// flash-style: key/value tiles stream through LDS, scores never reach HBM,
+// flash-style: key/value blocks stream through LDS, scores never reach HBM,
 // and a running max / running sum per query row rescales the accumulator
 // (online softmax). QK^T and PV are bf16 matrix-core contractions
 // (v_mfma_f32_32x32x16_bf16) accumulated in fp32; the softmax is fp32.
@@ -12,19 +12,32 @@
 //
 // Orientation. Each wave owns 32 query rows and computes S^T = K Q^T, so the
 // matrix-core result puts one query per lane column: lane l holds 16 of the
-// 32 keys of a 32x32 score tile for query l%32, and lane l^32 holds the other
-// 16. Row max needs one cross-half exchange per tile; the row sum is kept per
-// lane and combined once at the end. P^T then feeds O^T = V^T P^T straight
-// from registers: the keys a lane holds are exactly the keys its B operand
-// needs, provided V^T's key order inside each 16-key group is permuted by
-// sigma (swap bits 2 and 3 of the key index). The v relayout kernel writes
-// V^T in that order, so every LDS operand read here is one 16-byte access.
+// 32 keys of a 32x32 score block for query l%32, and lane l^32 holds the
+// other 16. P^T then feeds O^T = V^T P^T straight from registers: the keys a
+// lane holds are exactly the keys its B operand needs, provided V^T's key
+// order inside each 16-key group is permuted by sigma (swap bits 2 and 3 of
+// the key index). The v relayout kernel below writes V^T in that order.
 //
 // Matrix-core operand layouts used (32x32x16, wave64):
 //   A (32 x 16): lane l supplies row l%32, k = 8*(l/32) .. 8*(l/32)+7
 //   B (16 x 32): lane l supplies column l%32, k = 8*(l/32) .. +7
 //   D (32 x 32): lane l register r holds row 8*(r/4) + 4*(l/32) + r%4, col l%32
+//
+// Schedule. Keys are processed in 32-key sub-tiles u. Step u interleaves
+// QK^T of sub-tile u+1 with the exponentials of sub-tile u, then PV of
+// sub-tile u with the row maxima of sub-tile u+1, so the matrix core and
+// the vector ALU work on independent data within one wave, and two
+// workgroups per CU give each SIMD a second wave to fill gaps. Sub-tiles
+// land in a ring of four LDS buffers through direct global->LDS loads issued
+// three steps ahead; one barrier per step publishes them.
+//
+// Workspace layouts read here (written by the prologue and the relayout):
+//   qw [B*H][Sq_pad][128]          rows >= q_valid zero
+//   kw [B*H][Sk_pad][128]          rows >= kv_valid zero
+//   vt [B*H][Sk_pad/32][128][32]   vt[.., x, d, p] = v[key 32x + sigma(p)][d], zero past kv_valid
 #include "h3attn_internal.h"
+
+#include <type_traits>
 
 namespace h3 {
 namespace {
@@ -33,26 +46,58 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
   bf16x2_t v = {(__bf16)lo, (__bf16)hi};
   return __builtin_bit_cast(uint32_t, v);
 }
 
-__device__ inline float max3(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
+// Compiles to v_max3_f32 (scores are finite or -inf; built with
+// -fno-honor-nans, so no NaN canonicalisation is emitted). Written in C++
+// rather than inline asm so the compiler sees the read of matrix-core
+// results and inserts the required wait states.
+__device__ inline float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
-constexpr int kBK = 64;          // keys per LDS tile
-constexpr int kKPitch = 136;     // K tile row pitch in bf16 (272 B: rows shift 4 banks)
-constexpr int kVPitch = 72;      // V^T tile row pitch in bf16 (144 B)
+// Maximum / sum of x over the lane pair (l, l^32) with v_permlane32_swap.
+__device__ inline float max_lane_pair(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)sw[0]), __builtin_bit_cast(float, (uint32_t)sw[1]));
+}
+__device__ inline float sum_lane_pair(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (uint32_t)sw[0]) + __builtin_bit_cast(float, (uint32_t)sw[1]);
+}
+
+// Lazy rescaling: the running max m used in p = exp2(s*c - m) is only raised
+// when a score exceeds it by more than 2^kRescaleLog2 (in the exp2 domain), so
+// p <= 2^8 and the fp32 accumulator is rescaled only a handful of times per
+// row. The result o = O / l does not depend on m; bf16 rounding of p is
+// relative, so neither does its accuracy.
+constexpr float kRescaleLog2 = 8.0f;
+
+constexpr int kSub = 32;                       // keys per sub-tile
+constexpr int kNBuf = 4;                       // LDS ring depth (sub-tiles)
+constexpr int kKBytes = kSub * 256;            // K sub-tile: 32 rows x 256 B
+constexpr int kVBytes = 128 * kSub * 2;        // V^T sub-tile: 128 rows x 64 B
+constexpr int kBufBytes = kKBytes + kVBytes;   // 16 KB per ring slot
+
+// LDS layouts (no padding; XOR swizzles keep every 16-lane group of a
+// ds_read_b128 on 16 distinct 16-byte bank groups):
+//   K:   row r (key), 16-byte chunk c (channels 8c..8c+7) at r*256 + (c ^ (r & 15))*16
+//   V^T: row d (channel), chunk c (positions 8c..8c+7) at d*64 + (c ^ ((d >> 2) & 3))*16
 
 template <int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(AttnArgs a) {
-  constexpr int NT = NW * 64;
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_kernel(AttnArgs a) {
   constexpr int BM = NW * 32;
-  constexpr int KCH = kBK * 16 / NT;     // 16-byte K chunks per thread per tile
-  constexpr int VCH = 128 * 8 / NT;      // 16-byte V^T chunks per thread per tile
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kBK * kKPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][128 * kVPitch];
+  constexpr int KLD = kKBytes / 1024 / NW;     // 1 KB direct loads per wave per sub-tile (K)
+  constexpr int VLD = kVBytes / 1024 / NW;     // (V)
+  constexpr int LDPS = KLD + VLD;              // load instructions per wave per sub-tile
+  static_assert(KLD * NW * 1024 == kKBytes && VLD * NW * 1024 == kVBytes, "tile split");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kNBuf * kBufBytes];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -80,12 +125,60 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   if (q0 >= a.q_valid) {
     // Whole block lies in the invalid tail: zero rows [q0, min(q0+BM, Sq)).
-    for (int idx = tid; idx < BM * 16; idx += NT) {
+    for (int idx = tid; idx < BM * 16; idx += NW * 64) {
       const int q = q0 + (idx >> 4);
       if (q < a.Sq) *reinterpret_cast<u32x4_t*>(obase + q * orow + (idx & 15) * 8) = u32x4_t{0u, 0u, 0u, 0u};
     }
     return;
   }
+
+  const int NU = (a.kv_valid + kSub - 1) / kSub;     // sub-tiles with at least one valid key
+  const int last_valid = a.kv_valid - 1;
+
+  // Per-lane global element offsets of the direct loads within a sub-tile
+  // (K and V^T sub-tiles are contiguous 8 KB blocks in the workspace). The
+  // lane that fills LDS chunk Q fetches the logical chunk the swizzle puts
+  // there.
+  const uint16_t* kw = a.kw + (int64_t)bh * a.Sk_pad * 128;
+  const uint16_t* vt = a.vt + (int64_t)bh * a.Sk_pad * 128;
+  int koff[KLD], voff[VLD];
+#pragma unroll
+  for (int i = 0; i < KLD; ++i) {
+    const int Q = (wave + NW * i) * 64 + lane;
+    const int r = Q >> 4, p = Q & 15;
+    koff[i] = r * 128 + ((p ^ (r & 15)) * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < VLD; ++i) {
+    const int Q = (wave + NW * i) * 64 + lane;
+    const int d = Q >> 2, p = Q & 3;
+    voff[i] = d * kSub + ((p ^ ((d >> 2) & 3)) * 8);
+  }
+  auto issue_loads = [&](int x) {
+    uint8_t* slot = lds + (x & (kNBuf - 1)) * kBufBytes;
+    const uint16_t* kx = kw + (int64_t)x * (kSub * 128);
+    const uint16_t* vx = vt + (int64_t)x * (kSub * 128);
+#pragma unroll
+    for (int i = 0; i < KLD; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(kx + koff[i]), (lds_void_t*)(slot + (wave + NW * i) * 1024),
+                                       16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < VLD; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(vx + voff[i]),
+                                       (lds_void_t*)(slot + kKBytes + (wave + NW * i) * 1024), 16, 0, 0);
+  };
+
+  // Per-lane LDS byte offsets of the matrix-core operand reads.
+  int kaddr[8], vaddr[2];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) kaddr[kk] = lq * 256 + ((((2 * kk) | g) ^ (lq & 15)) * 16);
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) vaddr[ks] = kKBytes + lq * 64 + ((((2 * ks) | g) ^ ((lq >> 2) & 3)) * 16);
+
+  // Issue the first three sub-tiles, then load Q while they fly.
+  issue_loads(0);
+  if (NU > 1) issue_loads(1);
+  if (NU > 2) issue_loads(2);
 
   // Q fragments (B operand of S^T = K Q^T): lane holds query row lq of this
   // wave, channels 16*kk + 8*g .. +7.
@@ -96,127 +189,149 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     for (int kk = 0; kk < 8; ++kk) qf[kk] = *reinterpret_cast<const bf16x8_t*>(qp + kk * 16);
   }
 
-  const uint16_t* kw = a.kw + (int64_t)bh * a.Sk_pad * 128;
-  const uint16_t* vt = a.vt + (int64_t)bh * 128 * a.Sk_pad;
-  u32x4_t kreg[KCH], vreg[VCH];
-
-  auto gload = [&](int j) {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int idx = tid + i * NT;
-      kreg[i] = *reinterpret_cast<const u32x4_t*>(kw + (int64_t)(j * kBK + (idx >> 4)) * 128 + (idx & 15) * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int idx = tid + i * NT;
-      vreg[i] = *reinterpret_cast<const u32x4_t*>(vt + (int64_t)(idx >> 3) * a.Sk_pad + j * kBK + (idx & 7) * 8);
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int idx = tid + i * NT;
-      *reinterpret_cast<u32x4_t*>(&Ks[buf][(idx >> 4) * kKPitch + (idx & 15) * 8]) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int idx = tid + i * NT;
-      *reinterpret_cast<u32x4_t*>(&Vs[buf][(idx >> 3) * kVPitch + (idx & 7) * 8]) = vreg[i];
-    }
-  };
-
   f32x16_t acc[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
-  float m_run = -INFINITY;   // running max of scale*log2(e)*s for this lane's query
-  float l_run = 0.f;         // running sum of this lane's bf16 probabilities
+  float m_run = -INFINITY;   // running max of c*s for this lane's query (shared by the lane pair)
+  float l_run = 0.f;         // this lane's share of the row sum of bf16 probabilities
   const float c = a.scale_log2e;
-  const int ntiles = (a.kv_valid + kBK - 1) / kBK;
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
-
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < ntiles) gload(j + 1);
-    const uint16_t* ks = Ks[buf];
-    const uint16_t* vs = Vs[buf];
-
-    // S^T for keys 32n..32n+31 of the tile.
-    f32x16_t s[2];
+  auto qk = [&](int x) {
+    const uint8_t* kb = lds + (x & (kNBuf - 1)) * kBufBytes;
+    f32x16_t s;
 #pragma unroll
-    for (int n = 0; n < 2; ++n) {
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[n][r] = 0.f;
+    for (int kk = 0; kk < 8; ++kk) {
+      const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kb + kaddr[kk]);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s, 0, 0, 0);
+    }
+    return s;
+  };
+  // Row max of this lane's 16 scores; with MASK, keys past the end are set
+  // to -inf first (only the last sub-tile can hold such keys).
+  auto rowmax = [&](f32x16_t& s, int x, auto mask) {
+    if constexpr (decltype(mask)::value) {
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(ks + (n * 32 + lq) * kKPitch + kk * 16 + g * 8);
-        s[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s[n], 0, 0, 0);
+      for (int r = 0; r < 16; ++r) {
+        const int key = x * kSub + (r >> 2) * 8 + g * 4 + (r & 3);
+        if (key > last_valid) s[r] = -INFINITY;
       }
     }
-
-    if (j == ntiles - 1 && (a.kv_valid % kBK) != 0) {
+    // Depth-3 tree over the 16 values.
+    const float m0 = max3(s[0], s[1], s[2]), m1 = max3(s[3], s[4], s[5]), m2 = max3(s[6], s[7], s[8]);
+    const float m3 = max3(s[9], s[10], s[11]), m4 = max3(s[12], s[13], s[14]);
+    return fmaxf(max3(m0, m1, m2), max3(m3, m4, s[15]));
+  };
+  using NoMask = std::integral_constant<bool, false>;
+  using Mask = std::integral_constant<bool, true>;
+  // Raise the running max if some row of the wave needs it (rare).
+  auto maybe_rescale = [&](float mx) {
+    if (__builtin_amdgcn_ballot_w64(mx * c > m_run + kRescaleLog2) != 0) {
+      const float m_new = fmaxf(m_run, max_lane_pair(mx) * c);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
-      for (int n = 0; n < 2; ++n)
+      for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = j * kBK + n * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-          if (key >= a.kv_valid) s[n][r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
     }
-
-    float mx = s[0][0];
+  };
+  // bf16 probabilities of sub-tile scores, as the two B operands of PV.
+  auto probs = [&](const f32x16_t& s, bf16x8_t* pf) {
+    const float m = m_run;
 #pragma unroll
-    for (int r = 1; r < 15; r += 2) mx = max3(mx, s[0][r], s[0][r + 1]);
-    mx = max3(mx, s[0][15], s[1][0]);
-#pragma unroll
-    for (int r = 1; r < 15; r += 2) mx = max3(mx, s[1][r], s[1][r + 1]);
-    mx = fmaxf(mx, s[1][15]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-
-    const float m_new = fmaxf(m_run, mx * c);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-
-    bf16x8_t pf[4];
-    float psum = 0.f;
-#pragma unroll
-    for (int ks4 = 0; ks4 < 4; ++ks4) {
-      const int n = ks4 >> 1, r0 = (ks4 & 1) * 8;
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int i = 0; i < 8; i += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[n][r0 + i], c, -m_new));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[n][r0 + i + 1], c, -m_new));
-        const bf16x2_t pp = {(__bf16)p0, (__bf16)p1};
-        psum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, psum, false);
-        pf[ks4][i] = pp[0];
-        pf[ks4][i + 1] = pp[1];
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[ks * 8 + i], c, -m));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[ks * 8 + i + 1], c, -m));
+        pf[ks][i] = (__bf16)p0;
+        pf[ks][i + 1] = (__bf16)p1;
       }
-    }
-    l_run = l_run * alpha + psum;
+  };
+  auto psum = [&](const bf16x8_t* pf) {
+    float t = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) {
+        const bf16x2_t pp = {pf[ks][i], pf[ks][i + 1]};
+        t = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, t, false);
+      }
+    return t;
+  };
+  auto pv = [&](int x, const bf16x8_t* pf) {
+    const uint8_t* vb = lds + (x & (kNBuf - 1)) * kBufBytes;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
-
-    // O^T (128 x 32) += V^T (128 x 64) P^T (64 x 32), four 32-row d tiles.
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int ks4 = 0; ks4 < 4; ++ks4) {
-        const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(vs + (dt * 32 + lq) * kVPitch + ks4 * 16 + g * 8);
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks4], acc[dt], 0, 0, 0);
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(vb + dt * 2048 + vaddr[ks]);
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], acc[dt], 0, 0, 0);
       }
-
-    if (j + 1 < ntiles) lstore(buf ^ 1);
+  };
+  // One pipeline step for sub-tile u < NU-1 (there is a next sub-tile):
+  // wait for this wave's loads of sub-tile u+1 (loads retire in order; those
+  // of u+2 may stay in flight), publish everybody's with a barrier, refill
+  // the ring slot of sub-tile u-1 with sub-tile u+3, then
+  //   phase A: exponentials of sub-tile u alongside QK^T of sub-tile u+1,
+  //   phase B: PV of sub-tile u alongside the row maxima of sub-tile u+1.
+  f32x16_t s_cur;
+  auto step = [&](int u, auto mask_next) {
+    if (u + 2 < NU)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LDPS) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    if (u + 3 < NU) issue_loads(u + 3);
+    bf16x8_t pf[2];
+    probs(s_cur, pf);
+    f32x16_t s_nxt = qk(u + 1);
+    pv(u, pf);
+    l_run += psum(pf);
+    const float mx = rowmax(s_nxt, u + 1, mask_next);
+    maybe_rescale(mx);
+    s_cur = s_nxt;
+  };
+
+  // Sub-tile 0: scores and max before the pipeline starts. Its loads are the
+  // oldest; sub-tiles 1 and 2 may still be in flight.
+  if (NU > 2)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LDPS) : "memory");
+  else if (NU > 1)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LDPS) : "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  s_cur = qk(0);
+  const bool tail_partial = (a.kv_valid % kSub) != 0;
+  if (NU == 1 && tail_partial)
+    maybe_rescale(rowmax(s_cur, 0, Mask{}));
+  else
+    maybe_rescale(rowmax(s_cur, 0, NoMask{}));
+
+  // Steady state: the next sub-tile is never the masked last one.
+  for (int u = 0; u < NU - 2; ++u) step(u, NoMask{});
+  if (NU >= 2) {
+    if (tail_partial)
+      step(NU - 2, Mask{});
+    else
+      step(NU - 2, NoMask{});
+  }
+  {
+    // Last sub-tile: exponentials and PV only.
+    bf16x8_t pf[2];
+    probs(s_cur, pf);
+    pv(NU - 1, pf);
+    l_run += psum(pf);
   }
 
-  const float lsum = l_run + __shfl_xor(l_run, 32);
+  const float lsum = sum_lane_pair(l_run);
   const float inv = 1.0f / lsum;
   const int q = q0 + wave * 32 + lq;
   if (q < a.Sq) {
@@ -237,6 +352,48 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   }
 }
 
+// Transposed, key-blocked copy of v for the PV operand: a block moves 64 keys
+// (two sub-tiles) x 128 channels of one (b, h) through LDS, reading 256-byte
+// rows of v and writing one contiguous 16 KB block of vt. Keys at or past
+// kv_valid are written as zeros and never read.
+__global__ __launch_bounds__(256) void v_relayout_kernel(const uint16_t* __restrict__ v,
+                                                         uint16_t* __restrict__ vt, int32_t H,
+                                                         int32_t Sk, int32_t kv_valid,
+                                                         int32_t Sk_pad) {
+  constexpr int kPitch = 136;  // 272-byte rows
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64 * kPitch];
+  const int p0 = blockIdx.x * 64;
+  const int bh = blockIdx.y;
+  const int b = bh / H, h = bh - b * H;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = tid + 256 * i;
+    const int key = idx >> 4, ch = idx & 15;
+    u32x4_t val = u32x4_t{0u, 0u, 0u, 0u};
+    if (p0 + key < kv_valid)
+      val = *reinterpret_cast<const u32x4_t*>(v + (((int64_t)b * Sk + p0 + key) * H + h) * kHeadDim + ch * 8);
+    *reinterpret_cast<u32x4_t*>(&tile[key * kPitch + ch * 8]) = val;
+  }
+  __syncthreads();
+  // Output chunk idx covers sub-tile xs = idx/512, channel d, positions 8pc..8pc+7.
+  uint16_t* out = vt + ((int64_t)bh * Sk_pad + p0) * kHeadDim;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = tid + 256 * i;
+    const int xs = idx >> 9, d = (idx >> 2) & 127, pc = idx & 3;
+    uint32_t packed[4];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const int pa = pc * 8 + e, pb = pa + 1;
+      const int ka = xs * kSub + ((pa & ~0xC) | ((pa & 4) << 1) | ((pa & 8) >> 1));
+      const int kb = xs * kSub + ((pb & ~0xC) | ((pb & 4) << 1) | ((pb & 8) >> 1));
+      packed[e / 2] = (uint32_t)tile[ka * kPitch + d] | ((uint32_t)tile[kb * kPitch + d] << 16);
+    }
+    *reinterpret_cast<u32x4_t*>(out + idx * 8) = u32x4_t{packed[0], packed[1], packed[2], packed[3]};
+  }
+}
+
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
@@ -245,6 +402,13 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
   const int64_t n_tiles = (int64_t)a.B * a.H * ((a.Sq + BM - 1) / BM);
   if (n_tiles > 0x7fffffffLL) return hipErrorInvalidValue;
   attn_fwd_kernel<NW><<<dim3((unsigned)n_tiles), NW * 64, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_v_relayout(const uint16_t* v, uint16_t* vt, int32_t B, int32_t Sk, int32_t H,
+                             int32_t kv_valid, int32_t Sk_pad, hipStream_t stream) {
+  const dim3 grid((unsigned)(Sk_pad / 64), (unsigned)(B * H));
+  v_relayout_kernel<<<grid, 256, 0, stream>>>(v, vt, H, Sk, kv_valid, Sk_pad);
   return hipGetLastError();
 }
 

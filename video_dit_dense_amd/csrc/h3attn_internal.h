@@ -29,9 +29,8 @@ hipError_t launch_qk_prologue(const ProTensor& t0, const ProTensor& t1, int32_t 
                               float eps, const float* rope_cos, const float* rope_sin,
                               hipStream_t stream);
 
-// Writes the key-major copy of v used by the attention kernel:
-// vt[(b*H + h)*128 + d][p] = v[b][sigma(p)][h][d] for sigma(p) < kv_valid, else 0,
-// for p < Sk_pad, where sigma swaps bits 2 and 3 of p (see attn_fwd.hip).
+// Writes the transposed, key-blocked copy of v that the attention kernel
+// reads (layout in attn_fwd.hip); keys >= kv_valid are written as zeros.
 hipError_t launch_v_relayout(const uint16_t* v, uint16_t* vt, int32_t B, int32_t Sk, int32_t H,
                              int32_t kv_valid, int32_t Sk_pad, hipStream_t stream);
 
@@ -41,7 +40,7 @@ hipError_t launch_rope_tables(float* cos_out, float* sin_out, int32_t rows, doub
 struct AttnArgs {
   const uint16_t* qw;      // [B*H][Sq_pad][128], rows >= q_valid are zero
   const uint16_t* kw;      // [B*H][Sk_pad][128], rows >= kv_valid are zero
-  const uint16_t* vt;      // [B*H][128][Sk_pad], key-permuted, keys >= kv_valid zero
+  const uint16_t* vt;      // [B*H][Sk_pad/32][128][32], see attn_fwd.hip; keys >= kv_valid zero
   uint16_t* o;             // [B][Sq][H][128]
   int32_t B, H, Sq, Sq_pad, Sk_pad, q_valid, kv_valid;
   float scale_log2e;       // softmax_scale * log2(e)

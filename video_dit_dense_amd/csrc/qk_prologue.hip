@@ -1,5 +1,5 @@
-// Q/K prologue of the MiniMax-H3 attention step for gfx950, plus the two
-// small layout kernels the forward path uses (rotary tables, key-major v).
+// Q/K prologue of the MiniMax-H3 attention step for gfx950, plus the rotary
+// table kernel.
 //
 // The prologue is per-head RMSNorm followed by the rotary embedding on 96 of
 // the 128 channels (FastVideo PR #1832, "Preserve H3-specific attention
@@ -184,47 +184,6 @@ __global__ __launch_bounds__(256) void rope_tables_kernel(float* cos_out, float*
   sin_out[i] = (float)s;
 }
 
-// Key-major copy of v: a block moves 64 keys x 128 channels of one (b, h)
-// through LDS so both the read (256 B rows) and the write (128 B runs of
-// keys) are coalesced. Keys at or past kv_valid are written as zeros and
-// never read.
-__global__ __launch_bounds__(256) void v_relayout_kernel(const uint16_t* __restrict__ v,
-                                                         uint16_t* __restrict__ vt, int32_t H,
-                                                         int32_t Sk, int32_t kv_valid,
-                                                         int32_t Sk_pad) {
-  constexpr int kPitch = 136;  // 272-byte rows
-  __shared__ __attribute__((aligned(16))) uint16_t tile[64 * kPitch];
-  const int p0 = blockIdx.x * 64;
-  const int bh = blockIdx.y;
-  const int b = bh / H, h = bh - b * H;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int idx = tid + 256 * i;
-    const int key = idx >> 4, c = idx & 15;
-    U4 val = U4{0, 0, 0, 0};
-    if (p0 + key < kv_valid)
-      val = *reinterpret_cast<const U4*>(v + (((int64_t)b * Sk + p0 + key) * H + h) * kHeadDim + c * 8);
-    *reinterpret_cast<U4*>(&tile[key * kPitch + c * 8]) = val;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int idx = tid + 256 * i;
-    const int d = idx >> 3, pc = idx & 7;
-    uint32_t packed[4];
-#pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      const int pa = pc * 8 + e, pb = pa + 1;
-      const int ka = (pa & ~0xC) | ((pa & 4) << 1) | ((pa & 8) >> 1);
-      const int kb = (pb & ~0xC) | ((pb & 4) << 1) | ((pb & 8) >> 1);
-      packed[e / 2] = (uint32_t)tile[ka * kPitch + d] | ((uint32_t)tile[kb * kPitch + d] << 16);
-    }
-    *reinterpret_cast<U4*>(vt + ((int64_t)bh * kHeadDim + d) * Sk_pad + p0 + pc * 8) =
-        U4{packed[0], packed[1], packed[2], packed[3]};
-  }
-}
-
 }  // namespace
 
 hipError_t launch_qk_prologue(const ProTensor& t0, const ProTensor& t1, int32_t B, int32_t H,
@@ -255,13 +214,6 @@ hipError_t launch_qk_prologue(const ProTensor& t0, const ProTensor& t1, int32_t 
     qk_prologue_kernel<false, true><<<grid, kProThreads, 0, stream>>>(a);
   else
     qk_prologue_kernel<false, false><<<grid, kProThreads, 0, stream>>>(a);
-  return hipGetLastError();
-}
-
-hipError_t launch_v_relayout(const uint16_t* v, uint16_t* vt, int32_t B, int32_t Sk, int32_t H,
-                             int32_t kv_valid, int32_t Sk_pad, hipStream_t stream) {
-  const dim3 grid((unsigned)(Sk_pad / 64), (unsigned)(B * H));
-  v_relayout_kernel<<<grid, 256, 0, stream>>>(v, vt, H, Sk, kv_valid, Sk_pad);
   return hipGetLastError();
 }
 

@@ -77,9 +77,13 @@ def cpu_baseline(wl, inp, target_s: float):
                        norm=wl.norm, rows=rows)
         return time.perf_counter() - t0
 
-    probe_rows = 64
-    t_probe = run(probe_rows)
-    n = int(min(wl.q_valid, max(probe_rows, probe_rows * target_s / max(t_probe, 1e-3))))
+    # Fixed cost (prologue over all rows of the head) plus a per-row cost:
+    # fit t(n) = t0 + t1*n from two probes, then size the timed run.
+    n1, n2 = 128, 512
+    ta, tb = run(n1), run(n2)
+    per_row = max((tb - ta) / (n2 - n1), 1e-6)
+    fixed = max(ta - per_row * n1, 0.0)
+    n = int(min(wl.q_valid, max(n2, (target_s - fixed) / per_row)))
     t = run(n)
     flops = 4.0 * n * wl.kv_valid * 128 * 1
     return {
@@ -102,6 +106,10 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-baseline duration")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prologue-reps", type=int, default=20)
+    ap.add_argument("--only", choices=["all", "attention", "copy"], default="all",
+                    help="for profiler runs: 'attention' runs one prepare stage, then only the attention "
+                         "stage (warmup + steps launches); 'copy' runs a plain 1 GiB device copy "
+                         "(warmup + steps times) to calibrate HBM byte counters")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -118,6 +126,16 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     h3attn.load_library()
+    if args.only == "copy":
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"only": "copy", "bytes_read_per_launch": n, "bytes_written_per_launch": n,
+                          "launches": args.warmup + args.steps}), flush=True)
+        return 0
     wl = workloads.WORKLOADS[args.workload]
     log(f"workload {wl.name}: {wl.description}")
     t0 = time.perf_counter()
@@ -140,6 +158,15 @@ def main() -> int:
         h3attn.forward(q, k, v, w_q if wl.norm else None, w_k if wl.norm else None, wl.eps, cos, sin,
                        q_valid=wl.q_valid, kv_valid=wl.kv_valid, scale=wl.scale, out=o, workspace=ws,
                        stages=st)
+
+    if args.only == "attention":
+        stage(h3attn.STAGE_PREPARE)
+        for _ in range(args.warmup + args.steps):
+            stage(h3attn.STAGE_ATTEND)
+        torch.cuda.synchronize()
+        print(json.dumps({"only": "attention", "workload": wl.name, "flop_per_launch": wl.attention_flops(),
+                          "launches": args.warmup + args.steps}), flush=True)
+        return 0
 
     for _ in range(args.warmup):
         stage(h3attn.STAGE_PREPARE)

@@ -23,13 +23,21 @@
 //   B (16 x 32): lane l supplies column l%32, k = 8*(l/32) .. +7
 //   D (32 x 32): lane l register r holds row 8*(r/4) + 4*(l/32) + r%4, col l%32
 //
-// Schedule. Keys are processed in 32-key sub-tiles u. Step u interleaves
-// QK^T of sub-tile u+1 with the exponentials of sub-tile u, then PV of
-// sub-tile u with the row maxima of sub-tile u+1, so the matrix core and
-// the vector ALU work on independent data within one wave, and two
-// workgroups per CU give each SIMD a second wave to fill gaps. Sub-tiles
-// land in a ring of four LDS buffers through direct global->LDS loads issued
-// three steps ahead; one barrier per step publishes them.
+// Schedule. Keys are processed in 32-key sub-tiles u. Step u reads all 16
+// operand fragments it needs from LDS, then interleaves QK^T of sub-tile u+1
+// with the exponentials of sub-tile u, then PV of sub-tile u with the row
+// maxima of sub-tile u+1, so the matrix core and the vector ALU work on
+// independent data within one wave; two workgroups per CU give each SIMD a
+// second wave to fill gaps. Sub-tiles land in a ring of four LDS buffers
+// through direct global->LDS loads issued three steps ahead; one barrier per
+// step publishes them.
+//
+// Exponent arithmetic. q arrives pre-multiplied by softmax_scale*log2(e)
+// (applied in fp32 by the prologue before its single bf16 rounding), so
+// scores leave the matrix core in exp2 units. Each row keeps an offset m
+// (its running maximum, raised lazily), and the QK^T accumulation starts
+// from -m instead of 0, so p = exp2(score) needs no per-element arithmetic
+// before the exponential.
 //
 // Workspace layouts read here (written by the prologue and the relayout):
 //   qw [B*H][Sq_pad][128]          rows >= q_valid zero
@@ -194,16 +202,15 @@ void attn_fwd_kernel(AttnArgs a) {
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
-  float m_run = -INFINITY;   // running max of c*s for this lane's query (shared by the lane pair)
+  float m_run = 0.f;         // row offset (scores are in exp2 units), shared by the lane pair
   float l_run = 0.f;         // this lane's share of the row sum of bf16 probabilities
-  const float c = a.scale_log2e;
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  auto qk = [&](int x) {
+  // S^T of sub-tile x, accumulated onto `init` (the negated running max, so
+  // the result is already s - m in exp2 units: q carries softmax_scale*log2 e).
+  auto qk = [&](int x, const f32x16_t& init) {
     const uint8_t* kb = lds + (x & (kNBuf - 1)) * kBufBytes;
-    f32x16_t s;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+    f32x16_t s = init;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kb + kaddr[kk]);
@@ -228,13 +235,21 @@ void attn_fwd_kernel(AttnArgs a) {
   };
   using NoMask = std::integral_constant<bool, false>;
   using Mask = std::integral_constant<bool, true>;
-  // Raise the running max if some row of the wave needs it (rare).
-  auto maybe_rescale = [&](float mx) {
-    if (__builtin_amdgcn_ballot_w64(mx * c > m_run + kRescaleLog2) != 0) {
-      const float m_new = fmaxf(m_run, max_lane_pair(mx) * c);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
+  // The scores arrive as s - m_run. If some row of the wave exceeds its
+  // offset by more than 2^kRescaleLog2 (rare), raise that row's m_run by its
+  // excess, shift the scores and rescale the accumulator and partial sum.
+  f32x16_t msplat;     // -m_run in every accumulator slot: the QK^T initial value
+  auto maybe_rescale = [&](f32x16_t& s, float mx) {
+    if (__builtin_amdgcn_ballot_w64(mx > kRescaleLog2) != 0) {
+      const float delta = fmaxf(max_lane_pair(mx), 0.f);
+      m_run += delta;
+      const float alpha = __builtin_amdgcn_exp2f(-delta);
       l_run *= alpha;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] -= delta;
+        msplat[r] = -m_run;
+      }
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -243,13 +258,12 @@ void attn_fwd_kernel(AttnArgs a) {
   };
   // bf16 probabilities of sub-tile scores, as the two B operands of PV.
   auto probs = [&](const f32x16_t& s, bf16x8_t* pf) {
-    const float m = m_run;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int i = 0; i < 8; i += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[ks * 8 + i], c, -m));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[ks * 8 + i + 1], c, -m));
+        const float p0 = __builtin_amdgcn_exp2f(s[ks * 8 + i]);
+        const float p1 = __builtin_amdgcn_exp2f(s[ks * 8 + i + 1]);
         pf[ks][i] = (__bf16)p0;
         pf[ks][i + 1] = (__bf16)p1;
       }
@@ -289,13 +303,37 @@ void attn_fwd_kernel(AttnArgs a) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (u + 3 < NU) issue_loads(u + 3);
+    const uint8_t* kb = lds + ((u + 1) & (kNBuf - 1)) * kBufBytes;
+    const uint8_t* vb = lds + (u & (kNBuf - 1)) * kBufBytes;
+    bf16x8_t kf[8], vf[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) kf[kk] = *reinterpret_cast<const bf16x8_t*>(kb + kaddr[kk]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) vf[i] = *reinterpret_cast<const bf16x8_t*>(vb + (i >> 1) * 2048 + vaddr[i & 1]);
     bf16x8_t pf[2];
     probs(s_cur, pf);
-    f32x16_t s_nxt = qk(u + 1);
-    pv(u, pf);
+    f32x16_t s_nxt;
+    s_nxt = msplat;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s_nxt, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf[i & 1], acc[i >> 1], 0, 0, 0);
     l_run += psum(pf);
     const float mx = rowmax(s_nxt, u + 1, mask_next);
-    maybe_rescale(mx);
+    // Issue order: all 16 fragment reads, then QK^T MFMAs each followed by
+    // exponential work, then PV MFMAs each followed by sum / max work.
+    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    }
+    maybe_rescale(s_nxt, mx);
     s_cur = s_nxt;
   };
 
@@ -308,12 +346,24 @@ void attn_fwd_kernel(AttnArgs a) {
   else
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  s_cur = qk(0);
+  {
+    // Sub-tile 0 sets each row's offset to its exact maximum (so the row
+    // keeps one probability of 1), then scores are shifted by it.
+    f32x16_t zero;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) zero[r] = 0.f;
+    s_cur = qk(0, zero);
+  }
   const bool tail_partial = (a.kv_valid % kSub) != 0;
-  if (NU == 1 && tail_partial)
-    maybe_rescale(rowmax(s_cur, 0, Mask{}));
-  else
-    maybe_rescale(rowmax(s_cur, 0, NoMask{}));
+  {
+    const float mx0 = (NU == 1 && tail_partial) ? rowmax(s_cur, 0, Mask{}) : rowmax(s_cur, 0, NoMask{});
+    m_run = max_lane_pair(mx0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s_cur[r] -= m_run;
+      msplat[r] = -m_run;
+    }
+  }
 
   // Steady state: the next sub-tile is never the masked last one.
   for (int u = 0; u < NU - 2; ++u) step(u, NoMask{});

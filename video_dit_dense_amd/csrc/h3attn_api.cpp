@@ -143,9 +143,9 @@ H3_API int h3attn_qk_prologue(const uint16_t* q_in, const uint16_t* k_in, uint16
 
   const int64_t row = (int64_t)H * h3::kHeadDim;
   h3::ProTensor tq{q_in, q_out, q_norm_w, (int64_t)Sq * row, row, h3::kHeadDim,
-                   (int64_t)Sq * row, row, h3::kHeadDim, Sq, Sq};
+                   (int64_t)Sq * row, row, h3::kHeadDim, Sq, Sq, 1.0f};
   h3::ProTensor tk{k_in, k_out, k_norm_w, (int64_t)Sk * row, row, h3::kHeadDim,
-                   (int64_t)Sk * row, row, h3::kHeadDim, Sk, Sk};
+                   (int64_t)Sk * row, row, h3::kHeadDim, Sk, Sk, 1.0f};
   return status_from(h3::launch_qk_prologue(tq, tk, B, H, eps, rope_cos, rope_sin, (hipStream_t)stream));
 }
 
@@ -213,12 +213,15 @@ H3_API int h3attn_forward_stages(const uint16_t* q, const uint16_t* k, const uin
 
   // Prologue into the head-major workspace: rows past the valid length are
   // zero-filled so the attention kernel can read whole tiles.
+  // q is written pre-multiplied by softmax_scale*log2(e) (fp32, before its
+  // one bf16 rounding), so the attention kernel's scores are in exp2 units.
+  const float c = (float)((double)softmax_scale * 1.4426950408889634);
   h3::ProTensor tq{q, qw, q_norm_w, (int64_t)Sq * row, row, h3::kHeadDim,
                    (int64_t)H * wl.Sq_pad * h3::kHeadDim, h3::kHeadDim, wl.Sq_pad * h3::kHeadDim,
-                   q_valid, (int32_t)wl.Sq_pad};
+                   q_valid, (int32_t)wl.Sq_pad, c};
   h3::ProTensor tk{k, kw, k_norm_w, (int64_t)Sk * row, row, h3::kHeadDim,
                    (int64_t)H * wl.Sk_pad * h3::kHeadDim, h3::kHeadDim, wl.Sk_pad * h3::kHeadDim,
-                   kv_valid, (int32_t)wl.Sk_pad};
+                   kv_valid, (int32_t)wl.Sk_pad, 1.0f};
   if (stages & H3ATTN_STAGE_PREPARE) {
     hipError_t e = h3::launch_qk_prologue(tq, tk, B, H, eps, rope_cos, rope_sin, s);
     if (e != hipSuccess) return H3ATTN_ERR_HIP;
@@ -239,6 +242,5 @@ H3_API int h3attn_forward_stages(const uint16_t* q, const uint16_t* k, const uin
   a.Sk_pad = (int32_t)wl.Sk_pad;
   a.q_valid = q_valid;
   a.kv_valid = kv_valid;
-  a.scale_log2e = (float)((double)softmax_scale * 1.4426950408889634);
   return status_from(h3::launch_attention(a, s));
 }

@@ -21,6 +21,7 @@ struct ProTensor {
   int64_t out_sb, out_ss, out_sh;
   int32_t S_valid;         // rows s < S_valid are read and transformed
   int32_t S_out;           // rows S_valid <= s < S_out are written as zeros
+  float out_scale;         // outputs are multiplied by this in fp32 before the bf16 rounding
 };
 
 // Enqueues the fused RMSNorm + partial-rotary prologue over up to two tensors
@@ -38,12 +39,11 @@ hipError_t launch_rope_tables(float* cos_out, float* sin_out, int32_t rows, doub
                               hipStream_t stream);
 
 struct AttnArgs {
-  const uint16_t* qw;      // [B*H][Sq_pad][128], rows >= q_valid are zero
+  const uint16_t* qw;      // [B*H][Sq_pad][128] scaled by softmax_scale*log2(e), rows >= q_valid zero
   const uint16_t* kw;      // [B*H][Sk_pad][128], rows >= kv_valid are zero
   const uint16_t* vt;      // [B*H][Sk_pad/32][128][32], see attn_fwd.hip; keys >= kv_valid zero
   uint16_t* o;             // [B][Sq][H][128]
   int32_t B, H, Sq, Sq_pad, Sk_pad, q_valid, kv_valid;
-  float scale_log2e;       // softmax_scale * log2(e)
 };
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);

@@ -7,6 +7,11 @@
 // is HBM-bound: about 7 flop per 4 bytes moved, so the design goal is
 // full-width coalesced 16-byte accesses and enough bytes in flight.
 //
+// The forward path asks for q multiplied by softmax_scale*log2(e) (in fp32,
+// before the single bf16 rounding) so the attention kernel's scores come
+// out of the matrix core already in exp2 units; the stand-alone entry point
+// uses a scale of 1.
+//
 // Work unit: one (b, s, h) row of 128 bf16 channels (256 B), handled by 8
 // lanes. Lane t < 6 holds channel chunks t and t+6, i.e. channels 8t..8t+7
 // and their rotate-half partners 48+8t..48+8t+7, so the rotation needs no
@@ -85,6 +90,7 @@ __global__ __launch_bounds__(kProThreads) void qk_prologue_kernel(ProArgs a) {
   const int64_t out_sh = second ? a.t1.out_sh : a.t0.out_sh;
   const int32_t S_valid = second ? a.t1.S_valid : a.t0.S_valid;
   const int32_t S_out = second ? a.t1.S_out : a.t0.S_out;
+  const float out_scale = second ? a.t1.out_scale : a.t0.out_scale;
   const int64_t blk = second ? (int64_t)blockIdx.x - a.nblk0 : (int64_t)blockIdx.x;
 
   const int t = threadIdx.x & 7;                       // lane within the unit
@@ -140,11 +146,18 @@ __global__ __launch_bounds__(kProThreads) void qk_prologue_kernel(ProArgs a) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) ss = fmaf(f0[i], f0[i], fmaf(f1[i], f1[i], ss));
       ss = sum8(ss);
-      const float r = rsqrtf(ss * (1.0f / 128.0f) + a.eps);
+      // The output scale rides on the normalisation factor (one fp32 multiply).
+      const float r = rsqrtf(ss * (1.0f / 128.0f) + a.eps) * out_scale;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         f0[i] = f0[i] * r * w0[i];
         f1[i] = f1[i] * r * w1[i];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        f0[i] *= out_scale;
+        f1[i] *= out_scale;
       }
     }
     if (ROPE && t < 6 && load[k]) {

@@ -130,6 +130,7 @@ H3_API int h3attn_qk_prologue(const uint16_t* q_in, const uint16_t* k_in, uint16
   if (head_dim != h3::kHeadDim || B < 1 || Sq < 1 || Sk < 1 || H < 1) return H3ATTN_ERR_BAD_SHAPE;
   const size_t qbytes = bshd_bytes(B, Sq, H), kbytes = bshd_bytes(B, Sk, H);
   if (qbytes == 0 || kbytes == 0) return H3ATTN_ERR_BAD_SHAPE;
+  if ((int64_t)B * Sq * H >= (1ll << 31) || (int64_t)B * Sk * H >= (1ll << 31)) return H3ATTN_ERR_BAD_SHAPE;
   if (int st = check_prologue_args(Sq, Sk, q_norm_w, k_norm_w, eps, rope_cos, rope_sin, rope_rows)) return st;
   if (!aligned16(q_in) || !aligned16(k_in) || !aligned16(q_out) || !aligned16(k_out))
     return H3ATTN_ERR_BAD_ALIGNMENT;
@@ -186,6 +187,8 @@ H3_API int h3attn_forward_stages(const uint16_t* q, const uint16_t* k, const uin
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return H3ATTN_ERR_BAD_ALIGNMENT;
   WorkspaceLayout wl;
   if (!workspace_layout(B, Sq, Sk, H, &wl)) return H3ATTN_ERR_BAD_SHAPE;
+  if ((int64_t)B * H * wl.Sq_pad >= (1ll << 31) || (int64_t)B * H * wl.Sk_pad >= (1ll << 31))
+    return H3ATTN_ERR_BAD_SHAPE;
   if (!workspace || workspace_bytes < wl.total) return H3ATTN_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return H3ATTN_ERR_BAD_ALIGNMENT;
   const Range oq = range_of(o, qbytes);

@@ -11,6 +11,25 @@ constexpr int kHeadDim = 128;
 constexpr int kRopePairs = 48;      // rotate-half pairs (j, j+48), j < 48
 constexpr int kRowPad = 256;        // workspace rows are padded to this multiple
 
+// Exact unsigned division by a runtime divisor d >= 1 for dividends below
+// 2^31: q = (n * m) >> p with p = 31 + ceil(log2 d), m = ceil(2^p / d).
+// (m <= 2^32 + 1, so n * m fits in 64 bits; the error term m*d - 2^p < d
+// keeps floor exact for every n < 2^31.)
+struct FastDiv {
+  uint64_t m;
+  uint32_t p, d;
+  static FastDiv make(uint32_t d) {
+    uint32_t l = 0;
+    while ((1ull << l) < d) ++l;
+    FastDiv f;
+    f.d = d;
+    f.p = 31 + l;
+    f.m = (uint64_t)(((((unsigned __int128)1) << f.p) + d - 1) / d);
+    return f;
+  }
+  __device__ __host__ uint32_t div(uint32_t n) const { return (uint32_t)(((uint64_t)n * m) >> p); }
+};
+
 // One tensor handled by the prologue kernel. Strides are in elements and
 // describe a [B, S, H, 128] view (channel stride 1).
 struct ProTensor {
@@ -22,6 +41,7 @@ struct ProTensor {
   int32_t S_valid;         // rows s < S_valid are read and transformed
   int32_t S_out;           // rows S_valid <= s < S_out are written as zeros
   float out_scale;         // outputs are multiplied by this in fp32 before the bf16 rounding
+  FastDiv div_h, div_s;    // set by launch_qk_prologue: division by H and by S_out
 };
 
 // Enqueues the fused RMSNorm + partial-rotary prologue over up to two tensors

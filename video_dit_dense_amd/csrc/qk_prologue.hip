@@ -12,19 +12,15 @@
 // out of the matrix core already in exp2 units; the stand-alone entry point
 // uses a scale of 1.
 //
-// Work unit: one (b, s, h) row of 128 bf16 channels (256 B), handled by 8
-// lanes. Lane t < 6 holds channel chunks t and t+6, i.e. channels 8t..8t+7
-// and their rotate-half partners 48+8t..48+8t+7, so the rotation needs no
-// cross-lane traffic. Lanes 6 and 7 hold the pass-through channels 96..127.
-// The mean of squares is reduced over the 8 lanes with DPP moves.
+// Each (b, s, h) row of 128 bf16 channels (256 B) is handled by 16 lanes
+// with full-width coalesced 16-byte accesses; the mean of squares and the
+// rotate-half partners move between lanes with DPP. A thread handles the q
+// row and the k row at the same (b, s, h), so each rotary table row is read
+// once for both; outputs are streamed with non-temporal stores.
 #include "h3attn_internal.h"
 
 namespace h3 {
 namespace {
-
-struct alignas(16) U4 {
-  uint32_t x, y, z, w;
-};
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
@@ -37,34 +33,28 @@ __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-__device__ inline void unpack8(const U4& u, float* f) {
-  f[0] = bf16_lo(u.x); f[1] = bf16_hi(u.x);
-  f[2] = bf16_lo(u.y); f[3] = bf16_hi(u.y);
-  f[4] = bf16_lo(u.z); f[5] = bf16_hi(u.z);
-  f[6] = bf16_lo(u.w); f[7] = bf16_hi(u.w);
-}
-
-__device__ inline U4 pack8(const float* f) {
-  U4 u;
-  u.x = pack_bf16x2(f[0], f[1]);
-  u.y = pack_bf16x2(f[2], f[3]);
-  u.z = pack_bf16x2(f[4], f[5]);
-  u.w = pack_bf16x2(f[6], f[7]);
-  return u;
-}
-
-// Sum over the 8 lanes of an aligned group: quad_perm [1,0,3,2], quad_perm
-// [2,3,0,1], then row_half_mirror (lane i <-> 7-i within each 8 lanes).
-__device__ inline float sum8(float v) {
+// Sum over the 16 lanes of a DPP row: quad_perm [1,0,3,2], quad_perm
+// [2,3,0,1], row_half_mirror (i <-> 7-i), row_mirror (i <-> 15-i).
+__device__ inline float sum16(float v) {
   v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
   v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
   v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
   return v;
 }
 
+// Value of lane i+6 (row_shl:6) or i-6 (row_shr:6) within the DPP row.
+__device__ inline float from_lane_plus6(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x106, 0xF, 0xF, false));
+}
+__device__ inline float from_lane_minus6(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x116, 0xF, 0xF, false));
+}
+
+typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));
+
 struct ProArgs {
   ProTensor t0, t1;
-  int32_t nblk0;           // blocks [0, nblk0) serve t0, the rest t1
   int32_t B, H;
   float eps;
   const float* cos;
@@ -72,112 +62,97 @@ struct ProArgs {
 };
 
 constexpr int kProThreads = 256;
-constexpr int kUnitsPerThread = 2;
-constexpr int kUnitsPerBlock = kProThreads / 8 * kUnitsPerThread;
+constexpr int kUnitsPerThread = 1;
+constexpr int kUnitsPerBlock = kProThreads / 16 * kUnitsPerThread;
 
+// Work unit: one (b, s, h) row of 128 channels. Lane c of a 16-lane DPP row
+// holds channels 8c..8c+7, so each wave-wide 16-byte access covers four
+// whole rows (1 KB contiguous in BSHD). The rotate-half partner of chunk c
+// (c < 6) is chunk c+6, two DPP moves away; chunks 12..15 (channels 96..127)
+// are not rotated.
 template <bool NORM, bool ROPE>
 __global__ __launch_bounds__(kProThreads) void qk_prologue_kernel(ProArgs a) {
-  const bool second = (int32_t)blockIdx.x >= a.nblk0;
-  // Field-wise selects keep the argument struct out of scratch memory.
-  const uint16_t* in = second ? a.t1.in : a.t0.in;
-  uint16_t* out = second ? a.t1.out : a.t0.out;
-  const float* w = second ? a.t1.w : a.t0.w;
-  const int64_t in_sb = second ? a.t1.in_sb : a.t0.in_sb;
-  const int64_t in_ss = second ? a.t1.in_ss : a.t0.in_ss;
-  const int64_t in_sh = second ? a.t1.in_sh : a.t0.in_sh;
-  const int64_t out_sb = second ? a.t1.out_sb : a.t0.out_sb;
-  const int64_t out_ss = second ? a.t1.out_ss : a.t0.out_ss;
-  const int64_t out_sh = second ? a.t1.out_sh : a.t0.out_sh;
-  const int32_t S_valid = second ? a.t1.S_valid : a.t0.S_valid;
-  const int32_t S_out = second ? a.t1.S_out : a.t0.S_out;
-  const float out_scale = second ? a.t1.out_scale : a.t0.out_scale;
-  const int64_t blk = second ? (int64_t)blockIdx.x - a.nblk0 : (int64_t)blockIdx.x;
-
-  const int t = threadIdx.x & 7;                       // lane within the unit
-  const int c0 = t < 6 ? t : 2 * t;                    // 16-byte chunk indices
-  const int c1 = t < 6 ? t + 6 : 2 * t + 1;
-  const int64_t n_units = (int64_t)a.B * S_out * a.H;
-  const int64_t first = blk * kUnitsPerBlock + (threadIdx.x >> 3);
-
-  U4 x0[kUnitsPerThread], x1[kUnitsPerThread];
-  int64_t obase[kUnitsPerThread];
-  int srow[kUnitsPerThread];
-  bool live[kUnitsPerThread], load[kUnitsPerThread];
+  // Each thread takes one (b, s, h) row position and handles the q row and
+  // the k row there, so a rotary table row is loaded once for both.
+  const int c = threadIdx.x & 15;                      // 16-byte chunk: channels 8c..8c+7
+  const int32_t S_all = a.t0.S_out > a.t1.S_out ? a.t0.S_out : a.t1.S_out;
+  const int64_t n_units = (int64_t)a.B * S_all * a.H;
+  const int64_t first = (int64_t)blockIdx.x * kUnitsPerBlock + (threadIdx.x >> 4);
+  const bool rot = c < 12;
+  const float sgn = c < 6 ? -1.0f : 1.0f;            // own*cos + sgn*partner*sin
+  const int jb = (c < 6 ? c : c - 6) * 8;            // rotary pair index of this lane's first channel
 
 #pragma unroll
   for (int k = 0; k < kUnitsPerThread; ++k) {
-    const int64_t u = first + (int64_t)k * (kProThreads / 8);
-    live[k] = u < n_units;
-    const int64_t uu = live[k] ? u : 0;
-    const int h = (int)(uu % a.H);
-    const int64_t rest = uu / a.H;
-    const int s = (int)(rest % S_out);
-    const int b = (int)(rest / S_out);
-    srow[k] = s;
-    load[k] = live[k] && s < S_valid;
-    obase[k] = b * out_sb + s * out_ss + h * out_sh;
-    const int64_t ibase = b * in_sb + s * in_ss + h * in_sh;
-    if (load[k]) {
-      x0[k] = *reinterpret_cast<const U4*>(in + ibase + c0 * 8);
-      x1[k] = *reinterpret_cast<const U4*>(in + ibase + c1 * 8);
-    } else {
-      x0[k] = U4{0, 0, 0, 0};
-      x1[k] = U4{0, 0, 0, 0};
+    const int64_t u = first + (int64_t)k * (kProThreads / 16);
+    const bool live_u = u < n_units;
+    const uint32_t uu = live_u ? (uint32_t)u : 0u;      // unit counts are < 2^31 (host-checked)
+    const uint32_t rest = a.t0.div_h.div(uu);
+    const int h = (int)(uu - rest * (uint32_t)a.H);
+    const uint32_t bq = a.t0.div_s.div(rest);          // div_s divides by S_all
+    const int s = (int)(rest - bq * (uint32_t)S_all);
+    const int64_t b = (int64_t)bq;
+    v4u_t x[2];
+    bool live[2], load[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const ProTensor& T = t ? a.t1 : a.t0;
+      live[t] = live_u && s < T.S_out;
+      load[t] = live[t] && s < T.S_valid;
+      x[t] = load[t] ? *reinterpret_cast<const v4u_t*>(T.in + b * T.in_sb + s * T.in_ss + h * T.in_sh + c * 8)
+                     : v4u_t{0u, 0u, 0u, 0u};
     }
-  }
-
-  float w0[8], w1[8];
-  if (NORM) {
-    const float4* wp = reinterpret_cast<const float4*>(w);
-    float4 a0 = wp[c0 * 2], a1 = wp[c0 * 2 + 1], b0 = wp[c1 * 2], b1 = wp[c1 * 2 + 1];
-    w0[0] = a0.x; w0[1] = a0.y; w0[2] = a0.z; w0[3] = a0.w;
-    w0[4] = a1.x; w0[5] = a1.y; w0[6] = a1.z; w0[7] = a1.w;
-    w1[0] = b0.x; w1[1] = b0.y; w1[2] = b0.z; w1[3] = b0.w;
-    w1[4] = b1.x; w1[5] = b1.y; w1[6] = b1.z; w1[7] = b1.w;
-  }
-
+    float cs[8], sn[8];
+    if (ROPE) {
+      if (rot && (load[0] || load[1])) {
+        const float4* cp = reinterpret_cast<const float4*>(a.cos + (int64_t)s * kRopePairs + jb);
+        const float4* sp = reinterpret_cast<const float4*>(a.sin + (int64_t)s * kRopePairs + jb);
+        const float4 ca = cp[0], cb = cp[1], sa = sp[0], sb = sp[1];
+        cs[0] = ca.x; cs[1] = ca.y; cs[2] = ca.z; cs[3] = ca.w; cs[4] = cb.x; cs[5] = cb.y; cs[6] = cb.z; cs[7] = cb.w;
+        sn[0] = sa.x; sn[1] = sa.y; sn[2] = sa.z; sn[3] = sa.w; sn[4] = sb.x; sn[5] = sb.y; sn[6] = sb.z; sn[7] = sb.w;
+      } else {
 #pragma unroll
-  for (int k = 0; k < kUnitsPerThread; ++k) {
-    float f0[8], f1[8];
-    unpack8(x0[k], f0);
-    unpack8(x1[k], f1);
-    if (NORM) {
-      float ss = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) ss = fmaf(f0[i], f0[i], fmaf(f1[i], f1[i], ss));
-      ss = sum8(ss);
-      // The output scale rides on the normalisation factor (one fp32 multiply).
-      const float r = rsqrtf(ss * (1.0f / 128.0f) + a.eps) * out_scale;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        f0[i] = f0[i] * r * w0[i];
-        f1[i] = f1[i] * r * w1[i];
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        f0[i] *= out_scale;
-        f1[i] *= out_scale;
+        for (int i = 0; i < 8; ++i) { cs[i] = 1.0f; sn[i] = 0.0f; }
       }
     }
-    if (ROPE && t < 6 && load[k]) {
-      const float4* cp = reinterpret_cast<const float4*>(a.cos + (int64_t)srow[k] * kRopePairs + t * 8);
-      const float4* sp = reinterpret_cast<const float4*>(a.sin + (int64_t)srow[k] * kRopePairs + t * 8);
-      const float4 ca = cp[0], cb = cp[1], sa = sp[0], sb = sp[1];
-      const float cs[8] = {ca.x, ca.y, ca.z, ca.w, cb.x, cb.y, cb.z, cb.w};
-      const float sn[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float p = f0[i], q = f1[i];
-        f0[i] = p * cs[i] - q * sn[i];
-        f1[i] = q * cs[i] + p * sn[i];
+    for (int t = 0; t < 2; ++t) {
+      const ProTensor& T = t ? a.t1 : a.t0;
+      float f[8];
+      f[0] = bf16_lo(x[t][0]); f[1] = bf16_hi(x[t][0]);
+      f[2] = bf16_lo(x[t][1]); f[3] = bf16_hi(x[t][1]);
+      f[4] = bf16_lo(x[t][2]); f[5] = bf16_hi(x[t][2]);
+      f[6] = bf16_lo(x[t][3]); f[7] = bf16_hi(x[t][3]);
+      if (NORM) {
+        const float4* wp = reinterpret_cast<const float4*>(T.w + c * 8);
+        const float4 w0 = wp[0], w1 = wp[1];
+        const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ss = fmaf(f[i], f[i], ss);
+        ss = sum16(ss);
+        // The output scale rides on the normalisation factor (one fp32 multiply).
+        const float r = rsqrtf(ss * (1.0f / 128.0f) + a.eps) * T.out_scale;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = f[i] * r * wv[i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] *= T.out_scale;
       }
-    }
-    if (live[k]) {
-      // Rows past S_valid are zero-filled, never computed from (absent) data.
-      const U4 zero = U4{0, 0, 0, 0};
-      *reinterpret_cast<U4*>(out + obase[k] + c0 * 8) = load[k] ? pack8(f0) : zero;
-      *reinterpret_cast<U4*>(out + obase[k] + c1 * 8) = load[k] ? pack8(f1) : zero;
+      if (ROPE) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float up = from_lane_plus6(f[i]), dn = from_lane_minus6(f[i]);
+          const float partner = c < 6 ? up : dn;
+          f[i] = rot ? f[i] * cs[i] + sgn * partner * sn[i] : f[i];
+        }
+      }
+      if (live[t]) {
+        // Rows past S_valid are zero-filled, never computed from (absent) data.
+        v4u_t r = v4u_t{0u, 0u, 0u, 0u};
+        if (load[t]) r = v4u_t{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])};
+        __builtin_nontemporal_store(r, reinterpret_cast<v4u_t*>(T.out + b * T.out_sb + s * T.out_ss + h * T.out_sh + c * 8));
+      }
     }
   }
 }
@@ -210,13 +185,14 @@ hipError_t launch_qk_prologue(const ProTensor& t0, const ProTensor& t1, int32_t 
   a.eps = eps;
   a.cos = rope_cos;
   a.sin = rope_sin;
-  const int64_t u0 = (int64_t)B * t0.S_out * H;
-  const int64_t u1 = (int64_t)B * t1.S_out * H;
-  const int64_t nb0 = (u0 + kUnitsPerBlock - 1) / kUnitsPerBlock;
-  const int64_t nb1 = (u1 + kUnitsPerBlock - 1) / kUnitsPerBlock;
-  if (nb0 + nb1 > 0x7fffffffLL) return hipErrorInvalidValue;
-  a.nblk0 = (int32_t)nb0;
-  const dim3 grid((unsigned)(nb0 + nb1));
+  const int32_t S_all = t0.S_out > t1.S_out ? t0.S_out : t1.S_out;
+  const int64_t units = (int64_t)B * S_all * H;
+  if (units >= (1ll << 31)) return hipErrorInvalidValue;
+  a.t0.div_h = FastDiv::make((uint32_t)H);
+  a.t0.div_s = FastDiv::make((uint32_t)S_all);
+  a.t1.div_h = a.t0.div_h;
+  a.t1.div_s = a.t0.div_s;
+  const dim3 grid((unsigned)((units + kUnitsPerBlock - 1) / kUnitsPerBlock));
   const bool norm = t0.w != nullptr;
   const bool rope = rope_cos != nullptr;
   if (norm && rope)

@@ -27,10 +27,13 @@
 // operand fragments it needs from LDS, then interleaves QK^T of sub-tile u+1
 // with the exponentials of sub-tile u, then PV of sub-tile u with the row
 // maxima of sub-tile u+1, so the matrix core and the vector ALU work on
-// independent data within one wave; two workgroups per CU give each SIMD a
-// second wave to fill gaps. Sub-tiles land in a ring of four LDS buffers
-// through direct global->LDS loads issued three steps ahead; one barrier per
-// step publishes them.
+// independent data within one wave. A workgroup is eight waves (256 query
+// rows, one workgroup per CU), so each SIMD runs two waves that fill each
+// other's gaps and every K/V byte brought into LDS serves 256 queries.
+// Sub-tiles land in a ring of four LDS buffers through direct buffer->LDS
+// loads (one per wave for K and one for V per sub-tile) issued three steps
+// ahead; one barrier per step publishes them. The loads use a buffer
+// resource held in scalar registers, so they cost no vector instructions.
 //
 // Exponent arithmetic. q arrives pre-multiplied by softmax_scale*log2(e)
 // (applied in fp32 by the prologue before its single bf16 rounding), so
@@ -55,6 +58,20 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
+// Word 3 of a raw (stride 0) buffer resource on gfx9: 32-bit data format,
+// untyped loads.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
+// Direct global->LDS load of 16 bytes per lane: lane i's bytes land at
+// dst + 16 i. `base` must be wave-uniform; the buffer resource built from it
+// lives in SGPRs and covers `bytes` bytes, so the only per-lane operand is the
+// 32-bit byte offset.
+__device__ __forceinline__ void load_lds16(const void* base, int bytes, int byte_off, uint8_t* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufferRsrcWord3), (lds_void_t*)dst, 16,
+      byte_off, 0, 0, 0);
+}
+
 
 __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
   bf16x2_t v = {(__bf16)lo, (__bf16)hi};
@@ -108,7 +125,7 @@ void attn_fwd_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kNBuf * kBufBytes];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int lq = lane & 31;
   const int g = lane >> 5;
@@ -143,10 +160,9 @@ void attn_fwd_kernel(AttnArgs a) {
   const int NU = (a.kv_valid + kSub - 1) / kSub;     // sub-tiles with at least one valid key
   const int last_valid = a.kv_valid - 1;
 
-  // Per-lane global element offsets of the direct loads within a sub-tile
-  // (K and V^T sub-tiles are contiguous 8 KB blocks in the workspace). The
-  // lane that fills LDS chunk Q fetches the logical chunk the swizzle puts
-  // there.
+  // Per-lane byte offsets of the direct loads within a sub-tile (K and V^T
+  // sub-tiles are contiguous 8 KB blocks in the workspace). The lane that
+  // fills LDS chunk Q fetches the logical chunk the swizzle puts there.
   const uint16_t* kw = a.kw + (int64_t)bh * a.Sk_pad * 128;
   const uint16_t* vt = a.vt + (int64_t)bh * a.Sk_pad * 128;
   int koff[KLD], voff[VLD];
@@ -154,26 +170,29 @@ void attn_fwd_kernel(AttnArgs a) {
   for (int i = 0; i < KLD; ++i) {
     const int Q = (wave + NW * i) * 64 + lane;
     const int r = Q >> 4, p = Q & 15;
-    koff[i] = r * 128 + ((p ^ (r & 15)) * 8);
+    koff[i] = (r * 128 + ((p ^ (r & 15)) * 8)) * 2;
   }
 #pragma unroll
   for (int i = 0; i < VLD; ++i) {
     const int Q = (wave + NW * i) * 64 + lane;
     const int d = Q >> 2, p = Q & 3;
-    voff[i] = d * kSub + ((p ^ ((d >> 2) & 3)) * 8);
+    voff[i] = (d * kSub + ((p ^ ((d >> 2) & 3)) * 8)) * 2;
   }
+  // One buffer resource per sub-tile (base in SGPRs, 8 KB range), so the
+  // loads need no vector address arithmetic and offsets stay 32-bit at any
+  // sequence length. Steps always issue their refill so that no branch
+  // splits the step's schedule; a refill past the last sub-tile gets an
+  // empty range (the hardware returns zeros without touching memory) and
+  // lands in a ring slot that no later step reads.
   auto issue_loads = [&](int x) {
     uint8_t* slot = lds + (x & (kNBuf - 1)) * kBufBytes;
-    const uint16_t* kx = kw + (int64_t)x * (kSub * 128);
-    const uint16_t* vx = vt + (int64_t)x * (kSub * 128);
+    const bool live = x < NU;
+    const uint16_t* kx = kw + (int64_t)(live ? x : 0) * (kSub * 128);
+    const uint16_t* vx = vt + (int64_t)(live ? x : 0) * (kSub * 128);
 #pragma unroll
-    for (int i = 0; i < KLD; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(kx + koff[i]), (lds_void_t*)(slot + (wave + NW * i) * 1024),
-                                       16, 0, 0);
+    for (int i = 0; i < KLD; ++i) load_lds16(kx, live ? kKBytes : 0, koff[i], slot + (wave + NW * i) * 1024);
 #pragma unroll
-    for (int i = 0; i < VLD; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(vx + voff[i]),
-                                       (lds_void_t*)(slot + kKBytes + (wave + NW * i) * 1024), 16, 0, 0);
+    for (int i = 0; i < VLD; ++i) load_lds16(vx, live ? kVBytes : 0, voff[i], slot + kKBytes + (wave + NW * i) * 1024);
   };
 
   // Per-lane LDS byte offsets of the matrix-core operand reads.
@@ -302,7 +321,6 @@ void attn_fwd_kernel(AttnArgs a) {
     else
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (u + 3 < NU) issue_loads(u + 3);
     const uint8_t* kb = lds + ((u + 1) & (kNBuf - 1)) * kBufBytes;
     const uint8_t* vb = lds + (u & (kNBuf - 1)) * kBufBytes;
     bf16x8_t kf[8], vf[8];
@@ -310,6 +328,9 @@ void attn_fwd_kernel(AttnArgs a) {
     for (int kk = 0; kk < 8; ++kk) kf[kk] = *reinterpret_cast<const bf16x8_t*>(kb + kaddr[kk]);
 #pragma unroll
     for (int i = 0; i < 8; ++i) vf[i] = *reinterpret_cast<const bf16x8_t*>(vb + (i >> 1) * 2048 + vaddr[i & 1]);
+    // The refill targets the slot of sub-tile u-1, which no wave reads after
+    // the barrier, so it may follow this step's fragment reads.
+    issue_loads(u + 3);
     bf16x8_t pf[2];
     probs(s_cur, pf);
     f32x16_t s_nxt;
@@ -447,7 +468,7 @@ __global__ __launch_bounds__(256) void v_relayout_kernel(const uint16_t* __restr
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
-  constexpr int NW = 4;
+  constexpr int NW = 8;
   constexpr int BM = NW * 32;
   const int64_t n_tiles = (int64_t)a.B * a.H * ((a.Sq + BM - 1) / BM);
   if (n_tiles > 0x7fffffffLL) return hipErrorInvalidValue;

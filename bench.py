@@ -8,8 +8,9 @@ C-ABI (h3attn_forward_stages). The workload is one GPU's 6-head share of the
 104,448-row packed sequence (B=1, S=104448, H=6, d=128, bf16).
 
 Prints one JSON line. `value` is attention TFLOP/s over the whole step
-(4*S^2*d*H flop per step / step time). `roofline` is the attention kernel
-alone, timed with HIP events on the stream it runs on. `cpu_baseline` is the
+(4*S^2*d*H flop per step / step time). `roofline` is the attend stage alone
+(the attention kernel, plus the small kernel that merges tiles the schedule
+splits across workgroups), timed with HIP events on the stream it runs on. `cpu_baseline` is the
 fp64 oracle timed on this host on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -193,7 +194,7 @@ def main() -> int:
     attn_avg = sum(attn_ms) / len(attn_ms)
     prep_avg = sum(prep_ms) / len(prep_ms)
     flops = wl.attention_flops()
-    log(f"timed {args.steps} steps: {ms_step:.3f} ms/step, attention kernel {attn_avg:.3f} ms "
+    log(f"timed {args.steps} steps: {ms_step:.3f} ms/step, attend stage {attn_avg:.3f} ms "
         f"(min {min(attn_ms):.3f}, max {max(attn_ms):.3f}), prepare {prep_avg:.3f} ms")
 
     # Stand-alone prologue (h3attn_qk_prologue, BSHD in, BSHD out), HBM roofline.
@@ -234,7 +235,7 @@ def main() -> int:
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": "attn_fwd_kernel",
+            "kernel": "attn_fwd_kernel + attn_merge_kernel (attend stage)",
             "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",

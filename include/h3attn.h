@@ -103,9 +103,13 @@ int h3attn_qk_prologue(const uint16_t* q_in, const uint16_t* k_in,
                        void* stream);
 
 /*
- * Bytes of device workspace h3attn_forward needs for these sizes (the
- * normalised q and k and a key-major copy of v, each padded to whole tiles).
- * Returns 0 when a size is < 1 or the result would overflow.
+ * Bytes of device workspace h3attn_forward needs for these sizes: the
+ * normalised q and k and a key-major copy of v, each padded to whole tiles,
+ * then room for the partial results of query tiles whose keys the forward
+ * splits over several workgroups (it does so when the last round of tiles
+ * would leave compute units idle; two fp32 records of 132 KB per split
+ * workgroup, at most 512 records). Returns 0 when a size is < 1 or the
+ * result would overflow.
  */
 size_t h3attn_forward_workspace_bytes(int32_t B, int32_t Sq, int32_t Sk, int32_t H);
 
@@ -147,7 +151,9 @@ int h3attn_forward(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint
  * separately or prepare k/v once and attend several times.
  *   stages & H3ATTN_STAGE_PREPARE: the prologue on q and k and the key-major
  *     copy of v, written into the workspace (all other tensors read only).
- *   stages & H3ATTN_STAGE_ATTEND: attention from the prepared workspace into o.
+ *   stages & H3ATTN_STAGE_ATTEND: attention from the prepared workspace into o
+ *     (one kernel, plus a second that merges split tiles when the schedule
+ *     splits any).
  * Arguments and errors are those of h3attn_forward; stages must be 1, 2 or 3
  * (else BAD_VALUE). A call with only H3ATTN_STAGE_ATTEND must follow, in
  * stream order, a PREPARE call with the same sizes, valid lengths and

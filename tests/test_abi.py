@@ -52,8 +52,15 @@ def test_status_strings(lib):
 
 def test_workspace_bytes(lib):
     # q, k, v each padded to 256 rows, bf16, 128 channels
-    assert lib.h3attn_forward_workspace_bytes(1, 104448, 104448, 6) == 6 * 104448 * 256 * 3
-    assert lib.h3attn_forward_workspace_bytes(2, 1000, 300, 3) == 6 * (1024 + 2 * 512) * 256
+    # q, k and v^T rows padded to 256, 256 bytes each, then partial records
+    # for split tiles: 2 per split block, blocks = min(256, tiles*steps/16)
+    # with 256-row tiles and 32-key steps; a record is (64 + 2) x 512 floats.
+    rec = (64 + 2) * 512 * 4
+    assert lib.h3attn_forward_workspace_bytes(1, 104448, 104448, 6) == 6 * 104448 * 256 * 3 + 2 * 256 * rec
+    # 6 heads x 4 tiles x 10 steps = 240 steps -> 15 blocks
+    assert lib.h3attn_forward_workspace_bytes(2, 1000, 300, 3) == 6 * (1024 + 2 * 512) * 256 + 2 * 15 * rec
+    # 1 tile x 1 step: no split blocks
+    assert lib.h3attn_forward_workspace_bytes(1, 1, 1, 1) == 3 * 256 * 256
     assert lib.h3attn_forward_workspace_bytes(0, 1, 1, 1) == 0
     assert lib.h3attn_forward_workspace_bytes(1, -5, 1, 1) == 0
 

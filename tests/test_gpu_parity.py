@@ -184,6 +184,43 @@ def test_forward_ragged(h3, B, Sq, Sk, H, qv, kvv, norm, rope):
     assert np.all(got[:, qv:] == 0)
 
 
+# Shapes whose valid query tiles (256 rows each) leave the last round of a
+# 256-CU device partly empty, so the launcher splits those tiles' 32-key steps
+# over more workgroups than tiles (each covering at most two tiles) and a
+# second kernel merges their partial results. Checked against the full oracle.
+SPLIT = [
+    # B, Sq, Sk, H, q_valid, kv_valid
+    (1, 3000, 3000, 3, 3000, 3000),   # 36 tiles over 211 blocks; ranges cross tile ends; masked last step
+    (2, 4000, 3500, 2, 3500, 3333),   # partly valid query tiles, plus tiles that only write zeros
+    (1, 2100, 1200, 1, 2100, 1100),   # 35 steps per tile, ~17 per block: most blocks span two tiles
+]
+
+
+@pytest.mark.parametrize("B,Sq,Sk,H,qv,kvv", SPLIT)
+def test_forward_split_tiles(h3, B, Sq, Sk, H, qv, kvv):
+    say("split", B, Sq, Sk, H, qv, kvv)
+    inp = workloads.make_inputs(B, Sq, Sk, H, seed=Sq * 3 + Sk)
+    got = run_forward(h3, None, inp, qv, kvv, True, True)
+    ref = oracle.forward(inp.q, inp.k, inp.v, inp.w_q, inp.w_k, 1e-6, 1e4, 1 / math.sqrt(128), qv, kvv)
+    check(oracle.compare(got, ref), "split")
+    assert np.all(got[:, qv:] == 0)
+
+
+def test_forward_whole_and_split_tiles(h3):
+    """260 valid tiles: 256 run whole in the first round and the last 4 (rows
+    15616.. of head 3) are split over 130 workgroups. Sampled rows cover both
+    kinds, all heads."""
+    B, S, H = 1, 16640, 4
+    say("whole+split", B, S, H)
+    inp = workloads.make_inputs(B, S, S, H, seed=41)
+    got = run_forward(h3, None, inp, S, S, True, True)
+    rng = np.random.default_rng(41)
+    rows = np.unique(np.concatenate([rng.choice(15616, 48, replace=False),
+                                     15616 + rng.choice(S - 15616, 48, replace=False), [0, 15615, 15616, S - 1]]))
+    ref = oracle.forward(inp.q, inp.k, inp.v, inp.w_q, inp.w_k, 1e-6, 1e4, 1 / math.sqrt(128), S, S, rows=rows)
+    check(oracle.compare(got[:, rows], ref), f"whole+split ({len(rows)} rows)")
+
+
 # ---------------------------------------------------------------------- invariants
 
 def test_single_valid_key_returns_its_value_exactly(h3):
@@ -243,9 +280,9 @@ def test_permutation_of_keys_and_values(h3):
 
 @pytest.mark.parametrize("S,H,qv,kvv", [(2048, 4, 2000, 1999), (8192, 8, 8192, 8192)])
 def test_repeat_runs_are_bitwise_identical(h3, S, H, qv, kvv):
-    """No atomics and no races: repeated runs agree bit for bit. (Two workgroups
-    per CU at 8192x8 exercise the LDS ring and the matrix-core result hazards
-    under contention.)"""
+    """No atomics and no races: repeated runs agree bit for bit. (2048x4 splits
+    its tiles and merges partial results; 8192x8 fills every CU with whole
+    tiles, two waves per SIMD contending for the LDS ring and matrix cores.)"""
     inp = workloads.make_inputs(1, S, S, H, seed=38)
     a = run_forward(h3, None, inp, qv, kvv, True, True)
     for _ in range(3):

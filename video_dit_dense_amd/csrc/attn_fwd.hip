@@ -35,6 +35,14 @@
 // ahead; one barrier per step publishes them. The loads use a buffer
 // resource held in scalar registers, so they cost no vector instructions.
 //
+// Chip schedule. A workgroup owns one (b, h, 256-row query block) tile and
+// one CU, so tiles run in rounds of one per CU. When the last round is only
+// partly full, its tiles are not run whole: their 32-key steps are divided
+// evenly over up to one workgroup per CU, each workgroup writes an fp32
+// partial result (un-normalised accumulator, running max, row sum) per tile
+// it touches, and attn_merge_kernel combines them. Tiles wholly past q_valid
+// only write zeros.
+//
 // Exponent arithmetic. q arrives pre-multiplied by softmax_scale*log2(e)
 // (applied in fp32 by the prologue before its single bf16 rounding), so
 // scores leave the matrix core in exp2 units. Each row keeps an offset m
@@ -48,6 +56,8 @@
 //   vt [B*H][Sk_pad/32][128][32]   vt[.., x, d, p] = v[key 32x + sigma(p)][d], zero past kv_valid
 #include "h3attn_internal.h"
 
+#include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 namespace h3 {
@@ -114,6 +124,38 @@ constexpr int kBufBytes = kKBytes + kVBytes;   // 16 KB per ring slot
 //   K:   row r (key), 16-byte chunk c (channels 8c..8c+7) at r*256 + (c ^ (r & 15))*16
 //   V^T: row d (channel), chunk c (positions 8c..8c+7) at d*64 + (c ^ ((d >> 2) & 3))*16
 
+// Blocks are dispatched round-robin over the 8 XCDs, so block i of a range
+// of n runs on XCD i%8. This bijection gives each XCD a contiguous run of
+// work items (same head, neighbouring query blocks or steps), so its L2
+// serves one head's K/V stream.
+__device__ inline int xcd_order(int i, int n) {
+  const int xcd = i & 7;
+  const int per = n >> 3, rem = n & 7;
+  return xcd * per + min(xcd, rem) + (i >> 3);
+}
+
+// Writes this lane's query row of a finished tile: o = acc * inv rounded to
+// bf16, or +0.0 for rows at or past q_valid. Lane (l, register r of acc[dt])
+// holds channel dt*32 + 8*(r/4) + 4*(l/32) + r%4 of query row l%32.
+__device__ inline void store_row(const AttnArgs& a, uint16_t* obase, int q, int g, const f32x16_t* acc,
+                                 float inv) {
+  if (q >= a.Sq) return;
+  uint16_t* op = obase + q * ((int64_t)a.H * 128);
+  const bool live = q < a.q_valid;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      const int d0 = dt * 32 + rq * 8 + g * 4;
+      uint2 val = make_uint2(0u, 0u);
+      if (live) {
+        val.x = pack_bf16x2(acc[dt][rq * 4 + 0] * inv, acc[dt][rq * 4 + 1] * inv);
+        val.y = pack_bf16x2(acc[dt][rq * 4 + 2] * inv, acc[dt][rq * 4 + 3] * inv);
+      }
+      *reinterpret_cast<uint2*>(op + d0) = val;
+    }
+}
+
 template <int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(AttnArgs a) {
@@ -130,26 +172,49 @@ void attn_fwd_kernel(AttnArgs a) {
   const int lq = lane & 31;
   const int g = lane >> 5;
 
-  // Tile order: blocks are dispatched round-robin over the 8 XCDs, so block
-  // `bid` runs on XCD bid%8. Give each XCD a contiguous range of tiles (same
-  // head, neighbouring query blocks) so its L2 serves one head's K/V stream.
   const int n_qblocks = (a.Sq + BM - 1) / BM;
-  const int n_tiles = a.B * a.H * n_qblocks;
+  const int NU = (a.kv_valid + kSub - 1) / kSub;     // sub-tiles with at least one valid key
+  const int last_valid = a.kv_valid - 1;
+  const bool tail_partial = (a.kv_valid % kSub) != 0;
   const int bid = blockIdx.x;
-  const int xcd = bid & 7;
-  const int per = n_tiles >> 3, rem = n_tiles & 7;
-  const int tile = xcd * per + min(xcd, rem) + (bid >> 3);
-  const int bh = tile / n_qblocks;
-  const int qb = tile - bh * n_qblocks;
-  const int b = bh / a.H;
-  const int h = bh - b * a.H;
-  const int q0 = qb * BM;
 
-  const int64_t orow = (int64_t)a.H * 128;
-  uint16_t* obase = a.o + ((int64_t)b * a.Sq * a.H + h) * 128;
-
-  if (q0 >= a.q_valid) {
-    // Whole block lies in the invalid tail: zero rows [q0, min(q0+BM, Sq)).
+  // This block's work: one or two segments, each a valid tile g and its
+  // sub-tiles [xb, xe), finished either into o (rec < 0) or into partial
+  // record rec.
+  int g0, xb0, xe0, rec0, g1 = 0, xb1 = 0, xe1 = 0, rec1 = -1, nseg = 1;
+  if (bid < a.n_whole) {
+    g0 = xcd_order(bid, a.n_whole);
+    xb0 = 0;
+    xe0 = NU;
+    rec0 = -1;
+  } else if (bid < a.n_whole + a.n_split_blocks) {
+    // Split tiles: of the U = n_split*NU steps of tiles n_whole.., block j
+    // takes [j*U/n, (j+1)*U/n) with n = n_split_blocks > n_split, so at most
+    // NU steps and at most two tiles.
+    const int j = xcd_order(bid - a.n_whole, a.n_split_blocks);
+    const int64_t U = (int64_t)a.n_split * NU;
+    const int64_t s0 = (int64_t)j * U / a.n_split_blocks;
+    const int64_t s1 = (int64_t)(j + 1) * U / a.n_split_blocks;
+    const int t = (int)(s0 / NU);
+    g0 = a.n_whole + t;
+    xb0 = (int)(s0 - (int64_t)t * NU);
+    xe0 = (int)min<int64_t>(NU, s1 - (int64_t)t * NU);
+    rec0 = 2 * j;
+    if (s1 > (int64_t)(t + 1) * NU) {
+      nseg = 2;
+      g1 = g0 + 1;
+      xe1 = (int)(s1 - (int64_t)(t + 1) * NU);
+      rec1 = 2 * j + 1;
+    }
+  } else {
+    // A tile wholly past q_valid: zero rows [q0, min(q0 + BM, Sq)).
+    const int nqz = n_qblocks - a.nqv;
+    const int z = bid - a.n_whole - a.n_split_blocks;
+    const int bh = z / nqz;
+    const int q0 = (a.nqv + (z - bh * nqz)) * BM;
+    const int b = bh / a.H, h = bh - b * a.H;
+    uint16_t* obase = a.o + ((int64_t)b * a.Sq * a.H + h) * 128;
+    const int64_t orow = (int64_t)a.H * 128;
     for (int idx = tid; idx < BM * 16; idx += NW * 64) {
       const int q = q0 + (idx >> 4);
       if (q < a.Sq) *reinterpret_cast<u32x4_t*>(obase + q * orow + (idx & 15) * 8) = u32x4_t{0u, 0u, 0u, 0u};
@@ -157,8 +222,19 @@ void attn_fwd_kernel(AttnArgs a) {
     return;
   }
 
-  const int NU = (a.kv_valid + kSub - 1) / kSub;     // sub-tiles with at least one valid key
-  const int last_valid = a.kv_valid - 1;
+#pragma nounroll
+  for (int si = 0; si < nseg; ++si) {
+  const int tg = si ? g1 : g0;
+  const int xb = si ? xb1 : xb0;
+  const int xe = si ? xe1 : xe0;
+  const int rec = si ? rec1 : rec0;
+  const int NS = xe - xb;                         // sub-tiles in this segment, >= 1
+  const bool mask_end = tail_partial && xe == NU; // the segment ends with the partial sub-tile
+  const int bh = tg / a.nqv;
+  const int q0 = (tg - bh * a.nqv) * BM;
+  const int b = bh / a.H;
+  const int h = bh - b * a.H;
+  uint16_t* obase = a.o + ((int64_t)b * a.Sq * a.H + h) * 128;
 
   // Per-lane byte offsets of the direct loads within a sub-tile (K and V^T
   // sub-tiles are contiguous 8 KB blocks in the workspace). The lane that
@@ -186,7 +262,7 @@ void attn_fwd_kernel(AttnArgs a) {
   // lands in a ring slot that no later step reads.
   auto issue_loads = [&](int x) {
     uint8_t* slot = lds + (x & (kNBuf - 1)) * kBufBytes;
-    const bool live = x < NU;
+    const bool live = x < xe;
     const uint16_t* kx = kw + (int64_t)(live ? x : 0) * (kSub * 128);
     const uint16_t* vx = vt + (int64_t)(live ? x : 0) * (kSub * 128);
 #pragma unroll
@@ -203,9 +279,9 @@ void attn_fwd_kernel(AttnArgs a) {
   for (int ks = 0; ks < 2; ++ks) vaddr[ks] = kKBytes + lq * 64 + ((((2 * ks) | g) ^ ((lq >> 2) & 3)) * 16);
 
   // Issue the first three sub-tiles, then load Q while they fly.
-  issue_loads(0);
-  if (NU > 1) issue_loads(1);
-  if (NU > 2) issue_loads(2);
+  issue_loads(xb);
+  if (NS > 1) issue_loads(xb + 1);
+  if (NS > 2) issue_loads(xb + 2);
 
   // Q fragments (B operand of S^T = K Q^T): lane holds query row lq of this
   // wave, channels 16*kk + 8*g .. +7.
@@ -316,7 +392,7 @@ void attn_fwd_kernel(AttnArgs a) {
   //   phase B: PV of sub-tile u alongside the row maxima of sub-tile u+1.
   f32x16_t s_cur;
   auto step = [&](int u, auto mask_next) {
-    if (u + 2 < NU)
+    if (u + 2 < xe)
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LDPS) : "memory");
     else
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -360,9 +436,9 @@ void attn_fwd_kernel(AttnArgs a) {
 
   // Sub-tile 0: scores and max before the pipeline starts. Its loads are the
   // oldest; sub-tiles 1 and 2 may still be in flight.
-  if (NU > 2)
+  if (NS > 2)
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LDPS) : "memory");
-  else if (NU > 1)
+  else if (NS > 1)
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LDPS) : "memory");
   else
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -373,11 +449,10 @@ void attn_fwd_kernel(AttnArgs a) {
     f32x16_t zero;
 #pragma unroll
     for (int r = 0; r < 16; ++r) zero[r] = 0.f;
-    s_cur = qk(0, zero);
+    s_cur = qk(xb, zero);
   }
-  const bool tail_partial = (a.kv_valid % kSub) != 0;
   {
-    const float mx0 = (NU == 1 && tail_partial) ? rowmax(s_cur, 0, Mask{}) : rowmax(s_cur, 0, NoMask{});
+    const float mx0 = (NS == 1 && mask_end) ? rowmax(s_cur, xb, Mask{}) : rowmax(s_cur, xb, NoMask{});
     m_run = max_lane_pair(mx0);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -387,40 +462,89 @@ void attn_fwd_kernel(AttnArgs a) {
   }
 
   // Steady state: the next sub-tile is never the masked last one.
-  for (int u = 0; u < NU - 2; ++u) step(u, NoMask{});
-  if (NU >= 2) {
-    if (tail_partial)
-      step(NU - 2, Mask{});
+  for (int u = xb; u < xe - 2; ++u) step(u, NoMask{});
+  if (NS >= 2) {
+    if (mask_end)
+      step(xe - 2, Mask{});
     else
-      step(NU - 2, NoMask{});
+      step(xe - 2, NoMask{});
   }
+  // The last steps issued empty-range refills; let them retire so no LDS
+  // write is pending when the workgroup ends and its LDS is handed on.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   {
     // Last sub-tile: exponentials and PV only.
     bf16x8_t pf[2];
     probs(s_cur, pf);
-    pv(NU - 1, pf);
+    pv(xe - 1, pf);
     l_run += psum(pf);
   }
 
-  const float lsum = sum_lane_pair(l_run);
-  const float inv = 1.0f / lsum;
-  const int q = q0 + wave * 32 + lq;
-  if (q < a.Sq) {
-    uint16_t* op = obase + q * orow;
-    const bool live = q < a.q_valid;
+  if (rec < 0) {
+    store_row(a, obase, q0 + wave * 32 + lq, g, acc, 1.0f / sum_lane_pair(l_run));
+  } else {
+    // Partial record: acc register r at [r][thread], then m_run and l_run.
+    float* pr = a.part + (int64_t)rec * kPartFloats + tid;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const int d0 = dt * 32 + rq * 8 + g * 4;
-        uint2 val = make_uint2(0u, 0u);
-        if (live) {
-          val.x = pack_bf16x2(acc[dt][rq * 4 + 0] * inv, acc[dt][rq * 4 + 1] * inv);
-          val.y = pack_bf16x2(acc[dt][rq * 4 + 2] * inv, acc[dt][rq * 4 + 3] * inv);
-        }
-        *reinterpret_cast<uint2*>(op + d0) = val;
-      }
+      for (int r = 0; r < 16; ++r) pr[(dt * 16 + r) * (NW * 64)] = acc[dt][r];
+    pr[64 * (NW * 64)] = m_run;
+    pr[65 * (NW * 64)] = l_run;
   }
+  if (si + 1 < nseg) __syncthreads();   // the next segment refills the LDS ring
+  }
+}
+
+// Merge of a split tile t (tile n_whole + t): the blocks whose step ranges
+// meet the tile each left one partial record (O_i, m_i, l_i) with O_i and l_i
+// relative to their own offset m_i; with M = max m_i the tile's result is
+// sum 2^(m_i - M) O_i / sum 2^(m_i - M) l_i (scores are in exp2 units).
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void attn_merge_kernel(AttnArgs a) {
+  constexpr int BM = NW * 32;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int t = blockIdx.x;
+  const int NU = (a.kv_valid + kSub - 1) / kSub;
+  const int tg = a.n_whole + t;
+  const int bh = tg / a.nqv;
+  const int q0 = (tg - bh * a.nqv) * BM;
+  const int b = bh / a.H;
+  const int h = bh - b * a.H;
+  uint16_t* obase = a.o + ((int64_t)b * a.Sq * a.H + h) * 128;
+
+  // Block j covers steps [j*U/n, (j+1)*U/n), so step x lies in block
+  // floor(((x + 1) * n - 1) / U); its record for tile t is 2j + (t - first
+  // tile of block j).
+  const int n = a.n_split_blocks;
+  const int64_t U = (int64_t)a.n_split * NU;
+  const int64_t x0 = (int64_t)t * NU, x1 = x0 + NU - 1;
+  const int j0 = (int)(((x0 + 1) * n - 1) / U);
+  const int j1 = (int)(((x1 + 1) * n - 1) / U);
+  auto record = [&](int j) {
+    const int first = (int)(((int64_t)j * U / n) / NU);
+    return a.part + (int64_t)(2 * j + (t - first)) * kPartFloats + tid;
+  };
+  float M = -INFINITY;
+  for (int j = j0; j <= j1; ++j) M = fmaxf(M, record(j)[64 * (NW * 64)]);
+  f32x16_t acc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
+  float l = 0.f;
+  for (int j = j0; j <= j1; ++j) {
+    const float* pr = record(j);
+    const float w = __builtin_amdgcn_exp2f(pr[64 * (NW * 64)] - M);
+    l += w * pr[65 * (NW * 64)];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[dt][r] += w * pr[(dt * 16 + r) * (NW * 64)];
+  }
+  store_row(a, obase, q0 + wave * 32 + (lane & 31), lane >> 5, acc, 1.0f / sum_lane_pair(l));
 }
 
 // Transposed, key-blocked copy of v for the PV operand: a block moves 64 keys
@@ -467,12 +591,59 @@ __global__ __launch_bounds__(256) void v_relayout_kernel(const uint16_t* __restr
 
 }  // namespace
 
-hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
-  constexpr int NW = 8;
-  constexpr int BM = NW * 32;
-  const int64_t n_tiles = (int64_t)a.B * a.H * ((a.Sq + BM - 1) / BM);
-  if (n_tiles > 0x7fffffffLL) return hipErrorInvalidValue;
-  attn_fwd_kernel<NW><<<dim3((unsigned)n_tiles), NW * 64, 0, stream>>>(a);
+namespace {
+
+// Compute units of the current device (cached per device; 0 if unknown).
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+}  // namespace
+
+hipError_t launch_attention(AttnArgs a, hipStream_t stream) {
+  constexpr int NW = kAttnWaves;
+  constexpr int BM = kAttnRows;
+  static_assert(BM == NW * 32 && kAttnSub == kSub, "tiling constants");
+  const int64_t nq = (a.Sq + BM - 1) / BM;
+  const int64_t nqv = (a.q_valid + BM - 1) / BM;
+  const int64_t n_valid = (int64_t)a.B * a.H * nqv;
+  const int64_t n_zero = (int64_t)a.B * a.H * (nq - nqv);
+  const int64_t NU = (a.kv_valid + kSub - 1) / kSub;
+  // One tile per CU at a time: the last round holds n_valid % cus tiles. When
+  // that round is partial, split its tiles' steps over more blocks (at most
+  // one per CU, each at least kSplitMinSteps steps, and more blocks than
+  // tiles so no block spans more than two tiles).
+  int64_t n_whole = n_valid, n_split = 0, n_blocks = 0;
+  const int64_t cus = std::min<int64_t>(device_cus(), kSplitMaxBlocks);
+  if (cus > 0) {
+    const int64_t r = n_valid % cus;
+    const int64_t blocks = std::min<int64_t>({cus, r * NU / kSplitMinSteps, a.part_slots / 2});
+    if (r > 0 && blocks > r) {
+      n_whole = n_valid - r;
+      n_split = r;
+      n_blocks = blocks;
+    }
+  }
+  const int64_t grid = n_whole + n_blocks + n_zero;
+  if (grid > 0x7fffffffLL || nqv > 0x7fffffffLL) return hipErrorInvalidValue;
+  a.nqv = (int32_t)nqv;
+  a.n_whole = (int32_t)n_whole;
+  a.n_split = (int32_t)n_split;
+  a.n_split_blocks = (int32_t)n_blocks;
+  if (grid > 0) attn_fwd_kernel<NW><<<dim3((unsigned)grid), NW * 64, 0, stream>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || n_split == 0) return e;
+  attn_merge_kernel<NW><<<dim3((unsigned)n_split), NW * 64, 0, stream>>>(a);
   return hipGetLastError();
 }
 

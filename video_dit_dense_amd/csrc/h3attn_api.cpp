@@ -73,8 +73,8 @@ int check_prologue_args(int32_t Sq, int32_t Sk, const float* wq, const float* wk
 }
 
 struct WorkspaceLayout {
-  int64_t Sq_pad, Sk_pad;
-  size_t q_off, k_off, v_off, total;
+  int64_t Sq_pad, Sk_pad, part_slots;
+  size_t q_off, k_off, v_off, part_off, total;
 };
 
 bool workspace_layout(int32_t B, int32_t Sq, int32_t Sk, int32_t H, WorkspaceLayout* w) {
@@ -84,11 +84,14 @@ bool workspace_layout(int32_t B, int32_t Sq, int32_t Sk, int32_t H, WorkspaceLay
   const unsigned __int128 bh = (unsigned __int128)B * (unsigned __int128)H;
   const unsigned __int128 qb = bh * (unsigned __int128)w->Sq_pad * 256u;
   const unsigned __int128 kb = bh * (unsigned __int128)w->Sk_pad * 256u;
-  const unsigned __int128 tot = qb + 2 * kb;
+  w->part_slots = h3::split_part_slots(B, Sq, Sk, H);
+  const unsigned __int128 pb = (unsigned __int128)w->part_slots * h3::kPartBytes;
+  const unsigned __int128 tot = qb + 2 * kb + pb;
   if (tot > (unsigned __int128)(INT64_MAX / 4)) return false;
   w->q_off = 0;
   w->k_off = (size_t)qb;
   w->v_off = (size_t)(qb + kb);
+  w->part_off = (size_t)(qb + 2 * kb);
   w->total = (size_t)tot;
   return true;
 }
@@ -238,6 +241,8 @@ H3_API int h3attn_forward_stages(const uint16_t* q, const uint16_t* k, const uin
   a.kw = kw;
   a.vt = vt;
   a.o = o;
+  a.part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + wl.part_off);
+  a.part_slots = wl.part_slots;
   a.B = B;
   a.H = H;
   a.Sq = Sq;

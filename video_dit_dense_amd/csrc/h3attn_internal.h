@@ -58,14 +58,49 @@ hipError_t launch_v_relayout(const uint16_t* v, uint16_t* vt, int32_t B, int32_t
 hipError_t launch_rope_tables(float* cos_out, float* sin_out, int32_t rows, double theta,
                               hipStream_t stream);
 
+// Attention tiling: a workgroup of kAttnWaves waves owns kAttnRows query rows
+// of one (b, h) and walks the keys in kAttnSub-key sub-tiles.
+constexpr int kAttnWaves = 8;
+constexpr int kAttnRows = kAttnWaves * 32;
+constexpr int kAttnSub = 32;
+
+// Load balancing of the last, partial round of query tiles (stream-K): those
+// tiles' sub-tile steps are split evenly over up to kSplitMaxBlocks
+// workgroups, each taking at least kSplitMinSteps steps and touching at most
+// two tiles; each writes one partial record per tile it touches and a second
+// kernel merges them. A record holds the un-normalised fp32 accumulator (64
+// values per lane) plus the lane's running max and partial row sum.
+constexpr int kSplitMaxBlocks = 256;
+constexpr int kSplitMinSteps = 16;
+constexpr int kPartFloats = (64 + 2) * kAttnWaves * 64;
+constexpr size_t kPartBytes = sizeof(float) * kPartFloats;
+
+// Partial records the forward workspace reserves for these sizes: two per
+// split workgroup, for the largest split the launcher can choose.
+inline int64_t split_part_slots(int32_t B, int32_t Sq, int32_t Sk, int32_t H) {
+  const int64_t tiles = (int64_t)B * H * ((Sq + kAttnRows - 1) / kAttnRows);
+  const int64_t steps = tiles * ((Sk + kAttnSub - 1) / kAttnSub);
+  const int64_t blocks = steps / kSplitMinSteps < kSplitMaxBlocks ? steps / kSplitMinSteps : kSplitMaxBlocks;
+  return 2 * blocks;
+}
+
 struct AttnArgs {
   const uint16_t* qw;      // [B*H][Sq_pad][128] scaled by softmax_scale*log2(e), rows >= q_valid zero
   const uint16_t* kw;      // [B*H][Sk_pad][128], rows >= kv_valid are zero
   const uint16_t* vt;      // [B*H][Sk_pad/32][128][32], see attn_fwd.hip; keys >= kv_valid zero
   uint16_t* o;             // [B][Sq][H][128]
+  float* part;             // partial records for split tiles
+  int64_t part_slots;      // records available at part
   int32_t B, H, Sq, Sq_pad, Sk_pad, q_valid, kv_valid;
+  // Schedule, filled in by launch_attention: valid tiles (query block below
+  // q_valid) are numbered g = (b*H + h) * nqv + query block; tiles g < n_whole
+  // run whole, the n_split tiles after them are split over n_split_blocks
+  // workgroups; tiles past q_valid only write zeros.
+  int32_t nqv, n_whole, n_split, n_split_blocks;
 };
 
-hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);
+// Enqueues the attention kernel (and, when the schedule splits tiles, the
+// merge of their partial records) on `stream`.
+hipError_t launch_attention(AttnArgs a, hipStream_t stream);
 
 }  // namespace h3

@@ -23,17 +23,25 @@
 //   B (16 x 32): lane l supplies column l%32, k = 8*(l/32) .. +7
 //   D (32 x 32): lane l register r holds row 8*(r/4) + 4*(l/32) + r%4, col l%32
 //
-// Schedule. Keys are processed in 32-key sub-tiles u. Step u reads all 16
-// operand fragments it needs from LDS, then interleaves QK^T of sub-tile u+1
-// with the exponentials of sub-tile u, then PV of sub-tile u with the row
-// maxima of sub-tile u+1, so the matrix core and the vector ALU work on
-// independent data within one wave. A workgroup is eight waves (256 query
-// rows, one workgroup per CU), so each SIMD runs two waves that fill each
-// other's gaps and every K/V byte brought into LDS serves 256 queries.
-// Sub-tiles land in a ring of four LDS buffers through direct buffer->LDS
-// loads (one per wave for K and one for V per sub-tile) issued three steps
-// ahead; one barrier per step publishes them. The loads use a buffer
-// resource held in scalar registers, so they cost no vector instructions.
+// Schedule. A workgroup is eight waves (256 query rows), one workgroup per
+// CU, so every SIMD runs two waves and each K/V byte brought into LDS serves
+// 256 queries. Keys are processed in 32-key sub-tiles u, and step u is split
+// by workgroup barriers into two phases:
+//   X: matrix-core work only: QK^T of sub-tile u+1 and PV of sub-tile u,
+//      all operands already in registers;
+//   Y: vector and LDS work: the row maxima of u+1, the exponentials and row
+//      sums that turn them into the PV operand, the LDS reads of the next
+//      X phase's fragments and one ring refill.
+// The two waves of a SIMD run the phases in opposition (the second passes
+// one extra barrier first), so while one feeds the matrix core the other does
+// the softmax: a ping-pong. Both run the same instructions in the same
+// order, so the result does not depend on which wave runs which phase.
+// Sub-tiles land in an eight-slot LDS ring (128 KB) through direct
+// buffer->LDS loads issued up to seven sub-tiles ahead; the loads use a
+// buffer resource held in scalar registers, so they cost no vector
+// instructions. The chip runs this kernel at its power limit, so every
+// vector instruction and LDS byte per step costs clock: the step keeps them
+// few.
 //
 // Chip schedule. A workgroup owns one (b, h, 256-row query block) tile and
 // one CU, so tiles run in rounds of one per CU. When the last round is only
@@ -45,10 +53,7 @@
 //
 // Exponent arithmetic. q arrives pre-multiplied by softmax_scale*log2(e)
 // (applied in fp32 by the prologue before its single bf16 rounding), so
-// scores leave the matrix core in exp2 units. Each row keeps an offset m
-// (its running maximum, raised lazily), and the QK^T accumulation starts
-// from -m instead of 0, so p = exp2(score) needs no per-element arithmetic
-// before the exponential.
+// scores leave the matrix core in exp2 units and p = exp2(s - m).
 //
 // Workspace layouts read here (written by the prologue and the relayout):
 //   qw [B*H][Sq_pad][128]          rows >= q_valid zero
@@ -82,7 +87,6 @@ __device__ __forceinline__ void load_lds16(const void* base, int bytes, int byte
       byte_off, 0, 0, 0);
 }
 
-
 __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
   bf16x2_t v = {(__bf16)lo, (__bf16)hi};
   return __builtin_bit_cast(uint32_t, v);
@@ -106,7 +110,7 @@ __device__ inline float sum_lane_pair(float x) {
   return __builtin_bit_cast(float, (uint32_t)sw[0]) + __builtin_bit_cast(float, (uint32_t)sw[1]);
 }
 
-// Lazy rescaling: the running max m used in p = exp2(s*c - m) is only raised
+// Lazy rescaling: the running max m used in p = exp2(s - m) is only raised
 // when a score exceeds it by more than 2^kRescaleLog2 (in the exp2 domain), so
 // p <= 2^8 and the fp32 accumulator is rescaled only a handful of times per
 // row. The result o = O / l does not depend on m; bf16 rounding of p is
@@ -114,7 +118,7 @@ __device__ inline float sum_lane_pair(float x) {
 constexpr float kRescaleLog2 = 8.0f;
 
 constexpr int kSub = 32;                       // keys per sub-tile
-constexpr int kNBuf = 4;                       // LDS ring depth (sub-tiles)
+constexpr int kRing = 8;                       // LDS ring depth (sub-tiles)
 constexpr int kKBytes = kSub * 256;            // K sub-tile: 32 rows x 256 B
 constexpr int kVBytes = 128 * kSub * 2;        // V^T sub-tile: 128 rows x 64 B
 constexpr int kBufBytes = kKBytes + kVBytes;   // 16 KB per ring slot
@@ -134,9 +138,9 @@ __device__ inline int xcd_order(int i, int n) {
   return xcd * per + min(xcd, rem) + (i >> 3);
 }
 
-// Writes this lane's query row of a finished tile: o = acc * inv rounded to
-// bf16, or +0.0 for rows at or past q_valid. Lane (l, register r of acc[dt])
-// holds channel dt*32 + 8*(r/4) + 4*(l/32) + r%4 of query row l%32.
+// Writes one query row of a finished tile: o = acc * inv rounded to bf16, or
+// +0.0 for rows at or past q_valid. Lane (l, register r of acc[dt]) holds
+// channel dt*32 + 8*(r/4) + 4*(l/32) + r%4 of its row.
 __device__ inline void store_row(const AttnArgs& a, uint16_t* obase, int q, int g, const f32x16_t* acc,
                                  float inv) {
   if (q >= a.Sq) return;
@@ -156,15 +160,32 @@ __device__ inline void store_row(const AttnArgs& a, uint16_t* obase, int q, int 
     }
 }
 
+// Partial record of a split tile, per thread t of the T-thread workgroup
+// (fp32, thread-contiguous so every access is coalesced): accumulator
+// register r at [r * T + t], then the row offset m at [64 * T + t] and this
+// lane's row-sum share at [65 * T + t].
+constexpr int kRecM = 64, kRecL = 65;
+
+// Workgroup barrier without a memory fence: the callers order LDS traffic
+// through the ring schedule and their own vmcnt waits. The "memory" clobber
+// keeps the compiler from moving memory operations across it.
+__device__ __forceinline__ void bar() { asm volatile("s_barrier" ::: "memory"); }
+
 template <int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(AttnArgs a) {
   constexpr int BM = NW * 32;
+  constexpr int T = NW * 64;
   constexpr int KLD = kKBytes / 1024 / NW;     // 1 KB direct loads per wave per sub-tile (K)
   constexpr int VLD = kVBytes / 1024 / NW;     // (V)
   constexpr int LDPS = KLD + VLD;              // load instructions per wave per sub-tile
   static_assert(KLD * NW * 1024 == kKBytes && VLD * NW * 1024 == kVBytes, "tile split");
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kNBuf * kBufBytes];
+  static_assert(kPartFloats == 66 * T, "partial record size");
+  // One LDS object only: the ring, then the per-wave SIMD ids. (With a
+  // second LDS variable the compiler can no longer tell fragment reads from
+  // the ring's DMA writes and waits for every load in flight before each.)
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kRing * kBufBytes + NW * sizeof(int)];
+  int* simd_of = reinterpret_cast<int*>(lds + kRing * kBufBytes);
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -172,10 +193,21 @@ void attn_fwd_kernel(AttnArgs a) {
   const int lq = lane & 31;
   const int g = lane >> 5;
 
+  // Role of this wave among the waves that share its SIMD (HW_ID bits 5:4
+  // name the SIMD): the second one of each SIMD runs one phase behind.
+  if (lane == 0) simd_of[wave] = (int)(__builtin_amdgcn_s_getreg((1 << 11) | (4 << 6) | 4) & 3);
+  __syncthreads();
+  int role = 0;
+  {
+    const int mine = simd_of[wave];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) role += (w < wave && simd_of[w] == mine) ? 1 : 0;
+    role = __builtin_amdgcn_readfirstlane(role & 1);
+  }
+
   const int n_qblocks = (a.Sq + BM - 1) / BM;
   const int NU = (a.kv_valid + kSub - 1) / kSub;     // sub-tiles with at least one valid key
   const int last_valid = a.kv_valid - 1;
-  const bool tail_partial = (a.kv_valid % kSub) != 0;
   const int bid = blockIdx.x;
 
   // This block's work: one or two segments, each a valid tile g and its
@@ -215,12 +247,20 @@ void attn_fwd_kernel(AttnArgs a) {
     const int b = bh / a.H, h = bh - b * a.H;
     uint16_t* obase = a.o + ((int64_t)b * a.Sq * a.H + h) * 128;
     const int64_t orow = (int64_t)a.H * 128;
-    for (int idx = tid; idx < BM * 16; idx += NW * 64) {
+    for (int idx = tid; idx < BM * 16; idx += T) {
       const int q = q0 + (idx >> 4);
       if (q < a.Sq) *reinterpret_cast<u32x4_t*>(obase + q * orow + (idx & 15) * 8) = u32x4_t{0u, 0u, 0u, 0u};
     }
     return;
   }
+
+  // Per-lane LDS byte addresses of the matrix-core operand reads. K fragment
+  // kk of a sub-tile is at kbase ^ (32 kk) (the swizzle only touches address
+  // bits 4..7 and 32 kk only bits 5..7), so one register serves all eight.
+  const uint32_t kbase = lq * 256 + ((g ^ (lq & 15)) * 16);
+  uint32_t vaddr[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) vaddr[ks] = kKBytes + lq * 64 + ((((2 * ks) | g) ^ ((lq >> 2) & 3)) * 16);
 
 #pragma nounroll
   for (int si = 0; si < nseg; ++si) {
@@ -228,13 +268,21 @@ void attn_fwd_kernel(AttnArgs a) {
   const int xb = si ? xb1 : xb0;
   const int xe = si ? xe1 : xe0;
   const int rec = si ? rec1 : rec0;
-  const int NS = xe - xb;                         // sub-tiles in this segment, >= 1
-  const bool mask_end = tail_partial && xe == NU; // the segment ends with the partial sub-tile
   const int bh = tg / a.nqv;
   const int q0 = (tg - bh * a.nqv) * BM;
   const int b = bh / a.H;
   const int h = bh - b * a.H;
   uint16_t* obase = a.o + ((int64_t)b * a.Sq * a.H + h) * 128;
+
+  // Q fragments (B operand of S^T = K Q^T): the lane holds query row
+  // 32*wave + lq, channels 16*kk + 8*g .. +7. Loaded before the ring fill so
+  // the in-order load counter covers them.
+  bf16x8_t qf[8];
+  {
+    const uint16_t* qp = a.qw + ((int64_t)bh * a.Sq_pad + q0 + wave * 32 + lq) * 128 + g * 8;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) qf[kk] = *reinterpret_cast<const bf16x8_t*>(qp + kk * 16);
+  }
 
   // Per-lane byte offsets of the direct loads within a sub-tile (K and V^T
   // sub-tiles are contiguous 8 KB blocks in the workspace). The lane that
@@ -256,12 +304,12 @@ void attn_fwd_kernel(AttnArgs a) {
   }
   // One buffer resource per sub-tile (base in SGPRs, 8 KB range), so the
   // loads need no vector address arithmetic and offsets stay 32-bit at any
-  // sequence length. Steps always issue their refill so that no branch
-  // splits the step's schedule; a refill past the last sub-tile gets an
+  // sequence length. Every step issues exactly one refill so the wait counts
+  // are the same at every step; a refill past the last sub-tile gets an
   // empty range (the hardware returns zeros without touching memory) and
   // lands in a ring slot that no later step reads.
   auto issue_loads = [&](int x) {
-    uint8_t* slot = lds + (x & (kNBuf - 1)) * kBufBytes;
+    uint8_t* slot = lds + (x & (kRing - 1)) * kBufBytes;
     const bool live = x < xe;
     const uint16_t* kx = kw + (int64_t)(live ? x : 0) * (kSub * 128);
     const uint16_t* vx = vt + (int64_t)(live ? x : 0) * (kSub * 128);
@@ -270,51 +318,22 @@ void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < VLD; ++i) load_lds16(vx, live ? kVBytes : 0, voff[i], slot + kKBytes + (wave + NW * i) * 1024);
   };
-
-  // Per-lane LDS byte offsets of the matrix-core operand reads.
-  int kaddr[8], vaddr[2];
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) kaddr[kk] = lq * 256 + ((((2 * kk) | g) ^ (lq & 15)) * 16);
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) vaddr[ks] = kKBytes + lq * 64 + ((((2 * ks) | g) ^ ((lq >> 2) & 3)) * 16);
-
-  // Issue the first three sub-tiles, then load Q while they fly.
-  issue_loads(xb);
-  if (NS > 1) issue_loads(xb + 1);
-  if (NS > 2) issue_loads(xb + 2);
-
-  // Q fragments (B operand of S^T = K Q^T): lane holds query row lq of this
-  // wave, channels 16*kk + 8*g .. +7.
-  bf16x8_t qf[8];
-  {
-    const uint16_t* qp = a.qw + ((int64_t)bh * a.Sq_pad + q0 + wave * 32 + lq) * 128 + g * 8;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) qf[kk] = *reinterpret_cast<const bf16x8_t*>(qp + kk * 16);
-  }
+  for (int i = 0; i < kRing - 1; ++i) issue_loads(xb + i);
 
   f32x16_t acc[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
-  float m_run = 0.f;         // row offset (scores are in exp2 units), shared by the lane pair
-  float l_run = 0.f;         // this lane's share of the row sum of bf16 probabilities
+  float m_run = 0.f;       // row offset (exp2 units), shared by the lane pair
+  float l_run = 0.f;       // this lane's share of the row sum of bf16 probabilities
+  f32x16_t msplat;         // -m_run in every slot: the QK^T accumulator's initial value
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // S^T of sub-tile x, accumulated onto `init` (the negated running max, so
-  // the result is already s - m in exp2 units: q carries softmax_scale*log2 e).
-  auto qk = [&](int x, const f32x16_t& init) {
-    const uint8_t* kb = lds + (x & (kNBuf - 1)) * kBufBytes;
-    f32x16_t s = init;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kb + kaddr[kk]);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s, 0, 0, 0);
-    }
-    return s;
-  };
   // Row max of this lane's 16 scores; with MASK, keys past the end are set
-  // to -inf first (only the last sub-tile can hold such keys).
+  // to -inf first (only the last sub-tile can hold such keys; the mask is a
+  // no-op on any other).
   auto rowmax = [&](f32x16_t& s, int x, auto mask) {
     if constexpr (decltype(mask)::value) {
 #pragma unroll
@@ -333,17 +352,18 @@ void attn_fwd_kernel(AttnArgs a) {
   // The scores arrive as s - m_run. If some row of the wave exceeds its
   // offset by more than 2^kRescaleLog2 (rare), raise that row's m_run by its
   // excess, shift the scores and rescale the accumulator and partial sum.
-  f32x16_t msplat;     // -m_run in every accumulator slot: the QK^T initial value
   auto maybe_rescale = [&](f32x16_t& s, float mx) {
     if (__builtin_amdgcn_ballot_w64(mx > kRescaleLog2) != 0) {
       const float delta = fmaxf(max_lane_pair(mx), 0.f);
       m_run += delta;
       const float alpha = __builtin_amdgcn_exp2f(-delta);
       l_run *= alpha;
+      // msplat - delta is exactly -(m_run + delta): updated in place so the
+      // splat keeps its registers across the branch.
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         s[r] -= delta;
-        msplat[r] = -m_run;
+        msplat[r] -= delta;
       }
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
@@ -351,7 +371,9 @@ void attn_fwd_kernel(AttnArgs a) {
         for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
     }
   };
-  // bf16 probabilities of sub-tile scores, as the two B operands of PV.
+  // bf16 probabilities p = exp2(s) of the sub-tile scores (already shifted
+  // by the row offset), as the two B operands of PV, and this lane's share
+  // of their row sum.
   auto probs = [&](const f32x16_t& s, bf16x8_t* pf) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
@@ -362,8 +384,6 @@ void attn_fwd_kernel(AttnArgs a) {
         pf[ks][i] = (__bf16)p0;
         pf[ks][i + 1] = (__bf16)p1;
       }
-  };
-  auto psum = [&](const bf16x8_t* pf) {
     float t = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
@@ -372,125 +392,105 @@ void attn_fwd_kernel(AttnArgs a) {
         const bf16x2_t pp = {pf[ks][i], pf[ks][i + 1]};
         t = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, t, false);
       }
-    return t;
-  };
-  auto pv = [&](int x, const bf16x8_t* pf) {
-    const uint8_t* vb = lds + (x & (kNBuf - 1)) * kBufBytes;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(vb + dt * 2048 + vaddr[ks]);
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], acc[dt], 0, 0, 0);
-      }
-  };
-  // One pipeline step for sub-tile u < NU-1 (there is a next sub-tile):
-  // wait for this wave's loads of sub-tile u+1 (loads retire in order; those
-  // of u+2 may stay in flight), publish everybody's with a barrier, refill
-  // the ring slot of sub-tile u-1 with sub-tile u+3, then
-  //   phase A: exponentials of sub-tile u alongside QK^T of sub-tile u+1,
-  //   phase B: PV of sub-tile u alongside the row maxima of sub-tile u+1.
-  f32x16_t s_cur;
-  auto step = [&](int u, auto mask_next) {
-    if (u + 2 < xe)
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LDPS) : "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    const uint8_t* kb = lds + ((u + 1) & (kNBuf - 1)) * kBufBytes;
-    const uint8_t* vb = lds + (u & (kNBuf - 1)) * kBufBytes;
-    bf16x8_t kf[8], vf[8];
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) kf[kk] = *reinterpret_cast<const bf16x8_t*>(kb + kaddr[kk]);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) vf[i] = *reinterpret_cast<const bf16x8_t*>(vb + (i >> 1) * 2048 + vaddr[i & 1]);
-    // The refill targets the slot of sub-tile u-1, which no wave reads after
-    // the barrier, so it may follow this step's fragment reads.
-    issue_loads(u + 3);
-    bf16x8_t pf[2];
-    probs(s_cur, pf);
-    f32x16_t s_nxt;
-    s_nxt = msplat;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s_nxt, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf[i & 1], acc[i >> 1], 0, 0, 0);
-    l_run += psum(pf);
-    const float mx = rowmax(s_nxt, u + 1, mask_next);
-    // Issue order: all 16 fragment reads, then QK^T MFMAs each followed by
-    // exponential work, then PV MFMAs each followed by sum / max work.
-    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-    }
-    maybe_rescale(s_nxt, mx);
-    s_cur = s_nxt;
+    l_run += t;
   };
 
-  // Sub-tile 0: scores and max before the pipeline starts. Its loads are the
-  // oldest; sub-tiles 1 and 2 may still be in flight.
-  if (NS > 2)
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LDPS) : "memory");
-  else if (NS > 1)
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LDPS) : "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  {
-    // Sub-tile 0 sets each row's offset to its exact maximum (so the row
-    // keeps one probability of 1), then scores are shifted by it.
-    f32x16_t zero;
+  // sched_barrier(0) fences keep the compiler from moving instructions
+  // across the phase boundaries.
+  auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+  bf16x8_t kf[8], vf[8], pf[2];
+  auto read_k = [&](int x) {
+    const uint32_t t = (x & (kRing - 1)) * kBufBytes + kbase;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) zero[r] = 0.f;
-    s_cur = qk(xb, zero);
-  }
+    for (int kk = 0; kk < 8; ++kk) kf[kk] = *reinterpret_cast<const bf16x8_t*>(lds + (t ^ (32u * kk)));
+  };
+  auto read_v = [&](int x) {
+    const uint8_t* sb = lds + (x & (kRing - 1)) * kBufBytes;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) vf[i] = *reinterpret_cast<const bf16x8_t*>(sb + vaddr[i & 1] + (i >> 1) * 2048);
+  };
+
+  // Sub-tiles xb..xb+2 first (the other loads may still fly), then the
+  // prologue: scores of xb, which set each row's offset to its exact maximum
+  // (so the row keeps one probability of 1), and their probabilities.
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kRing - 4) * LDPS) : "memory");
+  __syncthreads();
+  f32x16_t s;
   {
-    const float mx0 = (NS == 1 && mask_end) ? rowmax(s_cur, xb, Mask{}) : rowmax(s_cur, xb, NoMask{});
+    read_k(xb);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s, 0, 0, 0);
+    read_k(min(xb + 1, xe - 1));
+    read_v(xb);
+    const float mx0 = rowmax(s, xb, Mask{});
     m_run = max_lane_pair(mx0);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      s_cur[r] -= m_run;
+      s[r] -= m_run;
       msplat[r] = -m_run;
     }
+    probs(s, pf);
   }
 
-  // Steady state: the next sub-tile is never the masked last one.
+  // Step u alternates two phases separated by workgroup barriers:
+  //   X: the matrix-core work, QK^T of u+1 (K fragments of u+1 in kf) and
+  //      PV of u (V fragments of u in vf, probabilities of u in pf);
+  //   Y: the vector and LDS work, refill of the ring slot of u-1, reads of
+  //      K(u+2) and V(u+1), row maxima and rescale of u+1, probabilities and
+  //      row sums of u+1.
+  // The second wave of each SIMD passes one extra barrier first, so it runs
+  // Y while the first runs X and the other way round: the matrix core of the
+  // SIMD always has one wave's work while the other wave does the softmax.
+  // Both roles execute the same instructions in the same order.
+  auto step = [&](int u, auto mask_next) {
+    fence();
+    s = msplat;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf[i & 1], acc[i >> 1], 0, 0, 0);
+    fence();
+    bar();
+    fence();
+    read_k(min(u + 2, xe - 1));
+    read_v(u + 1);
+    // Refill the slot of u-1, last read for its PV in the X phase before the
+    // previous barrier (or, for the lagging role, before this one). Issued
+    // after this phase's reads: a fragment read behind a pending LDS DMA
+    // would make the compiler wait for every load in flight.
+    issue_loads(u - 1 + kRing);
+    const float mx = rowmax(s, u + 1, mask_next);
+    maybe_rescale(s, mx);
+    probs(s, pf);
+    fence();
+    // Publish sub-tile u+3 once every wave has passed this point.
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((kRing - 4) * LDPS) : "memory");
+    fence();
+  };
+
+  if (role) bar();
   for (int u = xb; u < xe - 2; ++u) step(u, NoMask{});
-  if (NS >= 2) {
-    if (mask_end)
-      step(xe - 2, Mask{});
-    else
-      step(xe - 2, NoMask{});
-  }
-  // The last steps issued empty-range refills; let them retire so no LDS
-  // write is pending when the workgroup ends and its LDS is handed on.
+  if (xe - xb >= 2) step(xe - 2, Mask{});
+  // Last X phase: PV of the last sub-tile only.
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf[i & 1], acc[i >> 1], 0, 0, 0);
+  if (!role) bar();
+  // The ring holds refills that nobody reads; let them retire so no LDS
+  // write is pending when the workgroup ends or the next segment starts.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  {
-    // Last sub-tile: exponentials and PV only.
-    bf16x8_t pf[2];
-    probs(s_cur, pf);
-    pv(xe - 1, pf);
-    l_run += psum(pf);
-  }
 
   if (rec < 0) {
     store_row(a, obase, q0 + wave * 32 + lq, g, acc, 1.0f / sum_lane_pair(l_run));
   } else {
-    // Partial record: acc register r at [r][thread], then m_run and l_run.
     float* pr = a.part + (int64_t)rec * kPartFloats + tid;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) pr[(dt * 16 + r) * (NW * 64)] = acc[dt][r];
-    pr[64 * (NW * 64)] = m_run;
-    pr[65 * (NW * 64)] = l_run;
+      for (int r = 0; r < 16; ++r) pr[(dt * 16 + r) * T] = acc[dt][r];
+    pr[kRecM * T] = m_run;
+    pr[kRecL * T] = l_run;
   }
   if (si + 1 < nseg) __syncthreads();   // the next segment refills the LDS ring
   }
@@ -503,6 +503,7 @@ void attn_fwd_kernel(AttnArgs a) {
 template <int NW>
 __global__ __launch_bounds__(NW * 64) void attn_merge_kernel(AttnArgs a) {
   constexpr int BM = NW * 32;
+  constexpr int T = NW * 64;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -528,7 +529,7 @@ __global__ __launch_bounds__(NW * 64) void attn_merge_kernel(AttnArgs a) {
     return a.part + (int64_t)(2 * j + (t - first)) * kPartFloats + tid;
   };
   float M = -INFINITY;
-  for (int j = j0; j <= j1; ++j) M = fmaxf(M, record(j)[64 * (NW * 64)]);
+  for (int j = j0; j <= j1; ++j) M = fmaxf(M, record(j)[kRecM * T]);
   f32x16_t acc[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
@@ -537,12 +538,12 @@ __global__ __launch_bounds__(NW * 64) void attn_merge_kernel(AttnArgs a) {
   float l = 0.f;
   for (int j = j0; j <= j1; ++j) {
     const float* pr = record(j);
-    const float w = __builtin_amdgcn_exp2f(pr[64 * (NW * 64)] - M);
-    l += w * pr[65 * (NW * 64)];
+    const float w = __builtin_amdgcn_exp2f(pr[kRecM * T] - M);
+    l += w * pr[kRecL * T];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[dt][r] += w * pr[(dt * 16 + r) * (NW * 64)];
+      for (int r = 0; r < 16; ++r) acc[dt][r] += w * pr[(dt * 16 + r) * T];
   }
   store_row(a, obase, q0 + wave * 32 + (lane & 31), lane >> 5, acc, 1.0f / sum_lane_pair(l));
 }

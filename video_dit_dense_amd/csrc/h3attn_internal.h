@@ -58,8 +58,9 @@ hipError_t launch_v_relayout(const uint16_t* v, uint16_t* vt, int32_t B, int32_t
 hipError_t launch_rope_tables(float* cos_out, float* sin_out, int32_t rows, double theta,
                               hipStream_t stream);
 
-// Attention tiling: a workgroup of kAttnWaves waves owns kAttnRows query rows
-// of one (b, h) and walks the keys in kAttnSub-key sub-tiles.
+// Attention tiling: a workgroup of kAttnWaves waves (32 query rows each) owns
+// kAttnRows query rows of one (b, h) and walks the keys in kAttnSub-key
+// sub-tiles.
 constexpr int kAttnWaves = 8;
 constexpr int kAttnRows = kAttnWaves * 32;
 constexpr int kAttnSub = 32;

@@ -309,7 +309,7 @@ void attn_fwd_kernel(AttnArgs a) {
   // empty range (the hardware returns zeros without touching memory) and
   // lands in a ring slot that no later step reads.
   auto issue_loads = [&](int x) {
-    uint8_t* slot = lds + (x & (kRing - 1)) * kBufBytes;
+    uint8_t* slot = lds + ((x - xb) & (kRing - 1)) * kBufBytes;
     const bool live = x < xe;
     const uint16_t* kx = kw + (int64_t)(live ? x : 0) * (kSub * 128);
     const uint16_t* vx = vt + (int64_t)(live ? x : 0) * (kSub * 128);
@@ -384,31 +384,54 @@ void attn_fwd_kernel(AttnArgs a) {
         pf[ks][i] = (__bf16)p0;
         pf[ks][i + 1] = (__bf16)p1;
       }
-    float t = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int i = 0; i < 8; i += 2) {
         const bf16x2_t pp = {pf[ks][i], pf[ks][i + 1]};
-        t = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, t, false);
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_run, false);
       }
-    l_run += t;
   };
 
   // sched_barrier(0) fences keep the compiler from moving instructions
   // across the phase boundaries.
   auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
   bf16x8_t kf[8], vf[8], pf[2];
-  auto read_k = [&](int x) {
-    const uint32_t t = (x & (kRing - 1)) * kBufBytes + kbase;
+  // Ring slot of sub-tile x is (x - xb) mod kRing. Fragment reads take the
+  // slot either at run time or, in the unrolled steady state, as a
+  // compile-time constant that lands in the instruction's offset field (the
+  // field holds 16 bits, so slots 4..7 use addresses biased by 64 KB).
+  uint32_t ka[8], kah[8], vah[2];
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) kf[kk] = *reinterpret_cast<const bf16x8_t*>(lds + (t ^ (32u * kk)));
-  };
-  auto read_v = [&](int x) {
-    const uint8_t* sb = lds + (x & (kRing - 1)) * kBufBytes;
+  for (int kk = 0; kk < 8; ++kk) {
+    ka[kk] = kbase ^ (32u * kk);
+    kah[kk] = ka[kk] + 4 * kBufBytes;
+  }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) vf[i] = *reinterpret_cast<const bf16x8_t*>(sb + vaddr[i & 1] + (i >> 1) * 2048);
+  for (int ks = 0; ks < 2; ++ks) vah[ks] = vaddr[ks] + 4 * kBufBytes;
+  auto read_k = [&](auto slot) {
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      if constexpr (std::is_integral_v<decltype(slot)>)
+        kf[kk] = *reinterpret_cast<const bf16x8_t*>(lds + slot * kBufBytes + ka[kk]);
+      else if constexpr (decltype(slot)::value < 4)
+        kf[kk] = *reinterpret_cast<const bf16x8_t*>(lds + decltype(slot)::value * kBufBytes + ka[kk]);
+      else
+        kf[kk] = *reinterpret_cast<const bf16x8_t*>(lds + (decltype(slot)::value - 4) * kBufBytes + kah[kk]);
+    }
   };
+  auto read_v = [&](auto slot) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if constexpr (std::is_integral_v<decltype(slot)>)
+        vf[i] = *reinterpret_cast<const bf16x8_t*>(lds + slot * kBufBytes + vaddr[i & 1] + (i >> 1) * 2048);
+      else if constexpr (decltype(slot)::value < 4)
+        vf[i] = *reinterpret_cast<const bf16x8_t*>(lds + decltype(slot)::value * kBufBytes + vaddr[i & 1] + (i >> 1) * 2048);
+      else
+        vf[i] = *reinterpret_cast<const bf16x8_t*>(lds + (decltype(slot)::value - 4) * kBufBytes + vah[i & 1] + (i >> 1) * 2048);
+    }
+  };
+  auto rslot = [&](int x) { return (x - xb) & (kRing - 1); };
 
   // Sub-tiles xb..xb+2 first (the other loads may still fly), then the
   // prologue: scores of xb, which set each row's offset to its exact maximum
@@ -417,13 +440,13 @@ void attn_fwd_kernel(AttnArgs a) {
   __syncthreads();
   f32x16_t s;
   {
-    read_k(xb);
+    read_k(std::integral_constant<int, 0>{});
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s, 0, 0, 0);
-    read_k(min(xb + 1, xe - 1));
-    read_v(xb);
+    read_k(rslot(min(xb + 1, xe - 1)));
+    read_v(std::integral_constant<int, 0>{});
     const float mx0 = rowmax(s, xb, Mask{});
     m_run = max_lane_pair(mx0);
 #pragma unroll
@@ -444,7 +467,7 @@ void attn_fwd_kernel(AttnArgs a) {
   // Y while the first runs X and the other way round: the matrix core of the
   // SIMD always has one wave's work while the other wave does the softmax.
   // Both roles execute the same instructions in the same order.
-  auto step = [&](int u, auto mask_next) {
+  auto step = [&](int u, auto mask_next, auto slot_v, auto slot_k) {
     fence();
     s = msplat;
 #pragma unroll
@@ -454,8 +477,8 @@ void attn_fwd_kernel(AttnArgs a) {
     fence();
     bar();
     fence();
-    read_k(min(u + 2, xe - 1));
-    read_v(u + 1);
+    read_k(slot_k);
+    read_v(slot_v);
     // Refill the slot of u-1, last read for its PV in the X phase before the
     // previous barrier (or, for the lagging role, before this one). Issued
     // after this phase's reads: a fragment read behind a pending LDS DMA
@@ -470,9 +493,24 @@ void attn_fwd_kernel(AttnArgs a) {
     fence();
   };
 
+  // Steady state in blocks of kRing steps, so that each step's ring slots
+  // (V of u+1 at (u+1-xb) mod 8, K of u+2 at (u+2-xb) mod 8) are constants;
+  // the remaining steps address the ring at run time, the last one masked.
   if (role) bar();
-  for (int u = xb; u < xe - 2; ++u) step(u, NoMask{});
-  if (xe - xb >= 2) step(xe - 2, Mask{});
+  int u = xb;
+  for (; u + kRing <= xe - 2; u += kRing) {
+    using std::integral_constant;
+    step(u + 0, NoMask{}, integral_constant<int, 1>{}, integral_constant<int, 2>{});
+    step(u + 1, NoMask{}, integral_constant<int, 2>{}, integral_constant<int, 3>{});
+    step(u + 2, NoMask{}, integral_constant<int, 3>{}, integral_constant<int, 4>{});
+    step(u + 3, NoMask{}, integral_constant<int, 4>{}, integral_constant<int, 5>{});
+    step(u + 4, NoMask{}, integral_constant<int, 5>{}, integral_constant<int, 6>{});
+    step(u + 5, NoMask{}, integral_constant<int, 6>{}, integral_constant<int, 7>{});
+    step(u + 6, NoMask{}, integral_constant<int, 7>{}, integral_constant<int, 0>{});
+    step(u + 7, NoMask{}, integral_constant<int, 0>{}, integral_constant<int, 1>{});
+  }
+  for (; u < xe - 2; ++u) step(u, NoMask{}, rslot(u + 1), rslot(u + 2));
+  if (xe - xb >= 2) step(xe - 2, Mask{}, rslot(xe - 1), rslot(xe - 1));
   // Last X phase: PV of the last sub-tile only.
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf[i & 1], acc[i >> 1], 0, 0, 0);

@@ -14,12 +14,17 @@ attention):
   "2.2 Fuse Q/K RMSNorm, RoPE, and Ulysses Pack", steps 1 and 3).
 * Partial rotary embedding on 96 of the 128 channels, rotate-half pairs
   (j, j+48) (FastVideo PR #1832, "Preserve H3-specific attention behavior").
-* Dense non-causal softmax attention over BSHD tensors at head_dim 128
-  (FastVideo PR #1832, "Summary"), with keys past a valid length excluded
-  (FastVideo PR #1799, "Implementation": padding masks) and query rows past a
-  valid length set to zero (TeleFuser PR #37, "2.3 Add fixed-valid and
-  valid-only attention modes" and "2.4 Fuse valid-only gather with zero-tail
-  merge").
+* Dense softmax attention over BSHD tensors at head_dim 128 (FastVideo PR
+  #1832, "Summary"; non-causal for H3), with keys past a valid length
+  excluded (FastVideo PR #1799, "Implementation": padding masks) and query
+  rows past a valid length set to zero (TeleFuser PR #37, "2.3 Add
+  fixed-valid and valid-only attention modes" and "2.4 Fuse valid-only gather
+  with zero-tail merge").
+* The attention variants of the FastVideo PR #1799 backend ("Implementation":
+  MHA and GQA, causal attention, padding and causal masks combined): a causal
+  mask (key j visible to query i iff j <= i, the lower-triangular mask of
+  row indices), grouped heads (query head h reads key/value head
+  h // (Hq / Hkv)), and valid lengths per batch item.
 
 Readings where the pages are silent (each pinned by a test in tests/):
 per-head norm with one [128] weight shared by all heads, eps inside the square
@@ -104,37 +109,62 @@ def qk_prologue(q_bits, k_bits, w_q, w_k, eps: float, theta: float | None,
     return q, k
 
 
-def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
-              q_valid: int | None = None, kv_valid: int | None = None,
-              rows=None, block: int = 256) -> np.ndarray:
-    """Dense non-causal softmax attention on BSHD float64 tensors.
+def _per_batch(valid, B: int, full: int) -> list:
+    """A valid length for every batch item: None means `full`, an int is
+    shared by all items, a sequence gives one per item."""
+    if valid is None:
+        return [full] * B
+    if np.ndim(valid) == 0:
+        return [int(valid)] * B
+    vals = [int(x) for x in valid]
+    if len(vals) != B:
+        raise ValueError("one valid length per batch item is needed")
+    return vals
 
-    o_i = sum_{j < kv_valid} softmax_j(scale * q_i . k_j) v_j for i < q_valid,
-    o_i = 0 for i >= q_valid. With `rows`, only those query rows are computed
-    and the result has shape [B, len(rows), H, D]. Query rows are processed
-    `block` at a time so no Sq x Sk score matrix is held."""
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
+              q_valid=None, kv_valid=None, rows=None, block: int = 256,
+              causal: bool = False) -> np.ndarray:
+    """Softmax attention on BSHD float64 tensors, q [B, Sq, H, D] and k, v
+    [B, Sk, Hkv, D] with H a multiple of Hkv (query head h reads key/value
+    head h // (H // Hkv); Hkv = H is plain multi-head attention).
+
+    For batch item b and query row i < q_valid[b]:
+      o_i = sum_{j in V(i)} softmax_j(scale * q_i . k_j) v_j,
+      V(i) = {j < kv_valid[b]}, and with `causal` also j <= i;
+    o_i = 0 for i >= q_valid[b]. q_valid / kv_valid are None (everything
+    valid), one int for all items or one per item. With `rows` (absolute
+    query row indices), only those rows are computed and the result has shape
+    [B, len(rows), H, D]. Rows are processed `block` at a time so no Sq x Sk
+    score matrix is held."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     B, Sq, H, D = q.shape
-    Sk = k.shape[1]
-    q_valid = Sq if q_valid is None else int(q_valid)
-    kv_valid = Sk if kv_valid is None else int(kv_valid)
-    if kv_valid < 1:
+    Sk, Hkv = k.shape[1], k.shape[2]
+    if H % Hkv != 0:
+        raise ValueError("query heads must be a multiple of key/value heads")
+    group = H // Hkv
+    qv = _per_batch(q_valid, B, Sq)
+    kvv = _per_batch(kv_valid, B, Sk)
+    if min(kvv) < 1:
         raise ValueError("attention needs at least one valid key")
     row_idx = np.arange(Sq) if rows is None else np.asarray(rows, dtype=np.int64)
     out = np.zeros((B, len(row_idx), H, D), dtype=np.float64)
     for b in range(B):
         for h in range(H):
-            kh = np.ascontiguousarray(k[b, :kv_valid, h, :])
-            vh = np.ascontiguousarray(v[b, :kv_valid, h, :])
+            kh = np.ascontiguousarray(k[b, :kvv[b], h // group, :])
+            vh = np.ascontiguousarray(v[b, :kvv[b], h // group, :])
             for start in range(0, len(row_idx), block):
                 sel = row_idx[start:start + block]
-                live = sel < q_valid
+                live = sel < qv[b]
                 if not live.any():
                     continue
                 qh = q[b, sel[live], h, :]
                 s = (qh @ kh.T) * scale
+                if causal:
+                    # key j is visible to query row i iff j <= i
+                    s = np.where(np.arange(kvv[b])[None, :] <= sel[live][:, None], s, -np.inf)
                 m = s.max(axis=1, keepdims=True)
                 p = np.exp(s - m)
                 o = (p @ vh) / p.sum(axis=1, keepdims=True)
@@ -144,20 +174,13 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
 
 
 def forward(q_bits, k_bits, v_bits, w_q, w_k, eps: float, theta: float | None,
-            scale: float, q_valid: int | None = None, kv_valid: int | None = None,
-            norm: bool = True, rows=None) -> np.ndarray:
-    """The whole attention step: prologue on q and k, then attention with v."""
+            scale: float, q_valid=None, kv_valid=None, norm: bool = True, rows=None,
+            causal: bool = False) -> np.ndarray:
+    """The whole attention step: prologue on q and k, then attention with v.
+    Valid lengths, `rows` and `causal` are those of `attention`."""
     qn, kn = qk_prologue(q_bits, k_bits, w_q, w_k, eps, theta, norm=norm)
-    if rows is not None:
-        # Only the sampled query rows are needed; keep their prologue outputs.
-        qn = qn[:, np.asarray(rows, dtype=np.int64)]
-        rows_local = np.arange(qn.shape[1])
-        o = attention(qn, kn, bf16_bits_to_f64(v_bits), scale, None, kv_valid,
-                      rows=rows_local)
-        if q_valid is not None:
-            o[:, np.asarray(rows) >= q_valid] = 0.0
-        return o
-    return attention(qn, kn, bf16_bits_to_f64(v_bits), scale, q_valid, kv_valid)
+    return attention(qn, kn, bf16_bits_to_f64(v_bits), scale, q_valid, kv_valid,
+                     rows=rows, causal=causal)
 
 
 def compare(got_bits_or_f64, ref: np.ndarray) -> dict:

@@ -300,3 +300,107 @@ def test_compare_metrics():
     assert m["nonfinite"] == 0
     assert m["max_abs"] <= 2 ** -7
     assert m["max_ulp"] <= 1.0
+
+
+# ------------------------------------------- attention variants: causal, GQA, per-batch lengths
+
+def test_attention_variants_brute_force():
+    """Causal mask composed with key padding, grouped heads and per-item valid
+    lengths, against scalar loops (FastVideo PR #1799, "Implementation")."""
+    rng = np.random.default_rng(21)
+    B, Sq, Sk, H, Hkv = 2, 7, 9, 4, 2
+    q = rng.standard_normal((B, Sq, H, 128))
+    k = rng.standard_normal((B, Sk, Hkv, 128))
+    v = rng.standard_normal((B, Sk, Hkv, 128))
+    scale, qv, kvv = 0.13, [5, 7], [6, 3]
+    o = oracle.attention(q, k, v, scale, q_valid=qv, kv_valid=kvv, causal=True)
+    for b in range(B):
+        for h in range(H):
+            hk = h // (H // Hkv)
+            for i in range(Sq):
+                if i >= qv[b]:
+                    assert np.all(o[b, i, h] == 0.0)
+                    continue
+                keys = [j for j in range(Sk) if j < kvv[b] and j <= i]
+                s = [scale * math.fsum(q[b, i, h, c] * k[b, j, hk, c] for c in range(128)) for j in keys]
+                m = max(s)
+                e = [math.exp(t - m) for t in s]
+                z = math.fsum(e)
+                for c in range(128):
+                    ref = math.fsum(e[n] * v[b, j, hk, c] for n, j in enumerate(keys)) / z
+                    assert abs(o[b, i, h, c] - ref) < 1e-13
+
+
+def _sdpa_masked(q, k, v, scale, mask, gqa):
+    """torch CPU float64 SDPA with a boolean [B, 1, Sq, Sk] mask (True = attend)."""
+    qt = torch.from_numpy(q).transpose(1, 2)
+    kt = torch.from_numpy(k).transpose(1, 2)
+    vt = torch.from_numpy(v).transpose(1, 2)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=torch.from_numpy(mask),
+                                                         scale=scale, enable_gqa=gqa)
+    return o.transpose(1, 2).numpy()
+
+
+@pytest.mark.parametrize("B,Sq,Sk,H,Hkv,qv,kvv,causal", [
+    (1, 300, 300, 2, 2, 300, 300, True),        # causal self-attention
+    (1, 300, 300, 2, 2, 300, 211, True),        # causal composed with key padding
+    (2, 257, 257, 4, 1, [257, 130], [257, 90], True),   # per-item lengths, one kv head (MQA)
+    (2, 129, 400, 6, 2, [129, 77], [400, 1], False),    # GQA cross-attention, per-item lengths
+])
+def test_attention_variants_match_torch_sdpa_fp64(B, Sq, Sk, H, Hkv, qv, kvv, causal):
+    rng = np.random.default_rng(Sq * 7 + Sk + H)
+    q = rng.standard_normal((B, Sq, H, 128)) * 1.5
+    k = rng.standard_normal((B, Sk, Hkv, 128)) * 1.5
+    v = rng.standard_normal((B, Sk, Hkv, 128))
+    scale = 1 / math.sqrt(128)
+    o = oracle.attention(q, k, v, scale, q_valid=qv, kv_valid=kvv, causal=causal, block=64)
+    qvl = qv if isinstance(qv, list) else [qv] * B
+    kvl = kvv if isinstance(kvv, list) else [kvv] * B
+    mask = np.zeros((B, 1, Sq, Sk), dtype=bool)
+    for b in range(B):
+        mask[b, 0, :, :kvl[b]] = True
+    if causal:
+        mask &= torch.tril(torch.ones(Sq, Sk, dtype=torch.bool)).numpy()[None, None]
+    ref = _sdpa_masked(q, k, v, scale, mask, Hkv != H)
+    for b in range(B):
+        ref[b, qvl[b]:] = 0.0
+    assert np.allclose(o, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_attention_variant_invariants():
+    rng = np.random.default_rng(22)
+    B, S, H, Hkv = 1, 80, 4, 2
+    scale = 1 / math.sqrt(128)
+    q = rng.standard_normal((B, S, H, 128))
+    k = rng.standard_normal((B, S, Hkv, 128))
+    v = rng.standard_normal((B, S, Hkv, 128))
+    o = oracle.attention(q, k, v, scale, causal=True)
+    # causal row 0 sees only key 0: returns v_0 of its kv head
+    assert np.array_equal(o[0, 0], v[0, 0, np.arange(H) // 2])
+    # keys and values after position t do not change rows <= t (finite values:
+    # a causally masked key still meets a zero weight, and 0 * NaN is NaN)
+    t = 37
+    k2, v2 = k.copy(), v.copy()
+    k2[:, t + 1:] = rng.standard_normal(k2[:, t + 1:].shape) * 5
+    v2[:, t + 1:] = rng.standard_normal(v2[:, t + 1:].shape) * 1e6
+    o2 = oracle.attention(q, k2, v2, scale, causal=True)
+    assert np.array_equal(o2[:, :t + 1], o[:, :t + 1])
+    # grouped heads equal multi-head attention with each kv head repeated
+    rep_k, rep_v = np.repeat(k, H // Hkv, axis=2), np.repeat(v, H // Hkv, axis=2)
+    assert np.array_equal(oracle.attention(q, rep_k, rep_v, scale, causal=True), o)
+    # causal with kv_valid = 1: every row returns v_0
+    o1 = oracle.attention(q, k, v, scale, kv_valid=1, causal=True)
+    assert np.array_equal(o1, np.broadcast_to(v[:, :1, np.arange(H) // 2], o1.shape))
+    # per-item lengths: each item equals a one-item call with its own lengths
+    qb = rng.standard_normal((3, 50, H, 128))
+    kb = rng.standard_normal((3, 70, Hkv, 128))
+    vb = rng.standard_normal((3, 70, Hkv, 128))
+    qv, kvv = [50, 11, 30], [70, 5, 64]
+    ob = oracle.attention(qb, kb, vb, scale, q_valid=qv, kv_valid=kvv, causal=True)
+    for b in range(3):
+        one = oracle.attention(qb[b:b + 1], kb[b:b + 1], vb[b:b + 1], scale, q_valid=qv[b], kv_valid=kvv[b],
+                               causal=True)
+        assert np.array_equal(ob[b:b + 1], one)
+    # rows subset equals the full causal computation at those rows
+    rows = np.array([0, 1, 37, 79])
+    assert np.allclose(oracle.attention(q, k, v, scale, rows=rows, causal=True), o[:, rows], rtol=1e-13, atol=1e-14)

@@ -169,6 +169,75 @@ int h3attn_forward_stages(const uint16_t* q, const uint16_t* k, const uint16_t* 
                           int32_t q_valid, int32_t kv_valid, float softmax_scale,
                           void* workspace, size_t workspace_bytes, uint32_t stages, void* stream);
 
+/*
+ * The attention step with the variants of the FastVideo PR #1799 dense
+ * backend (section "Implementation": MHA and GQA, causal attention, padding
+ * and causal masks combined), plus strided inputs and per-item valid
+ * lengths. Everything h3attn_forward_stages does, generalised:
+ *
+ *   o[b, i, h] = sum_{j in V(b, i)} softmax_j(softmax_scale * q[b,i,h] . k[b,j,h/G]) v[b,j,h/G]
+ *                for i < q_valid(b), with G = Hq / Hkv (grouped heads; G = 1 is MHA),
+ *   V(b, i) = { j < kv_valid(b) }, and with causal also j <= i (the lower
+ *             triangle of row indices; for Sq != Sk this is the top-left
+ *             alignment of torch's scaled_dot_product_attention),
+ *   o[b, i, h] = 0 for q_valid(b) <= i < Sq.
+ *
+ * q, k, v are views: element strides along batch, sequence and head (the
+ * channel stride is 1), for instance slices of a fused QKV projection. All
+ * three strides 0 means dense BSHD. Strides must be >= 0 and multiples of 8
+ * (every row 16-byte aligned). Views may overlap each other (they are only
+ * read) but not o, the workspace or the valid-length array.
+ *
+ * valid_lengths: NULL, or a device int32 array [2*B] holding q_valid(b) at
+ *   [2b] and kv_valid(b) at [2b+1]; q_valid and kv_valid are then ignored.
+ *   The kernels clamp each entry to [0, Sq] / [0, Sk]; an item with
+ *   kv_valid(b) = 0 has no keys and its rows are written as +0.0. Without
+ *   the array, q_valid (-1 = Sq, else 0..Sq) and kv_valid (-1 = Sk, else
+ *   1..Sk) apply to every item.
+ * causal: 0 or 1. Keys masked by the causal mask still enter the
+ *   contraction with weight 0, so a non-finite value there propagates (as
+ *   in torch's SDPA); keys at or past kv_valid(b) are never read.
+ * head_dim: 128. Hq must be a multiple of Hkv. Norm, rotary and
+ *   softmax_scale arguments are those of h3attn_forward; the rotary table
+ *   rows serve sequence positions of q and k alike.
+ * Work split: no causal mask and no valid_lengths uses the schedule of
+ *   h3attn_forward (whole rounds of query tiles, the last round's key steps
+ *   split over all compute units); otherwise one workgroup per (b, h,
+ *   256-row query block), the longest first under the causal mask.
+ *
+ * h3attn_forward_ex_workspace_bytes() gives the workspace these arguments
+ * need (0 if a size is invalid); stages are those of h3attn_forward_stages
+ * (an ATTEND-only call must follow a PREPARE call with the same arguments).
+ * Errors: NULL_POINTER, BAD_SHAPE, BAD_ALIGNMENT (pointers, strides),
+ * ALIASING, BAD_VALUE (causal not 0/1, stages, scale, eps), WORKSPACE,
+ * UNSUPPORTED_DEVICE, HIP.
+ */
+typedef struct h3attn_forward_args {
+  const uint16_t* q;          /* [B, Sq, Hq, 128] view */
+  const uint16_t* k;          /* [B, Sk, Hkv, 128] view */
+  const uint16_t* v;          /* [B, Sk, Hkv, 128] view */
+  uint16_t* o;                /* [B, Sq, Hq, 128], dense, written in full */
+  int64_t q_stride[3];        /* element strides: batch, sequence, head */
+  int64_t k_stride[3];
+  int64_t v_stride[3];
+  int32_t B, Sq, Sk, Hq, Hkv, head_dim;
+  const float* q_norm_w;      /* fp32 [128] each, both NULL: no norm */
+  const float* k_norm_w;
+  float eps;
+  int32_t rope_rows;
+  const float* rope_cos;      /* fp32 [rope_rows, 48] each, both NULL: no rotary */
+  const float* rope_sin;
+  int32_t q_valid;
+  int32_t kv_valid;
+  const int32_t* valid_lengths;
+  int32_t causal;
+  float softmax_scale;
+} h3attn_forward_args;
+
+size_t h3attn_forward_ex_workspace_bytes(const h3attn_forward_args* args);
+int h3attn_forward_ex(const h3attn_forward_args* args, void* workspace, size_t workspace_bytes,
+                      uint32_t stages, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

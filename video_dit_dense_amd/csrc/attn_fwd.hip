@@ -142,10 +142,10 @@ __device__ inline int xcd_order(int i, int n) {
 // +0.0 for rows at or past q_valid. Lane (l, register r of acc[dt]) holds
 // channel dt*32 + 8*(r/4) + 4*(l/32) + r%4 of its row.
 __device__ inline void store_row(const AttnArgs& a, uint16_t* obase, int q, int g, const f32x16_t* acc,
-                                 float inv) {
+                                 float inv, int q_valid) {
   if (q >= a.Sq) return;
   uint16_t* op = obase + q * ((int64_t)a.H * 128);
-  const bool live = q < a.q_valid;
+  const bool live = q < q_valid;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -206,44 +206,10 @@ void attn_fwd_kernel(AttnArgs a) {
   }
 
   const int n_qblocks = (a.Sq + BM - 1) / BM;
-  const int NU = (a.kv_valid + kSub - 1) / kSub;     // sub-tiles with at least one valid key
-  const int last_valid = a.kv_valid - 1;
   const int bid = blockIdx.x;
-
-  // This block's work: one or two segments, each a valid tile g and its
-  // sub-tiles [xb, xe), finished either into o (rec < 0) or into partial
-  // record rec.
-  int g0, xb0, xe0, rec0, g1 = 0, xb1 = 0, xe1 = 0, rec1 = -1, nseg = 1;
-  if (bid < a.n_whole) {
-    g0 = xcd_order(bid, a.n_whole);
-    xb0 = 0;
-    xe0 = NU;
-    rec0 = -1;
-  } else if (bid < a.n_whole + a.n_split_blocks) {
-    // Split tiles: of the U = n_split*NU steps of tiles n_whole.., block j
-    // takes [j*U/n, (j+1)*U/n) with n = n_split_blocks > n_split, so at most
-    // NU steps and at most two tiles.
-    const int j = xcd_order(bid - a.n_whole, a.n_split_blocks);
-    const int64_t U = (int64_t)a.n_split * NU;
-    const int64_t s0 = (int64_t)j * U / a.n_split_blocks;
-    const int64_t s1 = (int64_t)(j + 1) * U / a.n_split_blocks;
-    const int t = (int)(s0 / NU);
-    g0 = a.n_whole + t;
-    xb0 = (int)(s0 - (int64_t)t * NU);
-    xe0 = (int)min<int64_t>(NU, s1 - (int64_t)t * NU);
-    rec0 = 2 * j;
-    if (s1 > (int64_t)(t + 1) * NU) {
-      nseg = 2;
-      g1 = g0 + 1;
-      xe1 = (int)(s1 - (int64_t)(t + 1) * NU);
-      rec1 = 2 * j + 1;
-    }
-  } else {
-    // A tile wholly past q_valid: zero rows [q0, min(q0 + BM, Sq)).
-    const int nqz = n_qblocks - a.nqv;
-    const int z = bid - a.n_whole - a.n_split_blocks;
-    const int bh = z / nqz;
-    const int q0 = (a.nqv + (z - bh * nqz)) * BM;
+  // Zero rows [q0, min(q0 + BM, Sq)) of head bh: a tile with no valid query
+  // row or no valid key.
+  auto zero_tile = [&](int bh, int q0) {
     const int b = bh / a.H, h = bh - b * a.H;
     uint16_t* obase = a.o + ((int64_t)b * a.Sq * a.H + h) * 128;
     const int64_t orow = (int64_t)a.H * 128;
@@ -251,7 +217,79 @@ void attn_fwd_kernel(AttnArgs a) {
       const int q = q0 + (idx >> 4);
       if (q < a.Sq) *reinterpret_cast<u32x4_t*>(obase + q * orow + (idx & 15) * 8) = u32x4_t{0u, 0u, 0u, 0u};
     }
-    return;
+  };
+
+  // This block's work: one or two segments, each a query tile (head bh,
+  // first row q0) and its sub-tiles [xb, xe), finished either into o
+  // (rec < 0) or into partial record rec. Per segment also: the valid query
+  // rows qv (rows at or past it are written as zeros) and the valid keys kvv.
+  int bh0, q00, xb0, xe0, rec0, bh1 = 0, q01 = 0, xb1 = 0, xe1 = 0, rec1 = -1, nseg = 1;
+  int qv_t = a.q_valid, kvv_t = a.kv_valid;
+  if (a.general) {
+    // One tile per block. With the causal mask a tile's work grows with its
+    // query block, so blocks take the longest tiles first.
+    const int nbh = a.B * a.H;
+    int qb;
+    if (a.causal) {
+      qb = n_qblocks - 1 - bid / nbh;
+      bh0 = bid - (bid / nbh) * nbh;
+    } else {
+      bh0 = bid / n_qblocks;
+      qb = bid - bh0 * n_qblocks;
+    }
+    q00 = qb * BM;
+    const int b = bh0 / a.H;
+    qv_t = item_valid(a.lengths, b, 0, a.q_valid, a.Sq);
+    kvv_t = item_valid(a.lengths, b, 1, a.kv_valid, a.Sk);
+    if (q00 >= qv_t || kvv_t == 0) {
+      zero_tile(bh0, q00);
+      return;
+    }
+    // Keys [0, key_end): with the causal mask no row of the tile sees a key
+    // at or past its last row + 1.
+    const int key_end = a.causal ? min(kvv_t, q00 + BM) : kvv_t;
+    xb0 = 0;
+    xe0 = (key_end + kSub - 1) / kSub;
+    rec0 = -1;
+  } else {
+    const int NU = (a.kv_valid + kSub - 1) / kSub;   // sub-tiles with at least one valid key
+    int g0 = 0, g1 = 0;
+    if (bid < a.n_whole) {
+      g0 = xcd_order(bid, a.n_whole);
+      xb0 = 0;
+      xe0 = NU;
+      rec0 = -1;
+    } else if (bid < a.n_whole + a.n_split_blocks) {
+      // Split tiles: of the U = n_split*NU steps of tiles n_whole.., block j
+      // takes [j*U/n, (j+1)*U/n) with n = n_split_blocks > n_split, so at
+      // most NU steps and at most two tiles.
+      const int j = xcd_order(bid - a.n_whole, a.n_split_blocks);
+      const int64_t U = (int64_t)a.n_split * NU;
+      const int64_t s0 = (int64_t)j * U / a.n_split_blocks;
+      const int64_t s1 = (int64_t)(j + 1) * U / a.n_split_blocks;
+      const int t = (int)(s0 / NU);
+      g0 = a.n_whole + t;
+      xb0 = (int)(s0 - (int64_t)t * NU);
+      xe0 = (int)min<int64_t>(NU, s1 - (int64_t)t * NU);
+      rec0 = 2 * j;
+      if (s1 > (int64_t)(t + 1) * NU) {
+        nseg = 2;
+        g1 = g0 + 1;
+        xe1 = (int)(s1 - (int64_t)(t + 1) * NU);
+        rec1 = 2 * j + 1;
+      }
+    } else {
+      // A tile wholly past q_valid.
+      const int nqz = n_qblocks - a.nqv;
+      const int z = bid - a.n_whole - a.n_split_blocks;
+      const int bh = z / nqz;
+      zero_tile(bh, (a.nqv + (z - bh * nqz)) * BM);
+      return;
+    }
+    bh0 = g0 / a.nqv;
+    q00 = (g0 - bh0 * a.nqv) * BM;
+    bh1 = g1 / a.nqv;
+    q01 = (g1 - bh1 * a.nqv) * BM;
   }
 
   // Per-lane LDS byte addresses of the matrix-core operand reads. K fragment
@@ -264,15 +302,22 @@ void attn_fwd_kernel(AttnArgs a) {
 
 #pragma nounroll
   for (int si = 0; si < nseg; ++si) {
-  const int tg = si ? g1 : g0;
+  const int bh = si ? bh1 : bh0;
+  const int q0 = si ? q01 : q00;
   const int xb = si ? xb1 : xb0;
   const int xe = si ? xe1 : xe0;
   const int rec = si ? rec1 : rec0;
-  const int bh = tg / a.nqv;
-  const int q0 = (tg - bh * a.nqv) * BM;
+  const int qv_seg = qv_t;
   const int b = bh / a.H;
   const int h = bh - b * a.H;
+  const int bh_kv = b * a.Hkv + h / (a.H / a.Hkv);
   uint16_t* obase = a.o + ((int64_t)b * a.Sq * a.H + h) * 128;
+  // Masking: lane's last visible key (its query row under the causal mask,
+  // capped by the valid keys), and the first sub-tile in which some lane of
+  // the workgroup may see a masked key; steps before it skip the mask.
+  const int row = q0 + wave * 32 + lq;
+  const int lim = a.causal ? min(row, kvv_t - 1) : kvv_t - 1;
+  const int x_mask = min(a.causal ? q0 / kSub : 0x7fffffff, (kvv_t % kSub) ? kvv_t / kSub : 0x7fffffff);
 
   // Q fragments (B operand of S^T = K Q^T): the lane holds query row
   // 32*wave + lq, channels 16*kk + 8*g .. +7. Loaded before the ring fill so
@@ -287,8 +332,8 @@ void attn_fwd_kernel(AttnArgs a) {
   // Per-lane byte offsets of the direct loads within a sub-tile (K and V^T
   // sub-tiles are contiguous 8 KB blocks in the workspace). The lane that
   // fills LDS chunk Q fetches the logical chunk the swizzle puts there.
-  const uint16_t* kw = a.kw + (int64_t)bh * a.Sk_pad * 128;
-  const uint16_t* vt = a.vt + (int64_t)bh * a.Sk_pad * 128;
+  const uint16_t* kw = a.kw + (int64_t)bh_kv * a.Sk_pad * 128;
+  const uint16_t* vt = a.vt + (int64_t)bh_kv * a.Sk_pad * 128;
   int koff[KLD], voff[VLD];
 #pragma unroll
   for (int i = 0; i < KLD; ++i) {
@@ -331,15 +376,15 @@ void attn_fwd_kernel(AttnArgs a) {
   f32x16_t msplat;         // -m_run in every slot: the QK^T accumulator's initial value
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // Row max of this lane's 16 scores; with MASK, keys past the end are set
-  // to -inf first (only the last sub-tile can hold such keys; the mask is a
-  // no-op on any other).
+  // Row max of this lane's 16 scores; with MASK, keys past the lane's last
+  // visible key are set to -inf first (a no-op in sub-tiles without such
+  // keys).
   auto rowmax = [&](f32x16_t& s, int x, auto mask) {
     if constexpr (decltype(mask)::value) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = x * kSub + (r >> 2) * 8 + g * 4 + (r & 3);
-        if (key > last_valid) s[r] = -INFINITY;
+        if (key > lim) s[r] = -INFINITY;
       }
     }
     // Depth-3 tree over the 16 values.
@@ -495,10 +540,11 @@ void attn_fwd_kernel(AttnArgs a) {
 
   // Steady state in blocks of kRing steps, so that each step's ring slots
   // (V of u+1 at (u+1-xb) mod 8, K of u+2 at (u+2-xb) mod 8) are constants;
-  // the remaining steps address the ring at run time, the last one masked.
+  // a block runs while all its steps read real sub-tiles and none needs the
+  // mask. The remaining steps address the ring at run time and mask.
   if (role) bar();
   int u = xb;
-  for (; u + kRing <= xe - 2; u += kRing) {
+  for (; u + kRing <= min(xe - 2, x_mask - 1); u += kRing) {
     using std::integral_constant;
     step(u + 0, NoMask{}, integral_constant<int, 1>{}, integral_constant<int, 2>{});
     step(u + 1, NoMask{}, integral_constant<int, 2>{}, integral_constant<int, 3>{});
@@ -509,8 +555,7 @@ void attn_fwd_kernel(AttnArgs a) {
     step(u + 6, NoMask{}, integral_constant<int, 7>{}, integral_constant<int, 0>{});
     step(u + 7, NoMask{}, integral_constant<int, 0>{}, integral_constant<int, 1>{});
   }
-  for (; u < xe - 2; ++u) step(u, NoMask{}, rslot(u + 1), rslot(u + 2));
-  if (xe - xb >= 2) step(xe - 2, Mask{}, rslot(xe - 1), rslot(xe - 1));
+  for (; u < xe - 1; ++u) step(u, Mask{}, rslot(u + 1), rslot(min(u + 2, xe - 1)));
   // Last X phase: PV of the last sub-tile only.
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf[i & 1], acc[i >> 1], 0, 0, 0);
@@ -520,7 +565,7 @@ void attn_fwd_kernel(AttnArgs a) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   if (rec < 0) {
-    store_row(a, obase, q0 + wave * 32 + lq, g, acc, 1.0f / sum_lane_pair(l_run));
+    store_row(a, obase, q0 + wave * 32 + lq, g, acc, 1.0f / sum_lane_pair(l_run), qv_seg);
   } else {
     float* pr = a.part + (int64_t)rec * kPartFloats + tid;
 #pragma unroll
@@ -583,16 +628,18 @@ __global__ __launch_bounds__(NW * 64) void attn_merge_kernel(AttnArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[dt][r] += w * pr[(dt * 16 + r) * T];
   }
-  store_row(a, obase, q0 + wave * 32 + (lane & 31), lane >> 5, acc, 1.0f / sum_lane_pair(l));
+  store_row(a, obase, q0 + wave * 32 + (lane & 31), lane >> 5, acc, 1.0f / sum_lane_pair(l), a.q_valid);
 }
 
 // Transposed, key-blocked copy of v for the PV operand: a block moves 64 keys
 // (two sub-tiles) x 128 channels of one (b, h) through LDS, reading 256-byte
 // rows of v and writing one contiguous 16 KB block of vt. Keys at or past
 // kv_valid are written as zeros and never read.
-__global__ __launch_bounds__(256) void v_relayout_kernel(const uint16_t* __restrict__ v,
+__global__ __launch_bounds__(256) void v_relayout_kernel(const uint16_t* __restrict__ v, int64_t sb,
+                                                         int64_t ss, int64_t sh,
                                                          uint16_t* __restrict__ vt, int32_t H,
                                                          int32_t Sk, int32_t kv_valid,
+                                                         const int32_t* __restrict__ lengths,
                                                          int32_t Sk_pad) {
   constexpr int kPitch = 136;  // 272-byte rows
   __shared__ __attribute__((aligned(16))) uint16_t tile[64 * kPitch];
@@ -600,13 +647,14 @@ __global__ __launch_bounds__(256) void v_relayout_kernel(const uint16_t* __restr
   const int bh = blockIdx.y;
   const int b = bh / H, h = bh - b * H;
   const int tid = threadIdx.x;
+  const int32_t valid = item_valid(lengths, b, 1, kv_valid, Sk);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int idx = tid + 256 * i;
     const int key = idx >> 4, ch = idx & 15;
     u32x4_t val = u32x4_t{0u, 0u, 0u, 0u};
-    if (p0 + key < kv_valid)
-      val = *reinterpret_cast<const u32x4_t*>(v + (((int64_t)b * Sk + p0 + key) * H + h) * kHeadDim + ch * 8);
+    if (p0 + key < valid)
+      val = *reinterpret_cast<const u32x4_t*>(v + (int64_t)b * sb + (int64_t)(p0 + key) * ss + (int64_t)h * sh + ch * 8);
     *reinterpret_cast<u32x4_t*>(&tile[key * kPitch + ch * 8]) = val;
   }
   __syncthreads();
@@ -654,6 +702,17 @@ hipError_t launch_attention(AttnArgs a, hipStream_t stream) {
   constexpr int BM = kAttnRows;
   static_assert(BM == NW * 32 && kAttnSub == kSub, "tiling constants");
   const int64_t nq = (a.Sq + BM - 1) / BM;
+  a.general = (a.causal || a.lengths != nullptr) ? 1 : 0;
+  if (a.general) {
+    // One block per (b, h, query block); each finds its own valid rows and
+    // key range, so nothing is split.
+    const int64_t grid = (int64_t)a.B * a.H * nq;
+    if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+    a.nqv = (int32_t)nq;
+    a.n_whole = a.n_split = a.n_split_blocks = 0;
+    if (grid > 0) attn_fwd_kernel<NW><<<dim3((unsigned)grid), NW * 64, 0, stream>>>(a);
+    return hipGetLastError();
+  }
   const int64_t nqv = (a.q_valid + BM - 1) / BM;
   const int64_t n_valid = (int64_t)a.B * a.H * nqv;
   const int64_t n_zero = (int64_t)a.B * a.H * (nq - nqv);
@@ -686,10 +745,11 @@ hipError_t launch_attention(AttnArgs a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_v_relayout(const uint16_t* v, uint16_t* vt, int32_t B, int32_t Sk, int32_t H,
-                             int32_t kv_valid, int32_t Sk_pad, hipStream_t stream) {
+hipError_t launch_v_relayout(const uint16_t* v, int64_t sb, int64_t ss, int64_t sh, uint16_t* vt,
+                             int32_t B, int32_t Sk, int32_t H, int32_t kv_valid,
+                             const int32_t* lengths, int32_t Sk_pad, hipStream_t stream) {
   const dim3 grid((unsigned)(Sk_pad / 64), (unsigned)(B * H));
-  v_relayout_kernel<<<grid, 256, 0, stream>>>(v, vt, H, Sk, kv_valid, Sk_pad);
+  v_relayout_kernel<<<grid, 256, 0, stream>>>(v, sb, ss, sh, vt, H, Sk, kv_valid, lengths, Sk_pad);
   return hipGetLastError();
 }
 

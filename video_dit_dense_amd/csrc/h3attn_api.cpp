@@ -77,14 +77,17 @@ struct WorkspaceLayout {
   size_t q_off, k_off, v_off, part_off, total;
 };
 
-bool workspace_layout(int32_t B, int32_t Sq, int32_t Sk, int32_t H, WorkspaceLayout* w) {
-  if (B < 1 || Sq < 1 || Sk < 1 || H < 1) return false;
+// Workspace of a forward with Hq query heads and Hkv key/value heads; the
+// partial records of split tiles are only needed by the uniform schedule
+// (no causal mask, no per-item lengths).
+bool workspace_layout(int32_t B, int32_t Sq, int32_t Sk, int32_t Hq, int32_t Hkv, bool uniform,
+                      WorkspaceLayout* w) {
+  if (B < 1 || Sq < 1 || Sk < 1 || Hq < 1 || Hkv < 1) return false;
   w->Sq_pad = round_up(Sq, h3::kRowPad);
   w->Sk_pad = round_up(Sk, h3::kRowPad);
-  const unsigned __int128 bh = (unsigned __int128)B * (unsigned __int128)H;
-  const unsigned __int128 qb = bh * (unsigned __int128)w->Sq_pad * 256u;
-  const unsigned __int128 kb = bh * (unsigned __int128)w->Sk_pad * 256u;
-  w->part_slots = h3::split_part_slots(B, Sq, Sk, H);
+  const unsigned __int128 qb = (unsigned __int128)B * (unsigned __int128)Hq * (unsigned __int128)w->Sq_pad * 256u;
+  const unsigned __int128 kb = (unsigned __int128)B * (unsigned __int128)Hkv * (unsigned __int128)w->Sk_pad * 256u;
+  w->part_slots = uniform ? h3::split_part_slots(B, Sq, Sk, Hq) : 0;
   const unsigned __int128 pb = (unsigned __int128)w->part_slots * h3::kPartBytes;
   const unsigned __int128 tot = qb + 2 * kb + pb;
   if (tot > (unsigned __int128)(INT64_MAX / 4)) return false;
@@ -93,6 +96,30 @@ bool workspace_layout(int32_t B, int32_t Sq, int32_t Sk, int32_t H, WorkspaceLay
   w->v_off = (size_t)(qb + kb);
   w->part_off = (size_t)(qb + 2 * kb);
   w->total = (size_t)tot;
+  return true;
+}
+
+// Element strides of a [B, S, H, 128] view: all three 0 means dense.
+void resolve_strides(const int64_t in[3], int32_t S, int32_t H, int64_t out[3]) {
+  if (in[0] == 0 && in[1] == 0 && in[2] == 0) {
+    out[2] = h3::kHeadDim;
+    out[1] = (int64_t)H * h3::kHeadDim;
+    out[0] = (int64_t)S * out[1];
+  } else {
+    out[0] = in[0];
+    out[1] = in[1];
+    out[2] = in[2];
+  }
+}
+
+// Byte range [lo, hi) a [B, S, H, 128] view with non-negative strides can
+// touch, or false on overflow.
+bool view_range(const void* p, const int64_t st[3], int32_t B, int32_t S, int32_t H, Range* r) {
+  const unsigned __int128 last = (unsigned __int128)(B - 1) * (uint64_t)st[0] + (unsigned __int128)(S - 1) * (uint64_t)st[1] +
+                                 (unsigned __int128)(H - 1) * (uint64_t)st[2] + h3::kHeadDim;
+  const unsigned __int128 bytes = last * 2u;
+  if (bytes > (unsigned __int128)(INT64_MAX / 4)) return false;
+  *r = range_of(p, (size_t)bytes);
   return true;
 }
 
@@ -147,17 +174,169 @@ H3_API int h3attn_qk_prologue(const uint16_t* q_in, const uint16_t* k_in, uint16
 
   const int64_t row = (int64_t)H * h3::kHeadDim;
   h3::ProTensor tq{q_in, q_out, q_norm_w, (int64_t)Sq * row, row, h3::kHeadDim,
-                   (int64_t)Sq * row, row, h3::kHeadDim, Sq, Sq, 1.0f};
+                   (int64_t)Sq * row, row, h3::kHeadDim, Sq, Sq, 1.0f, nullptr, 0, H};
   h3::ProTensor tk{k_in, k_out, k_norm_w, (int64_t)Sk * row, row, h3::kHeadDim,
-                   (int64_t)Sk * row, row, h3::kHeadDim, Sk, Sk, 1.0f};
-  return status_from(h3::launch_qk_prologue(tq, tk, B, H, eps, rope_cos, rope_sin, (hipStream_t)stream));
+                   (int64_t)Sk * row, row, h3::kHeadDim, Sk, Sk, 1.0f, nullptr, 1, H};
+  return status_from(h3::launch_qk_prologue(tq, tk, B, eps, rope_cos, rope_sin, (hipStream_t)stream));
 }
 
 H3_API size_t h3attn_forward_workspace_bytes(int32_t B, int32_t Sq, int32_t Sk, int32_t H) {
   WorkspaceLayout w;
-  if (!workspace_layout(B, Sq, Sk, H, &w)) return 0;
+  if (!workspace_layout(B, Sq, Sk, H, H, true, &w)) return 0;
   return w.total;
 }
+
+namespace {
+
+bool uniform_schedule(const h3attn_forward_args* a) { return !a->causal && a->valid_lengths == nullptr; }
+
+// Validates every argument of a forward before anything is enqueued; on
+// success fills the resolved strides and the workspace layout.
+int check_forward(const h3attn_forward_args* a, size_t workspace_bytes, const void* workspace, uint32_t stages,
+                  int64_t qs[3], int64_t ks[3], int64_t vs[3], WorkspaceLayout* wl) {
+  if (!a) return H3ATTN_ERR_NULL_POINTER;
+  if (!a->q || !a->k || !a->v || !a->o) return H3ATTN_ERR_NULL_POINTER;
+  if (stages == 0 || stages > (H3ATTN_STAGE_PREPARE | H3ATTN_STAGE_ATTEND)) return H3ATTN_ERR_BAD_VALUE;
+  const int32_t B = a->B, Sq = a->Sq, Sk = a->Sk, Hq = a->Hq, Hkv = a->Hkv;
+  if (a->head_dim != h3::kHeadDim || B < 1 || Sq < 1 || Sk < 1 || Hq < 1 || Hkv < 1) return H3ATTN_ERR_BAD_SHAPE;
+  if (Hq % Hkv != 0) return H3ATTN_ERR_BAD_SHAPE;
+  if ((int64_t)B * Hq > 65535 || Sq > (1 << 30) || Sk > (1 << 30)) return H3ATTN_ERR_BAD_SHAPE;
+  const size_t obytes = bshd_bytes(B, Sq, Hq);
+  if (obytes == 0 || bshd_bytes(B, Sk, Hkv) == 0) return H3ATTN_ERR_BAD_SHAPE;
+  if (a->causal != 0 && a->causal != 1) return H3ATTN_ERR_BAD_VALUE;
+  if (!a->valid_lengths) {
+    const int32_t qv = a->q_valid == -1 ? Sq : a->q_valid;
+    const int32_t kvv = a->kv_valid == -1 ? Sk : a->kv_valid;
+    if (qv < 0 || qv > Sq || kvv < 1 || kvv > Sk) return H3ATTN_ERR_BAD_SHAPE;
+  }
+  if (!std::isfinite(a->softmax_scale) || !(a->softmax_scale > 0.f)) return H3ATTN_ERR_BAD_VALUE;
+  if (int st = check_prologue_args(Sq, Sk, a->q_norm_w, a->k_norm_w, a->eps, a->rope_cos, a->rope_sin, a->rope_rows))
+    return st;
+  for (int i = 0; i < 3; ++i)
+    if (a->q_stride[i] < 0 || a->k_stride[i] < 0 || a->v_stride[i] < 0) return H3ATTN_ERR_BAD_SHAPE;
+  resolve_strides(a->q_stride, Sq, Hq, qs);
+  resolve_strides(a->k_stride, Sk, Hkv, ks);
+  resolve_strides(a->v_stride, Sk, Hkv, vs);
+  for (int i = 0; i < 3; ++i)
+    if ((qs[i] | ks[i] | vs[i]) & 7) return H3ATTN_ERR_BAD_ALIGNMENT;
+  if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o)) return H3ATTN_ERR_BAD_ALIGNMENT;
+  if (a->valid_lengths && (reinterpret_cast<uintptr_t>(a->valid_lengths) & 3u)) return H3ATTN_ERR_BAD_ALIGNMENT;
+  if (!workspace_layout(B, Sq, Sk, Hq, Hkv, uniform_schedule(a), wl)) return H3ATTN_ERR_BAD_SHAPE;
+  if ((int64_t)B * Hq * wl->Sq_pad >= (1ll << 31) || (int64_t)B * Hkv * wl->Sk_pad >= (1ll << 31))
+    return H3ATTN_ERR_BAD_SHAPE;
+  if ((int64_t)B * Sq * Hq >= (1ll << 31) || (int64_t)B * Sk * Hkv >= (1ll << 31)) return H3ATTN_ERR_BAD_SHAPE;
+  Range rq, rk, rv;
+  if (!view_range(a->q, qs, B, Sq, Hq, &rq) || !view_range(a->k, ks, B, Sk, Hkv, &rk) ||
+      !view_range(a->v, vs, B, Sk, Hkv, &rv))
+    return H3ATTN_ERR_BAD_SHAPE;
+  if (!workspace || workspace_bytes < wl->total) return H3ATTN_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return H3ATTN_ERR_BAD_ALIGNMENT;
+  const Range oq = range_of(a->o, obytes);
+  const Range ws = range_of(workspace, wl->total);
+  if (overlap(oq, rq) || overlap(oq, rk) || overlap(oq, rv) || overlap(oq, ws)) return H3ATTN_ERR_ALIASING;
+  if (overlap(ws, rq) || overlap(ws, rk) || overlap(ws, rv)) return H3ATTN_ERR_ALIASING;
+  if (a->q_norm_w) {
+    const Range w1 = range_of(a->q_norm_w, 512), w2 = range_of(a->k_norm_w, 512);
+    if (overlap(ws, w1) || overlap(ws, w2) || overlap(oq, w1) || overlap(oq, w2)) return H3ATTN_ERR_ALIASING;
+  }
+  if (a->rope_cos) {
+    const size_t tb = (size_t)a->rope_rows * h3::kRopePairs * sizeof(float);
+    const Range c1 = range_of(a->rope_cos, tb), c2 = range_of(a->rope_sin, tb);
+    if (overlap(ws, c1) || overlap(ws, c2) || overlap(oq, c1) || overlap(oq, c2)) return H3ATTN_ERR_ALIASING;
+  }
+  if (a->valid_lengths) {
+    const Range lr = range_of(a->valid_lengths, (size_t)B * 2 * sizeof(int32_t));
+    if (overlap(ws, lr) || overlap(oq, lr)) return H3ATTN_ERR_ALIASING;
+  }
+  return check_device();
+}
+
+int run_forward(const h3attn_forward_args* a, void* workspace, size_t workspace_bytes, uint32_t stages,
+                void* stream) {
+  int64_t qs[3], ks[3], vs[3];
+  WorkspaceLayout wl;
+  if (int st = check_forward(a, workspace_bytes, workspace, stages, qs, ks, vs, &wl)) return st;
+  const int32_t B = a->B, Sq = a->Sq, Sk = a->Sk, Hq = a->Hq, Hkv = a->Hkv;
+  const int32_t q_valid = a->valid_lengths ? Sq : (a->q_valid == -1 ? Sq : a->q_valid);
+  const int32_t kv_valid = a->valid_lengths ? Sk : (a->kv_valid == -1 ? Sk : a->kv_valid);
+
+  hipStream_t s = (hipStream_t)stream;
+  uint16_t* wsb = static_cast<uint16_t*>(workspace);
+  uint16_t* qw = wsb + wl.q_off / 2;
+  uint16_t* kw = wsb + wl.k_off / 2;
+  uint16_t* vt = wsb + wl.v_off / 2;
+
+  // Prologue into the head-major workspace: rows past the valid length are
+  // zero-filled so the attention kernel can read whole tiles.
+  // q is written pre-multiplied by softmax_scale*log2(e) (fp32, before its
+  // one bf16 rounding), so the attention kernel's scores are in exp2 units.
+  const float c = (float)((double)a->softmax_scale * 1.4426950408889634);
+  h3::ProTensor tq{a->q, qw, a->q_norm_w, qs[0], qs[1], qs[2],
+                   (int64_t)Hq * wl.Sq_pad * h3::kHeadDim, h3::kHeadDim, wl.Sq_pad * h3::kHeadDim,
+                   q_valid, (int32_t)wl.Sq_pad, c, a->valid_lengths, 0, Hq};
+  h3::ProTensor tk{a->k, kw, a->k_norm_w, ks[0], ks[1], ks[2],
+                   (int64_t)Hkv * wl.Sk_pad * h3::kHeadDim, h3::kHeadDim, wl.Sk_pad * h3::kHeadDim,
+                   kv_valid, (int32_t)wl.Sk_pad, 1.0f, a->valid_lengths, 1, Hkv};
+  if (stages & H3ATTN_STAGE_PREPARE) {
+    hipError_t e = h3::launch_qk_prologue(tq, tk, B, a->eps, a->rope_cos, a->rope_sin, s);
+    if (e != hipSuccess) return H3ATTN_ERR_HIP;
+    e = h3::launch_v_relayout(a->v, vs[0], vs[1], vs[2], vt, B, Sk, Hkv, kv_valid, a->valid_lengths,
+                              (int32_t)wl.Sk_pad, s);
+    if (e != hipSuccess) return H3ATTN_ERR_HIP;
+  }
+  if (!(stages & H3ATTN_STAGE_ATTEND)) return H3ATTN_OK;
+
+  h3::AttnArgs at{};
+  at.qw = qw;
+  at.kw = kw;
+  at.vt = vt;
+  at.o = a->o;
+  at.part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + wl.part_off);
+  at.part_slots = wl.part_slots;
+  at.B = B;
+  at.H = Hq;
+  at.Sq = Sq;
+  at.Sk = Sk;
+  at.Sq_pad = (int32_t)wl.Sq_pad;
+  at.Sk_pad = (int32_t)wl.Sk_pad;
+  at.q_valid = q_valid;
+  at.kv_valid = kv_valid;
+  at.Hkv = Hkv;
+  at.causal = a->causal;
+  at.lengths = a->valid_lengths;
+  return status_from(h3::launch_attention(at, s));
+}
+
+h3attn_forward_args dense_args(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, int32_t B,
+                               int32_t Sq, int32_t Sk, int32_t H, int32_t head_dim, const float* q_norm_w,
+                               const float* k_norm_w, float eps, const float* rope_cos, const float* rope_sin,
+                               int32_t rope_rows, int32_t q_valid, int32_t kv_valid, float softmax_scale) {
+  h3attn_forward_args a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.B = B;
+  a.Sq = Sq;
+  a.Sk = Sk;
+  a.Hq = H;
+  a.Hkv = H;
+  a.head_dim = head_dim;
+  a.q_norm_w = q_norm_w;
+  a.k_norm_w = k_norm_w;
+  a.eps = eps;
+  a.rope_rows = rope_rows;
+  a.rope_cos = rope_cos;
+  a.rope_sin = rope_sin;
+  a.q_valid = q_valid;
+  a.kv_valid = kv_valid;
+  a.valid_lengths = nullptr;
+  a.causal = 0;
+  a.softmax_scale = softmax_scale;
+  return a;
+}
+
+}  // namespace
 
 H3_API int h3attn_forward(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                           int32_t B, int32_t Sq, int32_t Sk, int32_t H, int32_t head_dim,
@@ -165,9 +344,9 @@ H3_API int h3attn_forward(const uint16_t* q, const uint16_t* k, const uint16_t* 
                           const float* rope_cos, const float* rope_sin, int32_t rope_rows,
                           int32_t q_valid, int32_t kv_valid, float softmax_scale,
                           void* workspace, size_t workspace_bytes, void* stream) {
-  return h3attn_forward_stages(q, k, v, o, B, Sq, Sk, H, head_dim, q_norm_w, k_norm_w, eps, rope_cos,
-                               rope_sin, rope_rows, q_valid, kv_valid, softmax_scale, workspace,
-                               workspace_bytes, H3ATTN_STAGE_PREPARE | H3ATTN_STAGE_ATTEND, stream);
+  const h3attn_forward_args a = dense_args(q, k, v, o, B, Sq, Sk, H, head_dim, q_norm_w, k_norm_w, eps, rope_cos,
+                                           rope_sin, rope_rows, q_valid, kv_valid, softmax_scale);
+  return run_forward(&a, workspace, workspace_bytes, H3ATTN_STAGE_PREPARE | H3ATTN_STAGE_ATTEND, stream);
 }
 
 H3_API int h3attn_forward_stages(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
@@ -176,79 +355,19 @@ H3_API int h3attn_forward_stages(const uint16_t* q, const uint16_t* k, const uin
                                  const float* rope_cos, const float* rope_sin, int32_t rope_rows,
                                  int32_t q_valid, int32_t kv_valid, float softmax_scale,
                                  void* workspace, size_t workspace_bytes, uint32_t stages, void* stream) {
-  if (!q || !k || !v || !o) return H3ATTN_ERR_NULL_POINTER;
-  if (stages == 0 || stages > (H3ATTN_STAGE_PREPARE | H3ATTN_STAGE_ATTEND)) return H3ATTN_ERR_BAD_VALUE;
-  if (head_dim != h3::kHeadDim || B < 1 || Sq < 1 || Sk < 1 || H < 1) return H3ATTN_ERR_BAD_SHAPE;
-  if ((int64_t)B * H > 65535 || Sq > (1 << 30) || Sk > (1 << 30)) return H3ATTN_ERR_BAD_SHAPE;
-  const size_t qbytes = bshd_bytes(B, Sq, H), kbytes = bshd_bytes(B, Sk, H);
-  if (qbytes == 0 || kbytes == 0) return H3ATTN_ERR_BAD_SHAPE;
-  if (q_valid == -1) q_valid = Sq;
-  if (kv_valid == -1) kv_valid = Sk;
-  if (q_valid < 0 || q_valid > Sq || kv_valid < 1 || kv_valid > Sk) return H3ATTN_ERR_BAD_SHAPE;
-  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return H3ATTN_ERR_BAD_VALUE;
-  if (int st = check_prologue_args(Sq, Sk, q_norm_w, k_norm_w, eps, rope_cos, rope_sin, rope_rows)) return st;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return H3ATTN_ERR_BAD_ALIGNMENT;
-  WorkspaceLayout wl;
-  if (!workspace_layout(B, Sq, Sk, H, &wl)) return H3ATTN_ERR_BAD_SHAPE;
-  if ((int64_t)B * H * wl.Sq_pad >= (1ll << 31) || (int64_t)B * H * wl.Sk_pad >= (1ll << 31))
-    return H3ATTN_ERR_BAD_SHAPE;
-  if (!workspace || workspace_bytes < wl.total) return H3ATTN_ERR_WORKSPACE;
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return H3ATTN_ERR_BAD_ALIGNMENT;
-  const Range oq = range_of(o, qbytes);
-  const Range ws = range_of(workspace, wl.total);
-  const Range rq = range_of(q, qbytes), rk = range_of(k, kbytes), rv = range_of(v, kbytes);
-  if (overlap(oq, rq) || overlap(oq, rk) || overlap(oq, rv) || overlap(oq, ws)) return H3ATTN_ERR_ALIASING;
-  if (overlap(ws, rq) || overlap(ws, rk) || overlap(ws, rv)) return H3ATTN_ERR_ALIASING;
-  if (q_norm_w) {
-    const Range w1 = range_of(q_norm_w, 512), w2 = range_of(k_norm_w, 512);
-    if (overlap(ws, w1) || overlap(ws, w2) || overlap(oq, w1) || overlap(oq, w2)) return H3ATTN_ERR_ALIASING;
-  }
-  if (rope_cos) {
-    const size_t tb = (size_t)rope_rows * h3::kRopePairs * sizeof(float);
-    const Range c1 = range_of(rope_cos, tb), c2 = range_of(rope_sin, tb);
-    if (overlap(ws, c1) || overlap(ws, c2) || overlap(oq, c1) || overlap(oq, c2)) return H3ATTN_ERR_ALIASING;
-  }
-  if (int st = check_device()) return st;
+  const h3attn_forward_args a = dense_args(q, k, v, o, B, Sq, Sk, H, head_dim, q_norm_w, k_norm_w, eps, rope_cos,
+                                           rope_sin, rope_rows, q_valid, kv_valid, softmax_scale);
+  return run_forward(&a, workspace, workspace_bytes, stages, stream);
+}
 
-  hipStream_t s = (hipStream_t)stream;
-  uint16_t* wsb = static_cast<uint16_t*>(workspace);
-  uint16_t* qw = wsb + wl.q_off / 2;
-  uint16_t* kw = wsb + wl.k_off / 2;
-  uint16_t* vt = wsb + wl.v_off / 2;
-  const int64_t row = (int64_t)H * h3::kHeadDim;
+H3_API size_t h3attn_forward_ex_workspace_bytes(const h3attn_forward_args* args) {
+  if (!args || args->Hkv < 1 || args->Hq < 1 || args->Hq % args->Hkv != 0) return 0;
+  WorkspaceLayout w;
+  if (!workspace_layout(args->B, args->Sq, args->Sk, args->Hq, args->Hkv, uniform_schedule(args), &w)) return 0;
+  return w.total;
+}
 
-  // Prologue into the head-major workspace: rows past the valid length are
-  // zero-filled so the attention kernel can read whole tiles.
-  // q is written pre-multiplied by softmax_scale*log2(e) (fp32, before its
-  // one bf16 rounding), so the attention kernel's scores are in exp2 units.
-  const float c = (float)((double)softmax_scale * 1.4426950408889634);
-  h3::ProTensor tq{q, qw, q_norm_w, (int64_t)Sq * row, row, h3::kHeadDim,
-                   (int64_t)H * wl.Sq_pad * h3::kHeadDim, h3::kHeadDim, wl.Sq_pad * h3::kHeadDim,
-                   q_valid, (int32_t)wl.Sq_pad, c};
-  h3::ProTensor tk{k, kw, k_norm_w, (int64_t)Sk * row, row, h3::kHeadDim,
-                   (int64_t)H * wl.Sk_pad * h3::kHeadDim, h3::kHeadDim, wl.Sk_pad * h3::kHeadDim,
-                   kv_valid, (int32_t)wl.Sk_pad, 1.0f};
-  if (stages & H3ATTN_STAGE_PREPARE) {
-    hipError_t e = h3::launch_qk_prologue(tq, tk, B, H, eps, rope_cos, rope_sin, s);
-    if (e != hipSuccess) return H3ATTN_ERR_HIP;
-    e = h3::launch_v_relayout(v, vt, B, Sk, H, kv_valid, (int32_t)wl.Sk_pad, s);
-    if (e != hipSuccess) return H3ATTN_ERR_HIP;
-  }
-  if (!(stages & H3ATTN_STAGE_ATTEND)) return H3ATTN_OK;
-
-  h3::AttnArgs a;
-  a.qw = qw;
-  a.kw = kw;
-  a.vt = vt;
-  a.o = o;
-  a.part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + wl.part_off);
-  a.part_slots = wl.part_slots;
-  a.B = B;
-  a.H = H;
-  a.Sq = Sq;
-  a.Sq_pad = (int32_t)wl.Sq_pad;
-  a.Sk_pad = (int32_t)wl.Sk_pad;
-  a.q_valid = q_valid;
-  a.kv_valid = kv_valid;
-  return status_from(h3::launch_attention(a, s));
+H3_API int h3attn_forward_ex(const h3attn_forward_args* args, void* workspace, size_t workspace_bytes,
+                             uint32_t stages, void* stream) {
+  return run_forward(args, workspace, workspace_bytes, stages, stream);
 }

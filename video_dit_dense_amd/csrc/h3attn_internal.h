@@ -30,6 +30,17 @@ struct FastDiv {
   __device__ __host__ uint32_t div(uint32_t n) const { return (uint32_t)(((uint64_t)n * m) >> p); }
 };
 
+// Valid length of batch item b from an optional device array of per-item
+// lengths (q at [2b], kv at [2b+1]), clamped to [0, limit]; `uniform` when
+// there is no array. Clamping keeps every access in bounds whatever the
+// array holds.
+__device__ inline int32_t item_valid(const int32_t* lengths, int b, int which, int32_t uniform,
+                                     int32_t limit) {
+  if (lengths == nullptr) return uniform;
+  const int32_t v = lengths[2 * b + which];
+  return v < 0 ? 0 : (v > limit ? limit : v);
+}
+
 // One tensor handled by the prologue kernel. Strides are in elements and
 // describe a [B, S, H, 128] view (channel stride 1).
 struct ProTensor {
@@ -41,19 +52,26 @@ struct ProTensor {
   int32_t S_valid;         // rows s < S_valid are read and transformed
   int32_t S_out;           // rows S_valid <= s < S_out are written as zeros
   float out_scale;         // outputs are multiplied by this in fp32 before the bf16 rounding
-  FastDiv div_h, div_s;    // set by launch_qk_prologue: division by H and by S_out
+  const int32_t* lengths;  // optional per-item lengths (device); item b then uses
+  int32_t which;           //   item_valid(lengths, b, which, S_valid, S_valid) as its S_valid
+  int32_t H;               // heads of this tensor
+  FastDiv div_h, div_s;    // set by launch_qk_prologue: division by the larger H and by S_out
 };
 
 // Enqueues the fused RMSNorm + partial-rotary prologue over up to two tensors
-// (t1 may have S_out == 0). rope_cos/rope_sin == nullptr disables rotary.
-hipError_t launch_qk_prologue(const ProTensor& t0, const ProTensor& t1, int32_t B, int32_t H,
+// (t1 may have S_out == 0; the two may have different head counts).
+// rope_cos/rope_sin == nullptr disables rotary.
+hipError_t launch_qk_prologue(const ProTensor& t0, const ProTensor& t1, int32_t B,
                               float eps, const float* rope_cos, const float* rope_sin,
                               hipStream_t stream);
 
-// Writes the transposed, key-blocked copy of v that the attention kernel
-// reads (layout in attn_fwd.hip); keys >= kv_valid are written as zeros.
-hipError_t launch_v_relayout(const uint16_t* v, uint16_t* vt, int32_t B, int32_t Sk, int32_t H,
-                             int32_t kv_valid, int32_t Sk_pad, hipStream_t stream);
+// Writes the transposed, key-blocked copy of v ([B, Sk, H, 128] with element
+// strides sb, ss, sh) that the attention kernel reads (layout in
+// attn_fwd.hip); keys at or past the valid length (kv_valid, or the item's
+// entry of `lengths` when given) are written as zeros and never read.
+hipError_t launch_v_relayout(const uint16_t* v, int64_t sb, int64_t ss, int64_t sh, uint16_t* vt,
+                             int32_t B, int32_t Sk, int32_t H, int32_t kv_valid,
+                             const int32_t* lengths, int32_t Sk_pad, hipStream_t stream);
 
 hipError_t launch_rope_tables(float* cos_out, float* sin_out, int32_t rows, double theta,
                               hipStream_t stream);
@@ -87,16 +105,22 @@ inline int64_t split_part_slots(int32_t B, int32_t Sq, int32_t Sk, int32_t H) {
 
 struct AttnArgs {
   const uint16_t* qw;      // [B*H][Sq_pad][128] scaled by softmax_scale*log2(e), rows >= q_valid zero
-  const uint16_t* kw;      // [B*H][Sk_pad][128], rows >= kv_valid are zero
-  const uint16_t* vt;      // [B*H][Sk_pad/32][128][32], see attn_fwd.hip; keys >= kv_valid zero
+  const uint16_t* kw;      // [B*Hkv][Sk_pad][128], rows >= kv_valid are zero
+  const uint16_t* vt;      // [B*Hkv][Sk_pad/32][128][32], see attn_fwd.hip; keys >= kv_valid zero
   uint16_t* o;             // [B][Sq][H][128]
   float* part;             // partial records for split tiles
   int64_t part_slots;      // records available at part
-  int32_t B, H, Sq, Sq_pad, Sk_pad, q_valid, kv_valid;
-  // Schedule, filled in by launch_attention: valid tiles (query block below
-  // q_valid) are numbered g = (b*H + h) * nqv + query block; tiles g < n_whole
-  // run whole, the n_split tiles after them are split over n_split_blocks
-  // workgroups; tiles past q_valid only write zeros.
+  int32_t B, H, Sq, Sk, Sq_pad, Sk_pad, q_valid, kv_valid;
+  int32_t Hkv;             // key/value heads; query head h reads kv head h / (H / Hkv)
+  int32_t causal;          // key j visible to query row i only if j <= i
+  const int32_t* lengths;  // optional per-item valid lengths (device), see item_valid()
+  // Schedule, filled in by launch_attention. Uniform mode (no causal mask,
+  // no per-item lengths): valid tiles (query block below q_valid) are
+  // numbered g = (b*H + h) * nqv + query block; tiles g < n_whole run whole,
+  // the n_split tiles after them are split over n_split_blocks workgroups;
+  // tiles past q_valid only write zeros. General mode: one workgroup per
+  // (b, h, query block), each finding its own key range.
+  int32_t general;
   int32_t nqv, n_whole, n_split, n_split_blocks;
 };
 

@@ -16,7 +16,8 @@
 // with full-width coalesced 16-byte accesses; the mean of squares and the
 // rotate-half partners move between lanes with DPP. A thread handles the q
 // row and the k row at the same (b, s, h), so each rotary table row is read
-// once for both; outputs are streamed with non-temporal stores.
+// once for both; inputs and outputs are streamed with non-temporal loads and
+// stores.
 #include "h3attn_internal.h"
 
 namespace h3 {
@@ -55,7 +56,7 @@ typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));
 
 struct ProArgs {
   ProTensor t0, t1;
-  int32_t B, H;
+  int32_t B, H;            // H = the larger head count of the two tensors
   float eps;
   const float* cos;
   const float* sin;
@@ -97,9 +98,12 @@ __global__ __launch_bounds__(kProThreads) void qk_prologue_kernel(ProArgs a) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const ProTensor& T = t ? a.t1 : a.t0;
-      live[t] = live_u && s < T.S_out;
-      load[t] = live[t] && s < T.S_valid;
-      x[t] = load[t] ? *reinterpret_cast<const v4u_t*>(T.in + b * T.in_sb + s * T.in_ss + h * T.in_sh + c * 8)
+      live[t] = live_u && h < T.H && s < T.S_out;
+      load[t] = live[t] && s < item_valid(T.lengths, (int)b, T.which, T.S_valid, T.S_valid);
+      // Streamed once: non-temporal loads (measured ~4% faster than cached
+      // loads at the full workload).
+      x[t] = load[t] ? __builtin_nontemporal_load(
+                           reinterpret_cast<const v4u_t*>(T.in + b * T.in_sb + s * T.in_ss + h * T.in_sh + c * 8))
                      : v4u_t{0u, 0u, 0u, 0u};
     }
     float cs[8], sn[8];
@@ -174,13 +178,14 @@ __global__ __launch_bounds__(256) void rope_tables_kernel(float* cos_out, float*
 
 }  // namespace
 
-hipError_t launch_qk_prologue(const ProTensor& t0, const ProTensor& t1, int32_t B, int32_t H,
+hipError_t launch_qk_prologue(const ProTensor& t0, const ProTensor& t1, int32_t B,
                               float eps, const float* rope_cos, const float* rope_sin,
                               hipStream_t stream) {
   ProArgs a;
   a.t0 = t0;
   a.t1 = t1;
   a.B = B;
+  const int32_t H = t0.H > t1.H ? t0.H : t1.H;
   a.H = H;
   a.eps = eps;
   a.cos = rope_cos;

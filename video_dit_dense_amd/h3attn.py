@@ -42,6 +42,24 @@ SIGNATURES = {
 STAGE_PREPARE = 1
 STAGE_ATTEND = 2
 
+
+class ForwardArgs(ctypes.Structure):
+    """Mirror of h3attn_forward_args (include/h3attn.h)."""
+    _fields_ = [
+        ("q", _P), ("k", _P), ("v", _P), ("o", _P),
+        ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3), ("v_stride", ctypes.c_int64 * 3),
+        ("B", _I), ("Sq", _I), ("Sk", _I), ("Hq", _I), ("Hkv", _I), ("head_dim", _I),
+        ("q_norm_w", _P), ("k_norm_w", _P), ("eps", _F),
+        ("rope_rows", _I), ("rope_cos", _P), ("rope_sin", _P),
+        ("q_valid", _I), ("kv_valid", _I), ("valid_lengths", _P), ("causal", _I),
+        ("softmax_scale", _F),
+    ]
+
+
+SIGNATURES["h3attn_forward_ex_workspace_bytes"] = (ctypes.c_size_t, [ctypes.POINTER(ForwardArgs)])
+SIGNATURES["h3attn_forward_ex"] = (ctypes.c_int, [ctypes.POINTER(ForwardArgs), _P, ctypes.c_size_t,
+                                                  ctypes.c_uint32, _P])
+
 _lib = None
 
 
@@ -84,7 +102,10 @@ def _stream(device: torch.device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _check_bshd(name: str, t: torch.Tensor) -> None:
+def _check_bshd(name: str, t: torch.Tensor, view: bool = False) -> None:
+    """A bf16 [B, S, H, 128] GPU tensor; contiguous, or with `view` any
+    strided view whose channels are contiguous (e.g. a slice of a fused QKV
+    projection)."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
@@ -93,7 +114,10 @@ def _check_bshd(name: str, t: torch.Tensor) -> None:
         raise ValueError(f"{name} must be bfloat16 (got {t.dtype}); the library is bf16-only")
     if t.dim() != 4 or t.shape[-1] != HEAD_DIM:
         raise ValueError(f"{name} must be [B, S, H, {HEAD_DIM}] (got {tuple(t.shape)})")
-    if not t.is_contiguous():
+    if view:
+        if t.stride(-1) != 1 or min(t.stride()) < 0:
+            raise ValueError(f"{name} must have contiguous channels and non-negative strides")
+    elif not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous BSHD")
     if t.requires_grad and torch.is_grad_enabled():
         raise RuntimeError(f"{name} requires grad: h3attn is inference-only (no backward)")
@@ -161,35 +185,86 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             rope_cos: torch.Tensor | None = None, rope_sin: torch.Tensor | None = None,
             q_valid: int | None = None, kv_valid: int | None = None, scale: float | None = None,
             out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-            stages: int = STAGE_PREPARE | STAGE_ATTEND) -> torch.Tensor:
+            stages: int = STAGE_PREPARE | STAGE_ATTEND, causal: bool = False,
+            valid_lengths: torch.Tensor | None = None) -> torch.Tensor:
     """The attention step: prologue on q/k (if weights/tables given), then
-    dense non-causal attention with key-padding (kv_valid) and a zeroed query
-    tail (q_valid). Returns o [B, Sq, H, 128] bf16. `stages` selects the
-    prepare and/or attend stage (h3attn_forward_stages); a lone attend stage
-    needs `workspace` from an earlier prepare call with the same arguments."""
+    softmax attention with key padding (kv_valid) and a zeroed query tail
+    (q_valid). Returns o [B, Sq, Hq, 128] bf16.
+
+    k and v may have fewer heads than q (grouped heads: query head h reads
+    kv head h // (Hq // Hkv)); q, k and v may be strided views with
+    contiguous channels. `causal` masks key j for query row i when j > i.
+    `valid_lengths`, an int32 GPU tensor [B, 2] of (q_valid, kv_valid) per
+    batch item, replaces q_valid / kv_valid. `stages` selects the prepare
+    and/or attend stage; a lone attend stage needs `workspace` from an earlier
+    prepare call with the same arguments. Dense inputs without the variants
+    go through h3attn_forward_stages, everything else through
+    h3attn_forward_ex."""
     lib = load_library()
     for name, t in (("q", q), ("k", k), ("v", v)):
-        _check_bshd(name, t)
+        _check_bshd(name, t, view=True)
     _check_f32("w_q", w_q, HEAD_DIM)
     _check_f32("w_k", w_k, HEAD_DIM)
     _check_f32("rope_cos", rope_cos)
     _check_f32("rope_sin", rope_sin)
     B, Sq, H, D = q.shape
-    Sk = k.shape[1]
-    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != H:
-        raise ValueError("k and v must be [B, Sk, H, 128] with q's B and H")
-    o = torch.empty_like(q) if out is None else out
+    Sk, Hkv = k.shape[1], k.shape[2]
+    if k.shape != v.shape or k.shape[0] != B or H % Hkv != 0:
+        raise ValueError("k and v must be [B, Sk, Hkv, 128] with q's B and Hkv dividing q's heads")
+    if valid_lengths is not None:
+        if (valid_lengths.device.type != "cuda" or valid_lengths.dtype != torch.int32
+                or tuple(valid_lengths.shape) != (B, 2) or not valid_lengths.is_contiguous()):
+            raise ValueError("valid_lengths must be a contiguous int32 GPU tensor [B, 2]")
+    o = torch.empty(B, Sq, H, D, dtype=q.dtype, device=q.device) if out is None else out
     _check_bshd("out", o)
-    ws = make_workspace(B, Sq, Sk, H, q.device) if workspace is None else workspace
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     rows = 0 if rope_cos is None else rope_cos.shape[0]
     if stages != (STAGE_PREPARE | STAGE_ATTEND) and workspace is None:
         raise ValueError("a single stage needs a caller-kept workspace")
-    st = lib.h3attn_forward_stages(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, Sq, Sk, H, D,
-                                   _ptr(w_q), _ptr(w_k), float(eps), _ptr(rope_cos), _ptr(rope_sin), rows,
-                                   -1 if q_valid is None else int(q_valid),
-                                   -1 if kv_valid is None else int(kv_valid),
-                                   scale, _ptr(ws), ws.numel() * ws.element_size(), int(stages),
-                                   _stream(q.device))
-    _check(st, "h3attn_forward_stages")
+    plain = (Hkv == H and not causal and valid_lengths is None
+             and q.is_contiguous() and k.is_contiguous() and v.is_contiguous())
+    if plain:
+        ws = make_workspace(B, Sq, Sk, H, q.device) if workspace is None else workspace
+        st = lib.h3attn_forward_stages(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, Sq, Sk, H, D,
+                                       _ptr(w_q), _ptr(w_k), float(eps), _ptr(rope_cos), _ptr(rope_sin), rows,
+                                       -1 if q_valid is None else int(q_valid),
+                                       -1 if kv_valid is None else int(kv_valid),
+                                       scale, _ptr(ws), ws.numel() * ws.element_size(), int(stages),
+                                       _stream(q.device))
+        _check(st, "h3attn_forward_stages")
+        return o
+    a = ForwardArgs()
+    a.q, a.k, a.v, a.o = q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr()
+    for field, t in (("q_stride", q), ("k_stride", k), ("v_stride", v)):
+        getattr(a, field)[:] = [t.stride(0), t.stride(1), t.stride(2)]
+    a.B, a.Sq, a.Sk, a.Hq, a.Hkv, a.head_dim = B, Sq, Sk, H, Hkv, D
+    a.q_norm_w = None if w_q is None else w_q.data_ptr()
+    a.k_norm_w = None if w_k is None else w_k.data_ptr()
+    a.eps = float(eps)
+    a.rope_rows = rows
+    a.rope_cos = None if rope_cos is None else rope_cos.data_ptr()
+    a.rope_sin = None if rope_sin is None else rope_sin.data_ptr()
+    a.q_valid = -1 if q_valid is None else int(q_valid)
+    a.kv_valid = -1 if kv_valid is None else int(kv_valid)
+    a.valid_lengths = None if valid_lengths is None else valid_lengths.data_ptr()
+    a.causal = 1 if causal else 0
+    a.softmax_scale = scale
+    if workspace is None:
+        n = int(lib.h3attn_forward_ex_workspace_bytes(ctypes.byref(a)))
+        if n == 0:
+            raise ValueError("bad sizes for the workspace")
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
+    st = lib.h3attn_forward_ex(ctypes.byref(a), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                               int(stages), _stream(q.device))
+    _check(st, "h3attn_forward_ex")
     return o
+
+
+def forward_ex_workspace_bytes(B: int, Sq: int, Sk: int, Hq: int, Hkv: int, causal: bool = False,
+                               per_item_lengths: bool = False) -> int:
+    """Workspace bytes h3attn_forward_ex needs for these sizes and variant."""
+    a = ForwardArgs()
+    a.B, a.Sq, a.Sk, a.Hq, a.Hkv, a.head_dim = B, Sq, Sk, Hq, Hkv, HEAD_DIM
+    a.causal = 1 if causal else 0
+    a.valid_lengths = 16 if per_item_lengths else None   # only NULL or not matters here
+    return int(load_library().h3attn_forward_ex_workspace_bytes(ctypes.byref(a)))

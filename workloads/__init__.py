@@ -111,14 +111,16 @@ def _normal_bf16(rng: np.random.Generator, shape) -> np.ndarray:
 
 
 def make_inputs(B: int, Sq: int, Sk: int, H: int, seed: int,
-                weight_sigma: float = 0.1) -> Inputs:
-    """Draw q, k, v ~ N(0,1) (float32, then RNE to bf16) and RMSNorm weights
-    1 + weight_sigma*N(0,1) (float64, rounded to bf16-representable values and
-    stored as float32), in that order, from numpy's PCG64 with `seed`."""
+                weight_sigma: float = 0.1, Hkv: int | None = None) -> Inputs:
+    """Draw q [B, Sq, H], k and v [B, Sk, Hkv] (Hkv defaults to H) ~ N(0,1)
+    (float32, then RNE to bf16) and RMSNorm weights 1 + weight_sigma*N(0,1)
+    (float64, rounded to bf16-representable values and stored as float32),
+    in that order, from numpy's PCG64 with `seed`."""
     rng = np.random.default_rng(seed)
+    Hkv = H if Hkv is None else Hkv
     q = _normal_bf16(rng, (B, Sq, H, HEAD_DIM))
-    k = _normal_bf16(rng, (B, Sk, H, HEAD_DIM))
-    v = _normal_bf16(rng, (B, Sk, H, HEAD_DIM))
+    k = _normal_bf16(rng, (B, Sk, Hkv, HEAD_DIM))
+    v = _normal_bf16(rng, (B, Sk, Hkv, HEAD_DIM))
     w = []
     for _ in range(2):
         w64 = 1.0 + weight_sigma * rng.standard_normal(HEAD_DIM)

@@ -152,3 +152,63 @@ def test_python_wrapper_rejections():
         h3attn.forward(q.float(), q, q)
     with pytest.raises(TypeError):
         h3attn._check_bshd("q", q.numpy())
+
+
+def fwd_ex(lib, stages=3, ws=16 * A, wsb=None, **kw):
+    """h3attn_forward_ex with a valid descriptor of fake pointers, then the
+    fields in kw overridden; the call fails validation or the device gate."""
+    a = h3attn.ForwardArgs()
+    a.q, a.k, a.v, a.o = A, 2 * A, 3 * A, 4 * A
+    a.B, a.Sq, a.Sk, a.Hq, a.Hkv, a.head_dim = 1, 8, 8, 4, 2, 128
+    a.q_norm_w, a.k_norm_w, a.eps = 5 * A, 5 * A + 512, 1e-6
+    a.rope_rows, a.rope_cos, a.rope_sin = 8, 6 * A, 7 * A
+    a.q_valid, a.kv_valid, a.valid_lengths, a.causal, a.softmax_scale = -1, -1, None, 0, 0.0883
+    for key, val in kw.items():
+        if key.endswith("_stride"):
+            getattr(a, key)[:] = val
+        else:
+            setattr(a, key, val)
+    if wsb is None:
+        wsb = lib.h3attn_forward_ex_workspace_bytes(ctypes.byref(a))
+    return lib.h3attn_forward_ex(ctypes.byref(a), P(ws), wsb, stages, None)
+
+
+def test_forward_ex_workspace_bytes(lib):
+    # q rows for Hq heads, k and v^T rows for Hkv heads, partial records only
+    # for the uniform schedule (no causal mask, no per-item lengths)
+    rec = (64 + 2) * 512 * 4
+    assert h3attn.forward_ex_workspace_bytes(1, 104448, 104448, 6, 2) == \
+        (6 + 2 * 2) * 104448 * 256 + 2 * 256 * rec
+    assert h3attn.forward_ex_workspace_bytes(1, 104448, 104448, 6, 2, causal=True) == (6 + 2 * 2) * 104448 * 256
+    assert h3attn.forward_ex_workspace_bytes(2, 1000, 300, 4, 1, per_item_lengths=True) == \
+        2 * (4 * 1024 + 2 * 1 * 512) * 256
+    assert h3attn.forward_ex_workspace_bytes(1, 8, 8, 6, 4) == 0      # 6 heads do not group into 4
+    assert h3attn.forward_ex_workspace_bytes(1, 8, 8, 4, 0) == 0
+    assert lib.h3attn_forward_ex_workspace_bytes(None) == 0
+
+
+def test_forward_ex_validation(lib):
+    assert lib.h3attn_forward_ex(None, P(16 * A), 1 << 20, 3, None) == NULLP
+    assert fwd_ex(lib, v=None) == NULLP
+    assert fwd_ex(lib, stages=0) == VALUE
+    assert fwd_ex(lib, Hkv=3, wsb=1 << 30) == SHAPE            # 4 query heads do not group into 3
+    assert fwd_ex(lib, Hkv=0, wsb=1 << 30) == SHAPE
+    assert fwd_ex(lib, causal=2) == VALUE
+    assert fwd_ex(lib, kv_valid=0) == SHAPE                    # uniform lengths need a valid key
+    assert fwd_ex(lib, q_stride=[8 * 4 * 128, 4 * 128, -128]) == SHAPE
+    assert fwd_ex(lib, k_stride=[2048, 260, 128]) == ALIGN     # rows must stay 16-byte aligned
+    assert fwd_ex(lib, valid_lengths=9 * A + 2) == ALIGN
+    assert fwd_ex(lib, valid_lengths=4 * A + 64) == ALIAS      # lengths inside o
+    # a strided q whose rows reach over o
+    assert fwd_ex(lib, q_stride=[0, 3 * A // 2, 128]) == ALIAS
+    assert fwd_ex(lib, wsb=4096) == WS
+    assert fwd_ex(lib, ws=0) == WS
+    assert fwd_ex(lib, o=A + 1024) == ALIAS                    # o on top of q
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="device gate is checked on a machine without a GPU")
+def test_forward_ex_device_gate_without_gpu(lib):
+    assert fwd_ex(lib) == DEVICE
+    assert fwd_ex(lib, causal=1) == DEVICE
+    assert fwd_ex(lib, valid_lengths=9 * A, kv_valid=0) == DEVICE   # per-item lengths replace kv_valid
+    assert fwd_ex(lib, q_stride=[8 * 12 * 128, 12 * 128, 128], k_stride=[8 * 12 * 128, 12 * 128, 128]) == DEVICE

@@ -68,32 +68,37 @@ def cpu_baseline(wl, inp, target_s: float):
         threads = max([d.get("num_threads", 1) for d in info if d.get("user_api") == "blas"] or [1])
     except Exception:  # noqa: BLE001
         threads = None
-    q1, k1, v1 = inp.q[:, :, :1].copy(), inp.k[:, :, :1].copy(), inp.v[:, :, :1].copy()
+    # Item 0, query head 0 and the key/value head it reads (head 0).
+    q1, k1, v1 = inp.q[:1, :, :1].copy(), inp.k[:1, :, :1].copy(), inp.v[:1, :, :1].copy()
     theta = wl.theta if wl.rope else None
+    qv0, kvv0 = wl.item_lengths()[0]
 
     def run(n_rows):
-        rows = np.sort(np.random.default_rng(99).choice(wl.q_valid, size=n_rows, replace=False))
+        rows = np.sort(np.random.default_rng(99).choice(qv0, size=n_rows, replace=False))
         t0 = time.perf_counter()
-        oracle.forward(q1, k1, v1, inp.w_q, inp.w_k, wl.eps, theta, wl.scale, wl.q_valid, wl.kv_valid,
-                       norm=wl.norm, rows=rows)
-        return time.perf_counter() - t0
+        oracle.forward(q1, k1, v1, inp.w_q, inp.w_k, wl.eps, theta, wl.scale, qv0, kvv0,
+                       norm=wl.norm, rows=rows, causal=wl.causal)
+        return time.perf_counter() - t0, rows
 
     # Fixed cost (prologue over all rows of the head) plus a per-row cost:
     # fit t(n) = t0 + t1*n from two probes, then size the timed run.
     n1, n2 = 128, 512
-    ta, tb = run(n1), run(n2)
+    ta, _ = run(n1)
+    tb, _ = run(n2)
     per_row = max((tb - ta) / (n2 - n1), 1e-6)
     fixed = max(ta - per_row * n1, 0.0)
-    n = int(min(wl.q_valid, max(n2, (target_s - fixed) / per_row)))
-    t = run(n)
-    flops = 4.0 * n * wl.kv_valid * 128 * 1
+    n = int(min(qv0, max(n2, (target_s - fixed) / per_row)))
+    t, rows = run(n)
+    keys = np.minimum(rows + 1, kvv0) if wl.causal else np.full(len(rows), kvv0)
+    flops = 4.0 * float(keys.sum()) * 128
     return {
         "value": flops / t / 1e12,
         "unit": "TFLOP/s",
         "cores": threads if threads is not None else len(os.sched_getaffinity(0)),
         "kind": "oracle",
-        "sample": f"fp64 NumPy oracle, head 0 of {wl.H}, {n} of {wl.q_valid} query rows against all "
-                  f"{wl.kv_valid} keys, prologue included, {t:.1f} s wall",
+        "sample": f"fp64 NumPy oracle, item 0, head 0 of {wl.H}, {n} of {qv0} query rows against "
+                  f"{'their causal prefix of ' if wl.causal else 'all '}{kvv0} keys, prologue included, "
+                  f"{t:.1f} s wall",
         "seconds": t,
     }
 
@@ -103,7 +108,9 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="full", help="workload name (default: full)")
+    ap.add_argument("--workload", default="full",
+                    help="workload name (default: full); also the attention variants "
+                         + ", ".join(sorted(__import__("workloads").VARIANT_WORKLOADS)))
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-baseline duration")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prologue-reps", type=int, default=20)
@@ -137,7 +144,9 @@ def main() -> int:
         print(json.dumps({"only": "copy", "bytes_read_per_launch": n, "bytes_written_per_launch": n,
                           "launches": args.warmup + args.steps}), flush=True)
         return 0
-    wl = workloads.WORKLOADS[args.workload]
+    all_wl = {**workloads.WORKLOADS, **workloads.VARIANT_WORKLOADS}
+    wl = all_wl[args.workload]
+    variant = args.workload in workloads.VARIANT_WORKLOADS
     log(f"workload {wl.name}: {wl.description}")
     t0 = time.perf_counter()
     inp = workloads.make_workload_inputs(wl)
@@ -152,13 +161,19 @@ def main() -> int:
     cos = sin = None
     if wl.rope:
         cos, sin = h3attn.rope_tables(max(wl.Sq, wl.Sk), wl.theta)
-    ws = h3attn.make_workspace(wl.B, wl.Sq, wl.Sk, wl.H)
+    lengths = (torch.tensor(wl.lengths, dtype=torch.int32, device="cuda:0") if wl.lengths else None)
+    if variant:
+        nbytes = h3attn.forward_ex_workspace_bytes(wl.B, wl.Sq, wl.Sk, wl.H, wl.kv_heads, causal=wl.causal,
+                                                   per_item_lengths=lengths is not None)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    else:
+        ws = h3attn.make_workspace(wl.B, wl.Sq, wl.Sk, wl.H)
     o = torch.empty_like(q)
 
     def stage(st):
         h3attn.forward(q, k, v, w_q if wl.norm else None, w_k if wl.norm else None, wl.eps, cos, sin,
-                       q_valid=wl.q_valid, kv_valid=wl.kv_valid, scale=wl.scale, out=o, workspace=ws,
-                       stages=st)
+                       q_valid=None if wl.lengths else wl.q_valid, kv_valid=None if wl.lengths else wl.kv_valid,
+                       scale=wl.scale, out=o, workspace=ws, stages=st, causal=wl.causal, valid_lengths=lengths)
 
     if args.only == "attention":
         stage(h3attn.STAGE_PREPARE)
@@ -197,25 +212,40 @@ def main() -> int:
     log(f"timed {args.steps} steps: {ms_step:.3f} ms/step, attend stage {attn_avg:.3f} ms "
         f"(min {min(attn_ms):.3f}, max {max(attn_ms):.3f}), prepare {prep_avg:.3f} ms")
 
-    # Stand-alone prologue (h3attn_qk_prologue, BSHD in, BSHD out), HBM roofline.
-    qo, ko = torch.empty_like(q), torch.empty_like(k)
-    for _ in range(3):
-        h3attn.qk_prologue(q, k, w_q if wl.norm else None, w_k if wl.norm else None, wl.eps, cos, sin, qo, ko)
-    pe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    torch.cuda.synchronize()
-    pe[0].record()
-    for _ in range(args.prologue_reps):
-        h3attn.qk_prologue(q, k, w_q if wl.norm else None, w_k if wl.norm else None, wl.eps, cos, sin, qo, ko)
-    pe[1].record()
-    torch.cuda.synchronize()
-    pro_ms = pe[0].elapsed_time(pe[1]) / args.prologue_reps
-    pro_gbs = wl.prologue_bytes() / (pro_ms * 1e-3) / 1e9
-    log(f"prologue: {pro_ms * 1e3:.1f} us, {pro_gbs:.0f} GB/s")
+    # Stand-alone prologue (h3attn_qk_prologue, BSHD in, BSHD out), HBM
+    # roofline; measured on the workloads whose q and k share head count and
+    # valid lengths (the stand-alone entry point's contract).
+    prologue = None
+    if wl.kv_heads == wl.H and not wl.lengths:
+        qo, ko = torch.empty_like(q), torch.empty_like(k)
+        for _ in range(3):
+            h3attn.qk_prologue(q, k, w_q if wl.norm else None, w_k if wl.norm else None, wl.eps, cos, sin, qo, ko)
+        pe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        pe[0].record()
+        for _ in range(args.prologue_reps):
+            h3attn.qk_prologue(q, k, w_q if wl.norm else None, w_k if wl.norm else None, wl.eps, cos, sin, qo, ko)
+        pe[1].record()
+        torch.cuda.synchronize()
+        pro_ms = pe[0].elapsed_time(pe[1]) / args.prologue_reps
+        pro_gbs = wl.prologue_bytes() / (pro_ms * 1e-3) / 1e9
+        log(f"prologue: {pro_ms * 1e3:.1f} us, {pro_gbs:.0f} GB/s")
+        prologue = {
+            "kernel": "qk_prologue_kernel (h3attn_qk_prologue, BSHD)",
+            "bound": "hbm",
+            "avg_us": round(pro_ms * 1e3, 2),
+            "achieved": round(pro_gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(pro_gbs / PEAK_HBM_GBS, 4),
+            "bytes": wl.prologue_bytes(),
+        }
 
     achieved = flops / (attn_avg * 1e-3) / 1e12
-    traffic = measured_traffic()
+    # The committed counters were taken on the full workload only.
+    traffic = measured_traffic() if wl.name == "full" else None
     result = {
-        "metric": METRIC,
+        "metric": METRIC if wl.name == "full" else f"attention fwd TFLOP/s + % bf16 MFMA peak, {wl.name}: {wl.description}",
         "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -228,8 +258,9 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": f"{wl.name}: B={wl.B} Sq={wl.Sq} Sk={wl.Sk} H={wl.H} d=128 q_valid={wl.q_valid} "
-                        f"kv_valid={wl.kv_valid} norm={wl.norm} rope={'96/128' if wl.rope else 'off'}",
+            "workload": f"{wl.name}: B={wl.B} Sq={wl.Sq} Sk={wl.Sk} H={wl.H} Hkv={wl.kv_heads} d=128 "
+                        + (f"lengths={list(wl.lengths)} " if wl.lengths else f"q_valid={wl.q_valid} kv_valid={wl.kv_valid} ")
+                        + f"causal={wl.causal} norm={wl.norm} rope={'96/128' if wl.rope else 'off'}",
             "flop_per_step": flops,
             "step": "prepare (RMSNorm+RoPE prologue, key-major v) + attention forward",
         },
@@ -243,16 +274,7 @@ def main() -> int:
             "traffic": traffic,
             "avg_ms": round(attn_avg, 4),
         },
-        "prologue": {
-            "kernel": "qk_prologue_kernel (h3attn_qk_prologue, BSHD)",
-            "bound": "hbm",
-            "avg_us": round(pro_ms * 1e3, 2),
-            "achieved": round(pro_gbs, 1),
-            "peak": PEAK_HBM_GBS,
-            "unit": "GB/s",
-            "frac": round(pro_gbs / PEAK_HBM_GBS, 4),
-            "bytes": wl.prologue_bytes(),
-        },
+        "prologue": prologue,
         "prepare_stage_ms": round(prep_avg, 4),
     }
     if not args.no_cpu_baseline:

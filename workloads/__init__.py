@@ -38,6 +38,13 @@ class Workload:
     eps: float = 1e-6
     theta: float = 1e4
     description: str = ""
+    causal: bool = False  # key j visible to query row i only if j <= i
+    Hkv: int = 0          # key/value heads (0: same as H)
+    lengths: tuple = ()   # per-item (q_valid, kv_valid) pairs, replacing q_valid / kv_valid
+
+    @property
+    def kv_heads(self) -> int:
+        return self.Hkv or self.H
 
     @property
     def D(self) -> int:
@@ -47,9 +54,22 @@ class Workload:
     def scale(self) -> float:
         return 1.0 / float(np.sqrt(HEAD_DIM))
 
+    def item_lengths(self) -> list:
+        """(q_valid, kv_valid) of every batch item."""
+        return list(self.lengths) if self.lengths else [(self.q_valid, self.kv_valid)] * self.B
+
     def attention_flops(self) -> float:
-        """4 * Sq_valid * Sk_valid * d * H * B: QK^T and PV, 2 flop per MAC."""
-        return 4.0 * self.q_valid * self.kv_valid * HEAD_DIM * self.H * self.B
+        """QK^T and PV at 2 flop per multiply-add: 4 * d * H per visible
+        (query, key) pair, summed over the items' valid rows and keys; under
+        the causal mask row i sees min(i + 1, kv_valid) keys."""
+        pairs = 0
+        for qv, kvv in self.item_lengths():
+            if self.causal:
+                m = min(qv, kvv)   # rows 0..m-1 see i + 1 keys, the rest all kv_valid
+                pairs += m * (m + 1) // 2 + (qv - m) * kvv
+            else:
+                pairs += qv * kvv
+        return 4.0 * pairs * HEAD_DIM * self.H
 
     def nominal_flops(self) -> float:
         return 4.0 * self.Sq * self.Sk * HEAD_DIM * self.H * self.B
@@ -58,7 +78,7 @@ class Workload:
         """Compulsory HBM bytes of the stand-alone Q/K prologue: read and write
         q and k in bf16, read the fp32 cos/sin tables (48 pairs per row) when
         rotary is on, and the two fp32 weight vectors."""
-        qk = 2 * 2 * self.B * (self.Sq + self.Sk) * self.H * HEAD_DIM
+        qk = 2 * 2 * self.B * (self.Sq * self.H + self.Sk * self.kv_heads) * HEAD_DIM
         tables = 2 * 4 * 48 * max(self.Sq, self.Sk) if self.rope else 0
         return qk + tables + 2 * 4 * HEAD_DIM
 
@@ -76,6 +96,21 @@ WORKLOADS = {
     "full": Workload("full", 1, 104448, 104448, 6, 104448, 104448, True, True, 4,
                      description="B=1 S=104448 packed rows (345 frames at 1344x768), H=6, "
                                  "prologue on, no mask"),
+}
+
+# Attention variants of the FastVideo PR #1799 backend ("Implementation":
+# GQA, causal attention, padding masks), at the full workload's shape or a
+# batch of unequal items. Measured beside the workloads above; not H3's own
+# shapes (H3 is non-causal multi-head attention).
+VARIANT_WORKLOADS = {
+    "full_causal": Workload("full_causal", 1, 104448, 104448, 6, 104448, 104448, True, True, 4,
+                            description="full shape with the causal mask", causal=True),
+    "full_gqa": Workload("full_gqa", 1, 104448, 104448, 6, 104448, 104448, True, True, 4,
+                         description="full shape, 6 query heads on 2 key/value heads", Hkv=2),
+    "batch_varlen": Workload("batch_varlen", 4, 32768, 32768, 8, 32768, 32768, True, True, 5,
+                             description="B=4 padded to 32768 rows, items valid for 32768, 24576, "
+                                         "16384 and 8192 query rows and keys, H=8",
+                             lengths=((32768, 32768), (24576, 24576), (16384, 16384), (8192, 8192))),
 }
 
 
@@ -129,7 +164,7 @@ def make_inputs(B: int, Sq: int, Sk: int, H: int, seed: int,
 
 
 def make_workload_inputs(wl: Workload, seed: int | None = None) -> Inputs:
-    return make_inputs(wl.B, wl.Sq, wl.Sk, wl.H, wl.seed if seed is None else seed)
+    return make_inputs(wl.B, wl.Sq, wl.Sk, wl.H, wl.seed if seed is None else seed, Hkv=wl.kv_heads)
 
 
 def sample_rows(S: int, valid: int, count: int, seed: int, tile: int = 256) -> np.ndarray:

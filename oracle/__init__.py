@@ -31,6 +31,9 @@ per-head norm with one [128] weight shared by all heads, eps inside the square
 root, weight multiplied as given; rotary frequency theta^(-2j/96) over the 96
 rotated channels; 1-D positions 0..S-1; no rounding between steps.
 
+The fused RMSNorm + indexed AdaLN scale/shift step has its own module,
+`oracle.scale_shift`, with bf16 rounding boundaries instead of fp64 results.
+
 Every function here is pinned by `tests/test_oracle_pins.py` against brute
 force on tiny inputs, closed forms, invariants and torch's CPU float64 SDPA.
 """

@@ -13,6 +13,9 @@ attention modes"), video-to-text cross-attention (FastVideo PR #1799,
 "Implementation": dense self- and cross-attention) and one GPU's 6-head
 share of the ~104k-row 345-frame packed sequence under Ulysses-8 (SGLang
 PR #37903, "Motivation" table).
+
+The scale/shift workloads at the end are the shapes of the DiT block's
+RMSNorm + indexed AdaLN modulation step that feeds the QKV projection.
 """
 from __future__ import annotations
 
@@ -178,3 +181,77 @@ def sample_rows(S: int, valid: int, count: int, seed: int, tile: int = 256) -> n
     extra = rng.choice(S, size=min(count, S), replace=False)
     rows = np.array(sorted(set(int(r) for r in must) | set(int(r) for r in extra)), dtype=np.int64)
     return rows
+
+
+# ------------------------------------------------- RMSNorm + indexed scale/shift
+
+@dataclasses.dataclass(frozen=True)
+class ScaleShiftWorkload:
+    """Shapes of the DiT block's RMSNorm + indexed AdaLN scale/shift step
+    (TeleFuser PR #37, "2.5 Fuse RMSNorm with indexed AdaLN modulation"):
+    hidden states [B, S, D], M modulation rows per batch item, one index per
+    token."""
+    name: str
+    B: int
+    S: int
+    D: int
+    M: int
+    seed: int
+    weight: bool = False   # an fp32 RMSNorm weight (the usual DiT block norm has none)
+    index: str = "frames"  # "frames": token s takes row s*M//S; "random": uniform; "none": no index (row 0)
+    eps: float = 1e-6
+    description: str = ""
+
+    def bytes(self) -> int:
+        """Compulsory HBM bytes: x read and y written (bf16), the scale and
+        shift rows read once, the int32 index and the fp32 weight."""
+        xy = 2 * 2 * self.B * self.S * self.D
+        mod = 2 * 2 * self.B * self.M * self.D
+        idx = 4 * self.B * self.S if self.index != "none" else 0
+        return xy + mod + idx + (4 * self.D if self.weight else 0)
+
+
+SCALE_SHIFT_WORKLOADS = {
+    "ss_tiny": ScaleShiftWorkload("ss_tiny", 2, 100, 520, 3, 20, weight=True, index="random",
+                                  description="B=2 S=100 D=520 (a ragged last chunk), M=3, random index, weight"),
+    "ss_mid": ScaleShiftWorkload("ss_mid", 1, 4096, 3072, 8, 21,
+                                 description="B=1 S=4096 D=3072, 8 frames of 512 tokens"),
+    "ss_shard": ScaleShiftWorkload("ss_shard", 1, 13056, 6144, 4, 22,
+                                   description="one GPU's 13056-row share of the 104448-row sequence under "
+                                               "8-way sequence parallelism, hidden width 6144 (48 heads x 128), "
+                                               "4 frames of modulation"),
+}
+
+
+@dataclasses.dataclass
+class ScaleShiftInputs:
+    x: np.ndarray            # uint16 bf16 bits [B, S, D]
+    scale: np.ndarray        # uint16 bf16 bits [B, M, D]
+    shift: np.ndarray        # uint16 bf16 bits [B, M, D]
+    index: np.ndarray | None  # int32 [B, S]
+    w: np.ndarray | None     # float32 [D], bf16-representable
+
+
+def make_scale_shift_inputs(wl: ScaleShiftWorkload, seed: int | None = None,
+                            x_sigma: float = 1.0) -> ScaleShiftInputs:
+    """Draw, in this order from PCG64 with `seed`: x ~ x_sigma*N(0,1), scale
+    and shift ~ 0.2*N(0,1) (float32, then RNE to bf16), the weight 1 +
+    0.1*N(0,1) (bf16-representable, stored as float32) when the workload has
+    one, then a uniform index when the workload asks for a random one."""
+    rng = np.random.default_rng(wl.seed if seed is None else seed)
+    x = f32_to_bf16_bits((rng.standard_normal((wl.B, wl.S, wl.D), dtype=np.float32)
+                          * np.float32(x_sigma)).astype(np.float32))
+    scale = f32_to_bf16_bits(rng.standard_normal((wl.B, wl.M, wl.D), dtype=np.float32) * np.float32(0.2))
+    shift = f32_to_bf16_bits(rng.standard_normal((wl.B, wl.M, wl.D), dtype=np.float32) * np.float32(0.2))
+    w = None
+    if wl.weight:
+        w64 = 1.0 + 0.1 * rng.standard_normal(wl.D)
+        w = bf16_bits_to_f32(f32_to_bf16_bits(w64.astype(np.float32)))
+    if wl.index == "random":
+        index = rng.integers(0, wl.M, (wl.B, wl.S)).astype(np.int32)
+    elif wl.index == "frames":
+        index = np.broadcast_to((np.arange(wl.S, dtype=np.int64) * wl.M // wl.S).astype(np.int32),
+                                (wl.B, wl.S)).copy()
+    else:
+        index = None
+    return ScaleShiftInputs(x, scale, shift, index, w)

@@ -89,7 +89,7 @@ def inv_rms(x_bits, eps: float):
     r64 = 1.0 / np.sqrt(ms + float(np.float32(eps)))
     r = r64.astype(np.float32)
     lo, hi = _f32_neighbours(r64, AMBIGUITY_REL)
-    return r, lo != hi, lo, hi
+    return r, (lo != hi) & np.isfinite(r64), lo, hi
 
 
 def inv_rms_exact(row_bits, eps: float) -> np.float32:

@@ -103,6 +103,130 @@ def cpu_baseline(wl, inp, target_s: float):
     }
 
 
+SS_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scale_shift_ss_shard_traffic.json")
+SS_SOURCE = os.path.join(ROOT, "video_dit_dense_amd", "csrc", "scale_shift.hip")
+
+
+def ss_measured_traffic():
+    """HBM bytes per scale/shift launch from the committed counter summary,
+    or None when it is missing or the kernel source changed since."""
+    try:
+        with open(SS_TRAFFIC_FILE) as f:
+            t = json.load(f)
+        with open(SS_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    return t.get("hbm_bytes_per_launch") if t.get("kernel_source_sha256") == sha else None
+
+
+def ss_cpu_baseline(wl, inp, target_s: float):
+    """Time the oracle's bf16 chain (as it stands) on the first rows of the
+    workload, sized to take about `target_s` seconds; reports GB/s of the
+    same per-row byte accounting as the GPU figure."""
+    import numpy as np
+    from oracle import scale_shift as ss
+
+    def run(n):
+        t0 = time.perf_counter()
+        idx = None if inp.index is None else inp.index[:1, :n]
+        ss.rmsnorm_scale_shift(inp.x[:1, :n], inp.w, wl.eps, inp.scale[:1], inp.shift[:1], idx)
+        return time.perf_counter() - t0
+
+    n = min(wl.S, 256)
+    t = run(n)
+    n = int(min(wl.S, max(n, n * target_s / max(t, 1e-6))))
+    t = run(n)
+    row_bytes = wl.bytes() / (wl.B * wl.S)
+    return {
+        "value": row_bytes * n / t / 1e9,
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"NumPy bf16-chain oracle on the first {n} of {wl.B * wl.S} rows (D={wl.D}), {t:.1f} s wall; "
+                  "bytes counted as the GPU figure counts them per row",
+        "seconds": t,
+    }
+
+
+def bench_scale_shift(args, wl) -> int:
+    """Times h3attn_rmsnorm_scale_shift on a scale/shift workload: `warmup`
+    untimed launches, then `steps` back-to-back launches between two HIP
+    events on the current stream (the stream the launches go to)."""
+    import numpy as np
+    import torch
+    import workloads
+    from video_dit_dense_amd import h3attn
+
+    log(f"workload {wl.name}: {wl.description}")
+    inp = workloads.make_scale_shift_inputs(wl)
+
+    def dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to("cuda:0")
+
+    sc, sh = dev(inp.scale), dev(inp.shift)
+    idx = None if inp.index is None else torch.from_numpy(inp.index).to("cuda:0")
+    w = None if inp.w is None else torch.from_numpy(inp.w).to("cuda:0")
+    # Launches rotate over copies of x and y that together are at least 1 GB,
+    # four times the 256 MB last-level cache, so each launch reads x from and
+    # writes y to HBM, and K launches run back to back between two events.
+    n_sets = min(64, max(2, -(-(1 << 30) // (2 * inp.x.nbytes))))
+    xs = [dev(inp.x) for _ in range(n_sets)]
+    ys = [torch.empty_like(xs[0]) for _ in range(n_sets)]
+
+    def step(k):
+        h3attn.rmsnorm_scale_shift(xs[k % n_sets], sc, sh, idx, w, wl.eps, out=ys[k % n_sets])
+
+    for k in range(args.warmup):
+        step(k)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for k in range(args.steps):
+        step(k)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    gbs = wl.bytes() / (ms * 1e-3) / 1e9
+    log(f"timed {args.steps} launches over {n_sets} input/output sets: {ms * 1e3:.1f} us each, {gbs:.0f} GB/s")
+    result = {
+        "metric": f"RMSNorm + indexed scale/shift GB/s + % HBM peak, {wl.name}: {wl.description}",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{wl.name}: B={wl.B} S={wl.S} D={wl.D} M={wl.M} index={wl.index} "
+                        f"weight={wl.weight} eps={wl.eps}",
+            "bytes_per_step": wl.bytes(),
+            "step": "one h3attn_rmsnorm_scale_shift launch",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "scale_shift_kernel",
+            "achieved": round(gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "traffic": ss_measured_traffic() if wl.name == "ss_shard" else None,
+            "avg_us": round(ms * 1e3, 2),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        result["cpu_baseline"] = ss_cpu_baseline(wl, inp, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -110,7 +234,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="full",
                     help="workload name (default: full); also the attention variants "
-                         + ", ".join(sorted(__import__("workloads").VARIANT_WORKLOADS)))
+                         + ", ".join(sorted(__import__("workloads").VARIANT_WORKLOADS))
+                         + " and the RMSNorm + scale/shift shapes "
+                         + ", ".join(sorted(__import__("workloads").SCALE_SHIFT_WORKLOADS)))
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-baseline duration")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prologue-reps", type=int, default=20)
@@ -144,6 +270,8 @@ def main() -> int:
         print(json.dumps({"only": "copy", "bytes_read_per_launch": n, "bytes_written_per_launch": n,
                           "launches": args.warmup + args.steps}), flush=True)
         return 0
+    if args.workload in workloads.SCALE_SHIFT_WORKLOADS:
+        return bench_scale_shift(args, workloads.SCALE_SHIFT_WORKLOADS[args.workload])
     all_wl = {**workloads.WORKLOADS, **workloads.VARIANT_WORKLOADS}
     wl = all_wl[args.workload]
     variant = args.workload in workloads.VARIANT_WORKLOADS

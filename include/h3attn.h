@@ -8,6 +8,8 @@
  * scaled-dot-product attention over BSHD tensors at head_dim 128 in bf16,
  * with an optional valid front / padded tail (TeleFuser PR #37, sections 2.3
  * and 2.4; FastVideo PR #1799, section "Implementation", padding masks).
+ * Beside it, the DiT block's RMSNorm with indexed AdaLN scale/shift that
+ * feeds the QKV projection (TeleFuser PR #37, section 2.5).
  *
  * Conventions shared by every entry point
  *  - bf16 tensors are passed as uint16_t bit patterns. Every pointer is a
@@ -237,6 +239,41 @@ typedef struct h3attn_forward_args {
 size_t h3attn_forward_ex_workspace_bytes(const h3attn_forward_args* args);
 int h3attn_forward_ex(const h3attn_forward_args* args, void* workspace, size_t workspace_bytes,
                       uint32_t stages, void* stream);
+
+/*
+ * Fused RMSNorm + indexed AdaLN scale/shift, the DiT block's norm before the
+ * QKV projection (TeleFuser PR #37, "2.5 Fuse RMSNorm with indexed AdaLN
+ * modulation"). It keeps every bf16 rounding of the unfused chain
+ * "RMSNorm, then x * (1 + scale) + shift", so the result equals that chain
+ * computed with bf16 tensor arithmetic bit for bit. For token (b, s) with
+ * channels x_c, c < D, and i = index[b*S + s] clamped to [0, M-1] (0 when
+ * index is NULL):
+ *   r   = 1 / sqrt(mean_c x_c^2 + eps), rounded to the nearest fp32
+ *   n_c = bf16(fp32(x_c * r) * w_c)            (without "* w_c" when norm_w is NULL)
+ *   t_c = bf16(1 + scale[b, i, c])
+ *   u_c = bf16(n_c * t_c)
+ *   y_c = bf16(u_c + shift[b, i, c])
+ * where every operation is one fp32 IEEE operation and bf16() rounds to
+ * nearest, ties to even. r is computed from an fp64 sum of squares, so it is
+ * the nearest fp32 value except when 1/sqrt(.) lies within ~2^-48 (relative)
+ * of a point halfway between two fp32 values, where either neighbour may
+ * result. NaN or infinity in a row of x makes that whole row NaN; NaN in
+ * scale or shift makes that channel NaN.
+ *   x, y:         bf16 [B, S, D], contiguous. y == x (in place) or y disjoint
+ *                 from every input.
+ *   norm_w:       fp32 [D] or NULL (no weight, the usual DiT block norm).
+ *   eps:          finite, >= 0.
+ *   scale, shift: bf16 [B, M, D], contiguous, M >= 1.
+ *   index:        int32 [B, S], contiguous, or NULL; values outside [0, M)
+ *                 are clamped (never read out of bounds).
+ *   B, S >= 1; D a multiple of 8, 8 <= D <= 16384; B*S < 2^31.
+ * Alignment: x, y, scale, shift, norm_w 16 bytes; index 4 bytes.
+ * Errors: NULL_POINTER, BAD_SHAPE, BAD_ALIGNMENT, ALIASING, BAD_VALUE (eps),
+ * UNSUPPORTED_DEVICE, HIP.
+ */
+int h3attn_rmsnorm_scale_shift(const uint16_t* x, uint16_t* y, int32_t B, int32_t S, int32_t D,
+                               const float* norm_w, float eps, const uint16_t* scale,
+                               const uint16_t* shift, int32_t M, const int32_t* index, void* stream);
 
 #ifdef __cplusplus
 }

@@ -212,3 +212,41 @@ def test_forward_ex_device_gate_without_gpu(lib):
     assert fwd_ex(lib, causal=1) == DEVICE
     assert fwd_ex(lib, valid_lengths=9 * A, kv_valid=0) == DEVICE   # per-item lengths replace kv_valid
     assert fwd_ex(lib, q_stride=[8 * 12 * 128, 12 * 128, 128], k_stride=[8 * 12 * 128, 12 * 128, 128]) == DEVICE
+
+
+def scale_shift(lib, x=A, y=2 * A, B=1, S=8, D=64, w=3 * A, eps=1e-6, sc=4 * A, sh=5 * A, M=2, idx=6 * A):
+    return lib.h3attn_rmsnorm_scale_shift(P(x), P(y), B, S, D, P(w), eps, P(sc), P(sh), M, P(idx), None)
+
+
+def test_scale_shift_validation(lib):
+    assert scale_shift(lib, x=0) == NULLP
+    assert scale_shift(lib, y=0) == NULLP
+    assert scale_shift(lib, sc=0) == NULLP
+    assert scale_shift(lib, sh=0) == NULLP
+    assert scale_shift(lib, B=0) == SHAPE
+    assert scale_shift(lib, S=0) == SHAPE
+    assert scale_shift(lib, M=0) == SHAPE
+    assert scale_shift(lib, D=0) == SHAPE
+    assert scale_shift(lib, D=60) == SHAPE            # not a multiple of 8
+    assert scale_shift(lib, D=16384 + 8) == SHAPE     # past the largest row
+    assert scale_shift(lib, B=1 << 16, S=1 << 15) == SHAPE   # B*S >= 2^31
+    assert scale_shift(lib, eps=float("inf")) == VALUE
+    assert scale_shift(lib, eps=-1e-6) == VALUE
+    assert scale_shift(lib, x=A + 8) == ALIGN
+    assert scale_shift(lib, sh=5 * A + 2) == ALIGN
+    assert scale_shift(lib, w=3 * A + 4) == ALIGN
+    assert scale_shift(lib, idx=6 * A + 2) == ALIGN
+    assert scale_shift(lib, y=A + 512) == ALIAS       # partial overlap with x
+    assert scale_shift(lib, y=4 * A + 128) == ALIAS   # on top of scale
+    assert scale_shift(lib, y=5 * A) == ALIAS         # on top of shift
+    assert scale_shift(lib, w=2 * A + 64) == ALIAS    # weight inside y
+    assert scale_shift(lib, idx=2 * A + 16) == ALIAS  # index inside y
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="device gate is checked on a machine without a GPU")
+def test_scale_shift_device_gate_without_gpu(lib):
+    assert scale_shift(lib) == DEVICE
+    assert scale_shift(lib, y=A) == DEVICE                   # exact in place passes validation
+    assert scale_shift(lib, w=0, idx=0) == DEVICE            # weight and index are optional
+    assert scale_shift(lib, D=16384, w=0) == DEVICE
+    assert scale_shift(lib, idx=6 * A + 4) == DEVICE         # 4-byte aligned index is enough

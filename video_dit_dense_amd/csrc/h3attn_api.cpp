@@ -371,3 +371,35 @@ H3_API int h3attn_forward_ex(const h3attn_forward_args* args, void* workspace, s
                              uint32_t stages, void* stream) {
   return run_forward(args, workspace, workspace_bytes, stages, stream);
 }
+
+H3_API int h3attn_rmsnorm_scale_shift(const uint16_t* x, uint16_t* y, int32_t B, int32_t S, int32_t D,
+                                      const float* norm_w, float eps, const uint16_t* scale,
+                                      const uint16_t* shift, int32_t M, const int32_t* index, void* stream) {
+  if (!x || !y || !scale || !shift) return H3ATTN_ERR_NULL_POINTER;
+  if (B < 1 || S < 1 || M < 1 || D < 8 || D % 8 != 0 || D > h3::kScaleShiftMaxD) return H3ATTN_ERR_BAD_SHAPE;
+  if ((int64_t)B * S >= (1ll << 31) || (int64_t)B * M >= (1ll << 31)) return H3ATTN_ERR_BAD_SHAPE;
+  if (!std::isfinite(eps) || !(eps >= 0.f)) return H3ATTN_ERR_BAD_VALUE;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(scale) || !aligned16(shift)) return H3ATTN_ERR_BAD_ALIGNMENT;
+  if (norm_w && !aligned16(norm_w)) return H3ATTN_ERR_BAD_ALIGNMENT;
+  if (index && (reinterpret_cast<uintptr_t>(index) & 3u)) return H3ATTN_ERR_BAD_ALIGNMENT;
+  const size_t xbytes = (size_t)B * S * D * 2, mbytes = (size_t)B * M * D * 2;
+  const Range xr = range_of(x, xbytes), yr = range_of(y, xbytes);
+  if (y != x && overlap(yr, xr)) return H3ATTN_ERR_ALIASING;
+  if (overlap(yr, range_of(scale, mbytes)) || overlap(yr, range_of(shift, mbytes))) return H3ATTN_ERR_ALIASING;
+  if (norm_w && overlap(yr, range_of(norm_w, (size_t)D * 4))) return H3ATTN_ERR_ALIASING;
+  if (index && overlap(yr, range_of(index, (size_t)B * S * 4))) return H3ATTN_ERR_ALIASING;
+  if (int st = check_device()) return st;
+  h3::ScaleShiftArgs a;
+  a.x = x;
+  a.y = y;
+  a.scale = scale;
+  a.shift = shift;
+  a.index = index;
+  a.w = norm_w;
+  a.eps = eps;
+  a.rows = B * S;
+  a.S = S;
+  a.D = D;
+  a.M = M;
+  return status_from(h3::launch_scale_shift(a, reinterpret_cast<hipStream_t>(stream)));
+}

@@ -128,4 +128,20 @@ struct AttnArgs {
 // merge of their partial records) on `stream`.
 hipError_t launch_attention(AttnArgs a, hipStream_t stream);
 
+// RMSNorm + indexed scale/shift (scale_shift.hip). x and y [rows = B*S, D]
+// bf16, scale and shift [B, M, D] bf16, index [B*S] int32 or null (row 0),
+// w fp32 [D] or null. D is a multiple of 8 and at most kScaleShiftMaxD.
+constexpr int kScaleShiftMaxD = 16384;
+struct ScaleShiftArgs {
+  const uint16_t* x;
+  uint16_t* y;
+  const uint16_t* scale;
+  const uint16_t* shift;
+  const int32_t* index;
+  const float* w;
+  float eps;
+  int32_t rows, S, D, M;
+};
+hipError_t launch_scale_shift(const ScaleShiftArgs& a, hipStream_t stream);
+
 }  // namespace h3

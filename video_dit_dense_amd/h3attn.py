@@ -59,6 +59,7 @@ class ForwardArgs(ctypes.Structure):
 SIGNATURES["h3attn_forward_ex_workspace_bytes"] = (ctypes.c_size_t, [ctypes.POINTER(ForwardArgs)])
 SIGNATURES["h3attn_forward_ex"] = (ctypes.c_int, [ctypes.POINTER(ForwardArgs), _P, ctypes.c_size_t,
                                                   ctypes.c_uint32, _P])
+SIGNATURES["h3attn_rmsnorm_scale_shift"] = (ctypes.c_int, [_P, _P, _I, _I, _I, _P, _F, _P, _P, _I, _P, _P])
 
 _lib = None
 
@@ -268,3 +269,46 @@ def forward_ex_workspace_bytes(B: int, Sq: int, Sk: int, Hq: int, Hkv: int, caus
     a.causal = 1 if causal else 0
     a.valid_lengths = 16 if per_item_lengths else None   # only NULL or not matters here
     return int(load_library().h3attn_forward_ex_workspace_bytes(ctypes.byref(a)))
+
+
+
+def _check_bf16_3d(name: str, t: torch.Tensor) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda" or t.dtype != torch.bfloat16 or t.dim() != 3 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous bfloat16 GPU tensor [B, rows, D] "
+                         f"(got {t.dtype} {tuple(t.shape)} on {t.device})")
+    if t.requires_grad and torch.is_grad_enabled():
+        raise RuntimeError(f"{name} requires grad: h3attn is inference-only (no backward)")
+
+
+def rmsnorm_scale_shift(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor,
+                        index: torch.Tensor | None = None, norm_w: torch.Tensor | None = None,
+                        eps: float = 1e-6, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Fused RMSNorm + indexed AdaLN scale/shift with the bf16 rounding of
+    the unfused chain: y = bf16(bf16(n * bf16(1 + scale[i])) + shift[i]),
+    n = bf16(x * r [* norm_w]), r = fp32(1/sqrt(mean x^2 + eps)), i =
+    index[b, s] clamped to [0, M). x [B, S, D], scale and shift [B, M, D]
+    (bf16), index int32 [B, S] or None (row 0), norm_w fp32 [D] or None.
+    Pass out=x to run in place. Returns y [B, S, D] bf16."""
+    lib = load_library()
+    _check_bf16_3d("x", x)
+    _check_bf16_3d("scale", scale)
+    _check_bf16_3d("shift", shift)
+    B, S, D = x.shape
+    if scale.shape != shift.shape or scale.shape[0] != B or scale.shape[2] != D:
+        raise ValueError("scale and shift must both be [B, M, D] with x's B and D")
+    M = scale.shape[1]
+    _check_f32("norm_w", norm_w, D)
+    if index is not None:
+        if (index.device.type != "cuda" or index.dtype != torch.int32 or tuple(index.shape) != (B, S)
+                or not index.is_contiguous()):
+            raise ValueError("index must be a contiguous int32 GPU tensor [B, S]")
+    y = torch.empty_like(x) if out is None else out
+    _check_bf16_3d("out", y)
+    if y.shape != x.shape:
+        raise ValueError("out must have x's shape")
+    st = lib.h3attn_rmsnorm_scale_shift(_ptr(x), _ptr(y), B, S, D, _ptr(norm_w), float(eps), _ptr(scale),
+                                        _ptr(shift), M, _ptr(index), _stream(x.device))
+    _check(st, "h3attn_rmsnorm_scale_shift")
+    return y

@@ -25,6 +25,11 @@ attention):
   mask (key j visible to query i iff j <= i, the lower-triangular mask of
   row indices), grouped heads (query head h reads key/value head
   h // (Hq / Hkv)), and valid lengths per batch item.
+* The frame-window attention of VDN-H3 (SGLang PR #37903, "Modifications",
+  hybrid_window_attn_h3: a chunk-5 / radius-1 window with anchor frames,
+  dense-query rows against all keys, a softmax gate epilogue), read as a
+  visibility rule over frame-major rows (`window_visible`) and a logistic
+  gate per (row, head) on the attention output.
 
 Readings where the pages are silent (each pinned by a test in tests/):
 per-head norm with one [128] weight shared by all heads, eps inside the square
@@ -112,6 +117,31 @@ def qk_prologue(q_bits, k_bits, w_q, w_k, eps: float, theta: float | None,
     return q, k
 
 
+def window_visible(rows, keys, F: int, C: int, R: int, A: int) -> np.ndarray:
+    """Frame-window visibility [len(rows), len(keys)] (SGLang PR #37903,
+    "Modifications", hybrid_window_attn_h3), read this way: row or key i lies
+    in frame i // F; frames 0..A-1 are anchor frames; the frames after them
+    form chunks of C frames, so frame f >= A is in chunk (f - A) // C (the
+    chunk grid is shifted by the anchors). A query in an anchor frame is a
+    dense-query row and sees every key. Any other query sees the anchor
+    frames and the frames of the chunks within R of its own."""
+    fi = np.asarray(rows, dtype=np.int64) // F
+    fj = np.asarray(keys, dtype=np.int64) // F
+    dense = fi < A
+    ci = np.where(dense, 0, (fi - A) // C)
+    anchor_key = fj < A
+    cj = np.where(anchor_key, 0, (fj - A) // C)
+    near = (~anchor_key)[None, :] & (np.abs(cj[None, :] - ci[:, None]) <= R)
+    return dense[:, None] | anchor_key[None, :] | near
+
+
+def sigmoid(x) -> np.ndarray:
+    """The logistic function 1 / (1 + e^-x), in float64, without overflow."""
+    x = np.asarray(x, dtype=np.float64)
+    e = np.exp(-np.abs(x))
+    return np.where(x >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+
+
 def _per_batch(valid, B: int, full: int) -> list:
     """A valid length for every batch item: None means `full`, an int is
     shared by all items, a sequence gives one per item."""
@@ -127,14 +157,17 @@ def _per_batch(valid, B: int, full: int) -> list:
 
 def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
               q_valid=None, kv_valid=None, rows=None, block: int = 256,
-              causal: bool = False) -> np.ndarray:
+              causal: bool = False, window=None, gate=None) -> np.ndarray:
     """Softmax attention on BSHD float64 tensors, q [B, Sq, H, D] and k, v
     [B, Sk, Hkv, D] with H a multiple of Hkv (query head h reads key/value
     head h // (H // Hkv); Hkv = H is plain multi-head attention).
 
     For batch item b and query row i < q_valid[b]:
       o_i = sum_{j in V(i)} softmax_j(scale * q_i . k_j) v_j,
-      V(i) = {j < kv_valid[b]}, and with `causal` also j <= i;
+      V(i) = {j < kv_valid[b]}, and with `causal` also j <= i, and with
+      `window` = (F, C, R, A) also window_visible(i, j); a row whose V(i)
+      is empty is 0. With `gate` (float [B, Sq, H]) the output is multiplied
+      by sigmoid(gate[b, i, h]) (the softmax gate epilogue);
     o_i = 0 for i >= q_valid[b]. q_valid / kv_valid are None (everything
     valid), one int for all items or one per item. With `rows` (absolute
     query row indices), only those rows are computed and the result has shape
@@ -150,8 +183,10 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
     group = H // Hkv
     qv = _per_batch(q_valid, B, Sq)
     kvv = _per_batch(kv_valid, B, Sk)
-    if min(kvv) < 1:
+    if min(kvv) < 1 and window is None:
         raise ValueError("attention needs at least one valid key")
+    if causal and window is not None:
+        raise ValueError("the frame window is not combined with the causal mask")
     row_idx = np.arange(Sq) if rows is None else np.asarray(rows, dtype=np.int64)
     out = np.zeros((B, len(row_idx), H, D), dtype=np.float64)
     for b in range(B):
@@ -168,9 +203,15 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
                 if causal:
                     # key j is visible to query row i iff j <= i
                     s = np.where(np.arange(kvv[b])[None, :] <= sel[live][:, None], s, -np.inf)
-                m = s.max(axis=1, keepdims=True)
+                if window is not None:
+                    s = np.where(window_visible(sel[live], np.arange(kvv[b]), *window), s, -np.inf)
+                seen = np.isfinite(s).any(axis=1) if s.shape[1] else np.zeros(len(s), dtype=bool)
+                m = np.where(seen, s.max(axis=1, initial=-np.inf), 0.0)[:, None]
                 p = np.exp(s - m)
-                o = (p @ vh) / p.sum(axis=1, keepdims=True)
+                z = np.where(seen[:, None], p.sum(axis=1, keepdims=True), 1.0)
+                o = np.where(seen[:, None], (p @ vh) / z, 0.0)
+                if gate is not None:
+                    o = o * sigmoid(np.asarray(gate, dtype=np.float64)[b, sel[live], h])[:, None]
                 dst = np.arange(start, start + len(sel))[live]
                 out[b, dst, h, :] = o
     return out
@@ -178,12 +219,14 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
 
 def forward(q_bits, k_bits, v_bits, w_q, w_k, eps: float, theta: float | None,
             scale: float, q_valid=None, kv_valid=None, norm: bool = True, rows=None,
-            causal: bool = False) -> np.ndarray:
+            causal: bool = False, window=None, gate_bits=None) -> np.ndarray:
     """The whole attention step: prologue on q and k, then attention with v.
-    Valid lengths, `rows` and `causal` are those of `attention`."""
+    Valid lengths, `rows`, `causal` and `window` are those of `attention`;
+    `gate_bits` is the gate as bf16 bit patterns [B, Sq, H]."""
     qn, kn = qk_prologue(q_bits, k_bits, w_q, w_k, eps, theta, norm=norm)
+    gate = None if gate_bits is None else bf16_bits_to_f64(gate_bits)
     return attention(qn, kn, bf16_bits_to_f64(v_bits), scale, q_valid, kv_valid,
-                     rows=rows, causal=causal)
+                     rows=rows, causal=causal, window=window, gate=gate)
 
 
 def compare(got_bits_or_f64, ref: np.ndarray) -> dict:

@@ -404,3 +404,124 @@ def test_attention_variant_invariants():
     # rows subset equals the full causal computation at those rows
     rows = np.array([0, 1, 37, 79])
     assert np.allclose(oracle.attention(q, k, v, scale, rows=rows, causal=True), o[:, rows], rtol=1e-13, atol=1e-14)
+
+
+# ------------------------------------------- frame-window attention with the softmax gate
+
+def _ranges(spec):
+    spec = spec if isinstance(spec[0], list) else [spec]
+    return sorted(j for lo, hi in spec for j in range(lo, hi))
+
+
+def test_window_visibility_hand():
+    g = _load("window_hand.json")
+    for case in g["cases"]:
+        vis = oracle.window_visible(np.arange(case["S"]), np.arange(case["S"]),
+                                    case["F"], case["C"], case["R"], case["A"])
+        for row, spec in case["visible"].items():
+            assert list(np.flatnonzero(vis[int(row)])) == _ranges(spec), (case, row)
+    for x, want in g["gate"]["sigmoid"].items():
+        assert abs(oracle.sigmoid(float(x)) - want) < 1e-15
+
+
+def _window_keys_constructive(i, S, F, C, R, A):
+    """The visible keys of row i built from frame lists: every key of a dense
+    row; else the anchor frames' rows and the rows of every frame in chunks
+    c-R .. c+R (chunk c covers frames A + cC .. A + cC + C - 1)."""
+    n_frames = (S + F - 1) // F
+    f = i // F
+    if f < A:
+        return set(range(S))
+    c = (f - A) // C
+    frames = set(range(min(A, n_frames)))
+    for cc in range(c - R, c + R + 1):
+        for ff in range(A + cc * C, A + cc * C + C):
+            if A <= ff < n_frames:
+                frames.add(ff)
+    return {j for ff in frames for j in range(ff * F, min(S, ff * F + F))}
+
+
+@pytest.mark.parametrize("F,C,R,A,S", [(3, 2, 1, 1, 40), (4, 5, 1, 2, 61), (5, 1, 0, 0, 33), (2, 3, 2, 0, 50),
+                                       (7, 2, 0, 3, 70)])
+def test_window_visibility_constructive(F, C, R, A, S):
+    vis = oracle.window_visible(np.arange(S), np.arange(S), F, C, R, A)
+    for i in range(S):
+        assert set(np.flatnonzero(vis[i]).tolist()) == _window_keys_constructive(i, S, F, C, R, A), i
+
+
+def _window_mask(B, Sq, Sk, F, C, R, A, qvl, kvl):
+    mask = np.zeros((B, 1, Sq, Sk), dtype=bool)
+    for b in range(B):
+        for i in range(Sq):
+            for j in _window_keys_constructive(i, max(Sq, Sk), F, C, R, A):
+                if j < kvl[b]:
+                    mask[b, 0, i, j] = True
+    return mask
+
+
+@pytest.mark.parametrize("B,S,H,Hkv,F,C,R,A,qv,kvv", [
+    (1, 96, 2, 2, 8, 2, 1, 1, 96, 96),
+    (2, 130, 4, 2, 10, 3, 1, 2, [130, 77], [130, 101]),
+    (1, 150, 3, 1, 6, 5, 0, 0, 150, 150),
+])
+def test_window_attention_matches_torch_sdpa_fp64(B, S, H, Hkv, F, C, R, A, qv, kvv):
+    rng = np.random.default_rng(S + F * 3 + R)
+    q = rng.standard_normal((B, S, H, 128)) * 1.5
+    k = rng.standard_normal((B, S, Hkv, 128)) * 1.5
+    v = rng.standard_normal((B, S, Hkv, 128))
+    gate = rng.standard_normal((B, S, H)) * 2
+    scale = 1 / math.sqrt(128)
+    o = oracle.attention(q, k, v, scale, q_valid=qv, kv_valid=kvv, window=(F, C, R, A), gate=gate, block=64)
+    qvl = qv if isinstance(qv, list) else [qv] * B
+    kvl = kvv if isinstance(kvv, list) else [kvv] * B
+    mask = _window_mask(B, S, S, F, C, R, A, qvl, kvl)
+    ref = _sdpa_masked(q, k, v, scale, mask, Hkv != H)
+    ref = ref * (1.0 / (1.0 + np.exp(-gate)))[..., None]
+    for b in range(B):
+        ref[b, qvl[b]:] = 0.0
+    assert np.allclose(o, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_window_attention_invariants():
+    rng = np.random.default_rng(23)
+    B, S, H = 1, 120, 2
+    F, C, R, A = 6, 2, 1, 1
+    scale = 1 / math.sqrt(128)
+    q = rng.standard_normal((B, S, H, 128))
+    k = rng.standard_normal((B, S, H, 128))
+    v = rng.standard_normal((B, S, H, 128))
+    dense = oracle.attention(q, k, v, scale)
+    # a radius covering every chunk is dense attention
+    assert np.array_equal(oracle.attention(q, k, v, scale, window=(F, C, 100, A)), dense)
+    # anchor frames covering the whole sequence: every row is a dense row
+    assert np.array_equal(oracle.attention(q, k, v, scale, window=(F, C, 0, 100)), dense)
+    o = oracle.attention(q, k, v, scale, window=(F, C, R, A))
+    # rows of the anchor frame are dense rows
+    assert np.array_equal(o[:, :F], dense[:, :F])
+    # keys outside a row's window do not affect it: chunk 0 = frames 1-2 sees
+    # frames 0-4 (rows 0..29); rewrite rows 30.. of k and v
+    k2, v2 = k.copy(), v.copy()
+    k2[:, 30:] = rng.standard_normal(k2[:, 30:].shape) * 9
+    v2[:, 30:] = 1e6
+    o2 = oracle.attention(q, k2, v2, scale, window=(F, C, R, A))
+    assert np.array_equal(o2[:, F:3 * F], o[:, F:3 * F])
+    # gate 0 halves the output exactly; a gate of 40 leaves it to 1e-17
+    g0 = np.zeros((B, S, H))
+    assert np.array_equal(oracle.attention(q, k, v, scale, window=(F, C, R, A), gate=g0), o * 0.5)
+    g40 = np.full((B, S, H), 40.0)
+    assert np.allclose(oracle.attention(q, k, v, scale, window=(F, C, R, A), gate=g40), o, rtol=1e-16, atol=1e-17)
+    # q = 0: each row is the mean of the v rows it sees
+    q0 = np.zeros_like(q)
+    o0 = oracle.attention(q0, k, v, scale, window=(F, C, R, A))
+    vis = oracle.window_visible(np.arange(S), np.arange(S), F, C, R, A)
+    for i in (0, 7, 40, 119):
+        assert np.allclose(o0[0, i], v[0, vis[i]].mean(axis=0), rtol=1e-13, atol=1e-14)
+    # no anchors, radius 0, keys cut at kv_valid: a row whose chunk lies past
+    # kv_valid sees nothing and is 0
+    oz = oracle.attention(q, k, v, scale, kv_valid=20, window=(F, C, 0, 0))
+    assert np.all(oz[0, 24:] == 0.0) and np.all(np.isfinite(oz))
+    # sigmoid: symmetry and no overflow at the extremes
+    x = np.array([-1000.0, -3.0, 0.0, 3.0, 1000.0])
+    sg = oracle.sigmoid(x)
+    assert np.allclose(sg + oracle.sigmoid(-x), 1.0, rtol=0, atol=4e-16)
+    assert sg[0] == 0.0 and sg[-1] == 1.0

@@ -55,6 +55,30 @@ def measured_traffic():
     return t.get("hbm_bytes_per_launch")
 
 
+def window_keys_per_row(wl, rows):
+    """Visible keys of each query row under the workload's frame window: a
+    row of an anchor frame sees all kv_valid keys; another row sees the
+    anchor frames plus the frames of the chunks within R of its own, cut at
+    kv_valid (the geometry h3attn_forward_args documents)."""
+    import numpy as np
+    F, C, R, A = wl.window
+    kvv = wl.kv_valid
+    f = np.asarray(rows, dtype=np.int64) // F
+    c = np.maximum(f - A, 0) // C
+    lo = np.minimum(F * (A + C * np.maximum(c - R, 0)), kvv)
+    hi = np.minimum(F * (A + C * (c + R + 1)), kvv)
+    return np.where(f < A, kvv, min(A * F, kvv) + np.maximum(hi - lo, 0))
+
+
+def step_flops(wl) -> float:
+    """Attention flops of one step: 4*d per visible (query, key) pair."""
+    if wl.window:
+        import numpy as np
+        pairs = float(window_keys_per_row(wl, np.arange(wl.q_valid)).sum()) * wl.B
+        return 4.0 * pairs * 128 * wl.H
+    return wl.attention_flops()
+
+
 def cpu_baseline(wl, inp, target_s: float):
     """Time the fp64 oracle (as it stands) on one head and a seeded sample of
     query rows against all keys; scale the row count so the run takes about
@@ -70,6 +94,7 @@ def cpu_baseline(wl, inp, target_s: float):
         threads = None
     # Item 0, query head 0 and the key/value head it reads (head 0).
     q1, k1, v1 = inp.q[:1, :, :1].copy(), inp.k[:1, :, :1].copy(), inp.v[:1, :, :1].copy()
+    gate1 = workloads.make_gate(wl.B, wl.Sq, wl.H, seed=wl.seed)[:1, :, :1].copy() if wl.gate else None
     theta = wl.theta if wl.rope else None
     qv0, kvv0 = wl.item_lengths()[0]
 
@@ -77,7 +102,8 @@ def cpu_baseline(wl, inp, target_s: float):
         rows = np.sort(np.random.default_rng(99).choice(qv0, size=n_rows, replace=False))
         t0 = time.perf_counter()
         oracle.forward(q1, k1, v1, inp.w_q, inp.w_k, wl.eps, theta, wl.scale, qv0, kvv0,
-                       norm=wl.norm, rows=rows, causal=wl.causal)
+                       norm=wl.norm, rows=rows, causal=wl.causal, window=wl.window or None,
+                       gate_bits=gate1)
         return time.perf_counter() - t0, rows
 
     # Fixed cost (prologue over all rows of the head) plus a per-row cost:
@@ -89,7 +115,10 @@ def cpu_baseline(wl, inp, target_s: float):
     fixed = max(ta - per_row * n1, 0.0)
     n = int(min(qv0, max(n2, (target_s - fixed) / per_row)))
     t, rows = run(n)
-    keys = np.minimum(rows + 1, kvv0) if wl.causal else np.full(len(rows), kvv0)
+    if wl.window:
+        keys = window_keys_per_row(wl, rows)
+    else:
+        keys = np.minimum(rows + 1, kvv0) if wl.causal else np.full(len(rows), kvv0)
     flops = 4.0 * float(keys.sum()) * 128
     return {
         "value": flops / t / 1e12,
@@ -97,7 +126,8 @@ def cpu_baseline(wl, inp, target_s: float):
         "cores": threads if threads is not None else len(os.sched_getaffinity(0)),
         "kind": "oracle",
         "sample": f"fp64 NumPy oracle, item 0, head 0 of {wl.H}, {n} of {qv0} query rows against "
-                  f"{'their causal prefix of ' if wl.causal else 'all '}{kvv0} keys, prologue included, "
+                  f"{'their causal prefix of ' if wl.causal else 'their frame window of ' if wl.window else 'all '}"
+                  f"{kvv0} keys, prologue included, "
                   f"{t:.1f} s wall",
         "seconds": t,
     }
@@ -290,8 +320,10 @@ def main() -> int:
     if wl.rope:
         cos, sin = h3attn.rope_tables(max(wl.Sq, wl.Sk), wl.theta)
     lengths = (torch.tensor(wl.lengths, dtype=torch.int32, device="cuda:0") if wl.lengths else None)
+    gate = dev(workloads.make_gate(wl.B, wl.Sq, wl.H, seed=wl.seed)) if wl.gate else None
     if variant:
         nbytes = h3attn.forward_ex_workspace_bytes(wl.B, wl.Sq, wl.Sk, wl.H, wl.kv_heads, causal=wl.causal,
+                                                   window=bool(wl.window),
                                                    per_item_lengths=lengths is not None)
         ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
     else:
@@ -301,14 +333,15 @@ def main() -> int:
     def stage(st):
         h3attn.forward(q, k, v, w_q if wl.norm else None, w_k if wl.norm else None, wl.eps, cos, sin,
                        q_valid=None if wl.lengths else wl.q_valid, kv_valid=None if wl.lengths else wl.kv_valid,
-                       scale=wl.scale, out=o, workspace=ws, stages=st, causal=wl.causal, valid_lengths=lengths)
+                       scale=wl.scale, out=o, workspace=ws, stages=st, causal=wl.causal, valid_lengths=lengths,
+                       window=wl.window or None, gate=gate)
 
     if args.only == "attention":
         stage(h3attn.STAGE_PREPARE)
         for _ in range(args.warmup + args.steps):
             stage(h3attn.STAGE_ATTEND)
         torch.cuda.synchronize()
-        print(json.dumps({"only": "attention", "workload": wl.name, "flop_per_launch": wl.attention_flops(),
+        print(json.dumps({"only": "attention", "workload": wl.name, "flop_per_launch": step_flops(wl),
                           "launches": args.warmup + args.steps}), flush=True)
         return 0
 
@@ -336,7 +369,7 @@ def main() -> int:
     attn_ms = [e[1].elapsed_time(e[2]) for e in ev]
     attn_avg = sum(attn_ms) / len(attn_ms)
     prep_avg = sum(prep_ms) / len(prep_ms)
-    flops = wl.attention_flops()
+    flops = step_flops(wl)
     log(f"timed {args.steps} steps: {ms_step:.3f} ms/step, attend stage {attn_avg:.3f} ms "
         f"(min {min(attn_ms):.3f}, max {max(attn_ms):.3f}), prepare {prep_avg:.3f} ms")
 

@@ -234,6 +234,27 @@ typedef struct h3attn_forward_args {
   const int32_t* valid_lengths;
   int32_t causal;
   float softmax_scale;
+  /* Frame-window attention (SGLang PR #37903, "Modifications",
+   * hybrid_window_attn_h3: a chunk-5 / radius-1 window with anchor frames,
+   * dense-query rows against all keys). Row or key i lies in frame
+   * i / window_frame_rows. Frames below window_anchor_frames are anchor
+   * frames: their queries see every key. Frame f >= window_anchor_frames is in
+   * chunk (f - window_anchor_frames) / window_chunk_frames; its queries see
+   * the anchor frames and the frames of the chunks within window_radius of
+   * their own. Composed with the valid lengths like the other masks; a row
+   * that sees no key is written as 0. window_frame_rows = 0 turns the window
+   * off (the other three fields must then be 0); otherwise
+   * window_chunk_frames >= 1, window_radius >= 0, window_anchor_frames >= 0,
+   * and causal must be 0. */
+  int32_t window_frame_rows;
+  int32_t window_chunk_frames;
+  int32_t window_radius;
+  int32_t window_anchor_frames;
+  /* Softmax gate epilogue: NULL, or bf16 [B, Sq, Hq] contiguous (2-byte
+   * aligned, disjoint from o); each output row (b, i, h) is multiplied by
+   * sigmoid(gate[b, i, h]) = 1 / (1 + exp(-gate)) before its bf16 rounding.
+   * Rows at or past q_valid stay +0.0. */
+  const uint16_t* gate;
 } h3attn_forward_args;
 
 size_t h3attn_forward_ex_workspace_bytes(const h3attn_forward_args* args);

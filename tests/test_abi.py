@@ -182,6 +182,7 @@ def test_forward_ex_workspace_bytes(lib):
     assert h3attn.forward_ex_workspace_bytes(1, 104448, 104448, 6, 2, causal=True) == (6 + 2 * 2) * 104448 * 256
     assert h3attn.forward_ex_workspace_bytes(2, 1000, 300, 4, 1, per_item_lengths=True) == \
         2 * (4 * 1024 + 2 * 1 * 512) * 256
+    assert h3attn.forward_ex_workspace_bytes(1, 104448, 104448, 6, 6, window=True) == 3 * 6 * 104448 * 256
     assert h3attn.forward_ex_workspace_bytes(1, 8, 8, 6, 4) == 0      # 6 heads do not group into 4
     assert h3attn.forward_ex_workspace_bytes(1, 8, 8, 4, 0) == 0
     assert lib.h3attn_forward_ex_workspace_bytes(None) == 0
@@ -204,6 +205,17 @@ def test_forward_ex_validation(lib):
     assert fwd_ex(lib, wsb=4096) == WS
     assert fwd_ex(lib, ws=0) == WS
     assert fwd_ex(lib, o=A + 1024) == ALIAS                    # o on top of q
+    # frame window and gate
+    assert fwd_ex(lib, window_frame_rows=-1) == VALUE
+    assert fwd_ex(lib, window_chunk_frames=5) == VALUE         # window fields without a window
+    assert fwd_ex(lib, window_frame_rows=4, window_chunk_frames=0) == VALUE
+    assert fwd_ex(lib, window_frame_rows=4, window_chunk_frames=2, window_radius=-1) == VALUE
+    assert fwd_ex(lib, window_frame_rows=4, window_chunk_frames=2, window_anchor_frames=-1) == VALUE
+    assert fwd_ex(lib, window_frame_rows=4, window_chunk_frames=2, causal=1) == VALUE
+    assert fwd_ex(lib, window_frame_rows=4, window_chunk_frames=2, Sq=1 << 28, Sk=1 << 28,
+                  rope_rows=1 << 28, wsb=1 << 40) == SHAPE
+    assert fwd_ex(lib, gate=9 * A + 1) == ALIGN
+    assert fwd_ex(lib, gate=4 * A + 256) == ALIAS               # gate inside o
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="device gate is checked on a machine without a GPU")
@@ -212,6 +224,10 @@ def test_forward_ex_device_gate_without_gpu(lib):
     assert fwd_ex(lib, causal=1) == DEVICE
     assert fwd_ex(lib, valid_lengths=9 * A, kv_valid=0) == DEVICE   # per-item lengths replace kv_valid
     assert fwd_ex(lib, q_stride=[8 * 12 * 128, 12 * 128, 128], k_stride=[8 * 12 * 128, 12 * 128, 128]) == DEVICE
+    assert fwd_ex(lib, window_frame_rows=4, window_chunk_frames=2, window_radius=1, window_anchor_frames=1,
+                  gate=9 * A + 2) == DEVICE
+    assert fwd_ex(lib, window_frame_rows=1 << 30, window_chunk_frames=1 << 30, window_radius=1 << 30,
+                  window_anchor_frames=1 << 30) == DEVICE          # huge geometry clamps, no overflow
 
 
 def scale_shift(lib, x=A, y=2 * A, B=1, S=8, D=64, w=3 * A, eps=1e-6, sc=4 * A, sh=5 * A, M=2, idx=6 * A):

@@ -1,0 +1,141 @@
+"""GPU parity of the frame-window attention with the softmax gate (SGLang
+PR #37903, "Modifications", hybrid_window_attn_h3) through h3attn_forward_ex,
+against the fp64 oracle on the same seeded inputs. Bar: max-abs <= 2e-2 and
+relative RMS <= 5e-3 on the bf16 outputs, as for the dense step."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import DevInputs, say, to_dev, to_host
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+MAX_ABS = 2e-2
+REL_RMS = 5e-3
+SCALE = 1 / math.sqrt(128)
+
+
+@pytest.fixture(scope="module")
+def h3():
+    from video_dit_dense_amd import h3attn
+    h3attn.load_library()
+    return h3attn
+
+
+def check(metrics, label):
+    say(f"{label}: {metrics}")
+    assert metrics["nonfinite"] == 0, label
+    assert metrics["max_abs"] <= MAX_ABS, label
+    assert metrics["rel_rms"] <= REL_RMS, label
+
+
+def run(h3, inp, window, gate_bits=None, q_valid=None, kv_valid=None, lengths=None):
+    d = DevInputs(inp)
+    S = max(inp.q.shape[1], inp.k.shape[1])
+    cos, sin = h3.rope_tables(S)
+    lt = None if lengths is None else torch.tensor(lengths, dtype=torch.int32, device="cuda:0")
+    gate = None if gate_bits is None else to_dev(gate_bits)
+    o = h3.forward(d.q, d.k, d.v, d.w_q, d.w_k, 1e-6, cos, sin, q_valid=q_valid, kv_valid=kv_valid,
+                   scale=SCALE, valid_lengths=lt, window=window, gate=gate)
+    torch.cuda.synchronize()
+    return to_host(o)
+
+
+def ref(inp, window, gate_bits=None, q_valid=None, kv_valid=None, rows=None):
+    return oracle.forward(inp.q, inp.k, inp.v, inp.w_q, inp.w_k, 1e-6, 1e4, SCALE, q_valid=q_valid,
+                          kv_valid=kv_valid, rows=rows, window=window, gate_bits=gate_bits)
+
+
+# (B, S, H, Hkv, window, gate, label): 256-row tiles aligned with frames and
+# chunks (the fast schedule), frames that do not align with 32-key sub-tiles
+# or tiles (every step masked), tiles straddling chunks without anchors and
+# radius 0 (rows that see nothing in the tile's first sub-tile), grouped heads.
+CASES = [
+    (1, 4096, 2, 2, (256, 2, 1, 1), True, "aligned frames, gate"),
+    (1, 4096, 2, 2, (256, 2, 1, 1), False, "aligned frames, no gate"),
+    (1, 2000, 2, 2, (100, 3, 1, 2), True, "frames of 100 rows"),
+    (1, 1536, 2, 2, (96, 2, 0, 0), True, "no anchors, radius 0, tiles straddle chunks"),
+    (2, 1800, 4, 2, (128, 5, 1, 1), True, "grouped heads, batch 2"),
+    (1, 3000, 2, 2, (64, 1, 2, 3), True, "chunks of one frame, radius 2, 3 anchors"),
+]
+
+
+@pytest.mark.parametrize("B,S,H,Hkv,window,gate,label", CASES)
+def test_window(h3, B, S, H, Hkv, window, gate, label):
+    say("window", label)
+    inp = workloads.make_inputs(B, S, S, H, seed=70 + S % 97, Hkv=Hkv)
+    g = workloads.make_gate(B, S, H, seed=S) if gate else None
+    check(oracle.compare(run(h3, inp, window, g), ref(inp, window, g)), label)
+
+
+def test_window_with_padding_and_lengths(h3):
+    say("window with padding and per-item lengths")
+    B, S, H = 2, 2304, 2
+    window = (192, 2, 1, 1)
+    inp = workloads.make_inputs(B, S, S, H, seed=81)
+    g = workloads.make_gate(B, S, H, seed=81)
+    got = run(h3, inp, window, g, q_valid=2000, kv_valid=1700)
+    check(oracle.compare(got, ref(inp, window, g, q_valid=2000, kv_valid=1700)), "uniform padding")
+    lengths = [[2304, 2304], [1500, 1100]]
+    got = run(h3, inp, window, g, lengths=lengths)
+    want = np.concatenate([ref(workloads.Inputs(inp.q[b:b + 1], inp.k[b:b + 1], inp.v[b:b + 1], inp.w_q, inp.w_k),
+                               window, g[b:b + 1], q_valid=lengths[b][0], kv_valid=lengths[b][1])
+                           for b in range(B)])
+    check(oracle.compare(got, want), "per-item lengths")
+
+
+def test_rows_without_keys_are_zero(h3):
+    """No anchors, radius 0 and keys cut at kv_valid: rows whose chunk lies
+    past the keys see nothing and are written as zeros."""
+    say("window rows without keys")
+    S, H = 1024, 2
+    window = (64, 2, 0, 0)
+    inp = workloads.make_inputs(1, S, S, H, seed=82)
+    got = run(h3, inp, window, kv_valid=300)
+    want = ref(inp, window, kv_valid=300)
+    check(oracle.compare(got, want), "rows without keys")
+    assert np.all(got[0, 384:] == 0)
+
+
+def test_gate_in_uniform_schedule(h3):
+    """The gate alone, on the dense schedule whose last round is split over
+    workgroups and merged (4096 rows x 8 heads: 128 tiles)."""
+    say("gate, dense split schedule")
+    S, H = 4096, 8
+    inp = workloads.make_inputs(1, S, S, H, seed=83)
+    g = workloads.make_gate(1, S, H, seed=83)
+    d = DevInputs(inp)
+    cos, sin = h3.rope_tables(S)
+    o = h3.forward(d.q, d.k, d.v, d.w_q, d.w_k, 1e-6, cos, sin, scale=SCALE, gate=to_dev(g))
+    torch.cuda.synchronize()
+    check(oracle.compare(to_host(o), oracle.forward(inp.q, inp.k, inp.v, inp.w_q, inp.w_k, 1e-6, 1e4, SCALE,
+                                                    gate_bits=g)), "gate on split tiles")
+
+
+def test_window_repeatable(h3):
+    inp = workloads.make_inputs(1, 2000, 2000, 2, seed=84)
+    g = workloads.make_gate(1, 2000, 2, seed=84)
+    a = run(h3, inp, (100, 3, 1, 2), g)
+    b = run(h3, inp, (100, 3, 1, 2), g)
+    assert np.array_equal(a, b)
+
+
+def test_full_window_sampled_rows(h3):
+    """The benchmark's window workload at its full size, in the launch
+    configuration it times, on sampled rows: the anchor frame, chunk edges,
+    the first and last rows."""
+    wl = workloads.VARIANT_WORKLOADS["full_window"]
+    say("full window, sampled rows")
+    inp = workloads.make_workload_inputs(wl)
+    g = workloads.make_gate(wl.B, wl.Sq, wl.H, seed=wl.seed)
+    got = run(h3, inp, wl.window, g)
+    F, C = wl.window[0], wl.window[1]
+    edges = [F - 1, F, F + C * F - 1, F + C * F, wl.Sq // 2]
+    rows = np.unique(np.concatenate([workloads.sample_rows(wl.Sq, wl.Sq, 96, wl.seed), edges]))
+    want = ref(inp, wl.window, g, rows=rows)
+    check(oracle.compare(got[:, rows], want), "full window sampled")

@@ -139,13 +139,19 @@ __device__ inline int xcd_order(int i, int n) {
 }
 
 // Writes one query row of a finished tile: o = acc * inv rounded to bf16, or
-// +0.0 for rows at or past q_valid. Lane (l, register r of acc[dt]) holds
-// channel dt*32 + 8*(r/4) + 4*(l/32) + r%4 of its row.
+// +0.0 for rows at or past q_valid. With a gate (gate_row: the head's gate
+// column of the batch item, stride H) the row is also multiplied by
+// sigmoid(gate), the softmax gate epilogue. Lane (l, register r of acc[dt])
+// holds channel dt*32 + 8*(r/4) + 4*(l/32) + r%4 of its row.
 __device__ inline void store_row(const AttnArgs& a, uint16_t* obase, int q, int g, const f32x16_t* acc,
-                                 float inv, int q_valid) {
+                                 float inv, int q_valid, const uint16_t* gate_row) {
   if (q >= a.Sq) return;
   uint16_t* op = obase + q * ((int64_t)a.H * 128);
   const bool live = q < q_valid;
+  if (gate_row && live) {
+    const float gv = __uint_as_float((uint32_t)gate_row[(int64_t)q * a.H] << 16);
+    inv *= 1.0f / (1.0f + __expf(-gv));
+  }
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -171,7 +177,10 @@ constexpr int kRecM = 64, kRecL = 65;
 // keeps the compiler from moving memory operations across it.
 __device__ __forceinline__ void bar() { asm volatile("s_barrier" ::: "memory"); }
 
-template <int NW>
+// WIN: the frame-window variant (general mode with a.win_F > 0); the other
+// modes are compiled without its per-lane window bounds and first-key
+// bookkeeping, which would cost registers in the steady state.
+template <int NW, bool WIN>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(AttnArgs a) {
   constexpr int BM = NW * 32;
@@ -225,6 +234,11 @@ void attn_fwd_kernel(AttnArgs a) {
   // rows qv (rows at or past it are written as zeros) and the valid keys kvv.
   int bh0, q00, xb0, xe0, rec0, bh1 = 0, q01 = 0, xb1 = 0, xe1 = 0, rec1 = -1, nseg = 1;
   int qv_t = a.q_valid, kvv_t = a.kv_valid;
+  // Frame window: virtual steps v < wn1 read sub-tile v, later ones sub-tile
+  // v + ws2; win_fast when every row of the tile sees the same whole
+  // sub-tiles (only the key-padding end needs the mask).
+  int wn1 = 0x7fffffff, ws2 = 0, win_cap = 0;
+  bool win_fast = true;
   if (a.general) {
     // One tile per block. With the causal mask a tile's work grows with its
     // query block, so blocks take the longest tiles first.
@@ -233,6 +247,11 @@ void attn_fwd_kernel(AttnArgs a) {
     if (a.causal) {
       qb = n_qblocks - 1 - bid / nbh;
       bh0 = bid - (bid / nbh) * nbh;
+    } else if (WIN) {
+      // The anchor frames come first and their dense rows see the most
+      // keys: query blocks in increasing order, heads inner.
+      qb = bid / nbh;
+      bh0 = bid - qb * nbh;
     } else {
       bh0 = bid / n_qblocks;
       qb = bid - bh0 * n_qblocks;
@@ -251,6 +270,41 @@ void attn_fwd_kernel(AttnArgs a) {
     xb0 = 0;
     xe0 = (key_end + kSub - 1) / kSub;
     rec0 = -1;
+    if constexpr (WIN) {
+      // The tile's sub-tiles: [0, wn1) (the anchor frames, or every key when
+      // the tile has a dense row) then [ws2, ws2 + xe0 - wn1) (the union of
+      // its rows' chunk windows), merged when they touch.
+      const int F = a.win_F, A = a.win_A, C = a.win_C, R = a.win_R;
+      win_cap = (kvv_t + F - 1) / F / C + 1;   // chunks past the keys change nothing
+      const int q1 = min(q00 + BM, qv_t);
+      const int f0 = q00 / F, f1 = (q1 - 1) / F;
+      int hi1, lo2 = 0, hi2 = 0;
+      if (f0 < A) {
+        hi1 = kvv_t;
+        win_fast = f1 < A;
+      } else {
+        const int c0 = (f0 - A) / C, c1 = (f1 - A) / C;
+        hi1 = min(A * F, kvv_t);
+        lo2 = min((A + C * max(c0 - R, 0)) * F, kvv_t);
+        hi2 = min((A + C * min(c1 + R + 1, win_cap)) * F, kvv_t);
+        win_fast = c0 == c1 && (hi1 % kSub == 0 || hi1 == kvv_t) && lo2 % kSub == 0 &&
+                   (hi2 % kSub == 0 || hi2 == kvv_t);
+      }
+      int s1 = (hi1 + kSub - 1) / kSub;
+      int s2lo = lo2 / kSub, s2hi = (hi2 + kSub - 1) / kSub;
+      if (hi2 <= lo2) s2lo = s2hi = s1;   // no window key below kv_valid
+      if (s2lo <= s1) {   // the ranges touch or overlap: one range
+        s1 = max(s1, s2hi);
+        s2lo = s2hi = s1;
+      }
+      wn1 = s1;
+      ws2 = s2lo - s1;       // sub-tile of virtual step v >= wn1 is v + ws2
+      xe0 = s1 + (s2hi - s2lo);
+      if (xe0 == 0) {
+        zero_tile(bh0, q00);
+        return;
+      }
+    }
   } else {
     const int NU = (a.kv_valid + kSub - 1) / kSub;   // sub-tiles with at least one valid key
     int g0 = 0, g1 = 0;
@@ -312,12 +366,30 @@ void attn_fwd_kernel(AttnArgs a) {
   const int h = bh - b * a.H;
   const int bh_kv = b * a.Hkv + h / (a.H / a.Hkv);
   uint16_t* obase = a.o + ((int64_t)b * a.Sq * a.H + h) * 128;
+  const uint16_t* gate_row = a.gate ? a.gate + (int64_t)b * a.Sq * a.H + h : nullptr;
   // Masking: lane's last visible key (its query row under the causal mask,
   // capped by the valid keys), and the first sub-tile in which some lane of
   // the workgroup may see a masked key; steps before it skip the mask.
   const int row = q0 + wave * 32 + lq;
   const int lim = a.causal ? min(row, kvv_t - 1) : kvv_t - 1;
-  const int x_mask = min(a.causal ? q0 / kSub : 0x7fffffff, (kvv_t % kSub) ? kvv_t / kSub : 0x7fffffff);
+  // Sub-tile of virtual step v (the identity unless a frame window skips
+  // the keys between its two ranges).
+  auto xmap = [&](int v) {
+    if constexpr (WIN) return v < wn1 ? v : v + ws2;
+    else return v;
+  };
+  int x_mask = min(a.causal ? q0 / kSub : 0x7fffffff, (kvv_t % kSub) ? kvv_t / kSub : 0x7fffffff);
+  // Frame window, per lane: the chunk of the lane's row, or -1 for a row of
+  // an anchor frame (a dense row). Masked steps derive the row's window from
+  // it, so the steady state keeps one register for the window.
+  int c_row = -1;
+  if constexpr (WIN) {
+    const int f = row / a.win_F;
+    c_row = f < a.win_A ? -1 : (f - a.win_A) / a.win_C;
+    // Uniform tiles mask only a partial last sub-tile; the others mask every
+    // step.
+    x_mask = !win_fast ? 0 : ((kvv_t % kSub) && xmap(xe - 1) == kvv_t / kSub ? xe - 1 : 0x7fffffff);
+  }
 
   // Q fragments (B operand of S^T = K Q^T): the lane holds query row
   // 32*wave + lq, channels 16*kk + 8*g .. +7. Loaded before the ring fill so
@@ -356,8 +428,9 @@ void attn_fwd_kernel(AttnArgs a) {
   auto issue_loads = [&](int x) {
     uint8_t* slot = lds + ((x - xb) & (kRing - 1)) * kBufBytes;
     const bool live = x < xe;
-    const uint16_t* kx = kw + (int64_t)(live ? x : 0) * (kSub * 128);
-    const uint16_t* vx = vt + (int64_t)(live ? x : 0) * (kSub * 128);
+    const int xs = live ? xmap(x) : 0;
+    const uint16_t* kx = kw + (int64_t)xs * (kSub * 128);
+    const uint16_t* vx = vt + (int64_t)xs * (kSub * 128);
 #pragma unroll
     for (int i = 0; i < KLD; ++i) load_lds16(kx, live ? kKBytes : 0, koff[i], slot + (wave + NW * i) * 1024);
 #pragma unroll
@@ -373,18 +446,38 @@ void attn_fwd_kernel(AttnArgs a) {
     for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
   float m_run = 0.f;       // row offset (exp2 units), shared by the lane pair
   float l_run = 0.f;       // this lane's share of the row sum of bf16 probabilities
+  bool seen = true;        // the row has met a visible key (m_run is its offset)
   f32x16_t msplat;         // -m_run in every slot: the QK^T accumulator's initial value
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // Row max of this lane's 16 scores; with MASK, keys past the lane's last
-  // visible key are set to -inf first (a no-op in sub-tiles without such
-  // keys).
+  // Row max of this lane's 16 scores of sub-tile x; with MASK, keys the
+  // lane's row does not see (past its last visible key, or outside its frame
+  // window) are set to -inf first (a no-op in sub-tiles without such keys).
   auto rowmax = [&](f32x16_t& s, int x, auto mask) {
     if constexpr (decltype(mask)::value) {
+      // Window rows see keys below a_end (the anchor frames) and in
+      // [w_lo, w_hi) (the chunks within R of theirs); dense rows see all.
+      int a_end = 0x7fffffff, w_lo = 0, w_hi = 0;
+      if constexpr (WIN) {
+        if (c_row >= 0) {
+          // The launcher clamps F, C, R, A to the sequence (which is below
+          // 2^28 rows), so these products stay below 2^31.
+          a_end = a.win_A * a.win_F;
+          w_lo = (a.win_A + a.win_C * max(c_row - a.win_R, 0)) * a.win_F;
+          w_hi = (a.win_A + a.win_C * min(c_row + a.win_R + 1, win_cap)) * a.win_F;
+        }
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = x * kSub + (r >> 2) * 8 + g * 4 + (r & 3);
-        if (key > lim) s[r] = -INFINITY;
+        if constexpr (WIN) {
+          // Bitwise, not short-circuit, so it compiles to compares and one
+          // select instead of branches.
+          const bool hidden = (key > lim) | ((key >= a_end) & ((key < w_lo) | (key >= w_hi)));
+          s[r] = hidden ? -INFINITY : s[r];
+        } else {
+          if (key > lim) s[r] = -INFINITY;
+        }
       }
     }
     // Depth-3 tree over the 16 values.
@@ -397,9 +490,20 @@ void attn_fwd_kernel(AttnArgs a) {
   // The scores arrive as s - m_run. If some row of the wave exceeds its
   // offset by more than 2^kRescaleLog2 (rare), raise that row's m_run by its
   // excess, shift the scores and rescale the accumulator and partial sum.
-  auto maybe_rescale = [&](f32x16_t& s, float mx) {
-    if (__builtin_amdgcn_ballot_w64(mx > kRescaleLog2) != 0) {
-      const float delta = fmaxf(max_lane_pair(mx), 0.f);
+  // With MASK, a row that saw no key before (seen false, m_run 0) takes its
+  // first visible keys' maximum as its offset.
+  auto maybe_rescale = [&](f32x16_t& s, float mx, auto mask) {
+    bool trigger = mx > kRescaleLog2;
+    if constexpr (WIN && decltype(mask)::value) trigger = trigger || (!seen && mx != -INFINITY);
+    if (__builtin_amdgcn_ballot_w64(trigger) != 0) {
+      float delta = max_lane_pair(mx);
+      if constexpr (WIN && decltype(mask)::value) {
+        const bool fresh = !seen && delta != -INFINITY;
+        seen = seen || fresh;
+        delta = fresh ? delta : fmaxf(delta, 0.f);
+      } else {
+        delta = fmaxf(delta, 0.f);
+      }
       m_run += delta;
       const float alpha = __builtin_amdgcn_exp2f(-delta);
       l_run *= alpha;
@@ -492,8 +596,14 @@ void attn_fwd_kernel(AttnArgs a) {
     for (int kk = 0; kk < 8; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s, 0, 0, 0);
     read_k(rslot(min(xb + 1, xe - 1)));
     read_v(std::integral_constant<int, 0>{});
-    const float mx0 = rowmax(s, xb, Mask{});
+    const float mx0 = rowmax(s, xmap(xb), Mask{});
     m_run = max_lane_pair(mx0);
+    // A row with no visible key here (possible only under a frame window)
+    // starts from offset 0 and takes its offset from the first keys it sees.
+    if constexpr (WIN) {
+      seen = m_run != -INFINITY;
+      if (!seen) m_run = 0.f;
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       s[r] -= m_run;
@@ -529,8 +639,8 @@ void attn_fwd_kernel(AttnArgs a) {
     // after this phase's reads: a fragment read behind a pending LDS DMA
     // would make the compiler wait for every load in flight.
     issue_loads(u - 1 + kRing);
-    const float mx = rowmax(s, u + 1, mask_next);
-    maybe_rescale(s, mx);
+    const float mx = rowmax(s, xmap(u + 1), mask_next);
+    maybe_rescale(s, mx, mask_next);
     probs(s, pf);
     fence();
     // Publish sub-tile u+3 once every wave has passed this point.
@@ -565,7 +675,9 @@ void attn_fwd_kernel(AttnArgs a) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   if (rec < 0) {
-    store_row(a, obase, q0 + wave * 32 + lq, g, acc, 1.0f / sum_lane_pair(l_run), qv_seg);
+    // A row that saw no key (frame window only) has l = 0 and is written as 0.
+    const float l = sum_lane_pair(l_run);
+    store_row(a, obase, q0 + wave * 32 + lq, g, acc, (!WIN || l > 0.f) ? 1.0f / l : 0.f, qv_seg, gate_row);
   } else {
     float* pr = a.part + (int64_t)rec * kPartFloats + tid;
 #pragma unroll
@@ -628,7 +740,8 @@ __global__ __launch_bounds__(NW * 64) void attn_merge_kernel(AttnArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[dt][r] += w * pr[(dt * 16 + r) * T];
   }
-  store_row(a, obase, q0 + wave * 32 + (lane & 31), lane >> 5, acc, 1.0f / sum_lane_pair(l), a.q_valid);
+  const uint16_t* gate_row = a.gate ? a.gate + (int64_t)b * a.Sq * a.H + h : nullptr;
+  store_row(a, obase, q0 + wave * 32 + (lane & 31), lane >> 5, acc, 1.0f / sum_lane_pair(l), a.q_valid, gate_row);
 }
 
 // Transposed, key-blocked copy of v for the PV operand: a block moves 64 keys
@@ -702,7 +815,7 @@ hipError_t launch_attention(AttnArgs a, hipStream_t stream) {
   constexpr int BM = kAttnRows;
   static_assert(BM == NW * 32 && kAttnSub == kSub, "tiling constants");
   const int64_t nq = (a.Sq + BM - 1) / BM;
-  a.general = (a.causal || a.lengths != nullptr) ? 1 : 0;
+  a.general = (a.causal || a.lengths != nullptr || a.win_F > 0) ? 1 : 0;
   if (a.general) {
     // One block per (b, h, query block); each finds its own valid rows and
     // key range, so nothing is split.
@@ -710,7 +823,12 @@ hipError_t launch_attention(AttnArgs a, hipStream_t stream) {
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
     a.nqv = (int32_t)nq;
     a.n_whole = a.n_split = a.n_split_blocks = 0;
-    if (grid > 0) attn_fwd_kernel<NW><<<dim3((unsigned)grid), NW * 64, 0, stream>>>(a);
+    if (grid > 0) {
+      if (a.win_F > 0)
+        attn_fwd_kernel<NW, true><<<dim3((unsigned)grid), NW * 64, 0, stream>>>(a);
+      else
+        attn_fwd_kernel<NW, false><<<dim3((unsigned)grid), NW * 64, 0, stream>>>(a);
+    }
     return hipGetLastError();
   }
   const int64_t nqv = (a.q_valid + BM - 1) / BM;
@@ -738,7 +856,7 @@ hipError_t launch_attention(AttnArgs a, hipStream_t stream) {
   a.n_whole = (int32_t)n_whole;
   a.n_split = (int32_t)n_split;
   a.n_split_blocks = (int32_t)n_blocks;
-  if (grid > 0) attn_fwd_kernel<NW><<<dim3((unsigned)grid), NW * 64, 0, stream>>>(a);
+  if (grid > 0) attn_fwd_kernel<NW, false><<<dim3((unsigned)grid), NW * 64, 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_split == 0) return e;
   attn_merge_kernel<NW><<<dim3((unsigned)n_split), NW * 64, 0, stream>>>(a);

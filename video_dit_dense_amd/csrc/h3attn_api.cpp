@@ -188,7 +188,9 @@ H3_API size_t h3attn_forward_workspace_bytes(int32_t B, int32_t Sq, int32_t Sk, 
 
 namespace {
 
-bool uniform_schedule(const h3attn_forward_args* a) { return !a->causal && a->valid_lengths == nullptr; }
+bool uniform_schedule(const h3attn_forward_args* a) {
+  return !a->causal && a->valid_lengths == nullptr && a->window_frame_rows == 0;
+}
 
 // Validates every argument of a forward before anything is enqueued; on
 // success fills the resolved strides and the workspace layout.
@@ -204,6 +206,14 @@ int check_forward(const h3attn_forward_args* a, size_t workspace_bytes, const vo
   const size_t obytes = bshd_bytes(B, Sq, Hq);
   if (obytes == 0 || bshd_bytes(B, Sk, Hkv) == 0) return H3ATTN_ERR_BAD_SHAPE;
   if (a->causal != 0 && a->causal != 1) return H3ATTN_ERR_BAD_VALUE;
+  if (a->window_frame_rows < 0) return H3ATTN_ERR_BAD_VALUE;
+  if (a->window_frame_rows == 0) {
+    if (a->window_chunk_frames || a->window_radius || a->window_anchor_frames) return H3ATTN_ERR_BAD_VALUE;
+  } else if (a->window_chunk_frames < 1 || a->window_radius < 0 || a->window_anchor_frames < 0 || a->causal) {
+    return H3ATTN_ERR_BAD_VALUE;
+  } else if (Sq >= (1 << 28) || Sk >= (1 << 28)) {
+    return H3ATTN_ERR_BAD_SHAPE;   // keeps the window's row arithmetic in 32 bits
+  }
   if (!a->valid_lengths) {
     const int32_t qv = a->q_valid == -1 ? Sq : a->q_valid;
     const int32_t kvv = a->kv_valid == -1 ? Sk : a->kv_valid;
@@ -221,6 +231,7 @@ int check_forward(const h3attn_forward_args* a, size_t workspace_bytes, const vo
     if ((qs[i] | ks[i] | vs[i]) & 7) return H3ATTN_ERR_BAD_ALIGNMENT;
   if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o)) return H3ATTN_ERR_BAD_ALIGNMENT;
   if (a->valid_lengths && (reinterpret_cast<uintptr_t>(a->valid_lengths) & 3u)) return H3ATTN_ERR_BAD_ALIGNMENT;
+  if (a->gate && (reinterpret_cast<uintptr_t>(a->gate) & 1u)) return H3ATTN_ERR_BAD_ALIGNMENT;
   if (!workspace_layout(B, Sq, Sk, Hq, Hkv, uniform_schedule(a), wl)) return H3ATTN_ERR_BAD_SHAPE;
   if ((int64_t)B * Hq * wl->Sq_pad >= (1ll << 31) || (int64_t)B * Hkv * wl->Sk_pad >= (1ll << 31))
     return H3ATTN_ERR_BAD_SHAPE;
@@ -247,6 +258,10 @@ int check_forward(const h3attn_forward_args* a, size_t workspace_bytes, const vo
   if (a->valid_lengths) {
     const Range lr = range_of(a->valid_lengths, (size_t)B * 2 * sizeof(int32_t));
     if (overlap(ws, lr) || overlap(oq, lr)) return H3ATTN_ERR_ALIASING;
+  }
+  if (a->gate) {
+    const Range gr = range_of(a->gate, (size_t)B * Sq * Hq * sizeof(uint16_t));
+    if (overlap(ws, gr) || overlap(oq, gr)) return H3ATTN_ERR_ALIASING;
   }
   return check_device();
 }
@@ -304,6 +319,21 @@ int run_forward(const h3attn_forward_args* a, void* workspace, size_t workspace_
   at.Hkv = Hkv;
   at.causal = a->causal;
   at.lengths = a->valid_lengths;
+  if (a->window_frame_rows > 0) {
+    // Clamp the geometry to the sequence without changing which keys a row
+    // sees: a frame longer than the sequence is one frame, and counts of
+    // anchor frames, chunk frames or radius chunks beyond the sequence's
+    // frames cover everything. With S < 2^28 the kernel's products
+    // (A + C*(c + R + 1)) * F then stay below 2^31.
+    const int32_t S = std::max(Sq, Sk);
+    const int32_t F = std::min(a->window_frame_rows, S);
+    const int32_t n_frames = (S + F - 1) / F;
+    at.win_F = F;
+    at.win_C = std::min(a->window_chunk_frames, n_frames);
+    at.win_R = std::min(a->window_radius, n_frames);
+    at.win_A = std::min(a->window_anchor_frames, n_frames);
+  }
+  at.gate = a->gate;
   return status_from(h3::launch_attention(at, s));
 }
 

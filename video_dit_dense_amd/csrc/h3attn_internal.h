@@ -114,12 +114,19 @@ struct AttnArgs {
   int32_t Hkv;             // key/value heads; query head h reads kv head h / (H / Hkv)
   int32_t causal;          // key j visible to query row i only if j <= i
   const int32_t* lengths;  // optional per-item valid lengths (device), see item_valid()
+  // Frame window (win_F > 0): row or key i is in frame i / win_F; frames
+  // below win_A are anchors whose queries see every key; frame f >= win_A is
+  // in chunk (f - win_A) / win_C, and its queries see the anchor frames and
+  // the chunks within win_R of their own.
+  int32_t win_F, win_C, win_R, win_A;
+  const uint16_t* gate;    // optional [B][Sq][H] bf16: o *= sigmoid(gate)
   // Schedule, filled in by launch_attention. Uniform mode (no causal mask,
   // no per-item lengths): valid tiles (query block below q_valid) are
   // numbered g = (b*H + h) * nqv + query block; tiles g < n_whole run whole,
   // the n_split tiles after them are split over n_split_blocks workgroups;
-  // tiles past q_valid only write zeros. General mode: one workgroup per
-  // (b, h, query block), each finding its own key range.
+  // tiles past q_valid only write zeros. General mode (causal mask,
+  // per-item lengths or frame window): one workgroup per (b, h, query
+  // block), each finding its own key ranges.
   int32_t general;
   int32_t nqv, n_whole, n_split, n_split_blocks;
 };

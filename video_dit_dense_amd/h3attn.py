@@ -53,6 +53,8 @@ class ForwardArgs(ctypes.Structure):
         ("rope_rows", _I), ("rope_cos", _P), ("rope_sin", _P),
         ("q_valid", _I), ("kv_valid", _I), ("valid_lengths", _P), ("causal", _I),
         ("softmax_scale", _F),
+        ("window_frame_rows", _I), ("window_chunk_frames", _I), ("window_radius", _I),
+        ("window_anchor_frames", _I), ("gate", _P),
     ]
 
 
@@ -187,7 +189,8 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             q_valid: int | None = None, kv_valid: int | None = None, scale: float | None = None,
             out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
             stages: int = STAGE_PREPARE | STAGE_ATTEND, causal: bool = False,
-            valid_lengths: torch.Tensor | None = None) -> torch.Tensor:
+            valid_lengths: torch.Tensor | None = None, window: tuple | None = None,
+            gate: torch.Tensor | None = None) -> torch.Tensor:
     """The attention step: prologue on q/k (if weights/tables given), then
     softmax attention with key padding (kv_valid) and a zeroed query tail
     (q_valid). Returns o [B, Sq, Hq, 128] bf16.
@@ -198,9 +201,12 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     `valid_lengths`, an int32 GPU tensor [B, 2] of (q_valid, kv_valid) per
     batch item, replaces q_valid / kv_valid. `stages` selects the prepare
     and/or attend stage; a lone attend stage needs `workspace` from an earlier
-    prepare call with the same arguments. Dense inputs without the variants
-    go through h3attn_forward_stages, everything else through
-    h3attn_forward_ex."""
+    prepare call with the same arguments. `window` = (frame_rows,
+    chunk_frames, radius, anchor_frames) restricts each row to its frame
+    window (anchor-frame rows see every key); `gate`, a bf16 GPU tensor
+    [B, Sq, Hq], multiplies each output row by sigmoid(gate). Dense inputs
+    without the variants go through h3attn_forward_stages, everything else
+    through h3attn_forward_ex."""
     lib = load_library()
     for name, t in (("q", q), ("k", k), ("v", v)):
         _check_bshd(name, t, view=True)
@@ -216,13 +222,19 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         if (valid_lengths.device.type != "cuda" or valid_lengths.dtype != torch.int32
                 or tuple(valid_lengths.shape) != (B, 2) or not valid_lengths.is_contiguous()):
             raise ValueError("valid_lengths must be a contiguous int32 GPU tensor [B, 2]")
+    if gate is not None:
+        if (gate.device.type != "cuda" or gate.dtype != torch.bfloat16 or tuple(gate.shape) != (B, Sq, H)
+                or not gate.is_contiguous()):
+            raise ValueError("gate must be a contiguous bfloat16 GPU tensor [B, Sq, Hq]")
+    if window is not None and len(window) != 4:
+        raise ValueError("window is (frame_rows, chunk_frames, radius, anchor_frames)")
     o = torch.empty(B, Sq, H, D, dtype=q.dtype, device=q.device) if out is None else out
     _check_bshd("out", o)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     rows = 0 if rope_cos is None else rope_cos.shape[0]
     if stages != (STAGE_PREPARE | STAGE_ATTEND) and workspace is None:
         raise ValueError("a single stage needs a caller-kept workspace")
-    plain = (Hkv == H and not causal and valid_lengths is None
+    plain = (Hkv == H and not causal and valid_lengths is None and window is None and gate is None
              and q.is_contiguous() and k.is_contiguous() and v.is_contiguous())
     if plain:
         ws = make_workspace(B, Sq, Sk, H, q.device) if workspace is None else workspace
@@ -250,6 +262,10 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     a.valid_lengths = None if valid_lengths is None else valid_lengths.data_ptr()
     a.causal = 1 if causal else 0
     a.softmax_scale = scale
+    if window is not None:
+        a.window_frame_rows, a.window_chunk_frames, a.window_radius, a.window_anchor_frames = (
+            int(x) for x in window)
+    a.gate = None if gate is None else gate.data_ptr()
     if workspace is None:
         n = int(lib.h3attn_forward_ex_workspace_bytes(ctypes.byref(a)))
         if n == 0:
@@ -262,11 +278,12 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
 
 
 def forward_ex_workspace_bytes(B: int, Sq: int, Sk: int, Hq: int, Hkv: int, causal: bool = False,
-                               per_item_lengths: bool = False) -> int:
+                               per_item_lengths: bool = False, window: bool = False) -> int:
     """Workspace bytes h3attn_forward_ex needs for these sizes and variant."""
     a = ForwardArgs()
     a.B, a.Sq, a.Sk, a.Hq, a.Hkv, a.head_dim = B, Sq, Sk, Hq, Hkv, HEAD_DIM
     a.causal = 1 if causal else 0
+    a.window_frame_rows = 1 if window else 0
     a.valid_lengths = 16 if per_item_lengths else None   # only NULL or not matters here
     return int(load_library().h3attn_forward_ex_workspace_bytes(ctypes.byref(a)))
 

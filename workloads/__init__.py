@@ -44,6 +44,8 @@ class Workload:
     causal: bool = False  # key j visible to query row i only if j <= i
     Hkv: int = 0          # key/value heads (0: same as H)
     lengths: tuple = ()   # per-item (q_valid, kv_valid) pairs, replacing q_valid / kv_valid
+    window: tuple = ()    # (frame_rows, chunk_frames, radius, anchor_frames) of a frame window
+    gate: bool = False    # a softmax gate per (row, head)
 
     @property
     def kv_heads(self) -> int:
@@ -65,6 +67,8 @@ class Workload:
         """QK^T and PV at 2 flop per multiply-add: 4 * d * H per visible
         (query, key) pair, summed over the items' valid rows and keys; under
         the causal mask row i sees min(i + 1, kv_valid) keys."""
+        if self.window:
+            raise ValueError("the frame window's pair count is the benchmark's to compute")
         pairs = 0
         for qv, kvv in self.item_lengths():
             if self.causal:
@@ -110,6 +114,14 @@ VARIANT_WORKLOADS = {
                             description="full shape with the causal mask", causal=True),
     "full_gqa": Workload("full_gqa", 1, 104448, 104448, 6, 104448, 104448, True, True, 4,
                          description="full shape, 6 query heads on 2 key/value heads", Hkv=2),
+    # VDN-H3's frame-window attention (SGLang PR #37903, "Modifications"):
+    # chunks of 5 frames, radius 1, one anchor frame, with the softmax gate.
+    # 34 frames of 3072 rows make the 104448 rows; the pages do not give the
+    # frame size.
+    "full_window": Workload("full_window", 1, 104448, 104448, 6, 104448, 104448, True, True, 4,
+                            description="full shape, frame window: 34 frames of 3072 rows, chunks of 5 "
+                                        "frames, radius 1, 1 anchor frame, softmax gate",
+                            window=(3072, 5, 1, 1), gate=True),
     "batch_varlen": Workload("batch_varlen", 4, 32768, 32768, 8, 32768, 32768, True, True, 5,
                              description="B=4 padded to 32768 rows, items valid for 32768, 24576, "
                                          "16384 and 8192 query rows and keys, H=8",
@@ -255,3 +267,11 @@ def make_scale_shift_inputs(wl: ScaleShiftWorkload, seed: int | None = None,
     else:
         index = None
     return ScaleShiftInputs(x, scale, shift, index, w)
+
+
+def make_gate(B: int, S: int, H: int, seed: int, sigma: float = 2.0) -> np.ndarray:
+    """Softmax-gate pre-activations [B, S, H] ~ sigma*N(0,1), as bf16 bits,
+    from PCG64 with seed 1000 + seed (a stream of its own, so adding a gate
+    leaves q, k and v unchanged)."""
+    rng = np.random.default_rng(1000 + seed)
+    return f32_to_bf16_bits(rng.standard_normal((B, S, H), dtype=np.float32) * np.float32(sigma))

@@ -75,7 +75,7 @@ def step_flops(wl) -> float:
     if wl.window:
         import numpy as np
         pairs = float(window_keys_per_row(wl, np.arange(wl.q_valid)).sum()) * wl.B
-        return 4.0 * pairs * 128 * wl.H
+        return 4.0 * pairs * wl.head_dim * wl.H
     return wl.attention_flops()
 
 
@@ -119,7 +119,7 @@ def cpu_baseline(wl, inp, target_s: float):
         keys = window_keys_per_row(wl, rows)
     else:
         keys = np.minimum(rows + 1, kvv0) if wl.causal else np.full(len(rows), kvv0)
-    flops = 4.0 * float(keys.sum()) * 128
+    flops = 4.0 * float(keys.sum()) * wl.head_dim
     return {
         "value": flops / t / 1e12,
         "unit": "TFLOP/s",
@@ -323,7 +323,7 @@ def main() -> int:
     gate = dev(workloads.make_gate(wl.B, wl.Sq, wl.H, seed=wl.seed)) if wl.gate else None
     if variant:
         nbytes = h3attn.forward_ex_workspace_bytes(wl.B, wl.Sq, wl.Sk, wl.H, wl.kv_heads, causal=wl.causal,
-                                                   window=bool(wl.window),
+                                                   window=bool(wl.window), head_dim=wl.head_dim,
                                                    per_item_lengths=lengths is not None)
         ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
     else:
@@ -377,7 +377,7 @@ def main() -> int:
     # roofline; measured on the workloads whose q and k share head count and
     # valid lengths (the stand-alone entry point's contract).
     prologue = None
-    if wl.kv_heads == wl.H and not wl.lengths:
+    if wl.kv_heads == wl.H and not wl.lengths and wl.head_dim == 128:
         qo, ko = torch.empty_like(q), torch.empty_like(k)
         for _ in range(3):
             h3attn.qk_prologue(q, k, w_q if wl.norm else None, w_k if wl.norm else None, wl.eps, cos, sin, qo, ko)
@@ -419,7 +419,7 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": f"{wl.name}: B={wl.B} Sq={wl.Sq} Sk={wl.Sk} H={wl.H} Hkv={wl.kv_heads} d=128 "
+            "workload": f"{wl.name}: B={wl.B} Sq={wl.Sq} Sk={wl.Sk} H={wl.H} Hkv={wl.kv_heads} d={wl.head_dim} "
                         + (f"lengths={list(wl.lengths)} " if wl.lengths else f"q_valid={wl.q_valid} kv_valid={wl.kv_valid} ")
                         + f"causal={wl.causal} norm={wl.norm} rope={'96/128' if wl.rope else 'off'}",
             "flop_per_step": flops,

@@ -42,7 +42,7 @@ extern "C" {
 enum h3attn_status {
   H3ATTN_OK = 0,
   H3ATTN_ERR_NULL_POINTER = 1,      /* a required pointer is NULL, or only one of a pair is given */
-  H3ATTN_ERR_BAD_SHAPE = 2,         /* a size is out of range (head_dim != 128, S < 1, valid lengths, table rows) */
+  H3ATTN_ERR_BAD_SHAPE = 2,         /* a size is out of range (head_dim, S < 1, valid lengths, table rows) */
   H3ATTN_ERR_BAD_ALIGNMENT = 3,     /* a pointer is not 16-byte aligned */
   H3ATTN_ERR_ALIASING = 4,          /* an output overlaps an input (other than an exact in-place prologue) */
   H3ATTN_ERR_BAD_VALUE = 5,         /* eps, theta or softmax_scale not finite / out of range */
@@ -199,13 +199,18 @@ int h3attn_forward_stages(const uint16_t* q, const uint16_t* k, const uint16_t* 
  * causal: 0 or 1. Keys masked by the causal mask still enter the
  *   contraction with weight 0, so a non-finite value there propagates (as
  *   in torch's SDPA); keys at or past kv_valid(b) are never read.
- * head_dim: 128. Hq must be a multiple of Hkv. Norm, rotary and
- *   softmax_scale arguments are those of h3attn_forward; the rotary table
- *   rows serve sequence positions of q and k alike.
- * Work split: no causal mask and no valid_lengths uses the schedule of
- *   h3attn_forward (whole rounds of query tiles, the last round's key steps
- *   split over all compute units); otherwise one workgroup per (b, h,
- *   256-row query block), the longest first under the causal mask.
+ * head_dim: 64, 128 or 256 (the head dims FastVideo PR #1799,
+ *   "Implementation", validates). q, k, v and o are [.., head_dim]; strides
+ *   are in elements as above. The norm and rotary arguments (H3's prologue,
+ *   defined on 128 channels) must be NULL unless head_dim is 128, else
+ *   BAD_SHAPE. Hq must be a multiple of Hkv. Norm, rotary and softmax_scale
+ *   arguments are those of h3attn_forward; the rotary table rows serve
+ *   sequence positions of q and k alike.
+ * Work split: no causal mask, no valid_lengths and no window uses the
+ *   schedule of h3attn_forward (whole rounds of query tiles, the last
+ *   round's key steps split over all compute units); otherwise one
+ *   workgroup per (b, h, query block of 256 rows, 128 at head_dim 256), the
+ *   longest first under the causal mask and the frame window.
  *
  * h3attn_forward_ex_workspace_bytes() gives the workspace these arguments
  * need (0 if a size is invalid); stages are those of h3attn_forward_stages

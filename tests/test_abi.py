@@ -183,6 +183,12 @@ def test_forward_ex_workspace_bytes(lib):
     assert h3attn.forward_ex_workspace_bytes(2, 1000, 300, 4, 1, per_item_lengths=True) == \
         2 * (4 * 1024 + 2 * 1 * 512) * 256
     assert h3attn.forward_ex_workspace_bytes(1, 104448, 104448, 6, 6, window=True) == 3 * 6 * 104448 * 256
+    # rows of 2 * head_dim bytes; split records of (head_dim / 2 + 2) floats per lane of 512 (256 at 256)
+    assert h3attn.forward_ex_workspace_bytes(1, 4096, 4096, 8, 8, head_dim=64) == \
+        3 * 8 * 4096 * 128 + 2 * 256 * (32 + 2) * 512 * 4
+    assert h3attn.forward_ex_workspace_bytes(1, 4096, 4096, 8, 8, head_dim=256) == \
+        3 * 8 * 4096 * 512 + 2 * 256 * (128 + 2) * 256 * 4
+    assert h3attn.forward_ex_workspace_bytes(1, 8, 8, 4, 4, head_dim=96) == 0
     assert h3attn.forward_ex_workspace_bytes(1, 8, 8, 6, 4) == 0      # 6 heads do not group into 4
     assert h3attn.forward_ex_workspace_bytes(1, 8, 8, 4, 0) == 0
     assert lib.h3attn_forward_ex_workspace_bytes(None) == 0
@@ -214,6 +220,9 @@ def test_forward_ex_validation(lib):
     assert fwd_ex(lib, window_frame_rows=4, window_chunk_frames=2, causal=1) == VALUE
     assert fwd_ex(lib, window_frame_rows=4, window_chunk_frames=2, Sq=1 << 28, Sk=1 << 28,
                   rope_rows=1 << 28, wsb=1 << 40) == SHAPE
+    assert fwd_ex(lib, head_dim=96, wsb=1 << 30) == SHAPE
+    assert fwd_ex(lib, head_dim=64, wsb=1 << 30) == SHAPE     # norm weights and rotary need 128
+    assert fwd_ex(lib, head_dim=256, q_norm_w=None, k_norm_w=None, wsb=1 << 30) == SHAPE   # rotary still given
     assert fwd_ex(lib, gate=9 * A + 1) == ALIGN
     assert fwd_ex(lib, gate=4 * A + 256) == ALIAS               # gate inside o
 
@@ -228,6 +237,9 @@ def test_forward_ex_device_gate_without_gpu(lib):
                   gate=9 * A + 2) == DEVICE
     assert fwd_ex(lib, window_frame_rows=1 << 30, window_chunk_frames=1 << 30, window_radius=1 << 30,
                   window_anchor_frames=1 << 30) == DEVICE          # huge geometry clamps, no overflow
+    for d in (64, 256):
+        assert fwd_ex(lib, head_dim=d, q_norm_w=None, k_norm_w=None, rope_cos=None, rope_sin=None,
+                      rope_rows=0) == DEVICE
 
 
 def scale_shift(lib, x=A, y=2 * A, B=1, S=8, D=64, w=3 * A, eps=1e-6, sc=4 * A, sh=5 * A, M=2, idx=6 * A):

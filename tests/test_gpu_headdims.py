@@ -1,0 +1,118 @@
+"""GPU parity of the attention kernels at head dims 64 and 256 (FastVideo PR
+#1799, "Implementation": validated head dims 64, 128 and 256) through
+h3attn_forward_ex, against the fp64 oracle on the same seeded inputs. The Q/K
+norm and rotary prologue are H3's and defined on 128 channels, so these run
+without them. Bar: max-abs <= 2e-2 and relative RMS <= 5e-3, as for 128."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import DevInputs, say, to_dev, to_host
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+MAX_ABS = 2e-2
+REL_RMS = 5e-3
+
+
+@pytest.fixture(scope="module")
+def h3():
+    from video_dit_dense_amd import h3attn
+    h3attn.load_library()
+    return h3attn
+
+
+def check(metrics, label):
+    say(f"{label}: {metrics}")
+    assert metrics["nonfinite"] == 0, label
+    assert metrics["max_abs"] <= MAX_ABS, label
+    assert metrics["rel_rms"] <= REL_RMS, label
+
+
+def gpu(h3, inp, D, **kw):
+    d = DevInputs(inp)
+    lengths = kw.pop("lengths", None)
+    lt = None if lengths is None else torch.tensor(lengths, dtype=torch.int32, device="cuda:0")
+    gate = kw.pop("gate_bits", None)
+    o = h3.forward(d.q, d.k, d.v, scale=1 / math.sqrt(D), valid_lengths=lt,
+                   gate=None if gate is None else to_dev(gate), **kw)
+    torch.cuda.synchronize()
+    return to_host(o)
+
+
+def ref(inp, D, rows=None, **kw):
+    return oracle.forward(inp.q, inp.k, inp.v, None, None, 1e-6, None, 1 / math.sqrt(D), norm=False, rows=rows,
+                          **kw)
+
+
+# (B, Sq, Sk, H, Hkv, kwargs, label): the dense schedule with split last
+# round, padding, causal, grouped heads, per-item lengths, a frame window.
+CASES = [
+    (1, 2048, 2048, 4, 4, {}, "dense"),
+    (1, 1000, 777, 2, 2, {"q_valid": 900, "kv_valid": 700}, "padding, ragged"),
+    (1, 1300, 1300, 2, 2, {"causal": True}, "causal"),
+    (2, 600, 900, 4, 2, {}, "grouped heads"),
+    (1, 1500, 1500, 2, 1, {"window": (100, 3, 1, 1)}, "frame window, one kv head"),
+]
+
+
+@pytest.mark.parametrize("D", [64, 256])
+@pytest.mark.parametrize("B,Sq,Sk,H,Hkv,kw,label", CASES)
+def test_head_dim(h3, D, B, Sq, Sk, H, Hkv, kw, label):
+    say("head dim", D, label)
+    inp = workloads.make_inputs(B, Sq, Sk, H, seed=90 + D + Sq % 13, Hkv=Hkv, D=D)
+    check(oracle.compare(gpu(h3, inp, D, **kw), ref(inp, D, **kw)), f"D={D} {label}")
+
+
+@pytest.mark.parametrize("D", [64, 256])
+def test_head_dim_lengths_and_gate(h3, D):
+    say("head dim", D, "per-item lengths and gate")
+    B, S, H = 2, 700, 2
+    inp = workloads.make_inputs(B, S, S, H, seed=95 + D, D=D)
+    g = workloads.make_gate(B, S, H, seed=95 + D)
+    lengths = [[700, 650], [333, 100]]
+    got = gpu(h3, inp, D, lengths=lengths, gate_bits=g)
+    want = np.concatenate([ref(workloads.Inputs(inp.q[b:b + 1], inp.k[b:b + 1], inp.v[b:b + 1], inp.w_q, inp.w_k),
+                               D, q_valid=lengths[b][0], kv_valid=lengths[b][1], gate_bits=g[b:b + 1])
+                           for b in range(B)])
+    check(oracle.compare(got, want), f"D={D} lengths + gate")
+
+
+@pytest.mark.parametrize("D", [64, 256])
+def test_head_dim_fused_qkv_views(h3, D):
+    """q, k, v as slices of one [B, S, 3H, D] projection output equal the
+    dense call bit for bit."""
+    say("head dim", D, "fused QKV views")
+    B, S, H = 1, 800, 2
+    inp = workloads.make_inputs(B, S, S, H, seed=97 + D, D=D)
+    d = DevInputs(inp)
+    qkv = torch.cat([d.q, d.k, d.v], dim=2).contiguous()
+    q, k, v = qkv[:, :, :H], qkv[:, :, H:2 * H], qkv[:, :, 2 * H:]
+    o1 = h3.forward(q, k, v, scale=1 / math.sqrt(D))
+    o2 = h3.forward(d.q, d.k, d.v, scale=1 / math.sqrt(D))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("name", ["full_d64", "full_d256"])
+def test_full_sequence_sampled_rows(h3, name):
+    wl = workloads.VARIANT_WORKLOADS[name]
+    say("head dim full sequence", name)
+    inp = workloads.make_workload_inputs(wl)
+    got = gpu(h3, inp, wl.head_dim)
+    rows = workloads.sample_rows(wl.Sq, wl.Sq, 96, wl.seed)
+    check(oracle.compare(got[:, rows], ref(inp, wl.head_dim, rows=rows)), f"{name} sampled")
+
+
+def test_head_dim_rejections(h3):
+    inp = workloads.make_inputs(1, 64, 64, 1, seed=1, D=64)
+    d = DevInputs(inp)
+    with pytest.raises(ValueError, match="head_dim 128 only"):
+        h3.forward(d.q, d.k, d.v, d.w_q, d.w_k)
+    with pytest.raises(ValueError, match="D in"):
+        h3.forward(d.q[..., :32].contiguous(), d.k[..., :32].contiguous(), d.v[..., :32].contiguous())

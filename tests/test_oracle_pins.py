@@ -525,3 +525,26 @@ def test_window_attention_invariants():
     sg = oracle.sigmoid(x)
     assert np.allclose(sg + oracle.sigmoid(-x), 1.0, rtol=0, atol=4e-16)
     assert sg[0] == 0.0 and sg[-1] == 1.0
+
+
+@pytest.mark.parametrize("D", [64, 256])
+def test_attention_head_dims_match_torch_sdpa_fp64(D):
+    """The oracle's attention at the backend's other head dims (FastVideo PR
+    #1799, "Implementation": 64, 128 and 256), with padding, grouped heads
+    and the causal mask, against torch's CPU float64 SDPA."""
+    rng = np.random.default_rng(D)
+    B, Sq, Sk, H, Hkv = 2, 150, 170, 4, 2
+    q = rng.standard_normal((B, Sq, H, D))
+    k = rng.standard_normal((B, Sk, Hkv, D))
+    v = rng.standard_normal((B, Sk, Hkv, D))
+    scale = 1 / math.sqrt(D)
+    for causal in (False, True):
+        o = oracle.attention(q, k, v, scale, q_valid=[150, 99], kv_valid=[170, 120], causal=causal, block=64)
+        mask = np.zeros((B, 1, Sq, Sk), dtype=bool)
+        mask[0, 0, :, :170] = True
+        mask[1, 0, :, :120] = True
+        if causal:
+            mask &= torch.tril(torch.ones(Sq, Sk, dtype=torch.bool)).numpy()[None, None]
+        ref = _sdpa_masked(q, k, v, scale, mask, True)
+        ref[1, 99:] = 0.0
+        assert np.allclose(o, ref, rtol=1e-12, atol=1e-13)

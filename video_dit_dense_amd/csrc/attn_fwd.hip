@@ -64,6 +64,7 @@
 #include <algorithm>
 #include <atomic>
 #include <type_traits>
+#include <utility>
 
 namespace h3 {
 namespace {
@@ -118,14 +119,35 @@ __device__ inline float sum_lane_pair(float x) {
 constexpr float kRescaleLog2 = 8.0f;
 
 constexpr int kSub = 32;                       // keys per sub-tile
-constexpr int kRing = 8;                       // LDS ring depth (sub-tiles)
-constexpr int kKBytes = kSub * 256;            // K sub-tile: 32 rows x 256 B
-constexpr int kVBytes = 128 * kSub * 2;        // V^T sub-tile: 128 rows x 64 B
-constexpr int kBufBytes = kKBytes + kVBytes;   // 16 KB per ring slot
 
-// LDS layouts (no padding; XOR swizzles keep every 16-lane group of a
-// ds_read_b128 on 16 distinct 16-byte bank groups):
-//   K:   row r (key), 16-byte chunk c (channels 8c..8c+7) at r*256 + (c ^ (r & 15))*16
+// Tiling by head dim D (64, 128 or 256). D <= 128: eight waves (256 query
+// rows) per workgroup, two per SIMD, and an eight-slot ring. D = 256 holds
+// twice the accumulators and fragments, so one wave per SIMD (four waves,
+// 128 rows) with the whole register file, and a four-slot ring (32 KB slots).
+template <int D>
+struct Geo {
+  static_assert(D == 64 || D == 128 || D == 256, "head dim");
+  static constexpr int NW = D <= 128 ? 8 : 4;           // waves per workgroup
+  static constexpr int WPE = D <= 128 ? 2 : 1;          // waves per SIMD
+  static constexpr int BM = NW * 32;                    // query rows per workgroup
+  static constexpr int kRing = D <= 128 ? 8 : 4;        // LDS ring depth (sub-tiles)
+  static constexpr int kKBytes = kSub * D * 2;          // K sub-tile: 32 rows x 2D bytes
+  static constexpr int kVBytes = D * kSub * 2;          // V^T sub-tile: D rows x 64 B
+  static constexpr int kBufBytes = kKBytes + kVBytes;   // one ring slot
+  static constexpr int NF = D / 16;                     // 16-channel (QK) / 16-key (PV) fragments
+  static constexpr int NT = D / 32;                     // 32-channel output tiles
+  static constexpr int kSwz = (D / 8 < 16 ? D / 8 : 16) - 1;   // K chunk swizzle mask
+  static constexpr int nK = kKBytes / 1024;             // 1 KB direct loads per sub-tile (K)
+  static constexpr int LDPS = (kKBytes + kVBytes) / 1024 / NW;   // per wave per sub-tile
+  static constexpr int kSlotsPerSeg = 65536 / kBufBytes;         // slots in a 16-bit LDS offset
+  static constexpr int kRecM = NT * 16, kRecL = NT * 16 + 1;     // partial record layout
+  static_assert(LDPS * NW * 1024 == kKBytes + kVBytes, "tile split");
+  static_assert(kRing <= 2 * kSlotsPerSeg, "two address segments at most");
+};
+
+// LDS layouts (no padding; XOR swizzles keep every 8-lane group of a
+// ds_read_b128 on 8 distinct 16-byte bank groups):
+//   K:   row r (key), 16-byte chunk c (channels 8c..8c+7) at r*2D + (c ^ (r & kSwz))*16
 //   V^T: row d (channel), chunk c (positions 8c..8c+7) at d*64 + (c ^ ((d >> 2) & 3))*16
 
 // Blocks are dispatched round-robin over the 8 XCDs, so block i of a range
@@ -143,17 +165,18 @@ __device__ inline int xcd_order(int i, int n) {
 // column of the batch item, stride H) the row is also multiplied by
 // sigmoid(gate), the softmax gate epilogue. Lane (l, register r of acc[dt])
 // holds channel dt*32 + 8*(r/4) + 4*(l/32) + r%4 of its row.
+template <int D>
 __device__ inline void store_row(const AttnArgs& a, uint16_t* obase, int q, int g, const f32x16_t* acc,
                                  float inv, int q_valid, const uint16_t* gate_row) {
   if (q >= a.Sq) return;
-  uint16_t* op = obase + q * ((int64_t)a.H * 128);
+  uint16_t* op = obase + q * ((int64_t)a.H * D);
   const bool live = q < q_valid;
   if (gate_row && live) {
     const float gv = __uint_as_float((uint32_t)gate_row[(int64_t)q * a.H] << 16);
     inv *= 1.0f / (1.0f + __expf(-gv));
   }
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
+  for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq) {
       const int d0 = dt * 32 + rq * 8 + g * 4;
@@ -168,28 +191,37 @@ __device__ inline void store_row(const AttnArgs& a, uint16_t* obase, int q, int 
 
 // Partial record of a split tile, per thread t of the T-thread workgroup
 // (fp32, thread-contiguous so every access is coalesced): accumulator
-// register r at [r * T + t], then the row offset m at [64 * T + t] and this
-// lane's row-sum share at [65 * T + t].
-constexpr int kRecM = 64, kRecL = 65;
+// register r at [r * T + t] (D/2 of them), then the row offset m at
+// [kRecM * T + t] and this lane's row-sum share at [kRecL * T + t].
+
+// f(integral_constant<int, K>) for each K of the sequence, in order.
+template <int... K, typename F>
+__device__ __forceinline__ void for_each_index(std::integer_sequence<int, K...>, F&& f) {
+  (f(std::integral_constant<int, K>{}), ...);
+}
 
 // Workgroup barrier without a memory fence: the callers order LDS traffic
 // through the ring schedule and their own vmcnt waits. The "memory" clobber
 // keeps the compiler from moving memory operations across it.
 __device__ __forceinline__ void bar() { asm volatile("s_barrier" ::: "memory"); }
 
-// WIN: the frame-window variant (general mode with a.win_F > 0); the other
-// modes are compiled without its per-lane window bounds and first-key
-// bookkeeping, which would cost registers in the steady state.
-template <int NW, bool WIN>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// D: the head dim. WIN: the frame-window variant (general mode with
+// a.win_F > 0); the other modes are compiled without its per-lane window
+// bounds and first-key bookkeeping, which would cost registers in the
+// steady state.
+template <int D, bool WIN>
+__global__ __launch_bounds__(Geo<D>::NW * 64) __attribute__((amdgpu_waves_per_eu(Geo<D>::WPE, Geo<D>::WPE)))
 void attn_fwd_kernel(AttnArgs a) {
-  constexpr int BM = NW * 32;
+  using G = Geo<D>;
+  constexpr int NW = G::NW;
+  constexpr int BM = G::BM;
   constexpr int T = NW * 64;
-  constexpr int KLD = kKBytes / 1024 / NW;     // 1 KB direct loads per wave per sub-tile (K)
-  constexpr int VLD = kVBytes / 1024 / NW;     // (V)
-  constexpr int LDPS = KLD + VLD;              // load instructions per wave per sub-tile
-  static_assert(KLD * NW * 1024 == kKBytes && VLD * NW * 1024 == kVBytes, "tile split");
-  static_assert(kPartFloats == 66 * T, "partial record size");
+  constexpr int LDPS = G::LDPS;                // 1 KB load instructions per wave per sub-tile
+  constexpr int kRing = G::kRing;
+  constexpr int kKBytes = G::kKBytes;
+  constexpr int kBufBytes = G::kBufBytes;
+  constexpr int NF = G::NF;
+  constexpr int NT = G::NT;
   // One LDS object only: the ring, then the per-wave SIMD ids. (With a
   // second LDS variable the compiler can no longer tell fragment reads from
   // the ring's DMA writes and waits for every load in flight before each.)
@@ -220,11 +252,12 @@ void attn_fwd_kernel(AttnArgs a) {
   // row or no valid key.
   auto zero_tile = [&](int bh, int q0) {
     const int b = bh / a.H, h = bh - b * a.H;
-    uint16_t* obase = a.o + ((int64_t)b * a.Sq * a.H + h) * 128;
-    const int64_t orow = (int64_t)a.H * 128;
-    for (int idx = tid; idx < BM * 16; idx += T) {
-      const int q = q0 + (idx >> 4);
-      if (q < a.Sq) *reinterpret_cast<u32x4_t*>(obase + q * orow + (idx & 15) * 8) = u32x4_t{0u, 0u, 0u, 0u};
+    uint16_t* obase = a.o + ((int64_t)b * a.Sq * a.H + h) * D;
+    const int64_t orow = (int64_t)a.H * D;
+    constexpr int CPR = D / 8;   // 16-byte chunks per row
+    for (int idx = tid; idx < BM * CPR; idx += T) {
+      const int q = q0 + idx / CPR;
+      if (q < a.Sq) *reinterpret_cast<u32x4_t*>(obase + q * orow + (idx % CPR) * 8) = u32x4_t{0u, 0u, 0u, 0u};
     }
   };
 
@@ -347,9 +380,10 @@ void attn_fwd_kernel(AttnArgs a) {
   }
 
   // Per-lane LDS byte addresses of the matrix-core operand reads. K fragment
-  // kk of a sub-tile is at kbase ^ (32 kk) (the swizzle only touches address
-  // bits 4..7 and 32 kk only bits 5..7), so one register serves all eight.
-  const uint32_t kbase = lq * 256 + ((g ^ (lq & 15)) * 16);
+  // kk of a sub-tile is at kbase ^ (32 kk): its chunk is 2kk + g, stored at
+  // (2kk + g) ^ (lq & kSwz) = 2kk ^ (g ^ (lq & kSwz)), and 32 kk stays below
+  // the row size, so one register serves every fragment of the row.
+  const uint32_t kbase = lq * (2 * D) + ((g ^ (lq & G::kSwz)) * 16);
   uint32_t vaddr[2];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) vaddr[ks] = kKBytes + lq * 64 + ((((2 * ks) | g) ^ ((lq >> 2) & 3)) * 16);
@@ -365,7 +399,7 @@ void attn_fwd_kernel(AttnArgs a) {
   const int b = bh / a.H;
   const int h = bh - b * a.H;
   const int bh_kv = b * a.Hkv + h / (a.H / a.Hkv);
-  uint16_t* obase = a.o + ((int64_t)b * a.Sq * a.H + h) * 128;
+  uint16_t* obase = a.o + ((int64_t)b * a.Sq * a.H + h) * D;
   const uint16_t* gate_row = a.gate ? a.gate + (int64_t)b * a.Sq * a.H + h : nullptr;
   // Masking: lane's last visible key (its query row under the causal mask,
   // capped by the valid keys), and the first sub-tile in which some lane of
@@ -394,30 +428,33 @@ void attn_fwd_kernel(AttnArgs a) {
   // Q fragments (B operand of S^T = K Q^T): the lane holds query row
   // 32*wave + lq, channels 16*kk + 8*g .. +7. Loaded before the ring fill so
   // the in-order load counter covers them.
-  bf16x8_t qf[8];
+  bf16x8_t qf[NF];
   {
-    const uint16_t* qp = a.qw + ((int64_t)bh * a.Sq_pad + q0 + wave * 32 + lq) * 128 + g * 8;
+    const uint16_t* qp = a.qw + ((int64_t)bh * a.Sq_pad + q0 + wave * 32 + lq) * D + g * 8;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) qf[kk] = *reinterpret_cast<const bf16x8_t*>(qp + kk * 16);
+    for (int kk = 0; kk < NF; ++kk) qf[kk] = *reinterpret_cast<const bf16x8_t*>(qp + kk * 16);
   }
 
   // Per-lane byte offsets of the direct loads within a sub-tile (K and V^T
-  // sub-tiles are contiguous 8 KB blocks in the workspace). The lane that
-  // fills LDS chunk Q fetches the logical chunk the swizzle puts there.
-  const uint16_t* kw = a.kw + (int64_t)bh_kv * a.Sk_pad * 128;
-  const uint16_t* vt = a.vt + (int64_t)bh_kv * a.Sk_pad * 128;
-  int koff[KLD], voff[VLD];
+  // sub-tiles are contiguous blocks of kKBytes in the workspace). Load i of
+  // this wave fills LDS bytes [1024 j, 1024 j + 1024) of the slot, j = wave
+  // + NW i: K's chunks for j < nK, V^T's after them. The lane that fills
+  // LDS chunk Q fetches the logical chunk the swizzle puts there.
+  const uint16_t* kw = a.kw + (int64_t)bh_kv * a.Sk_pad * D;
+  const uint16_t* vt = a.vt + (int64_t)bh_kv * a.Sk_pad * D;
+  int loff[LDPS];
 #pragma unroll
-  for (int i = 0; i < KLD; ++i) {
-    const int Q = (wave + NW * i) * 64 + lane;
-    const int r = Q >> 4, p = Q & 15;
-    koff[i] = (r * 128 + ((p ^ (r & 15)) * 8)) * 2;
-  }
-#pragma unroll
-  for (int i = 0; i < VLD; ++i) {
-    const int Q = (wave + NW * i) * 64 + lane;
-    const int d = Q >> 2, p = Q & 3;
-    voff[i] = (d * kSub + ((p ^ ((d >> 2) & 3)) * 8)) * 2;
+  for (int i = 0; i < LDPS; ++i) {
+    const int j = wave + NW * i;
+    if (j < G::nK) {
+      const int Q = j * 64 + lane;
+      const int r = Q / (D / 8), p = Q % (D / 8);
+      loff[i] = (r * D + ((p ^ (r & G::kSwz)) * 8)) * 2;
+    } else {
+      const int Q = (j - G::nK) * 64 + lane;
+      const int d = Q >> 2, p = Q & 3;
+      loff[i] = (d * kSub + ((p ^ ((d >> 2) & 3)) * 8)) * 2;
+    }
   }
   // One buffer resource per sub-tile (base in SGPRs, 8 KB range), so the
   // loads need no vector address arithmetic and offsets stay 32-bit at any
@@ -429,19 +466,20 @@ void attn_fwd_kernel(AttnArgs a) {
     uint8_t* slot = lds + ((x - xb) & (kRing - 1)) * kBufBytes;
     const bool live = x < xe;
     const int xs = live ? xmap(x) : 0;
-    const uint16_t* kx = kw + (int64_t)xs * (kSub * 128);
-    const uint16_t* vx = vt + (int64_t)xs * (kSub * 128);
+    const uint16_t* kx = kw + (int64_t)xs * (kSub * D);
+    const uint16_t* vx = vt + (int64_t)xs * (kSub * D);
 #pragma unroll
-    for (int i = 0; i < KLD; ++i) load_lds16(kx, live ? kKBytes : 0, koff[i], slot + (wave + NW * i) * 1024);
-#pragma unroll
-    for (int i = 0; i < VLD; ++i) load_lds16(vx, live ? kVBytes : 0, voff[i], slot + kKBytes + (wave + NW * i) * 1024);
+    for (int i = 0; i < LDPS; ++i) {
+      const int j = wave + NW * i;
+      load_lds16(j < G::nK ? kx : vx, live ? kKBytes : 0, loff[i], slot + j * 1024);
+    }
   };
 #pragma unroll
   for (int i = 0; i < kRing - 1; ++i) issue_loads(xb + i);
 
-  f32x16_t acc[4];
+  f32x16_t acc[NT];
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
+  for (int dt = 0; dt < NT; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
   float m_run = 0.f;       // row offset (exp2 units), shared by the lane pair
@@ -515,7 +553,7 @@ void attn_fwd_kernel(AttnArgs a) {
         msplat[r] -= delta;
       }
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+      for (int dt = 0; dt < NT; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
     }
@@ -545,39 +583,41 @@ void attn_fwd_kernel(AttnArgs a) {
   // sched_barrier(0) fences keep the compiler from moving instructions
   // across the phase boundaries.
   auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
-  bf16x8_t kf[8], vf[8], pf[2];
+  bf16x8_t kf[NF], vf[NF], pf[2];
   // Ring slot of sub-tile x is (x - xb) mod kRing. Fragment reads take the
   // slot either at run time or, in the unrolled steady state, as a
   // compile-time constant that lands in the instruction's offset field (the
-  // field holds 16 bits, so slots 4..7 use addresses biased by 64 KB).
-  uint32_t ka[8], kah[8], vah[2];
+  // field holds 16 bits, so slots past the first 64 KB use addresses biased
+  // by 64 KB).
+  constexpr int SPS = G::kSlotsPerSeg;
+  uint32_t ka[NF], kah[NF], vah[2];
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
+  for (int kk = 0; kk < NF; ++kk) {
     ka[kk] = kbase ^ (32u * kk);
-    kah[kk] = ka[kk] + 4 * kBufBytes;
+    kah[kk] = ka[kk] + SPS * kBufBytes;
   }
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) vah[ks] = vaddr[ks] + 4 * kBufBytes;
+  for (int ks = 0; ks < 2; ++ks) vah[ks] = vaddr[ks] + SPS * kBufBytes;
   auto read_k = [&](auto slot) {
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
+    for (int kk = 0; kk < NF; ++kk) {
       if constexpr (std::is_integral_v<decltype(slot)>)
         kf[kk] = *reinterpret_cast<const bf16x8_t*>(lds + slot * kBufBytes + ka[kk]);
-      else if constexpr (decltype(slot)::value < 4)
+      else if constexpr (decltype(slot)::value < SPS)
         kf[kk] = *reinterpret_cast<const bf16x8_t*>(lds + decltype(slot)::value * kBufBytes + ka[kk]);
       else
-        kf[kk] = *reinterpret_cast<const bf16x8_t*>(lds + (decltype(slot)::value - 4) * kBufBytes + kah[kk]);
+        kf[kk] = *reinterpret_cast<const bf16x8_t*>(lds + (decltype(slot)::value - SPS) * kBufBytes + kah[kk]);
     }
   };
   auto read_v = [&](auto slot) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < NF; ++i) {
       if constexpr (std::is_integral_v<decltype(slot)>)
         vf[i] = *reinterpret_cast<const bf16x8_t*>(lds + slot * kBufBytes + vaddr[i & 1] + (i >> 1) * 2048);
-      else if constexpr (decltype(slot)::value < 4)
+      else if constexpr (decltype(slot)::value < SPS)
         vf[i] = *reinterpret_cast<const bf16x8_t*>(lds + decltype(slot)::value * kBufBytes + vaddr[i & 1] + (i >> 1) * 2048);
       else
-        vf[i] = *reinterpret_cast<const bf16x8_t*>(lds + (decltype(slot)::value - 4) * kBufBytes + vah[i & 1] + (i >> 1) * 2048);
+        vf[i] = *reinterpret_cast<const bf16x8_t*>(lds + (decltype(slot)::value - SPS) * kBufBytes + vah[i & 1] + (i >> 1) * 2048);
     }
   };
   auto rslot = [&](int x) { return (x - xb) & (kRing - 1); };
@@ -593,7 +633,7 @@ void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s, 0, 0, 0);
+    for (int kk = 0; kk < NF; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s, 0, 0, 0);
     read_k(rslot(min(xb + 1, xe - 1)));
     read_v(std::integral_constant<int, 0>{});
     const float mx0 = rowmax(s, xmap(xb), Mask{});
@@ -626,9 +666,9 @@ void attn_fwd_kernel(AttnArgs a) {
     fence();
     s = msplat;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s, 0, 0, 0);
+    for (int kk = 0; kk < NF; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s, 0, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf[i & 1], acc[i >> 1], 0, 0, 0);
+    for (int i = 0; i < NF; ++i) acc[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf[i & 1], acc[i >> 1], 0, 0, 0);
     fence();
     bar();
     fence();
@@ -655,20 +695,18 @@ void attn_fwd_kernel(AttnArgs a) {
   if (role) bar();
   int u = xb;
   for (; u + kRing <= min(xe - 2, x_mask - 1); u += kRing) {
-    using std::integral_constant;
-    step(u + 0, NoMask{}, integral_constant<int, 1>{}, integral_constant<int, 2>{});
-    step(u + 1, NoMask{}, integral_constant<int, 2>{}, integral_constant<int, 3>{});
-    step(u + 2, NoMask{}, integral_constant<int, 3>{}, integral_constant<int, 4>{});
-    step(u + 3, NoMask{}, integral_constant<int, 4>{}, integral_constant<int, 5>{});
-    step(u + 4, NoMask{}, integral_constant<int, 5>{}, integral_constant<int, 6>{});
-    step(u + 5, NoMask{}, integral_constant<int, 6>{}, integral_constant<int, 7>{});
-    step(u + 6, NoMask{}, integral_constant<int, 7>{}, integral_constant<int, 0>{});
-    step(u + 7, NoMask{}, integral_constant<int, 0>{}, integral_constant<int, 1>{});
+    // Steps u + k, k = 0..kRing-1: V of sub-tile u+k+1 in slot (k+1) mod
+    // kRing, K of u+k+2 in slot (k+2) mod kRing.
+    for_each_index(std::make_integer_sequence<int, kRing>{}, [&](auto k) {
+      constexpr int K = decltype(k)::value;
+      step(u + K, NoMask{}, std::integral_constant<int, (K + 1) % kRing>{},
+           std::integral_constant<int, (K + 2) % kRing>{});
+    });
   }
   for (; u < xe - 1; ++u) step(u, Mask{}, rslot(u + 1), rslot(min(u + 2, xe - 1)));
   // Last X phase: PV of the last sub-tile only.
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf[i & 1], acc[i >> 1], 0, 0, 0);
+  for (int i = 0; i < NF; ++i) acc[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf[i & 1], acc[i >> 1], 0, 0, 0);
   if (!role) bar();
   // The ring holds refills that nobody reads; let them retire so no LDS
   // write is pending when the workgroup ends or the next segment starts.
@@ -677,15 +715,15 @@ void attn_fwd_kernel(AttnArgs a) {
   if (rec < 0) {
     // A row that saw no key (frame window only) has l = 0 and is written as 0.
     const float l = sum_lane_pair(l_run);
-    store_row(a, obase, q0 + wave * 32 + lq, g, acc, (!WIN || l > 0.f) ? 1.0f / l : 0.f, qv_seg, gate_row);
+    store_row<D>(a, obase, q0 + wave * 32 + lq, g, acc, (!WIN || l > 0.f) ? 1.0f / l : 0.f, qv_seg, gate_row);
   } else {
-    float* pr = a.part + (int64_t)rec * kPartFloats + tid;
+    float* pr = a.part + (int64_t)rec * attn_part_floats(D) + tid;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+    for (int dt = 0; dt < NT; ++dt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) pr[(dt * 16 + r) * T] = acc[dt][r];
-    pr[kRecM * T] = m_run;
-    pr[kRecL * T] = l_run;
+    pr[G::kRecM * T] = m_run;
+    pr[G::kRecL * T] = l_run;
   }
   if (si + 1 < nseg) __syncthreads();   // the next segment refills the LDS ring
   }
@@ -695,10 +733,12 @@ void attn_fwd_kernel(AttnArgs a) {
 // meet the tile each left one partial record (O_i, m_i, l_i) with O_i and l_i
 // relative to their own offset m_i; with M = max m_i the tile's result is
 // sum 2^(m_i - M) O_i / sum 2^(m_i - M) l_i (scores are in exp2 units).
-template <int NW>
-__global__ __launch_bounds__(NW * 64) void attn_merge_kernel(AttnArgs a) {
-  constexpr int BM = NW * 32;
-  constexpr int T = NW * 64;
+template <int D>
+__global__ __launch_bounds__(Geo<D>::NW * 64) void attn_merge_kernel(AttnArgs a) {
+  using G = Geo<D>;
+  constexpr int BM = G::BM;
+  constexpr int T = G::NW * 64;
+  constexpr int NT = G::NT;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -709,7 +749,7 @@ __global__ __launch_bounds__(NW * 64) void attn_merge_kernel(AttnArgs a) {
   const int q0 = (tg - bh * a.nqv) * BM;
   const int b = bh / a.H;
   const int h = bh - b * a.H;
-  uint16_t* obase = a.o + ((int64_t)b * a.Sq * a.H + h) * 128;
+  uint16_t* obase = a.o + ((int64_t)b * a.Sq * a.H + h) * D;
 
   // Block j covers steps [j*U/n, (j+1)*U/n), so step x lies in block
   // floor(((x + 1) * n - 1) / U); its record for tile t is 2j + (t - first
@@ -721,40 +761,42 @@ __global__ __launch_bounds__(NW * 64) void attn_merge_kernel(AttnArgs a) {
   const int j1 = (int)(((x1 + 1) * n - 1) / U);
   auto record = [&](int j) {
     const int first = (int)(((int64_t)j * U / n) / NU);
-    return a.part + (int64_t)(2 * j + (t - first)) * kPartFloats + tid;
+    return a.part + (int64_t)(2 * j + (t - first)) * attn_part_floats(D) + tid;
   };
   float M = -INFINITY;
-  for (int j = j0; j <= j1; ++j) M = fmaxf(M, record(j)[kRecM * T]);
-  f32x16_t acc[4];
+  for (int j = j0; j <= j1; ++j) M = fmaxf(M, record(j)[G::kRecM * T]);
+  f32x16_t acc[NT];
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
+  for (int dt = 0; dt < NT; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
   float l = 0.f;
   for (int j = j0; j <= j1; ++j) {
     const float* pr = record(j);
-    const float w = __builtin_amdgcn_exp2f(pr[kRecM * T] - M);
-    l += w * pr[kRecL * T];
+    const float w = __builtin_amdgcn_exp2f(pr[G::kRecM * T] - M);
+    l += w * pr[G::kRecL * T];
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+    for (int dt = 0; dt < NT; ++dt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[dt][r] += w * pr[(dt * 16 + r) * T];
   }
   const uint16_t* gate_row = a.gate ? a.gate + (int64_t)b * a.Sq * a.H + h : nullptr;
-  store_row(a, obase, q0 + wave * 32 + (lane & 31), lane >> 5, acc, 1.0f / sum_lane_pair(l), a.q_valid, gate_row);
+  store_row<D>(a, obase, q0 + wave * 32 + (lane & 31), lane >> 5, acc, 1.0f / sum_lane_pair(l), a.q_valid, gate_row);
 }
 
 // Transposed, key-blocked copy of v for the PV operand: a block moves 64 keys
-// (two sub-tiles) x 128 channels of one (b, h) through LDS, reading 256-byte
-// rows of v and writing one contiguous 16 KB block of vt. Keys at or past
-// kv_valid are written as zeros and never read.
+// (two sub-tiles) x D channels of one (b, h) through LDS, reading 2D-byte
+// rows of v and writing one contiguous block of 128 D bytes of vt. Keys at or
+// past kv_valid are written as zeros and never read.
+template <int D>
 __global__ __launch_bounds__(256) void v_relayout_kernel(const uint16_t* __restrict__ v, int64_t sb,
                                                          int64_t ss, int64_t sh,
                                                          uint16_t* __restrict__ vt, int32_t H,
                                                          int32_t Sk, int32_t kv_valid,
                                                          const int32_t* __restrict__ lengths,
                                                          int32_t Sk_pad) {
-  constexpr int kPitch = 136;  // 272-byte rows
+  constexpr int kPitch = D + 8;   // row pitch in elements: 16 bytes of padding
+  constexpr int CPR = D / 8;      // 16-byte chunks per row of v
   __shared__ __attribute__((aligned(16))) uint16_t tile[64 * kPitch];
   const int p0 = blockIdx.x * 64;
   const int bh = blockIdx.y;
@@ -762,21 +804,21 @@ __global__ __launch_bounds__(256) void v_relayout_kernel(const uint16_t* __restr
   const int tid = threadIdx.x;
   const int32_t valid = item_valid(lengths, b, 1, kv_valid, Sk);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < D / 32; ++i) {
     const int idx = tid + 256 * i;
-    const int key = idx >> 4, ch = idx & 15;
+    const int key = idx / CPR, ch = idx % CPR;
     u32x4_t val = u32x4_t{0u, 0u, 0u, 0u};
     if (p0 + key < valid)
       val = *reinterpret_cast<const u32x4_t*>(v + (int64_t)b * sb + (int64_t)(p0 + key) * ss + (int64_t)h * sh + ch * 8);
     *reinterpret_cast<u32x4_t*>(&tile[key * kPitch + ch * 8]) = val;
   }
   __syncthreads();
-  // Output chunk idx covers sub-tile xs = idx/512, channel d, positions 8pc..8pc+7.
-  uint16_t* out = vt + ((int64_t)bh * Sk_pad + p0) * kHeadDim;
+  // Output chunk idx covers sub-tile xs = idx/(4D), channel d, positions 8pc..8pc+7.
+  uint16_t* out = vt + ((int64_t)bh * Sk_pad + p0) * D;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < D / 32; ++i) {
     const int idx = tid + 256 * i;
-    const int xs = idx >> 9, d = (idx >> 2) & 127, pc = idx & 3;
+    const int xs = idx / (4 * D), d = (idx >> 2) % D, pc = idx & 3;
     uint32_t packed[4];
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
@@ -810,10 +852,13 @@ int device_cus() {
 
 }  // namespace
 
-hipError_t launch_attention(AttnArgs a, hipStream_t stream) {
-  constexpr int NW = kAttnWaves;
-  constexpr int BM = kAttnRows;
-  static_assert(BM == NW * 32 && kAttnSub == kSub, "tiling constants");
+namespace {
+
+template <int D>
+hipError_t launch_attention_d(AttnArgs a, hipStream_t stream) {
+  constexpr int NW = Geo<D>::NW;
+  constexpr int BM = Geo<D>::BM;
+  static_assert(BM == attn_rows(D) && NW * 64 == attn_threads(D) && kAttnSub == kSub, "tiling constants");
   const int64_t nq = (a.Sq + BM - 1) / BM;
   a.general = (a.causal || a.lengths != nullptr || a.win_F > 0) ? 1 : 0;
   if (a.general) {
@@ -825,9 +870,9 @@ hipError_t launch_attention(AttnArgs a, hipStream_t stream) {
     a.n_whole = a.n_split = a.n_split_blocks = 0;
     if (grid > 0) {
       if (a.win_F > 0)
-        attn_fwd_kernel<NW, true><<<dim3((unsigned)grid), NW * 64, 0, stream>>>(a);
+        attn_fwd_kernel<D, true><<<dim3((unsigned)grid), NW * 64, 0, stream>>>(a);
       else
-        attn_fwd_kernel<NW, false><<<dim3((unsigned)grid), NW * 64, 0, stream>>>(a);
+        attn_fwd_kernel<D, false><<<dim3((unsigned)grid), NW * 64, 0, stream>>>(a);
     }
     return hipGetLastError();
   }
@@ -856,18 +901,34 @@ hipError_t launch_attention(AttnArgs a, hipStream_t stream) {
   a.n_whole = (int32_t)n_whole;
   a.n_split = (int32_t)n_split;
   a.n_split_blocks = (int32_t)n_blocks;
-  if (grid > 0) attn_fwd_kernel<NW, false><<<dim3((unsigned)grid), NW * 64, 0, stream>>>(a);
+  if (grid > 0) attn_fwd_kernel<D, false><<<dim3((unsigned)grid), NW * 64, 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_split == 0) return e;
-  attn_merge_kernel<NW><<<dim3((unsigned)n_split), NW * 64, 0, stream>>>(a);
+  attn_merge_kernel<D><<<dim3((unsigned)n_split), NW * 64, 0, stream>>>(a);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attention(AttnArgs a, hipStream_t stream) {
+  switch (a.D) {
+    case 64: return launch_attention_d<64>(a, stream);
+    case 128: return launch_attention_d<128>(a, stream);
+    case 256: return launch_attention_d<256>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_v_relayout(const uint16_t* v, int64_t sb, int64_t ss, int64_t sh, uint16_t* vt,
                              int32_t B, int32_t Sk, int32_t H, int32_t kv_valid,
-                             const int32_t* lengths, int32_t Sk_pad, hipStream_t stream) {
+                             const int32_t* lengths, int32_t Sk_pad, int32_t D, hipStream_t stream) {
   const dim3 grid((unsigned)(Sk_pad / 64), (unsigned)(B * H));
-  v_relayout_kernel<<<grid, 256, 0, stream>>>(v, sb, ss, sh, vt, H, Sk, kv_valid, lengths, Sk_pad);
+  switch (D) {
+    case 64: v_relayout_kernel<64><<<grid, 256, 0, stream>>>(v, sb, ss, sh, vt, H, Sk, kv_valid, lengths, Sk_pad); break;
+    case 128: v_relayout_kernel<128><<<grid, 256, 0, stream>>>(v, sb, ss, sh, vt, H, Sk, kv_valid, lengths, Sk_pad); break;
+    case 256: v_relayout_kernel<256><<<grid, 256, 0, stream>>>(v, sb, ss, sh, vt, H, Sk, kv_valid, lengths, Sk_pad); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

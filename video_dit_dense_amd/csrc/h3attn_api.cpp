@@ -45,9 +45,9 @@ Range range_of(const void* p, size_t bytes) {
 }
 bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 
-// Element count of a [B, S, H, 128] tensor, or 0 on overflow.
-size_t bshd_bytes(int32_t B, int32_t S, int32_t H) {
-  const unsigned __int128 n = (unsigned __int128)B * (unsigned __int128)S * (unsigned __int128)H * 128u * 2u;
+// Bytes of a [B, S, H, D] bf16 tensor, or 0 on overflow.
+size_t bshd_bytes(int32_t B, int32_t S, int32_t H, int32_t D = h3::kHeadDim) {
+  const unsigned __int128 n = (unsigned __int128)B * (unsigned __int128)S * (unsigned __int128)H * (unsigned)D * 2u;
   if (n > (unsigned __int128)(INT64_MAX / 4)) return 0;
   return (size_t)n;
 }
@@ -80,15 +80,17 @@ struct WorkspaceLayout {
 // Workspace of a forward with Hq query heads and Hkv key/value heads; the
 // partial records of split tiles are only needed by the uniform schedule
 // (no causal mask, no per-item lengths).
-bool workspace_layout(int32_t B, int32_t Sq, int32_t Sk, int32_t Hq, int32_t Hkv, bool uniform,
+bool workspace_layout(int32_t B, int32_t Sq, int32_t Sk, int32_t Hq, int32_t Hkv, bool uniform, int32_t D,
                       WorkspaceLayout* w) {
   if (B < 1 || Sq < 1 || Sk < 1 || Hq < 1 || Hkv < 1) return false;
+  if (D != 64 && D != 128 && D != 256) return false;
   w->Sq_pad = round_up(Sq, h3::kRowPad);
   w->Sk_pad = round_up(Sk, h3::kRowPad);
-  const unsigned __int128 qb = (unsigned __int128)B * (unsigned __int128)Hq * (unsigned __int128)w->Sq_pad * 256u;
-  const unsigned __int128 kb = (unsigned __int128)B * (unsigned __int128)Hkv * (unsigned __int128)w->Sk_pad * 256u;
-  w->part_slots = uniform ? h3::split_part_slots(B, Sq, Sk, Hq) : 0;
-  const unsigned __int128 pb = (unsigned __int128)w->part_slots * h3::kPartBytes;
+  const unsigned row = 2u * (unsigned)D;
+  const unsigned __int128 qb = (unsigned __int128)B * (unsigned __int128)Hq * (unsigned __int128)w->Sq_pad * row;
+  const unsigned __int128 kb = (unsigned __int128)B * (unsigned __int128)Hkv * (unsigned __int128)w->Sk_pad * row;
+  w->part_slots = uniform ? h3::split_part_slots(B, Sq, Sk, Hq, D) : 0;
+  const unsigned __int128 pb = (unsigned __int128)w->part_slots * (sizeof(float) * h3::attn_part_floats(D));
   const unsigned __int128 tot = qb + 2 * kb + pb;
   if (tot > (unsigned __int128)(INT64_MAX / 4)) return false;
   w->q_off = 0;
@@ -99,11 +101,11 @@ bool workspace_layout(int32_t B, int32_t Sq, int32_t Sk, int32_t Hq, int32_t Hkv
   return true;
 }
 
-// Element strides of a [B, S, H, 128] view: all three 0 means dense.
-void resolve_strides(const int64_t in[3], int32_t S, int32_t H, int64_t out[3]) {
+// Element strides of a [B, S, H, D] view: all three 0 means dense.
+void resolve_strides(const int64_t in[3], int32_t S, int32_t H, int32_t D, int64_t out[3]) {
   if (in[0] == 0 && in[1] == 0 && in[2] == 0) {
-    out[2] = h3::kHeadDim;
-    out[1] = (int64_t)H * h3::kHeadDim;
+    out[2] = D;
+    out[1] = (int64_t)H * D;
     out[0] = (int64_t)S * out[1];
   } else {
     out[0] = in[0];
@@ -112,11 +114,11 @@ void resolve_strides(const int64_t in[3], int32_t S, int32_t H, int64_t out[3]) 
   }
 }
 
-// Byte range [lo, hi) a [B, S, H, 128] view with non-negative strides can
+// Byte range [lo, hi) a [B, S, H, D] view with non-negative strides can
 // touch, or false on overflow.
-bool view_range(const void* p, const int64_t st[3], int32_t B, int32_t S, int32_t H, Range* r) {
+bool view_range(const void* p, const int64_t st[3], int32_t B, int32_t S, int32_t H, int32_t D, Range* r) {
   const unsigned __int128 last = (unsigned __int128)(B - 1) * (uint64_t)st[0] + (unsigned __int128)(S - 1) * (uint64_t)st[1] +
-                                 (unsigned __int128)(H - 1) * (uint64_t)st[2] + h3::kHeadDim;
+                                 (unsigned __int128)(H - 1) * (uint64_t)st[2] + (unsigned)D;
   const unsigned __int128 bytes = last * 2u;
   if (bytes > (unsigned __int128)(INT64_MAX / 4)) return false;
   *r = range_of(p, (size_t)bytes);
@@ -129,7 +131,7 @@ H3_API const char* h3attn_status_string(int status) {
   switch (status) {
     case H3ATTN_OK: return "ok";
     case H3ATTN_ERR_NULL_POINTER: return "a required pointer is NULL (or only one of a pair was given)";
-    case H3ATTN_ERR_BAD_SHAPE: return "a size is out of range (head_dim must be 128; S, H, B >= 1; valid lengths; rotary table rows)";
+    case H3ATTN_ERR_BAD_SHAPE: return "a size is out of range (head_dim 128, or 64/256 without norm and rotary; S, H, B >= 1; valid lengths; rotary table rows)";
     case H3ATTN_ERR_BAD_ALIGNMENT: return "a pointer is not 16-byte aligned (workspace: 256-byte)";
     case H3ATTN_ERR_ALIASING: return "an output overlaps an input or another output";
     case H3ATTN_ERR_BAD_VALUE: return "eps, theta or softmax_scale is not finite or out of range";
@@ -182,7 +184,7 @@ H3_API int h3attn_qk_prologue(const uint16_t* q_in, const uint16_t* k_in, uint16
 
 H3_API size_t h3attn_forward_workspace_bytes(int32_t B, int32_t Sq, int32_t Sk, int32_t H) {
   WorkspaceLayout w;
-  if (!workspace_layout(B, Sq, Sk, H, H, true, &w)) return 0;
+  if (!workspace_layout(B, Sq, Sk, H, H, true, h3::kHeadDim, &w)) return 0;
   return w.total;
 }
 
@@ -200,11 +202,17 @@ int check_forward(const h3attn_forward_args* a, size_t workspace_bytes, const vo
   if (!a->q || !a->k || !a->v || !a->o) return H3ATTN_ERR_NULL_POINTER;
   if (stages == 0 || stages > (H3ATTN_STAGE_PREPARE | H3ATTN_STAGE_ATTEND)) return H3ATTN_ERR_BAD_VALUE;
   const int32_t B = a->B, Sq = a->Sq, Sk = a->Sk, Hq = a->Hq, Hkv = a->Hkv;
-  if (a->head_dim != h3::kHeadDim || B < 1 || Sq < 1 || Sk < 1 || Hq < 1 || Hkv < 1) return H3ATTN_ERR_BAD_SHAPE;
+  if ((a->head_dim != 64 && a->head_dim != 128 && a->head_dim != 256) || B < 1 || Sq < 1 || Sk < 1 || Hq < 1 ||
+      Hkv < 1)
+    return H3ATTN_ERR_BAD_SHAPE;
+  // The Q/K norm and the partial rotary embedding are H3's, defined on 128 channels.
+  if (a->head_dim != h3::kHeadDim && (a->q_norm_w || a->k_norm_w || a->rope_cos || a->rope_sin))
+    return H3ATTN_ERR_BAD_SHAPE;
   if (Hq % Hkv != 0) return H3ATTN_ERR_BAD_SHAPE;
   if ((int64_t)B * Hq > 65535 || Sq > (1 << 30) || Sk > (1 << 30)) return H3ATTN_ERR_BAD_SHAPE;
-  const size_t obytes = bshd_bytes(B, Sq, Hq);
-  if (obytes == 0 || bshd_bytes(B, Sk, Hkv) == 0) return H3ATTN_ERR_BAD_SHAPE;
+  const int32_t D = a->head_dim;
+  const size_t obytes = bshd_bytes(B, Sq, Hq, D);
+  if (obytes == 0 || bshd_bytes(B, Sk, Hkv, D) == 0) return H3ATTN_ERR_BAD_SHAPE;
   if (a->causal != 0 && a->causal != 1) return H3ATTN_ERR_BAD_VALUE;
   if (a->window_frame_rows < 0) return H3ATTN_ERR_BAD_VALUE;
   if (a->window_frame_rows == 0) {
@@ -224,21 +232,21 @@ int check_forward(const h3attn_forward_args* a, size_t workspace_bytes, const vo
     return st;
   for (int i = 0; i < 3; ++i)
     if (a->q_stride[i] < 0 || a->k_stride[i] < 0 || a->v_stride[i] < 0) return H3ATTN_ERR_BAD_SHAPE;
-  resolve_strides(a->q_stride, Sq, Hq, qs);
-  resolve_strides(a->k_stride, Sk, Hkv, ks);
-  resolve_strides(a->v_stride, Sk, Hkv, vs);
+  resolve_strides(a->q_stride, Sq, Hq, D, qs);
+  resolve_strides(a->k_stride, Sk, Hkv, D, ks);
+  resolve_strides(a->v_stride, Sk, Hkv, D, vs);
   for (int i = 0; i < 3; ++i)
     if ((qs[i] | ks[i] | vs[i]) & 7) return H3ATTN_ERR_BAD_ALIGNMENT;
   if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o)) return H3ATTN_ERR_BAD_ALIGNMENT;
   if (a->valid_lengths && (reinterpret_cast<uintptr_t>(a->valid_lengths) & 3u)) return H3ATTN_ERR_BAD_ALIGNMENT;
   if (a->gate && (reinterpret_cast<uintptr_t>(a->gate) & 1u)) return H3ATTN_ERR_BAD_ALIGNMENT;
-  if (!workspace_layout(B, Sq, Sk, Hq, Hkv, uniform_schedule(a), wl)) return H3ATTN_ERR_BAD_SHAPE;
+  if (!workspace_layout(B, Sq, Sk, Hq, Hkv, uniform_schedule(a), D, wl)) return H3ATTN_ERR_BAD_SHAPE;
   if ((int64_t)B * Hq * wl->Sq_pad >= (1ll << 31) || (int64_t)B * Hkv * wl->Sk_pad >= (1ll << 31))
     return H3ATTN_ERR_BAD_SHAPE;
   if ((int64_t)B * Sq * Hq >= (1ll << 31) || (int64_t)B * Sk * Hkv >= (1ll << 31)) return H3ATTN_ERR_BAD_SHAPE;
   Range rq, rk, rv;
-  if (!view_range(a->q, qs, B, Sq, Hq, &rq) || !view_range(a->k, ks, B, Sk, Hkv, &rk) ||
-      !view_range(a->v, vs, B, Sk, Hkv, &rv))
+  if (!view_range(a->q, qs, B, Sq, Hq, D, &rq) || !view_range(a->k, ks, B, Sk, Hkv, D, &rk) ||
+      !view_range(a->v, vs, B, Sk, Hkv, D, &rv))
     return H3ATTN_ERR_BAD_SHAPE;
   if (!workspace || workspace_bytes < wl->total) return H3ATTN_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return H3ATTN_ERR_BAD_ALIGNMENT;
@@ -286,22 +294,27 @@ int run_forward(const h3attn_forward_args* a, void* workspace, size_t workspace_
   // q is written pre-multiplied by softmax_scale*log2(e) (fp32, before its
   // one bf16 rounding), so the attention kernel's scores are in exp2 units.
   const float c = (float)((double)a->softmax_scale * 1.4426950408889634);
+  const int32_t D = a->head_dim;
   h3::ProTensor tq{a->q, qw, a->q_norm_w, qs[0], qs[1], qs[2],
-                   (int64_t)Hq * wl.Sq_pad * h3::kHeadDim, h3::kHeadDim, wl.Sq_pad * h3::kHeadDim,
+                   (int64_t)Hq * wl.Sq_pad * D, D, wl.Sq_pad * D,
                    q_valid, (int32_t)wl.Sq_pad, c, a->valid_lengths, 0, Hq};
   h3::ProTensor tk{a->k, kw, a->k_norm_w, ks[0], ks[1], ks[2],
-                   (int64_t)Hkv * wl.Sk_pad * h3::kHeadDim, h3::kHeadDim, wl.Sk_pad * h3::kHeadDim,
+                   (int64_t)Hkv * wl.Sk_pad * D, D, wl.Sk_pad * D,
                    kv_valid, (int32_t)wl.Sk_pad, 1.0f, a->valid_lengths, 1, Hkv};
   if (stages & H3ATTN_STAGE_PREPARE) {
-    hipError_t e = h3::launch_qk_prologue(tq, tk, B, a->eps, a->rope_cos, a->rope_sin, s);
+    // Head dim 128 runs H3's norm + rotary prologue (each part optional);
+    // other head dims have neither and only copy (q scaled) into the layout.
+    hipError_t e = D == h3::kHeadDim ? h3::launch_qk_prologue(tq, tk, B, a->eps, a->rope_cos, a->rope_sin, s)
+                                     : h3::launch_qk_copy(tq, tk, B, D, s);
     if (e != hipSuccess) return H3ATTN_ERR_HIP;
     e = h3::launch_v_relayout(a->v, vs[0], vs[1], vs[2], vt, B, Sk, Hkv, kv_valid, a->valid_lengths,
-                              (int32_t)wl.Sk_pad, s);
+                              (int32_t)wl.Sk_pad, D, s);
     if (e != hipSuccess) return H3ATTN_ERR_HIP;
   }
   if (!(stages & H3ATTN_STAGE_ATTEND)) return H3ATTN_OK;
 
   h3::AttnArgs at{};
+  at.D = D;
   at.qw = qw;
   at.kw = kw;
   at.vt = vt;
@@ -393,7 +406,9 @@ H3_API int h3attn_forward_stages(const uint16_t* q, const uint16_t* k, const uin
 H3_API size_t h3attn_forward_ex_workspace_bytes(const h3attn_forward_args* args) {
   if (!args || args->Hkv < 1 || args->Hq < 1 || args->Hq % args->Hkv != 0) return 0;
   WorkspaceLayout w;
-  if (!workspace_layout(args->B, args->Sq, args->Sk, args->Hq, args->Hkv, uniform_schedule(args), &w)) return 0;
+  if (!workspace_layout(args->B, args->Sq, args->Sk, args->Hq, args->Hkv, uniform_schedule(args), args->head_dim,
+                        &w))
+    return 0;
   return w.total;
 }
 

@@ -65,49 +65,56 @@ hipError_t launch_qk_prologue(const ProTensor& t0, const ProTensor& t1, int32_t 
                               float eps, const float* rope_cos, const float* rope_sin,
                               hipStream_t stream);
 
-// Writes the transposed, key-blocked copy of v ([B, Sk, H, 128] with element
+// Writes the transposed, key-blocked copy of v ([B, Sk, H, D] with element
 // strides sb, ss, sh) that the attention kernel reads (layout in
 // attn_fwd.hip); keys at or past the valid length (kv_valid, or the item's
 // entry of `lengths` when given) are written as zeros and never read.
 hipError_t launch_v_relayout(const uint16_t* v, int64_t sb, int64_t ss, int64_t sh, uint16_t* vt,
                              int32_t B, int32_t Sk, int32_t H, int32_t kv_valid,
-                             const int32_t* lengths, int32_t Sk_pad, hipStream_t stream);
+                             const int32_t* lengths, int32_t Sk_pad, int32_t D, hipStream_t stream);
+
+// The prepare stage for head dims other than 128 (no norm, no rotary): copies
+// t0 and t1 ([B, S, H, D] views) into the head-major workspace, multiplying
+// by out_scale in fp32 before the bf16 rounding and zero-filling rows at or
+// past the valid length. The ProTensor strides are in elements.
+hipError_t launch_qk_copy(const ProTensor& t0, const ProTensor& t1, int32_t B, int32_t D,
+                          hipStream_t stream);
 
 hipError_t launch_rope_tables(float* cos_out, float* sin_out, int32_t rows, double theta,
                               hipStream_t stream);
 
-// Attention tiling: a workgroup of kAttnWaves waves (32 query rows each) owns
-// kAttnRows query rows of one (b, h) and walks the keys in kAttnSub-key
-// sub-tiles.
-constexpr int kAttnWaves = 8;
-constexpr int kAttnRows = kAttnWaves * 32;
+// Attention tiling by head dim D (64, 128 or 256): a workgroup of
+// attn_threads(D) / 64 waves (32 query rows each) owns attn_rows(D) query
+// rows of one (b, h) and walks the keys in kAttnSub-key sub-tiles.
 constexpr int kAttnSub = 32;
+constexpr int attn_threads(int D) { return D <= 128 ? 512 : 256; }
+constexpr int attn_rows(int D) { return attn_threads(D) / 2; }
 
 // Load balancing of the last, partial round of query tiles (stream-K): those
 // tiles' sub-tile steps are split evenly over up to kSplitMaxBlocks
 // workgroups, each taking at least kSplitMinSteps steps and touching at most
 // two tiles; each writes one partial record per tile it touches and a second
-// kernel merges them. A record holds the un-normalised fp32 accumulator (64
+// kernel merges them. A record holds the un-normalised fp32 accumulator (D/2
 // values per lane) plus the lane's running max and partial row sum.
 constexpr int kSplitMaxBlocks = 256;
 constexpr int kSplitMinSteps = 16;
-constexpr int kPartFloats = (64 + 2) * kAttnWaves * 64;
-constexpr size_t kPartBytes = sizeof(float) * kPartFloats;
+constexpr int attn_part_floats(int D) { return (D / 2 + 2) * attn_threads(D); }
 
 // Partial records the forward workspace reserves for these sizes: two per
 // split workgroup, for the largest split the launcher can choose.
-inline int64_t split_part_slots(int32_t B, int32_t Sq, int32_t Sk, int32_t H) {
-  const int64_t tiles = (int64_t)B * H * ((Sq + kAttnRows - 1) / kAttnRows);
+inline int64_t split_part_slots(int32_t B, int32_t Sq, int32_t Sk, int32_t H, int32_t D) {
+  const int64_t tiles = (int64_t)B * H * ((Sq + attn_rows(D) - 1) / attn_rows(D));
   const int64_t steps = tiles * ((Sk + kAttnSub - 1) / kAttnSub);
   const int64_t blocks = steps / kSplitMinSteps < kSplitMaxBlocks ? steps / kSplitMinSteps : kSplitMaxBlocks;
   return 2 * blocks;
 }
 
 struct AttnArgs {
-  const uint16_t* qw;      // [B*H][Sq_pad][128] scaled by softmax_scale*log2(e), rows >= q_valid zero
-  const uint16_t* kw;      // [B*Hkv][Sk_pad][128], rows >= kv_valid are zero
-  const uint16_t* vt;      // [B*Hkv][Sk_pad/32][128][32], see attn_fwd.hip; keys >= kv_valid zero
-  uint16_t* o;             // [B][Sq][H][128]
+  int32_t D;               // head dim: 64, 128 or 256
+  const uint16_t* qw;      // [B*H][Sq_pad][D] scaled by softmax_scale*log2(e), rows >= q_valid zero
+  const uint16_t* kw;      // [B*Hkv][Sk_pad][D], rows >= kv_valid are zero
+  const uint16_t* vt;      // [B*Hkv][Sk_pad/32][D][32], see attn_fwd.hip; keys >= kv_valid zero
+  uint16_t* o;             // [B][Sq][H][D]
   float* part;             // partial records for split tiles
   int64_t part_slots;      // records available at part
   int32_t B, H, Sq, Sk, Sq_pad, Sk_pad, q_valid, kv_valid;

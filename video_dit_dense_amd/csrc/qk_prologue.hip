@@ -176,6 +176,44 @@ __global__ __launch_bounds__(256) void rope_tables_kernel(float* cos_out, float*
   sin_out[i] = (float)s;
 }
 
+// The prepare stage for head dims other than 128, which have neither H3's
+// norm nor its rotary embedding: each thread moves one 16-byte chunk (8
+// channels) of one (b, s, h) row of t into the head-major workspace,
+// multiplied by t.out_scale in fp32 before the bf16 rounding; rows at or
+// past the valid length are written as zeros. Rows are numbered
+// r = (b * S_out + s) * H + h (below 2^31, host-checked).
+template <int D>
+__global__ __launch_bounds__(256) void qk_copy_kernel(ProTensor t, int32_t B) {
+  constexpr int CPR = D / 8;   // chunks per row
+  const int64_t n = (int64_t)B * t.S_out * t.H * CPR;
+  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (u >= n) return;
+  const int c = (int)(u % CPR);
+  const int r = (int)(u / CPR);
+  const int h = r % t.H;
+  const int bs = r / t.H;
+  const int s = bs % t.S_out;
+  const int b = bs / t.S_out;
+  v4u_t x = v4u_t{0u, 0u, 0u, 0u};
+  if (s < item_valid(t.lengths, b, t.which, t.S_valid, t.S_valid)) {
+    x = __builtin_nontemporal_load(
+        reinterpret_cast<const v4u_t*>(t.in + b * t.in_sb + s * t.in_ss + h * t.in_sh + c * 8));
+    if (t.out_scale != 1.0f) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = pack_bf16x2(bf16_lo(x[i]) * t.out_scale, bf16_hi(x[i]) * t.out_scale);
+    }
+  }
+  *reinterpret_cast<v4u_t*>(t.out + b * t.out_sb + s * t.out_ss + h * t.out_sh + c * 8) = x;
+}
+
+template <int D>
+hipError_t launch_copy_d(const ProTensor& t, int32_t B, hipStream_t stream) {
+  const int64_t n = (int64_t)B * t.S_out * t.H * (D / 8);
+  if ((int64_t)B * t.S_out * t.H >= (1ll << 31)) return hipErrorInvalidValue;
+  if (n > 0) qk_copy_kernel<D><<<dim3((unsigned)((n + 255) / 256)), 256, 0, stream>>>(t, B);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_qk_prologue(const ProTensor& t0, const ProTensor& t1, int32_t B,
@@ -209,6 +247,20 @@ hipError_t launch_qk_prologue(const ProTensor& t0, const ProTensor& t1, int32_t 
   else
     qk_prologue_kernel<false, false><<<grid, kProThreads, 0, stream>>>(a);
   return hipGetLastError();
+}
+
+hipError_t launch_qk_copy(const ProTensor& t0, const ProTensor& t1, int32_t B, int32_t D,
+                          hipStream_t stream) {
+  for (const ProTensor* t : {&t0, &t1}) {
+    hipError_t e;
+    switch (D) {
+      case 64: e = launch_copy_d<64>(*t, B, stream); break;
+      case 256: e = launch_copy_d<256>(*t, B, stream); break;
+      default: return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_rope_tables(float* cos_out, float* sin_out, int32_t rows, double theta,

@@ -15,7 +15,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libh3attn.so")
 
-HEAD_DIM = 128
+HEAD_DIM = 128                 # H3's head dim: the Q/K norm and rotary prologue apply to it only
+HEAD_DIMS = (64, 128, 256)     # head dims the attention kernels take
 ROPE_PAIRS = 48
 
 STATUS = {
@@ -105,18 +106,18 @@ def _stream(device: torch.device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _check_bshd(name: str, t: torch.Tensor, view: bool = False) -> None:
-    """A bf16 [B, S, H, 128] GPU tensor; contiguous, or with `view` any
-    strided view whose channels are contiguous (e.g. a slice of a fused QKV
-    projection)."""
+def _check_bshd(name: str, t: torch.Tensor, view: bool = False, dims=(HEAD_DIM,)) -> None:
+    """A bf16 [B, S, H, D] GPU tensor with D in `dims`; contiguous, or with
+    `view` any strided view whose channels are contiguous (e.g. a slice of a
+    fused QKV projection)."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
     if t.dtype != torch.bfloat16:
         raise ValueError(f"{name} must be bfloat16 (got {t.dtype}); the library is bf16-only")
-    if t.dim() != 4 or t.shape[-1] != HEAD_DIM:
-        raise ValueError(f"{name} must be [B, S, H, {HEAD_DIM}] (got {tuple(t.shape)})")
+    if t.dim() != 4 or t.shape[-1] not in dims:
+        raise ValueError(f"{name} must be [B, S, H, D] with D in {dims} (got {tuple(t.shape)})")
     if view:
         if t.stride(-1) != 1 or min(t.stride()) < 0:
             raise ValueError(f"{name} must have contiguous channels and non-negative strides")
@@ -209,15 +210,17 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     through h3attn_forward_ex."""
     lib = load_library()
     for name, t in (("q", q), ("k", k), ("v", v)):
-        _check_bshd(name, t, view=True)
+        _check_bshd(name, t, view=True, dims=HEAD_DIMS)
+    if q.shape[-1] != HEAD_DIM and any(x is not None for x in (w_q, w_k, rope_cos, rope_sin)):
+        raise ValueError(f"the Q/K norm and rotary prologue are defined for head_dim {HEAD_DIM} only")
     _check_f32("w_q", w_q, HEAD_DIM)
     _check_f32("w_k", w_k, HEAD_DIM)
     _check_f32("rope_cos", rope_cos)
     _check_f32("rope_sin", rope_sin)
     B, Sq, H, D = q.shape
     Sk, Hkv = k.shape[1], k.shape[2]
-    if k.shape != v.shape or k.shape[0] != B or H % Hkv != 0:
-        raise ValueError("k and v must be [B, Sk, Hkv, 128] with q's B and Hkv dividing q's heads")
+    if k.shape != v.shape or k.shape[0] != B or H % Hkv != 0 or k.shape[3] != D:
+        raise ValueError("k and v must be [B, Sk, Hkv, D] with q's B and D, and Hkv dividing q's heads")
     if valid_lengths is not None:
         if (valid_lengths.device.type != "cuda" or valid_lengths.dtype != torch.int32
                 or tuple(valid_lengths.shape) != (B, 2) or not valid_lengths.is_contiguous()):
@@ -229,13 +232,13 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if window is not None and len(window) != 4:
         raise ValueError("window is (frame_rows, chunk_frames, radius, anchor_frames)")
     o = torch.empty(B, Sq, H, D, dtype=q.dtype, device=q.device) if out is None else out
-    _check_bshd("out", o)
+    _check_bshd("out", o, dims=(D,))
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     rows = 0 if rope_cos is None else rope_cos.shape[0]
     if stages != (STAGE_PREPARE | STAGE_ATTEND) and workspace is None:
         raise ValueError("a single stage needs a caller-kept workspace")
-    plain = (Hkv == H and not causal and valid_lengths is None and window is None and gate is None
-             and q.is_contiguous() and k.is_contiguous() and v.is_contiguous())
+    plain = (D == HEAD_DIM and Hkv == H and not causal and valid_lengths is None and window is None
+             and gate is None and q.is_contiguous() and k.is_contiguous() and v.is_contiguous())
     if plain:
         ws = make_workspace(B, Sq, Sk, H, q.device) if workspace is None else workspace
         st = lib.h3attn_forward_stages(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, Sq, Sk, H, D,
@@ -278,10 +281,11 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
 
 
 def forward_ex_workspace_bytes(B: int, Sq: int, Sk: int, Hq: int, Hkv: int, causal: bool = False,
-                               per_item_lengths: bool = False, window: bool = False) -> int:
+                               per_item_lengths: bool = False, window: bool = False,
+                               head_dim: int = HEAD_DIM) -> int:
     """Workspace bytes h3attn_forward_ex needs for these sizes and variant."""
     a = ForwardArgs()
-    a.B, a.Sq, a.Sk, a.Hq, a.Hkv, a.head_dim = B, Sq, Sk, Hq, Hkv, HEAD_DIM
+    a.B, a.Sq, a.Sk, a.Hq, a.Hkv, a.head_dim = B, Sq, Sk, Hq, Hkv, head_dim
     a.causal = 1 if causal else 0
     a.window_frame_rows = 1 if window else 0
     a.valid_lengths = 16 if per_item_lengths else None   # only NULL or not matters here

@@ -46,6 +46,7 @@ class Workload:
     lengths: tuple = ()   # per-item (q_valid, kv_valid) pairs, replacing q_valid / kv_valid
     window: tuple = ()    # (frame_rows, chunk_frames, radius, anchor_frames) of a frame window
     gate: bool = False    # a softmax gate per (row, head)
+    head_dim: int = HEAD_DIM   # 64 and 256 run without the Q/K norm and rotary prologue
 
     @property
     def kv_heads(self) -> int:
@@ -53,11 +54,11 @@ class Workload:
 
     @property
     def D(self) -> int:
-        return HEAD_DIM
+        return self.head_dim
 
     @property
     def scale(self) -> float:
-        return 1.0 / float(np.sqrt(HEAD_DIM))
+        return 1.0 / float(np.sqrt(self.head_dim))
 
     def item_lengths(self) -> list:
         """(q_valid, kv_valid) of every batch item."""
@@ -76,10 +77,10 @@ class Workload:
                 pairs += m * (m + 1) // 2 + (qv - m) * kvv
             else:
                 pairs += qv * kvv
-        return 4.0 * pairs * HEAD_DIM * self.H
+        return 4.0 * pairs * self.head_dim * self.H
 
     def nominal_flops(self) -> float:
-        return 4.0 * self.Sq * self.Sk * HEAD_DIM * self.H * self.B
+        return 4.0 * self.Sq * self.Sk * self.head_dim * self.H * self.B
 
     def prologue_bytes(self) -> int:
         """Compulsory HBM bytes of the stand-alone Q/K prologue: read and write
@@ -122,6 +123,15 @@ VARIANT_WORKLOADS = {
                             description="full shape, frame window: 34 frames of 3072 rows, chunks of 5 "
                                         "frames, radius 1, 1 anchor frame, softmax gate",
                             window=(3072, 5, 1, 1), gate=True),
+    # The other head dims of the FastVideo PR #1799 backend ("Implementation":
+    # head dims 64, 128 and 256), at the full sequence with the head count
+    # that keeps the width of one GPU's share (6 x 128 = 768 channels). The
+    # Q/K norm and rotary prologue are H3's, on 128 channels, so these run
+    # without them.
+    "full_d64": Workload("full_d64", 1, 104448, 104448, 12, 104448, 104448, False, False, 6,
+                         description="full sequence at head dim 64, 12 heads, no prologue", head_dim=64),
+    "full_d256": Workload("full_d256", 1, 104448, 104448, 3, 104448, 104448, False, False, 7,
+                          description="full sequence at head dim 256, 3 heads, no prologue", head_dim=256),
     "batch_varlen": Workload("batch_varlen", 4, 32768, 32768, 8, 32768, 32768, True, True, 5,
                              description="B=4 padded to 32768 rows, items valid for 32768, 24576, "
                                          "16384 and 8192 query rows and keys, H=8",
@@ -161,25 +171,26 @@ def _normal_bf16(rng: np.random.Generator, shape) -> np.ndarray:
 
 
 def make_inputs(B: int, Sq: int, Sk: int, H: int, seed: int,
-                weight_sigma: float = 0.1, Hkv: int | None = None) -> Inputs:
-    """Draw q [B, Sq, H], k and v [B, Sk, Hkv] (Hkv defaults to H) ~ N(0,1)
-    (float32, then RNE to bf16) and RMSNorm weights 1 + weight_sigma*N(0,1)
-    (float64, rounded to bf16-representable values and stored as float32),
-    in that order, from numpy's PCG64 with `seed`."""
+                weight_sigma: float = 0.1, Hkv: int | None = None, D: int = HEAD_DIM) -> Inputs:
+    """Draw q [B, Sq, H, D], k and v [B, Sk, Hkv, D] (Hkv defaults to H) ~
+    N(0,1) (float32, then RNE to bf16) and RMSNorm weights [D] 1 +
+    weight_sigma*N(0,1) (float64, rounded to bf16-representable values and
+    stored as float32), in that order, from numpy's PCG64 with `seed`."""
     rng = np.random.default_rng(seed)
     Hkv = H if Hkv is None else Hkv
-    q = _normal_bf16(rng, (B, Sq, H, HEAD_DIM))
-    k = _normal_bf16(rng, (B, Sk, Hkv, HEAD_DIM))
-    v = _normal_bf16(rng, (B, Sk, Hkv, HEAD_DIM))
+    q = _normal_bf16(rng, (B, Sq, H, D))
+    k = _normal_bf16(rng, (B, Sk, Hkv, D))
+    v = _normal_bf16(rng, (B, Sk, Hkv, D))
     w = []
     for _ in range(2):
-        w64 = 1.0 + weight_sigma * rng.standard_normal(HEAD_DIM)
+        w64 = 1.0 + weight_sigma * rng.standard_normal(D)
         w.append(bf16_bits_to_f32(f32_to_bf16_bits(w64.astype(np.float32))))
     return Inputs(q, k, v, w[0], w[1])
 
 
 def make_workload_inputs(wl: Workload, seed: int | None = None) -> Inputs:
-    return make_inputs(wl.B, wl.Sq, wl.Sk, wl.H, wl.seed if seed is None else seed, Hkv=wl.kv_heads)
+    return make_inputs(wl.B, wl.Sq, wl.Sk, wl.H, wl.seed if seed is None else seed, Hkv=wl.kv_heads,
+                       D=wl.head_dim)
 
 
 def sample_rows(S: int, valid: int, count: int, seed: int, tile: int = 256) -> np.ndarray:

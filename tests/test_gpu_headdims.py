@@ -116,3 +116,21 @@ def test_head_dim_rejections(h3):
         h3.forward(d.q, d.k, d.v, d.w_q, d.w_k)
     with pytest.raises(ValueError, match="D in"):
         h3.forward(d.q[..., :32].contiguous(), d.k[..., :32].contiguous(), d.v[..., :32].contiguous())
+
+
+@pytest.mark.parametrize("D", [64, 256])
+@pytest.mark.parametrize("B,Sq,Sk,H,kw", [
+    (1, 1, 1, 1, {}),
+    (2, 5, 3, 3, {"kv_valid": 1}),
+    (1, 300, 40, 2, {"q_valid": 0}),
+    (3, 257, 257, 1, {"causal": True, "kv_valid": 200}),
+])
+def test_head_dim_degenerate(h3, D, B, Sq, Sk, H, kw):
+    say("head dim degenerate", D, B, Sq, Sk, H, kw)
+    inp = workloads.make_inputs(B, Sq, Sk, H, seed=7 + Sq, D=D)
+    got = gpu(h3, inp, D, **kw)
+    want = ref(inp, D, **kw)
+    if kw.get("q_valid") == 0:
+        assert np.all(got == 0)
+        return
+    check(oracle.compare(got, want), f"D={D} degenerate {B}x{Sq}x{Sk}x{H} {kw}")

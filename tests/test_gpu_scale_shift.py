@@ -162,3 +162,10 @@ def test_special_rows(h3):
         say("scale_shift special rows, eps", eps)
         with np.errstate(divide="ignore", invalid="ignore"):
             check(run(h3, spec, eps), spec, eps, f"special eps={eps}")
+
+
+def test_single_row_and_single_modulation_row(h3):
+    wl = workloads.ScaleShiftWorkload("one", 1, 1, 6144, 1, 63, weight=True, index="none")
+    say("scale_shift one row")
+    inp = workloads.make_scale_shift_inputs(wl)
+    check(run(h3, inp, 1e-6), inp, 1e-6, "one row")

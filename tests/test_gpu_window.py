@@ -139,3 +139,29 @@ def test_full_window_sampled_rows(h3):
     rows = np.unique(np.concatenate([workloads.sample_rows(wl.Sq, wl.Sq, 96, wl.seed), edges]))
     want = ref(inp, wl.window, g, rows=rows)
     check(oracle.compare(got[:, rows], want), "full window sampled")
+
+
+def test_window_cross_lengths(h3):
+    """Queries and keys of different lengths share one frame grid."""
+    say("window, Sq != Sk")
+    inp = workloads.make_inputs(1, 1000, 700, 2, seed=85)
+    window = (64, 2, 1, 1)
+    d = DevInputs(inp)
+    o = h3.forward(d.q, d.k, d.v, d.w_q, d.w_k, 1e-6, None, None, scale=SCALE, window=window)
+    torch.cuda.synchronize()
+    want = oracle.forward(inp.q, inp.k, inp.v, inp.w_q, inp.w_k, 1e-6, None, SCALE, window=window)
+    check(oracle.compare(to_host(o), want), "window Sq=1000 Sk=700")
+
+
+def test_gate_saturation(h3):
+    """Gates of +-1000: sigmoid 1 leaves the output bit for bit, sigmoid 0
+    zeroes it."""
+    say("gate saturation")
+    S, H = 512, 2
+    inp = workloads.make_inputs(1, S, S, H, seed=86)
+    window = (128, 2, 1, 1)
+    base = run(h3, inp, window)
+    up = np.full((1, S, H), 0x447A, dtype=np.uint16)     # bf16 1000.0
+    down = np.full((1, S, H), 0xC47A, dtype=np.uint16)   # bf16 -1000.0
+    assert np.array_equal(run(h3, inp, window, up), base)
+    assert np.all(oracle.bf16_bits_to_f64(run(h3, inp, window, down)) == 0.0)

@@ -1,14 +1,20 @@
-// Dense non-causal attention forward at head_dim 128 for gfx950 (MI355X).
+// Attention forward for gfx950 (MI355X): the dense step and its variants.
 //
 // Computes, per (b, h) and query row i < q_valid,
-//   o_i = sum_{j < kv_valid} softmax_j(scale * q_i . k_j) v_j
+//   o_i = sum_{j visible to i} softmax_j(scale * q_i . k_j) v_j
 // flash-style: key/value blocks stream through LDS, scores never reach HBM,
 // and a running max / running sum per query row rescales the accumulator
 // (online softmax). QK^T and PV are bf16 matrix-core contractions
 // (v_mfma_f32_32x32x16_bf16) accumulated in fp32; the softmax is fp32.
-// The step is the dense attention of FastVideo PR #1832 ("Summary": BSHD,
-// head_dim 128, dense non-causal) with the valid-front / zero-tail layout of
-// TeleFuser PR #37 (sections 2.3 and 2.4).
+// The main step is the dense attention of FastVideo PR #1832 ("Summary":
+// BSHD, head_dim 128, dense non-causal) with the valid-front / zero-tail
+// layout of TeleFuser PR #37 (sections 2.3 and 2.4): key j is visible to
+// row i iff j < kv_valid. The variants narrow that set: the causal mask
+// (j <= i), per-item valid lengths and grouped key/value heads (FastVideo PR
+// #1799, "Implementation"), and a frame window with anchor frames (SGLang PR
+// #37903, "Modifications", hybrid_window_attn_h3), whose optional softmax
+// gate multiplies each output row by sigmoid(g). Head dims 64, 128 and 256
+// share the code through the Geo<D> tiling constants.
 //
 // Orientation. Each wave owns 32 query rows and computes S^T = K Q^T, so the
 // matrix-core result puts one query per lane column: lane l holds 16 of the
@@ -23,9 +29,10 @@
 //   B (16 x 32): lane l supplies column l%32, k = 8*(l/32) .. +7
 //   D (32 x 32): lane l register r holds row 8*(r/4) + 4*(l/32) + r%4, col l%32
 //
-// Schedule. A workgroup is eight waves (256 query rows), one workgroup per
-// CU, so every SIMD runs two waves and each K/V byte brought into LDS serves
-// 256 queries. Keys are processed in 32-key sub-tiles u, and step u is split
+// Schedule (head dims 64 and 128; 256 runs four waves, one per SIMD, with
+// a four-slot ring). A workgroup is eight waves (256 query rows), one
+// workgroup per CU, so every SIMD runs two waves and each K/V byte brought
+// into LDS serves 256 queries. Keys are processed in 32-key sub-tiles u, and step u is split
 // by workgroup barriers into two phases:
 //   X: matrix-core work only: QK^T of sub-tile u+1 and PV of sub-tile u,
 //      all operands already in registers;
@@ -43,22 +50,24 @@
 // vector instruction and LDS byte per step costs clock: the step keeps them
 // few.
 //
-// Chip schedule. A workgroup owns one (b, h, 256-row query block) tile and
-// one CU, so tiles run in rounds of one per CU. When the last round is only
-// partly full, its tiles are not run whole: their 32-key steps are divided
-// evenly over up to one workgroup per CU, each workgroup writes an fp32
-// partial result (un-normalised accumulator, running max, row sum) per tile
-// it touches, and attn_merge_kernel combines them. Tiles wholly past q_valid
-// only write zeros.
+// Chip schedule. A workgroup owns one (b, h, query block) tile and one CU,
+// so tiles run in rounds of one per CU. In the uniform mode (no causal mask,
+// per-item lengths or window), when the last round is only partly full, its
+// tiles are not run whole: their 32-key steps are divided evenly over up to
+// one workgroup per CU, each workgroup writes an fp32 partial result
+// (un-normalised accumulator, running max, row sum) per tile it touches, and
+// attn_merge_kernel combines them. Tiles wholly past q_valid only write
+// zeros. The general mode (the other variants) runs one workgroup per tile,
+// each finding its own key ranges.
 //
 // Exponent arithmetic. q arrives pre-multiplied by softmax_scale*log2(e)
 // (applied in fp32 by the prologue before its single bf16 rounding), so
 // scores leave the matrix core in exp2 units and p = exp2(s - m).
 //
 // Workspace layouts read here (written by the prologue and the relayout):
-//   qw [B*H][Sq_pad][128]          rows >= q_valid zero
-//   kw [B*H][Sk_pad][128]          rows >= kv_valid zero
-//   vt [B*H][Sk_pad/32][128][32]   vt[.., x, d, p] = v[key 32x + sigma(p)][d], zero past kv_valid
+//   qw [B*H][Sq_pad][D]            rows >= q_valid zero
+//   kw [B*Hkv][Sk_pad][D]          rows >= kv_valid zero
+//   vt [B*Hkv][Sk_pad/32][D][32]   vt[.., x, d, p] = v[key 32x + sigma(p)][d], zero past kv_valid
 #include "h3attn_internal.h"
 
 #include <algorithm>

@@ -42,11 +42,12 @@ __device__ inline int32_t item_valid(const int32_t* lengths, int b, int which, i
 }
 
 // One tensor handled by the prologue kernel. Strides are in elements and
-// describe a [B, S, H, 128] view (channel stride 1).
+// describe a [B, S, H, D] view (channel stride 1); the norm and rotary
+// prologue takes D = 128, the copy of the other head dims 64 and 256.
 struct ProTensor {
   const uint16_t* in;
   uint16_t* out;
-  const float* w;          // RMSNorm weight [128] or nullptr (no norm)
+  const float* w;          // RMSNorm weight [128] or nullptr (no norm; always for the copy)
   int64_t in_sb, in_ss, in_sh;
   int64_t out_sb, out_ss, out_sh;
   int32_t S_valid;         // rows s < S_valid are read and transformed

@@ -194,7 +194,8 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             gate: torch.Tensor | None = None) -> torch.Tensor:
     """The attention step: prologue on q/k (if weights/tables given), then
     softmax attention with key padding (kv_valid) and a zeroed query tail
-    (q_valid). Returns o [B, Sq, Hq, 128] bf16.
+    (q_valid). Returns o [B, Sq, Hq, D] bf16. D is 128 (H3), 64 or 256; the
+    norm and rotary prologue apply to 128 only.
 
     k and v may have fewer heads than q (grouped heads: query head h reads
     kv head h // (Hq // Hkv)); q, k and v may be strided views with

@@ -154,6 +154,18 @@ def test_python_wrapper_rejections():
         h3attn._check_bshd("q", q.numpy())
 
 
+def test_python_wrapper_variant_rejections():
+    """Argument checks of the binding's variants, before any device call."""
+    q = torch.zeros(1, 8, 2, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        h3attn.forward(q, q, q, window=(4, 2, 1, 1))
+    x = torch.zeros(1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        h3attn.rmsnorm_scale_shift(x, x[:, :1], x[:, :1])
+    with pytest.raises(ValueError, match="bfloat16"):
+        h3attn.rmsnorm_scale_shift(x.float(), x[:, :1], x[:, :1])
+
+
 def fwd_ex(lib, stages=3, ws=16 * A, wsb=None, **kw):
     """h3attn_forward_ex with a valid descriptor of fake pointers, then the
     fields in kw overridden; the call fails validation or the device gate."""

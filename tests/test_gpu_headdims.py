@@ -134,3 +134,42 @@ def test_head_dim_degenerate(h3, D, B, Sq, Sk, H, kw):
         assert np.all(got == 0)
         return
     check(oracle.compare(got, want), f"D={D} degenerate {B}x{Sq}x{Sk}x{H} {kw}")
+
+
+@pytest.mark.parametrize("Sk", [32, 64, 96, 128, 160, 200, 330])
+def test_head_dim_256_key_lengths(h3, Sk):
+    """Head dim 256 pipelines QK^T two sub-tiles ahead of PV: key lengths of
+    1 to 11 sub-tiles cover the prologue alone, the last step without a
+    QK^T, whole blocks of ring steps and ragged tails, in the uniform (split
+    last round) and per-item-length (one tile per block) schedules."""
+    say("head dim 256 key length", Sk)
+    inp = workloads.make_inputs(1, 300, Sk, 2, seed=300 + Sk, D=256)
+    check(oracle.compare(gpu(h3, inp, 256), ref(inp, 256)), f"D=256 Sk={Sk}")
+    got = gpu(h3, inp, 256, lengths=[[300, Sk]])
+    check(oracle.compare(got, ref(inp, 256)), f"D=256 Sk={Sk} per-item lengths")
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_rising_row_maxima(h3, D):
+    """Keys whose magnitude grows along the sequence, so each row's running
+    maximum rises by many units at several steps and the accumulator is
+    rescaled there. q has entries in {-1, 0, 1} and key j entries in
+    {-c, 0, c} with c = 1 + j // 256, and the scale is ln 2: q * scale *
+    log2(e) stays an exact small integer in bf16, so the scores (exp2 units)
+    are exact integers however large, and only v and the output are
+    rounded."""
+    say("rising row maxima", D)
+    Sq, Sk, H = 512, 2048, 2
+    rng = np.random.default_rng(330 + D)
+    qv = rng.integers(-1, 2, size=(1, Sq, H, D)).astype(np.float32)
+    c = (1 + np.arange(Sk) // 256).astype(np.float32)
+    kv = rng.integers(-1, 2, size=(1, Sk, H, D)).astype(np.float32) * c[None, :, None, None]
+    bits = lambda x: (x.view(np.uint32) >> 16).astype(np.uint16)   # exact: small integers
+    inp = workloads.make_inputs(1, Sq, Sk, H, seed=330 + D, D=D)
+    q, k = bits(qv), bits(kv)
+    scale = math.log(2.0)
+    d = DevInputs(workloads.Inputs(q, k, inp.v, inp.w_q, inp.w_k))
+    o = h3.forward(d.q, d.k, d.v, scale=scale)
+    torch.cuda.synchronize()
+    want = oracle.forward(q, k, inp.v, None, None, 1e-6, None, scale, norm=False)
+    check(oracle.compare(to_host(o), want), f"D={D} rising maxima")

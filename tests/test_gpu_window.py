@@ -102,6 +102,29 @@ def test_rows_without_keys_are_zero(h3):
     assert np.all(got[0, 384:] == 0)
 
 
+@pytest.mark.parametrize("D", [128, 256])
+def test_first_keys_far_below_zero(h3, D):
+    """Rows that see no key in their tile's first sub-tile (no anchors,
+    radius 0, tiles straddling chunks) take their offset from the first keys
+    they meet. Here every score is about -204 in exp2 units (q = 40 e_0,
+    k = -40 e_0 on raw inputs), so the rescale of such a row must not form
+    exp2(+204) (fp32 overflow); each row is the mean of v over its chunk."""
+    say("window first keys far below zero", D)
+    S, H = 1024, 2
+    window = (64, 1, 0, 0)
+    inp = workloads.make_inputs(1, S, S, H, seed=83, D=D)
+    big = np.uint16(0x4220)            # 40.0 in bf16
+    q = np.zeros_like(inp.q)
+    k = np.zeros_like(inp.k)
+    q[..., 0] = big
+    k[..., 0] = big | np.uint16(0x8000)
+    d = DevInputs(workloads.Inputs(q, k, inp.v, inp.w_q, inp.w_k))
+    o = h3.forward(d.q, d.k, d.v, scale=SCALE, window=window)
+    torch.cuda.synchronize()
+    want = oracle.forward(q, k, inp.v, None, None, 1e-6, None, SCALE, norm=False, window=window)
+    check(oracle.compare(to_host(o), want), f"D={D} first keys far below zero")
+
+
 def test_gate_in_uniform_schedule(h3):
     """The gate alone, on the dense schedule whose last round is split over
     workgroups and merged (4096 rows x 8 heads: 128 tiles)."""

@@ -139,7 +139,7 @@ struct Geo {
   static constexpr int NW = D <= 128 ? 8 : 4;           // waves per workgroup
   static constexpr int WPE = D <= 128 ? 2 : 1;          // waves per SIMD
   static constexpr int BM = NW * 32;                    // query rows per workgroup
-  static constexpr int kRing = D <= 128 ? 8 : 4;        // LDS ring depth (sub-tiles)
+  static constexpr int kRing = D <= 128 ? 8 : 4;        // ring depth (sub-tiles; per operand at 256)
   static constexpr int kKBytes = kSub * D * 2;          // K sub-tile: 32 rows x 2D bytes
   static constexpr int kVBytes = D * kSub * 2;          // V^T sub-tile: D rows x 64 B
   static constexpr int kBufBytes = kKBytes + kVBytes;   // one ring slot
@@ -150,8 +150,12 @@ struct Geo {
   static constexpr int LDPS = (kKBytes + kVBytes) / 1024 / NW;   // per wave per sub-tile
   static constexpr int kSlotsPerSeg = 65536 / kBufBytes;         // slots in a 16-bit LDS offset
   static constexpr int kRecM = NT * 16, kRecL = NT * 16 + 1;     // partial record layout
+  // LDS: the ring and one int per wave (its SIMD) for D <= 128; at 256 the
+  // two operand rings fill the 160 KB.
+  static constexpr int kLdsBytes = D <= 128 ? kRing * kBufBytes + NW * 4 : 2 * kRing * kKBytes;
   static_assert(LDPS * NW * 1024 == kKBytes + kVBytes, "tile split");
-  static_assert(kRing <= 2 * kSlotsPerSeg, "two address segments at most");
+  static_assert(D == 256 || kRing <= 2 * kSlotsPerSeg, "two address segments at most");
+  static_assert(kLdsBytes <= 160 * 1024, "LDS");
 };
 
 // LDS layouts (no padding; XOR swizzles keep every 8-lane group of a
@@ -234,8 +238,7 @@ void attn_fwd_kernel(AttnArgs a) {
   // One LDS object only: the ring, then the per-wave SIMD ids. (With a
   // second LDS variable the compiler can no longer tell fragment reads from
   // the ring's DMA writes and waits for every load in flight before each.)
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kRing * kBufBytes + NW * sizeof(int)];
-  int* simd_of = reinterpret_cast<int*>(lds + kRing * kBufBytes);
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[G::kLdsBytes];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -244,11 +247,13 @@ void attn_fwd_kernel(AttnArgs a) {
   const int g = lane >> 5;
 
   // Role of this wave among the waves that share its SIMD (HW_ID bits 5:4
-  // name the SIMD): the second one of each SIMD runs one phase behind.
-  if (lane == 0) simd_of[wave] = (int)(__builtin_amdgcn_s_getreg((1 << 11) | (4 << 6) | 4) & 3);
-  __syncthreads();
+  // name the SIMD): the second one of each SIMD runs one phase behind. (At
+  // head dim 256 every wave has its SIMD to itself.)
   int role = 0;
-  {
+  if constexpr (D <= 128) {
+    int* simd_of = reinterpret_cast<int*>(lds + kRing * kBufBytes);
+    if (lane == 0) simd_of[wave] = (int)(__builtin_amdgcn_s_getreg((1 << 11) | (4 << 6) | 4) & 3);
+    __syncthreads();
     const int mine = simd_of[wave];
 #pragma unroll
     for (int w = 0; w < NW; ++w) role += (w < wave && simd_of[w] == mine) ? 1 : 0;
@@ -444,48 +449,6 @@ void attn_fwd_kernel(AttnArgs a) {
     for (int kk = 0; kk < NF; ++kk) qf[kk] = *reinterpret_cast<const bf16x8_t*>(qp + kk * 16);
   }
 
-  // Per-lane byte offsets of the direct loads within a sub-tile (K and V^T
-  // sub-tiles are contiguous blocks of kKBytes in the workspace). Load i of
-  // this wave fills LDS bytes [1024 j, 1024 j + 1024) of the slot, j = wave
-  // + NW i: K's chunks for j < nK, V^T's after them. The lane that fills
-  // LDS chunk Q fetches the logical chunk the swizzle puts there.
-  const uint16_t* kw = a.kw + (int64_t)bh_kv * a.Sk_pad * D;
-  const uint16_t* vt = a.vt + (int64_t)bh_kv * a.Sk_pad * D;
-  int loff[LDPS];
-#pragma unroll
-  for (int i = 0; i < LDPS; ++i) {
-    const int j = wave + NW * i;
-    if (j < G::nK) {
-      const int Q = j * 64 + lane;
-      const int r = Q / (D / 8), p = Q % (D / 8);
-      loff[i] = (r * D + ((p ^ (r & G::kSwz)) * 8)) * 2;
-    } else {
-      const int Q = (j - G::nK) * 64 + lane;
-      const int d = Q >> 2, p = Q & 3;
-      loff[i] = (d * kSub + ((p ^ ((d >> 2) & 3)) * 8)) * 2;
-    }
-  }
-  // One buffer resource per sub-tile (base in SGPRs, 8 KB range), so the
-  // loads need no vector address arithmetic and offsets stay 32-bit at any
-  // sequence length. Every step issues exactly one refill so the wait counts
-  // are the same at every step; a refill past the last sub-tile gets an
-  // empty range (the hardware returns zeros without touching memory) and
-  // lands in a ring slot that no later step reads.
-  auto issue_loads = [&](int x) {
-    uint8_t* slot = lds + ((x - xb) & (kRing - 1)) * kBufBytes;
-    const bool live = x < xe;
-    const int xs = live ? xmap(x) : 0;
-    const uint16_t* kx = kw + (int64_t)xs * (kSub * D);
-    const uint16_t* vx = vt + (int64_t)xs * (kSub * D);
-#pragma unroll
-    for (int i = 0; i < LDPS; ++i) {
-      const int j = wave + NW * i;
-      load_lds16(j < G::nK ? kx : vx, live ? kKBytes : 0, loff[i], slot + j * 1024);
-    }
-  };
-#pragma unroll
-  for (int i = 0; i < kRing - 1; ++i) issue_loads(xb + i);
-
   f32x16_t acc[NT];
 #pragma unroll
   for (int dt = 0; dt < NT; ++dt)
@@ -494,7 +457,6 @@ void attn_fwd_kernel(AttnArgs a) {
   float m_run = 0.f;       // row offset (exp2 units), shared by the lane pair
   float l_run = 0.f;       // this lane's share of the row sum of bf16 probabilities
   bool seen = true;        // the row has met a visible key (m_run is its offset)
-  f32x16_t msplat;         // -m_run in every slot: the QK^T accumulator's initial value
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   // Row max of this lane's 16 scores of sub-tile x; with MASK, keys the
@@ -534,193 +496,517 @@ void attn_fwd_kernel(AttnArgs a) {
   };
   using NoMask = std::integral_constant<bool, false>;
   using Mask = std::integral_constant<bool, true>;
-  // The scores arrive as s - m_run. If some row of the wave exceeds its
-  // offset by more than 2^kRescaleLog2 (rare), raise that row's m_run by its
-  // excess, shift the scores and rescale the accumulator and partial sum.
-  // With MASK, a row that saw no key before (seen false, m_run 0) takes its
-  // first visible keys' maximum as its offset.
-  auto maybe_rescale = [&](f32x16_t& s, float mx, auto mask) {
-    bool trigger = mx > kRescaleLog2;
-    if constexpr (WIN && decltype(mask)::value) trigger = trigger || (!seen && mx != -INFINITY);
-    if (__builtin_amdgcn_ballot_w64(trigger) != 0) {
+  // sched_barrier(0) fences keep the compiler from moving instructions
+  // across them (phase boundaries, interleave groups).
+  auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+  if constexpr (D == 256) {
+    // Head dim 256 runs one wave per SIMD, so no second wave covers the
+    // softmax: each wave overlaps it with its own matrix-core work. Step u
+    // sends QK^T of sub-tile u+2 and PV of sub-tile u to the matrix core and
+    // computes, between those instructions, the softmax of sub-tile u+1,
+    // whose scores the previous step produced. K and V^T have rings of their
+    // own, kRing slots of one 16 KB sub-tile each, together the whole LDS:
+    // K(x) is read at step x-2 and V^T(x) at step x, and each slot is
+    // refilled the step after its last read, so a load has kRing-2 steps and
+    // more to land.
+    constexpr int kS = kKBytes;                 // one K or V^T sub-tile
+    constexpr int kV0 = kRing * kS;             // V^T ring base
+    constexpr int LPS = kS / 1024 / NW;         // 1 KB loads per wave per sub-tile and operand
+    constexpr int kWait = (2 * kRing - 4) * LPS;   // loads that may stay in flight at a step's end
+    int loffK[LPS], loffV[LPS];
+#pragma unroll
+    for (int i = 0; i < LPS; ++i) {
+      const int Q = (wave + NW * i) * 64 + lane;
+      const int r = Q / (D / 8), p = Q % (D / 8);
+      loffK[i] = (r * D + ((p ^ (r & G::kSwz)) * 8)) * 2;
+      const int d = Q >> 2, pv = Q & 3;
+      loffV[i] = (d * kSub + ((pv ^ ((d >> 2) & 3)) * 8)) * 2;
+    }
+    const uint16_t* kw = a.kw + (int64_t)bh_kv * a.Sk_pad * D;
+    const uint16_t* vt = a.vt + (int64_t)bh_kv * a.Sk_pad * D;
+    auto slot_of = [&](int x) { return (x - xb) % kRing; };
+    // Loads of sub-tile x into its ring slot; past the last sub-tile the
+    // range is empty (zeros, no memory access) and the slot is never read.
+    auto issue_k = [&](int x) __attribute__((always_inline)) {
+      const bool live = x < xe;
+      const uint16_t* src = kw + (int64_t)(live ? xmap(x) : 0) * (kSub * D);
+      uint8_t* dst = lds + slot_of(x) * kS;
+#pragma unroll
+      for (int i = 0; i < LPS; ++i) load_lds16(src, live ? kS : 0, loffK[i], dst + (wave + NW * i) * 1024);
+    };
+    auto issue_v = [&](int x) __attribute__((always_inline)) {
+      const bool live = x < xe;
+      const uint16_t* src = vt + (int64_t)(live ? xmap(x) : 0) * (kSub * D);
+      uint8_t* dst = lds + kV0 + slot_of(x) * kS;
+#pragma unroll
+      for (int i = 0; i < LPS; ++i) load_lds16(src, live ? kS : 0, loffV[i], dst + (wave + NW * i) * 1024);
+    };
+    // Fragment reads. K fragments kk and kk + 8 differ only in bit 4 of the
+    // chunk index, which the swizzle leaves alone (256 bytes apart).
+    // The V^T addresses hold the ring base (64 KB or more, past the offset
+    // field), hidden from the compiler so it stays out of the per-read offsets.
+    uint32_t ka[8], va[2];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) ka[k] = kbase ^ (32u * k);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      va[ks] = vaddr[ks] - kKBytes + kV0;
+      asm("" : "+v"(va[ks]));
+    }
+    auto kfrag = [&](int slot, int kk) __attribute__((always_inline)) {
+      return *reinterpret_cast<const bf16x8_t*>(lds + slot * kS + (kk >> 3) * 256 + ka[kk & 7]);
+    };
+    auto vfrag = [&](int slot, int i) __attribute__((always_inline)) {
+      return *reinterpret_cast<const bf16x8_t*>(lds + slot * kS + (i >> 1) * 2048 + va[i & 1]);
+    };
+
+    // p = exp2(s - m_run) as the two B operands of PV, and this lane's share
+    // of their sum added to ls.
+    auto probs256 = [&](const f32x16_t& s, bf16x8_t* pn, float& ls) __attribute__((always_inline)) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pn[ks][i] = (__bf16)__builtin_amdgcn_exp2f(s[ks * 8 + i] - m_run);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) {
+          const bf16x2_t pp = {pn[ks][i], pn[ks][i + 1]};
+          ls = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ls, false);
+        }
+    };
+    // Raises the row offset by the lane pair's excess mx over it (under a
+    // frame window, a row meeting its first visible keys takes their maximum
+    // as its offset) and rescales the accumulator and the running sum.
+    auto rescale256 = [&](float mx, auto mask) __attribute__((always_inline)) {
       float delta = max_lane_pair(mx);
+      float alpha;
       if constexpr (WIN && decltype(mask)::value) {
         const bool fresh = !seen && delta != -INFINITY;
         seen = seen || fresh;
         delta = fresh ? delta : fmaxf(delta, 0.f);
+        // A fresh row's accumulator and sum are still zero.
+        alpha = fresh ? 1.f : __builtin_amdgcn_exp2f(-delta);
       } else {
         delta = fmaxf(delta, 0.f);
+        alpha = __builtin_amdgcn_exp2f(-delta);
       }
       m_run += delta;
-      const float alpha = __builtin_amdgcn_exp2f(-delta);
       l_run *= alpha;
-      // msplat - delta is exactly -(m_run + delta): updated in place so the
-      // splat keeps its registers across the branch.
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] -= delta;
-        msplat[r] -= delta;
-      }
 #pragma unroll
       for (int dt = 0; dt < NT; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
-    }
-  };
-  // bf16 probabilities p = exp2(s) of the sub-tile scores (already shifted
-  // by the row offset), as the two B operands of PV, and this lane's share
-  // of their row sum.
-  auto probs = [&](const f32x16_t& s, bf16x8_t* pf) {
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int i = 0; i < 8; i += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(s[ks * 8 + i]);
-        const float p1 = __builtin_amdgcn_exp2f(s[ks * 8 + i + 1]);
-        pf[ks][i] = (__bf16)p0;
-        pf[ks][i + 1] = (__bf16)p1;
-      }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int i = 0; i < 8; i += 2) {
-        const bf16x2_t pp = {pf[ks][i], pf[ks][i + 1]};
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_run, false);
-      }
-  };
+    };
 
-  // sched_barrier(0) fences keep the compiler from moving instructions
-  // across the phase boundaries.
-  auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
-  bf16x8_t kf[NF], vf[NF], pf[2];
-  // Ring slot of sub-tile x is (x - xb) mod kRing. Fragment reads take the
-  // slot either at run time or, in the unrolled steady state, as a
-  // compile-time constant that lands in the instruction's offset field (the
-  // field holds 16 bits, so slots past the first 64 KB use addresses biased
-  // by 64 KB).
-  constexpr int SPS = G::kSlotsPerSeg;
-  uint32_t ka[NF], kah[NF], vah[2];
+    // Prologue. Ring fill in the order of first use: K(xb), K(xb+1), then
+    // V^T(xb+t), K(xb+2+t) for t < kRing-2. The scores of xb set each row's
+    // offset to its exact maximum (so the row keeps one probability of 1).
+    // Q fragments live in the accumulation registers (the matrix core reads
+    // its operands from either file), leaving the vector registers to the
+    // fragments in flight and the softmax.
 #pragma unroll
-  for (int kk = 0; kk < NF; ++kk) {
-    ka[kk] = kbase ^ (32u * kk);
-    kah[kk] = ka[kk] + SPS * kBufBytes;
-  }
+    for (int kk = 0; kk < NF; ++kk) asm volatile("" : "+a"(qf[kk]));
+    issue_k(xb);
+    issue_k(xb + 1);
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) vah[ks] = vaddr[ks] + SPS * kBufBytes;
-  auto read_k = [&](auto slot) {
+    for (int t = 0; t < kRing - 2; ++t) {
+      issue_v(xb + t);
+      issue_k(xb + 2 + t);
+    }
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((2 * kRing - 4) * LPS) : "memory");
+    __syncthreads();
+    const f32x16_t zero16 = {};
+    f32x16_t s0 = zero16, s_nx = zero16;   // s_nx: raw scores of the next sub-tile
+#pragma unroll
+    for (int kk = 0; kk < NF; ++kk) s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(0, kk), qf[kk], s0, 0, 0, 0);
+#pragma unroll
+    for (int kk = 0; kk < NF; ++kk) s_nx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(1, kk), qf[kk], s_nx, 0, 0, 0);
+    bf16x8_t pf[2];
+    {
+      m_run = max_lane_pair(rowmax(s0, xmap(xb), Mask{}));
+      // A row with no visible key here (possible only under a frame window)
+      // starts from offset 0 and takes its offset from the first keys it sees.
+      if constexpr (WIN) {
+        seen = m_run != -INFINITY;
+        if (!seen) m_run = 0.f;
+      }
+      probs256(s0, pf, l_run);
+    }
+    // Every wave has read K slots 0 and 1: the refills of the first step
+    // before it, then the wait for K(xb+2) and V^T(xb).
+    bar();
+    issue_k(xb + kRing);
+    issue_v(xb + kRing - 2);
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kWait) : "memory");
+
+    // Step u: refills of the slots read last step (K(u+1), V^T(u-1)); QK^T
+    // of u+2 (when it exists) and PV of u; the softmax of u+1. At the end,
+    // K(u+3) and V^T(u+1) have landed for every wave. Without the mask the
+    // step has no data-dependent branch before its last instruction: each row
+    // raises its offset by its excess when that passes 2^kRescaleLog2 and the
+    // running sum takes the factor at once, while the accumulator, which PV of
+    // u (still relative to the old offset) is updating, is scaled after it in
+    // the rare step where some row raised. So the matrix-core and vector work
+    // form one block that the scheduler interleaves: one fragment read and a
+    // few vector instructions per matrix-core instruction.
+    auto step256 = [&](int u, auto mask, auto kslot, auto vslot, auto with_qk) __attribute__((always_inline)) {
+      constexpr bool kMask = decltype(mask)::value;
+      issue_k(u + 1 + kRing);
+      issue_v(u - 1 + kRing);
+      f32x16_t s = s_nx;
+      bf16x8_t pn[2];
+      float ls = 0.f;
+      if constexpr (!kMask && decltype(with_qk)::value) {
+        // The 32 matrix-core instructions f (even: QK^T fragment f/2, odd: PV
+        // fragment f/2) each with the LDS read of fragment f+4 and a slice of
+        // the softmax, in groups the compiler keeps in this order.
+        auto frag = [&](int f) __attribute__((always_inline)) {
+          return (f & 1) ? vfrag(vslot, f >> 1) : kfrag(kslot, f >> 1);
+        };
+        bf16x8_t fr[2 * NF];
+        f32x16_t sn = zero16;
+        float m0, m1, m2, m3, m4, mx, delta, alpha;
+        uint32_t pk[8];
+#pragma unroll
+        for (int f = 0; f < 4; ++f) fr[f] = frag(f);
+        fence();
+        for_each_index(std::make_integer_sequence<int, 2 * NF>{}, [&](auto fc) __attribute__((always_inline)) {
+          constexpr int f = decltype(fc)::value;
+          if constexpr (f + 4 < 2 * NF) fr[f + 4] = frag(f + 4);
+          if constexpr (f & 1)
+            acc[f >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[f], pf[(f >> 1) & 1], acc[f >> 2], 0, 0, 0);
+          else
+            sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[f], qf[f >> 1], sn, 0, 0, 0);
+          // Each slice's result is pinned in its group by an empty asm use:
+          // the fences bind the scheduler, not the passes that move pure
+          // arithmetic towards its first use.
+          if constexpr (f < 5) {
+            const float t = max3(s[3 * f], s[3 * f + 1], s[3 * f + 2]);
+            asm volatile("" ::"v"(t));
+            if constexpr (f == 0) m0 = t;
+            else if constexpr (f == 1) m1 = t;
+            else if constexpr (f == 2) m2 = t;
+            else if constexpr (f == 3) m3 = t;
+            else m4 = t;
+          } else if constexpr (f == 5) {
+            mx = fmaxf(max3(m0, m1, m2), max3(m3, m4, s[15])) - m_run;
+            asm volatile("" ::"v"(mx));
+          } else if constexpr (f == 6) {
+            mx = max_lane_pair(mx);
+            asm volatile("" ::"v"(mx));
+          } else if constexpr (f == 7) {
+            // Each row raises its offset by its excess when that passes
+            // 2^kRescaleLog2; the sum takes the factor now, the accumulator
+            // after this step's PV.
+            delta = mx > kRescaleLog2 ? mx : 0.f;
+            m_run += delta;
+            alpha = __builtin_amdgcn_exp2f(-delta);
+            l_run *= alpha;
+            asm volatile("" ::"v"(m_run), "v"(l_run), "v"(alpha));
+          } else if constexpr (f < 16) {
+            constexpr int i = 2 * (f - 8);
+            pk[f - 8] = pack_bf16x2(__builtin_amdgcn_exp2f(s[i] - m_run), __builtin_amdgcn_exp2f(s[i + 1] - m_run));
+            asm volatile("" ::"v"(pk[f - 8]));
+          } else if constexpr (f < 24) {
+            ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[f - 16]), ones, ls, false);
+            asm volatile("" ::"v"(ls));
+          }
+          fence();
+        });
+        s_nx = sn;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          pn[ks] = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]});
+        if (__builtin_amdgcn_ballot_w64(delta != 0.f) != 0) {
+#pragma unroll
+          for (int dt = 0; dt < NT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+        }
+      } else {
+        if constexpr (decltype(with_qk)::value) {
+          f32x16_t sn = zero16;
+#pragma unroll
+          for (int m = 0; m < NF; ++m) {
+            sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(kslot, m), qf[m], sn, 0, 0, 0);
+            acc[m >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag(vslot, m), pf[m & 1], acc[m >> 1], 0, 0, 0);
+          }
+          s_nx = sn;
+        } else {
+#pragma unroll
+          for (int m = 0; m < NF; ++m)
+            acc[m >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag(vslot, m), pf[m & 1], acc[m >> 1], 0, 0, 0);
+        }
+        const float mx = rowmax(s, xmap(u + 1), mask) - m_run;
+        bool trigger = mx > kRescaleLog2;
+        if constexpr (WIN && kMask) trigger = trigger || (!seen && mx != -INFINITY);
+        if (__builtin_amdgcn_ballot_w64(trigger) != 0) rescale256(mx, mask);
+        probs256(s, pn, ls);
+      }
+      l_run += ls;
+      pf[0] = pn[0];
+      pf[1] = pn[1];
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kWait) : "memory");
+    };
+
+    // Steady state in blocks of kRing steps (ring slots as constants) while
+    // the steps have a QK^T and need no mask; the rest address the ring at
+    // run time and mask.
+    int u = xb;
+    for (; u + kRing <= min(xe - 2, x_mask - 1); u += kRing) {
+      for_each_index(std::make_integer_sequence<int, kRing>{}, [&](auto k) {
+        constexpr int K = decltype(k)::value;
+        step256(u + K, NoMask{}, (K + 2) % kRing, K, std::true_type{});
+      });
+    }
+    for (; u < xe - 2; ++u) step256(u, Mask{}, slot_of(u + 2), slot_of(u), std::true_type{});
+    if (u == xe - 2) {
+      step256(u, Mask{}, 0, slot_of(u), std::false_type{});
+      ++u;
+    }
+    // PV of the last sub-tile.
+    {
+      const int vs = slot_of(xe - 1);
+#pragma unroll
+      for (int m = 0; m < NF; ++m)
+        acc[m >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag(vs, m), pf[m & 1], acc[m >> 1], 0, 0, 0);
+    }
+    // Let the refills nobody reads retire before the workgroup ends or the
+    // next segment refills the rings.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else {
+    // Per-lane byte offsets of the direct loads within a sub-tile (K and V^T
+    // sub-tiles are contiguous blocks of kKBytes in the workspace). Load i of
+    // this wave fills LDS bytes [1024 j, 1024 j + 1024) of the slot, j = wave
+    // + NW i: K's chunks for j < nK, V^T's after them. The lane that fills
+    // LDS chunk Q fetches the logical chunk the swizzle puts there.
+    const uint16_t* kw = a.kw + (int64_t)bh_kv * a.Sk_pad * D;
+    const uint16_t* vt = a.vt + (int64_t)bh_kv * a.Sk_pad * D;
+    int loff[LDPS];
+#pragma unroll
+    for (int i = 0; i < LDPS; ++i) {
+      const int j = wave + NW * i;
+      if (j < G::nK) {
+        const int Q = j * 64 + lane;
+        const int r = Q / (D / 8), p = Q % (D / 8);
+        loff[i] = (r * D + ((p ^ (r & G::kSwz)) * 8)) * 2;
+      } else {
+        const int Q = (j - G::nK) * 64 + lane;
+        const int d = Q >> 2, p = Q & 3;
+        loff[i] = (d * kSub + ((p ^ ((d >> 2) & 3)) * 8)) * 2;
+      }
+    }
+    // One buffer resource per sub-tile (base in SGPRs, 8 KB range), so the
+    // loads need no vector address arithmetic and offsets stay 32-bit at any
+    // sequence length. Every step issues exactly one refill so the wait counts
+    // are the same at every step; a refill past the last sub-tile gets an
+    // empty range (the hardware returns zeros without touching memory) and
+    // lands in a ring slot that no later step reads.
+    auto issue_loads = [&](int x) {
+      uint8_t* slot = lds + ((x - xb) & (kRing - 1)) * kBufBytes;
+      const bool live = x < xe;
+      const int xs = live ? xmap(x) : 0;
+      const uint16_t* kx = kw + (int64_t)xs * (kSub * D);
+      const uint16_t* vx = vt + (int64_t)xs * (kSub * D);
+#pragma unroll
+      for (int i = 0; i < LDPS; ++i) {
+        const int j = wave + NW * i;
+        load_lds16(j < G::nK ? kx : vx, live ? kKBytes : 0, loff[i], slot + j * 1024);
+      }
+    };
+#pragma unroll
+    for (int i = 0; i < kRing - 1; ++i) issue_loads(xb + i);
+
+    f32x16_t msplat;         // -m_run in every slot: the QK^T accumulator's initial value
+    // The scores arrive as s - m_run. If some row of the wave exceeds its
+    // offset by more than 2^kRescaleLog2 (rare), raise that row's m_run by its
+    // excess, shift the scores and rescale the accumulator and partial sum.
+    // With MASK, a row that saw no key before (seen false, m_run 0) takes its
+    // first visible keys' maximum as its offset.
+    auto maybe_rescale = [&](f32x16_t& s, float mx, auto mask) {
+      bool trigger = mx > kRescaleLog2;
+      if constexpr (WIN && decltype(mask)::value) trigger = trigger || (!seen && mx != -INFINITY);
+      if (__builtin_amdgcn_ballot_w64(trigger) != 0) {
+        float delta = max_lane_pair(mx);
+        float alpha;
+        if constexpr (WIN && decltype(mask)::value) {
+          const bool fresh = !seen && delta != -INFINITY;
+          seen = seen || fresh;
+          delta = fresh ? delta : fmaxf(delta, 0.f);
+          // A fresh row's accumulator and sum are still zero (exp2(-delta)
+          // would overflow when its first visible scores lie far below 0).
+          alpha = fresh ? 1.f : __builtin_amdgcn_exp2f(-delta);
+        } else {
+          delta = fmaxf(delta, 0.f);
+          alpha = __builtin_amdgcn_exp2f(-delta);
+        }
+        m_run += delta;
+        l_run *= alpha;
+        // msplat - delta is exactly -(m_run + delta): updated in place so the
+        // splat keeps its registers across the branch.
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          s[r] -= delta;
+          msplat[r] -= delta;
+        }
+#pragma unroll
+        for (int dt = 0; dt < NT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+      }
+    };
+    // bf16 probabilities p = exp2(s) of the sub-tile scores (already shifted
+    // by the row offset), as the two B operands of PV, and this lane's share
+    // of their row sum.
+    auto probs = [&](const f32x16_t& s, bf16x8_t* pf) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(s[ks * 8 + i]);
+          const float p1 = __builtin_amdgcn_exp2f(s[ks * 8 + i + 1]);
+          pf[ks][i] = (__bf16)p0;
+          pf[ks][i + 1] = (__bf16)p1;
+        }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) {
+          const bf16x2_t pp = {pf[ks][i], pf[ks][i + 1]};
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_run, false);
+        }
+    };
+
+    bf16x8_t kf[NF], vf[NF], pf[2];
+    // Ring slot of sub-tile x is (x - xb) mod kRing. Fragment reads take the
+    // slot either at run time or, in the unrolled steady state, as a
+    // compile-time constant that lands in the instruction's offset field (the
+    // field holds 16 bits, so slots past the first 64 KB use addresses biased
+    // by 64 KB).
+    constexpr int SPS = G::kSlotsPerSeg;
+    uint32_t ka[NF], kah[NF], vah[2];
 #pragma unroll
     for (int kk = 0; kk < NF; ++kk) {
-      if constexpr (std::is_integral_v<decltype(slot)>)
-        kf[kk] = *reinterpret_cast<const bf16x8_t*>(lds + slot * kBufBytes + ka[kk]);
-      else if constexpr (decltype(slot)::value < SPS)
-        kf[kk] = *reinterpret_cast<const bf16x8_t*>(lds + decltype(slot)::value * kBufBytes + ka[kk]);
-      else
-        kf[kk] = *reinterpret_cast<const bf16x8_t*>(lds + (decltype(slot)::value - SPS) * kBufBytes + kah[kk]);
+      ka[kk] = kbase ^ (32u * kk);
+      kah[kk] = ka[kk] + SPS * kBufBytes;
     }
-  };
-  auto read_v = [&](auto slot) {
 #pragma unroll
-    for (int i = 0; i < NF; ++i) {
-      if constexpr (std::is_integral_v<decltype(slot)>)
-        vf[i] = *reinterpret_cast<const bf16x8_t*>(lds + slot * kBufBytes + vaddr[i & 1] + (i >> 1) * 2048);
-      else if constexpr (decltype(slot)::value < SPS)
-        vf[i] = *reinterpret_cast<const bf16x8_t*>(lds + decltype(slot)::value * kBufBytes + vaddr[i & 1] + (i >> 1) * 2048);
-      else
-        vf[i] = *reinterpret_cast<const bf16x8_t*>(lds + (decltype(slot)::value - SPS) * kBufBytes + vah[i & 1] + (i >> 1) * 2048);
-    }
-  };
-  auto rslot = [&](int x) { return (x - xb) & (kRing - 1); };
+    for (int ks = 0; ks < 2; ++ks) vah[ks] = vaddr[ks] + SPS * kBufBytes;
+    auto read_k = [&](auto slot) {
+#pragma unroll
+      for (int kk = 0; kk < NF; ++kk) {
+        if constexpr (std::is_integral_v<decltype(slot)>)
+          kf[kk] = *reinterpret_cast<const bf16x8_t*>(lds + slot * kBufBytes + ka[kk]);
+        else if constexpr (decltype(slot)::value < SPS)
+          kf[kk] = *reinterpret_cast<const bf16x8_t*>(lds + decltype(slot)::value * kBufBytes + ka[kk]);
+        else
+          kf[kk] = *reinterpret_cast<const bf16x8_t*>(lds + (decltype(slot)::value - SPS) * kBufBytes + kah[kk]);
+      }
+    };
+    auto read_v = [&](auto slot) {
+#pragma unroll
+      for (int i = 0; i < NF; ++i) {
+        if constexpr (std::is_integral_v<decltype(slot)>)
+          vf[i] = *reinterpret_cast<const bf16x8_t*>(lds + slot * kBufBytes + vaddr[i & 1] + (i >> 1) * 2048);
+        else if constexpr (decltype(slot)::value < SPS)
+          vf[i] = *reinterpret_cast<const bf16x8_t*>(lds + decltype(slot)::value * kBufBytes + vaddr[i & 1] + (i >> 1) * 2048);
+        else
+          vf[i] = *reinterpret_cast<const bf16x8_t*>(lds + (decltype(slot)::value - SPS) * kBufBytes + vah[i & 1] + (i >> 1) * 2048);
+      }
+    };
+    auto rslot = [&](int x) { return (x - xb) & (kRing - 1); };
 
-  // Sub-tiles xb..xb+2 first (the other loads may still fly), then the
-  // prologue: scores of xb, which set each row's offset to its exact maximum
-  // (so the row keeps one probability of 1), and their probabilities.
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kRing - 4) * LDPS) : "memory");
-  __syncthreads();
-  f32x16_t s;
-  {
-    read_k(std::integral_constant<int, 0>{});
+    // Sub-tiles xb..xb+2 first (the other loads may still fly), then the
+    // prologue: scores of xb, which set each row's offset to its exact maximum
+    // (so the row keeps one probability of 1), and their probabilities.
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kRing - 4) * LDPS) : "memory");
+    __syncthreads();
+    f32x16_t s;
+    {
+      read_k(std::integral_constant<int, 0>{});
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+      for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < NF; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s, 0, 0, 0);
-    read_k(rslot(min(xb + 1, xe - 1)));
-    read_v(std::integral_constant<int, 0>{});
-    const float mx0 = rowmax(s, xmap(xb), Mask{});
-    m_run = max_lane_pair(mx0);
-    // A row with no visible key here (possible only under a frame window)
-    // starts from offset 0 and takes its offset from the first keys it sees.
-    if constexpr (WIN) {
-      seen = m_run != -INFINITY;
-      if (!seen) m_run = 0.f;
+      for (int kk = 0; kk < NF; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s, 0, 0, 0);
+      read_k(rslot(min(xb + 1, xe - 1)));
+      read_v(std::integral_constant<int, 0>{});
+      const float mx0 = rowmax(s, xmap(xb), Mask{});
+      m_run = max_lane_pair(mx0);
+      // A row with no visible key here (possible only under a frame window)
+      // starts from offset 0 and takes its offset from the first keys it sees.
+      if constexpr (WIN) {
+        seen = m_run != -INFINITY;
+        if (!seen) m_run = 0.f;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] -= m_run;
+        msplat[r] = -m_run;
+      }
+      probs(s, pf);
     }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s[r] -= m_run;
-      msplat[r] = -m_run;
-    }
-    probs(s, pf);
-  }
 
-  // Step u alternates two phases separated by workgroup barriers:
-  //   X: the matrix-core work, QK^T of u+1 (K fragments of u+1 in kf) and
-  //      PV of u (V fragments of u in vf, probabilities of u in pf);
-  //   Y: the vector and LDS work, refill of the ring slot of u-1, reads of
-  //      K(u+2) and V(u+1), row maxima and rescale of u+1, probabilities and
-  //      row sums of u+1.
-  // The second wave of each SIMD passes one extra barrier first, so it runs
-  // Y while the first runs X and the other way round: the matrix core of the
-  // SIMD always has one wave's work while the other wave does the softmax.
-  // Both roles execute the same instructions in the same order.
-  auto step = [&](int u, auto mask_next, auto slot_v, auto slot_k) {
-    fence();
-    s = msplat;
+    // Step u alternates two phases separated by workgroup barriers:
+    //   X: the matrix-core work, QK^T of u+1 (K fragments of u+1 in kf) and
+    //      PV of u (V fragments of u in vf, probabilities of u in pf);
+    //   Y: the vector and LDS work, refill of the ring slot of u-1, reads of
+    //      K(u+2) and V(u+1), row maxima and rescale of u+1, probabilities and
+    //      row sums of u+1.
+    // The second wave of each SIMD passes one extra barrier first, so it runs
+    // Y while the first runs X and the other way round: the matrix core of the
+    // SIMD always has one wave's work while the other wave does the softmax.
+    // Both roles execute the same instructions in the same order.
+    auto step = [&](int u, auto mask_next, auto slot_v, auto slot_k) {
+      fence();
+      s = msplat;
 #pragma unroll
-    for (int kk = 0; kk < NF; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s, 0, 0, 0);
+      for (int kk = 0; kk < NF; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < NF; ++i) acc[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf[i & 1], acc[i >> 1], 0, 0, 0);
+      fence();
+      bar();
+      fence();
+      read_k(slot_k);
+      read_v(slot_v);
+      // Refill the slot of u-1, last read for its PV in the X phase before the
+      // previous barrier (or, for the lagging role, before this one). Issued
+      // after this phase's reads: a fragment read behind a pending LDS DMA
+      // would make the compiler wait for every load in flight.
+      issue_loads(u - 1 + kRing);
+      const float mx = rowmax(s, xmap(u + 1), mask_next);
+      maybe_rescale(s, mx, mask_next);
+      probs(s, pf);
+      fence();
+      // Publish sub-tile u+3 once every wave has passed this point.
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((kRing - 4) * LDPS) : "memory");
+      fence();
+    };
+
+    // Steady state in blocks of kRing steps, so that each step's ring slots
+    // (V of u+1 at (u+1-xb) mod 8, K of u+2 at (u+2-xb) mod 8) are constants;
+    // a block runs while all its steps read real sub-tiles and none needs the
+    // mask. The remaining steps address the ring at run time and mask.
+    if (role) bar();
+    int u = xb;
+    for (; u + kRing <= min(xe - 2, x_mask - 1); u += kRing) {
+      // Steps u + k, k = 0..kRing-1: V of sub-tile u+k+1 in slot (k+1) mod
+      // kRing, K of u+k+2 in slot (k+2) mod kRing.
+      for_each_index(std::make_integer_sequence<int, kRing>{}, [&](auto k) {
+        constexpr int K = decltype(k)::value;
+        step(u + K, NoMask{}, std::integral_constant<int, (K + 1) % kRing>{},
+             std::integral_constant<int, (K + 2) % kRing>{});
+      });
+    }
+    for (; u < xe - 1; ++u) step(u, Mask{}, rslot(u + 1), rslot(min(u + 2, xe - 1)));
+    // Last X phase: PV of the last sub-tile only.
 #pragma unroll
     for (int i = 0; i < NF; ++i) acc[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf[i & 1], acc[i >> 1], 0, 0, 0);
-    fence();
-    bar();
-    fence();
-    read_k(slot_k);
-    read_v(slot_v);
-    // Refill the slot of u-1, last read for its PV in the X phase before the
-    // previous barrier (or, for the lagging role, before this one). Issued
-    // after this phase's reads: a fragment read behind a pending LDS DMA
-    // would make the compiler wait for every load in flight.
-    issue_loads(u - 1 + kRing);
-    const float mx = rowmax(s, xmap(u + 1), mask_next);
-    maybe_rescale(s, mx, mask_next);
-    probs(s, pf);
-    fence();
-    // Publish sub-tile u+3 once every wave has passed this point.
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((kRing - 4) * LDPS) : "memory");
-    fence();
-  };
-
-  // Steady state in blocks of kRing steps, so that each step's ring slots
-  // (V of u+1 at (u+1-xb) mod 8, K of u+2 at (u+2-xb) mod 8) are constants;
-  // a block runs while all its steps read real sub-tiles and none needs the
-  // mask. The remaining steps address the ring at run time and mask.
-  if (role) bar();
-  int u = xb;
-  for (; u + kRing <= min(xe - 2, x_mask - 1); u += kRing) {
-    // Steps u + k, k = 0..kRing-1: V of sub-tile u+k+1 in slot (k+1) mod
-    // kRing, K of u+k+2 in slot (k+2) mod kRing.
-    for_each_index(std::make_integer_sequence<int, kRing>{}, [&](auto k) {
-      constexpr int K = decltype(k)::value;
-      step(u + K, NoMask{}, std::integral_constant<int, (K + 1) % kRing>{},
-           std::integral_constant<int, (K + 2) % kRing>{});
-    });
+    if (!role) bar();
+    // The ring holds refills that nobody reads; let them retire so no LDS
+    // write is pending when the workgroup ends or the next segment starts.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
-  for (; u < xe - 1; ++u) step(u, Mask{}, rslot(u + 1), rslot(min(u + 2, xe - 1)));
-  // Last X phase: PV of the last sub-tile only.
-#pragma unroll
-  for (int i = 0; i < NF; ++i) acc[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf[i & 1], acc[i >> 1], 0, 0, 0);
-  if (!role) bar();
-  // The ring holds refills that nobody reads; let them retire so no LDS
-  // write is pending when the workgroup ends or the next segment starts.
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-
   if (rec < 0) {
     // A row that saw no key (frame window only) has l = 0 and is written as 0.
     const float l = sum_lane_pair(l_run);

@@ -139,7 +139,16 @@ struct Geo {
   static constexpr int NW = D <= 128 ? 8 : 4;           // waves per workgroup
   static constexpr int WPE = D <= 128 ? 2 : 1;          // waves per SIMD
   static constexpr int BM = NW * 32;                    // query rows per workgroup
-  static constexpr int kRing = D <= 128 ? 8 : 4;        // ring depth (sub-tiles; per operand at 256)
+  // kPipe: the software-pipelined step (one wave per SIMD at 256) instead of
+  // the two-wave ping-pong.
+  static constexpr bool kPipe = D == 256;
+  // kJit (ping-pong only): the X phase reads its own fragments just in time,
+  // one per matrix-core instruction, instead of the Y phase reading them all.
+  // That moves the LDS reads' issue time off the softmax wave; it pays at
+  // head dim 64, where the Y phase is the longer one, and is neutral at 128,
+  // which runs at the chip's power limit.
+  static constexpr bool kJit = D == 64;
+  static constexpr int kRing = D <= 128 ? 8 : 4;        // ring depth (sub-tiles; per operand when kPipe)
   static constexpr int kKBytes = kSub * D * 2;          // K sub-tile: 32 rows x 2D bytes
   static constexpr int kVBytes = D * kSub * 2;          // V^T sub-tile: D rows x 64 B
   static constexpr int kBufBytes = kKBytes + kVBytes;   // one ring slot
@@ -152,9 +161,9 @@ struct Geo {
   static constexpr int kRecM = NT * 16, kRecL = NT * 16 + 1;     // partial record layout
   // LDS: the ring and one int per wave (its SIMD) for D <= 128; at 256 the
   // two operand rings fill the 160 KB.
-  static constexpr int kLdsBytes = D <= 128 ? kRing * kBufBytes + NW * 4 : 2 * kRing * kKBytes;
+  static constexpr int kLdsBytes = kPipe ? 2 * kRing * kKBytes : kRing * kBufBytes + NW * 4;
   static_assert(LDPS * NW * 1024 == kKBytes + kVBytes, "tile split");
-  static_assert(D == 256 || kRing <= 2 * kSlotsPerSeg, "two address segments at most");
+  static_assert(kPipe || kRing <= 2 * kSlotsPerSeg, "two address segments at most");
   static_assert(kLdsBytes <= 160 * 1024, "LDS");
 };
 
@@ -250,7 +259,7 @@ void attn_fwd_kernel(AttnArgs a) {
   // name the SIMD): the second one of each SIMD runs one phase behind. (At
   // head dim 256 every wave has its SIMD to itself.)
   int role = 0;
-  if constexpr (D <= 128) {
+  if constexpr (!G::kPipe) {
     int* simd_of = reinterpret_cast<int*>(lds + kRing * kBufBytes);
     if (lane == 0) simd_of[wave] = (int)(__builtin_amdgcn_s_getreg((1 << 11) | (4 << 6) | 4) & 3);
     __syncthreads();
@@ -499,7 +508,7 @@ void attn_fwd_kernel(AttnArgs a) {
   // sched_barrier(0) fences keep the compiler from moving instructions
   // across them (phase boundaries, interleave groups).
   auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
-  if constexpr (D == 256) {
+  if constexpr (G::kPipe) {
     // Head dim 256 runs one wave per SIMD, so no second wave covers the
     // softmax: each wave overlaps it with its own matrix-core work. Step u
     // sends QK^T of sub-tile u+2 and PV of sub-tile u to the matrix core and
@@ -605,8 +614,10 @@ void attn_fwd_kernel(AttnArgs a) {
     // Q fragments live in the accumulation registers (the matrix core reads
     // its operands from either file), leaving the vector registers to the
     // fragments in flight and the softmax.
+    if constexpr (G::WPE == 1) {
 #pragma unroll
-    for (int kk = 0; kk < NF; ++kk) asm volatile("" : "+a"(qf[kk]));
+      for (int kk = 0; kk < NF; ++kk) asm volatile("" : "+a"(qf[kk]));
+    }
     issue_k(xb);
     issue_k(xb + 1);
 #pragma unroll
@@ -678,40 +689,48 @@ void attn_fwd_kernel(AttnArgs a) {
             acc[f >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[f], pf[(f >> 1) & 1], acc[f >> 2], 0, 0, 0);
           else
             sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[f], qf[f >> 1], sn, 0, 0, 0);
-          // Each slice's result is pinned in its group by an empty asm use:
-          // the fences bind the scheduler, not the passes that move pure
-          // arithmetic towards its first use.
-          if constexpr (f < 5) {
-            const float t = max3(s[3 * f], s[3 * f + 1], s[3 * f + 2]);
-            asm volatile("" ::"v"(t));
-            if constexpr (f == 0) m0 = t;
-            else if constexpr (f == 1) m1 = t;
-            else if constexpr (f == 2) m2 = t;
-            else if constexpr (f == 3) m3 = t;
-            else m4 = t;
-          } else if constexpr (f == 5) {
-            mx = fmaxf(max3(m0, m1, m2), max3(m3, m4, s[15])) - m_run;
-            asm volatile("" ::"v"(mx));
-          } else if constexpr (f == 6) {
-            mx = max_lane_pair(mx);
-            asm volatile("" ::"v"(mx));
-          } else if constexpr (f == 7) {
-            // Each row raises its offset by its excess when that passes
-            // 2^kRescaleLog2; the sum takes the factor now, the accumulator
-            // after this step's PV.
-            delta = mx > kRescaleLog2 ? mx : 0.f;
-            m_run += delta;
-            alpha = __builtin_amdgcn_exp2f(-delta);
-            l_run *= alpha;
-            asm volatile("" ::"v"(m_run), "v"(l_run), "v"(alpha));
-          } else if constexpr (f < 16) {
-            constexpr int i = 2 * (f - 8);
-            pk[f - 8] = pack_bf16x2(__builtin_amdgcn_exp2f(s[i] - m_run), __builtin_amdgcn_exp2f(s[i + 1] - m_run));
-            asm volatile("" ::"v"(pk[f - 8]));
-          } else if constexpr (f < 24) {
-            ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[f - 16]), ones, ls, false);
-            asm volatile("" ::"v"(ls));
-          }
+          // The softmax in 24 slices, slice i in group i (2 NF = 32) or
+          // spread in order over the 16 groups (2 NF = 16). Each slice's
+          // result is pinned in its group by an empty asm use: the fences
+          // bind the scheduler, not the passes that move pure arithmetic
+          // towards its first use.
+          for_each_index(std::make_integer_sequence<int, 24>{}, [&](auto ic) __attribute__((always_inline)) {
+            constexpr int i = decltype(ic)::value;
+            constexpr int grp = 2 * NF >= 24 ? i : i * 2 * NF / 24;
+            if constexpr (grp == f) {
+              if constexpr (i < 5) {
+                const float t = max3(s[3 * i], s[3 * i + 1], s[3 * i + 2]);
+                asm volatile("" ::"v"(t));
+                if constexpr (i == 0) m0 = t;
+                else if constexpr (i == 1) m1 = t;
+                else if constexpr (i == 2) m2 = t;
+                else if constexpr (i == 3) m3 = t;
+                else m4 = t;
+              } else if constexpr (i == 5) {
+                mx = fmaxf(max3(m0, m1, m2), max3(m3, m4, s[15])) - m_run;
+                asm volatile("" ::"v"(mx));
+              } else if constexpr (i == 6) {
+                mx = max_lane_pair(mx);
+                asm volatile("" ::"v"(mx));
+              } else if constexpr (i == 7) {
+                // Each row raises its offset by its excess when that passes
+                // 2^kRescaleLog2; the sum takes the factor now, the
+                // accumulator after this step's PV.
+                delta = mx > kRescaleLog2 ? mx : 0.f;
+                m_run += delta;
+                alpha = __builtin_amdgcn_exp2f(-delta);
+                l_run *= alpha;
+                asm volatile("" ::"v"(m_run), "v"(l_run), "v"(alpha));
+              } else if constexpr (i < 16) {
+                constexpr int e = 2 * (i - 8);
+                pk[i - 8] = pack_bf16x2(__builtin_amdgcn_exp2f(s[e] - m_run), __builtin_amdgcn_exp2f(s[e + 1] - m_run));
+                asm volatile("" ::"v"(pk[i - 8]));
+              } else {
+                ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[i - 16]), ones, ls, false);
+                asm volatile("" ::"v"(ls));
+              }
+            }
+          });
           fence();
         });
         s_nx = sn;
@@ -929,8 +948,10 @@ void attn_fwd_kernel(AttnArgs a) {
       for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
       for (int kk = 0; kk < NF; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s, 0, 0, 0);
-      read_k(rslot(min(xb + 1, xe - 1)));
-      read_v(std::integral_constant<int, 0>{});
+      if constexpr (!G::kJit) {
+        read_k(rslot(min(xb + 1, xe - 1)));
+        read_v(std::integral_constant<int, 0>{});
+      }
       const float mx0 = rowmax(s, xmap(xb), Mask{});
       m_run = max_lane_pair(mx0);
       // A row with no visible key here (possible only under a frame window)
@@ -957,18 +978,65 @@ void attn_fwd_kernel(AttnArgs a) {
     // Y while the first runs X and the other way round: the matrix core of the
     // SIMD always has one wave's work while the other wave does the softmax.
     // Both roles execute the same instructions in the same order.
-    auto step = [&](int u, auto mask_next, auto slot_v, auto slot_k) {
+    // One fragment of an X phase: f even is K fragment f/2, f odd is V
+    // fragment f/2 (the order the phase consumes them).
+    auto kread = [&](auto slot, int kk) -> bf16x8_t {
+      if constexpr (std::is_integral_v<decltype(slot)>)
+        return *reinterpret_cast<const bf16x8_t*>(lds + slot * kBufBytes + ka[kk]);
+      else if constexpr (decltype(slot)::value < SPS)
+        return *reinterpret_cast<const bf16x8_t*>(lds + decltype(slot)::value * kBufBytes + ka[kk]);
+      else
+        return *reinterpret_cast<const bf16x8_t*>(lds + (decltype(slot)::value - SPS) * kBufBytes + kah[kk]);
+    };
+    auto vread = [&](auto slot, int i) -> bf16x8_t {
+      if constexpr (std::is_integral_v<decltype(slot)>)
+        return *reinterpret_cast<const bf16x8_t*>(lds + slot * kBufBytes + vaddr[i & 1] + (i >> 1) * 2048);
+      else if constexpr (decltype(slot)::value < SPS)
+        return *reinterpret_cast<const bf16x8_t*>(lds + decltype(slot)::value * kBufBytes + vaddr[i & 1] + (i >> 1) * 2048);
+      else
+        return *reinterpret_cast<const bf16x8_t*>(lds + (decltype(slot)::value - SPS) * kBufBytes + vah[i & 1] + (i >> 1) * 2048);
+    };
+    auto xread = [&](int f, auto slot_k, auto slot_v) -> bf16x8_t {
+      return (f & 1) ? vread(slot_v, f >> 1) : kread(slot_k, f >> 1);
+    };
+    bf16x8_t fr[4];   // kJit: the first four fragments of the next X phase
+    // slot_vn, slot_kn: the slots of V(u+1) and K(u+2), read in this step's
+    // Y phase; slot_vc, slot_kc: those of V(u) and K(u+1), which the X phase
+    // reads itself when kJit.
+    auto step = [&](int u, auto mask_next, auto slot_vn, auto slot_kn, auto slot_vc, auto slot_kc) {
       fence();
       s = msplat;
+      if constexpr (G::kJit) {
+        // Fenced groups: one matrix-core instruction and the read of the
+        // fragment four ahead.
+        bf16x8_t gfr[2 * NF];
 #pragma unroll
-      for (int kk = 0; kk < NF; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s, 0, 0, 0);
+        for (int f = 0; f < 4; ++f) gfr[f] = fr[f];
+        for_each_index(std::make_integer_sequence<int, 2 * NF>{}, [&](auto fc) {
+          constexpr int f = decltype(fc)::value;
+          if constexpr (f + 4 < 2 * NF) gfr[f + 4] = xread(f + 4, slot_kc, slot_vc);
+          if constexpr (f & 1)
+            acc[f >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gfr[f], pf[(f >> 1) & 1], acc[f >> 2], 0, 0, 0);
+          else
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gfr[f], qf[f >> 1], s, 0, 0, 0);
+          fence();
+        });
+      } else {
 #pragma unroll
-      for (int i = 0; i < NF; ++i) acc[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf[i & 1], acc[i >> 1], 0, 0, 0);
+        for (int kk = 0; kk < NF; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < NF; ++i) acc[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf[i & 1], acc[i >> 1], 0, 0, 0);
+      }
       fence();
       bar();
       fence();
-      read_k(slot_k);
-      read_v(slot_v);
+      if constexpr (G::kJit) {
+#pragma unroll
+        for (int f = 0; f < 4; ++f) fr[f] = xread(f, slot_kn, slot_vn);
+      } else {
+        read_k(slot_kn);
+        read_v(slot_vn);
+      }
       // Refill the slot of u-1, last read for its PV in the X phase before the
       // previous barrier (or, for the lagging role, before this one). Issued
       // after this phase's reads: a fragment read behind a pending LDS DMA
@@ -987,21 +1055,33 @@ void attn_fwd_kernel(AttnArgs a) {
     // (V of u+1 at (u+1-xb) mod 8, K of u+2 at (u+2-xb) mod 8) are constants;
     // a block runs while all its steps read real sub-tiles and none needs the
     // mask. The remaining steps address the ring at run time and mask.
+    if constexpr (G::kJit) {
+#pragma unroll
+      for (int f = 0; f < 4; ++f) fr[f] = xread(f, rslot(min(xb + 1, xe - 1)), 0);
+    }
     if (role) bar();
     int u = xb;
     for (; u + kRing <= min(xe - 2, x_mask - 1); u += kRing) {
       // Steps u + k, k = 0..kRing-1: V of sub-tile u+k+1 in slot (k+1) mod
-      // kRing, K of u+k+2 in slot (k+2) mod kRing.
+      // kRing, K of u+k+2 in slot (k+2) mod kRing (and V of u+k, K of u+k+1).
       for_each_index(std::make_integer_sequence<int, kRing>{}, [&](auto k) {
         constexpr int K = decltype(k)::value;
         step(u + K, NoMask{}, std::integral_constant<int, (K + 1) % kRing>{},
-             std::integral_constant<int, (K + 2) % kRing>{});
+             std::integral_constant<int, (K + 2) % kRing>{}, std::integral_constant<int, K % kRing>{},
+             std::integral_constant<int, (K + 1) % kRing>{});
       });
     }
-    for (; u < xe - 1; ++u) step(u, Mask{}, rslot(u + 1), rslot(min(u + 2, xe - 1)));
+    for (; u < xe - 1; ++u) step(u, Mask{}, rslot(u + 1), rslot(min(u + 2, xe - 1)), rslot(u), rslot(u + 1));
     // Last X phase: PV of the last sub-tile only.
+    if constexpr (G::kJit) {
+      const int vs = rslot(xe - 1);
 #pragma unroll
-    for (int i = 0; i < NF; ++i) acc[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf[i & 1], acc[i >> 1], 0, 0, 0);
+      for (int i = 0; i < NF; ++i)
+        acc[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vread(vs, i), pf[i & 1], acc[i >> 1], 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NF; ++i) acc[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf[i & 1], acc[i >> 1], 0, 0, 0);
+    }
     if (!role) bar();
     // The ring holds refills that nobody reads; let them retire so no LDS
     // write is pending when the workgroup ends or the next segment starts.

@@ -569,13 +569,13 @@ void attn_fwd_kernel(AttnArgs a) {
       return *reinterpret_cast<const bf16x8_t*>(lds + slot * kS + (i >> 1) * 2048 + va[i & 1]);
     };
 
-    // p = exp2(s - m_run) as the two B operands of PV, and this lane's share
-    // of their sum added to ls.
+    // p = exp2(s) of scores already relative to the row offset, as the two
+    // B operands of PV, and this lane's share of their sum added to ls.
     auto probs256 = [&](const f32x16_t& s, bf16x8_t* pn, float& ls) __attribute__((always_inline)) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) pn[ks][i] = (__bf16)__builtin_amdgcn_exp2f(s[ks * 8 + i] - m_run);
+        for (int i = 0; i < 8; ++i) pn[ks][i] = (__bf16)__builtin_amdgcn_exp2f(s[ks * 8 + i]);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -586,8 +586,9 @@ void attn_fwd_kernel(AttnArgs a) {
     };
     // Raises the row offset by the lane pair's excess mx over it (under a
     // frame window, a row meeting its first visible keys takes their maximum
-    // as its offset) and rescales the accumulator and the running sum.
-    auto rescale256 = [&](float mx, auto mask) __attribute__((always_inline)) {
+    // as its offset), rescales the accumulator and the running sum, and
+    // returns the change of the offset.
+    auto rescale256 = [&](float mx, auto mask) __attribute__((always_inline)) -> float {
       float delta = max_lane_pair(mx);
       float alpha;
       if constexpr (WIN && decltype(mask)::value) {
@@ -606,6 +607,7 @@ void attn_fwd_kernel(AttnArgs a) {
       for (int dt = 0; dt < NT; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+      return delta;
     };
 
     // Prologue. Ring fill in the order of first use: K(xb), K(xb+1), then
@@ -628,12 +630,11 @@ void attn_fwd_kernel(AttnArgs a) {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"((2 * kRing - 4) * LPS) : "memory");
     __syncthreads();
     const f32x16_t zero16 = {};
-    f32x16_t s0 = zero16, s_nx = zero16;   // s_nx: raw scores of the next sub-tile
+    f32x16_t s0 = zero16, s_nx, msplat;
 #pragma unroll
     for (int kk = 0; kk < NF; ++kk) s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(0, kk), qf[kk], s0, 0, 0, 0);
-#pragma unroll
-    for (int kk = 0; kk < NF; ++kk) s_nx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(1, kk), qf[kk], s_nx, 0, 0, 0);
     bf16x8_t pf[2];
+    float dprev = 0.f;
     {
       m_run = max_lane_pair(rowmax(s0, xmap(xb), Mask{}));
       // A row with no visible key here (possible only under a frame window)
@@ -642,8 +643,16 @@ void attn_fwd_kernel(AttnArgs a) {
         seen = m_run != -INFINITY;
         if (!seen) m_run = 0.f;
       }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s0[r] -= m_run;
+        msplat[r] = -m_run;
+      }
       probs256(s0, pf, l_run);
     }
+    s_nx = msplat;
+#pragma unroll
+    for (int kk = 0; kk < NF; ++kk) s_nx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(1, kk), qf[kk], s_nx, 0, 0, 0);
     // Every wave has read K slots 0 and 1: the refills of the first step
     // before it, then the wait for K(xb+2) and V^T(xb).
     bar();
@@ -658,14 +667,27 @@ void attn_fwd_kernel(AttnArgs a) {
     // raises its offset by its excess when that passes 2^kRescaleLog2 and the
     // running sum takes the factor at once, while the accumulator, which PV of
     // u (still relative to the old offset) is updating, is scaled after it in
-    // the rare step where some row raised. So the matrix-core and vector work
-    // form one block that the scheduler interleaves: one fragment read and a
-    // few vector instructions per matrix-core instruction.
+    // the rare step where some row raised, together with the probabilities,
+    // which the block computed with the old offset. So the matrix-core and
+    // vector work form one block that the scheduler interleaves: one fragment
+    // read and a few vector instructions per matrix-core instruction.
+    // Scores leave QK^T relative to the row offset (the accumulator starts at
+    // msplat = -offset); scores computed before a raise are shifted at the
+    // next step's start, in the same rare case.
     auto step256 = [&](int u, auto mask, auto kslot, auto vslot, auto with_qk) __attribute__((always_inline)) {
       constexpr bool kMask = decltype(mask)::value;
       issue_k(u + 1 + kRing);
       issue_v(u - 1 + kRing);
       f32x16_t s = s_nx;
+      // s came out of last step's QK^T relative to the offset before that
+      // step raised it by dprev (rare).
+      if (__builtin_amdgcn_ballot_w64(dprev != 0.f) != 0) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          s[r] -= dprev;
+          msplat[r] -= dprev;
+        }
+      }
       bf16x8_t pn[2];
       float ls = 0.f;
       if constexpr (!kMask && decltype(with_qk)::value) {
@@ -676,7 +698,7 @@ void attn_fwd_kernel(AttnArgs a) {
           return (f & 1) ? vfrag(vslot, f >> 1) : kfrag(kslot, f >> 1);
         };
         bf16x8_t fr[2 * NF];
-        f32x16_t sn = zero16;
+        f32x16_t sn = msplat;
         float m0, m1, m2, m3, m4, mx, delta, alpha;
         uint32_t pk[8];
 #pragma unroll
@@ -707,7 +729,7 @@ void attn_fwd_kernel(AttnArgs a) {
                 else if constexpr (i == 3) m3 = t;
                 else m4 = t;
               } else if constexpr (i == 5) {
-                mx = fmaxf(max3(m0, m1, m2), max3(m3, m4, s[15])) - m_run;
+                mx = fmaxf(max3(m0, m1, m2), max3(m3, m4, s[15]));
                 asm volatile("" ::"v"(mx));
               } else if constexpr (i == 6) {
                 mx = max_lane_pair(mx);
@@ -723,7 +745,7 @@ void attn_fwd_kernel(AttnArgs a) {
                 asm volatile("" ::"v"(m_run), "v"(l_run), "v"(alpha));
               } else if constexpr (i < 16) {
                 constexpr int e = 2 * (i - 8);
-                pk[i - 8] = pack_bf16x2(__builtin_amdgcn_exp2f(s[e] - m_run), __builtin_amdgcn_exp2f(s[e + 1] - m_run));
+                pk[i - 8] = pack_bf16x2(__builtin_amdgcn_exp2f(s[e]), __builtin_amdgcn_exp2f(s[e + 1]));
                 asm volatile("" ::"v"(pk[i - 8]));
               } else {
                 ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[i - 16]), ones, ls, false);
@@ -734,18 +756,29 @@ void attn_fwd_kernel(AttnArgs a) {
           fence();
         });
         s_nx = sn;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-          pn[ks] = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]});
         if (__builtin_amdgcn_ballot_w64(delta != 0.f) != 0) {
 #pragma unroll
           for (int dt = 0; dt < NT; ++dt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[r] -= delta;
+          ls = 0.f;
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              pk[4 * ks + i] = pack_bf16x2(__builtin_amdgcn_exp2f(s[8 * ks + 2 * i]), __builtin_amdgcn_exp2f(s[8 * ks + 2 * i + 1]));
+              ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[4 * ks + i]), ones, ls, false);
+            }
         }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          pn[ks] = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]});
+        dprev = delta;
       } else {
         if constexpr (decltype(with_qk)::value) {
-          f32x16_t sn = zero16;
+          f32x16_t sn = msplat;
 #pragma unroll
           for (int m = 0; m < NF; ++m) {
             sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(kslot, m), qf[m], sn, 0, 0, 0);
@@ -757,10 +790,15 @@ void attn_fwd_kernel(AttnArgs a) {
           for (int m = 0; m < NF; ++m)
             acc[m >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag(vslot, m), pf[m & 1], acc[m >> 1], 0, 0, 0);
         }
-        const float mx = rowmax(s, xmap(u + 1), mask) - m_run;
+        const float mx = rowmax(s, xmap(u + 1), mask);
         bool trigger = mx > kRescaleLog2;
         if constexpr (WIN && kMask) trigger = trigger || (!seen && mx != -INFINITY);
-        if (__builtin_amdgcn_ballot_w64(trigger) != 0) rescale256(mx, mask);
+        dprev = 0.f;
+        if (__builtin_amdgcn_ballot_w64(trigger) != 0) {
+          dprev = rescale256(mx, mask);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[r] -= dprev;
+        }
         probs256(s, pn, ls);
       }
       l_run += ls;

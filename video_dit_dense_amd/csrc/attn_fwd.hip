@@ -29,8 +29,8 @@
 //   B (16 x 32): lane l supplies column l%32, k = 8*(l/32) .. +7
 //   D (32 x 32): lane l register r holds row 8*(r/4) + 4*(l/32) + r%4, col l%32
 //
-// Schedule (head dims 64 and 128; 256 runs four waves, one per SIMD, with
-// a four-slot ring). A workgroup is eight waves (256 query rows), one
+// Schedule (head dims 64 and 128; 256 runs its own software-pipelined step,
+// described where it is built). A workgroup is eight waves (256 query rows), one
 // workgroup per CU, so every SIMD runs two waves and each K/V byte brought
 // into LDS serves 256 queries. Keys are processed in 32-key sub-tiles u, and step u is split
 // by workgroup barriers into two phases:
@@ -132,7 +132,8 @@ constexpr int kSub = 32;                       // keys per sub-tile
 // Tiling by head dim D (64, 128 or 256). D <= 128: eight waves (256 query
 // rows) per workgroup, two per SIMD, and an eight-slot ring. D = 256 holds
 // twice the accumulators and fragments, so one wave per SIMD (four waves,
-// 128 rows) with the whole register file, and a four-slot ring (32 KB slots).
+// 128 rows) with the whole register file, and a K ring and a V^T ring of
+// four 16 KB slots each.
 template <int D>
 struct Geo {
   static_assert(D == 64 || D == 128 || D == 256, "head dim");
@@ -514,10 +515,11 @@ void attn_fwd_kernel(AttnArgs a) {
     // sends QK^T of sub-tile u+2 and PV of sub-tile u to the matrix core and
     // computes, between those instructions, the softmax of sub-tile u+1,
     // whose scores the previous step produced. K and V^T have rings of their
-    // own, kRing slots of one 16 KB sub-tile each, together the whole LDS:
-    // K(x) is read at step x-2 and V^T(x) at step x, and each slot is
-    // refilled the step after its last read, so a load has kRing-2 steps and
-    // more to land.
+    // own, kRing slots of one 16 KB sub-tile each (128 KB, which keeps every
+    // fragment offset inside the 16-bit field): K(x) is read at step x-2 and
+    // V^T(x) at step x, and each slot is refilled the step after its last
+    // read, so a load has kRing-2 steps and more to land (two and three
+    // slots measured the same: load latency is not the limit here).
     constexpr int kS = kKBytes;                 // one K or V^T sub-tile
     constexpr int kV0 = kRing * kS;             // V^T ring base
     constexpr int LPS = kS / 1024 / NW;         // 1 KB loads per wave per sub-tile and operand

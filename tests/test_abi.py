@@ -54,8 +54,10 @@ def test_workspace_bytes(lib):
     # q, k, v each padded to 256 rows, bf16, 128 channels
     # q, k and v^T rows padded to 256, 256 bytes each, then partial records
     # for split tiles: 2 per split block, blocks = min(256, tiles*steps/16)
-    # with 256-row tiles and 32-key steps; a record is (64 + 2) x 512 floats.
-    rec = (64 + 2) * 512 * 4
+    # with 256-row tiles and 32-key steps; a record is (64 + 4) x 512 floats
+    # (the accumulators, then two row offsets and two partial sums per lane:
+    # head dim 128 holds each wave's rows as two 16-row tiles).
+    rec = (64 + 4) * 512 * 4
     assert lib.h3attn_forward_workspace_bytes(1, 104448, 104448, 6) == 6 * 104448 * 256 * 3 + 2 * 256 * rec
     # 6 heads x 4 tiles x 10 steps = 240 steps -> 15 blocks
     assert lib.h3attn_forward_workspace_bytes(2, 1000, 300, 3) == 6 * (1024 + 2 * 512) * 256 + 2 * 15 * rec
@@ -187,8 +189,9 @@ def fwd_ex(lib, stages=3, ws=16 * A, wsb=None, **kw):
 
 def test_forward_ex_workspace_bytes(lib):
     # q rows for Hq heads, k and v^T rows for Hkv heads, partial records only
-    # for the uniform schedule (no causal mask, no per-item lengths)
-    rec = (64 + 2) * 512 * 4
+    # for the uniform schedule (no causal mask, no per-item lengths); at head
+    # dim 128 a record holds two row offsets and two partial sums per lane
+    rec = (64 + 4) * 512 * 4
     assert h3attn.forward_ex_workspace_bytes(1, 104448, 104448, 6, 2) == \
         (6 + 2 * 2) * 104448 * 256 + 2 * 256 * rec
     assert h3attn.forward_ex_workspace_bytes(1, 104448, 104448, 6, 2, causal=True) == (6 + 2 * 2) * 104448 * 256
@@ -196,6 +199,7 @@ def test_forward_ex_workspace_bytes(lib):
         2 * (4 * 1024 + 2 * 1 * 512) * 256
     assert h3attn.forward_ex_workspace_bytes(1, 104448, 104448, 6, 6, window=True) == 3 * 6 * 104448 * 256
     # rows of 2 * head_dim bytes; split records of (head_dim / 2 + 2) floats per lane of 512 (256 at 256)
+    # at head dims 64 and 256
     assert h3attn.forward_ex_workspace_bytes(1, 4096, 4096, 8, 8, head_dim=64) == \
         3 * 8 * 4096 * 128 + 2 * 256 * (32 + 2) * 512 * 4
     assert h3attn.forward_ex_workspace_bytes(1, 4096, 4096, 8, 8, head_dim=256) == \

@@ -5,7 +5,9 @@
 // flash-style: key/value blocks stream through LDS, scores never reach HBM,
 // and a running max / running sum per query row rescales the accumulator
 // (online softmax). QK^T and PV are bf16 matrix-core contractions
-// (v_mfma_f32_32x32x16_bf16) accumulated in fp32; the softmax is fp32.
+// accumulated in fp32 (v_mfma_f32_16x16x32_bf16 at head dim 128, whose
+// layout is described where it is built; v_mfma_f32_32x32x16_bf16 at 64 and
+// 256, described below); the softmax is fp32.
 // The main step is the dense attention of FastVideo PR #1832 ("Summary":
 // BSHD, head_dim 128, dense non-causal) with the valid-front / zero-tail
 // layout of TeleFuser PR #37 (sections 2.3 and 2.4): key j is visible to
@@ -16,7 +18,7 @@
 // gate multiplies each output row by sigmoid(g). Head dims 64, 128 and 256
 // share the code through the Geo<D> tiling constants.
 //
-// Orientation. Each wave owns 32 query rows and computes S^T = K Q^T, so the
+// Orientation (32x32x16 paths). Each wave owns 32 query rows and computes S^T = K Q^T, so the
 // matrix-core result puts one query per lane column: lane l holds 16 of the
 // 32 keys of a 32x32 score block for query l%32, and lane l^32 holds the
 // other 16. P^T then feeds O^T = V^T P^T straight from registers: the keys a
@@ -82,6 +84,7 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 // Word 3 of a raw (stride 0) buffer resource on gfx9: 32-bit data format,
 // untyped loads.
@@ -149,6 +152,9 @@ struct Geo {
   // head dim 64, where the Y phase is the longer one, and is neutral at 128,
   // which runs at the chip's power limit.
   static constexpr bool kJit = D == 64;
+  // kM16: head dim 128 runs the ping-pong on 16x16x32 matrix-core
+  // instructions (two 16-row query tiles per wave) instead of 32x32x16.
+  static constexpr bool kM16 = D == 128;
   static constexpr int kRing = D <= 128 ? 8 : 4;        // ring depth (sub-tiles; per operand when kPipe)
   static constexpr int kKBytes = kSub * D * 2;          // K sub-tile: 32 rows x 2D bytes
   static constexpr int kVBytes = D * kSub * 2;          // V^T sub-tile: D rows x 64 B
@@ -210,6 +216,29 @@ __device__ inline void store_row(const AttnArgs& a, uint16_t* obase, int q, int 
       }
       *reinterpret_cast<uint2*>(op + d0) = val;
     }
+}
+
+// store_row for the 16x16 output layout: lane (l, register r of acc[ct])
+// holds channel 16 ct + 4 (l/16) + r of its row (g4 = l/16).
+template <int D>
+__device__ inline void store_row16(const AttnArgs& a, uint16_t* obase, int q, int g4, const f32x4_t* acc,
+                                   float inv, int q_valid, const uint16_t* gate_row) {
+  if (q >= a.Sq) return;
+  uint16_t* op = obase + q * ((int64_t)a.H * D);
+  const bool live = q < q_valid;
+  if (gate_row && live) {
+    const float gv = __uint_as_float((uint32_t)gate_row[(int64_t)q * a.H] << 16);
+    inv *= 1.0f / (1.0f + __expf(-gv));
+  }
+#pragma unroll
+  for (int ct = 0; ct < D / 16; ++ct) {
+    uint2 val = make_uint2(0u, 0u);
+    if (live) {
+      val.x = pack_bf16x2(acc[ct][0] * inv, acc[ct][1] * inv);
+      val.y = pack_bf16x2(acc[ct][2] * inv, acc[ct][3] * inv);
+    }
+    *reinterpret_cast<uint2*>(op + ct * 16 + g4 * 4) = val;
+  }
 }
 
 // Partial record of a split tile, per thread t of the T-thread workgroup
@@ -425,6 +454,377 @@ void attn_fwd_kernel(AttnArgs a) {
   const int bh_kv = b * a.Hkv + h / (a.H / a.Hkv);
   uint16_t* obase = a.o + ((int64_t)b * a.Sq * a.H + h) * D;
   const uint16_t* gate_row = a.gate ? a.gate + (int64_t)b * a.Sq * a.H + h : nullptr;
+  if constexpr (G::kM16) {
+  // Head dim 128 on v_mfma_f32_16x16x32_bf16 (A 16 x 32: lane l supplies
+  // row l%16, k = 8(l/16) .. +7; B 32 x 16: column l%16, the same k; D 16 x
+  // 16: lane l register r holds row 4(l/16) + r, column l%16). The smaller
+  // shape sustains more flops at the chip's power limit. Each wave keeps its
+  // 32 query rows as two 16-row tiles qt: QK^T is 2 key tiles x 2 query tiles
+  // x D/32 channel chunks (each K fragment serves both query tiles), so lane
+  // l holds, for query row 16 qt + l%16, the 8 keys 16 kt + 4 g4 + r (g4 =
+  // l/16, r < 4); a row's 32 keys are spread over the four lanes l%16 + 16 j.
+  // PV takes those 8 keys as positions 8 g4 .. 8 g4 + 7 of the sub-tile, with
+  // V^T's keys permuted to match (position 8g + j holds key 16 (j/4) + 4g +
+  // j%4), and is D/16 channel tiles x 2 query tiles. The ring, the loads and
+  // the ping-pong schedule are those of the 32x32 path; the X phase reads its
+  // own fragments, two ahead, in fenced groups.
+  constexpr int NC = D / 32;       // 32-channel chunks
+  constexpr int NT16 = D / 16;     // 16-channel output tiles
+  const int l16 = lane & 15, g4 = lane >> 4;
+  int rowq[2], limq[2];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    rowq[qt] = q0 + wave * 32 + qt * 16 + l16;
+    limq[qt] = a.causal ? min(rowq[qt], kvv_t - 1) : kvv_t - 1;
+  }
+  auto xmap = [&](int v) __attribute__((always_inline)) {
+    if constexpr (WIN) return v < wn1 ? v : v + ws2;
+    else return v;
+  };
+  int x_mask = min(a.causal ? q0 / kSub : 0x7fffffff, (kvv_t % kSub) ? kvv_t / kSub : 0x7fffffff);
+  int c_row[2] = {-1, -1};
+  if constexpr (WIN) {
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const int f = rowq[qt] / a.win_F;
+      c_row[qt] = f < a.win_A ? -1 : (f - a.win_A) / a.win_C;
+    }
+    x_mask = !win_fast ? 0 : ((kvv_t % kSub) && xmap(xe - 1) == kvv_t / kSub ? xe - 1 : 0x7fffffff);
+  }
+
+  // Q fragments (B operand of S^T = K Q^T): query row 16 qt + l%16 of the
+  // wave, channels 32 cc + 8 g4 .. +7. Loaded before the ring fill.
+  bf16x8_t qf[2][NC];
+  {
+    const uint16_t* qp = a.qw + ((int64_t)bh * a.Sq_pad + q0 + wave * 32 + l16) * D + g4 * 8;
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) qf[qt][cc] = *reinterpret_cast<const bf16x8_t*>(qp + qt * 16 * D + cc * 32);
+  }
+
+  // Direct loads: the same sub-tile layouts as the 32x32 path, but the ring
+  // keeps all K sub-tiles in its first 64 KB and all V^T sub-tiles in the
+  // second (slot s: K at s * kKBytes, V^T at kRing * kKBytes + s * kKBytes),
+  // so every fragment offset fits the instruction's 16-bit field from one
+  // base register per operand.
+  const uint16_t* kw = a.kw + (int64_t)bh_kv * a.Sk_pad * D;
+  const uint16_t* vt = a.vt + (int64_t)bh_kv * a.Sk_pad * D;
+  int loff[LDPS];
+#pragma unroll
+  for (int i = 0; i < LDPS; ++i) {
+    const int j = wave + NW * i;
+    if (j < G::nK) {
+      const int Q = j * 64 + lane;
+      const int r = Q / (D / 8), p = Q % (D / 8);
+      loff[i] = (r * D + ((p ^ (r & G::kSwz)) * 8)) * 2;
+    } else {
+      const int Q = (j - G::nK) * 64 + lane;
+      const int d = Q >> 2, p = Q & 3;
+      loff[i] = (d * kSub + ((p ^ ((d >> 2) & 3)) * 8)) * 2;
+    }
+  }
+  auto issue_loads = [&](int x) __attribute__((always_inline)) {
+    const int sl = (x - xb) & (kRing - 1);
+    const bool live = x < xe;
+    const int xs = live ? xmap(x) : 0;
+    const uint16_t* kx = kw + (int64_t)xs * (kSub * D);
+    const uint16_t* vx = vt + (int64_t)xs * (kSub * D);
+#pragma unroll
+    for (int i = 0; i < LDPS; ++i) {
+      const int j = wave + NW * i;
+      uint8_t* dst = j < G::nK ? lds + sl * kKBytes + j * 1024 : lds + (kRing + sl) * kKBytes + (j - G::nK) * 1024;
+      load_lds16(j < G::nK ? kx : vx, live ? kKBytes : 0, loff[i], dst);
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < kRing - 1; ++i) issue_loads(xb + i);
+
+  // Accumulator tiles (qt, ct) live as 4-register slices of 16-register
+  // tuples (tile i = qt NT16 + ct in tuple i/4, slice i%4): with the tiles as
+  // separate 4-register values the register allocator writes most results to
+  // fresh registers instead of in place and doubles them.
+  constexpr int NA = 2 * NT16 / 4;
+  f32x16_t accq[NA];
+#pragma unroll
+  for (int i = 0; i < NA; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) accq[i][r] = 0.f;
+  auto acc_mfma = [&](int qt, int ct, bf16x8_t va_, bf16x8_t vb_) __attribute__((always_inline)) {
+    const int i = qt * NT16 + ct;
+    f32x16_t& t = accq[i >> 2];
+    const int o = (i & 3) * 4;
+    f32x4_t c = {t[o], t[o + 1], t[o + 2], t[o + 3]};
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va_, vb_, c, 0, 0, 0);
+    t[o] = c[0]; t[o + 1] = c[1]; t[o + 2] = c[2]; t[o + 3] = c[3];
+  };
+  auto acc_get = [&](int qt, int ct) __attribute__((always_inline)) -> f32x4_t {
+    const int i = qt * NT16 + ct;
+    const int o = (i & 3) * 4;
+    return f32x4_t{accq[i >> 2][o], accq[i >> 2][o + 1], accq[i >> 2][o + 2], accq[i >> 2][o + 3]};
+  };
+  float m_run[2] = {0.f, 0.f};   // row offsets (exp2 units), shared by the row's four lanes
+  float l_run[2] = {0.f, 0.f};   // this lane's share of each row sum
+  bool seen[2] = {true, true};   // the row has met a visible key
+  f32x4_t msplat[2];             // -m_run: the QK^T accumulators' initial value
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+  auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+
+  // This lane's maximum of the 8 scores of query tile qt in sub-tile x; with
+  // MASK, keys its row does not see are set to -inf first.
+  auto rowmax16 = [&](f32x4_t* sq, int x, int qt, auto mask) __attribute__((always_inline)) {
+    if constexpr (decltype(mask)::value) {
+      int a_end = 0x7fffffff, w_lo = 0, w_hi = 0;
+      if constexpr (WIN) {
+        if (c_row[qt] >= 0) {
+          a_end = a.win_A * a.win_F;
+          w_lo = (a.win_A + a.win_C * max(c_row[qt] - a.win_R, 0)) * a.win_F;
+          w_hi = (a.win_A + a.win_C * min(c_row[qt] + a.win_R + 1, win_cap)) * a.win_F;
+        }
+      }
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = x * kSub + kt * 16 + g4 * 4 + r;
+          if constexpr (WIN) {
+            const bool hidden = (key > limq[qt]) | ((key >= a_end) & ((key < w_lo) | (key >= w_hi)));
+            sq[kt][r] = hidden ? -INFINITY : sq[kt][r];
+          } else {
+            if (key > limq[qt]) sq[kt][r] = -INFINITY;
+          }
+        }
+    }
+    return fmaxf(max3(max3(sq[0][0], sq[0][1], sq[0][2]), sq[0][3], sq[1][0]), max3(sq[1][1], sq[1][2], sq[1][3]));
+  };
+  // Maximum / sum over the four lanes of a row (l, l^16, l^32, l^48).
+  auto max_row16 = [](float x) __attribute__((always_inline)) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto sw = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return max_lane_pair(fmaxf(__builtin_bit_cast(float, (uint32_t)sw[0]), __builtin_bit_cast(float, (uint32_t)sw[1])));
+  };
+  auto sum_row16 = [](float x) __attribute__((always_inline)) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto sw = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return sum_lane_pair(__builtin_bit_cast(float, (uint32_t)sw[0]) + __builtin_bit_cast(float, (uint32_t)sw[1]));
+  };
+  using NoMask = std::integral_constant<bool, false>;
+  using Mask = std::integral_constant<bool, true>;
+  // Scores arrive as s - m_run. If some row of the wave exceeds its offset by
+  // more than 2^kRescaleLog2 (rare), raise the offsets by the rows' excess,
+  // shift the scores and rescale the accumulators and partial sums; with
+  // MASK, a row that saw no key before takes its first keys' maximum.
+  auto maybe_rescale16 = [&](f32x4_t (&s)[2][2], const float* mx, auto mask) __attribute__((always_inline)) {
+    bool trigger = (mx[0] > kRescaleLog2) | (mx[1] > kRescaleLog2);
+    if constexpr (WIN && decltype(mask)::value)
+      trigger = trigger | (!seen[0] & (mx[0] != -INFINITY)) | (!seen[1] & (mx[1] != -INFINITY));
+    if (__builtin_amdgcn_ballot_w64(trigger) != 0) {
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        float delta = max_row16(mx[qt]);
+        float alpha;
+        if constexpr (WIN && decltype(mask)::value) {
+          const bool fresh = !seen[qt] && delta != -INFINITY;
+          seen[qt] = seen[qt] || fresh;
+          delta = fresh ? delta : fmaxf(delta, 0.f);
+          alpha = fresh ? 1.f : __builtin_amdgcn_exp2f(-delta);
+        } else {
+          delta = fmaxf(delta, 0.f);
+          alpha = __builtin_amdgcn_exp2f(-delta);
+        }
+        m_run[qt] += delta;
+        l_run[qt] *= alpha;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          s[qt][0][r] -= delta;
+          s[qt][1][r] -= delta;
+          msplat[qt][r] -= delta;
+        }
+#pragma unroll
+        for (int ct = 0; ct < NT16; ++ct)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) accq[(qt * NT16 + ct) >> 2][((qt * NT16 + ct) & 3) * 4 + r] *= alpha;
+      }
+    }
+  };
+  // bf16 probabilities p = exp2(s) as the PV operand of each query tile
+  // (element j: key 16 (j/4) + 4 g4 + j%4), and this lane's share of the sums.
+  auto probs16 = [&](const f32x4_t (&s)[2][2], bf16x8_t* pf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pf[qt][j] = (__bf16)__builtin_amdgcn_exp2f(s[qt][j >> 2][j & 3]);
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        const bf16x2_t pp = {pf[qt][j], pf[qt][j + 1]};
+        l_run[qt] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_run[qt], false);
+      }
+    }
+  };
+
+  // Fragment reads. K fragment (kt, cc): key row 16 kt + l%16, chunk 4 cc +
+  // g4, stored at (4 cc + g4) ^ (l%16) = (g4 ^ l%16) ^ 4 cc, so one address
+  // register per cc; V^T fragment ct: channel row 16 ct + l%16, chunk g4.
+  // The V^T base (64 KB) is hidden from the compiler so that it stays in the
+  // register and out of the offset field.
+  static_assert(kRing * kKBytes == 65536, "K sub-tiles fill the first 64 KB");
+  bf16x8_t pf[2];
+  const uint32_t kb16 = l16 * (2 * D) + ((g4 ^ (l16 & G::kSwz)) * 16);
+  uint32_t ka[NC];
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc) ka[cc] = kb16 ^ (64u * cc);
+  uint32_t va = kRing * kKBytes + l16 * 64 + ((g4 ^ ((l16 >> 2) & 3)) * 16);
+  asm("" : "+v"(va));
+  // Fragment g of a step: g < 2 NC is K fragment (kt, cc) = (g % 2, g / 2)
+  // of the sub-tile in slot_k, the others V^T fragment ct = g - 2 NC of the
+  // one in slot_v. Each feeds two matrix-core instructions (both query tiles).
+  auto frag = [&](int g, auto slot_k, auto slot_v) __attribute__((always_inline)) -> bf16x8_t {
+    int sk, sv;
+    if constexpr (std::is_integral_v<decltype(slot_k)>) sk = slot_k;
+    else sk = decltype(slot_k)::value;
+    if constexpr (std::is_integral_v<decltype(slot_v)>) sv = slot_v;
+    else sv = decltype(slot_v)::value;
+    if (g < 2 * NC)
+      return *reinterpret_cast<const bf16x8_t*>(lds + sk * kKBytes + (g & 1) * (16 * 2 * D) + ka[g >> 1]);
+    return *reinterpret_cast<const bf16x8_t*>(lds + sv * kKBytes + (g - 2 * NC) * 1024 + va);
+  };
+  constexpr int NG = 2 * NC + NT16;   // fragments per step
+  auto rslot = [&](int x) { return (x - xb) & (kRing - 1); };
+  // One X phase: QK^T into s (K fragments of slot_k) and PV into acc (V^T
+  // fragments of slot_v, probabilities pf), in fenced groups of the two
+  // instructions that use fragment g and the read of fragment g + 2; fr holds
+  // the first two fragments, read by the caller.
+  bf16x8_t fr[2];
+  auto xphase = [&](f32x4_t (&s)[2][2], auto slot_k, auto slot_v, bool do_qk) __attribute__((always_inline)) {
+    bf16x8_t gf[NG];
+    gf[0] = fr[0];
+    gf[1] = fr[1];
+    for_each_index(std::make_integer_sequence<int, NG>{}, [&](auto gc) __attribute__((always_inline)) {
+      constexpr int g = decltype(gc)::value;
+      if constexpr (g + 2 < NG) gf[g + 2] = frag(g + 2, slot_k, slot_v);
+      if constexpr (g < 2 * NC) {
+        if (do_qk) {
+#pragma unroll
+          for (int qt = 0; qt < 2; ++qt)
+            s[qt][g & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gf[g], qf[qt][g >> 1], s[qt][g & 1], 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) acc_mfma(qt, g - 2 * NC, gf[g], pf[qt]);
+      }
+      fence();
+    });
+  };
+
+  // Prologue: scores of xb set each row's offset to its exact maximum.
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kRing - 4) * LDPS) : "memory");
+  __syncthreads();
+  f32x4_t s[2][2];
+  {
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) s[qt][kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int g = 0; g < 2 * NC; ++g) {
+      const bf16x8_t kfr = frag(g, 0, 0);
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+        s[qt][g & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfr, qf[qt][g >> 1], s[qt][g & 1], 0, 0, 0);
+    }
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      m_run[qt] = max_row16(rowmax16(s[qt], xmap(xb), qt, Mask{}));
+      if constexpr (WIN) {
+        seen[qt] = m_run[qt] != -INFINITY;
+        if (!seen[qt]) m_run[qt] = 0.f;
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        s[qt][0][r] -= m_run[qt];
+        s[qt][1][r] -= m_run[qt];
+        msplat[qt][r] = -m_run[qt];
+      }
+    }
+    probs16(s, pf);
+  }
+  // The first fragments of the first X phase: K(xb+1), V(xb).
+  fr[0] = frag(0, rslot(min(xb + 1, xe - 1)), 0);
+  fr[1] = frag(1, rslot(min(xb + 1, xe - 1)), 0);
+
+  // Step u: X = QK^T of u+1 and PV of u; Y = fragment reads of K(u+2) and
+  // V(u+1), the refill of the slot of u-1, the softmax of u+1 (as the
+  // 32x32 path).
+  // slot_vc, slot_kc: V(u) and K(u+1), read by this X phase; slot_vn,
+  // slot_kn: V(u+1) and K(u+2), whose first fragments the Y phase reads.
+  auto step = [&](int u, auto mask_next, auto slot_vn, auto slot_kn, auto slot_vc, auto slot_kc) __attribute__((always_inline)) {
+    fence();
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) s[qt][kt] = msplat[qt];
+    xphase(s, slot_kc, slot_vc, true);
+    bar();
+    fence();
+    fr[0] = frag(0, slot_kn, slot_vn);
+    fr[1] = frag(1, slot_kn, slot_vn);
+    issue_loads(u - 1 + kRing);
+    float mx[2];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) mx[qt] = rowmax16(s[qt], xmap(u + 1), qt, mask_next);
+    maybe_rescale16(s, mx, mask_next);
+    probs16(s, pf);
+    fence();
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((kRing - 4) * LDPS) : "memory");
+    fence();
+  };
+
+  if (role) bar();
+  int u = xb;
+  for (; u + kRing <= min(xe - 2, x_mask - 1); u += kRing) {
+    for_each_index(std::make_integer_sequence<int, kRing>{}, [&](auto k) __attribute__((always_inline)) {
+      constexpr int K = decltype(k)::value;
+      step(u + K, NoMask{}, std::integral_constant<int, (K + 1) % kRing>{},
+           std::integral_constant<int, (K + 2) % kRing>{}, std::integral_constant<int, K % kRing>{},
+           std::integral_constant<int, (K + 1) % kRing>{});
+    });
+  }
+  for (; u < xe - 1; ++u) step(u, Mask{}, rslot(u + 1), rslot(min(u + 2, xe - 1)), rslot(u), rslot(u + 1));
+  // Last X phase: PV of the last sub-tile only.
+  {
+    const int vs = rslot(xe - 1);
+#pragma unroll
+    for (int ct = 0; ct < NT16; ++ct) {
+      const bf16x8_t vfr = frag(2 * NC + ct, 0, vs);
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) acc_mfma(qt, ct, vfr, pf[qt]);
+    }
+  }
+  if (!role) bar();
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  if (rec < 0) {
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const float l = sum_row16(l_run[qt]);
+      f32x4_t at[NT16];
+#pragma unroll
+      for (int ct = 0; ct < NT16; ++ct) at[ct] = acc_get(qt, ct);
+      store_row16<D>(a, obase, rowq[qt], g4, at, (!WIN || l > 0.f) ? 1.0f / l : 0.f, qv_seg, gate_row);
+    }
+  } else {
+    float* pr = a.part + (int64_t)rec * attn_part_floats(D) + tid;
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+#pragma unroll
+      for (int ct = 0; ct < NT16; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pr[((qt * NT16 + ct) * 4 + r) * T] = accq[(qt * NT16 + ct) >> 2][((qt * NT16 + ct) & 3) * 4 + r];
+      pr[(G::kRecM + qt) * T] = m_run[qt];
+      pr[(G::kRecM + 2 + qt) * T] = l_run[qt];
+    }
+  }
+  } else {
   // Masking: lane's last visible key (its query row under the causal mask,
   // capped by the valid keys), and the first sub-tile in which some lane of
   // the workgroup may see a masked key; steps before it skip the mask.
@@ -1140,6 +1540,7 @@ void attn_fwd_kernel(AttnArgs a) {
     pr[G::kRecM * T] = m_run;
     pr[G::kRecL * T] = l_run;
   }
+  }
   if (si + 1 < nseg) __syncthreads();   // the next segment refills the LDS ring
   }
 }
@@ -1178,6 +1579,41 @@ __global__ __launch_bounds__(Geo<D>::NW * 64) void attn_merge_kernel(AttnArgs a)
     const int first = (int)(((int64_t)j * U / n) / NU);
     return a.part + (int64_t)(2 * j + (t - first)) * attn_part_floats(D) + tid;
   };
+  const uint16_t* gate_row = a.gate ? a.gate + (int64_t)b * a.Sq * a.H + h : nullptr;
+  if constexpr (G::kM16) {
+    // Records in the 16x16 layout: 2 query tiles x D/16 tiles x 4
+    // registers, then the two rows' offsets and the two partial sums.
+    constexpr int NT16 = D / 16;
+    f32x4_t acc[2][NT16];
+    float M[2], l[2] = {0.f, 0.f};
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      M[qt] = -INFINITY;
+      for (int j = j0; j <= j1; ++j) M[qt] = fmaxf(M[qt], record(j)[(G::kRecM + qt) * T]);
+#pragma unroll
+      for (int ct = 0; ct < NT16; ++ct) acc[qt][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int j = j0; j <= j1; ++j) {
+      const float* pr = record(j);
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        const float w = __builtin_amdgcn_exp2f(pr[(G::kRecM + qt) * T] - M[qt]);
+        l[qt] += w * pr[(G::kRecM + 2 + qt) * T];
+#pragma unroll
+        for (int ct = 0; ct < NT16; ++ct)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[qt][ct][r] += w * pr[((qt * NT16 + ct) * 4 + r) * T];
+      }
+    }
+    const int l16 = lane & 15, g4 = lane >> 4;
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const uint32_t u = __builtin_bit_cast(uint32_t, l[qt]);
+      const auto sw = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+      const float lr = sum_lane_pair(__builtin_bit_cast(float, (uint32_t)sw[0]) + __builtin_bit_cast(float, (uint32_t)sw[1]));
+      store_row16<D>(a, obase, q0 + wave * 32 + qt * 16 + l16, g4, acc[qt], 1.0f / lr, a.q_valid, gate_row);
+    }
+  } else {
   float M = -INFINITY;
   for (int j = j0; j <= j1; ++j) M = fmaxf(M, record(j)[G::kRecM * T]);
   f32x16_t acc[NT];
@@ -1195,8 +1631,17 @@ __global__ __launch_bounds__(Geo<D>::NW * 64) void attn_merge_kernel(AttnArgs a)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[dt][r] += w * pr[(dt * 16 + r) * T];
   }
-  const uint16_t* gate_row = a.gate ? a.gate + (int64_t)b * a.Sq * a.H + h : nullptr;
   store_row<D>(a, obase, q0 + wave * 32 + (lane & 31), lane >> 5, acc, 1.0f / sum_lane_pair(l), a.q_valid, gate_row);
+  }
+}
+
+// Key held at position p (< 32) of a V^T sub-tile: sigma (bits 2 and 3 of
+// p swapped) for the 32x32 PV operand; for the 16x16x32 path (kM16),
+// position 8g + j holds key 16 (j/4) + 4g + j%4.
+template <int D>
+__device__ inline int key_of_position(int p) {
+  if constexpr (Geo<D>::kM16) return ((p & 4) << 2) | ((p & 0x18) >> 1) | (p & 3);
+  else return (p & ~0xC) | ((p & 4) << 1) | ((p & 8) >> 1);
 }
 
 // Transposed, key-blocked copy of v for the PV operand: a block moves 64 keys
@@ -1238,8 +1683,8 @@ __global__ __launch_bounds__(256) void v_relayout_kernel(const uint16_t* __restr
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
       const int pa = pc * 8 + e, pb = pa + 1;
-      const int ka = xs * kSub + ((pa & ~0xC) | ((pa & 4) << 1) | ((pa & 8) >> 1));
-      const int kb = xs * kSub + ((pb & ~0xC) | ((pb & 4) << 1) | ((pb & 8) >> 1));
+      const int ka = xs * kSub + key_of_position<D>(pa);
+      const int kb = xs * kSub + key_of_position<D>(pb);
       packed[e / 2] = (uint32_t)tile[ka * kPitch + d] | ((uint32_t)tile[kb * kPitch + d] << 16);
     }
     *reinterpret_cast<u32x4_t*>(out + idx * 8) = u32x4_t{packed[0], packed[1], packed[2], packed[3]};

@@ -99,7 +99,10 @@ constexpr int attn_rows(int D) { return attn_threads(D) / 2; }
 // values per lane) plus the lane's running max and partial row sum.
 constexpr int kSplitMaxBlocks = 256;
 constexpr int kSplitMinSteps = 16;
-constexpr int attn_part_floats(int D) { return (D / 2 + 2) * attn_threads(D); }
+// Floats per partial record: the accumulator registers of every thread, then
+// each thread's row offsets and partial sums (two of each at head dim 128,
+// whose waves hold their rows as two 16-row tiles).
+constexpr int attn_part_floats(int D) { return (D / 2 + (D == 128 ? 4 : 2)) * attn_threads(D); }
 
 // Partial records the forward workspace reserves for these sizes: two per
 // split workgroup, for the largest split the launcher can choose.

@@ -467,7 +467,7 @@ void attn_fwd_kernel(AttnArgs a) {
   // V^T's keys permuted to match (position 8g + j holds key 16 (j/4) + 4g +
   // j%4), and is D/16 channel tiles x 2 query tiles. The ring, the loads and
   // the ping-pong schedule are those of the 32x32 path; the X phase reads its
-  // own fragments, two ahead, in fenced groups.
+  // own fragments, four ahead, in fenced groups.
   constexpr int NC = D / 32;       // 32-channel chunks
   constexpr int NT16 = D / 16;     // 16-channel output tiles
   const int l16 = lane & 15, g4 = lane >> 4;
@@ -692,16 +692,16 @@ void attn_fwd_kernel(AttnArgs a) {
   auto rslot = [&](int x) { return (x - xb) & (kRing - 1); };
   // One X phase: QK^T into s (K fragments of slot_k) and PV into acc (V^T
   // fragments of slot_v, probabilities pf), in fenced groups of the two
-  // instructions that use fragment g and the read of fragment g + 2; fr holds
-  // the first two fragments, read by the caller.
-  bf16x8_t fr[2];
+  // instructions that use fragment g and the read of fragment g + 4; fr holds
+  // the first four fragments, read by the caller.
+  bf16x8_t fr[4];
   auto xphase = [&](f32x4_t (&s)[2][2], auto slot_k, auto slot_v, bool do_qk) __attribute__((always_inline)) {
     bf16x8_t gf[NG];
-    gf[0] = fr[0];
-    gf[1] = fr[1];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) gf[g] = fr[g];
     for_each_index(std::make_integer_sequence<int, NG>{}, [&](auto gc) __attribute__((always_inline)) {
       constexpr int g = decltype(gc)::value;
-      if constexpr (g + 2 < NG) gf[g + 2] = frag(g + 2, slot_k, slot_v);
+      if constexpr (g + 4 < NG) gf[g + 4] = frag(g + 4, slot_k, slot_v);
       if constexpr (g < 2 * NC) {
         if (do_qk) {
 #pragma unroll
@@ -749,8 +749,8 @@ void attn_fwd_kernel(AttnArgs a) {
     probs16(s, pf);
   }
   // The first fragments of the first X phase: K(xb+1), V(xb).
-  fr[0] = frag(0, rslot(min(xb + 1, xe - 1)), 0);
-  fr[1] = frag(1, rslot(min(xb + 1, xe - 1)), 0);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) fr[g] = frag(g, rslot(min(xb + 1, xe - 1)), 0);
 
   // Step u: X = QK^T of u+1 and PV of u; Y = fragment reads of K(u+2) and
   // V(u+1), the refill of the slot of u-1, the softmax of u+1 (as the
@@ -766,8 +766,8 @@ void attn_fwd_kernel(AttnArgs a) {
     xphase(s, slot_kc, slot_vc, true);
     bar();
     fence();
-    fr[0] = frag(0, slot_kn, slot_vn);
-    fr[1] = frag(1, slot_kn, slot_vn);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) fr[g] = frag(g, slot_kn, slot_vn);
     issue_loads(u - 1 + kRing);
     float mx[2];
 #pragma unroll

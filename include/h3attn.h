@@ -109,7 +109,7 @@ int h3attn_qk_prologue(const uint16_t* q_in, const uint16_t* k_in,
  * normalised q and k and a key-major copy of v, each padded to whole tiles,
  * then room for the partial results of query tiles whose keys the forward
  * splits over several workgroups (it does so when the last round of tiles
- * would leave compute units idle; two fp32 records of 132 KB per split
+ * would leave compute units idle; two fp32 records of 136 KB per split
  * workgroup, at most 512 records). Returns 0 when a size is < 1 or the
  * result would overflow.
  */

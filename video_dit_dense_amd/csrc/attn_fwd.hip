@@ -918,12 +918,15 @@ void attn_fwd_kernel(AttnArgs a) {
     // own, kRing slots of one 16 KB sub-tile each (128 KB, which keeps every
     // fragment offset inside the 16-bit field): K(x) is read at step x-2 and
     // V^T(x) at step x, and each slot is refilled the step after its last
-    // read, so a load has kRing-2 steps and more to land (two and three
-    // slots measured the same: load latency is not the limit here).
+    // read. A step's end waits for the loads of the step before, so a load
+    // has one step and more to land (load latency is not the limit here:
+    // waiting a step earlier, and rings of two and three slots, measured the
+    // same), and the next step's first fragments can be read before the
+    // barrier.
     constexpr int kS = kKBytes;                 // one K or V^T sub-tile
     constexpr int kV0 = kRing * kS;             // V^T ring base
     constexpr int LPS = kS / 1024 / NW;         // 1 KB loads per wave per sub-tile and operand
-    constexpr int kWait = (2 * kRing - 4) * LPS;   // loads that may stay in flight at a step's end
+    constexpr int kWait = (2 * kRing - 6) * LPS;   // loads that may stay in flight at a step's end
     int loffK[LPS], loffV[LPS];
 #pragma unroll
     for (int i = 0; i < LPS; ++i) {
@@ -1056,15 +1059,23 @@ void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
     for (int kk = 0; kk < NF; ++kk) s_nx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(1, kk), qf[kk], s_nx, 0, 0, 0);
     // Every wave has read K slots 0 and 1: the refills of the first step
-    // before it, then the wait for K(xb+2) and V^T(xb).
+    // before it, then the wait for K(xb+2), V^T(xb), K(xb+3) and V^T(xb+1).
     bar();
     issue_k(xb + kRing);
     issue_v(xb + kRing - 2);
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kWait) : "memory");
+    // The first four fragments of the first step (K(xb+2) 0, V^T(xb) 0,
+    // K(xb+2) 1, V^T(xb) 1); each step without a mask reads those of the next.
+    bf16x8_t nf[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) nf[f] = (f & 1) ? vfrag(0, f >> 1) : kfrag(2, f >> 1);
 
     // Step u: refills of the slots read last step (K(u+1), V^T(u-1)); QK^T
     // of u+2 (when it exists) and PV of u; the softmax of u+1. At the end,
-    // K(u+3) and V^T(u+1) have landed for every wave. Without the mask the
+    // K(u+4) and V^T(u+2) have landed for every wave; a step without a mask
+    // has read the first fragments of K(u+3) and V^T(u+1), which landed a
+    // step earlier, before that wait, so the next step's first matrix-core
+    // instruction does not wait on LDS. Without the mask the
     // step has no data-dependent branch before its last instruction: each row
     // raises its offset by its excess when that passes 2^kRescaleLog2 and the
     // running sum takes the factor at once, while the accumulator, which PV of
@@ -1076,7 +1087,7 @@ void attn_fwd_kernel(AttnArgs a) {
     // Scores leave QK^T relative to the row offset (the accumulator starts at
     // msplat = -offset); scores computed before a raise are shifted at the
     // next step's start, in the same rare case.
-    auto step256 = [&](int u, auto mask, auto kslot, auto vslot, auto with_qk) __attribute__((always_inline)) {
+    auto step256 = [&](int u, auto mask, auto kslot, auto vslot, auto with_qk, int nkslot = 0, int nvslot = 0) __attribute__((always_inline)) {
       constexpr bool kMask = decltype(mask)::value;
       issue_k(u + 1 + kRing);
       issue_v(u - 1 + kRing);
@@ -1104,7 +1115,7 @@ void attn_fwd_kernel(AttnArgs a) {
         float m0, m1, m2, m3, m4, mx, delta, alpha;
         uint32_t pk[8];
 #pragma unroll
-        for (int f = 0; f < 4; ++f) fr[f] = frag(f);
+        for (int f = 0; f < 4; ++f) fr[f] = nf[f];
         fence();
         for_each_index(std::make_integer_sequence<int, 2 * NF>{}, [&](auto fc) __attribute__((always_inline)) {
           constexpr int f = decltype(fc)::value;
@@ -1206,6 +1217,10 @@ void attn_fwd_kernel(AttnArgs a) {
       l_run += ls;
       pf[0] = pn[0];
       pf[1] = pn[1];
+      if constexpr (!kMask && decltype(with_qk)::value) {
+#pragma unroll
+        for (int f = 0; f < 4; ++f) nf[f] = (f & 1) ? vfrag(nvslot, f >> 1) : kfrag(nkslot, f >> 1);
+      }
       asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kWait) : "memory");
     };
 
@@ -1216,7 +1231,7 @@ void attn_fwd_kernel(AttnArgs a) {
     for (; u + kRing <= min(xe - 2, x_mask - 1); u += kRing) {
       for_each_index(std::make_integer_sequence<int, kRing>{}, [&](auto k) {
         constexpr int K = decltype(k)::value;
-        step256(u + K, NoMask{}, (K + 2) % kRing, K, std::true_type{});
+        step256(u + K, NoMask{}, (K + 2) % kRing, K, std::true_type{}, (K + 3) % kRing, (K + 1) % kRing);
       });
     }
     for (; u < xe - 2; ++u) step256(u, Mask{}, slot_of(u + 2), slot_of(u), std::true_type{});

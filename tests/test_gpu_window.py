@@ -164,6 +164,34 @@ def test_full_window_sampled_rows(h3):
     check(oracle.compare(got[:, rows], want), "full window sampled")
 
 
+@pytest.mark.parametrize("D,H", [(64, 8), (128, 8), (256, 4)])
+def test_window_longest_first_sampled_rows(h3, D, H):
+    """A window geometry whose tiles are uneven enough that the launcher
+    hands the query blocks out longest first (frames of 1024 rows, chunks of
+    five, radius 1, one anchor frame; S = 24576 gives 768 tiles of four
+    lengths on 256 CUs), on sampled rows: the anchor frame, chunk edges and
+    random rows, every head."""
+    say("window longest first, sampled rows", D)
+    S, window = 24576, (1024, 5, 1, 1)
+    inp = workloads.make_inputs(1, S, S, H, seed=85, D=D)
+    d = DevInputs(inp)
+    if D == 128:
+        cos, sin = h3.rope_tables(S)
+        o = h3.forward(d.q, d.k, d.v, d.w_q, d.w_k, 1e-6, cos, sin, scale=SCALE, window=window)
+    else:
+        o = h3.forward(d.q, d.k, d.v, scale=SCALE, window=window)
+    torch.cuda.synchronize()
+    F, C = window[0], window[1]
+    edges = [0, F - 1, F, F + C * F - 1, F + C * F, S - C * F, S - 1]
+    rows = np.unique(np.concatenate([workloads.sample_rows(S, S, 64, 85), edges]))
+    if D == 128:
+        want = ref(inp, window, rows=rows)
+    else:
+        want = oracle.forward(inp.q, inp.k, inp.v, None, None, 1e-6, None, SCALE, norm=False, rows=rows,
+                              window=window)
+    check(oracle.compare(to_host(o)[:, rows], want), f"D={D} window longest first")
+
+
 def test_window_cross_lengths(h3):
     """Queries and keys of different lengths share one frame grid."""
     say("window, Sq != Sk")

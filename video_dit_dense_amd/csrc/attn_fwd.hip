@@ -74,6 +74,11 @@
 
 #include <algorithm>
 #include <atomic>
+#include <functional>
+#include <mutex>
+#include <numeric>
+#include <queue>
+#include <vector>
 #include <type_traits>
 #include <utility>
 
@@ -129,6 +134,9 @@ __device__ inline float sum_lane_pair(float x) {
 // row. The result o = O / l does not depend on m; bf16 rounding of p is
 // relative, so neither does its accuracy.
 constexpr float kRescaleLog2 = 8.0f;
+// Frame window: the most query blocks per head that are handed out longest
+// first.
+constexpr int kWinOrderMax = 1024;
 
 constexpr int kSub = 32;                       // keys per sub-tile
 
@@ -261,6 +269,49 @@ __device__ __forceinline__ void bar() { asm volatile("s_barrier" ::: "memory"); 
 // a.win_F > 0); the other modes are compiled without its per-lane window
 // bounds and first-key bookkeeping, which would cost registers in the
 // steady state.
+// Frame window: the sub-tiles of the query tile at rows [q00, q00 + BM)
+// with qv valid rows and kvv valid keys: [0, wn1) (the anchor frames, or
+// every key when the tile has a dense row) then [wn1 + ws2, xe + ws2) (the
+// union of its rows' chunk windows), merged when they touch; fast when every
+// row of the tile sees the same whole sub-tiles. cap: the chunks that can
+// hold keys, plus one.
+struct WinSpan {
+  int wn1, ws2, xe, cap;
+  bool fast;
+};
+__host__ __device__ inline WinSpan win_span(const AttnArgs& a, int BM, int q00, int qv, int kvv) {
+  auto imin = [](int x, int y) { return x < y ? x : y; };
+  auto imax = [](int x, int y) { return x > y ? x : y; };
+  const int F = a.win_F, A = a.win_A, C = a.win_C, R = a.win_R;
+  WinSpan w;
+  w.cap = (kvv + F - 1) / F / C + 1;
+  w.fast = true;
+  const int q1 = imin(q00 + BM, qv);
+  const int f0 = q00 / F, f1 = (q1 - 1) / F;
+  int hi1, lo2 = 0, hi2 = 0;
+  if (f0 < A) {
+    hi1 = kvv;
+    w.fast = f1 < A;
+  } else {
+    const int c0 = (f0 - A) / C, c1 = (f1 - A) / C;
+    hi1 = imin(A * F, kvv);
+    lo2 = imin((A + C * imax(c0 - R, 0)) * F, kvv);
+    hi2 = imin((A + C * imin(c1 + R + 1, w.cap)) * F, kvv);
+    w.fast = c0 == c1 && (hi1 % kSub == 0 || hi1 == kvv) && lo2 % kSub == 0 && (hi2 % kSub == 0 || hi2 == kvv);
+  }
+  int s1 = (hi1 + kSub - 1) / kSub;
+  int s2lo = lo2 / kSub, s2hi = (hi2 + kSub - 1) / kSub;
+  if (hi2 <= lo2) s2lo = s2hi = s1;   // no window key below kvv
+  if (s2lo <= s1) {                   // the ranges touch or overlap: one range
+    s1 = imax(s1, s2hi);
+    s2lo = s2hi = s1;
+  }
+  w.wn1 = s1;
+  w.ws2 = s2lo - s1;   // sub-tile of virtual step v >= wn1 is v + ws2
+  w.xe = s1 + (s2hi - s2lo);
+  return w;
+}
+
 template <int D, bool WIN>
 __global__ __launch_bounds__(Geo<D>::NW * 64) __attribute__((amdgpu_waves_per_eu(Geo<D>::WPE, Geo<D>::WPE)))
 void attn_fwd_kernel(AttnArgs a) {
@@ -334,10 +385,59 @@ void attn_fwd_kernel(AttnArgs a) {
       qb = n_qblocks - 1 - bid / nbh;
       bh0 = bid - (bid / nbh) * nbh;
     } else if (WIN) {
-      // The anchor frames come first and their dense rows see the most
-      // keys: query blocks in increasing order, heads inner.
-      qb = bid / nbh;
-      bh0 = bid - qb * nbh;
+      // Heads inner. Query blocks in increasing order (the anchor frames,
+      // whose dense rows see the most keys, first) or, when the launcher
+      // found that it shortens the schedule, longest first: block bid takes,
+      // for head bh = bid % (B H), the query block of rank bid / (B H) in the
+      // order of decreasing sub-tile count (ties by index) of its batch item,
+      // ranked in LDS before the ring is filled.
+      const int rank = bid / nbh;
+      bh0 = bid - rank * nbh;
+      qb = rank;
+      if (a.win_longest_first && n_qblocks <= kWinOrderMax) {
+        const int b = bh0 / a.H;
+        const int qv = item_valid(a.lengths, b, 0, a.q_valid, a.Sq);
+        const int kvv = item_valid(a.lengths, b, 1, a.kv_valid, a.Sk);
+        // Unique keys: sub-tile count above, 1023 - index below, plus one,
+        // so a padding key of zero is below them all; the block of rank r
+        // has exactly r larger keys.
+        uint32_t* key = reinterpret_cast<uint32_t*>(lds);   // [n4] keys, then the chosen block
+        const int n4 = (n_qblocks + 3) & ~3;
+        for (int j = tid; j < n4; j += T) {
+          uint32_t k = 0;
+          if (j < n_qblocks) {
+            const int xe = (j * BM >= qv || kvv == 0) ? 0 : win_span(a, BM, j * BM, qv, kvv).xe;
+            k = ((uint32_t)min(xe, (1 << 21) - 1) << 10 | (uint32_t)(kWinOrderMax - 1 - j)) + 1u;
+          }
+          key[j] = k;
+        }
+        __syncthreads();
+        // One pass over the keys counts, for each of this thread's blocks
+        // j = tid + m T, the larger ones (several reads in flight).
+        constexpr int JM = (kWinOrderMax + T - 1) / T;
+        uint32_t kj[JM];
+        int rj[JM];
+#pragma unroll
+        for (int m = 0; m < JM; ++m) {
+          const int j = tid + m * T;
+          kj[m] = j < n_qblocks ? key[j] : 0xffffffffu;
+          rj[m] = 0;
+        }
+#pragma unroll 4
+        for (int i = 0; i < n4; i += 4) {
+          const u32x4_t k4 = *reinterpret_cast<const u32x4_t*>(key + i);
+#pragma unroll
+          for (int m = 0; m < JM; ++m)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rj[m] += k4[e] > kj[m] ? 1 : 0;
+        }
+#pragma unroll
+        for (int m = 0; m < JM; ++m)
+          if (tid + m * T < n_qblocks && rj[m] == rank) key[n4] = (uint32_t)(tid + m * T);
+        __syncthreads();
+        qb = __builtin_amdgcn_readfirstlane((int)key[n4]);
+        __syncthreads();   // the ring fill overwrites the keys
+      }
     } else {
       bh0 = bid / n_qblocks;
       qb = bid - bh0 * n_qblocks;
@@ -357,35 +457,12 @@ void attn_fwd_kernel(AttnArgs a) {
     xe0 = (key_end + kSub - 1) / kSub;
     rec0 = -1;
     if constexpr (WIN) {
-      // The tile's sub-tiles: [0, wn1) (the anchor frames, or every key when
-      // the tile has a dense row) then [ws2, ws2 + xe0 - wn1) (the union of
-      // its rows' chunk windows), merged when they touch.
-      const int F = a.win_F, A = a.win_A, C = a.win_C, R = a.win_R;
-      win_cap = (kvv_t + F - 1) / F / C + 1;   // chunks past the keys change nothing
-      const int q1 = min(q00 + BM, qv_t);
-      const int f0 = q00 / F, f1 = (q1 - 1) / F;
-      int hi1, lo2 = 0, hi2 = 0;
-      if (f0 < A) {
-        hi1 = kvv_t;
-        win_fast = f1 < A;
-      } else {
-        const int c0 = (f0 - A) / C, c1 = (f1 - A) / C;
-        hi1 = min(A * F, kvv_t);
-        lo2 = min((A + C * max(c0 - R, 0)) * F, kvv_t);
-        hi2 = min((A + C * min(c1 + R + 1, win_cap)) * F, kvv_t);
-        win_fast = c0 == c1 && (hi1 % kSub == 0 || hi1 == kvv_t) && lo2 % kSub == 0 &&
-                   (hi2 % kSub == 0 || hi2 == kvv_t);
-      }
-      int s1 = (hi1 + kSub - 1) / kSub;
-      int s2lo = lo2 / kSub, s2hi = (hi2 + kSub - 1) / kSub;
-      if (hi2 <= lo2) s2lo = s2hi = s1;   // no window key below kv_valid
-      if (s2lo <= s1) {   // the ranges touch or overlap: one range
-        s1 = max(s1, s2hi);
-        s2lo = s2hi = s1;
-      }
-      wn1 = s1;
-      ws2 = s2lo - s1;       // sub-tile of virtual step v >= wn1 is v + ws2
-      xe0 = s1 + (s2hi - s2lo);
+      const WinSpan w = win_span(a, BM, q00, qv_t, kvv_t);
+      win_cap = w.cap;
+      wn1 = w.wn1;
+      ws2 = w.ws2;
+      xe0 = w.xe;
+      win_fast = w.fast;
       if (xe0 == 0) {
         zero_tile(bh0, q00);
         return;
@@ -1729,6 +1806,47 @@ int device_cus() {
 
 namespace {
 
+// Frame window: whether handing the query blocks out longest first (as the
+// kernel ranks them) shortens a greedy schedule of the tiles, one per CU at
+// a time in grid order, by more than 1% against increasing order. Tiles in
+// the increasing order share their windows' keys in L2 more, so the ranked
+// order pays only where the tile lengths leave the last round uneven. With
+// per-item lengths (on the device) the tile lengths are unknown here:
+// increasing order. The decision for the last geometry is kept.
+bool win_longest_first(const AttnArgs& a, int BM, int64_t nq, int cus) {
+  const int64_t nbh = (int64_t)a.B * a.H;
+  if (a.lengths != nullptr || cus <= 0 || nq > kWinOrderMax || nq * nbh > (1 << 16)) return false;
+  static std::mutex mu;
+  static int64_t last_key[12] = {-1};
+  static bool last = false;
+  const int64_t key[12] = {a.B, a.H, a.Sq, a.Sk, a.q_valid, a.kv_valid, a.win_F, a.win_C, a.win_R, a.win_A, BM, cus};
+  std::lock_guard<std::mutex> lock(mu);
+  if (std::equal(key, key + 12, last_key)) return last;
+  std::vector<int64_t> len(nq);
+  for (int64_t j = 0; j < nq; ++j)
+    len[j] = j * BM >= a.q_valid ? 0 : win_span(a, BM, (int)(j * BM), a.q_valid, a.kv_valid).xe;
+  auto makespan = [&](const std::vector<int>& order) {
+    std::priority_queue<int64_t, std::vector<int64_t>, std::greater<int64_t>> free_at;
+    for (int c = 0; c < cus; ++c) free_at.push(0);
+    int64_t end = 0;
+    for (const int j : order)
+      for (int64_t h = 0; h < nbh; ++h) {
+        const int64_t t = free_at.top() + len[j] + 1;
+        free_at.pop();
+        free_at.push(t);
+        end = std::max(end, t);
+      }
+    return end;
+  };
+  std::vector<int> plain(nq);
+  std::iota(plain.begin(), plain.end(), 0);
+  std::vector<int> ranked = plain;
+  std::stable_sort(ranked.begin(), ranked.end(), [&](int x, int y) { return len[x] > len[y]; });
+  last = makespan(ranked) * 100 < makespan(plain) * 99;
+  std::copy(key, key + 12, last_key);
+  return last;
+}
+
 template <int D>
 hipError_t launch_attention_d(AttnArgs a, hipStream_t stream) {
   constexpr int NW = Geo<D>::NW;
@@ -1743,6 +1861,7 @@ hipError_t launch_attention_d(AttnArgs a, hipStream_t stream) {
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
     a.nqv = (int32_t)nq;
     a.n_whole = a.n_split = a.n_split_blocks = 0;
+    a.win_longest_first = a.win_F > 0 && win_longest_first(a, BM, nq, device_cus()) ? 1 : 0;
     if (grid > 0) {
       if (a.win_F > 0)
         attn_fwd_kernel<D, true><<<dim3((unsigned)grid), NW * 64, 0, stream>>>(a);

@@ -140,6 +140,9 @@ struct AttnArgs {
   // block), each finding its own key ranges.
   int32_t general;
   int32_t nqv, n_whole, n_split, n_split_blocks;
+  // Frame window: 1 when workgroups take the query blocks longest first
+  // (set by the launcher when that shortens the schedule), else 0.
+  int32_t win_longest_first;
 };
 
 // Enqueues the attention kernel (and, when the schedule splits tiles, the

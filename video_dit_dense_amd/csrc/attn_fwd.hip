@@ -197,6 +197,33 @@ __device__ inline int xcd_order(int i, int n) {
   return xcd * per + min(xcd, rem) + (i >> 3);
 }
 
+// Causal tiles, longest first (rank 0: the last query block), spread so
+// that each XCD works on few heads and its L2 serves their shared key
+// prefixes. Workgroup bid runs on XCD bid % 8 as that XCD's (bid / 8)-th
+// block. With L = lcm(nbh, 8), each head's ranks split into S = L / nbh
+// residue classes mod S, and XCD x takes classes [P x, P x + P), P = L / 8
+// (at most two heads when nbh is even), its k-th block taking element k / P
+// of class P x + k % P. Every XCD so sees the same mix of lengths, in
+// decreasing order. Ranks past the whole rows of classes (fewer than S per
+// head) come last, heads inner. A bijection onto (rank, head).
+__device__ inline void causal_tile(int bid, int nq, int nbh, int& rank, int& bh) {
+  const int g = min(nbh & -nbh, 8);
+  const int64_t L = (int64_t)nbh * (8 / g);
+  const int S = 8 / g, P = (int)(L / 8);
+  const int R = nq / S;
+  const int64_t rect = (int64_t)R * L;
+  if (bid >= rect) {
+    const int i = (int)(bid - rect);
+    rank = R * S + i / nbh;
+    bh = i - (i / nbh) * nbh;
+    return;
+  }
+  const int x = bid & 7, k = bid >> 3;
+  const int cls = x * P + k % P, e = k / P;
+  bh = cls / S;
+  rank = e * S + cls % S;
+}
+
 // Writes one query row of a finished tile: o = acc * inv rounded to bf16, or
 // +0.0 for rows at or past q_valid. With a gate (gate_row: the head's gate
 // column of the batch item, stride H) the row is also multiplied by
@@ -382,8 +409,9 @@ void attn_fwd_kernel(AttnArgs a) {
     const int nbh = a.B * a.H;
     int qb;
     if (a.causal) {
-      qb = n_qblocks - 1 - bid / nbh;
-      bh0 = bid - (bid / nbh) * nbh;
+      int rank;
+      causal_tile(bid, n_qblocks, nbh, rank, bh0);
+      qb = n_qblocks - 1 - rank;
     } else if (WIN) {
       // Heads inner. Query blocks in increasing order (the anchor frames,
       // whose dense rows see the most keys, first) or, when the launcher

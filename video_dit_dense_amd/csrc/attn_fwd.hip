@@ -197,16 +197,16 @@ __device__ inline int xcd_order(int i, int n) {
   return xcd * per + min(xcd, rem) + (i >> 3);
 }
 
-// Causal tiles, longest first (rank 0: the last query block), spread so
-// that each XCD works on few heads and its L2 serves their shared key
-// prefixes. Workgroup bid runs on XCD bid % 8 as that XCD's (bid / 8)-th
-// block. With L = lcm(nbh, 8), each head's ranks split into S = L / nbh
+// General-mode tiles in rank order (rank 0 first: under the causal mask the
+// last query block, under the frame window the first or the longest), spread
+// so that each XCD works on few heads and its L2 serves their shared keys.
+// Workgroup bid runs on XCD bid % 8 as that XCD's (bid / 8)-th block. With L = lcm(nbh, 8), each head's ranks split into S = L / nbh
 // residue classes mod S, and XCD x takes classes [P x, P x + P), P = L / 8
 // (at most two heads when nbh is even), its k-th block taking element k / P
-// of class P x + k % P. Every XCD so sees the same mix of lengths, in
-// decreasing order. Ranks past the whole rows of classes (fewer than S per
+// of class P x + k % P. Every XCD so sees the same mix of ranks, in
+// increasing order. Ranks past the whole rows of classes (fewer than S per
 // head) come last, heads inner. A bijection onto (rank, head).
-__device__ inline void causal_tile(int bid, int nq, int nbh, int& rank, int& bh) {
+__device__ inline void spread_tile(int bid, int nq, int nbh, int& rank, int& bh) {
   const int g = min(nbh & -nbh, 8);
   const int64_t L = (int64_t)nbh * (8 / g);
   const int S = 8 / g, P = (int)(L / 8);
@@ -410,17 +410,17 @@ void attn_fwd_kernel(AttnArgs a) {
     int qb;
     if (a.causal) {
       int rank;
-      causal_tile(bid, n_qblocks, nbh, rank, bh0);
+      spread_tile(bid, n_qblocks, nbh, rank, bh0);
       qb = n_qblocks - 1 - rank;
     } else if (WIN) {
-      // Heads inner. Query blocks in increasing order (the anchor frames,
-      // whose dense rows see the most keys, first) or, when the launcher
-      // found that it shortens the schedule, longest first: block bid takes,
-      // for head bh = bid % (B H), the query block of rank bid / (B H) in the
-      // order of decreasing sub-tile count (ties by index) of its batch item,
-      // ranked in LDS before the ring is filled.
-      const int rank = bid / nbh;
-      bh0 = bid - rank * nbh;
+      // Block bid takes rank r and head bh from spread_tile. The query block
+      // of rank r is r (increasing order: the anchor frames, whose dense rows
+      // see the most keys, first) or, when the launcher found that it
+      // shortens the schedule, the block of rank r in the order of
+      // decreasing sub-tile count (ties by index) of its batch item, ranked
+      // in LDS before the ring is filled.
+      int rank;
+      spread_tile(bid, n_qblocks, nbh, rank, bh0);
       qb = rank;
       if (a.win_longest_first && n_qblocks <= kWinOrderMax) {
         const int b = bh0 / a.H;
@@ -1836,7 +1836,7 @@ namespace {
 
 // Frame window: whether handing the query blocks out longest first (as the
 // kernel ranks them) shortens a greedy schedule of the tiles, one per CU at
-// a time in grid order, by more than 1% against increasing order. Tiles in
+// a time in rank order, by more than 1% against increasing order. Tiles in
 // the increasing order share their windows' keys in L2 more, so the ranked
 // order pays only where the tile lengths leave the last round uneven. With
 // per-item lengths (on the device) the tile lengths are unknown here:

@@ -205,8 +205,16 @@ __device__ inline int xcd_order(int i, int n) {
 // (at most two heads when nbh is even), its k-th block taking element k / P
 // of class P x + k % P. Every XCD so sees the same mix of ranks, in
 // increasing order. Ranks past the whole rows of classes (fewer than S per
-// head) come last, heads inner. A bijection onto (rank, head).
-__device__ inline void spread_tile(int bid, int nq, int nbh, int& rank, int& bh) {
+// head) come last, heads inner. A bijection onto (rank, head). With
+// per-item lengths the heads of different items differ in work, so each
+// rank keeps all of them together (heads inner) and no XCD is left with the
+// short items only.
+__device__ inline void spread_tile(int bid, int nq, int nbh, bool ragged, int& rank, int& bh) {
+  if (ragged) {
+    rank = bid / nbh;
+    bh = bid - rank * nbh;
+    return;
+  }
   const int g = min(nbh & -nbh, 8);
   const int64_t L = (int64_t)nbh * (8 / g);
   const int S = 8 / g, P = (int)(L / 8);
@@ -410,7 +418,7 @@ void attn_fwd_kernel(AttnArgs a) {
     int qb;
     if (a.causal) {
       int rank;
-      spread_tile(bid, n_qblocks, nbh, rank, bh0);
+      spread_tile(bid, n_qblocks, nbh, a.lengths != nullptr, rank, bh0);
       qb = n_qblocks - 1 - rank;
     } else if (WIN) {
       // Block bid takes rank r and head bh from spread_tile. The query block
@@ -420,7 +428,7 @@ void attn_fwd_kernel(AttnArgs a) {
       // decreasing sub-tile count (ties by index) of its batch item, ranked
       // in LDS before the ring is filled.
       int rank;
-      spread_tile(bid, n_qblocks, nbh, rank, bh0);
+      spread_tile(bid, n_qblocks, nbh, a.lengths != nullptr, rank, bh0);
       qb = rank;
       if (a.win_longest_first && n_qblocks <= kWinOrderMax) {
         const int b = bh0 / a.H;

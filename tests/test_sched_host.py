@@ -1,0 +1,53 @@
+"""CPU checks of the attention kernel's chip schedule, on the same source the
+kernels compile: `sched_check.cpp` includes `attn_sched.h` in a host build
+and sweeps the tile orders, the frame-window key ranges and the split of the
+last partial round of tiles (see its header). The split's partial records
+must also fit in the workspace the library asks for, which this test checks
+against the library's own h3attn_forward_ex_workspace_bytes."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+from video_dit_dense_amd import h3attn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "video_dit_dense_amd", "csrc")
+SRC = os.path.join(ROOT, "tests", "sched_check.cpp")
+
+
+def record_floats(D):
+    """Floats per partial record: D/2 accumulators per thread, then the
+    thread's row offsets and sums (two each at head dim 128), for the 512
+    threads of a head-dim-64/128 workgroup or the 256 of a head-dim-256 one."""
+    threads = 512 if D <= 128 else 256
+    return (D // 2 + (4 if D == 128 else 2)) * threads
+
+
+@pytest.fixture(scope="module")
+def sched_output(tmp_path_factory):
+    cxx = shutil.which("g++") or shutil.which("c++")
+    if cxx is None:
+        pytest.skip("no host C++ compiler")
+    exe = str(tmp_path_factory.mktemp("sched") / "sched_check")
+    subprocess.run([cxx, "-O2", "-std=c++17", "-Wall", "-Werror", "-I", CSRC, SRC, "-o", exe], check=True)
+    res = subprocess.run([exe], capture_output=True, text=True, timeout=300)
+    assert res.returncode == 0, res.stdout[-2000:] + res.stderr[-2000:]
+    return res.stdout
+
+
+def test_schedule_sweeps_pass(sched_output):
+    last = sched_output.strip().splitlines()[-1]
+    assert last.startswith("OK "), last
+
+
+def test_split_records_fit_the_workspace(sched_output):
+    rows = [l.split()[1:] for l in sched_output.splitlines() if l.startswith("WS ")]
+    assert len(rows) >= 10
+    for B, Sq, Sk, H, D, slots, max_rec in ((int(x) for x in r) for r in rows):
+        assert max_rec < slots, (B, Sq, Sk, H, D)
+        pad = lambda s: (s + 255) // 256 * 256   # noqa: E731
+        needed = (B * H * pad(Sq) + 2 * B * H * pad(Sk)) * 2 * D + slots * record_floats(D) * 4
+        got = h3attn.forward_ex_workspace_bytes(B, Sq, Sk, H, H, head_dim=D)
+        assert got == needed, (B, Sq, Sk, H, D, got, needed)

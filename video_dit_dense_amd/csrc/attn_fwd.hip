@@ -134,10 +134,6 @@ __device__ inline float sum_lane_pair(float x) {
 // row. The result o = O / l does not depend on m; bf16 rounding of p is
 // relative, so neither does its accuracy.
 constexpr float kRescaleLog2 = 8.0f;
-// Frame window: the most query blocks per head that are handed out longest
-// first.
-constexpr int kWinOrderMax = 1024;
-
 constexpr int kSub = 32;                       // keys per sub-tile
 
 // Tiling by head dim D (64, 128 or 256). D <= 128: eight waves (256 query
@@ -180,57 +176,17 @@ struct Geo {
   static_assert(LDPS * NW * 1024 == kKBytes + kVBytes, "tile split");
   static_assert(kPipe || kRing <= 2 * kSlotsPerSeg, "two address segments at most");
   static_assert(kLdsBytes <= 160 * 1024, "LDS");
+  // Floats each thread writes to a partial record (the accumulators, then
+  // two row offsets and two partial sums at head dim 128, else one of each)
+  // fill exactly the record size the host reserves per record.
+  static_assert((kM16 ? kRecM + 4 : kRecL + 1) * NW * 64 == attn_part_floats(D), "partial record size");
+  static_assert(NT * 16 == D / 2, "accumulator registers per thread");
 };
 
 // LDS layouts (no padding; XOR swizzles keep every 8-lane group of a
 // ds_read_b128 on 8 distinct 16-byte bank groups):
 //   K:   row r (key), 16-byte chunk c (channels 8c..8c+7) at r*2D + (c ^ (r & kSwz))*16
 //   V^T: row d (channel), chunk c (positions 8c..8c+7) at d*64 + (c ^ ((d >> 2) & 3))*16
-
-// Blocks are dispatched round-robin over the 8 XCDs, so block i of a range
-// of n runs on XCD i%8. This bijection gives each XCD a contiguous run of
-// work items (same head, neighbouring query blocks or steps), so its L2
-// serves one head's K/V stream.
-__device__ inline int xcd_order(int i, int n) {
-  const int xcd = i & 7;
-  const int per = n >> 3, rem = n & 7;
-  return xcd * per + min(xcd, rem) + (i >> 3);
-}
-
-// General-mode tiles in rank order (rank 0 first: under the causal mask the
-// last query block, under the frame window the first or the longest), spread
-// so that each XCD works on few heads and its L2 serves their shared keys.
-// Workgroup bid runs on XCD bid % 8 as that XCD's (bid / 8)-th block. With L = lcm(nbh, 8), each head's ranks split into S = L / nbh
-// residue classes mod S, and XCD x takes classes [P x, P x + P), P = L / 8
-// (at most two heads when nbh is even), its k-th block taking element k / P
-// of class P x + k % P. Every XCD so sees the same mix of ranks, in
-// increasing order. Ranks past the whole rows of classes (fewer than S per
-// head) come last, heads inner. A bijection onto (rank, head). With
-// per-item lengths the heads of different items differ in work, so each
-// rank keeps all of them together (heads inner) and no XCD is left with the
-// short items only.
-__device__ inline void spread_tile(int bid, int nq, int nbh, bool ragged, int& rank, int& bh) {
-  if (ragged) {
-    rank = bid / nbh;
-    bh = bid - rank * nbh;
-    return;
-  }
-  const int g = min(nbh & -nbh, 8);
-  const int64_t L = (int64_t)nbh * (8 / g);
-  const int S = 8 / g, P = (int)(L / 8);
-  const int R = nq / S;
-  const int64_t rect = (int64_t)R * L;
-  if (bid >= rect) {
-    const int i = (int)(bid - rect);
-    rank = R * S + i / nbh;
-    bh = i - (i / nbh) * nbh;
-    return;
-  }
-  const int x = bid & 7, k = bid >> 3;
-  const int cls = x * P + k % P, e = k / P;
-  bh = cls / S;
-  rank = e * S + cls % S;
-}
 
 // Writes one query row of a finished tile: o = acc * inv rounded to bf16, or
 // +0.0 for rows at or past q_valid. With a gate (gate_row: the head's gate
@@ -304,49 +260,6 @@ __device__ __forceinline__ void bar() { asm volatile("s_barrier" ::: "memory"); 
 // a.win_F > 0); the other modes are compiled without its per-lane window
 // bounds and first-key bookkeeping, which would cost registers in the
 // steady state.
-// Frame window: the sub-tiles of the query tile at rows [q00, q00 + BM)
-// with qv valid rows and kvv valid keys: [0, wn1) (the anchor frames, or
-// every key when the tile has a dense row) then [wn1 + ws2, xe + ws2) (the
-// union of its rows' chunk windows), merged when they touch; fast when every
-// row of the tile sees the same whole sub-tiles. cap: the chunks that can
-// hold keys, plus one.
-struct WinSpan {
-  int wn1, ws2, xe, cap;
-  bool fast;
-};
-__host__ __device__ inline WinSpan win_span(const AttnArgs& a, int BM, int q00, int qv, int kvv) {
-  auto imin = [](int x, int y) { return x < y ? x : y; };
-  auto imax = [](int x, int y) { return x > y ? x : y; };
-  const int F = a.win_F, A = a.win_A, C = a.win_C, R = a.win_R;
-  WinSpan w;
-  w.cap = (kvv + F - 1) / F / C + 1;
-  w.fast = true;
-  const int q1 = imin(q00 + BM, qv);
-  const int f0 = q00 / F, f1 = (q1 - 1) / F;
-  int hi1, lo2 = 0, hi2 = 0;
-  if (f0 < A) {
-    hi1 = kvv;
-    w.fast = f1 < A;
-  } else {
-    const int c0 = (f0 - A) / C, c1 = (f1 - A) / C;
-    hi1 = imin(A * F, kvv);
-    lo2 = imin((A + C * imax(c0 - R, 0)) * F, kvv);
-    hi2 = imin((A + C * imin(c1 + R + 1, w.cap)) * F, kvv);
-    w.fast = c0 == c1 && (hi1 % kSub == 0 || hi1 == kvv) && lo2 % kSub == 0 && (hi2 % kSub == 0 || hi2 == kvv);
-  }
-  int s1 = (hi1 + kSub - 1) / kSub;
-  int s2lo = lo2 / kSub, s2hi = (hi2 + kSub - 1) / kSub;
-  if (hi2 <= lo2) s2lo = s2hi = s1;   // no window key below kvv
-  if (s2lo <= s1) {                   // the ranges touch or overlap: one range
-    s1 = imax(s1, s2hi);
-    s2lo = s2hi = s1;
-  }
-  w.wn1 = s1;
-  w.ws2 = s2lo - s1;   // sub-tile of virtual step v >= wn1 is v + ws2
-  w.xe = s1 + (s2hi - s2lo);
-  return w;
-}
-
 template <int D, bool WIN>
 __global__ __launch_bounds__(Geo<D>::NW * 64) __attribute__((amdgpu_waves_per_eu(Geo<D>::WPE, Geo<D>::WPE)))
 void attn_fwd_kernel(AttnArgs a) {
@@ -434,16 +347,15 @@ void attn_fwd_kernel(AttnArgs a) {
         const int b = bh0 / a.H;
         const int qv = item_valid(a.lengths, b, 0, a.q_valid, a.Sq);
         const int kvv = item_valid(a.lengths, b, 1, a.kv_valid, a.Sk);
-        // Unique keys: sub-tile count above, 1023 - index below, plus one,
-        // so a padding key of zero is below them all; the block of rank r
-        // has exactly r larger keys.
+        // Unique keys (win_rank_key), so the block of rank r has exactly r
+        // larger keys; a padding key of zero is below them all.
         uint32_t* key = reinterpret_cast<uint32_t*>(lds);   // [n4] keys, then the chosen block
         const int n4 = (n_qblocks + 3) & ~3;
         for (int j = tid; j < n4; j += T) {
           uint32_t k = 0;
           if (j < n_qblocks) {
-            const int xe = (j * BM >= qv || kvv == 0) ? 0 : win_span(a, BM, j * BM, qv, kvv).xe;
-            k = ((uint32_t)min(xe, (1 << 21) - 1) << 10 | (uint32_t)(kWinOrderMax - 1 - j)) + 1u;
+            const int xe = (j * BM >= qv || kvv == 0) ? 0 : win_span(a.win_F, a.win_C, a.win_R, a.win_A, BM, j * BM, qv, kvv).xe;
+            k = win_rank_key(xe, j);
           }
           key[j] = k;
         }
@@ -493,7 +405,7 @@ void attn_fwd_kernel(AttnArgs a) {
     xe0 = (key_end + kSub - 1) / kSub;
     rec0 = -1;
     if constexpr (WIN) {
-      const WinSpan w = win_span(a, BM, q00, qv_t, kvv_t);
+      const WinSpan w = win_span(a.win_F, a.win_C, a.win_R, a.win_A, BM, q00, qv_t, kvv_t);
       win_cap = w.cap;
       wn1 = w.wn1;
       ws2 = w.ws2;
@@ -513,23 +425,19 @@ void attn_fwd_kernel(AttnArgs a) {
       xe0 = NU;
       rec0 = -1;
     } else if (bid < a.n_whole + a.n_split_blocks) {
-      // Split tiles: of the U = n_split*NU steps of tiles n_whole.., block j
-      // takes [j*U/n, (j+1)*U/n) with n = n_split_blocks > n_split, so at
-      // most NU steps and at most two tiles.
-      const int j = xcd_order(bid - a.n_whole, a.n_split_blocks);
-      const int64_t U = (int64_t)a.n_split * NU;
-      const int64_t s0 = (int64_t)j * U / a.n_split_blocks;
-      const int64_t s1 = (int64_t)(j + 1) * U / a.n_split_blocks;
-      const int t = (int)(s0 / NU);
-      g0 = a.n_whole + t;
-      xb0 = (int)(s0 - (int64_t)t * NU);
-      xe0 = (int)min<int64_t>(NU, s1 - (int64_t)t * NU);
-      rec0 = 2 * j;
-      if (s1 > (int64_t)(t + 1) * NU) {
+      // Split tiles (split_segments): block j takes its share of the split
+      // tiles' steps, at most NU steps over at most two tiles.
+      const SplitSeg sg = split_segments(xcd_order(bid - a.n_whole, a.n_split_blocks), a.n_split, NU,
+                                         a.n_split_blocks);
+      g0 = a.n_whole + sg.tile;
+      xb0 = sg.xb0;
+      xe0 = sg.xe0;
+      rec0 = sg.rec0;
+      if (sg.nseg == 2) {
         nseg = 2;
         g1 = g0 + 1;
-        xe1 = (int)(s1 - (int64_t)(t + 1) * NU);
-        rec1 = 2 * j + 1;
+        xe1 = sg.xe1;
+        rec1 = sg.rec1;
       }
     } else {
       // A tile wholly past q_valid.
@@ -1695,17 +1603,11 @@ __global__ __launch_bounds__(Geo<D>::NW * 64) void attn_merge_kernel(AttnArgs a)
   const int h = bh - b * a.H;
   uint16_t* obase = a.o + ((int64_t)b * a.Sq * a.H + h) * D;
 
-  // Block j covers steps [j*U/n, (j+1)*U/n), so step x lies in block
-  // floor(((x + 1) * n - 1) / U); its record for tile t is 2j + (t - first
-  // tile of block j).
-  const int n = a.n_split_blocks;
-  const int64_t U = (int64_t)a.n_split * NU;
-  const int64_t x0 = (int64_t)t * NU, x1 = x0 + NU - 1;
-  const int j0 = (int)(((x0 + 1) * n - 1) / U);
-  const int j1 = (int)(((x1 + 1) * n - 1) / U);
+  // The blocks j0 .. j1 that touch tile t, and block j's record for it.
+  int j0, j1;
+  merge_blocks(t, a.n_split, NU, a.n_split_blocks, j0, j1);
   auto record = [&](int j) {
-    const int first = (int)(((int64_t)j * U / n) / NU);
-    return a.part + (int64_t)(2 * j + (t - first)) * attn_part_floats(D) + tid;
+    return a.part + (int64_t)merge_record(j, t, a.n_split, NU, a.n_split_blocks) * attn_part_floats(D) + tid;
   };
   const uint16_t* gate_row = a.gate ? a.gate + (int64_t)b * a.Sq * a.H + h : nullptr;
   if constexpr (G::kM16) {
@@ -1860,7 +1762,7 @@ bool win_longest_first(const AttnArgs& a, int BM, int64_t nq, int cus) {
   if (std::equal(key, key + 12, last_key)) return last;
   std::vector<int64_t> len(nq);
   for (int64_t j = 0; j < nq; ++j)
-    len[j] = j * BM >= a.q_valid ? 0 : win_span(a, BM, (int)(j * BM), a.q_valid, a.kv_valid).xe;
+    len[j] = j * BM >= a.q_valid ? 0 : win_span(a.win_F, a.win_C, a.win_R, a.win_A, BM, (int)(j * BM), a.q_valid, a.kv_valid).xe;
   auto makespan = [&](const std::vector<int>& order) {
     std::priority_queue<int64_t, std::vector<int64_t>, std::greater<int64_t>> free_at;
     for (int c = 0; c < cus; ++c) free_at.push(0);
@@ -1914,17 +1816,8 @@ hipError_t launch_attention_d(AttnArgs a, hipStream_t stream) {
   // that round is partial, split its tiles' steps over more blocks (at most
   // one per CU, each at least kSplitMinSteps steps, and more blocks than
   // tiles so no block spans more than two tiles).
-  int64_t n_whole = n_valid, n_split = 0, n_blocks = 0;
-  const int64_t cus = std::min<int64_t>(device_cus(), kSplitMaxBlocks);
-  if (cus > 0) {
-    const int64_t r = n_valid % cus;
-    const int64_t blocks = std::min<int64_t>({cus, r * NU / kSplitMinSteps, a.part_slots / 2});
-    if (r > 0 && blocks > r) {
-      n_whole = n_valid - r;
-      n_split = r;
-      n_blocks = blocks;
-    }
-  }
+  const SplitPlan sp = split_plan(n_valid, NU, device_cus(), a.part_slots);
+  const int64_t n_whole = sp.n_whole, n_split = sp.n_split, n_blocks = sp.n_blocks;
   const int64_t grid = n_whole + n_blocks + n_zero;
   if (grid > 0x7fffffffLL || nqv > 0x7fffffffLL) return hipErrorInvalidValue;
   a.nqv = (int32_t)nqv;

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "attn_sched.h"
+
 namespace h3 {
 
 constexpr int kHeadDim = 128;
@@ -83,35 +85,6 @@ hipError_t launch_qk_copy(const ProTensor& t0, const ProTensor& t1, int32_t B, i
 
 hipError_t launch_rope_tables(float* cos_out, float* sin_out, int32_t rows, double theta,
                               hipStream_t stream);
-
-// Attention tiling by head dim D (64, 128 or 256): a workgroup of
-// attn_threads(D) / 64 waves (32 query rows each) owns attn_rows(D) query
-// rows of one (b, h) and walks the keys in kAttnSub-key sub-tiles.
-constexpr int kAttnSub = 32;
-constexpr int attn_threads(int D) { return D <= 128 ? 512 : 256; }
-constexpr int attn_rows(int D) { return attn_threads(D) / 2; }
-
-// Load balancing of the last, partial round of query tiles (stream-K): those
-// tiles' sub-tile steps are split evenly over up to kSplitMaxBlocks
-// workgroups, each taking at least kSplitMinSteps steps and touching at most
-// two tiles; each writes one partial record per tile it touches and a second
-// kernel merges them. A record holds the un-normalised fp32 accumulator (D/2
-// values per lane) plus the lane's running max and partial row sum.
-constexpr int kSplitMaxBlocks = 256;
-constexpr int kSplitMinSteps = 16;
-// Floats per partial record: the accumulator registers of every thread, then
-// each thread's row offsets and partial sums (two of each at head dim 128,
-// whose waves hold their rows as two 16-row tiles).
-constexpr int attn_part_floats(int D) { return (D / 2 + (D == 128 ? 4 : 2)) * attn_threads(D); }
-
-// Partial records the forward workspace reserves for these sizes: two per
-// split workgroup, for the largest split the launcher can choose.
-inline int64_t split_part_slots(int32_t B, int32_t Sq, int32_t Sk, int32_t H, int32_t D) {
-  const int64_t tiles = (int64_t)B * H * ((Sq + attn_rows(D) - 1) / attn_rows(D));
-  const int64_t steps = tiles * ((Sk + kAttnSub - 1) / kAttnSub);
-  const int64_t blocks = steps / kSplitMinSteps < kSplitMaxBlocks ? steps / kSplitMinSteps : kSplitMaxBlocks;
-  return 2 * blocks;
-}
 
 struct AttnArgs {
   int32_t D;               // head dim: 64, 128 or 256

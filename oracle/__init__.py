@@ -231,8 +231,10 @@ def forward(q_bits, k_bits, v_bits, w_q, w_k, eps: float, theta: float | None,
 
 def compare(got_bits_or_f64, ref: np.ndarray) -> dict:
     """Error metrics of a bf16 (bit patterns) or float result against the
-    fp64 reference: max-abs, relative RMS ||d||_2 / ||ref||_2, and the
-    largest distance in bf16 units in the last place."""
+    fp64 reference: max-abs, relative RMS ||d||_2 / ||ref||_2, the largest
+    distance in bf16 units in the last place, and the largest relative L2
+    error of one row (the last axis: ||d_row||_2 / ||ref_row||_2, or
+    ||d_row||_2 where the reference row is zero)."""
     got = np.asarray(got_bits_or_f64)
     if got.dtype == np.uint16:
         got = bf16_bits_to_f64(got)
@@ -245,9 +247,13 @@ def compare(got_bits_or_f64, ref: np.ndarray) -> dict:
     a = np.abs(ref)
     e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
     ulp = np.where(a > 0, np.exp2(np.maximum(e, -126.0) - 7.0), np.exp2(-133.0))
+    dr = np.sqrt(np.sum(d * d, axis=-1)) if d.size else np.zeros(0)
+    rr = np.sqrt(np.sum(ref * ref, axis=-1)) if d.size else np.zeros(0)
+    row_rel = np.where(rr > 0, dr / np.where(rr > 0, rr, 1.0), dr)
     return {
         "max_abs": float(np.max(np.abs(d))) if d.size else 0.0,
         "rel_rms": rel_rms,
         "max_ulp": float(np.max(np.abs(d) / ulp)) if d.size else 0.0,
         "nonfinite": int(np.size(got) - np.count_nonzero(np.isfinite(got))),
+        "row_rel_l2_max": float(np.max(row_rel)) if row_rel.size else 0.0,
     }

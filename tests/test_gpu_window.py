@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import workloads
-from gpu_util import DevInputs, say, to_dev, to_host
+from gpu_util import DevInputs, check_metrics, say, to_dev, to_host
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -28,10 +28,7 @@ def h3():
 
 
 def check(metrics, label):
-    say(f"{label}: {metrics}")
-    assert metrics["nonfinite"] == 0, label
-    assert metrics["max_abs"] <= MAX_ABS, label
-    assert metrics["rel_rms"] <= REL_RMS, label
+    check_metrics(metrics, label, MAX_ABS, REL_RMS)
 
 
 def run(h3, inp, window, gate_bits=None, q_valid=None, kv_valid=None, lengths=None):
@@ -148,30 +145,14 @@ def test_window_repeatable(h3):
     assert np.array_equal(a, b)
 
 
-def test_full_window_sampled_rows(h3):
-    """The benchmark's window workload at its full size, in the launch
-    configuration it times, on sampled rows: the anchor frame, chunk edges,
-    the first and last rows."""
-    wl = workloads.VARIANT_WORKLOADS["full_window"]
-    say("full window, sampled rows")
-    inp = workloads.make_workload_inputs(wl)
-    g = workloads.make_gate(wl.B, wl.Sq, wl.H, seed=wl.seed)
-    got = run(h3, inp, wl.window, g)
-    F, C = wl.window[0], wl.window[1]
-    edges = [F - 1, F, F + C * F - 1, F + C * F, wl.Sq // 2]
-    rows = np.unique(np.concatenate([workloads.sample_rows(wl.Sq, wl.Sq, 96, wl.seed), edges]))
-    want = ref(inp, wl.window, g, rows=rows)
-    check(oracle.compare(got[:, rows], want), "full window sampled")
-
-
 @pytest.mark.parametrize("D,H", [(64, 8), (128, 8), (256, 4)])
-def test_window_longest_first_sampled_rows(h3, D, H):
+def test_window_longest_first_every_tile(h3, D, H):
     """A window geometry whose tiles are uneven enough that the launcher
     hands the query blocks out longest first (frames of 1024 rows, chunks of
     five, radius 1, one anchor frame; S = 24576 gives 768 tiles of four
-    lengths on 256 CUs), on sampled rows: the anchor frame, chunk edges and
-    random rows, every head."""
-    say("window longest first, sampled rows", D)
+    lengths on 256 CUs), on a seeded row of every query block of every head,
+    the anchor frame and chunk edges."""
+    say("window longest first, every tile", D)
     S, window = 24576, (1024, 5, 1, 1)
     inp = workloads.make_inputs(1, S, S, H, seed=85, D=D)
     d = DevInputs(inp)
@@ -183,7 +164,7 @@ def test_window_longest_first_sampled_rows(h3, D, H):
     torch.cuda.synchronize()
     F, C = window[0], window[1]
     edges = [0, F - 1, F, F + C * F - 1, F + C * F, S - C * F, S - 1]
-    rows = np.unique(np.concatenate([workloads.sample_rows(S, S, 64, 85), edges]))
+    rows = np.unique(np.concatenate([workloads.tile_rows(S, S, 128 if D == 256 else 256, 1, 85), edges]))
     if D == 128:
         want = ref(inp, window, rows=rows)
     else:

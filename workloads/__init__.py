@@ -193,17 +193,18 @@ def make_workload_inputs(wl: Workload, seed: int | None = None) -> Inputs:
                        D=wl.head_dim)
 
 
-def sample_rows(S: int, valid: int, count: int, seed: int, tile: int = 256) -> np.ndarray:
-    """A seeded, sorted subset of query rows for sampled parity at full size.
-    Always includes the first and last row, the last valid row and the rows
-    either side of every `tile` boundary up to `count` draws."""
-    rng = np.random.default_rng(10_000 + seed)
-    must = {0, S - 1, max(valid - 1, 0), min(valid, S - 1)}
-    for t in range(tile, S, tile * max(1, S // (tile * 8))):
-        must.update({t - 1, t})
-    extra = rng.choice(S, size=min(count, S), replace=False)
-    rows = np.array(sorted(set(int(r) for r in must) | set(int(r) for r in extra)), dtype=np.int64)
-    return rows
+def tile_rows(S: int, valid: int, tile: int, per_tile: int, seed: int) -> np.ndarray:
+    """A seeded, sorted set of query rows with `per_tile` distinct rows drawn
+    in every `tile`-row block below `valid` (fewer in a short last block),
+    plus the first and last rows, the last valid row and the first tail row.
+    An oracle that computes these rows for every head covers every (head,
+    query block) tile of a launch with `tile`-row query blocks."""
+    rng = np.random.default_rng(20_000 + seed)
+    rows = {0, S - 1, max(valid - 1, 0), min(valid, S - 1)}
+    for t0 in range(0, valid, tile):
+        n = min(tile, valid - t0)
+        rows.update(int(t0 + r) for r in rng.choice(n, size=min(per_tile, n), replace=False))
+    return np.array(sorted(rows), dtype=np.int64)
 
 
 # ------------------------------------------------- RMSNorm + indexed scale/shift

@@ -3,15 +3,25 @@
 
 One step = one pass of the whole hot path over one batch of synthetic input
 already resident in HBM: the fused Q/K RMSNorm + partial-rotary prologue
-(with the key-major copy of v) and the dense attention forward, through the
-C-ABI (h3attn_forward_stages). The workload is one GPU's 6-head share of the
-104,448-row packed sequence (B=1, S=104448, H=6, d=128, bf16).
+(with the key-major copy of v) and the attention forward, through the C-ABI
+(h3attn_forward_stages). The default workload is one GPU's 6-head share of
+the 104,448-row packed sequence (B=1, S=104448, H=6, d=128, bf16);
+--workload names the other configurations (tiny, mid, padded, cross), the
+attention variants and the RMSNorm + scale/shift shapes.
 
 Prints one JSON line. `value` is attention TFLOP/s over the whole step
-(4*S^2*d*H flop per step / step time). `roofline` is the attend stage alone
-(the attention kernel, plus the small kernel that merges tiles the schedule
-splits across workgroups), timed with HIP events on the stream it runs on. `cpu_baseline` is the
-fp64 oracle timed on this host on a bounded sample of the same workload.
+(valid-pair flops / mean step time of K back-to-back steps between two
+events). `roofline` is the attend stage alone (the attention kernel, plus
+the small kernel that merges tiles the schedule splits across workgroups),
+timed with HIP events on the stream it runs on, against the roofline that
+bounds it (the bf16 matrix cores, or HBM where the compulsory bytes take
+longer, as for cross-attention), with the other roofline beside it.
+`timing` adds the protocol of repeated runs with the 256 MB last-level cache
+flushed by a 512 MB write before each: median, min and coefficient of
+variation. `achievable` holds what the chip sustains in this run on the
+matrix-core, exponential and copy microbenchmarks, beside the nominal peaks.
+`cpu_baseline` is the fp64 oracle timed on this host on a bounded sample of
+the same workload.
 """
 from __future__ import annotations
 
@@ -29,8 +39,10 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 matrix-core peak
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 METRIC = "attention fwd TFLOP/s + % bf16 MFMA peak at S=104448,H=6,d=128 (1 GPU)"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_full_traffic.json")
-ATTN_SOURCE = os.path.join(ROOT, "video_dit_dense_amd", "csrc", "attn_fwd.hip")
+# The attention kernels' source: counter summaries under profiles/ are valid
+# for the hash of these files only.
+ATTN_SOURCES = [os.path.join(ROOT, "video_dit_dense_amd", "csrc", f) for f in ("attn_fwd.hip", "attn_sched.h")]
+FLUSH_BYTES = 512 << 20        # twice the 256 MB last-level cache (MALL)
 
 
 def log(*a):
@@ -38,21 +50,113 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
-    with open(ATTN_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in ATTN_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per attention launch from the committed rocprofv3 counter
-    summary, or None when it is missing or the kernel source changed since."""
+def traffic_file(name: str) -> str:
+    return os.path.join(ROOT, "profiles", f"attn_fwd_{name}_traffic.json")
+
+
+def measured_traffic(name: str):
+    """HBM bytes per attend stage of workload `name` from its committed
+    rocprofv3 counter summary, or None when it is missing or the kernel
+    source changed since the counters were taken."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(name)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
     if t.get("kernel_source_sha256") != kernel_source_hash():
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+def stats(xs) -> dict:
+    """Median, min, mean, max and coefficient of variation of timings (ms)."""
+    import numpy as np
+    a = np.asarray(xs, dtype=np.float64)
+    mean = float(a.mean())
+    return {"median": round(float(np.median(a)), 5), "min": round(float(a.min()), 5), "mean": round(mean, 5),
+            "max": round(float(a.max()), 5), "cv": round(float(a.std() / mean) if mean > 0 else 0.0, 5), "n": len(a)}
+
+
+def host_info() -> dict:
+    """Cores this process may run on and the host CPU model."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"host_cores": len(os.sched_getaffinity(0)), "cpu_model": model}
+
+
+def achievable(device="cuda:0") -> dict:
+    """What the chip sustains in this run on the microbenchmarks of
+    include/h3attn_micro.h: the bf16 matrix-core rate of 16x16x32
+    instructions on every SIMD and the shader clock under that load, the
+    v_exp_f32 rate (one exponential per attention score), and a streaming
+    copy's read + write bandwidth. Each is the median of a few launches
+    timed with events, after one untimed launch."""
+    import numpy as np
+    import torch
+    from video_dit_dense_amd import micro
+
+    def timed(fn, reps):
+        fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e-3
+
+    mb, mi = 1024, 100000            # 4 waves per SIMD, ~20 ms per launch
+    sink = torch.empty(mb * 256, dtype=torch.float32, device=device)
+    clocks = torch.empty((mb * 4, 2), dtype=torch.int64, device=device)
+    t_mfma = timed(lambda: micro.mfma_bf16(mb, mi, sink=sink, clocks=clocks), 5)
+    c = clocks.cpu().numpy().astype(np.float64)
+    clock_ghz = float(np.median(c[:, 0] / c[:, 1])) * micro.REFERENCE_CLOCK_HZ / 1e9
+    mfma_tflops = mb * 4 * mi * micro.MFMA_FLOP_PER_WAVE_ITER / t_mfma / 1e12
+    eb, ei = 2048, 1000
+    esink = torch.empty(eb * 256, dtype=torch.float32, device=device)
+    t_exp = timed(lambda: micro.exp(eb, ei, sink=esink), 3)
+    exp_rate = eb * 256 * ei * micro.EXP_PER_LANE_ITER / t_exp
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device=device)
+    dst = torch.empty_like(src)
+    t_copy = timed(lambda: micro.copy(src, dst), 10)
+    del src, dst
+    return {
+        "mfma_bf16_tflops": round(mfma_tflops, 1),
+        "mfma_bf16_frac_of_nominal": round(mfma_tflops / PEAK_BF16_TFLOPS, 4),
+        "clock_ghz_under_mfma_load": round(clock_ghz, 3),
+        "exp_per_s": float(f"{exp_rate:.4g}"),
+        "copy_gbs": round(2 * n / t_copy / 1e9, 1),
+        "copy_frac_of_nominal": round(2 * n / t_copy / 1e9 / PEAK_HBM_GBS, 4),
+        "method": "h3micro_mfma_bf16 (1024 workgroups x 4 waves x 100000 x 8 v_mfma_f32_16x16x32_bf16; clock = "
+                  "s_memtime cycles / s_memrealtime ticks x 100 MHz per wave, median), h3micro_exp (2048 x 256 lanes "
+                  "x 1000 x 8 v_exp_f32), h3micro_copy (1 GiB, read + write bytes); median of 5, 3 and 10 launches",
+    }
+
+
+def attention_bytes(wl) -> int:
+    """Compulsory HBM bytes of the attention (attend stage): the valid rows
+    of q and the valid keys and values read once, and o written in full
+    (rows past q_valid as zeros)."""
+    D = wl.head_dim
+    total = 0
+    for qv, kvv in wl.item_lengths():
+        total += 2 * D * (qv * wl.H + 2 * kvv * wl.kv_heads + wl.Sq * wl.H)
+    return total
 
 
 def window_keys_per_row(wl, rows):
@@ -124,6 +228,8 @@ def cpu_baseline(wl, inp, target_s: float):
         "value": flops / t / 1e12,
         "unit": "TFLOP/s",
         "cores": threads if threads is not None else len(os.sched_getaffinity(0)),
+        "cores_meaning": "BLAS threads of the one oracle process (its matrix products); the rest runs on one",
+        **host_info(),
         "kind": "oracle",
         "sample": f"fp64 NumPy oracle, item 0, head 0 of {wl.H}, {n} of {qv0} query rows against "
                   f"{'their causal prefix of ' if wl.causal else 'their frame window of ' if wl.window else 'all '}"
@@ -172,6 +278,7 @@ def ss_cpu_baseline(wl, inp, target_s: float):
         "value": row_bytes * n / t / 1e9,
         "unit": "GB/s",
         "cores": 1,
+        **host_info(),
         "kind": "oracle",
         "sample": f"NumPy bf16-chain oracle on the first {n} of {wl.B * wl.S} rows (D={wl.D}), {t:.1f} s wall; "
                   "bytes counted as the GPU figure counts them per row",
@@ -270,11 +377,17 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-baseline duration")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prologue-reps", type=int, default=20)
+    ap.add_argument("--flush-reps", type=int, default=None,
+                    help="repetitions timed with the last-level cache flushed before each (default: --steps; "
+                         "0 for profiler runs, so the kernel trace holds the back-to-back launches only)")
+    ap.add_argument("--no-achievable", action="store_true", help="skip the microbenchmarks of the achievable peaks")
     ap.add_argument("--only", choices=["all", "attention", "copy"], default="all",
                     help="for profiler runs: 'attention' runs one prepare stage, then only the attention "
                          "stage (warmup + steps launches); 'copy' runs a plain 1 GiB device copy "
                          "(warmup + steps times) to calibrate HBM byte counters")
     args = ap.parse_args()
+    if args.flush_reps is None:
+        args.flush_reps = args.steps
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (no sharding or "
@@ -351,6 +464,8 @@ def main() -> int:
     torch.cuda.synchronize()
     log(f"warmup done ({args.warmup} steps)")
 
+    # The timed steps: K back-to-back steps between two events, with events
+    # between the stages of each step as well.
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -372,6 +487,28 @@ def main() -> int:
     flops = step_flops(wl)
     log(f"timed {args.steps} steps: {ms_step:.3f} ms/step, attend stage {attn_avg:.3f} ms "
         f"(min {min(attn_ms):.3f}, max {max(attn_ms):.3f}), prepare {prep_avg:.3f} ms")
+
+    # Repetitions with the last-level cache flushed before each (a 512 MB
+    # write, outside the events), so no repetition finds its inputs in the
+    # 256 MB MALL that the previous one left there.
+    flushed = None
+    if args.flush_reps > 0:
+        scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda:0")
+        fev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.flush_reps)]
+        for i in range(args.flush_reps):
+            scratch.fill_(i & 0xFF)
+            fev[i][0].record()
+            stage(h3attn.STAGE_PREPARE)
+            fev[i][1].record()
+            stage(h3attn.STAGE_ATTEND)
+            fev[i][2].record()
+        torch.cuda.synchronize()
+        del scratch
+        flushed = {"step_ms": stats([e[0].elapsed_time(e[2]) for e in fev]),
+                   "prepare_ms": stats([e[0].elapsed_time(e[1]) for e in fev]),
+                   "attend_ms": stats([e[1].elapsed_time(e[2]) for e in fev])}
+        log(f"MALL-flushed repetitions: attend median {flushed['attend_ms']['median']:.4f} ms, "
+            f"min {flushed['attend_ms']['min']:.4f}, cv {flushed['attend_ms']['cv']:.4f}")
 
     # Stand-alone prologue (h3attn_qk_prologue, BSHD in, BSHD out), HBM
     # roofline; measured on the workloads whose q and k share head count and
@@ -402,9 +539,33 @@ def main() -> int:
             "bytes": wl.prologue_bytes(),
         }
 
-    achieved = flops / (attn_avg * 1e-3) / 1e12
-    # The committed counters were taken on the full workload only.
-    traffic = measured_traffic() if wl.name == "full" else None
+    # The attend stage against both rooflines; the one whose time at peak is
+    # longer bounds it.
+    abytes = attention_bytes(wl)
+    tflops = flops / (attn_avg * 1e-3) / 1e12
+    gbs = abytes / (attn_avg * 1e-3) / 1e9
+    mfma_roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                 "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "work": flops}
+    hbm_roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "work": abytes}
+    hbm_bound = abytes / (PEAK_HBM_GBS * 1e9) > flops / (PEAK_BF16_TFLOPS * 1e12)
+    main_roof, other_roof = (hbm_roof, mfma_roof) if hbm_bound else (mfma_roof, hbm_roof)
+    roofline = {
+        **{k: v for k, v in main_roof.items() if k != "work"},
+        "kernel": "attn_fwd_kernel + attn_merge_kernel (attend stage)",
+        "traffic": measured_traffic(wl.name),
+        "avg_ms": round(attn_avg, 4),
+        "work_per_launch": main_roof["work"],
+        "work_unit": "bytes (q, k, v valid rows read once, o written)" if hbm_bound else "flop (4*d per valid pair)",
+        "other": other_roof,
+    }
+    ach = None
+    if not args.no_achievable:
+        log("achievable peaks (microbenchmarks) ...")
+        ach = achievable()
+        roofline["frac_of_achievable"] = round(
+            (gbs / ach["copy_gbs"]) if hbm_bound else (tflops / ach["mfma_bf16_tflops"]), 4)
+        log(f"achievable: {ach}")
     result = {
         "metric": METRIC if wl.name == "full" else f"attention fwd TFLOP/s + % bf16 MFMA peak, {wl.name}: {wl.description}",
         "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
@@ -423,20 +584,19 @@ def main() -> int:
                         + (f"lengths={list(wl.lengths)} " if wl.lengths else f"q_valid={wl.q_valid} kv_valid={wl.kv_valid} ")
                         + f"causal={wl.causal} norm={wl.norm} rope={'96/128' if wl.rope else 'off'}",
             "flop_per_step": flops,
+            "nominal_flop_per_step": wl.nominal_flops() if not wl.window else None,
             "step": "prepare (RMSNorm+RoPE prologue, key-major v) + attention forward",
         },
-        "roofline": {
-            "bound": "mfma",
-            "kernel": "attn_fwd_kernel + attn_merge_kernel (attend stage)",
-            "achieved": round(achieved, 2),
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": traffic,
-            "avg_ms": round(attn_avg, 4),
+        "roofline": roofline,
+        "timing": {
+            "back_to_back": {"step_ms": stats([a + b for a, b in zip(prep_ms, attn_ms)]),
+                             "prepare_ms": stats(prep_ms), "attend_ms": stats(attn_ms)},
+            "mall_flushed": flushed,
+            "flush_bytes": FLUSH_BYTES if flushed else None,
         },
         "prologue": prologue,
         "prepare_stage_ms": round(prep_avg, 4),
+        "achievable": ach,
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle) ...")

@@ -294,3 +294,42 @@ def test_scale_shift_device_gate_without_gpu(lib):
     assert scale_shift(lib, w=0, idx=0) == DEVICE            # weight and index are optional
     assert scale_shift(lib, D=16384, w=0) == DEVICE
     assert scale_shift(lib, idx=6 * A + 4) == DEVICE         # 4-byte aligned index is enough
+
+
+# ------------------------------------------------------------- microbenchmarks
+
+MICRO_HEADER = os.path.join(ROOT, "include", "h3attn_micro.h")
+
+
+def test_micro_exports_every_declared_symbol(lib):
+    from video_dit_dense_amd import micro
+    text = re.sub(r"/\*.*?\*/", "", open(MICRO_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(h3micro_\w+)\s*\(", text)))
+    assert names == sorted(micro.SIGNATURES)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_micro_validation(lib):
+    from video_dit_dense_amd import micro
+    m = micro.load_library()
+    assert m.h3micro_mfma_bf16(1, 1, None, P(2 * A), None) == NULLP
+    assert m.h3micro_mfma_bf16(0, 1, P(A), P(2 * A), None) == SHAPE
+    assert m.h3micro_mfma_bf16(1, 0, P(A), P(2 * A), None) == SHAPE
+    assert m.h3micro_mfma_bf16(65537, 1, P(A), P(2 * A), None) == SHAPE
+    assert m.h3micro_mfma_bf16(65536, 1 << 17, P(A), P(2 * A), None) == SHAPE   # > 2^32 block-iterations
+    assert m.h3micro_mfma_bf16(4, 10, P(A), P(2 * A + 4), None) == ALIGN
+    assert m.h3micro_mfma_bf16(4, 10, P(A), P(A + 1024), None) == ALIAS           # sink is 4 KB
+    assert m.h3micro_exp(1, 1, None, None) == NULLP
+    assert m.h3micro_exp(1, 1 << 25, P(A), None) == SHAPE
+    assert m.h3micro_exp(1, 1, P(A + 2), None) == ALIGN
+    assert m.h3micro_copy(None, P(A), 16, None) == NULLP
+    assert m.h3micro_copy(P(A), P(2 * A), 0, None) == SHAPE
+    assert m.h3micro_copy(P(A), P(2 * A), 24, None) == SHAPE
+    assert m.h3micro_copy(P(A + 8), P(2 * A), 16, None) == ALIGN
+    assert m.h3micro_copy(P(A), P(A + 16), 32, None) == ALIAS
+    if not torch.cuda.is_available():   # valid arguments reach the device gate
+        assert m.h3micro_mfma_bf16(4, 10, P(A), P(2 * A), None) == DEVICE
+        assert m.h3micro_exp(4, 10, P(A), None) == DEVICE
+        assert m.h3micro_copy(P(A), P(2 * A), 16, None) == DEVICE
+

@@ -41,3 +41,29 @@ def test_multi_gpu_request_is_refused():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_config_work_matches_the_tabulated_figures():
+    """Valid-pair flops and compulsory attention bytes of the five
+    configurations, as tabulated for the measurement: Padded counts its
+    30720 valid rows and keys, Cross its 300 valid keys (and is the one
+    whose compulsory bytes outlast its flops at the nominal peaks)."""
+    W = workloads.WORKLOADS
+    assert bench.step_flops(W["padded"]) == 4.0 * 30720 * 30720 * 128 * 8
+    assert bench.step_flops(W["cross"]) == 4.0 * 32760 * 300 * 128 * 8
+    assert bench.attention_bytes(W["cross"]) == 2 * 128 * 8 * (32760 + 2 * 300 + 32760)
+    assert round(bench.attention_bytes(W["cross"]) / 1e6, 1) == 135.4
+    assert bench.attention_bytes(W["full"]) == 4 * 104448 * 6 * 256
+    assert bench.attention_bytes(W["padded"]) == 2 * 128 * 8 * (30720 + 2 * 30720 + 32768)
+    for name, wl in W.items():
+        t_mfma = bench.step_flops(wl) / (bench.PEAK_BF16_TFLOPS * 1e12)
+        t_hbm = bench.attention_bytes(wl) / (bench.PEAK_HBM_GBS * 1e9)
+        assert (t_hbm > t_mfma) == (name in ("cross", "tiny")), name
+
+
+def test_timing_stats():
+    s = bench.stats([1.0, 2.0, 3.0, 10.0])
+    assert s["median"] == 2.5 and s["min"] == 1.0 and s["max"] == 10.0 and s["n"] == 4
+    assert abs(s["cv"] - np.std([1, 2, 3, 10]) / 4.0) < 1e-4
+    h = bench.host_info()
+    assert h["host_cores"] == len(os.sched_getaffinity(0))

@@ -34,6 +34,12 @@ int check_device() {
   return kind == 1 ? H3ATTN_OK : H3ATTN_ERR_UNSUPPORTED_DEVICE;
 }
 
+}  // namespace
+
+int h3::check_gfx950() { return check_device(); }
+
+namespace {
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 struct Range {
@@ -196,8 +202,10 @@ bool uniform_schedule(const h3attn_forward_args* a) {
 
 // Validates every argument of a forward before anything is enqueued; on
 // success fills the resolved strides and the workspace layout.
+// With with_workspace false, the workspace and the device gate are not
+// checked (a caller that brings its own workspace checks them after).
 int check_forward(const h3attn_forward_args* a, size_t workspace_bytes, const void* workspace, uint32_t stages,
-                  int64_t qs[3], int64_t ks[3], int64_t vs[3], WorkspaceLayout* wl) {
+                  int64_t qs[3], int64_t ks[3], int64_t vs[3], WorkspaceLayout* wl, bool with_workspace = true) {
   if (!a) return H3ATTN_ERR_NULL_POINTER;
   if (!a->q || !a->k || !a->v || !a->o) return H3ATTN_ERR_NULL_POINTER;
   if (stages == 0 || stages > (H3ATTN_STAGE_PREPARE | H3ATTN_STAGE_ATTEND)) return H3ATTN_ERR_BAD_VALUE;
@@ -248,10 +256,12 @@ int check_forward(const h3attn_forward_args* a, size_t workspace_bytes, const vo
   if (!view_range(a->q, qs, B, Sq, Hq, D, &rq) || !view_range(a->k, ks, B, Sk, Hkv, D, &rk) ||
       !view_range(a->v, vs, B, Sk, Hkv, D, &rv))
     return H3ATTN_ERR_BAD_SHAPE;
-  if (!workspace || workspace_bytes < wl->total) return H3ATTN_ERR_WORKSPACE;
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return H3ATTN_ERR_BAD_ALIGNMENT;
+  if (with_workspace) {
+    if (!workspace || workspace_bytes < wl->total) return H3ATTN_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return H3ATTN_ERR_BAD_ALIGNMENT;
+  }
   const Range oq = range_of(a->o, obytes);
-  const Range ws = range_of(workspace, wl->total);
+  const Range ws = with_workspace ? range_of(workspace, wl->total) : Range{0, 0};
   if (overlap(oq, rq) || overlap(oq, rk) || overlap(oq, rv) || overlap(oq, ws)) return H3ATTN_ERR_ALIASING;
   if (overlap(ws, rq) || overlap(ws, rk) || overlap(ws, rv)) return H3ATTN_ERR_ALIASING;
   if (a->q_norm_w) {
@@ -271,7 +281,7 @@ int check_forward(const h3attn_forward_args* a, size_t workspace_bytes, const vo
     const Range gr = range_of(a->gate, (size_t)B * Sq * Hq * sizeof(uint16_t));
     if (overlap(ws, gr) || overlap(oq, gr)) return H3ATTN_ERR_ALIASING;
   }
-  return check_device();
+  return with_workspace ? check_device() : H3ATTN_OK;
 }
 
 int run_forward(const h3attn_forward_args* a, void* workspace, size_t workspace_bytes, uint32_t stages,
@@ -380,6 +390,30 @@ h3attn_forward_args dense_args(const uint16_t* q, const uint16_t* k, const uint1
 }
 
 }  // namespace
+
+int h3::check_dense_args(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, int32_t B,
+                         int32_t Sq, int32_t Sk, int32_t H, int32_t head_dim, const float* q_norm_w,
+                         const float* k_norm_w, float eps, const float* rope_cos, const float* rope_sin,
+                         int32_t rope_rows, int32_t q_valid, int32_t kv_valid, float softmax_scale,
+                         size_t* workspace_bytes) {
+  const h3attn_forward_args a = dense_args(q, k, v, o, B, Sq, Sk, H, head_dim, q_norm_w, k_norm_w, eps, rope_cos,
+                                           rope_sin, rope_rows, q_valid, kv_valid, softmax_scale);
+  int64_t qs[3], ks[3], vs[3];
+  WorkspaceLayout wl;
+  const int st = check_forward(&a, 0, nullptr, H3ATTN_STAGE_PREPARE | H3ATTN_STAGE_ATTEND, qs, ks, vs, &wl, false);
+  if (st == H3ATTN_OK) *workspace_bytes = wl.total;
+  return st;
+}
+
+int h3::forward_dense(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, int32_t B, int32_t Sq,
+                      int32_t Sk, int32_t H, int32_t head_dim, const float* q_norm_w, const float* k_norm_w, float eps,
+                      const float* rope_cos, const float* rope_sin, int32_t rope_rows, int32_t q_valid,
+                      int32_t kv_valid, float softmax_scale, void* workspace, size_t workspace_bytes, uint32_t stages,
+                      void* stream) {
+  const h3attn_forward_args a = dense_args(q, k, v, o, B, Sq, Sk, H, head_dim, q_norm_w, k_norm_w, eps, rope_cos,
+                                           rope_sin, rope_rows, q_valid, kv_valid, softmax_scale);
+  return run_forward(&a, workspace, workspace_bytes, stages, stream);
+}
 
 H3_API int h3attn_forward(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                           int32_t B, int32_t Sq, int32_t Sk, int32_t H, int32_t head_dim,

@@ -61,6 +61,24 @@ struct ProTensor {
   FastDiv div_h, div_s;    // set by launch_qk_prologue: division by the larger H and by S_out
 };
 
+// h3attn_forward_stages with every argument validated first (the C-ABI
+// entry points share it): returns an h3attn status code.
+int forward_dense(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, int32_t B, int32_t Sq,
+                  int32_t Sk, int32_t H, int32_t head_dim, const float* q_norm_w, const float* k_norm_w, float eps,
+                  const float* rope_cos, const float* rope_sin, int32_t rope_rows, int32_t q_valid, int32_t kv_valid,
+                  float softmax_scale, void* workspace, size_t workspace_bytes, uint32_t stages, void* stream);
+
+// Validates h3attn_forward's arguments other than the workspace, without
+// the device gate; on success sets the workspace bytes the call needs.
+int check_dense_args(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, int32_t B, int32_t Sq,
+                     int32_t Sk, int32_t H, int32_t head_dim, const float* q_norm_w, const float* k_norm_w,
+                     float eps, const float* rope_cos, const float* rope_sin, int32_t rope_rows, int32_t q_valid,
+                     int32_t kv_valid, float softmax_scale, size_t* workspace_bytes);
+
+// H3ATTN_OK when the current device is gfx950, else the h3attn status the
+// entry points return (UNSUPPORTED_DEVICE, or HIP when the query fails).
+int check_gfx950();
+
 // Enqueues the fused RMSNorm + partial-rotary prologue over up to two tensors
 // (t1 may have S_out == 0; the two may have different head counts).
 // rope_cos/rope_sin == nullptr disables rotary.

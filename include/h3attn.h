@@ -16,9 +16,10 @@
  *    caller-owned device pointer unless stated otherwise. q, k, v and o are
  *    dense, contiguous [B, S, H, 128] (BSHD, channel fastest).
  *  - Every device pointer must be 16-byte aligned.
- *  - The library allocates no device memory and keeps no pointer after a call
- *    returns. Work is enqueued asynchronously on `stream` (a hipStream_t
- *    passed as void*; NULL is the null stream).
+ *  - The library allocates no device memory at run time and keeps no caller
+ *    pointer after a call returns (h3attn_forward_noalloc's workspace is a
+ *    static array of the loaded library). Work is enqueued asynchronously on
+ *    `stream` (a hipStream_t passed as void*; NULL is the null stream).
  *  - All arguments are validated before anything is enqueued: when a call
  *    returns an error, nothing has run and no output was touched.
  *  - Device faults, like any asynchronous HIP error, surface at the caller's
@@ -147,6 +148,37 @@ int h3attn_forward(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint
                    const float* rope_cos, const float* rope_sin, int32_t rope_rows,
                    int32_t q_valid, int32_t kv_valid, float softmax_scale,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * h3attn_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation with the same kernels, with the workspace in a
+ * static device array of the library instead of a caller buffer. The call
+ * allocates nothing: no hipMalloc or hipFree and no allocating library
+ * routine. The array is H3ATTN_NOALLOC_SCRATCH_BYTES on every GPU that
+ * loads the library, held until the process ends; the first call on a
+ * device looks up its device address (hipGetSymbolAddress).
+ *
+ * Arguments, results and errors are those of h3attn_forward without
+ * workspace and workspace_bytes. Sizes whose workspace
+ * (h3attn_forward_workspace_bytes) exceeds H3ATTN_NOALLOC_SCRATCH_BYTES are
+ * rejected with H3ATTN_ERR_WORKSPACE before anything is enqueued: the tiny,
+ * mid (8192 x 8 heads, 122 MB) and cross-attention (32760 x 8 heads against
+ * 512 keys, 141 MB) shapes fit; padded (32768 x 8, 273 MB) and the full
+ * 104448 x 6 share (550 MB) do not.
+ *
+ * Every call on one GPU uses that GPU's one array, which keeps the last
+ * call's contents; nothing in it needs to start at zero (every call writes
+ * what it reads). Calls ordered on one stream are safe; calls that overlap
+ * on one GPU (different streams, or host threads without ordering between
+ * their launches) race on the array and their outputs are undefined.
+ */
+#define H3ATTN_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+int h3attn_forward_noalloc(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
+                           int32_t B, int32_t Sq, int32_t Sk, int32_t H, int32_t head_dim,
+                           const float* q_norm_w, const float* k_norm_w, float eps,
+                           const float* rope_cos, const float* rope_sin, int32_t rope_rows,
+                           int32_t q_valid, int32_t kv_valid, float softmax_scale, void* stream);
 
 /*
  * h3attn_forward split into its two stages, for callers that time them

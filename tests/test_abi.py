@@ -333,3 +333,35 @@ def test_micro_validation(lib):
         assert m.h3micro_exp(4, 10, P(A), None) == DEVICE
         assert m.h3micro_copy(P(A), P(2 * A), 16, None) == DEVICE
 
+
+# ---------------------------------------------------- no-allocation forward
+
+G = 1 << 30   # fake pointers 1 GiB apart, so full-size tensors do not overlap
+
+
+def noalloc(lib, q=A, k=2 * A, v=3 * A, o=4 * A, B=1, Sq=8, Sk=8, H=2, D=128, wq=5 * A, wk=5 * A + 512,
+            eps=1e-6, rc=6 * A, rs=7 * A, rows=8, qv=-1, kvv=-1, scale=0.0883):
+    return lib.h3attn_forward_noalloc(P(q), P(k), P(v), P(o), B, Sq, Sk, H, D, P(wq), P(wk), eps, P(rc), P(rs),
+                                      rows, qv, kvv, scale, None)
+
+
+def test_noalloc_validation(lib):
+    assert h3attn.NOALLOC_SCRATCH_BYTES == 256 << 20
+    assert noalloc(lib, q=0) == NULLP
+    assert noalloc(lib, D=64) == SHAPE
+    assert noalloc(lib, kvv=0) == SHAPE
+    assert noalloc(lib, scale=-1.0) == VALUE
+    assert noalloc(lib, o=4 * A + 8) == ALIGN
+    assert noalloc(lib, o=2 * A) == ALIAS
+    # Sizes whose workspace exceeds the static array: padded (273 MB) and the
+    # full 104448 x 6 share (550 MB) are rejected before anything else runs.
+    big = dict(q=G, k=2 * G, v=3 * G, o=4 * G, wq=5 * G, wk=5 * G + 512, rc=6 * G, rs=7 * G)
+    assert lib.h3attn_forward_workspace_bytes(1, 32768, 32768, 8) > h3attn.NOALLOC_SCRATCH_BYTES
+    assert noalloc(lib, B=1, Sq=32768, Sk=32768, H=8, rows=32768, **big) == WS
+    assert noalloc(lib, B=1, Sq=104448, Sk=104448, H=6, rows=104448, **big) == WS
+    # mid and cross fit
+    assert lib.h3attn_forward_workspace_bytes(1, 8192, 8192, 8) <= h3attn.NOALLOC_SCRATCH_BYTES
+    assert lib.h3attn_forward_workspace_bytes(1, 32760, 512, 8) <= h3attn.NOALLOC_SCRATCH_BYTES
+    if not torch.cuda.is_available():   # valid arguments reach the device gate
+        assert noalloc(lib) == DEVICE
+        assert noalloc(lib, B=1, Sq=8192, Sk=8192, H=8, rows=8192, **big) == DEVICE

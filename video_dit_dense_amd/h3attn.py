@@ -38,7 +38,13 @@ SIGNATURES = {
                                       _I, _I, _F, _P, ctypes.c_size_t, _P]),
     "h3attn_forward_stages": (ctypes.c_int, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _F, _P, _P, _I,
                                              _I, _I, _F, _P, ctypes.c_size_t, ctypes.c_uint32, _P]),
+    "h3attn_forward_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _F, _P, _P, _I,
+                                              _I, _I, _F, _P]),
 }
+
+# Bytes of the library's static workspace used by h3attn_forward_noalloc
+# (H3ATTN_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 256 << 20
 
 STAGE_PREPARE = 1
 STAGE_ATTEND = 2
@@ -279,6 +285,36 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                int(stages), _stream(q.device))
     _check(st, "h3attn_forward_ex")
     return o
+
+
+def forward_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                    w_q: torch.Tensor | None = None, w_k: torch.Tensor | None = None, eps: float = 1e-6,
+                    rope_cos: torch.Tensor | None = None, rope_sin: torch.Tensor | None = None,
+                    q_valid: int | None = None, kv_valid: int | None = None,
+                    scale: float | None = None) -> torch.Tensor:
+    """h3attn_forward_noalloc: the dense attention step of forward() with the
+    library's static workspace, for callers that cannot allocate. The caller
+    passes the output `out` [B, Sq, H, 128] bf16; nothing is allocated here
+    either. Sizes whose workspace exceeds NOALLOC_SCRATCH_BYTES raise
+    H3AttnError (ERR_WORKSPACE)."""
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        _check_bshd(name, t)
+    _check_f32("w_q", w_q, HEAD_DIM)
+    _check_f32("w_k", w_k, HEAD_DIM)
+    _check_f32("rope_cos", rope_cos)
+    _check_f32("rope_sin", rope_sin)
+    B, Sq, H, D = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != H or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("k and v must be [B, Sk, H, 128] and out like q")
+    rows = 0 if rope_cos is None else rope_cos.shape[0]
+    st = lib.h3attn_forward_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Sq, k.shape[1], H, D,
+                                    _ptr(w_q), _ptr(w_k), float(eps), _ptr(rope_cos), _ptr(rope_sin), rows,
+                                    -1 if q_valid is None else int(q_valid),
+                                    -1 if kv_valid is None else int(kv_valid),
+                                    1.0 / math.sqrt(D) if scale is None else float(scale), _stream(q.device))
+    _check(st, "h3attn_forward_noalloc")
+    return out
 
 
 def forward_ex_workspace_bytes(B: int, Sq: int, Sk: int, Hq: int, Hkv: int, causal: bool = False,

@@ -31,6 +31,11 @@ attention):
   visibility rule over frame-major rows (`window_visible`) and a logistic
   gate per (row, head) on the attention output.
 
+* The prologue fused with the destination-major Ulysses pack of one rank's
+  sequence shard (TeleFuser PR #37, "2.2 Fuse Q/K RMSNorm, RoPE, and
+  Ulysses Pack", step 4): `ulysses_pack`, rotary positions offset by the
+  shard's first global row, each tensor laid out destination rank first.
+
 Readings where the pages are silent (each pinned by a test in tests/):
 per-head norm with one [128] weight shared by all heads, eps inside the square
 root, weight multiplied as given; rotary frequency theta^(-2j/96) over the 96
@@ -102,19 +107,47 @@ def apply_rope(y: np.ndarray, positions, theta: float, rot_dim: int = ROT_DIM) -
 
 
 def qk_prologue(q_bits, k_bits, w_q, w_k, eps: float, theta: float | None,
-                norm: bool = True):
-    """The Q/K prologue of the attention step: RMSNorm, then rotary at
-    positions 0..S-1 when `theta` is given. Inputs are bf16 bit patterns
-    [B, S, H, 128]; outputs are exact float64 (no rounding)."""
+                norm: bool = True, row_offset: int = 0):
+    """The Q/K prologue of the attention step: RMSNorm, then rotary when
+    `theta` is given, row s at position row_offset + s (0..S-1 for a whole
+    sequence; a sequence shard starting at global row row_offset otherwise).
+    Inputs are bf16 bit patterns [B, S, H, 128]; outputs are exact float64
+    (no rounding)."""
     q = bf16_bits_to_f64(q_bits)
     k = bf16_bits_to_f64(k_bits)
     if norm:
         q = rms_norm(q, w_q, eps)
         k = rms_norm(k, w_k, eps)
     if theta is not None:
-        q = apply_rope(q, np.arange(q.shape[1]), theta)
-        k = apply_rope(k, np.arange(k.shape[1]), theta)
+        q = apply_rope(q, row_offset + np.arange(q.shape[1]), theta)
+        k = apply_rope(k, row_offset + np.arange(k.shape[1]), theta)
     return q, k
+
+
+def ulysses_pack(q_bits, k_bits, v_bits, w_q, w_k, eps: float, theta: float | None, P: int,
+                 row_offset: int = 0, norm: bool = True):
+    """The prologue fused with the destination-major Ulysses pack (TeleFuser
+    PR #37, "2.2 Fuse Q/K RMSNorm, RoPE, and Ulysses Pack", step 4, feeding
+    the all-to-all of section 2.1 that turns sequence shards into head
+    shards). One rank holds rows row_offset .. row_offset + S - 1 of the
+    sequence for all H heads (q, k, v bf16 bit patterns [B, S, H, 128]).
+    Destination rank p gets heads p*H/P .. (p+1)*H/P - 1 of them, so each
+    tensor is laid out with the destination outermost:
+
+      send[p, b, s, j, :] = x[b, s, p*(H/P) + j, :],  x = prologue(q) or prologue(k) or v
+
+    (the layout is a reading: the pages name the packing, not its layout).
+    Returns (q_send, k_send) as exact float64 [P, B, S, H/P, 128] and v_send
+    as the unchanged bf16 bit patterns in the same layout."""
+    B, S, H, D = np.shape(q_bits)
+    if P < 1 or H % P != 0:
+        raise ValueError("the heads must split evenly over the P ranks")
+    qn, kn = qk_prologue(q_bits, k_bits, w_q, w_k, eps, theta, norm=norm, row_offset=row_offset)
+
+    def pack(x):
+        return np.ascontiguousarray(np.asarray(x).reshape(B, S, P, H // P, D).transpose(2, 0, 1, 3, 4))
+
+    return pack(qn), pack(kn), pack(np.asarray(v_bits, dtype=np.uint16))
 
 
 def window_visible(rows, keys, F: int, C: int, R: int, A: int) -> np.ndarray:

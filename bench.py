@@ -364,6 +364,148 @@ def bench_scale_shift(args, wl) -> int:
     return 0
 
 
+PACK_SOURCES = [os.path.join(ROOT, "video_dit_dense_amd", "csrc", "qk_prologue.hip")]
+PACK_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qkv_pack_pack_shard_traffic.json")
+
+
+def pack_measured_traffic():
+    """HBM bytes per pack launch from the committed counter summary, or None
+    when it is missing or the kernel source changed since."""
+    try:
+        with open(PACK_TRAFFIC_FILE) as f:
+            t = json.load(f)
+        with open(PACK_SOURCES[0], "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    return t.get("hbm_bytes_per_launch") if t.get("kernel_source_sha256") == sha else None
+
+
+def pack_cpu_baseline(wl, inp, target_s: float):
+    """Time oracle.ulysses_pack (as it stands) on the shard's first rows, sized
+    to take about `target_s` seconds; GB/s with the GPU figure's per-row
+    byte accounting."""
+    import oracle
+
+    def run(n):
+        t0 = time.perf_counter()
+        oracle.ulysses_pack(inp.q[:, :n], inp.k[:, :n], inp.v[:, :n], inp.w_q, inp.w_k, wl.eps, wl.theta, wl.P,
+                            row_offset=wl.row_offset)
+        return time.perf_counter() - t0
+
+    n = min(wl.S_local, 256)
+    t = run(n)
+    n = int(min(wl.S_local, max(n, n * target_s / max(t, 1e-6))))
+    t = run(n)
+    row_bytes = wl.bytes() / wl.S_local
+    return {
+        "value": row_bytes * n / t / 1e9,
+        "unit": "GB/s",
+        "cores": 1,
+        **host_info(),
+        "kind": "oracle",
+        "sample": f"fp64 NumPy oracle (ulysses_pack) on the first {n} of {wl.S_local} shard rows x {wl.H} heads, "
+                  f"{t:.1f} s wall; bytes counted as the GPU figure counts them per row",
+        "seconds": t,
+    }
+
+
+def bench_pack(args, wl) -> int:
+    """Times h3attn_qkv_pack on one rank's shard: `warmup` untimed launches,
+    then `steps` back-to-back launches between two HIP events on the current
+    stream, rotating over two input/output sets (each ~1 GB, four times the
+    last-level cache) so every launch reads from and writes to HBM; then
+    flushed repetitions as for the attention."""
+    import numpy as np
+    import torch
+    import workloads
+    from video_dit_dense_amd import h3attn
+
+    log(f"workload {wl.name}: {wl.description}")
+    inp = workloads.make_pack_inputs(wl)
+
+    def dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to("cuda:0")
+
+    w_q = torch.from_numpy(inp.w_q).to("cuda:0")
+    w_k = torch.from_numpy(inp.w_k).to("cuda:0")
+    cos, sin = h3attn.rope_tables(wl.row_offset + wl.S_local, wl.theta)
+    n_sets = 2
+    ins = [(dev(inp.q), dev(inp.k), dev(inp.v)) for _ in range(n_sets)]
+    shape = (wl.P, wl.B, wl.S_local, wl.H // wl.P, 128)
+    outs = [tuple(torch.empty(shape, dtype=torch.bfloat16, device="cuda:0") for _ in range(3)) for _ in range(n_sets)]
+
+    def step(i):
+        q, k, v = ins[i % n_sets]
+        h3attn.qkv_pack(q, k, v, wl.P, wl.row_offset, w_q, w_k, wl.eps, cos, sin, out=outs[i % n_sets])
+
+    for i in range(args.warmup):
+        step(i)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(i)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    gbs = wl.bytes() / (ms * 1e-3) / 1e9
+    log(f"timed {args.steps} launches: {ms * 1e3:.1f} us each, {gbs:.0f} GB/s")
+    flushed = None
+    if args.flush_reps > 0:
+        scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda:0")
+        fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.flush_reps)]
+        for i, (a, b) in enumerate(fev):
+            scratch.fill_(i & 0xFF)
+            a.record()
+            step(i)
+            b.record()
+        torch.cuda.synchronize()
+        flushed = stats([a.elapsed_time(b) for a, b in fev])
+    result = {
+        "metric": f"Q/K prologue + destination-major Ulysses pack GB/s + % HBM peak, {wl.name}: {wl.description}",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{wl.name}: B={wl.B} S_local={wl.S_local} H={wl.H} P={wl.P} rank={wl.rank} "
+                        f"row_offset={wl.row_offset} eps={wl.eps} theta={wl.theta}",
+            "bytes_per_step": wl.bytes(),
+            "step": "one h3attn_qkv_pack launch (q, k RMSNorm + 96/128 rotary, v copy, destination-major layout)",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "qkv_pack_kernel",
+            "achieved": round(gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "traffic": pack_measured_traffic(),
+            "avg_us": round(ms * 1e3, 2),
+        },
+        "timing": {"mall_flushed_ms": flushed, "flush_bytes": FLUSH_BYTES if flushed else None},
+    }
+    if not args.no_achievable:
+        ach = achievable()
+        result["achievable"] = ach
+        result["roofline"]["frac_of_achievable"] = round(gbs / ach["copy_gbs"], 4)
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        result["cpu_baseline"] = pack_cpu_baseline(wl, inp, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -372,8 +514,10 @@ def main() -> int:
     ap.add_argument("--workload", default="full",
                     help="workload name (default: full); also the attention variants "
                          + ", ".join(sorted(__import__("workloads").VARIANT_WORKLOADS))
-                         + " and the RMSNorm + scale/shift shapes "
-                         + ", ".join(sorted(__import__("workloads").SCALE_SHIFT_WORKLOADS)))
+                         + ", the RMSNorm + scale/shift shapes "
+                         + ", ".join(sorted(__import__("workloads").SCALE_SHIFT_WORKLOADS))
+                         + " and the prologue + Ulysses pack shard "
+                         + ", ".join(sorted(__import__("workloads").PACK_WORKLOADS)))
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-baseline duration")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prologue-reps", type=int, default=20)
@@ -415,6 +559,8 @@ def main() -> int:
         return 0
     if args.workload in workloads.SCALE_SHIFT_WORKLOADS:
         return bench_scale_shift(args, workloads.SCALE_SHIFT_WORKLOADS[args.workload])
+    if args.workload in workloads.PACK_WORKLOADS:
+        return bench_pack(args, workloads.PACK_WORKLOADS[args.workload])
     all_wl = {**workloads.WORKLOADS, **workloads.VARIANT_WORKLOADS}
     wl = all_wl[args.workload]
     variant = args.workload in workloads.VARIANT_WORKLOADS

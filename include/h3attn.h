@@ -106,6 +106,44 @@ int h3attn_qk_prologue(const uint16_t* q_in, const uint16_t* k_in,
                        void* stream);
 
 /*
+ * The prologue fused with the destination-major Ulysses pack, for one rank
+ * of P that hold sequence shards (TeleFuser PR #37, section 2.2: Q/K
+ * RMSNorm, rounding, RoPE and destination-major Q/K/V packing in one
+ * kernel; section 2.1: the packed buffers feed the all-to-all that turns
+ * sequence shards into head shards). This rank holds rows row_offset ..
+ * row_offset + S_local - 1 of the sequence for all H heads; destination
+ * rank p takes heads p*H/P .. (p+1)*H/P - 1. With Hl = H / P:
+ *   q_send[p][b][s][j][:] = prologue(q)[b][s][p*Hl + j][:]
+ *   k_send[p][b][s][j][:] = prologue(k)[b][s][p*Hl + j][:]
+ *   v_send[p][b][s][j][:] = v[b][s][p*Hl + j][:]          (bit for bit)
+ * where prologue() is h3attn_qk_prologue's RMSNorm + rotary embedding, one
+ * bf16 rounding, with rotary table row row_offset + s serving local row s.
+ * Chunk p of each buffer (B * S_local * Hl * 128 elements, contiguous) is
+ * what rank p receives from this rank: after an equal-split all-to-all of
+ * the three buffers, rank p holds [P][B][S_local][Hl][128] in source-rank
+ * order, which for B = 1 is the whole sequence of its heads as dense BSHD
+ * [1, P * S_local, Hl, 128] (h3attn_forward's layout). The layout of the
+ * chunks is this library's reading; the pages name the packing only.
+ *
+ *   q, k, v: device bf16 [B, S_local, H, 128], dense, read only.
+ *   q_send, k_send, v_send: device bf16 [P, B, S_local, Hl, 128], dense,
+ *     disjoint from each other and from every input (no in-place form: the
+ *     layouts differ).
+ *   head_dim: 128.  P >= 1 and H a multiple of P.  row_offset >= 0.
+ *   q_norm_w, k_norm_w, eps, rope_cos, rope_sin: as for h3attn_qk_prologue
+ *     (both weights NULL: no norm; both tables NULL: no rotary); with the
+ *     rotary embedding, rope_rows >= row_offset + S_local.
+ *   B * S_local * H < 2^31.
+ * Errors: NULL_POINTER, BAD_SHAPE, BAD_ALIGNMENT, ALIASING, BAD_VALUE,
+ * UNSUPPORTED_DEVICE, HIP.
+ */
+int h3attn_qkv_pack(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                    uint16_t* q_send, uint16_t* k_send, uint16_t* v_send,
+                    int32_t B, int32_t S_local, int32_t H, int32_t P, int32_t head_dim, int32_t row_offset,
+                    const float* q_norm_w, const float* k_norm_w, float eps,
+                    const float* rope_cos, const float* rope_sin, int32_t rope_rows, void* stream);
+
+/*
  * Bytes of device workspace h3attn_forward needs for these sizes: the
  * normalised q and k and a key-major copy of v, each padded to whole tiles,
  * then room for the partial results of query tiles whose keys the forward

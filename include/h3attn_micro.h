@@ -55,7 +55,7 @@ int h3micro_exp(int32_t blocks, int32_t iters, float* sink, void* stream);
 /*
  * Device copy dst[0, bytes) = src[0, bytes) with 16-byte accesses,
  * non-temporal (streamed past the caches), one workgroup of 256 lanes per
- * 64 KB.
+ * 4 KB.
  *   src, dst: device, 16-byte aligned, disjoint; bytes a multiple of 16,
  *   1 <= bytes / 16 < 2^31.
  * Errors: NULL_POINTER, BAD_SHAPE, BAD_ALIGNMENT, ALIASING,

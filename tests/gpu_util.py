@@ -64,3 +64,19 @@ def assert_all_written(bits: np.ndarray, label: str) -> None:
     a prefilled output survived, so every tile of the launch was written."""
     bad = int(np.count_nonzero((bits & 0x7F80) == 0x7F80))
     assert bad == 0, f"{label}: {bad} of {bits.size} output elements unwritten or not finite"
+
+
+def assert_prologue_rounding(got_bits, ref, label):
+    """Every bf16 output within half an ulp of the exact fp64 value (one
+    correct rounding), plus 1e-6 absolute: the fp32 error where the
+    rotation a*cos - b*sin cancels to a small value; and all but 1e-4 of
+    them without that slack."""
+    import oracle
+    got = oracle.bf16_bits_to_f64(got_bits)
+    a = np.abs(ref)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    half_ulp = np.where(a > 0, np.exp2(np.maximum(e, -126.0) - 8.0), 0.0)
+    err = np.abs(got - ref)
+    assert np.all(np.isfinite(got)), label
+    assert np.all(err <= half_ulp * (1 + 1e-6) + 1e-6), (label, float((err - half_ulp).max()))
+    assert np.mean(err <= half_ulp * (1 + 1e-6)) > 0.9999, label

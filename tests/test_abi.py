@@ -365,3 +365,31 @@ def test_noalloc_validation(lib):
     if not torch.cuda.is_available():   # valid arguments reach the device gate
         assert noalloc(lib) == DEVICE
         assert noalloc(lib, B=1, Sq=8192, Sk=8192, H=8, rows=8192, **big) == DEVICE
+
+
+# ------------------------------------------------------ prologue + Ulysses pack
+
+def pack(lib, q=A, k=2 * A, v=3 * A, qs=4 * A, ks=5 * A, vs=6 * A, B=1, S=8, H=4, Pr=2, D=128, off=0,
+         wq=7 * A, wk=7 * A + 512, eps=1e-6, rc=8 * A, rs=9 * A, rows=8):
+    return lib.h3attn_qkv_pack(P(q), P(k), P(v), P(qs), P(ks), P(vs), B, S, H, Pr, D, off, P(wq), P(wk), eps,
+                               P(rc), P(rs), rows, None)
+
+
+def test_pack_validation(lib):
+    assert pack(lib, v=0) == NULLP
+    assert pack(lib, vs=0) == NULLP
+    assert pack(lib, wk=0) == NULLP
+    assert pack(lib, Pr=3) == SHAPE             # 4 heads over 3 ranks
+    assert pack(lib, Pr=0) == SHAPE
+    assert pack(lib, D=64) == SHAPE
+    assert pack(lib, off=-1) == SHAPE
+    assert pack(lib, off=1) == SHAPE            # table rows 8 < 1 + 8
+    assert pack(lib, eps=float("nan")) == VALUE
+    assert pack(lib, ks=5 * A + 8) == ALIGN
+    assert pack(lib, qs=A) == ALIAS             # no in-place form
+    assert pack(lib, vs=4 * A + 256) == ALIAS   # send buffers overlap
+    assert pack(lib, qs=8 * A) == ALIAS         # onto the cos table
+    if not torch.cuda.is_available():
+        assert pack(lib) == DEVICE
+        assert pack(lib, off=2, rows=10) == DEVICE
+        assert pack(lib, wq=0, wk=0, rc=0, rs=0, rows=0, off=1000) == DEVICE   # no rotary: any offset

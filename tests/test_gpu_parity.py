@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import workloads
-from gpu_util import DevInputs, check_metrics, say, to_dev, to_host, f32_dev
+from gpu_util import DevInputs, assert_prologue_rounding, check_metrics, say, to_dev, to_host, f32_dev
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -40,17 +40,6 @@ def run_forward(h3, wl_or_shape, inp, q_valid=None, kv_valid=None, norm=True, ro
                    q_valid=q_valid, kv_valid=kv_valid, scale=1 / math.sqrt(128))
     torch.cuda.synchronize()
     return to_host(o)
-
-
-def assert_prologue_rounding(got_bits, ref, label):
-    got = oracle.bf16_bits_to_f64(got_bits)
-    a = np.abs(ref)
-    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
-    half_ulp = np.where(a > 0, np.exp2(np.maximum(e, -126.0) - 8.0), 0.0)
-    err = np.abs(got - ref)
-    assert np.all(np.isfinite(got)), label
-    assert np.all(err <= half_ulp * (1 + 1e-6) + 1e-6), (label, float((err - half_ulp).max()))
-    assert np.mean(err <= half_ulp * (1 + 1e-6)) > 0.9999, label
 
 
 def check(metrics, label):

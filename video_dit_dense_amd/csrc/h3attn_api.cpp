@@ -188,6 +188,39 @@ H3_API int h3attn_qk_prologue(const uint16_t* q_in, const uint16_t* k_in, uint16
   return status_from(h3::launch_qk_prologue(tq, tk, B, eps, rope_cos, rope_sin, (hipStream_t)stream));
 }
 
+H3_API int h3attn_qkv_pack(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* q_send,
+                           uint16_t* k_send, uint16_t* v_send, int32_t B, int32_t S_local, int32_t H, int32_t P,
+                           int32_t head_dim, int32_t row_offset, const float* q_norm_w, const float* k_norm_w,
+                           float eps, const float* rope_cos, const float* rope_sin, int32_t rope_rows,
+                           void* stream) {
+  if (!q || !k || !v || !q_send || !k_send || !v_send) return H3ATTN_ERR_NULL_POINTER;
+  if (head_dim != h3::kHeadDim || B < 1 || S_local < 1 || H < 1 || P < 1 || H % P != 0 || row_offset < 0)
+    return H3ATTN_ERR_BAD_SHAPE;
+  const size_t bytes = bshd_bytes(B, S_local, H);
+  if (bytes == 0 || (int64_t)B * S_local * H >= (1ll << 31)) return H3ATTN_ERR_BAD_SHAPE;
+  if (rope_cos && (int64_t)rope_rows < (int64_t)row_offset + S_local) return H3ATTN_ERR_BAD_SHAPE;
+  if (int st = check_prologue_args(1, 1, q_norm_w, k_norm_w, eps, rope_cos, rope_sin, rope_rows)) return st;
+  const void* ptrs[6] = {q, k, v, q_send, k_send, v_send};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return H3ATTN_ERR_BAD_ALIGNMENT;
+  for (int i = 3; i < 6; ++i)
+    for (int j = 0; j < 6; ++j)
+      if (i != j && overlap(range_of(ptrs[i], bytes), range_of(ptrs[j], bytes))) return H3ATTN_ERR_ALIASING;
+  for (int i = 3; i < 6; ++i) {
+    const Range o = range_of(ptrs[i], bytes);
+    if (q_norm_w && (overlap(o, range_of(q_norm_w, 512)) || overlap(o, range_of(k_norm_w, 512))))
+      return H3ATTN_ERR_ALIASING;
+    if (rope_cos) {
+      const size_t tb = (size_t)rope_rows * h3::kRopePairs * sizeof(float);
+      if (overlap(o, range_of(rope_cos, tb)) || overlap(o, range_of(rope_sin, tb))) return H3ATTN_ERR_ALIASING;
+    }
+  }
+  if (int st = check_device()) return st;
+  h3::QkvPack t{q, k, v, q_send, k_send, v_send, q_norm_w, k_norm_w, eps, rope_cos, rope_sin,
+                B, S_local, H, P, row_offset};
+  return status_from(h3::launch_qkv_pack(t, (hipStream_t)stream));
+}
+
 H3_API size_t h3attn_forward_workspace_bytes(int32_t B, int32_t Sq, int32_t Sk, int32_t H) {
   WorkspaceLayout w;
   if (!workspace_layout(B, Sq, Sk, H, H, true, h3::kHeadDim, &w)) return 0;

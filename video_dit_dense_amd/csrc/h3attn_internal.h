@@ -104,6 +104,26 @@ hipError_t launch_qk_copy(const ProTensor& t0, const ProTensor& t1, int32_t B, i
 hipError_t launch_rope_tables(float* cos_out, float* sin_out, int32_t rows, double theta,
                               hipStream_t stream);
 
+// The prologue fused with the destination-major Ulysses pack of one rank's
+// sequence shard (dense [B, S, H, 128] q, k, v in; three [P][B][S][H/P][128]
+// send buffers out; rotary position row_offset + s; w_q == nullptr: no norm,
+// rope_cos == nullptr: no rotary).
+struct QkvPack {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* q_send;
+  uint16_t* k_send;
+  uint16_t* v_send;
+  const float* w_q;
+  const float* w_k;
+  float eps;
+  const float* rope_cos;
+  const float* rope_sin;
+  int32_t B, S, H, P, row_offset;
+};
+hipError_t launch_qkv_pack(const QkvPack& t, hipStream_t stream);
+
 struct AttnArgs {
   int32_t D;               // head dim: 64, 128 or 256
   const uint16_t* qw;      // [B*H][Sq_pad][D] scaled by softmax_scale*log2(e), rows >= q_valid zero

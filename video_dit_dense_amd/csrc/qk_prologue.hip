@@ -62,6 +62,70 @@ struct ProArgs {
   const float* sin;
 };
 
+// RMSNorm then the rotary embedding of one lane's 8 channels (8c .. 8c+7)
+// of a 128-channel row held by a 16-lane DPP row, in fp32; `scale`
+// multiplies the result (it rides on the normalisation factor). The rotated
+// lanes (c < 12) take their rotate-half partner from lane c+6 or c-6. Every
+// fused multiply-add is written out (fmaf) and no other product meets an
+// addition, so every kernel that inlines this computes the same bits.
+template <bool NORM, bool ROPE>
+__device__ __forceinline__ void norm_rope8(float (&f)[8], const float* w, float eps, float scale,
+                                           const float (&cs)[8], const float (&sn)[8], int c) {
+  if (NORM) {
+    const float4* wp = reinterpret_cast<const float4*>(w + c * 8);
+    const float4 w0 = wp[0], w1 = wp[1];
+    const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss = fmaf(f[i], f[i], ss);
+    ss = sum16(ss);
+    const float r = rsqrtf(fmaf(ss, 1.0f / 128.0f, eps)) * scale;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = f[i] * r * wv[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] *= scale;
+  }
+  if (ROPE) {
+    const bool rot = c < 12;
+    const float sgn = c < 6 ? -1.0f : 1.0f;   // own*cos + sgn*partner*sin
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float up = from_lane_plus6(f[i]), dn = from_lane_minus6(f[i]);
+      const float partner = c < 6 ? up : dn;
+      f[i] = rot ? fmaf(sgn * partner, sn[i], f[i] * cs[i]) : f[i];
+    }
+  }
+}
+
+// Loads the 8 rotary pairs of lane c (pairs 8(c mod 6) .. +7) for table row
+// `row`, or the identity rotation for the unrotated lanes and rows not loaded.
+__device__ __forceinline__ void rope_row8(const float* cos_t, const float* sin_t, int64_t row, int c, bool load,
+                                          float (&cs)[8], float (&sn)[8]) {
+  if (c < 12 && load) {
+    const int jb = (c < 6 ? c : c - 6) * 8;
+    const float4* cp = reinterpret_cast<const float4*>(cos_t + row * kRopePairs + jb);
+    const float4* sp = reinterpret_cast<const float4*>(sin_t + row * kRopePairs + jb);
+    const float4 ca = cp[0], cb = cp[1], sa = sp[0], sb = sp[1];
+    cs[0] = ca.x; cs[1] = ca.y; cs[2] = ca.z; cs[3] = ca.w; cs[4] = cb.x; cs[5] = cb.y; cs[6] = cb.z; cs[7] = cb.w;
+    sn[0] = sa.x; sn[1] = sa.y; sn[2] = sa.z; sn[3] = sa.w; sn[4] = sb.x; sn[5] = sb.y; sn[6] = sb.z; sn[7] = sb.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { cs[i] = 1.0f; sn[i] = 0.0f; }
+  }
+}
+
+__device__ __forceinline__ void unpack8(v4u_t x, float (&f)[8]) {
+  f[0] = bf16_lo(x[0]); f[1] = bf16_hi(x[0]);
+  f[2] = bf16_lo(x[1]); f[3] = bf16_hi(x[1]);
+  f[4] = bf16_lo(x[2]); f[5] = bf16_hi(x[2]);
+  f[6] = bf16_lo(x[3]); f[7] = bf16_hi(x[3]);
+}
+
+__device__ __forceinline__ v4u_t pack8(const float (&f)[8]) {
+  return v4u_t{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])};
+}
+
 constexpr int kProThreads = 256;
 constexpr int kUnitsPerThread = 1;
 constexpr int kUnitsPerBlock = kProThreads / 16 * kUnitsPerThread;
@@ -79,10 +143,6 @@ __global__ __launch_bounds__(kProThreads) void qk_prologue_kernel(ProArgs a) {
   const int32_t S_all = a.t0.S_out > a.t1.S_out ? a.t0.S_out : a.t1.S_out;
   const int64_t n_units = (int64_t)a.B * S_all * a.H;
   const int64_t first = (int64_t)blockIdx.x * kUnitsPerBlock + (threadIdx.x >> 4);
-  const bool rot = c < 12;
-  const float sgn = c < 6 ? -1.0f : 1.0f;            // own*cos + sgn*partner*sin
-  const int jb = (c < 6 ? c : c - 6) * 8;            // rotary pair index of this lane's first channel
-
 #pragma unroll
   for (int k = 0; k < kUnitsPerThread; ++k) {
     const int64_t u = first + (int64_t)k * (kProThreads / 16);
@@ -107,57 +167,81 @@ __global__ __launch_bounds__(kProThreads) void qk_prologue_kernel(ProArgs a) {
                      : v4u_t{0u, 0u, 0u, 0u};
     }
     float cs[8], sn[8];
-    if (ROPE) {
-      if (rot && (load[0] || load[1])) {
-        const float4* cp = reinterpret_cast<const float4*>(a.cos + (int64_t)s * kRopePairs + jb);
-        const float4* sp = reinterpret_cast<const float4*>(a.sin + (int64_t)s * kRopePairs + jb);
-        const float4 ca = cp[0], cb = cp[1], sa = sp[0], sb = sp[1];
-        cs[0] = ca.x; cs[1] = ca.y; cs[2] = ca.z; cs[3] = ca.w; cs[4] = cb.x; cs[5] = cb.y; cs[6] = cb.z; cs[7] = cb.w;
-        sn[0] = sa.x; sn[1] = sa.y; sn[2] = sa.z; sn[3] = sa.w; sn[4] = sb.x; sn[5] = sb.y; sn[6] = sb.z; sn[7] = sb.w;
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) { cs[i] = 1.0f; sn[i] = 0.0f; }
-      }
-    }
+    if (ROPE) rope_row8(a.cos, a.sin, s, c, load[0] || load[1], cs, sn);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const ProTensor& T = t ? a.t1 : a.t0;
       float f[8];
-      f[0] = bf16_lo(x[t][0]); f[1] = bf16_hi(x[t][0]);
-      f[2] = bf16_lo(x[t][1]); f[3] = bf16_hi(x[t][1]);
-      f[4] = bf16_lo(x[t][2]); f[5] = bf16_hi(x[t][2]);
-      f[6] = bf16_lo(x[t][3]); f[7] = bf16_hi(x[t][3]);
-      if (NORM) {
-        const float4* wp = reinterpret_cast<const float4*>(T.w + c * 8);
-        const float4 w0 = wp[0], w1 = wp[1];
-        const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-        float ss = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) ss = fmaf(f[i], f[i], ss);
-        ss = sum16(ss);
-        // The output scale rides on the normalisation factor (one fp32 multiply).
-        const float r = rsqrtf(ss * (1.0f / 128.0f) + a.eps) * T.out_scale;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) f[i] = f[i] * r * wv[i];
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) f[i] *= T.out_scale;
-      }
-      if (ROPE) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float up = from_lane_plus6(f[i]), dn = from_lane_minus6(f[i]);
-          const float partner = c < 6 ? up : dn;
-          f[i] = rot ? f[i] * cs[i] + sgn * partner * sn[i] : f[i];
-        }
-      }
+      unpack8(x[t], f);
+      norm_rope8<NORM, ROPE>(f, T.w, a.eps, T.out_scale, cs, sn, c);
       if (live[t]) {
         // Rows past S_valid are zero-filled, never computed from (absent) data.
         v4u_t r = v4u_t{0u, 0u, 0u, 0u};
-        if (load[t]) r = v4u_t{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])};
+        if (load[t]) r = pack8(f);
         __builtin_nontemporal_store(r, reinterpret_cast<v4u_t*>(T.out + b * T.out_sb + s * T.out_ss + h * T.out_sh + c * 8));
       }
     }
+  }
+}
+
+// The prologue fused with the destination-major Ulysses pack (TeleFuser PR
+// #37, section 2.2, step 4). One rank's sequence shard q, k, v [B, S, H, 128]
+// (dense BSHD) goes out as P destination chunks per tensor: head h = p Hl + j
+// of row (b, s) lands at chunk p, row ((b S + s) Hl + j), so each chunk is one
+// contiguous block that an equal-split all-to-all sends to rank p. q and k
+// take RMSNorm and the rotary embedding at global position row_offset + s,
+// rounded once to bf16; v is copied bit for bit. Same lane layout as the
+// prologue: 16 lanes per (b, s, h) row, the q, k and v rows at one (b, s, h)
+// in one thread group, so the rotary table row is read once for both.
+struct PackArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* q_send;
+  uint16_t* k_send;
+  uint16_t* v_send;
+  const float* w_q;
+  const float* w_k;
+  const float* cos;
+  const float* sin;
+  float eps;
+  int32_t B, S, H, Hl, row_offset;
+  int64_t chunk;           // elements per destination chunk: B * S * Hl * 128
+  FastDiv div_h, div_s, div_hl;
+};
+
+template <bool NORM, bool ROPE>
+__global__ __launch_bounds__(kProThreads) void qkv_pack_kernel(PackArgs a) {
+  const int c = threadIdx.x & 15;
+  const int64_t n_units = (int64_t)a.B * a.S * a.H;
+  const int64_t u = (int64_t)blockIdx.x * kUnitsPerBlock + (threadIdx.x >> 4);
+  const bool live = u < n_units;
+  const uint32_t uu = live ? (uint32_t)u : 0u;          // unit counts are < 2^31 (host-checked)
+  const uint32_t bs = a.div_h.div(uu);                  // b * S + s
+  const int h = (int)(uu - bs * (uint32_t)a.H);
+  const uint32_t b = a.div_s.div(bs);
+  const int s = (int)(bs - b * (uint32_t)a.S);
+  const uint32_t p = a.div_hl.div((uint32_t)h);
+  const int j = (int)((uint32_t)h - p * (uint32_t)a.Hl);
+  const int64_t in_off = (int64_t)uu * kHeadDim + c * 8;
+  const int64_t out_off = (int64_t)p * a.chunk + ((int64_t)bs * a.Hl + j) * kHeadDim + c * 8;
+  v4u_t xq = v4u_t{0u, 0u, 0u, 0u}, xk = xq, xv = xq;
+  if (live) {
+    xq = __builtin_nontemporal_load(reinterpret_cast<const v4u_t*>(a.q + in_off));
+    xk = __builtin_nontemporal_load(reinterpret_cast<const v4u_t*>(a.k + in_off));
+    xv = __builtin_nontemporal_load(reinterpret_cast<const v4u_t*>(a.v + in_off));
+  }
+  float cs[8], sn[8];
+  if (ROPE) rope_row8(a.cos, a.sin, (int64_t)a.row_offset + s, c, live, cs, sn);
+  float fq[8], fk[8];
+  unpack8(xq, fq);
+  unpack8(xk, fk);
+  norm_rope8<NORM, ROPE>(fq, a.w_q, a.eps, 1.0f, cs, sn, c);
+  norm_rope8<NORM, ROPE>(fk, a.w_k, a.eps, 1.0f, cs, sn, c);
+  if (live) {
+    __builtin_nontemporal_store(pack8(fq), reinterpret_cast<v4u_t*>(a.q_send + out_off));
+    __builtin_nontemporal_store(pack8(fk), reinterpret_cast<v4u_t*>(a.k_send + out_off));
+    __builtin_nontemporal_store(xv, reinterpret_cast<v4u_t*>(a.v_send + out_off));
   }
 }
 
@@ -261,6 +345,44 @@ hipError_t launch_qk_copy(const ProTensor& t0, const ProTensor& t1, int32_t B, i
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+hipError_t launch_qkv_pack(const QkvPack& t, hipStream_t stream) {
+  PackArgs a;
+  a.q = t.q;
+  a.k = t.k;
+  a.v = t.v;
+  a.q_send = t.q_send;
+  a.k_send = t.k_send;
+  a.v_send = t.v_send;
+  a.w_q = t.w_q;
+  a.w_k = t.w_k;
+  a.cos = t.rope_cos;
+  a.sin = t.rope_sin;
+  a.eps = t.eps;
+  a.B = t.B;
+  a.S = t.S;
+  a.H = t.H;
+  a.Hl = t.H / t.P;
+  a.row_offset = t.row_offset;
+  a.chunk = (int64_t)t.B * t.S * a.Hl * kHeadDim;
+  const int64_t units = (int64_t)t.B * t.S * t.H;
+  if (units >= (1ll << 31) || a.Hl < 1 || a.Hl * t.P != t.H) return hipErrorInvalidValue;
+  a.div_h = FastDiv::make((uint32_t)t.H);
+  a.div_s = FastDiv::make((uint32_t)t.S);
+  a.div_hl = FastDiv::make((uint32_t)a.Hl);
+  const dim3 grid((unsigned)((units + kUnitsPerBlock - 1) / kUnitsPerBlock));
+  const bool norm = t.w_q != nullptr;
+  const bool rope = t.rope_cos != nullptr;
+  if (norm && rope)
+    qkv_pack_kernel<true, true><<<grid, kProThreads, 0, stream>>>(a);
+  else if (norm)
+    qkv_pack_kernel<true, false><<<grid, kProThreads, 0, stream>>>(a);
+  else if (rope)
+    qkv_pack_kernel<false, true><<<grid, kProThreads, 0, stream>>>(a);
+  else
+    qkv_pack_kernel<false, false><<<grid, kProThreads, 0, stream>>>(a);
+  return hipGetLastError();
 }
 
 hipError_t launch_rope_tables(float* cos_out, float* sin_out, int32_t rows, double theta,

@@ -33,6 +33,8 @@ SIGNATURES = {
     "h3attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "h3attn_rope_tables": (ctypes.c_int, [_P, _P, _I, ctypes.c_double, _P]),
     "h3attn_qk_prologue": (ctypes.c_int, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _F, _P, _P, _I, _P]),
+    "h3attn_qkv_pack": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _F, _P, _P, _I,
+                                       _P]),
     "h3attn_forward_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "h3attn_forward": (ctypes.c_int, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _F, _P, _P, _I,
                                       _I, _I, _F, _P, ctypes.c_size_t, _P]),
@@ -177,6 +179,41 @@ def qk_prologue(q: torch.Tensor, k: torch.Tensor, w_q: torch.Tensor | None, w_k:
                                 _stream(q.device))
     _check(st, "h3attn_qk_prologue")
     return q_out, k_out
+
+
+def qkv_pack(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: int, row_offset: int = 0,
+             w_q: torch.Tensor | None = None, w_k: torch.Tensor | None = None, eps: float = 1e-6,
+             rope_cos: torch.Tensor | None = None, rope_sin: torch.Tensor | None = None,
+             out: tuple | None = None) -> tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """h3attn_qkv_pack: one rank's sequence shard q, k, v [B, S_local, H, 128]
+    (rows row_offset .. of the sequence) to destination-major send buffers
+    [P, B, S_local, H/P, 128], q and k through the RMSNorm + rotary prologue,
+    v copied. Returns (q_send, k_send, v_send); `out` may pass them in."""
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_bshd(name, t)
+    _check_f32("w_q", w_q, HEAD_DIM)
+    _check_f32("w_k", w_k, HEAD_DIM)
+    _check_f32("rope_cos", rope_cos)
+    _check_f32("rope_sin", rope_sin)
+    B, S, H, D = q.shape
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k and v must have the same shape")
+    if P < 1 or H % P:
+        raise ValueError("P must divide the head count")
+    shape = (P, B, S, H // P, D)
+    if out is None:
+        out = tuple(torch.empty(shape, dtype=q.dtype, device=q.device) for _ in range(3))
+    for name, t in zip(("q_send", "k_send", "v_send"), out):
+        if (t.device.type != "cuda" or t.dtype != torch.bfloat16 or tuple(t.shape) != shape
+                or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous bfloat16 GPU tensor {list(shape)}")
+    rows = 0 if rope_cos is None else rope_cos.shape[0]
+    st = lib.h3attn_qkv_pack(_ptr(q), _ptr(k), _ptr(v), *(_ptr(t) for t in out), B, S, H, int(P), D,
+                             int(row_offset), _ptr(w_q), _ptr(w_k), float(eps), _ptr(rope_cos), _ptr(rope_sin),
+                             rows, _stream(q.device))
+    _check(st, "h3attn_qkv_pack")
+    return out
 
 
 def workspace_bytes(B: int, Sq: int, Sk: int, H: int) -> int:

@@ -139,6 +139,48 @@ VARIANT_WORKLOADS = {
 }
 
 
+@dataclasses.dataclass(frozen=True)
+class PackWorkload:
+    """One rank's sequence shard for the prologue fused with the
+    destination-major Ulysses pack (TeleFuser PR #37, "2.2 Fuse Q/K RMSNorm,
+    RoPE, and Ulysses Pack"): q, k, v [B, S_local, H, 128] holding rows
+    rank*S_local .. of the sequence, packed for P ranks."""
+    name: str
+    B: int
+    S_local: int
+    H: int
+    P: int
+    rank: int
+    seed: int
+    eps: float = 1e-6
+    theta: float = 1e4
+    description: str = ""
+
+    @property
+    def row_offset(self) -> int:
+        return self.rank * self.S_local
+
+    def bytes(self) -> int:
+        """Compulsory HBM bytes: q, k, v read and their send buffers written
+        (bf16), the fp32 cos/sin table rows of the shard and the two fp32
+        weight vectors."""
+        return 3 * 2 * 2 * self.B * self.S_local * self.H * HEAD_DIM + 2 * 4 * 48 * self.S_local + 2 * 4 * HEAD_DIM
+
+
+PACK_WORKLOADS = {
+    # The 104448-row sequence over 8 ranks: each holds 13056 rows of all 48
+    # heads (the head count the 6-head-per-GPU share implies) and sends 6
+    # heads to every rank. Rank 3 exercises the rotary row offset.
+    "pack_shard": PackWorkload("pack_shard", 1, 13056, 48, 8, 3, 30,
+                               description="one rank's 13056-row shard of the 104448-row sequence, 48 heads, "
+                                           "packed for 8 ranks (6 heads each), rank 3"),
+}
+
+
+def make_pack_inputs(wl: PackWorkload) -> Inputs:
+    return make_inputs(wl.B, wl.S_local, wl.S_local, wl.H, wl.seed)
+
+
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 values to bfloat16 (round to nearest, ties to even) and
     return the 16-bit patterns. NaN inputs map to a quiet NaN."""

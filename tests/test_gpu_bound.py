@@ -1,0 +1,138 @@
+"""GPU parity of the two softmax paths of the head-dim-128 attention kernel.
+
+With H3's Q/K RMSNorm every score is bounded a priori by
+M = c * 128 * max|w_q| * max|w_k| * (1 + 2^-6) (c = softmax_scale *
+log2(e), scores in exp2 units). When M <= 60 the kernel uses M as a fixed
+softmax offset and drops the running maximum; otherwise (larger weights,
+or q and k not normalised) it keeps the online maximum with lazy rescaling.
+The other GPU tests use weights 1 + 0.1 N(0,1), so M is about 27 there and
+they run the bounded path. Here:
+- weights 1 + 0.1 N(0,1) with a weight of 4 on a channel whose input is
+  zero (channel 3 of q, the unrotated channel 100 of k) force the online
+  path (M about 265) on the shapes that stress it: split tiles, ragged
+  lengths, causal, frame window. The bound depends on max|w| alone, while a
+  weight on a zero channel changes no score; weights that really scale the
+  scores would grow every logit, and with it the error that bf16 q and k
+  carry, past the tolerance whatever the kernel does;
+- weights of exactly 1.875 (M = 58.3, the bounded path near its limit) with
+  every key anti-aligned to the query give scores of about -57.4, so every
+  probability is about 2^-116: the output must still be the mean of the
+  values, as the oracle says;
+- a largest weight just below and just above the limit gives results that
+  meet the oracle's bar on both sides.
+Bar: max-abs <= 2e-2, relative RMS <= 5e-3, per-row relative L2 <= 1e-2."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import DevInputs, check_metrics, say, to_dev, to_host
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+SCALE = 1 / math.sqrt(128)
+
+
+@pytest.fixture(scope="module")
+def h3():
+    from video_dit_dense_amd import h3attn
+    h3attn.load_library()
+    return h3attn
+
+
+def bound(w_q, w_k):
+    c = np.float32(SCALE * math.log2(math.e))
+    return float(c) * 128 * float(np.abs(w_q).max()) * float(np.abs(w_k).max()) * (1 + 1 / 64)
+
+
+def with_weights(inp, w_q, w_k):
+    return workloads.Inputs(inp.q, inp.k, inp.v, np.asarray(w_q, np.float32), np.asarray(w_k, np.float32))
+
+
+def run(h3, inp, rope=True, **kw):
+    d = DevInputs(inp)
+    S = max(inp.q.shape[1], inp.k.shape[1])
+    cos = sin = None
+    if rope:
+        cos, sin = h3.rope_tables(S)
+    gate = kw.pop("gate_bits", None)
+    o = h3.forward(d.q, d.k, d.v, d.w_q, d.w_k, 1e-6, cos, sin, scale=SCALE,
+                   gate=None if gate is None else to_dev(gate), **kw)
+    torch.cuda.synchronize()
+    return to_host(o)
+
+
+# (B, Sq, Sk, H, kwargs): 36 tiles split over the CUs with a masked last
+# step, ragged valid lengths, the causal mask, a frame window with a gate.
+ONLINE_CASES = [
+    (1, 3000, 3000, 3, {}),
+    (2, 1000, 777, 2, {"q_valid": 900, "kv_valid": 700}),
+    (1, 1500, 1500, 2, {"causal": True}),
+    (1, 2000, 2000, 2, {"window": (100, 3, 1, 2), "gate": True}),
+]
+
+
+@pytest.mark.parametrize("B,Sq,Sk,H,kw", ONLINE_CASES)
+def test_large_weights_take_the_online_path(h3, B, Sq, Sk, H, kw):
+    kw = dict(kw)
+    base = workloads.make_inputs(B, Sq, Sk, H, seed=900 + Sq)
+    w_q, w_k = base.w_q.copy(), base.w_k.copy()
+    w_q[3] = w_k[100] = 4.0
+    assert bound(w_q, w_k) > 60
+    q, k = base.q.copy(), base.k.copy()
+    q[..., 3] = 0
+    k[..., 100] = 0
+    inp = workloads.Inputs(q, k, base.v, w_q, w_k)
+    gate = workloads.make_gate(B, Sq, H, seed=Sq) if kw.pop("gate", False) else None
+    say("online path", B, Sq, Sk, H, kw, f"M={bound(w_q, w_k):.1f}")
+    got = run(h3, inp, gate_bits=gate, **kw)
+    ref = oracle.forward(inp.q, inp.k, inp.v, inp.w_q, inp.w_k, 1e-6, 1e4, SCALE, kw.get("q_valid"),
+                         kw.get("kv_valid"), causal=kw.get("causal", False), window=kw.get("window"),
+                         gate_bits=gate)
+    check_metrics(oracle.compare(got, ref), f"online path {B}x{Sq}x{Sk}x{H} {kw}")
+
+
+def test_anti_aligned_keys_at_the_bound_limit(h3):
+    """Every key is the negated query direction (scores about -57.4 against
+    the offset M = 58.3): the softmax is uniform, so o is the mean of the
+    valid values."""
+    B, S, H = 1, 1024, 2
+    rng = np.random.default_rng(910)
+    x = rng.standard_normal((B, 1, H, 128)).astype(np.float32)
+    q = workloads.f32_to_bf16_bits(np.broadcast_to(x, (B, S, H, 128)).copy())
+    k = workloads.f32_to_bf16_bits(np.broadcast_to(-x, (B, S, H, 128)).copy())
+    v = workloads.f32_to_bf16_bits(rng.standard_normal((B, S, H, 128)).astype(np.float32))
+    w = np.full(128, 1.875, np.float32)
+    assert 55 < bound(w, w) <= 60
+    inp = workloads.Inputs(q, k, v, w, w)
+    for kvv in (1024, 777, 1):
+        say("anti-aligned keys, kv_valid", kvv)
+        got = run(h3, inp, rope=False, kv_valid=kvv)
+        ref = oracle.forward(q, k, v, w, w, 1e-6, None, SCALE, None, kvv)
+        mean = oracle.bf16_bits_to_f64(v)[:, :kvv].mean(axis=1, keepdims=True)
+        assert np.allclose(ref, np.broadcast_to(mean, ref.shape), atol=1e-12)
+        check_metrics(oracle.compare(got, ref), f"anti-aligned kv_valid={kvv}")
+
+
+@pytest.mark.parametrize("w", [1.8125, 1.9375])
+def test_weights_either_side_of_the_limit(h3, w):
+    """Unit weights with the unrotated channel 127 (zero in q and k) at
+    1.8125 (M = 54.5, bounded) or 1.9375 (M = 62.2, online): the same
+    scores either way, on random inputs with a mix of aligned rows."""
+    B, S, H = 1, 2048, 2
+    base = workloads.make_inputs(B, S, S, H, seed=920)
+    ww = np.ones(128, np.float32)
+    ww[127] = w
+    say("weights", w, f"M={bound(ww, ww):.1f}")
+    q, k = base.q.copy(), base.k.copy()
+    k[:, ::7] = q[:, ::7]                 # some keys equal to their query row: large scores
+    q[..., 127] = 0
+    k[..., 127] = 0
+    inp = workloads.Inputs(q, k, base.v, ww, ww)
+    got = run(h3, inp)
+    ref = oracle.forward(inp.q, inp.k, inp.v, ww, ww, 1e-6, 1e4, SCALE)
+    check_metrics(oracle.compare(got, ref), f"weights {w}")

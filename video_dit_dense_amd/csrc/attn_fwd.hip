@@ -134,6 +134,10 @@ __device__ inline float sum_lane_pair(float x) {
 // row. The result o = O / l does not depend on m; bf16 rounding of p is
 // relative, so neither does its accuracy.
 constexpr float kRescaleLog2 = 8.0f;
+// The largest a priori score bound M (exp2 units) the fixed-offset softmax
+// takes: scores then lie in [-M, M], so exp2(s - M) >= 2^-120 stays a normal
+// fp32 and bf16 number and no row sum can underflow.
+constexpr float kBoundMax = 60.0f;
 constexpr int kSub = 32;                       // keys per sub-tile
 
 // Tiling by head dim D (64, 128 or 256). D <= 128: eight waves (256 query
@@ -591,31 +595,34 @@ void attn_fwd_kernel(AttnArgs a) {
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
   auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
 
+  // Sets this lane's scores of query tile qt in sub-tile x that its row does
+  // not see to -inf.
+  auto mask16 = [&](f32x4_t* sq, int x, int qt) __attribute__((always_inline)) {
+    int a_end = 0x7fffffff, w_lo = 0, w_hi = 0;
+    if constexpr (WIN) {
+      if (c_row[qt] >= 0) {
+        a_end = a.win_A * a.win_F;
+        w_lo = (a.win_A + a.win_C * max(c_row[qt] - a.win_R, 0)) * a.win_F;
+        w_hi = (a.win_A + a.win_C * min(c_row[qt] + a.win_R + 1, win_cap)) * a.win_F;
+      }
+    }
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = x * kSub + kt * 16 + g4 * 4 + r;
+        if constexpr (WIN) {
+          const bool hidden = (key > limq[qt]) | ((key >= a_end) & ((key < w_lo) | (key >= w_hi)));
+          sq[kt][r] = hidden ? -INFINITY : sq[kt][r];
+        } else {
+          if (key > limq[qt]) sq[kt][r] = -INFINITY;
+        }
+      }
+  };
   // This lane's maximum of the 8 scores of query tile qt in sub-tile x; with
   // MASK, keys its row does not see are set to -inf first.
   auto rowmax16 = [&](f32x4_t* sq, int x, int qt, auto mask) __attribute__((always_inline)) {
-    if constexpr (decltype(mask)::value) {
-      int a_end = 0x7fffffff, w_lo = 0, w_hi = 0;
-      if constexpr (WIN) {
-        if (c_row[qt] >= 0) {
-          a_end = a.win_A * a.win_F;
-          w_lo = (a.win_A + a.win_C * max(c_row[qt] - a.win_R, 0)) * a.win_F;
-          w_hi = (a.win_A + a.win_C * min(c_row[qt] + a.win_R + 1, win_cap)) * a.win_F;
-        }
-      }
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = x * kSub + kt * 16 + g4 * 4 + r;
-          if constexpr (WIN) {
-            const bool hidden = (key > limq[qt]) | ((key >= a_end) & ((key < w_lo) | (key >= w_hi)));
-            sq[kt][r] = hidden ? -INFINITY : sq[kt][r];
-          } else {
-            if (key > limq[qt]) sq[kt][r] = -INFINITY;
-          }
-        }
-    }
+    if constexpr (decltype(mask)::value) mask16(sq, x, qt);
     return fmaxf(max3(max3(sq[0][0], sq[0][1], sq[0][2]), sq[0][3], sq[1][0]), max3(sq[1][1], sq[1][2], sq[1][3]));
   };
   // Maximum / sum over the four lanes of a row (l, l^16, l^32, l^48).
@@ -629,6 +636,41 @@ void attn_fwd_kernel(AttnArgs a) {
     const auto sw = __builtin_amdgcn_permlane16_swap(u, u, false, false);
     return sum_lane_pair(__builtin_bit_cast(float, (uint32_t)sw[0]) + __builtin_bit_cast(float, (uint32_t)sw[1]));
   };
+  // A priori score bound. After H3's RMSNorm (weight w) a row y of 128
+  // channels has |y| <= sqrt(128) max|w| (r^2 sum x^2 = 128 ms / (ms + eps));
+  // the rotary embedding keeps |y|, q carries the factor c = scale log2(e)
+  // and the bf16 rounding grows a norm by at most 2^-8, so by Cauchy-Schwarz
+  // every score (exp2 units) lies in [-M, M] with
+  //   M = c * 128 * max|w_q| * max|w_k| * (1 + 2^-6)
+  // (2^-6 covers the roundings and the fp32 sums with room to spare). When
+  // M <= kBoundMax the fixed offset m = M serves every row: p = exp2(s - M)
+  // lies in [2^-2M, 1], finite and normal in fp32 and bf16, so the running
+  // maximum, its wave-wide check and the rescale drop out of every step and
+  // o = O / l is unchanged (softmax does not depend on the offset; bf16
+  // rounding of p is relative). Otherwise (unnormalised inputs, large
+  // weights) the online maximum runs as before.
+  bool bounded = false;
+  if (a.wq != nullptr) {
+    auto wmax = [&](const float* w) __attribute__((always_inline)) {
+      float x = fmaxf(fabsf(w[lane]), fabsf(w[lane + 64]));
+      x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false)));
+      x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false)));
+      x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false)));
+      x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false)));
+      return max_row16(x);
+    };
+    const float M = a.c_log2 * 128.0f * wmax(a.wq) * wmax(a.wk) * (1.0f + 1.0f / 64.0f);
+    const float Mu = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, M)));
+    bounded = Mu <= kBoundMax;
+    if (bounded) {
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        m_run[qt] = Mu;
+        msplat[qt] = f32x4_t{-Mu, -Mu, -Mu, -Mu};
+      }
+    }
+  }
+
   using NoMask = std::integral_constant<bool, false>;
   using Mask = std::integral_constant<bool, true>;
   // Scores arrive as s - m_run. If some row of the wave exceeds its offset by
@@ -737,90 +779,110 @@ void attn_fwd_kernel(AttnArgs a) {
     });
   };
 
-  // Prologue: scores of xb set each row's offset to its exact maximum.
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kRing - 4) * LDPS) : "memory");
-  __syncthreads();
-  f32x4_t s[2][2];
-  {
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) s[qt][kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int g = 0; g < 2 * NC; ++g) {
-      const bf16x8_t kfr = frag(g, 0, 0);
+  // The rest of the tile, for the online maximum (BND false) or the fixed
+  // bounded offset (BND true); the bounded steps have no row maximum, no
+  // wave-wide check and no rescale.
+  auto run_tile = [&](auto bnd) __attribute__((always_inline)) {
+  constexpr bool BND = decltype(bnd)::value;
+    // Prologue: scores of xb set each row's offset to its exact maximum
+    // (online path), or start from the fixed offset (bounded path).
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kRing - 4) * LDPS) : "memory");
+    __syncthreads();
+    f32x4_t s[2][2];
+    {
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt)
-        s[qt][g & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfr, qf[qt][g >> 1], s[qt][g & 1], 0, 0, 0);
-    }
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      m_run[qt] = max_row16(rowmax16(s[qt], xmap(xb), qt, Mask{}));
-      if constexpr (WIN) {
-        seen[qt] = m_run[qt] != -INFINITY;
-        if (!seen[qt]) m_run[qt] = 0.f;
+        for (int kt = 0; kt < 2; ++kt) s[qt][kt] = BND ? msplat[qt] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int g = 0; g < 2 * NC; ++g) {
+        const bf16x8_t kfr = frag(g, 0, 0);
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+          s[qt][g & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfr, qf[qt][g >> 1], s[qt][g & 1], 0, 0, 0);
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        s[qt][0][r] -= m_run[qt];
-        s[qt][1][r] -= m_run[qt];
-        msplat[qt][r] = -m_run[qt];
-      }
-    }
-    probs16(s, pf);
-  }
-  // The first fragments of the first X phase: K(xb+1), V(xb).
+      for (int qt = 0; qt < 2; ++qt) {
+        if constexpr (BND) {
+          mask16(s[qt], xmap(xb), qt);
+        } else {
+          m_run[qt] = max_row16(rowmax16(s[qt], xmap(xb), qt, Mask{}));
+          if constexpr (WIN) {
+            seen[qt] = m_run[qt] != -INFINITY;
+            if (!seen[qt]) m_run[qt] = 0.f;
+          }
 #pragma unroll
-  for (int g = 0; g < 4; ++g) fr[g] = frag(g, rslot(min(xb + 1, xe - 1)), 0);
+          for (int r = 0; r < 4; ++r) {
+            s[qt][0][r] -= m_run[qt];
+            s[qt][1][r] -= m_run[qt];
+            msplat[qt][r] = -m_run[qt];
+          }
+        }
+      }
+      probs16(s, pf);
+    }
+    // The first fragments of the first X phase: K(xb+1), V(xb).
+#pragma unroll
+    for (int g = 0; g < 4; ++g) fr[g] = frag(g, rslot(min(xb + 1, xe - 1)), 0);
 
-  // Step u: X = QK^T of u+1 and PV of u; Y = fragment reads of K(u+2) and
-  // V(u+1), the refill of the slot of u-1, the softmax of u+1 (as the
-  // 32x32 path).
-  // slot_vc, slot_kc: V(u) and K(u+1), read by this X phase; slot_vn,
-  // slot_kn: V(u+1) and K(u+2), whose first fragments the Y phase reads.
-  auto step = [&](int u, auto mask_next, auto slot_vn, auto slot_kn, auto slot_vc, auto slot_kc) __attribute__((always_inline)) {
-    fence();
+    // Step u: X = QK^T of u+1 and PV of u; Y = fragment reads of K(u+2) and
+    // V(u+1), the refill of the slot of u-1, the softmax of u+1 (as the
+    // 32x32 path).
+    // slot_vc, slot_kc: V(u) and K(u+1), read by this X phase; slot_vn,
+    // slot_kn: V(u+1) and K(u+2), whose first fragments the Y phase reads.
+    auto step = [&](int u, auto mask_next, auto slot_vn, auto slot_kn, auto slot_vc, auto slot_kc) __attribute__((always_inline)) {
+      fence();
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
+      for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) s[qt][kt] = msplat[qt];
-    xphase(s, slot_kc, slot_vc, true);
-    bar();
-    fence();
+        for (int kt = 0; kt < 2; ++kt) s[qt][kt] = msplat[qt];
+      xphase(s, slot_kc, slot_vc, true);
+      bar();
+      fence();
 #pragma unroll
-    for (int g = 0; g < 4; ++g) fr[g] = frag(g, slot_kn, slot_vn);
-    issue_loads(u - 1 + kRing);
-    float mx[2];
+      for (int g = 0; g < 4; ++g) fr[g] = frag(g, slot_kn, slot_vn);
+      issue_loads(u - 1 + kRing);
+      if constexpr (BND) {
+        if constexpr (decltype(mask_next)::value) {
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) mx[qt] = rowmax16(s[qt], xmap(u + 1), qt, mask_next);
-    maybe_rescale16(s, mx, mask_next);
-    probs16(s, pf);
-    fence();
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((kRing - 4) * LDPS) : "memory");
-    fence();
+          for (int qt = 0; qt < 2; ++qt) mask16(s[qt], xmap(u + 1), qt);
+        }
+      } else {
+        float mx[2];
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) mx[qt] = rowmax16(s[qt], xmap(u + 1), qt, mask_next);
+        maybe_rescale16(s, mx, mask_next);
+      }
+      probs16(s, pf);
+      fence();
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((kRing - 4) * LDPS) : "memory");
+      fence();
+    };
+
+    if (role) bar();
+    int u = xb;
+    for (; u + kRing <= min(xe - 2, x_mask - 1); u += kRing) {
+      for_each_index(std::make_integer_sequence<int, kRing>{}, [&](auto k) __attribute__((always_inline)) {
+        constexpr int K = decltype(k)::value;
+        step(u + K, NoMask{}, std::integral_constant<int, (K + 1) % kRing>{},
+             std::integral_constant<int, (K + 2) % kRing>{}, std::integral_constant<int, K % kRing>{},
+             std::integral_constant<int, (K + 1) % kRing>{});
+      });
+    }
+    for (; u < xe - 1; ++u) step(u, Mask{}, rslot(u + 1), rslot(min(u + 2, xe - 1)), rslot(u), rslot(u + 1));
+    // Last X phase: PV of the last sub-tile only.
+    {
+      const int vs = rslot(xe - 1);
+#pragma unroll
+      for (int ct = 0; ct < NT16; ++ct) {
+        const bf16x8_t vfr = frag(2 * NC + ct, 0, vs);
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) acc_mfma(qt, ct, vfr, pf[qt]);
+      }
+    }
   };
-
-  if (role) bar();
-  int u = xb;
-  for (; u + kRing <= min(xe - 2, x_mask - 1); u += kRing) {
-    for_each_index(std::make_integer_sequence<int, kRing>{}, [&](auto k) __attribute__((always_inline)) {
-      constexpr int K = decltype(k)::value;
-      step(u + K, NoMask{}, std::integral_constant<int, (K + 1) % kRing>{},
-           std::integral_constant<int, (K + 2) % kRing>{}, std::integral_constant<int, K % kRing>{},
-           std::integral_constant<int, (K + 1) % kRing>{});
-    });
-  }
-  for (; u < xe - 1; ++u) step(u, Mask{}, rslot(u + 1), rslot(min(u + 2, xe - 1)), rslot(u), rslot(u + 1));
-  // Last X phase: PV of the last sub-tile only.
-  {
-    const int vs = rslot(xe - 1);
-#pragma unroll
-    for (int ct = 0; ct < NT16; ++ct) {
-      const bf16x8_t vfr = frag(2 * NC + ct, 0, vs);
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) acc_mfma(qt, ct, vfr, pf[qt]);
-    }
-  }
+  if (bounded) run_tile(std::true_type{});
+  else run_tile(std::false_type{});
   if (!role) bar();
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 

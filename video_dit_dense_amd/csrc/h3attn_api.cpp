@@ -390,6 +390,9 @@ int run_forward(const h3attn_forward_args* a, void* workspace, size_t workspace_
     at.win_A = std::min(a->window_anchor_frames, n_frames);
   }
   at.gate = a->gate;
+  at.wq = a->q_norm_w;
+  at.wk = a->k_norm_w;
+  at.c_log2 = c;
   return status_from(h3::launch_attention(at, s));
 }
 

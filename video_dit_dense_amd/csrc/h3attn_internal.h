@@ -142,6 +142,13 @@ struct AttnArgs {
   // the chunks within win_R of their own.
   int32_t win_F, win_C, win_R, win_A;
   const uint16_t* gate;    // optional [B][Sq][H] bf16: o *= sigmoid(gate)
+  // H3's Q/K RMSNorm weights ([128] fp32 each, or nullptr when q and k were
+  // not normalised) and the factor c = softmax_scale * log2(e) the prologue
+  // multiplied q by: with them every score (in exp2 units) is bounded by
+  // c * 128 * max|w_q| * max|w_k| (see attn_fwd.hip).
+  const float* wq;
+  const float* wk;
+  float c_log2;
   // Schedule, filled in by launch_attention. Uniform mode (no causal mask,
   // no per-item lengths): valid tiles (query block below q_valid) are
   // numbered g = (b*H + h) * nqv + query block; tiles g < n_whole run whole,

@@ -57,12 +57,15 @@ def test_workspace_bytes(lib):
     # with 256-row tiles and 32-key steps; a record is (64 + 4) x 512 floats
     # (the accumulators, then two row offsets and two partial sums per lane:
     # head dim 128 holds each wave's rows as two 16-row tiles).
+    # Then the key-norm maxima: one fp32 per 4096 padded keys of each
+    # (b, head), padded to 256 bytes.
     rec = (64 + 4) * 512 * 4
-    assert lib.h3attn_forward_workspace_bytes(1, 104448, 104448, 6) == 6 * 104448 * 256 * 3 + 2 * 256 * rec
+    kn = lambda n: (n * 4 + 255) // 256 * 256   # noqa: E731
+    assert lib.h3attn_forward_workspace_bytes(1, 104448, 104448, 6) == 6 * 104448 * 256 * 3 + 2 * 256 * rec + kn(6 * 26)
     # 6 heads x 4 tiles x 10 steps = 240 steps -> 15 blocks
-    assert lib.h3attn_forward_workspace_bytes(2, 1000, 300, 3) == 6 * (1024 + 2 * 512) * 256 + 2 * 15 * rec
+    assert lib.h3attn_forward_workspace_bytes(2, 1000, 300, 3) == 6 * (1024 + 2 * 512) * 256 + 2 * 15 * rec + kn(6)
     # 1 tile x 1 step: no split blocks
-    assert lib.h3attn_forward_workspace_bytes(1, 1, 1, 1) == 3 * 256 * 256
+    assert lib.h3attn_forward_workspace_bytes(1, 1, 1, 1) == 3 * 256 * 256 + kn(1)
     assert lib.h3attn_forward_workspace_bytes(0, 1, 1, 1) == 0
     assert lib.h3attn_forward_workspace_bytes(1, -5, 1, 1) == 0
 
@@ -190,20 +193,25 @@ def fwd_ex(lib, stages=3, ws=16 * A, wsb=None, **kw):
 def test_forward_ex_workspace_bytes(lib):
     # q rows for Hq heads, k and v^T rows for Hkv heads, partial records only
     # for the uniform schedule (no causal mask, no per-item lengths); at head
-    # dim 128 a record holds two row offsets and two partial sums per lane
+    # dim 128 a record holds two row offsets and two partial sums per lane;
+    # then the key-norm maxima, one fp32 per 4096 padded keys of each
+    # (b, kv head), padded to 256 bytes
     rec = (64 + 4) * 512 * 4
+    kn = lambda n: (n * 4 + 255) // 256 * 256   # noqa: E731
     assert h3attn.forward_ex_workspace_bytes(1, 104448, 104448, 6, 2) == \
-        (6 + 2 * 2) * 104448 * 256 + 2 * 256 * rec
-    assert h3attn.forward_ex_workspace_bytes(1, 104448, 104448, 6, 2, causal=True) == (6 + 2 * 2) * 104448 * 256
+        (6 + 2 * 2) * 104448 * 256 + 2 * 256 * rec + kn(2 * 26)
+    assert h3attn.forward_ex_workspace_bytes(1, 104448, 104448, 6, 2, causal=True) == \
+        (6 + 2 * 2) * 104448 * 256 + kn(2 * 26)
     assert h3attn.forward_ex_workspace_bytes(2, 1000, 300, 4, 1, per_item_lengths=True) == \
-        2 * (4 * 1024 + 2 * 1 * 512) * 256
-    assert h3attn.forward_ex_workspace_bytes(1, 104448, 104448, 6, 6, window=True) == 3 * 6 * 104448 * 256
+        2 * (4 * 1024 + 2 * 1 * 512) * 256 + kn(2)
+    assert h3attn.forward_ex_workspace_bytes(1, 104448, 104448, 6, 6, window=True) == \
+        3 * 6 * 104448 * 256 + kn(6 * 26)
     # rows of 2 * head_dim bytes; split records of (head_dim / 2 + 2) floats per lane of 512 (256 at 256)
     # at head dims 64 and 256
     assert h3attn.forward_ex_workspace_bytes(1, 4096, 4096, 8, 8, head_dim=64) == \
-        3 * 8 * 4096 * 128 + 2 * 256 * (32 + 2) * 512 * 4
+        3 * 8 * 4096 * 128 + 2 * 256 * (32 + 2) * 512 * 4 + kn(8)
     assert h3attn.forward_ex_workspace_bytes(1, 4096, 4096, 8, 8, head_dim=256) == \
-        3 * 8 * 4096 * 512 + 2 * 256 * (128 + 2) * 256 * 4
+        3 * 8 * 4096 * 512 + 2 * 256 * (128 + 2) * 256 * 4 + kn(8)
     assert h3attn.forward_ex_workspace_bytes(1, 8, 8, 4, 4, head_dim=96) == 0
     assert h3attn.forward_ex_workspace_bytes(1, 8, 8, 6, 4) == 0      # 6 heads do not group into 4
     assert h3attn.forward_ex_workspace_bytes(1, 8, 8, 4, 0) == 0

@@ -136,3 +136,31 @@ def test_weights_either_side_of_the_limit(h3, w):
     got = run(h3, inp)
     ref = oracle.forward(inp.q, inp.k, inp.v, ww, ww, 1e-6, 1e4, SCALE)
     check_metrics(oracle.compare(got, ref), f"weights {w}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_data_bound_mixes_paths_within_a_workgroup(h3, D):
+    """Without the norm the bound is |q_i| max_j |k_j| per row, decided per
+    wave. Key 7 gets a norm above 100 on channel 5, which every query has at
+    zero (its scores stay those of a plain key), so max_j |k_j| > 100; the
+    query rows of every other 32-row wave are scaled by 1/16 (exactly), so
+    those waves have m_i below the limit and run the bounded path while
+    their neighbours in the same workgroup run the online maximum."""
+    B, S, H = 1, 2048, 2
+    base = workloads.make_inputs(B, S, S, H, seed=930 + D, D=D)
+    q = base.q.copy()
+    k = base.k.copy()
+    q[..., 5] = 0
+    k[:, 7, :, 5] = workloads.f32_to_bf16_bits(np.float32(100.0))
+    rows = np.arange(S)
+    small = (rows // 32) % 2 == 1
+    qf = workloads.bf16_bits_to_f32(q)
+    qf[:, small] *= np.float32(1 / 16)
+    q = workloads.f32_to_bf16_bits(qf)
+    inp = workloads.Inputs(q, k, base.v, base.w_q, base.w_k)
+    d = DevInputs(inp)
+    say("data bound, mixed waves", D)
+    o = h3.forward(d.q, d.k, d.v, scale=1 / math.sqrt(D))
+    torch.cuda.synchronize()
+    ref = oracle.forward(inp.q, inp.k, inp.v, None, None, 1e-6, None, 1 / math.sqrt(D), norm=False)
+    check_metrics(oracle.compare(to_host(o), ref), f"D={D} mixed bounded/online waves")

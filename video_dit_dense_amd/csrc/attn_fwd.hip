@@ -128,6 +128,35 @@ __device__ inline float sum_lane_pair(float x) {
   return __builtin_bit_cast(float, (uint32_t)sw[0]) + __builtin_bit_cast(float, (uint32_t)sw[1]);
 }
 
+// Maximum of x over the whole wave, in every lane: within each 16-lane row
+// by DPP (quad_perm [1,0,3,2], [2,3,0,1], row_half_mirror, row_mirror), then
+// over the four rows with v_permlane16_swap and v_permlane32_swap.
+__device__ inline float wave_max(float x) {
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false)));
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false)));
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false)));
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false)));
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto sw = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return max_lane_pair(fmaxf(__builtin_bit_cast(float, (uint32_t)sw[0]), __builtin_bit_cast(float, (uint32_t)sw[1])));
+}
+
+// The largest prepared key norm of key/value head bh_kv (the maximum over
+// its chunks' maxima), in every lane of the wave.
+__device__ inline float key_norm_max(const AttnArgs& a, int bh_kv) {
+  const float* kn = a.knorm + (int64_t)bh_kv * a.kn_chunks;
+  float x = 0.f;
+  for (int i = (int)(threadIdx.x & 63); i < a.kn_chunks; i += 64) x = fmaxf(x, kn[i]);
+  return wave_max(x);
+}
+
+// Sum of squares of bf16 values, in fp32.
+__device__ inline float sum_sq(const bf16x8_t& v, float ss) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ss = fmaf((float)v[e], (float)v[e], ss);
+  return ss;
+}
+
 // Lazy rescaling: the running max m used in p = exp2(s - m) is only raised
 // when a score exceeds it by more than 2^kRescaleLog2 (in the exp2 domain), so
 // p <= 2^8 and the fp32 accumulator is rescaled only a handful of times per
@@ -138,6 +167,10 @@ constexpr float kRescaleLog2 = 8.0f;
 // takes: scores then lie in [-M, M], so exp2(s - M) >= 2^-120 stays a normal
 // fp32 and bf16 number and no row sum can underflow.
 constexpr float kBoundMax = 60.0f;
+// Relative slack of the data-derived bound |q_i| max_j |k_j|: the fp32 sums
+// of squares and square roots of bf16 rows and the matrix core's fp32
+// accumulation of the score each err by far less.
+constexpr float kBoundSlack = 1.0f + 1.0f / 1024.0f;
 constexpr int kSub = 32;                       // keys per sub-tile
 
 // Tiling by head dim D (64, 128 or 256). D <= 128: eight waves (256 query
@@ -649,15 +682,14 @@ void attn_fwd_kernel(AttnArgs a) {
   // o = O / l is unchanged (softmax does not depend on the offset; bf16
   // rounding of p is relative). Otherwise (unnormalised inputs, large
   // weights) the online maximum runs as before.
+  // Without the norm, the bound comes from the data: row i's scores lie in
+  // [-m_i, m_i] with m_i = |q_i| max_j |k_j| (Cauchy-Schwarz on the bf16
+  // rows the matrix core reads; q carries c already), each row taking its own
+  // m_i as its offset when every row of the wave has m_i <= kBoundMax.
   bool bounded = false;
   if (a.wq != nullptr) {
     auto wmax = [&](const float* w) __attribute__((always_inline)) {
-      float x = fmaxf(fabsf(w[lane]), fabsf(w[lane + 64]));
-      x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false)));
-      x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false)));
-      x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false)));
-      x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false)));
-      return max_row16(x);
+      return wave_max(fmaxf(fabsf(w[lane]), fabsf(w[lane + 64])));
     };
     const float M = a.c_log2 * 128.0f * wmax(a.wq) * wmax(a.wk) * (1.0f + 1.0f / 64.0f);
     const float Mu = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, M)));
@@ -667,6 +699,24 @@ void attn_fwd_kernel(AttnArgs a) {
       for (int qt = 0; qt < 2; ++qt) {
         m_run[qt] = Mu;
         msplat[qt] = f32x4_t{-Mu, -Mu, -Mu, -Mu};
+      }
+    }
+  } else if (a.knorm != nullptr) {
+    const float kmax = key_norm_max(a, bh_kv);
+    float m[2];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      float ss = 0.f;
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) ss = sum_sq(qf[qt][cc], ss);
+      m[qt] = sqrtf(sum_row16(ss)) * kmax * kBoundSlack;
+    }
+    bounded = __builtin_amdgcn_ballot_w64(!(m[0] <= kBoundMax) | !(m[1] <= kBoundMax)) == 0;
+    if (bounded) {
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        m_run[qt] = m[qt];
+        msplat[qt] = f32x4_t{-m[qt], -m[qt], -m[qt], -m[qt]};
       }
     }
   }
@@ -952,36 +1002,56 @@ void attn_fwd_kernel(AttnArgs a) {
   bool seen = true;        // the row has met a visible key (m_run is its offset)
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // Row max of this lane's 16 scores of sub-tile x; with MASK, keys the
-  // lane's row does not see (past its last visible key, or outside its frame
-  // window) are set to -inf first (a no-op in sub-tiles without such keys).
-  auto rowmax = [&](f32x16_t& s, int x, auto mask) {
-    if constexpr (decltype(mask)::value) {
-      // Window rows see keys below a_end (the anchor frames) and in
-      // [w_lo, w_hi) (the chunks within R of theirs); dense rows see all.
-      int a_end = 0x7fffffff, w_lo = 0, w_hi = 0;
-      if constexpr (WIN) {
-        if (c_row >= 0) {
-          // The launcher clamps F, C, R, A to the sequence (which is below
-          // 2^28 rows), so these products stay below 2^31.
-          a_end = a.win_A * a.win_F;
-          w_lo = (a.win_A + a.win_C * max(c_row - a.win_R, 0)) * a.win_F;
-          w_hi = (a.win_A + a.win_C * min(c_row + a.win_R + 1, win_cap)) * a.win_F;
-        }
-      }
+  // The a priori bound of the ping-pong paths (head dim 64; H3's norm is
+  // defined on 128 channels only, so the bound comes from the data): row
+  // i's scores lie in [-m_i, m_i], m_i = |q_i| max_j |k_j| (the lane pair
+  // holds the row's channels in qf); when every row of the wave has m_i <=
+  // kBoundMax, m_i is its fixed offset and the steps keep no row maximum.
+  bool bounded = false;
+  if constexpr (!G::kPipe) {
+    if (a.knorm != nullptr) {
+      float ss = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = x * kSub + (r >> 2) * 8 + g * 4 + (r & 3);
-        if constexpr (WIN) {
-          // Bitwise, not short-circuit, so it compiles to compares and one
-          // select instead of branches.
-          const bool hidden = (key > lim) | ((key >= a_end) & ((key < w_lo) | (key >= w_hi)));
-          s[r] = hidden ? -INFINITY : s[r];
-        } else {
-          if (key > lim) s[r] = -INFINITY;
-        }
+      for (int kk = 0; kk < NF; ++kk) ss = sum_sq(qf[kk], ss);
+      const float m = sqrtf(sum_lane_pair(ss)) * key_norm_max(a, bh_kv) * kBoundSlack;
+      bounded = __builtin_amdgcn_ballot_w64(!(m <= kBoundMax)) == 0;
+      if (bounded) m_run = m;
+    }
+  }
+
+  // Sets this lane's scores of sub-tile x that its row does not see (past
+  // its last visible key, or outside its frame window) to -inf (a no-op in
+  // sub-tiles without such keys).
+  auto mask_scores = [&](f32x16_t& s, int x) {
+    // Window rows see keys below a_end (the anchor frames) and in
+    // [w_lo, w_hi) (the chunks within R of theirs); dense rows see all.
+    int a_end = 0x7fffffff, w_lo = 0, w_hi = 0;
+    if constexpr (WIN) {
+      if (c_row >= 0) {
+        // The launcher clamps F, C, R, A to the sequence (which is below
+        // 2^28 rows), so these products stay below 2^31.
+        a_end = a.win_A * a.win_F;
+        w_lo = (a.win_A + a.win_C * max(c_row - a.win_R, 0)) * a.win_F;
+        w_hi = (a.win_A + a.win_C * min(c_row + a.win_R + 1, win_cap)) * a.win_F;
       }
     }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = x * kSub + (r >> 2) * 8 + g * 4 + (r & 3);
+      if constexpr (WIN) {
+        // Bitwise, not short-circuit, so it compiles to compares and one
+        // select instead of branches.
+        const bool hidden = (key > lim) | ((key >= a_end) & ((key < w_lo) | (key >= w_hi)));
+        s[r] = hidden ? -INFINITY : s[r];
+      } else {
+        if (key > lim) s[r] = -INFINITY;
+      }
+    }
+  };
+  // Row max of this lane's 16 scores of sub-tile x; with MASK, the keys the
+  // lane's row does not see are set to -inf first.
+  auto rowmax = [&](f32x16_t& s, int x, auto mask) {
+    if constexpr (decltype(mask)::value) mask_scores(s, x);
     // Depth-3 tree over the 16 values.
     const float m0 = max3(s[0], s[1], s[2]), m1 = max3(s[3], s[4], s[5]), m2 = max3(s[6], s[7], s[8]);
     const float m3 = max3(s[9], s[10], s[11]), m4 = max3(s[12], s[13], s[14]);
@@ -1474,151 +1544,171 @@ void attn_fwd_kernel(AttnArgs a) {
     };
     auto rslot = [&](int x) { return (x - xb) & (kRing - 1); };
 
-    // Sub-tiles xb..xb+2 first (the other loads may still fly), then the
-    // prologue: scores of xb, which set each row's offset to its exact maximum
-    // (so the row keeps one probability of 1), and their probabilities.
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kRing - 4) * LDPS) : "memory");
-    __syncthreads();
-    f32x16_t s;
-    {
-      read_k(std::integral_constant<int, 0>{});
+    // The rest of the tile, with the online maximum (BND false) or the
+    // fixed per-row bounds (BND true: no row maximum, no rescale).
+    auto run_tile = [&](auto bnd) {
+    constexpr bool BND = decltype(bnd)::value;
+      // Sub-tiles xb..xb+2 first (the other loads may still fly), then the
+      // prologue: scores of xb, which set each row's offset to its exact maximum
+      // (so the row keeps one probability of 1), and their probabilities.
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kRing - 4) * LDPS) : "memory");
+      __syncthreads();
+      f32x16_t s;
+      {
+        read_k(std::integral_constant<int, 0>{});
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < NF; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s, 0, 0, 0);
-      if constexpr (!G::kJit) {
-        read_k(rslot(min(xb + 1, xe - 1)));
-        read_v(std::integral_constant<int, 0>{});
-      }
-      const float mx0 = rowmax(s, xmap(xb), Mask{});
-      m_run = max_lane_pair(mx0);
-      // A row with no visible key here (possible only under a frame window)
-      // starts from offset 0 and takes its offset from the first keys it sees.
-      if constexpr (WIN) {
-        seen = m_run != -INFINITY;
-        if (!seen) m_run = 0.f;
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] -= m_run;
-        msplat[r] = -m_run;
-      }
-      probs(s, pf);
-    }
-
-    // Step u alternates two phases separated by workgroup barriers:
-    //   X: the matrix-core work, QK^T of u+1 (K fragments of u+1 in kf) and
-    //      PV of u (V fragments of u in vf, probabilities of u in pf);
-    //   Y: the vector and LDS work, refill of the ring slot of u-1, reads of
-    //      K(u+2) and V(u+1), row maxima and rescale of u+1, probabilities and
-    //      row sums of u+1.
-    // The second wave of each SIMD passes one extra barrier first, so it runs
-    // Y while the first runs X and the other way round: the matrix core of the
-    // SIMD always has one wave's work while the other wave does the softmax.
-    // Both roles execute the same instructions in the same order.
-    // One fragment of an X phase: f even is K fragment f/2, f odd is V
-    // fragment f/2 (the order the phase consumes them).
-    auto kread = [&](auto slot, int kk) -> bf16x8_t {
-      if constexpr (std::is_integral_v<decltype(slot)>)
-        return *reinterpret_cast<const bf16x8_t*>(lds + slot * kBufBytes + ka[kk]);
-      else if constexpr (decltype(slot)::value < SPS)
-        return *reinterpret_cast<const bf16x8_t*>(lds + decltype(slot)::value * kBufBytes + ka[kk]);
-      else
-        return *reinterpret_cast<const bf16x8_t*>(lds + (decltype(slot)::value - SPS) * kBufBytes + kah[kk]);
-    };
-    auto vread = [&](auto slot, int i) -> bf16x8_t {
-      if constexpr (std::is_integral_v<decltype(slot)>)
-        return *reinterpret_cast<const bf16x8_t*>(lds + slot * kBufBytes + vaddr[i & 1] + (i >> 1) * 2048);
-      else if constexpr (decltype(slot)::value < SPS)
-        return *reinterpret_cast<const bf16x8_t*>(lds + decltype(slot)::value * kBufBytes + vaddr[i & 1] + (i >> 1) * 2048);
-      else
-        return *reinterpret_cast<const bf16x8_t*>(lds + (decltype(slot)::value - SPS) * kBufBytes + vah[i & 1] + (i >> 1) * 2048);
-    };
-    auto xread = [&](int f, auto slot_k, auto slot_v) -> bf16x8_t {
-      return (f & 1) ? vread(slot_v, f >> 1) : kread(slot_k, f >> 1);
-    };
-    bf16x8_t fr[4];   // kJit: the first four fragments of the next X phase
-    // slot_vn, slot_kn: the slots of V(u+1) and K(u+2), read in this step's
-    // Y phase; slot_vc, slot_kc: those of V(u) and K(u+1), which the X phase
-    // reads itself when kJit.
-    auto step = [&](int u, auto mask_next, auto slot_vn, auto slot_kn, auto slot_vc, auto slot_kc) {
-      fence();
-      s = msplat;
-      if constexpr (G::kJit) {
-        // Fenced groups: one matrix-core instruction and the read of the
-        // fragment four ahead.
-        bf16x8_t gfr[2 * NF];
-#pragma unroll
-        for (int f = 0; f < 4; ++f) gfr[f] = fr[f];
-        for_each_index(std::make_integer_sequence<int, 2 * NF>{}, [&](auto fc) {
-          constexpr int f = decltype(fc)::value;
-          if constexpr (f + 4 < 2 * NF) gfr[f + 4] = xread(f + 4, slot_kc, slot_vc);
-          if constexpr (f & 1)
-            acc[f >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gfr[f], pf[(f >> 1) & 1], acc[f >> 2], 0, 0, 0);
-          else
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gfr[f], qf[f >> 1], s, 0, 0, 0);
-          fence();
-        });
-      } else {
+        for (int r = 0; r < 16; ++r) s[r] = BND ? msplat[r] : 0.f;
 #pragma unroll
         for (int kk = 0; kk < NF; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s, 0, 0, 0);
+        if constexpr (!G::kJit) {
+          read_k(rslot(min(xb + 1, xe - 1)));
+          read_v(std::integral_constant<int, 0>{});
+        }
+        if constexpr (BND) {
+          mask_scores(s, xmap(xb));
+        } else {
+          const float mx0 = rowmax(s, xmap(xb), Mask{});
+          m_run = max_lane_pair(mx0);
+          // A row with no visible key here (possible only under a frame window)
+          // starts from offset 0 and takes its offset from the first keys it sees.
+          if constexpr (WIN) {
+            seen = m_run != -INFINITY;
+            if (!seen) m_run = 0.f;
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            s[r] -= m_run;
+            msplat[r] = -m_run;
+          }
+        }
+        probs(s, pf);
+      }
+
+      // Step u alternates two phases separated by workgroup barriers:
+      //   X: the matrix-core work, QK^T of u+1 (K fragments of u+1 in kf) and
+      //      PV of u (V fragments of u in vf, probabilities of u in pf);
+      //   Y: the vector and LDS work, refill of the ring slot of u-1, reads of
+      //      K(u+2) and V(u+1), row maxima and rescale of u+1, probabilities and
+      //      row sums of u+1.
+      // The second wave of each SIMD passes one extra barrier first, so it runs
+      // Y while the first runs X and the other way round: the matrix core of the
+      // SIMD always has one wave's work while the other wave does the softmax.
+      // Both roles execute the same instructions in the same order.
+      // One fragment of an X phase: f even is K fragment f/2, f odd is V
+      // fragment f/2 (the order the phase consumes them).
+      auto kread = [&](auto slot, int kk) -> bf16x8_t {
+        if constexpr (std::is_integral_v<decltype(slot)>)
+          return *reinterpret_cast<const bf16x8_t*>(lds + slot * kBufBytes + ka[kk]);
+        else if constexpr (decltype(slot)::value < SPS)
+          return *reinterpret_cast<const bf16x8_t*>(lds + decltype(slot)::value * kBufBytes + ka[kk]);
+        else
+          return *reinterpret_cast<const bf16x8_t*>(lds + (decltype(slot)::value - SPS) * kBufBytes + kah[kk]);
+      };
+      auto vread = [&](auto slot, int i) -> bf16x8_t {
+        if constexpr (std::is_integral_v<decltype(slot)>)
+          return *reinterpret_cast<const bf16x8_t*>(lds + slot * kBufBytes + vaddr[i & 1] + (i >> 1) * 2048);
+        else if constexpr (decltype(slot)::value < SPS)
+          return *reinterpret_cast<const bf16x8_t*>(lds + decltype(slot)::value * kBufBytes + vaddr[i & 1] + (i >> 1) * 2048);
+        else
+          return *reinterpret_cast<const bf16x8_t*>(lds + (decltype(slot)::value - SPS) * kBufBytes + vah[i & 1] + (i >> 1) * 2048);
+      };
+      auto xread = [&](int f, auto slot_k, auto slot_v) -> bf16x8_t {
+        return (f & 1) ? vread(slot_v, f >> 1) : kread(slot_k, f >> 1);
+      };
+      bf16x8_t fr[4];   // kJit: the first four fragments of the next X phase
+      // slot_vn, slot_kn: the slots of V(u+1) and K(u+2), read in this step's
+      // Y phase; slot_vc, slot_kc: those of V(u) and K(u+1), which the X phase
+      // reads itself when kJit.
+      auto step = [&](int u, auto mask_next, auto slot_vn, auto slot_kn, auto slot_vc, auto slot_kc) {
+        fence();
+        s = msplat;
+        if constexpr (G::kJit) {
+          // Fenced groups: one matrix-core instruction and the read of the
+          // fragment four ahead.
+          bf16x8_t gfr[2 * NF];
+#pragma unroll
+          for (int f = 0; f < 4; ++f) gfr[f] = fr[f];
+          for_each_index(std::make_integer_sequence<int, 2 * NF>{}, [&](auto fc) {
+            constexpr int f = decltype(fc)::value;
+            if constexpr (f + 4 < 2 * NF) gfr[f + 4] = xread(f + 4, slot_kc, slot_vc);
+            if constexpr (f & 1)
+              acc[f >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gfr[f], pf[(f >> 1) & 1], acc[f >> 2], 0, 0, 0);
+            else
+              s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gfr[f], qf[f >> 1], s, 0, 0, 0);
+            fence();
+          });
+        } else {
+#pragma unroll
+          for (int kk = 0; kk < NF; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < NF; ++i) acc[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf[i & 1], acc[i >> 1], 0, 0, 0);
+        }
+        fence();
+        bar();
+        fence();
+        if constexpr (G::kJit) {
+#pragma unroll
+          for (int f = 0; f < 4; ++f) fr[f] = xread(f, slot_kn, slot_vn);
+        } else {
+          read_k(slot_kn);
+          read_v(slot_vn);
+        }
+        // Refill the slot of u-1, last read for its PV in the X phase before the
+        // previous barrier (or, for the lagging role, before this one). Issued
+        // after this phase's reads: a fragment read behind a pending LDS DMA
+        // would make the compiler wait for every load in flight.
+        issue_loads(u - 1 + kRing);
+        if constexpr (BND) {
+          if constexpr (decltype(mask_next)::value) mask_scores(s, xmap(u + 1));
+        } else {
+          const float mx = rowmax(s, xmap(u + 1), mask_next);
+          maybe_rescale(s, mx, mask_next);
+        }
+        probs(s, pf);
+        fence();
+        // Publish sub-tile u+3 once every wave has passed this point.
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((kRing - 4) * LDPS) : "memory");
+        fence();
+      };
+
+      // Steady state in blocks of kRing steps, so that each step's ring slots
+      // (V of u+1 at (u+1-xb) mod 8, K of u+2 at (u+2-xb) mod 8) are constants;
+      // a block runs while all its steps read real sub-tiles and none needs the
+      // mask. The remaining steps address the ring at run time and mask.
+      if constexpr (G::kJit) {
+#pragma unroll
+        for (int f = 0; f < 4; ++f) fr[f] = xread(f, rslot(min(xb + 1, xe - 1)), 0);
+      }
+      if (role) bar();
+      int u = xb;
+      for (; u + kRing <= min(xe - 2, x_mask - 1); u += kRing) {
+        // Steps u + k, k = 0..kRing-1: V of sub-tile u+k+1 in slot (k+1) mod
+        // kRing, K of u+k+2 in slot (k+2) mod kRing (and V of u+k, K of u+k+1).
+        for_each_index(std::make_integer_sequence<int, kRing>{}, [&](auto k) {
+          constexpr int K = decltype(k)::value;
+          step(u + K, NoMask{}, std::integral_constant<int, (K + 1) % kRing>{},
+               std::integral_constant<int, (K + 2) % kRing>{}, std::integral_constant<int, K % kRing>{},
+               std::integral_constant<int, (K + 1) % kRing>{});
+        });
+      }
+      for (; u < xe - 1; ++u) step(u, Mask{}, rslot(u + 1), rslot(min(u + 2, xe - 1)), rslot(u), rslot(u + 1));
+      // Last X phase: PV of the last sub-tile only.
+      if constexpr (G::kJit) {
+        const int vs = rslot(xe - 1);
+#pragma unroll
+        for (int i = 0; i < NF; ++i)
+          acc[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vread(vs, i), pf[i & 1], acc[i >> 1], 0, 0, 0);
+      } else {
 #pragma unroll
         for (int i = 0; i < NF; ++i) acc[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf[i & 1], acc[i >> 1], 0, 0, 0);
       }
-      fence();
-      bar();
-      fence();
-      if constexpr (G::kJit) {
-#pragma unroll
-        for (int f = 0; f < 4; ++f) fr[f] = xread(f, slot_kn, slot_vn);
-      } else {
-        read_k(slot_kn);
-        read_v(slot_vn);
-      }
-      // Refill the slot of u-1, last read for its PV in the X phase before the
-      // previous barrier (or, for the lagging role, before this one). Issued
-      // after this phase's reads: a fragment read behind a pending LDS DMA
-      // would make the compiler wait for every load in flight.
-      issue_loads(u - 1 + kRing);
-      const float mx = rowmax(s, xmap(u + 1), mask_next);
-      maybe_rescale(s, mx, mask_next);
-      probs(s, pf);
-      fence();
-      // Publish sub-tile u+3 once every wave has passed this point.
-      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((kRing - 4) * LDPS) : "memory");
-      fence();
     };
-
-    // Steady state in blocks of kRing steps, so that each step's ring slots
-    // (V of u+1 at (u+1-xb) mod 8, K of u+2 at (u+2-xb) mod 8) are constants;
-    // a block runs while all its steps read real sub-tiles and none needs the
-    // mask. The remaining steps address the ring at run time and mask.
-    if constexpr (G::kJit) {
+    if (bounded) {
 #pragma unroll
-      for (int f = 0; f < 4; ++f) fr[f] = xread(f, rslot(min(xb + 1, xe - 1)), 0);
-    }
-    if (role) bar();
-    int u = xb;
-    for (; u + kRing <= min(xe - 2, x_mask - 1); u += kRing) {
-      // Steps u + k, k = 0..kRing-1: V of sub-tile u+k+1 in slot (k+1) mod
-      // kRing, K of u+k+2 in slot (k+2) mod kRing (and V of u+k, K of u+k+1).
-      for_each_index(std::make_integer_sequence<int, kRing>{}, [&](auto k) {
-        constexpr int K = decltype(k)::value;
-        step(u + K, NoMask{}, std::integral_constant<int, (K + 1) % kRing>{},
-             std::integral_constant<int, (K + 2) % kRing>{}, std::integral_constant<int, K % kRing>{},
-             std::integral_constant<int, (K + 1) % kRing>{});
-      });
-    }
-    for (; u < xe - 1; ++u) step(u, Mask{}, rslot(u + 1), rslot(min(u + 2, xe - 1)), rslot(u), rslot(u + 1));
-    // Last X phase: PV of the last sub-tile only.
-    if constexpr (G::kJit) {
-      const int vs = rslot(xe - 1);
-#pragma unroll
-      for (int i = 0; i < NF; ++i)
-        acc[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vread(vs, i), pf[i & 1], acc[i >> 1], 0, 0, 0);
+      for (int r = 0; r < 16; ++r) msplat[r] = -m_run;
+      run_tile(std::true_type{});
     } else {
-#pragma unroll
-      for (int i = 0; i < NF; ++i) acc[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf[i & 1], acc[i >> 1], 0, 0, 0);
+      run_tile(std::false_type{});
     }
     if (!role) bar();
     // The ring holds refills that nobody reads; let them retire so no LDS

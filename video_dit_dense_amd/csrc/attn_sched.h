@@ -38,6 +38,11 @@ inline int64_t split_part_slots(int32_t B, int32_t Sq, int32_t Sk, int32_t H, in
   return 2 * blocks;
 }
 
+// Key-norm maxima for the a priori score bound of unnormalised inputs: one
+// fp32 per chunk of kKnChunk prepared key rows of each (b, kv head).
+constexpr int kKnChunk = 4096;
+inline int64_t key_norm_chunks(int64_t Sk_pad) { return (Sk_pad + kKnChunk - 1) / kKnChunk; }
+
 // Blocks are dispatched round-robin over the 8 XCDs, so block i of a range
 // of n runs on XCD i%8. This bijection of [0, n) gives each XCD a contiguous
 // run of work items (same head, neighbouring query blocks or steps), so its

@@ -79,8 +79,8 @@ int check_prologue_args(int32_t Sq, int32_t Sk, const float* wq, const float* wk
 }
 
 struct WorkspaceLayout {
-  int64_t Sq_pad, Sk_pad, part_slots;
-  size_t q_off, k_off, v_off, part_off, total;
+  int64_t Sq_pad, Sk_pad, part_slots, kn_chunks;
+  size_t q_off, k_off, v_off, part_off, kn_off, total;
 };
 
 // Workspace of a forward with Hq query heads and Hkv key/value heads; the
@@ -97,12 +97,16 @@ bool workspace_layout(int32_t B, int32_t Sq, int32_t Sk, int32_t Hq, int32_t Hkv
   const unsigned __int128 kb = (unsigned __int128)B * (unsigned __int128)Hkv * (unsigned __int128)w->Sk_pad * row;
   w->part_slots = uniform ? h3::split_part_slots(B, Sq, Sk, Hq, D) : 0;
   const unsigned __int128 pb = (unsigned __int128)w->part_slots * (sizeof(float) * h3::attn_part_floats(D));
-  const unsigned __int128 tot = qb + 2 * kb + pb;
+  // Key-norm maxima (fp32 per chunk of keys of each (b, kv head)), padded to 256 bytes.
+  w->kn_chunks = h3::key_norm_chunks(w->Sk_pad);
+  const unsigned __int128 nb = ((unsigned __int128)B * Hkv * w->kn_chunks * sizeof(float) + 255) / 256 * 256;
+  const unsigned __int128 tot = qb + 2 * kb + pb + nb;
   if (tot > (unsigned __int128)(INT64_MAX / 4)) return false;
   w->q_off = 0;
   w->k_off = (size_t)qb;
   w->v_off = (size_t)(qb + kb);
   w->part_off = (size_t)(qb + 2 * kb);
+  w->kn_off = (size_t)(qb + 2 * kb + pb);
   w->total = (size_t)tot;
   return true;
 }
@@ -331,6 +335,7 @@ int run_forward(const h3attn_forward_args* a, void* workspace, size_t workspace_
   uint16_t* qw = wsb + wl.q_off / 2;
   uint16_t* kw = wsb + wl.k_off / 2;
   uint16_t* vt = wsb + wl.v_off / 2;
+  float* kn = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + wl.kn_off);
 
   // Prologue into the head-major workspace: rows past the valid length are
   // zero-filled so the attention kernel can read whole tiles.
@@ -353,6 +358,12 @@ int run_forward(const h3attn_forward_args* a, void* workspace, size_t workspace_
     e = h3::launch_v_relayout(a->v, vs[0], vs[1], vs[2], vt, B, Sk, Hkv, kv_valid, a->valid_lengths,
                               (int32_t)wl.Sk_pad, D, s);
     if (e != hipSuccess) return H3ATTN_ERR_HIP;
+    // Without H3's norm the score bound comes from the data: the largest
+    // prepared key norm of each chunk of keys.
+    if (a->k_norm_w == nullptr) {
+      e = h3::launch_key_norms(kw, kn, B * Hkv, (int32_t)wl.Sk_pad, (int32_t)wl.kn_chunks, D, s);
+      if (e != hipSuccess) return H3ATTN_ERR_HIP;
+    }
   }
   if (!(stages & H3ATTN_STAGE_ATTEND)) return H3ATTN_OK;
 
@@ -393,6 +404,8 @@ int run_forward(const h3attn_forward_args* a, void* workspace, size_t workspace_
   at.wq = a->q_norm_w;
   at.wk = a->k_norm_w;
   at.c_log2 = c;
+  at.knorm = a->k_norm_w == nullptr ? kn : nullptr;
+  at.kn_chunks = (int32_t)wl.kn_chunks;
   return status_from(h3::launch_attention(at, s));
 }
 

@@ -94,6 +94,12 @@ hipError_t launch_v_relayout(const uint16_t* v, int64_t sb, int64_t ss, int64_t 
                              int32_t B, int32_t Sk, int32_t H, int32_t kv_valid,
                              const int32_t* lengths, int32_t Sk_pad, int32_t D, hipStream_t stream);
 
+// The largest norm of the prepared key rows kw [BH][Sk_pad][D] in each chunk
+// of kKnChunk rows: kn[bh * kn_chunks + chunk] (rows past the valid length
+// are zero in kw and do not count).
+hipError_t launch_key_norms(const uint16_t* kw, float* kn, int32_t BH, int32_t Sk_pad, int32_t kn_chunks, int32_t D,
+                            hipStream_t stream);
+
 // The prepare stage for head dims other than 128 (no norm, no rotary): copies
 // t0 and t1 ([B, S, H, D] views) into the head-major workspace, multiplying
 // by out_scale in fp32 before the bf16 rounding and zero-filling rows at or
@@ -149,6 +155,11 @@ struct AttnArgs {
   const float* wq;
   const float* wk;
   float c_log2;
+  // Without the norm (wq == nullptr): the largest prepared key norm of each
+  // chunk of kKnChunk keys, [B*Hkv][kn_chunks] fp32 (key_norm_kernel), from
+  // which the kernel bounds each row's scores by |q_i| max_j |k_j|.
+  const float* knorm;
+  int32_t kn_chunks;
   // Schedule, filled in by launch_attention. Uniform mode (no causal mask,
   // no per-item lengths): valid tiles (query block below q_valid) are
   // numbered g = (b*H + h) * nqv + query block; tiles g < n_whole run whole,

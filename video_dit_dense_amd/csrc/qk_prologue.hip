@@ -290,6 +290,42 @@ __global__ __launch_bounds__(256) void qk_copy_kernel(ProTensor t, int32_t B) {
   *reinterpret_cast<v4u_t*>(t.out + b * t.out_sb + s * t.out_ss + h * t.out_sh + c * 8) = x;
 }
 
+// The largest norm of the prepared key rows in each chunk of kKnChunk rows
+// of one (b, kv head): D/8 lanes per row (16 bytes each), the squares of the
+// bf16 values summed in fp32 and over the row's lanes, the maximum over the
+// chunk's rows through the waves and LDS, one sqrt.
+template <int D>
+__global__ __launch_bounds__(256) void key_norm_kernel(const uint16_t* __restrict__ kw, float* __restrict__ kn,
+                                                       int32_t Sk_pad, int32_t kn_chunks) {
+  constexpr int CPR = D / 8;        // 16-byte chunks per row
+  constexpr int RPI = 256 / CPR;    // rows per iteration of the block
+  __shared__ float wave_max[4];
+  const int chunk = blockIdx.x, bh = blockIdx.y;
+  const int c = threadIdx.x % CPR;
+  const int r1 = min((chunk + 1) * kKnChunk, Sk_pad);
+  const uint16_t* base = kw + (int64_t)bh * Sk_pad * D + c * 8;
+  float mx = 0.f;
+  for (int r = chunk * kKnChunk + (int)threadIdx.x / CPR; r < r1; r += RPI) {
+    const v4u_t x = *reinterpret_cast<const v4u_t*>(base + (int64_t)r * D);
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float lo = bf16_lo(x[i]), hi = bf16_hi(x[i]);
+      ss = fmaf(lo, lo, ss);
+      ss = fmaf(hi, hi, ss);
+    }
+#pragma unroll
+    for (int o = 1; o < CPR; o <<= 1) ss += __shfl_xor(ss, o);
+    mx = fmaxf(mx, ss);
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    kn[(int64_t)bh * kn_chunks + chunk] = sqrtf(fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3])));
+}
+
 template <int D>
 hipError_t launch_copy_d(const ProTensor& t, int32_t B, hipStream_t stream) {
   const int64_t n = (int64_t)B * t.S_out * t.H * (D / 8);
@@ -382,6 +418,18 @@ hipError_t launch_qkv_pack(const QkvPack& t, hipStream_t stream) {
     qkv_pack_kernel<false, true><<<grid, kProThreads, 0, stream>>>(a);
   else
     qkv_pack_kernel<false, false><<<grid, kProThreads, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_key_norms(const uint16_t* kw, float* kn, int32_t BH, int32_t Sk_pad, int32_t kn_chunks, int32_t D,
+                            hipStream_t stream) {
+  const dim3 grid((unsigned)kn_chunks, (unsigned)BH);
+  switch (D) {
+    case 64: key_norm_kernel<64><<<grid, 256, 0, stream>>>(kw, kn, Sk_pad, kn_chunks); break;
+    case 128: key_norm_kernel<128><<<grid, 256, 0, stream>>>(kw, kn, Sk_pad, kn_chunks); break;
+    case 256: key_norm_kernel<256><<<grid, 256, 0, stream>>>(kw, kn, Sk_pad, kn_chunks); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

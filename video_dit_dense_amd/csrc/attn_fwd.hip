@@ -1002,13 +1002,13 @@ void attn_fwd_kernel(AttnArgs a) {
   bool seen = true;        // the row has met a visible key (m_run is its offset)
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // The a priori bound of the ping-pong paths (head dim 64; H3's norm is
-  // defined on 128 channels only, so the bound comes from the data): row
+  // The a priori bound of the 32x32 paths (head dims 64 and 256; H3's norm
+  // is defined on 128 channels only, so the bound comes from the data): row
   // i's scores lie in [-m_i, m_i], m_i = |q_i| max_j |k_j| (the lane pair
   // holds the row's channels in qf); when every row of the wave has m_i <=
   // kBoundMax, m_i is its fixed offset and the steps keep no row maximum.
   bool bounded = false;
-  if constexpr (!G::kPipe) {
+  {
     if (a.knorm != nullptr) {
       float ss = 0.f;
 #pragma unroll
@@ -1187,218 +1187,241 @@ void attn_fwd_kernel(AttnArgs a) {
     }
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"((2 * kRing - 4) * LPS) : "memory");
     __syncthreads();
-    const f32x16_t zero16 = {};
-    f32x16_t s0 = zero16, s_nx, msplat;
+    // The rest of the tile, with the online maximum (BND false) or the
+    // fixed per-row bounds (BND true: no row maximum, no rescale).
+    auto run_tile = [&](auto bnd) __attribute__((always_inline)) {
+    constexpr bool BND = decltype(bnd)::value;
+      const f32x16_t zero16 = {};
+      f32x16_t s_nx, msplat;
+      if constexpr (BND) {
 #pragma unroll
-    for (int kk = 0; kk < NF; ++kk) s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(0, kk), qf[kk], s0, 0, 0, 0);
-    bf16x8_t pf[2];
-    float dprev = 0.f;
-    {
-      m_run = max_lane_pair(rowmax(s0, xmap(xb), Mask{}));
-      // A row with no visible key here (possible only under a frame window)
-      // starts from offset 0 and takes its offset from the first keys it sees.
-      if constexpr (WIN) {
-        seen = m_run != -INFINITY;
-        if (!seen) m_run = 0.f;
+        for (int r = 0; r < 16; ++r) msplat[r] = -m_run;
       }
+      f32x16_t s0 = BND ? msplat : zero16;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s0[r] -= m_run;
-        msplat[r] = -m_run;
-      }
-      probs256(s0, pf, l_run);
-    }
-    s_nx = msplat;
-#pragma unroll
-    for (int kk = 0; kk < NF; ++kk) s_nx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(1, kk), qf[kk], s_nx, 0, 0, 0);
-    // Every wave has read K slots 0 and 1: the refills of the first step
-    // before it, then the wait for K(xb+2), V^T(xb), K(xb+3) and V^T(xb+1).
-    bar();
-    issue_k(xb + kRing);
-    issue_v(xb + kRing - 2);
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kWait) : "memory");
-    // The first four fragments of the first step (K(xb+2) 0, V^T(xb) 0,
-    // K(xb+2) 1, V^T(xb) 1); each step without a mask reads those of the next.
-    bf16x8_t nf[4];
-#pragma unroll
-    for (int f = 0; f < 4; ++f) nf[f] = (f & 1) ? vfrag(0, f >> 1) : kfrag(2, f >> 1);
-
-    // Step u: refills of the slots read last step (K(u+1), V^T(u-1)); QK^T
-    // of u+2 (when it exists) and PV of u; the softmax of u+1. At the end,
-    // K(u+4) and V^T(u+2) have landed for every wave; a step without a mask
-    // has read the first fragments of K(u+3) and V^T(u+1), which landed a
-    // step earlier, before that wait, so the next step's first matrix-core
-    // instruction does not wait on LDS. Without the mask the
-    // step has no data-dependent branch before its last instruction: each row
-    // raises its offset by its excess when that passes 2^kRescaleLog2 and the
-    // running sum takes the factor at once, while the accumulator, which PV of
-    // u (still relative to the old offset) is updating, is scaled after it in
-    // the rare step where some row raised, together with the probabilities,
-    // which the block computed with the old offset. So the matrix-core and
-    // vector work form one block that the scheduler interleaves: one fragment
-    // read and a few vector instructions per matrix-core instruction.
-    // Scores leave QK^T relative to the row offset (the accumulator starts at
-    // msplat = -offset); scores computed before a raise are shifted at the
-    // next step's start, in the same rare case.
-    auto step256 = [&](int u, auto mask, auto kslot, auto vslot, auto with_qk, int nkslot = 0, int nvslot = 0) __attribute__((always_inline)) {
-      constexpr bool kMask = decltype(mask)::value;
-      issue_k(u + 1 + kRing);
-      issue_v(u - 1 + kRing);
-      f32x16_t s = s_nx;
-      // s came out of last step's QK^T relative to the offset before that
-      // step raised it by dprev (rare).
-      if (__builtin_amdgcn_ballot_w64(dprev != 0.f) != 0) {
+      for (int kk = 0; kk < NF; ++kk) s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(0, kk), qf[kk], s0, 0, 0, 0);
+      bf16x8_t pf[2];
+      float dprev = 0.f;
+      if constexpr (BND) {
+        mask_scores(s0, xmap(xb));
+        probs256(s0, pf, l_run);
+      } else {
+        m_run = max_lane_pair(rowmax(s0, xmap(xb), Mask{}));
+        // A row with no visible key here (possible only under a frame window)
+        // starts from offset 0 and takes its offset from the first keys it sees.
+        if constexpr (WIN) {
+          seen = m_run != -INFINITY;
+          if (!seen) m_run = 0.f;
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          s[r] -= dprev;
-          msplat[r] -= dprev;
+          s0[r] -= m_run;
+          msplat[r] = -m_run;
         }
+        probs256(s0, pf, l_run);
       }
-      bf16x8_t pn[2];
-      float ls = 0.f;
-      if constexpr (!kMask && decltype(with_qk)::value) {
-        // The 32 matrix-core instructions f (even: QK^T fragment f/2, odd: PV
-        // fragment f/2) each with the LDS read of fragment f+4 and a slice of
-        // the softmax, in groups the compiler keeps in this order.
-        auto frag = [&](int f) __attribute__((always_inline)) {
-          return (f & 1) ? vfrag(vslot, f >> 1) : kfrag(kslot, f >> 1);
-        };
-        bf16x8_t fr[2 * NF];
-        f32x16_t sn = msplat;
-        float m0, m1, m2, m3, m4, mx, delta, alpha;
-        uint32_t pk[8];
+      s_nx = msplat;
 #pragma unroll
-        for (int f = 0; f < 4; ++f) fr[f] = nf[f];
-        fence();
-        for_each_index(std::make_integer_sequence<int, 2 * NF>{}, [&](auto fc) __attribute__((always_inline)) {
-          constexpr int f = decltype(fc)::value;
-          if constexpr (f + 4 < 2 * NF) fr[f + 4] = frag(f + 4);
-          if constexpr (f & 1)
-            acc[f >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[f], pf[(f >> 1) & 1], acc[f >> 2], 0, 0, 0);
-          else
-            sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[f], qf[f >> 1], sn, 0, 0, 0);
-          // The softmax in 24 slices, slice i in group i (2 NF = 32) or
-          // spread in order over the 16 groups (2 NF = 16). Each slice's
-          // result is pinned in its group by an empty asm use: the fences
-          // bind the scheduler, not the passes that move pure arithmetic
-          // towards its first use.
-          for_each_index(std::make_integer_sequence<int, 24>{}, [&](auto ic) __attribute__((always_inline)) {
-            constexpr int i = decltype(ic)::value;
-            constexpr int grp = 2 * NF >= 24 ? i : i * 2 * NF / 24;
-            if constexpr (grp == f) {
-              if constexpr (i < 5) {
-                const float t = max3(s[3 * i], s[3 * i + 1], s[3 * i + 2]);
-                asm volatile("" ::"v"(t));
-                if constexpr (i == 0) m0 = t;
-                else if constexpr (i == 1) m1 = t;
-                else if constexpr (i == 2) m2 = t;
-                else if constexpr (i == 3) m3 = t;
-                else m4 = t;
-              } else if constexpr (i == 5) {
-                mx = fmaxf(max3(m0, m1, m2), max3(m3, m4, s[15]));
-                asm volatile("" ::"v"(mx));
-              } else if constexpr (i == 6) {
-                mx = max_lane_pair(mx);
-                asm volatile("" ::"v"(mx));
-              } else if constexpr (i == 7) {
-                // Each row raises its offset by its excess when that passes
-                // 2^kRescaleLog2; the sum takes the factor now, the
-                // accumulator after this step's PV.
-                delta = mx > kRescaleLog2 ? mx : 0.f;
-                m_run += delta;
-                alpha = __builtin_amdgcn_exp2f(-delta);
-                l_run *= alpha;
-                asm volatile("" ::"v"(m_run), "v"(l_run), "v"(alpha));
-              } else if constexpr (i < 16) {
-                constexpr int e = 2 * (i - 8);
-                pk[i - 8] = pack_bf16x2(__builtin_amdgcn_exp2f(s[e]), __builtin_amdgcn_exp2f(s[e + 1]));
-                asm volatile("" ::"v"(pk[i - 8]));
-              } else {
-                ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[i - 16]), ones, ls, false);
-                asm volatile("" ::"v"(ls));
-              }
+      for (int kk = 0; kk < NF; ++kk) s_nx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(1, kk), qf[kk], s_nx, 0, 0, 0);
+      // Every wave has read K slots 0 and 1: the refills of the first step
+      // before it, then the wait for K(xb+2), V^T(xb), K(xb+3) and V^T(xb+1).
+      bar();
+      issue_k(xb + kRing);
+      issue_v(xb + kRing - 2);
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kWait) : "memory");
+      // The first four fragments of the first step (K(xb+2) 0, V^T(xb) 0,
+      // K(xb+2) 1, V^T(xb) 1); each step without a mask reads those of the next.
+      bf16x8_t nf[4];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) nf[f] = (f & 1) ? vfrag(0, f >> 1) : kfrag(2, f >> 1);
+
+      // Step u: refills of the slots read last step (K(u+1), V^T(u-1)); QK^T
+      // of u+2 (when it exists) and PV of u; the softmax of u+1. At the end,
+      // K(u+4) and V^T(u+2) have landed for every wave; a step without a mask
+      // has read the first fragments of K(u+3) and V^T(u+1), which landed a
+      // step earlier, before that wait, so the next step's first matrix-core
+      // instruction does not wait on LDS. Without the mask the
+      // step has no data-dependent branch before its last instruction: each row
+      // raises its offset by its excess when that passes 2^kRescaleLog2 and the
+      // running sum takes the factor at once, while the accumulator, which PV of
+      // u (still relative to the old offset) is updating, is scaled after it in
+      // the rare step where some row raised, together with the probabilities,
+      // which the block computed with the old offset. So the matrix-core and
+      // vector work form one block that the scheduler interleaves: one fragment
+      // read and a few vector instructions per matrix-core instruction.
+      // Scores leave QK^T relative to the row offset (the accumulator starts at
+      // msplat = -offset); scores computed before a raise are shifted at the
+      // next step's start, in the same rare case.
+      auto step256 = [&](int u, auto mask, auto kslot, auto vslot, auto with_qk, int nkslot = 0, int nvslot = 0) __attribute__((always_inline)) {
+        constexpr bool kMask = decltype(mask)::value;
+        issue_k(u + 1 + kRing);
+        issue_v(u - 1 + kRing);
+        f32x16_t s = s_nx;
+        // s came out of last step's QK^T relative to the offset before that
+        // step raised it by dprev (rare).
+        if constexpr (!BND) {
+          if (__builtin_amdgcn_ballot_w64(dprev != 0.f) != 0) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              s[r] -= dprev;
+              msplat[r] -= dprev;
             }
-          });
+          }
+        }
+        bf16x8_t pn[2];
+        float ls = 0.f;
+        if constexpr (!kMask && decltype(with_qk)::value) {
+          // The 32 matrix-core instructions f (even: QK^T fragment f/2, odd: PV
+          // fragment f/2) each with the LDS read of fragment f+4 and a slice of
+          // the softmax, in groups the compiler keeps in this order.
+          auto frag = [&](int f) __attribute__((always_inline)) {
+            return (f & 1) ? vfrag(vslot, f >> 1) : kfrag(kslot, f >> 1);
+          };
+          bf16x8_t fr[2 * NF];
+          f32x16_t sn = msplat;
+          float m0, m1, m2, m3, m4, mx, delta, alpha;
+          uint32_t pk[8];
+#pragma unroll
+          for (int f = 0; f < 4; ++f) fr[f] = nf[f];
           fence();
-        });
-        s_nx = sn;
-        if (__builtin_amdgcn_ballot_w64(delta != 0.f) != 0) {
+          for_each_index(std::make_integer_sequence<int, 2 * NF>{}, [&](auto fc) __attribute__((always_inline)) {
+            constexpr int f = decltype(fc)::value;
+            if constexpr (f + 4 < 2 * NF) fr[f + 4] = frag(f + 4);
+            if constexpr (f & 1)
+              acc[f >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[f], pf[(f >> 1) & 1], acc[f >> 2], 0, 0, 0);
+            else
+              sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[f], qf[f >> 1], sn, 0, 0, 0);
+            // The softmax in 24 slices, slice i in group i (2 NF = 32) or
+            // spread in order over the 16 groups (2 NF = 16). Each slice's
+            // result is pinned in its group by an empty asm use: the fences
+            // bind the scheduler, not the passes that move pure arithmetic
+            // towards its first use. With the fixed offsets (BND) the first
+            // eight slices (row maximum, offset raise) do not exist and the
+            // other sixteen spread over the groups.
+            for_each_index(std::make_integer_sequence<int, 24>{}, [&](auto ic) __attribute__((always_inline)) {
+              constexpr int i = decltype(ic)::value;
+              constexpr int grp = BND ? (i < 8 ? -1 : (i - 8) * 2 * NF / 16) : (2 * NF >= 24 ? i : i * 2 * NF / 24);
+              if constexpr (grp == f) {
+                if constexpr (i < 5) {
+                  const float t = max3(s[3 * i], s[3 * i + 1], s[3 * i + 2]);
+                  asm volatile("" ::"v"(t));
+                  if constexpr (i == 0) m0 = t;
+                  else if constexpr (i == 1) m1 = t;
+                  else if constexpr (i == 2) m2 = t;
+                  else if constexpr (i == 3) m3 = t;
+                  else m4 = t;
+                } else if constexpr (i == 5) {
+                  mx = fmaxf(max3(m0, m1, m2), max3(m3, m4, s[15]));
+                  asm volatile("" ::"v"(mx));
+                } else if constexpr (i == 6) {
+                  mx = max_lane_pair(mx);
+                  asm volatile("" ::"v"(mx));
+                } else if constexpr (i == 7) {
+                  // Each row raises its offset by its excess when that passes
+                  // 2^kRescaleLog2; the sum takes the factor now, the
+                  // accumulator after this step's PV.
+                  delta = mx > kRescaleLog2 ? mx : 0.f;
+                  m_run += delta;
+                  alpha = __builtin_amdgcn_exp2f(-delta);
+                  l_run *= alpha;
+                  asm volatile("" ::"v"(m_run), "v"(l_run), "v"(alpha));
+                } else if constexpr (i < 16) {
+                  constexpr int e = 2 * (i - 8);
+                  pk[i - 8] = pack_bf16x2(__builtin_amdgcn_exp2f(s[e]), __builtin_amdgcn_exp2f(s[e + 1]));
+                  asm volatile("" ::"v"(pk[i - 8]));
+                } else {
+                  ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[i - 16]), ones, ls, false);
+                  asm volatile("" ::"v"(ls));
+                }
+              }
+            });
+            fence();
+          });
+          s_nx = sn;
+          if (!BND && __builtin_amdgcn_ballot_w64(delta != 0.f) != 0) {
 #pragma unroll
-          for (int dt = 0; dt < NT; ++dt)
+            for (int dt = 0; dt < NT; ++dt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+              for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) s[r] -= delta;
-          ls = 0.f;
+            for (int r = 0; r < 16; ++r) s[r] -= delta;
+            ls = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                pk[4 * ks + i] = pack_bf16x2(__builtin_amdgcn_exp2f(s[8 * ks + 2 * i]), __builtin_amdgcn_exp2f(s[8 * ks + 2 * i + 1]));
+                ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[4 * ks + i]), ones, ls, false);
+              }
+          }
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              pk[4 * ks + i] = pack_bf16x2(__builtin_amdgcn_exp2f(s[8 * ks + 2 * i]), __builtin_amdgcn_exp2f(s[8 * ks + 2 * i + 1]));
-              ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[4 * ks + i]), ones, ls, false);
-            }
-        }
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-          pn[ks] = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]});
-        dprev = delta;
-      } else {
-        if constexpr (decltype(with_qk)::value) {
-          f32x16_t sn = msplat;
-#pragma unroll
-          for (int m = 0; m < NF; ++m) {
-            sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(kslot, m), qf[m], sn, 0, 0, 0);
-            acc[m >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag(vslot, m), pf[m & 1], acc[m >> 1], 0, 0, 0);
-          }
-          s_nx = sn;
+            pn[ks] = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]});
+          if constexpr (!BND) dprev = delta;
         } else {
+          if constexpr (decltype(with_qk)::value) {
+            f32x16_t sn = msplat;
 #pragma unroll
-          for (int m = 0; m < NF; ++m)
-            acc[m >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag(vslot, m), pf[m & 1], acc[m >> 1], 0, 0, 0);
+            for (int m = 0; m < NF; ++m) {
+              sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(kslot, m), qf[m], sn, 0, 0, 0);
+              acc[m >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag(vslot, m), pf[m & 1], acc[m >> 1], 0, 0, 0);
+            }
+            s_nx = sn;
+          } else {
+#pragma unroll
+            for (int m = 0; m < NF; ++m)
+              acc[m >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag(vslot, m), pf[m & 1], acc[m >> 1], 0, 0, 0);
+          }
+          if constexpr (BND) {
+            if constexpr (kMask) mask_scores(s, xmap(u + 1));
+          } else {
+            const float mx = rowmax(s, xmap(u + 1), mask);
+            bool trigger = mx > kRescaleLog2;
+            if constexpr (WIN && kMask) trigger = trigger || (!seen && mx != -INFINITY);
+            dprev = 0.f;
+            if (__builtin_amdgcn_ballot_w64(trigger) != 0) {
+              dprev = rescale256(mx, mask);
+#pragma unroll
+              for (int r = 0; r < 16; ++r) s[r] -= dprev;
+            }
+          }
+          probs256(s, pn, ls);
         }
-        const float mx = rowmax(s, xmap(u + 1), mask);
-        bool trigger = mx > kRescaleLog2;
-        if constexpr (WIN && kMask) trigger = trigger || (!seen && mx != -INFINITY);
-        dprev = 0.f;
-        if (__builtin_amdgcn_ballot_w64(trigger) != 0) {
-          dprev = rescale256(mx, mask);
+        l_run += ls;
+        pf[0] = pn[0];
+        pf[1] = pn[1];
+        if constexpr (!kMask && decltype(with_qk)::value) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) s[r] -= dprev;
+          for (int f = 0; f < 4; ++f) nf[f] = (f & 1) ? vfrag(nvslot, f >> 1) : kfrag(nkslot, f >> 1);
         }
-        probs256(s, pn, ls);
-      }
-      l_run += ls;
-      pf[0] = pn[0];
-      pf[1] = pn[1];
-      if constexpr (!kMask && decltype(with_qk)::value) {
-#pragma unroll
-        for (int f = 0; f < 4; ++f) nf[f] = (f & 1) ? vfrag(nvslot, f >> 1) : kfrag(nkslot, f >> 1);
-      }
-      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kWait) : "memory");
-    };
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kWait) : "memory");
+      };
 
-    // Steady state in blocks of kRing steps (ring slots as constants) while
-    // the steps have a QK^T and need no mask; the rest address the ring at
-    // run time and mask.
-    int u = xb;
-    for (; u + kRing <= min(xe - 2, x_mask - 1); u += kRing) {
-      for_each_index(std::make_integer_sequence<int, kRing>{}, [&](auto k) {
-        constexpr int K = decltype(k)::value;
-        step256(u + K, NoMask{}, (K + 2) % kRing, K, std::true_type{}, (K + 3) % kRing, (K + 1) % kRing);
-      });
-    }
-    for (; u < xe - 2; ++u) step256(u, Mask{}, slot_of(u + 2), slot_of(u), std::true_type{});
-    if (u == xe - 2) {
-      step256(u, Mask{}, 0, slot_of(u), std::false_type{});
-      ++u;
-    }
-    // PV of the last sub-tile.
-    {
-      const int vs = slot_of(xe - 1);
+      // Steady state in blocks of kRing steps (ring slots as constants) while
+      // the steps have a QK^T and need no mask; the rest address the ring at
+      // run time and mask.
+      int u = xb;
+      for (; u + kRing <= min(xe - 2, x_mask - 1); u += kRing) {
+        for_each_index(std::make_integer_sequence<int, kRing>{}, [&](auto k) {
+          constexpr int K = decltype(k)::value;
+          step256(u + K, NoMask{}, (K + 2) % kRing, K, std::true_type{}, (K + 3) % kRing, (K + 1) % kRing);
+        });
+      }
+      for (; u < xe - 2; ++u) step256(u, Mask{}, slot_of(u + 2), slot_of(u), std::true_type{});
+      if (u == xe - 2) {
+        step256(u, Mask{}, 0, slot_of(u), std::false_type{});
+        ++u;
+      }
+      // PV of the last sub-tile.
+      {
+        const int vs = slot_of(xe - 1);
 #pragma unroll
-      for (int m = 0; m < NF; ++m)
-        acc[m >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag(vs, m), pf[m & 1], acc[m >> 1], 0, 0, 0);
-    }
+        for (int m = 0; m < NF; ++m)
+          acc[m >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag(vs, m), pf[m & 1], acc[m >> 1], 0, 0, 0);
+      }
+    };
+    if (bounded) run_tile(std::true_type{});
+    else run_tile(std::false_type{});
     // Let the refills nobody reads retire before the workgroup ends or the
     // next segment refills the rings.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");

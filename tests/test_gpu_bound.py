@@ -67,12 +67,16 @@ def run(h3, inp, rope=True, **kw):
 
 
 # (B, Sq, Sk, H, kwargs): 36 tiles split over the CUs with a masked last
-# step, ragged valid lengths, the causal mask, a frame window with a gate.
+# step, ragged valid lengths, the causal mask, a frame window with a gate,
+# and key ranges short enough to stay resident in LDS.
 ONLINE_CASES = [
     (1, 3000, 3000, 3, {}),
     (2, 1000, 777, 2, {"q_valid": 900, "kv_valid": 700}),
     (1, 1500, 1500, 2, {"causal": True}),
     (1, 2000, 2000, 2, {"window": (100, 3, 1, 2), "gate": True}),
+    # Short key ranges (keys resident in LDS): the exact two-pass softmax.
+    (1, 3000, 300, 2, {"kv_valid": 250}),
+    (2, 700, 64, 3, {"q_valid": 650}),
 ]
 
 
@@ -138,8 +142,8 @@ def test_weights_either_side_of_the_limit(h3, w):
     check_metrics(oracle.compare(got, ref), f"weights {w}")
 
 
-@pytest.mark.parametrize("D", [64, 128])
-def test_data_bound_mixes_paths_within_a_workgroup(h3, D):
+@pytest.mark.parametrize("D,Sk", [(64, 2048), (128, 2048), (128, 300)])
+def test_data_bound_mixes_paths_within_a_workgroup(h3, D, Sk):
     """Without the norm the bound is |q_i| max_j |k_j| per row, decided per
     wave. Key 7 gets a norm above 100 on channel 5, which every query has at
     zero (its scores stay those of a plain key), so max_j |k_j| > 100; the
@@ -147,7 +151,7 @@ def test_data_bound_mixes_paths_within_a_workgroup(h3, D):
     those waves have m_i below the limit and run the bounded path while
     their neighbours in the same workgroup run the online maximum."""
     B, S, H = 1, 2048, 2
-    base = workloads.make_inputs(B, S, S, H, seed=930 + D, D=D)
+    base = workloads.make_inputs(B, S, Sk, H, seed=930 + D, D=D)
     q = base.q.copy()
     k = base.k.copy()
     q[..., 5] = 0
@@ -159,8 +163,8 @@ def test_data_bound_mixes_paths_within_a_workgroup(h3, D):
     q = workloads.f32_to_bf16_bits(qf)
     inp = workloads.Inputs(q, k, base.v, base.w_q, base.w_k)
     d = DevInputs(inp)
-    say("data bound, mixed waves", D)
+    say("data bound, mixed waves", D, Sk)
     o = h3.forward(d.q, d.k, d.v, scale=1 / math.sqrt(D))
     torch.cuda.synchronize()
     ref = oracle.forward(inp.q, inp.k, inp.v, None, None, 1e-6, None, 1 / math.sqrt(D), norm=False)
-    check_metrics(oracle.compare(to_host(o), ref), f"D={D} mixed bounded/online waves")
+    check_metrics(oracle.compare(to_host(o), ref), f"D={D} Sk={Sk} mixed bounded/online waves")

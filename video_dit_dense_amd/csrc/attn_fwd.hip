@@ -1756,6 +1756,267 @@ void attn_fwd_kernel(AttnArgs a) {
   }
 }
 
+// Short key ranges at head dim 128 (cross-attention against a few hundred
+// text keys): when the valid keys of a (b, kv head) fill at most kResMaxSub
+// sub-tiles, their K and V^T (8 KB each per sub-tile, 160 KB at 10) stay
+// resident in LDS. A workgroup of eight waves then owns one (b, h) and one
+// residue class of its query tiles (tiles gi, gi + G, ...): it loads the keys
+// once, and each tile costs only its Q fragments (loaded a tile ahead, into
+// registers) and its output, instead of a launch, a ring fill and a drain.
+// The arithmetic is the main kernel's on 16x16x32 instructions: per
+// sub-tile, QK^T from the Q fragments and the K fragments in LDS, p =
+// exp2(s - m) rounded to bf16, PV into fp32 accumulators; o = O / l. With
+// the a priori bound (norm weights, or the key-norm maxima) m is the row's
+// fixed bound; otherwise a first pass over the resident keys finds each
+// row's exact maximum (two QK^T passes, no rescale). The LDS layouts are
+// the ring slots' (K rows and V^T rows swizzled as there), filled by plain
+// loads and stores.
+constexpr int kResMaxSub = 10;
+
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_resident_kernel(AttnArgs a, int32_t G) {
+  constexpr int D = 128;
+  using Gm = Geo<D>;
+  constexpr int BM = Gm::BM, T = Gm::NW * 64, NC = D / 32, NT16 = D / 16;
+  constexpr int kKB = Gm::kKBytes;                 // one K or V^T sub-tile (8 KB)
+  constexpr int kVBase = kResMaxSub * kKB;         // V^T region
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kResMaxSub * kKB];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
+  const int bh = blockIdx.x / G, gi = blockIdx.x - bh * G;
+  const int b = bh / a.H, h = bh - b * a.H;
+  const int bh_kv = b * a.Hkv + h / (a.H / a.Hkv);
+  const int kvv = a.kv_valid, NU = (kvv + kSub - 1) / kSub;
+  const int nq = (a.Sq + BM - 1) / BM, nqv = (a.q_valid + BM - 1) / BM;
+  uint16_t* obase = a.o + ((int64_t)b * a.Sq * a.H + h) * D;
+  const uint16_t* gate_row = a.gate ? a.gate + (int64_t)b * a.Sq * a.H + h : nullptr;
+
+  // Resident keys: LDS byte P of sub-tile x (K at x kKB, V^T at kVBase + x
+  // kKB) holds the 16 bytes that the ring's direct loads would put there:
+  // chunk Q = P / 16 comes from sub-tile byte offset loff(Q) below.
+  {
+    const uint16_t* kw = a.kw + (int64_t)bh_kv * a.Sk_pad * D;
+    const uint16_t* vt = a.vt + (int64_t)bh_kv * a.Sk_pad * D;
+    constexpr int CH = kKB / 16;                   // 512 chunks per sub-tile and operand
+    constexpr int kFill = 2 * kResMaxSub * CH / T; // chunks per thread (all loads issued before any store)
+    u32x4_t tmp[kFill];
+    int dst[kFill];
+#pragma unroll
+    for (int k = 0; k < kFill; ++k) {
+      const int i = tid + k * T;
+      const int x = i / (2 * CH), rem = i - x * 2 * CH;
+      const bool is_v = rem >= CH;
+      const int Q = is_v ? rem - CH : rem;
+      int off;
+      if (!is_v) {
+        const int r = Q / (D / 8), pp = Q % (D / 8);
+        off = (r * D + ((pp ^ (r & Gm::kSwz)) * 8)) * 2;
+      } else {
+        const int d = Q >> 2, pp = Q & 3;
+        off = (d * kSub + ((pp ^ ((d >> 2) & 3)) * 8)) * 2;
+      }
+      dst[k] = (is_v ? kVBase : 0) + x * kKB + Q * 16;
+      if (x < NU)
+        tmp[k] = *reinterpret_cast<const u32x4_t*>(
+            reinterpret_cast<const uint8_t*>((is_v ? vt : kw) + (int64_t)x * (kSub * D)) + off);
+    }
+#pragma unroll
+    for (int k = 0; k < kFill; ++k)
+      if ((tid + k * T) / (2 * CH) < NU) *reinterpret_cast<u32x4_t*>(lds + dst[k]) = tmp[k];
+  }
+
+  // Fragment addresses as in the main kernel's 16x16x32 path.
+  const uint32_t kb16 = l16 * (2 * D) + ((g4 ^ (l16 & Gm::kSwz)) * 16);
+  const uint32_t va = kVBase + l16 * 64 + ((g4 ^ ((l16 >> 2) & 3)) * 16);
+  auto kfrag = [&](int x, int g) __attribute__((always_inline)) {
+    return *reinterpret_cast<const bf16x8_t*>(lds + x * kKB + (g & 1) * (16 * 2 * D) + (kb16 ^ (64u * (g >> 1))));
+  };
+  auto vfrag = [&](int x, int ct) __attribute__((always_inline)) {
+    return *reinterpret_cast<const bf16x8_t*>(lds + x * kKB + ct * 1024 + va);
+  };
+  // Q fragments of tile t: query row 16 qt + l%16 of the wave, channels
+  // 32 cc + 8 g4 .. +7 (rows past the workspace's valid rows are zero).
+  bf16x8_t qn[2][NC];
+  auto load_q = [&](int t) __attribute__((always_inline)) {
+    const uint16_t* qp = a.qw + ((int64_t)bh * a.Sq_pad + t * BM + wave * 32 + l16) * D + g4 * 8;
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) qn[qt][cc] = *reinterpret_cast<const bf16x8_t*>(qp + qt * 16 * D + cc * 32);
+  };
+  int t = gi;
+  if (t < nqv) load_q(t);
+  __syncthreads();
+
+  // A priori bound with H3's norm weights (uniform), else per row from the
+  // key-norm maxima and the Q fragments; INFINITY when neither applies.
+  float w_bound = INFINITY, kmax = INFINITY;
+  if (a.wq != nullptr) {
+    w_bound = a.c_log2 * 128.0f * wave_max(fmaxf(fabsf(a.wq[lane]), fabsf(a.wq[lane + 64]))) *
+              wave_max(fmaxf(fabsf(a.wk[lane]), fabsf(a.wk[lane + 64]))) * (1.0f + 1.0f / 64.0f);
+  } else if (a.knorm != nullptr) {
+    kmax = key_norm_max(a, bh_kv);
+  }
+  auto sum_row16 = [](float x) __attribute__((always_inline)) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto sw = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return sum_lane_pair(__builtin_bit_cast(float, (uint32_t)sw[0]) + __builtin_bit_cast(float, (uint32_t)sw[1]));
+  };
+  auto max_row16 = [](float x) __attribute__((always_inline)) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto sw = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return max_lane_pair(fmaxf(__builtin_bit_cast(float, (uint32_t)sw[0]), __builtin_bit_cast(float, (uint32_t)sw[1])));
+  };
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  for (; t < nq; t += G) {
+    if (t >= nqv) {
+      // Query tile wholly past q_valid: zeros.
+      constexpr int CPR = D / 8;
+      for (int idx = tid; idx < BM * CPR; idx += T) {
+        const int q = t * BM + idx / CPR;
+        if (q < a.Sq) *reinterpret_cast<u32x4_t*>(obase + (int64_t)q * a.H * D + (idx % CPR) * 8) = u32x4_t{0u, 0u, 0u, 0u};
+      }
+      continue;
+    }
+    bf16x8_t qf[2][NC];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) qf[qt][cc] = qn[qt][cc];
+    if (t + G < nqv) load_q(t + G);
+
+    // QK^T of sub-tile x into s (initial value sinit); keys at or past kvv set to -inf.
+    auto scores = [&](int x, const f32x4_t* sinit, f32x4_t (&s)[2][2]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        s[qt][0] = sinit[qt];
+        s[qt][1] = sinit[qt];
+      }
+#pragma unroll
+      for (int g = 0; g < 2 * NC; ++g) {
+        const bf16x8_t kf = kfrag(x, g);
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+          s[qt][g & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qt][g >> 1], s[qt][g & 1], 0, 0, 0);
+      }
+      if (x == NU - 1 && (kvv % kSub) != 0) {
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (x * kSub + kt * 16 + g4 * 4 + r >= kvv) s[qt][kt][r] = -INFINITY;
+      }
+    };
+
+    // Row offsets: the bound when it is known and at most kBoundMax for every
+    // row of the wave, else the exact row maxima from a first pass.
+    float m[2];
+    bool have = false;
+    if (a.wq != nullptr) {
+      m[0] = m[1] = w_bound;
+      have = __builtin_amdgcn_readfirstlane(w_bound <= kBoundMax ? 1 : 0) != 0;
+    } else if (a.knorm != nullptr) {
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        float ss = 0.f;
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) ss = sum_sq(qf[qt][cc], ss);
+        m[qt] = sqrtf(sum_row16(ss)) * kmax * kBoundSlack;
+      }
+      have = __builtin_amdgcn_ballot_w64(!(m[0] <= kBoundMax) | !(m[1] <= kBoundMax)) == 0;
+    }
+    if (!have) {
+      const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+      const f32x4_t z[2] = {zero4, zero4};
+      float mx[2] = {-INFINITY, -INFINITY};
+      for (int x = 0; x < NU; ++x) {
+        f32x4_t s[2][2];
+        scores(x, z, s);
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+          mx[qt] = fmaxf(mx[qt], fmaxf(max3(max3(s[qt][0][0], s[qt][0][1], s[qt][0][2]), s[qt][0][3], s[qt][1][0]),
+                                       max3(s[qt][1][1], s[qt][1][2], s[qt][1][3])));
+      }
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) m[qt] = max_row16(mx[qt]);
+    }
+    const f32x4_t msplat[2] = {f32x4_t{-m[0], -m[0], -m[0], -m[0]}, f32x4_t{-m[1], -m[1], -m[1], -m[1]}};
+
+    f32x4_t acc[2][NT16];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int ct = 0; ct < NT16; ++ct) acc[qt][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float l_run[2] = {0.f, 0.f};
+    // Software pipeline over the resident sub-tiles: QK^T of x + 1 goes to
+    // the matrix core before the softmax and PV of x, and each sub-tile's
+    // eight K fragments are read together.
+    bf16x8_t kf[2 * NC];
+    auto read_k = [&](int x) __attribute__((always_inline)) {
+#pragma unroll
+      for (int g = 0; g < 2 * NC; ++g) kf[g] = kfrag(x, g);
+    };
+    auto qk = [&](f32x4_t (&s)[2][2]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        s[qt][0] = msplat[qt];
+        s[qt][1] = msplat[qt];
+      }
+#pragma unroll
+      for (int g = 0; g < 2 * NC; ++g)
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+          s[qt][g & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[g], qf[qt][g >> 1], s[qt][g & 1], 0, 0, 0);
+    };
+    f32x4_t s[2][2], sn[2][2];
+    read_k(0);
+    qk(s);
+    for (int x = 0; x < NU; ++x) {
+      if (x + 1 < NU) read_k(x + 1);
+      if (x == NU - 1 && (kvv % kSub) != 0) {
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (x * kSub + kt * 16 + g4 * 4 + r >= kvv) s[qt][kt][r] = -INFINITY;
+      }
+      if (x + 1 < NU) qk(sn);
+      bf16x8_t pf[2];
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pf[qt][j] = (__bf16)__builtin_amdgcn_exp2f(s[qt][j >> 2][j & 3]);
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+          const bf16x2_t pp = {pf[qt][j], pf[qt][j + 1]};
+          l_run[qt] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_run[qt], false);
+        }
+      }
+#pragma unroll
+      for (int ct = 0; ct < NT16; ++ct) {
+        const bf16x8_t vf = vfrag(x, ct);
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) acc[qt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qt], acc[qt][ct], 0, 0, 0);
+      }
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        s[qt][0] = sn[qt][0];
+        s[qt][1] = sn[qt][1];
+      }
+    }
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+      store_row16<D>(a, obase, t * BM + wave * 32 + qt * 16 + l16, g4, acc[qt], 1.0f / sum_row16(l_run[qt]), a.q_valid,
+                     gate_row);
+  }
+}
+
 // Merge of a split tile t (tile n_whole + t): the blocks whose step ranges
 // meet the tile each left one partial record (O_i, m_i, l_i) with O_i and l_i
 // relative to their own offset m_i; with M = max m_i the tile's result is
@@ -1987,6 +2248,20 @@ hipError_t launch_attention_d(AttnArgs a, hipStream_t stream) {
   const int64_t n_valid = (int64_t)a.B * a.H * nqv;
   const int64_t n_zero = (int64_t)a.B * a.H * (nq - nqv);
   const int64_t NU = (a.kv_valid + kSub - 1) / kSub;
+  if constexpr (D == 128) {
+    if (NU <= kResMaxSub) {
+      // Keys resident in LDS: one workgroup per (b, h) and residue class of
+      // its query tiles, G classes per head so that the grid covers the CUs.
+      const int64_t cus = std::max(device_cus(), 1);
+      const int64_t bh = (int64_t)a.B * a.H;
+      const int64_t G = std::max<int64_t>(1, std::min<int64_t>(nq, (cus + bh - 1) / bh));
+      if (bh * G > 0x7fffffffLL) return hipErrorInvalidValue;
+      a.nqv = (int32_t)nqv;
+      a.n_whole = a.n_split = a.n_split_blocks = 0;
+      attn_resident_kernel<<<dim3((unsigned)(bh * G)), NW * 64, 0, stream>>>(a, (int32_t)G);
+      return hipGetLastError();
+    }
+  }
   // One tile per CU at a time: the last round holds n_valid % cus tiles. When
   // that round is partial, split its tiles' steps over more blocks (at most
   // one per CU, each at least kSplitMinSteps steps, and more blocks than

@@ -159,6 +159,27 @@ def attention_bytes(wl) -> int:
     return total
 
 
+# Most key sub-tiles (32 keys each) whose K and V^T stay resident in LDS:
+# dense head-dim-128 attention over at most this many runs in one kernel
+# with no ring (the launcher's rule in attn_fwd.hip).
+RESIDENT_MAX_SUBTILES = 10
+
+
+def attend_kernels(wl) -> str:
+    """The kernels the attend stage launches for a workload, by the
+    launcher's dispatch: the general mode (causal mask, per-item lengths,
+    frame window) runs one tile per workgroup with no split; dense
+    head-dim-128 attention over at most RESIDENT_MAX_SUBTILES key sub-tiles
+    keeps its keys in LDS; every other dense launch may split the last
+    partial round of tiles and merge it."""
+    D = wl.head_dim
+    if wl.causal or wl.lengths or wl.window:
+        return f"attn_fwd_kernel<{D}, {'true' if wl.window else 'false'}> (general mode)"
+    if D == 128 and (wl.kv_valid + 31) // 32 <= RESIDENT_MAX_SUBTILES:
+        return "attn_resident_kernel (keys resident in LDS)"
+    return f"attn_fwd_kernel<{D}, false> + attn_merge_kernel<{D}> (when the last round is split)"
+
+
 def window_keys_per_row(wl, rows):
     """Visible keys of each query row under the workload's frame window: a
     row of an anchor frame sees all kv_valid keys; another row sees the
@@ -698,7 +719,7 @@ def main() -> int:
     main_roof, other_roof = (hbm_roof, mfma_roof) if hbm_bound else (mfma_roof, hbm_roof)
     roofline = {
         **{k: v for k, v in main_roof.items() if k != "work"},
-        "kernel": "attn_fwd_kernel + attn_merge_kernel (attend stage)",
+        "kernel": attend_kernels(wl) + ", attend stage",
         "traffic": measured_traffic(wl.name),
         "avg_ms": round(attn_avg, 4),
         "work_per_launch": main_roof["work"],

@@ -149,8 +149,10 @@ int h3attn_qkv_pack(const uint16_t* q, const uint16_t* k, const uint16_t* v,
  * then room for the partial results of query tiles whose keys the forward
  * splits over several workgroups (it does so when the last round of tiles
  * would leave compute units idle; two fp32 records of 136 KB per split
- * workgroup, at most 512 records). Returns 0 when a size is < 1 or the
- * result would overflow.
+ * workgroup, at most 512 records), then one fp32 per (b, head, 4096 keys):
+ * the largest key norm of each chunk, which bounds the scores when q and k
+ * are not normalised. Returns 0 when a size is < 1 or the result would
+ * overflow.
  */
 size_t h3attn_forward_workspace_bytes(int32_t B, int32_t Sq, int32_t Sk, int32_t H);
 
@@ -278,7 +280,9 @@ int h3attn_forward_stages(const uint16_t* q, const uint16_t* k, const uint16_t* 
  *   sequence positions of q and k alike.
  * Work split: no causal mask, no valid_lengths and no window uses the
  *   schedule of h3attn_forward (whole rounds of query tiles, the last
- *   round's key steps split over all compute units); otherwise one
+ *   round's key steps split over all compute units; at head_dim 128 with
+ *   at most 320 valid keys, the keys stay resident in LDS and each
+ *   workgroup streams several query tiles past them); otherwise one
  *   workgroup per (b, h, query block of 256 rows, 128 at head_dim 256), the
  *   longest first under the causal mask and the frame window.
  *

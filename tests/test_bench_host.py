@@ -67,3 +67,21 @@ def test_timing_stats():
     assert abs(s["cv"] - np.std([1, 2, 3, 10]) / 4.0) < 1e-4
     h = bench.host_info()
     assert h["host_cores"] == len(os.sched_getaffinity(0))
+
+
+def test_attend_kernel_names_follow_the_launcher():
+    """The bench names the kernels the launcher dispatches; its resident-key
+    limit is the kernel source's."""
+    import re
+    src = open(os.path.join(ROOT, "video_dit_dense_amd", "csrc", "attn_fwd.hip")).read()
+    assert int(re.search(r"constexpr int kResMaxSub = (\d+);", src).group(1)) == bench.RESIDENT_MAX_SUBTILES
+    W = {**workloads.WORKLOADS, **workloads.VARIANT_WORKLOADS}
+    assert bench.attend_kernels(W["cross"]).startswith("attn_resident_kernel")
+    assert bench.attend_kernels(W["full"]).startswith("attn_fwd_kernel<128, false> + attn_merge_kernel")
+    assert bench.attend_kernels(W["full_causal"]) == "attn_fwd_kernel<128, false> (general mode)"
+    assert bench.attend_kernels(W["full_window"]) == "attn_fwd_kernel<128, true> (general mode)"
+    assert bench.attend_kernels(W["full_d64"]).startswith("attn_fwd_kernel<64, false>")
+    wl = workloads.Workload("w", 1, 4096, 321, 2, 4096, 321, True, False, 0)
+    assert bench.attend_kernels(wl).startswith("attn_fwd_kernel<128")      # 11 sub-tiles: the ring kernel
+    wl = workloads.Workload("w", 1, 4096, 320, 2, 4096, 320, True, False, 0)
+    assert bench.attend_kernels(wl).startswith("attn_resident_kernel")

@@ -16,7 +16,7 @@ Coverage:
   an item's q_valid must be exactly +0.0.
 
 Bars: max-abs <= 2e-2 and relative RMS <= 5e-3 on the checked rows (the
-spec tolerance), and relative L2 <= 1e-2 on every checked row.
+tolerance the step is specified to), and relative L2 <= 1e-2 on every checked row.
 """
 import functools
 import math

@@ -1,6 +1,6 @@
 """GPU parity of the HIP path against the fp64 oracle, through the C-ABI.
 
-Bar (spec tolerance on bf16 outputs): max-abs error <= 2e-2 and
+Bar (the step's specified tolerance on bf16 outputs): max-abs error <= 2e-2 and
 relative RMS error <= 5e-3 against the fp64 oracle on the same seeded inputs.
 The prologue alone is held to a tighter bar: every output within half a
 bf16 ulp of the exact fp64 value (one correct rounding) plus 1e-6 absolute,

@@ -220,6 +220,25 @@ static int64_t check_split(const Shape& s, int D, int cus) {
     }
   }
   REQUIRE(next == U, "blocks cover %lld of %lld steps", (long long)next, (long long)U);
+  // The key sub-tiles each block reads: every split tile's [0, NU) exactly
+  // once, each segment a range inside [0, NU), and a block that starts in a
+  // tile as the first there begins at key sub-tile 0.
+  std::vector<std::vector<uint8_t>> keys(nsp, std::vector<uint8_t>(NU, 0));
+  for (int j = 0; j < nb; ++j) {
+    const SplitSeg& g = seg[j];
+    const int n0 = g.xe0 - g.xb0;
+    REQUIRE(g.kb0 >= 0 && g.kb0 + n0 <= NU, "block %d keys [%d, %d) of %d", j, g.kb0, g.kb0 + n0, NU);
+    for (int x = g.kb0; x < g.kb0 + n0; ++x) keys[g.tile][x]++;
+    if (j == 0 || seg[j - 1].tile < g.tile)   // the first block that starts inside its tile
+      REQUIRE(g.kb0 == 0, "first block %d of tile %d starts at key sub-tile %d", j, g.tile, g.kb0);
+    if (g.nseg == 2) {
+      REQUIRE(g.kb1 >= 0 && g.kb1 + g.xe1 == NU, "block %d second keys [%d, %d) of %d", j, g.kb1, g.kb1 + g.xe1, NU);
+      for (int x = g.kb1; x < g.kb1 + g.xe1; ++x) keys[g.tile + 1][x]++;
+    }
+  }
+  for (int t = 0; t < nsp; ++t)
+    for (int x = 0; x < NU; ++x)
+      REQUIRE(keys[t][x] == 1, "tile %d key sub-tile %d read %d times", t, x, (int)keys[t][x]);
   for (int t = 0; t < nsp; ++t) {
     REQUIRE(steps[t] == NU, "tile %d covered %d of %d steps", t, steps[t], NU);
     int j0, j1;

@@ -467,13 +467,14 @@ void attn_fwd_kernel(AttnArgs a) {
       const SplitSeg sg = split_segments(xcd_order(bid - a.n_whole, a.n_split_blocks), a.n_split, NU,
                                          a.n_split_blocks);
       g0 = a.n_whole + sg.tile;
-      xb0 = sg.xb0;
-      xe0 = sg.xe0;
+      xb0 = sg.kb0;
+      xe0 = sg.kb0 + (sg.xe0 - sg.xb0);
       rec0 = sg.rec0;
       if (sg.nseg == 2) {
         nseg = 2;
         g1 = g0 + 1;
-        xe1 = sg.xe1;
+        xb1 = sg.kb1;
+        xe1 = sg.kb1 + sg.xe1;
         rec1 = sg.rec1;
       }
     } else {

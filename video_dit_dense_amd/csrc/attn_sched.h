@@ -122,9 +122,25 @@ inline SplitPlan split_plan(int64_t n_valid, int64_t NU, int64_t cus, int64_t pa
 // split tile `tile` (its steps [xb0, xe0)) and, when nseg = 2, the first
 // xe1 steps of tile + 1. The block writes record rec0 = 2j for the first
 // tile and rec1 = 2j + 1 for the second.
+//
+// Step p of a split tile t reads key sub-tile (p - o_t) mod NU, where o_t is
+// the first block start inside tile t (split_key_origin): every block that
+// starts in a tile then begins at key sub-tile 0 (or, for a second start in
+// the same tile, at its own length), and every block that runs into a tile
+// from the previous one reads that tile's last sub-tiles. Blocks that share
+// an XCD (consecutive j, one head) so stream the same keys at the same time
+// and fetch them once through its L2, instead of each streaming its own
+// offset. No segment wraps: the rotation's seam is a block start. The keys
+// of segment 0 are [kb0, kb0 + xe0 - xb0), those of segment 1 [kb1, kb1 + xe1);
+// both lie in [0, NU), and a segment holding the last sub-tile ends there.
 struct SplitSeg {
-  int tile, xb0, xe0, rec0, nseg, xe1, rec1;
+  int tile, xb0, xe0, rec0, nseg, xe1, rec1, kb0, kb1;
 };
+__host__ __device__ inline int split_key_origin(int t, int n_split, int NU, int n_blocks) {
+  const int64_t U = (int64_t)n_split * NU;
+  const int64_t j = ((int64_t)t * NU * n_blocks + U - 1) / U;   // the first block with start >= t NU
+  return (int)(j * U / n_blocks - (int64_t)t * NU);
+}
 __host__ __device__ inline SplitSeg split_segments(int j, int n_split, int NU, int n_blocks) {
   const int64_t U = (int64_t)n_split * NU;
   const int64_t s0 = (int64_t)j * U / n_blocks;
@@ -135,13 +151,16 @@ __host__ __device__ inline SplitSeg split_segments(int j, int n_split, int NU, i
   const int64_t e0 = s1 - (int64_t)sg.tile * NU;
   sg.xe0 = (int)(e0 < NU ? e0 : NU);
   sg.rec0 = 2 * j;
+  sg.kb0 = sg.xb0 - split_key_origin(sg.tile, n_split, NU, n_blocks);
   sg.nseg = 1;
   sg.xe1 = 0;
   sg.rec1 = -1;
+  sg.kb1 = 0;
   if (s1 > (int64_t)(sg.tile + 1) * NU) {
     sg.nseg = 2;
     sg.xe1 = (int)(s1 - (int64_t)(sg.tile + 1) * NU);
     sg.rec1 = 2 * j + 1;
+    sg.kb1 = NU - split_key_origin(sg.tile + 1, n_split, NU, n_blocks);
   }
   return sg;
 }

@@ -18,11 +18,22 @@ SRC = os.path.join(ROOT, "tests", "sched_check.cpp")
 
 
 def record_floats(D):
-    """Floats per partial record: D/2 accumulators per thread, then the
-    thread's row offsets and sums (two each at head dim 128), for the 512
-    threads of a head-dim-64/128 workgroup or the 256 of a head-dim-256 one."""
-    threads = 512 if D <= 128 else 256
-    return (D // 2 + (4 if D == 128 else 2)) * threads
+    """Floats per partial record, per thread: the accumulators of its share
+    of the workgroup's query rows x D channels, then one row offset and one
+    partial sum per 16-row query tile it holds (four at head dim 64, whose
+    waves hold 64 rows; two at 128, 32 rows), over the 512 threads of a
+    head-dim-64/128 workgroup; at 256, D/2 accumulators and one of each over
+    256 threads (32 rows per wave of 64 lanes)."""
+    if D <= 128:
+        tiles = 4 if D == 64 else 2
+        rows = 8 * 16 * tiles
+        return (rows * D // 512 + 2 * tiles) * 512
+    return (D // 2 + 2) * 256
+
+
+def query_rows(D):
+    """Query rows per workgroup, the multiple the workspace pads q to."""
+    return {64: 512, 128: 256, 256: 128}[D]
 
 
 @pytest.fixture(scope="module")
@@ -47,8 +58,9 @@ def test_split_records_fit_the_workspace(sched_output):
     assert len(rows) >= 10
     for B, Sq, Sk, H, D, slots, max_rec in ((int(x) for x in r) for r in rows):
         assert max_rec < slots, (B, Sq, Sk, H, D)
-        pad = lambda s: (s + 255) // 256 * 256   # noqa: E731
+        pad = lambda s, m=256: (s + m - 1) // m * m   # noqa: E731
         kn = (B * H * ((pad(Sk) + 4095) // 4096) * 4 + 255) // 256 * 256   # key-norm maxima
-        needed = (B * H * pad(Sq) + 2 * B * H * pad(Sk)) * 2 * D + slots * record_floats(D) * 4 + kn
+        needed = (B * H * pad(Sq, max(256, query_rows(D))) + 2 * B * H * pad(Sk)) * 2 * D + \
+            slots * record_floats(D) * 4 + kn
         got = h3attn.forward_ex_workspace_bytes(B, Sq, Sk, H, H, head_dim=D)
         assert got == needed, (B, Sq, Sk, H, D, got, needed)

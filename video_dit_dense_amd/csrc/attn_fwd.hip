@@ -173,29 +173,26 @@ constexpr float kBoundMax = 60.0f;
 constexpr float kBoundSlack = 1.0f + 1.0f / 1024.0f;
 constexpr int kSub = 32;                       // keys per sub-tile
 
-// Tiling by head dim D (64, 128 or 256). D <= 128: eight waves (256 query
-// rows) per workgroup, two per SIMD, and an eight-slot ring. D = 256 holds
-// twice the accumulators and fragments, so one wave per SIMD (four waves,
-// 128 rows) with the whole register file, and a K ring and a V^T ring of
-// four 16 KB slots each.
+// Tiling by head dim D (64, 128 or 256). D <= 128: eight waves per
+// workgroup, two per SIMD, an eight-slot ring, and 16x16x32 matrix-core
+// instructions on QT 16-row query tiles per wave (four at 64, so 512 rows per
+// workgroup; two at 128, 256 rows). D = 256 holds twice the accumulators and
+// fragments of a 32-row tile, so one wave per SIMD (four waves, 128 rows)
+// with the whole register file, 32x32x16 instructions, and a K ring and a
+// V^T ring of four 16 KB slots each.
 template <int D>
 struct Geo {
   static_assert(D == 64 || D == 128 || D == 256, "head dim");
   static constexpr int NW = D <= 128 ? 8 : 4;           // waves per workgroup
   static constexpr int WPE = D <= 128 ? 2 : 1;          // waves per SIMD
-  static constexpr int BM = NW * 32;                    // query rows per workgroup
-  // kPipe: the software-pipelined step (one wave per SIMD at 256) instead of
-  // the two-wave ping-pong.
+  // kM16: the two-wave ping-pong on 16x16x32 matrix-core instructions with
+  // QT 16-row query tiles per wave; otherwise (D = 256) the
+  // software-pipelined step (kPipe) on 32x32x16, one wave per SIMD.
+  static constexpr bool kM16 = D <= 128;
   static constexpr bool kPipe = D == 256;
-  // kJit (ping-pong only): the X phase reads its own fragments just in time,
-  // one per matrix-core instruction, instead of the Y phase reading them all.
-  // That moves the LDS reads' issue time off the softmax wave; it pays at
-  // head dim 64, where the Y phase is the longer one, and is neutral at 128,
-  // which runs at the chip's power limit.
-  static constexpr bool kJit = D == 64;
-  // kM16: head dim 128 runs the ping-pong on 16x16x32 matrix-core
-  // instructions (two 16-row query tiles per wave) instead of 32x32x16.
-  static constexpr bool kM16 = D == 128;
+  static constexpr int QT = attn_query_tiles(D);        // 16-row query tiles per wave (kM16)
+  static constexpr int WROWS = kM16 ? 16 * QT : 32;     // query rows per wave
+  static constexpr int BM = NW * WROWS;                 // query rows per workgroup
   static constexpr int kRing = D <= 128 ? 8 : 4;        // ring depth (sub-tiles; per operand when kPipe)
   static constexpr int kKBytes = kSub * D * 2;          // K sub-tile: 32 rows x 2D bytes
   static constexpr int kVBytes = D * kSub * 2;          // V^T sub-tile: D rows x 64 B
@@ -205,19 +202,20 @@ struct Geo {
   static constexpr int kSwz = (D / 8 < 16 ? D / 8 : 16) - 1;   // K chunk swizzle mask
   static constexpr int nK = kKBytes / 1024;             // 1 KB direct loads per sub-tile (K)
   static constexpr int LDPS = (kKBytes + kVBytes) / 1024 / NW;   // per wave per sub-tile
-  static constexpr int kSlotsPerSeg = 65536 / kBufBytes;         // slots in a 16-bit LDS offset
-  static constexpr int kRecM = NT * 16, kRecL = NT * 16 + 1;     // partial record layout
+  // Partial record layout per thread: kRecA accumulator floats, then the row
+  // offsets and partial sums (QT of each for kM16; one each at 256, at
+  // kRecM and kRecL).
+  static constexpr int kRecA = kM16 ? WROWS * D / 64 : NT * 16;
+  static constexpr int kRecM = kRecA, kRecL = kRecA + 1;
   // LDS: the ring and one int per wave (its SIMD) for D <= 128; at 256 the
-  // two operand rings fill the 160 KB.
+  // two operand rings fill 128 KB.
   static constexpr int kLdsBytes = kPipe ? 2 * kRing * kKBytes : kRing * kBufBytes + NW * 4;
   static_assert(LDPS * NW * 1024 == kKBytes + kVBytes, "tile split");
-  static_assert(kPipe || kRing <= 2 * kSlotsPerSeg, "two address segments at most");
   static_assert(kLdsBytes <= 160 * 1024, "LDS");
-  // Floats each thread writes to a partial record (the accumulators, then
-  // two row offsets and two partial sums at head dim 128, else one of each)
-  // fill exactly the record size the host reserves per record.
-  static_assert((kM16 ? kRecM + 4 : kRecL + 1) * NW * 64 == attn_part_floats(D), "partial record size");
-  static_assert(NT * 16 == D / 2, "accumulator registers per thread");
+  static_assert(BM == attn_rows(D) && NW * 64 == attn_threads(D), "tiling constants");
+  // Floats each thread writes to a partial record fill exactly the record
+  // size the host reserves per record.
+  static_assert((kM16 ? kRecA + 2 * QT : kRecL + 1) * NW * 64 == attn_part_floats(D), "partial record size");
 };
 
 // LDS layouts (no padding; XOR swizzles keep every 8-lane group of a
@@ -514,26 +512,35 @@ void attn_fwd_kernel(AttnArgs a) {
   uint16_t* obase = a.o + ((int64_t)b * a.Sq * a.H + h) * D;
   const uint16_t* gate_row = a.gate ? a.gate + (int64_t)b * a.Sq * a.H + h : nullptr;
   if constexpr (G::kM16) {
-  // Head dim 128 on v_mfma_f32_16x16x32_bf16 (A 16 x 32: lane l supplies
-  // row l%16, k = 8(l/16) .. +7; B 32 x 16: column l%16, the same k; D 16 x
-  // 16: lane l register r holds row 4(l/16) + r, column l%16). The smaller
-  // shape sustains more flops at the chip's power limit. Each wave keeps its
-  // 32 query rows as two 16-row tiles qt: QK^T is 2 key tiles x 2 query tiles
-  // x D/32 channel chunks (each K fragment serves both query tiles), so lane
-  // l holds, for query row 16 qt + l%16, the 8 keys 16 kt + 4 g4 + r (g4 =
-  // l/16, r < 4); a row's 32 keys are spread over the four lanes l%16 + 16 j.
-  // PV takes those 8 keys as positions 8 g4 .. 8 g4 + 7 of the sub-tile, with
-  // V^T's keys permuted to match (position 8g + j holds key 16 (j/4) + 4g +
-  // j%4), and is D/16 channel tiles x 2 query tiles. The ring, the loads and
-  // the ping-pong schedule are those of the 32x32 path; the X phase reads its
-  // own fragments, four ahead, in fenced groups.
+  // Head dims 64 and 128 on v_mfma_f32_16x16x32_bf16 (A 16 x 32: lane l
+  // supplies row l%16, k = 8(l/16) .. +7; B 32 x 16: column l%16, the same k;
+  // D 16 x 16: lane l register r holds row 4(l/16) + r, column l%16). The
+  // smaller shape sustains more flops at the chip's power limit. Each wave
+  // keeps its 16 QT query rows as QT 16-row tiles qt: QK^T is 2 key tiles x
+  // QT query tiles x D/32 channel chunks (each K fragment serves every query
+  // tile), so lane l holds, for query row 16 qt + l%16, the 8 keys 16 kt + 4
+  // g4 + r (g4 = l/16, r < 4); a row's 32 keys are spread over the four lanes
+  // l%16 + 16 j. PV takes those 8 keys as positions 8 g4 .. 8 g4 + 7 of the
+  // sub-tile, with V^T's keys permuted to match (position 8g + j holds key 16
+  // (j/4) + 4g + j%4), and is D/16 channel tiles x QT query tiles (each V^T
+  // fragment serves every query tile). Head dim 64 holds four query tiles
+  // (64 rows) per wave, so that each fragment read and each step's softmax
+  // feed as many matrix-core cycles as at 128.
+  //
+  // Schedule (ping-pong): the two waves of a SIMD alternate an X phase
+  // (matrix-core work only: QK^T of sub-tile u+1 and PV of sub-tile u, the
+  // wave reading its own fragments four ahead in fenced groups) and a Y
+  // phase (softmax of u+1, the first fragment reads of the next X, one ring
+  // refill), separated by workgroup barriers, so one wave feeds the matrix
+  // core while the other computes the softmax.
   constexpr int NC = D / 32;       // 32-channel chunks
   constexpr int NT16 = D / 16;     // 16-channel output tiles
   const int l16 = lane & 15, g4 = lane >> 4;
-  int rowq[2], limq[2];
+  constexpr int QT = G::QT;        // 16-row query tiles per wave
+  int rowq[QT], limq[QT];
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    rowq[qt] = q0 + wave * 32 + qt * 16 + l16;
+  for (int qt = 0; qt < QT; ++qt) {
+    rowq[qt] = q0 + wave * G::WROWS + qt * 16 + l16;
     limq[qt] = a.causal ? min(rowq[qt], kvv_t - 1) : kvv_t - 1;
   }
   auto xmap = [&](int v) __attribute__((always_inline)) {
@@ -541,10 +548,12 @@ void attn_fwd_kernel(AttnArgs a) {
     else return v;
   };
   int x_mask = min(a.causal ? q0 / kSub : 0x7fffffff, (kvv_t % kSub) ? kvv_t / kSub : 0x7fffffff);
-  int c_row[2] = {-1, -1};
+  int c_row[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) c_row[qt] = -1;
   if constexpr (WIN) {
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+    for (int qt = 0; qt < QT; ++qt) {
       const int f = rowq[qt] / a.win_F;
       c_row[qt] = f < a.win_A ? -1 : (f - a.win_A) / a.win_C;
     }
@@ -553,11 +562,11 @@ void attn_fwd_kernel(AttnArgs a) {
 
   // Q fragments (B operand of S^T = K Q^T): query row 16 qt + l%16 of the
   // wave, channels 32 cc + 8 g4 .. +7. Loaded before the ring fill.
-  bf16x8_t qf[2][NC];
+  bf16x8_t qf[QT][NC];
   {
-    const uint16_t* qp = a.qw + ((int64_t)bh * a.Sq_pad + q0 + wave * 32 + l16) * D + g4 * 8;
+    const uint16_t* qp = a.qw + ((int64_t)bh * a.Sq_pad + q0 + wave * G::WROWS + l16) * D + g4 * 8;
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
+    for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
       for (int cc = 0; cc < NC; ++cc) qf[qt][cc] = *reinterpret_cast<const bf16x8_t*>(qp + qt * 16 * D + cc * 32);
   }
@@ -603,7 +612,7 @@ void attn_fwd_kernel(AttnArgs a) {
   // tuples (tile i = qt NT16 + ct in tuple i/4, slice i%4): with the tiles as
   // separate 4-register values the register allocator writes most results to
   // fresh registers instead of in place and doubles them.
-  constexpr int NA = 2 * NT16 / 4;
+  constexpr int NA = QT * NT16 / 4;
   f32x16_t accq[NA];
 #pragma unroll
   for (int i = 0; i < NA; ++i)
@@ -622,10 +631,15 @@ void attn_fwd_kernel(AttnArgs a) {
     const int o = (i & 3) * 4;
     return f32x4_t{accq[i >> 2][o], accq[i >> 2][o + 1], accq[i >> 2][o + 2], accq[i >> 2][o + 3]};
   };
-  float m_run[2] = {0.f, 0.f};   // row offsets (exp2 units), shared by the row's four lanes
-  float l_run[2] = {0.f, 0.f};   // this lane's share of each row sum
-  bool seen[2] = {true, true};   // the row has met a visible key
-  f32x4_t msplat[2];             // -m_run: the QK^T accumulators' initial value
+  float m_run[QT];      // row offsets (exp2 units), shared by the row's four lanes
+  float l_run[QT];      // this lane's share of each row sum
+  bool seen[QT];        // the row has met a visible key
+  f32x4_t msplat[QT];   // -m_run: the QK^T accumulators' initial value
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    m_run[qt] = l_run[qt] = 0.f;
+    seen[qt] = true;
+  }
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
   auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
 
@@ -697,25 +711,28 @@ void attn_fwd_kernel(AttnArgs a) {
     bounded = Mu <= kBoundMax;
     if (bounded) {
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
+      for (int qt = 0; qt < QT; ++qt) {
         m_run[qt] = Mu;
         msplat[qt] = f32x4_t{-Mu, -Mu, -Mu, -Mu};
       }
     }
   } else if (a.knorm != nullptr) {
     const float kmax = key_norm_max(a, bh_kv);
-    float m[2];
+    float m[QT];
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+    for (int qt = 0; qt < QT; ++qt) {
       float ss = 0.f;
 #pragma unroll
       for (int cc = 0; cc < NC; ++cc) ss = sum_sq(qf[qt][cc], ss);
       m[qt] = sqrtf(sum_row16(ss)) * kmax * kBoundSlack;
     }
-    bounded = __builtin_amdgcn_ballot_w64(!(m[0] <= kBoundMax) | !(m[1] <= kBoundMax)) == 0;
+    bool over = false;
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) over = over | !(m[qt] <= kBoundMax);
+    bounded = __builtin_amdgcn_ballot_w64(over) == 0;
     if (bounded) {
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
+      for (int qt = 0; qt < QT; ++qt) {
         m_run[qt] = m[qt];
         msplat[qt] = f32x4_t{-m[qt], -m[qt], -m[qt], -m[qt]};
       }
@@ -728,13 +745,16 @@ void attn_fwd_kernel(AttnArgs a) {
   // more than 2^kRescaleLog2 (rare), raise the offsets by the rows' excess,
   // shift the scores and rescale the accumulators and partial sums; with
   // MASK, a row that saw no key before takes its first keys' maximum.
-  auto maybe_rescale16 = [&](f32x4_t (&s)[2][2], const float* mx, auto mask) __attribute__((always_inline)) {
-    bool trigger = (mx[0] > kRescaleLog2) | (mx[1] > kRescaleLog2);
-    if constexpr (WIN && decltype(mask)::value)
-      trigger = trigger | (!seen[0] & (mx[0] != -INFINITY)) | (!seen[1] & (mx[1] != -INFINITY));
+  auto maybe_rescale16 = [&](f32x4_t (&s)[QT][2], const float* mx, auto mask) __attribute__((always_inline)) {
+    bool trigger = false;
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      trigger = trigger | (mx[qt] > kRescaleLog2);
+      if constexpr (WIN && decltype(mask)::value) trigger = trigger | (!seen[qt] & (mx[qt] != -INFINITY));
+    }
     if (__builtin_amdgcn_ballot_w64(trigger) != 0) {
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
+      for (int qt = 0; qt < QT; ++qt) {
         float delta = max_row16(mx[qt]);
         float alpha;
         if constexpr (WIN && decltype(mask)::value) {
@@ -763,9 +783,9 @@ void attn_fwd_kernel(AttnArgs a) {
   };
   // bf16 probabilities p = exp2(s) as the PV operand of each query tile
   // (element j: key 16 (j/4) + 4 g4 + j%4), and this lane's share of the sums.
-  auto probs16 = [&](const f32x4_t (&s)[2][2], bf16x8_t* pf) __attribute__((always_inline)) {
+  auto probs16 = [&](const f32x4_t (&s)[QT][2], bf16x8_t* pf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+    for (int qt = 0; qt < QT; ++qt) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) pf[qt][j] = (__bf16)__builtin_amdgcn_exp2f(s[qt][j >> 2][j & 3]);
 #pragma unroll
@@ -777,12 +797,13 @@ void attn_fwd_kernel(AttnArgs a) {
   };
 
   // Fragment reads. K fragment (kt, cc): key row 16 kt + l%16, chunk 4 cc +
-  // g4, stored at (4 cc + g4) ^ (l%16) = (g4 ^ l%16) ^ 4 cc, so one address
-  // register per cc; V^T fragment ct: channel row 16 ct + l%16, chunk g4.
-  // The V^T base (64 KB) is hidden from the compiler so that it stays in the
-  // register and out of the offset field.
-  static_assert(kRing * kKBytes == 65536, "K sub-tiles fill the first 64 KB");
-  bf16x8_t pf[2];
+  // g4, stored at (4 cc + g4) ^ s = (g4 ^ s) ^ 4 cc, so one address
+  // register per cc (the swizzle takes l%16 & kSwz); V^T fragment ct:
+  // channel row 16 ct + l%16, chunk g4. The V^T base (kRing K sub-tiles in)
+  // is hidden from the compiler so that it stays in the register and out of
+  // the offset field.
+  static_assert(kRing * kKBytes <= 65536, "K sub-tiles within the first 64 KB");
+  bf16x8_t pf[QT];
   const uint32_t kb16 = l16 * (2 * D) + ((g4 ^ (l16 & G::kSwz)) * 16);
   uint32_t ka[NC];
 #pragma unroll
@@ -809,7 +830,7 @@ void attn_fwd_kernel(AttnArgs a) {
   // instructions that use fragment g and the read of fragment g + 4; fr holds
   // the first four fragments, read by the caller.
   bf16x8_t fr[4];
-  auto xphase = [&](f32x4_t (&s)[2][2], auto slot_k, auto slot_v, bool do_qk) __attribute__((always_inline)) {
+  auto xphase = [&](f32x4_t (&s)[QT][2], auto slot_k, auto slot_v, bool do_qk) __attribute__((always_inline)) {
     bf16x8_t gf[NG];
 #pragma unroll
     for (int g = 0; g < 4; ++g) gf[g] = fr[g];
@@ -819,12 +840,12 @@ void attn_fwd_kernel(AttnArgs a) {
       if constexpr (g < 2 * NC) {
         if (do_qk) {
 #pragma unroll
-          for (int qt = 0; qt < 2; ++qt)
+          for (int qt = 0; qt < QT; ++qt)
             s[qt][g & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gf[g], qf[qt][g >> 1], s[qt][g & 1], 0, 0, 0);
         }
       } else {
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) acc_mfma(qt, g - 2 * NC, gf[g], pf[qt]);
+        for (int qt = 0; qt < QT; ++qt) acc_mfma(qt, g - 2 * NC, gf[g], pf[qt]);
       }
       fence();
     });
@@ -839,21 +860,21 @@ void attn_fwd_kernel(AttnArgs a) {
     // (online path), or start from the fixed offset (bounded path).
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kRing - 4) * LDPS) : "memory");
     __syncthreads();
-    f32x4_t s[2][2];
+    f32x4_t s[QT][2];
     {
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
+      for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) s[qt][kt] = BND ? msplat[qt] : f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int g = 0; g < 2 * NC; ++g) {
         const bf16x8_t kfr = frag(g, 0, 0);
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
+        for (int qt = 0; qt < QT; ++qt)
           s[qt][g & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfr, qf[qt][g >> 1], s[qt][g & 1], 0, 0, 0);
       }
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
+      for (int qt = 0; qt < QT; ++qt) {
         if constexpr (BND) {
           mask16(s[qt], xmap(xb), qt);
         } else {
@@ -884,7 +905,7 @@ void attn_fwd_kernel(AttnArgs a) {
     auto step = [&](int u, auto mask_next, auto slot_vn, auto slot_kn, auto slot_vc, auto slot_kc) __attribute__((always_inline)) {
       fence();
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
+      for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) s[qt][kt] = msplat[qt];
       xphase(s, slot_kc, slot_vc, true);
@@ -896,12 +917,12 @@ void attn_fwd_kernel(AttnArgs a) {
       if constexpr (BND) {
         if constexpr (decltype(mask_next)::value) {
 #pragma unroll
-          for (int qt = 0; qt < 2; ++qt) mask16(s[qt], xmap(u + 1), qt);
+          for (int qt = 0; qt < QT; ++qt) mask16(s[qt], xmap(u + 1), qt);
         }
       } else {
-        float mx[2];
+        float mx[QT];
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) mx[qt] = rowmax16(s[qt], xmap(u + 1), qt, mask_next);
+        for (int qt = 0; qt < QT; ++qt) mx[qt] = rowmax16(s[qt], xmap(u + 1), qt, mask_next);
         maybe_rescale16(s, mx, mask_next);
       }
       probs16(s, pf);
@@ -928,7 +949,7 @@ void attn_fwd_kernel(AttnArgs a) {
       for (int ct = 0; ct < NT16; ++ct) {
         const bf16x8_t vfr = frag(2 * NC + ct, 0, vs);
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) acc_mfma(qt, ct, vfr, pf[qt]);
+        for (int qt = 0; qt < QT; ++qt) acc_mfma(qt, ct, vfr, pf[qt]);
       }
     }
   };
@@ -939,7 +960,7 @@ void attn_fwd_kernel(AttnArgs a) {
 
   if (rec < 0) {
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+    for (int qt = 0; qt < QT; ++qt) {
       const float l = sum_row16(l_run[qt]);
       f32x4_t at[NT16];
 #pragma unroll
@@ -949,13 +970,13 @@ void attn_fwd_kernel(AttnArgs a) {
   } else {
     float* pr = a.part + (int64_t)rec * attn_part_floats(D) + tid;
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+    for (int qt = 0; qt < QT; ++qt) {
 #pragma unroll
       for (int ct = 0; ct < NT16; ++ct)
 #pragma unroll
         for (int r = 0; r < 4; ++r) pr[((qt * NT16 + ct) * 4 + r) * T] = accq[(qt * NT16 + ct) >> 2][((qt * NT16 + ct) & 3) * 4 + r];
-      pr[(G::kRecM + qt) * T] = m_run[qt];
-      pr[(G::kRecM + 2 + qt) * T] = l_run[qt];
+      pr[(G::kRecA + qt) * T] = m_run[qt];
+      pr[(G::kRecA + QT + qt) * T] = l_run[qt];
     }
   }
   } else {
@@ -1426,318 +1447,6 @@ void attn_fwd_kernel(AttnArgs a) {
     // Let the refills nobody reads retire before the workgroup ends or the
     // next segment refills the rings.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  } else {
-    // Per-lane byte offsets of the direct loads within a sub-tile (K and V^T
-    // sub-tiles are contiguous blocks of kKBytes in the workspace). Load i of
-    // this wave fills LDS bytes [1024 j, 1024 j + 1024) of the slot, j = wave
-    // + NW i: K's chunks for j < nK, V^T's after them. The lane that fills
-    // LDS chunk Q fetches the logical chunk the swizzle puts there.
-    const uint16_t* kw = a.kw + (int64_t)bh_kv * a.Sk_pad * D;
-    const uint16_t* vt = a.vt + (int64_t)bh_kv * a.Sk_pad * D;
-    int loff[LDPS];
-#pragma unroll
-    for (int i = 0; i < LDPS; ++i) {
-      const int j = wave + NW * i;
-      if (j < G::nK) {
-        const int Q = j * 64 + lane;
-        const int r = Q / (D / 8), p = Q % (D / 8);
-        loff[i] = (r * D + ((p ^ (r & G::kSwz)) * 8)) * 2;
-      } else {
-        const int Q = (j - G::nK) * 64 + lane;
-        const int d = Q >> 2, p = Q & 3;
-        loff[i] = (d * kSub + ((p ^ ((d >> 2) & 3)) * 8)) * 2;
-      }
-    }
-    // One buffer resource per sub-tile (base in SGPRs, 8 KB range), so the
-    // loads need no vector address arithmetic and offsets stay 32-bit at any
-    // sequence length. Every step issues exactly one refill so the wait counts
-    // are the same at every step; a refill past the last sub-tile gets an
-    // empty range (the hardware returns zeros without touching memory) and
-    // lands in a ring slot that no later step reads.
-    auto issue_loads = [&](int x) {
-      uint8_t* slot = lds + ((x - xb) & (kRing - 1)) * kBufBytes;
-      const bool live = x < xe;
-      const int xs = live ? xmap(x) : 0;
-      const uint16_t* kx = kw + (int64_t)xs * (kSub * D);
-      const uint16_t* vx = vt + (int64_t)xs * (kSub * D);
-#pragma unroll
-      for (int i = 0; i < LDPS; ++i) {
-        const int j = wave + NW * i;
-        load_lds16(j < G::nK ? kx : vx, live ? kKBytes : 0, loff[i], slot + j * 1024);
-      }
-    };
-#pragma unroll
-    for (int i = 0; i < kRing - 1; ++i) issue_loads(xb + i);
-
-    f32x16_t msplat;         // -m_run in every slot: the QK^T accumulator's initial value
-    // The scores arrive as s - m_run. If some row of the wave exceeds its
-    // offset by more than 2^kRescaleLog2 (rare), raise that row's m_run by its
-    // excess, shift the scores and rescale the accumulator and partial sum.
-    // With MASK, a row that saw no key before (seen false, m_run 0) takes its
-    // first visible keys' maximum as its offset.
-    auto maybe_rescale = [&](f32x16_t& s, float mx, auto mask) {
-      bool trigger = mx > kRescaleLog2;
-      if constexpr (WIN && decltype(mask)::value) trigger = trigger || (!seen && mx != -INFINITY);
-      if (__builtin_amdgcn_ballot_w64(trigger) != 0) {
-        float delta = max_lane_pair(mx);
-        float alpha;
-        if constexpr (WIN && decltype(mask)::value) {
-          const bool fresh = !seen && delta != -INFINITY;
-          seen = seen || fresh;
-          delta = fresh ? delta : fmaxf(delta, 0.f);
-          // A fresh row's accumulator and sum are still zero (exp2(-delta)
-          // would overflow when its first visible scores lie far below 0).
-          alpha = fresh ? 1.f : __builtin_amdgcn_exp2f(-delta);
-        } else {
-          delta = fmaxf(delta, 0.f);
-          alpha = __builtin_amdgcn_exp2f(-delta);
-        }
-        m_run += delta;
-        l_run *= alpha;
-        // msplat - delta is exactly -(m_run + delta): updated in place so the
-        // splat keeps its registers across the branch.
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          s[r] -= delta;
-          msplat[r] -= delta;
-        }
-#pragma unroll
-        for (int dt = 0; dt < NT; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
-      }
-    };
-    // bf16 probabilities p = exp2(s) of the sub-tile scores (already shifted
-    // by the row offset), as the two B operands of PV, and this lane's share
-    // of their row sum.
-    auto probs = [&](const f32x16_t& s, bf16x8_t* pf) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int i = 0; i < 8; i += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(s[ks * 8 + i]);
-          const float p1 = __builtin_amdgcn_exp2f(s[ks * 8 + i + 1]);
-          pf[ks][i] = (__bf16)p0;
-          pf[ks][i + 1] = (__bf16)p1;
-        }
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int i = 0; i < 8; i += 2) {
-          const bf16x2_t pp = {pf[ks][i], pf[ks][i + 1]};
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_run, false);
-        }
-    };
-
-    bf16x8_t kf[NF], vf[NF], pf[2];
-    // Ring slot of sub-tile x is (x - xb) mod kRing. Fragment reads take the
-    // slot either at run time or, in the unrolled steady state, as a
-    // compile-time constant that lands in the instruction's offset field (the
-    // field holds 16 bits, so slots past the first 64 KB use addresses biased
-    // by 64 KB).
-    constexpr int SPS = G::kSlotsPerSeg;
-    uint32_t ka[NF], kah[NF], vah[2];
-#pragma unroll
-    for (int kk = 0; kk < NF; ++kk) {
-      ka[kk] = kbase ^ (32u * kk);
-      kah[kk] = ka[kk] + SPS * kBufBytes;
-    }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) vah[ks] = vaddr[ks] + SPS * kBufBytes;
-    auto read_k = [&](auto slot) {
-#pragma unroll
-      for (int kk = 0; kk < NF; ++kk) {
-        if constexpr (std::is_integral_v<decltype(slot)>)
-          kf[kk] = *reinterpret_cast<const bf16x8_t*>(lds + slot * kBufBytes + ka[kk]);
-        else if constexpr (decltype(slot)::value < SPS)
-          kf[kk] = *reinterpret_cast<const bf16x8_t*>(lds + decltype(slot)::value * kBufBytes + ka[kk]);
-        else
-          kf[kk] = *reinterpret_cast<const bf16x8_t*>(lds + (decltype(slot)::value - SPS) * kBufBytes + kah[kk]);
-      }
-    };
-    auto read_v = [&](auto slot) {
-#pragma unroll
-      for (int i = 0; i < NF; ++i) {
-        if constexpr (std::is_integral_v<decltype(slot)>)
-          vf[i] = *reinterpret_cast<const bf16x8_t*>(lds + slot * kBufBytes + vaddr[i & 1] + (i >> 1) * 2048);
-        else if constexpr (decltype(slot)::value < SPS)
-          vf[i] = *reinterpret_cast<const bf16x8_t*>(lds + decltype(slot)::value * kBufBytes + vaddr[i & 1] + (i >> 1) * 2048);
-        else
-          vf[i] = *reinterpret_cast<const bf16x8_t*>(lds + (decltype(slot)::value - SPS) * kBufBytes + vah[i & 1] + (i >> 1) * 2048);
-      }
-    };
-    auto rslot = [&](int x) { return (x - xb) & (kRing - 1); };
-
-    // The rest of the tile, with the online maximum (BND false) or the
-    // fixed per-row bounds (BND true: no row maximum, no rescale).
-    auto run_tile = [&](auto bnd) {
-    constexpr bool BND = decltype(bnd)::value;
-      // Sub-tiles xb..xb+2 first (the other loads may still fly), then the
-      // prologue: scores of xb, which set each row's offset to its exact maximum
-      // (so the row keeps one probability of 1), and their probabilities.
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kRing - 4) * LDPS) : "memory");
-      __syncthreads();
-      f32x16_t s;
-      {
-        read_k(std::integral_constant<int, 0>{});
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = BND ? msplat[r] : 0.f;
-#pragma unroll
-        for (int kk = 0; kk < NF; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s, 0, 0, 0);
-        if constexpr (!G::kJit) {
-          read_k(rslot(min(xb + 1, xe - 1)));
-          read_v(std::integral_constant<int, 0>{});
-        }
-        if constexpr (BND) {
-          mask_scores(s, xmap(xb));
-        } else {
-          const float mx0 = rowmax(s, xmap(xb), Mask{});
-          m_run = max_lane_pair(mx0);
-          // A row with no visible key here (possible only under a frame window)
-          // starts from offset 0 and takes its offset from the first keys it sees.
-          if constexpr (WIN) {
-            seen = m_run != -INFINITY;
-            if (!seen) m_run = 0.f;
-          }
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            s[r] -= m_run;
-            msplat[r] = -m_run;
-          }
-        }
-        probs(s, pf);
-      }
-
-      // Step u alternates two phases separated by workgroup barriers:
-      //   X: the matrix-core work, QK^T of u+1 (K fragments of u+1 in kf) and
-      //      PV of u (V fragments of u in vf, probabilities of u in pf);
-      //   Y: the vector and LDS work, refill of the ring slot of u-1, reads of
-      //      K(u+2) and V(u+1), row maxima and rescale of u+1, probabilities and
-      //      row sums of u+1.
-      // The second wave of each SIMD passes one extra barrier first, so it runs
-      // Y while the first runs X and the other way round: the matrix core of the
-      // SIMD always has one wave's work while the other wave does the softmax.
-      // Both roles execute the same instructions in the same order.
-      // One fragment of an X phase: f even is K fragment f/2, f odd is V
-      // fragment f/2 (the order the phase consumes them).
-      auto kread = [&](auto slot, int kk) -> bf16x8_t {
-        if constexpr (std::is_integral_v<decltype(slot)>)
-          return *reinterpret_cast<const bf16x8_t*>(lds + slot * kBufBytes + ka[kk]);
-        else if constexpr (decltype(slot)::value < SPS)
-          return *reinterpret_cast<const bf16x8_t*>(lds + decltype(slot)::value * kBufBytes + ka[kk]);
-        else
-          return *reinterpret_cast<const bf16x8_t*>(lds + (decltype(slot)::value - SPS) * kBufBytes + kah[kk]);
-      };
-      auto vread = [&](auto slot, int i) -> bf16x8_t {
-        if constexpr (std::is_integral_v<decltype(slot)>)
-          return *reinterpret_cast<const bf16x8_t*>(lds + slot * kBufBytes + vaddr[i & 1] + (i >> 1) * 2048);
-        else if constexpr (decltype(slot)::value < SPS)
-          return *reinterpret_cast<const bf16x8_t*>(lds + decltype(slot)::value * kBufBytes + vaddr[i & 1] + (i >> 1) * 2048);
-        else
-          return *reinterpret_cast<const bf16x8_t*>(lds + (decltype(slot)::value - SPS) * kBufBytes + vah[i & 1] + (i >> 1) * 2048);
-      };
-      auto xread = [&](int f, auto slot_k, auto slot_v) -> bf16x8_t {
-        return (f & 1) ? vread(slot_v, f >> 1) : kread(slot_k, f >> 1);
-      };
-      bf16x8_t fr[4];   // kJit: the first four fragments of the next X phase
-      // slot_vn, slot_kn: the slots of V(u+1) and K(u+2), read in this step's
-      // Y phase; slot_vc, slot_kc: those of V(u) and K(u+1), which the X phase
-      // reads itself when kJit.
-      auto step = [&](int u, auto mask_next, auto slot_vn, auto slot_kn, auto slot_vc, auto slot_kc) {
-        fence();
-        s = msplat;
-        if constexpr (G::kJit) {
-          // Fenced groups: one matrix-core instruction and the read of the
-          // fragment four ahead.
-          bf16x8_t gfr[2 * NF];
-#pragma unroll
-          for (int f = 0; f < 4; ++f) gfr[f] = fr[f];
-          for_each_index(std::make_integer_sequence<int, 2 * NF>{}, [&](auto fc) {
-            constexpr int f = decltype(fc)::value;
-            if constexpr (f + 4 < 2 * NF) gfr[f + 4] = xread(f + 4, slot_kc, slot_vc);
-            if constexpr (f & 1)
-              acc[f >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gfr[f], pf[(f >> 1) & 1], acc[f >> 2], 0, 0, 0);
-            else
-              s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gfr[f], qf[f >> 1], s, 0, 0, 0);
-            fence();
-          });
-        } else {
-#pragma unroll
-          for (int kk = 0; kk < NF; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s, 0, 0, 0);
-#pragma unroll
-          for (int i = 0; i < NF; ++i) acc[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf[i & 1], acc[i >> 1], 0, 0, 0);
-        }
-        fence();
-        bar();
-        fence();
-        if constexpr (G::kJit) {
-#pragma unroll
-          for (int f = 0; f < 4; ++f) fr[f] = xread(f, slot_kn, slot_vn);
-        } else {
-          read_k(slot_kn);
-          read_v(slot_vn);
-        }
-        // Refill the slot of u-1, last read for its PV in the X phase before the
-        // previous barrier (or, for the lagging role, before this one). Issued
-        // after this phase's reads: a fragment read behind a pending LDS DMA
-        // would make the compiler wait for every load in flight.
-        issue_loads(u - 1 + kRing);
-        if constexpr (BND) {
-          if constexpr (decltype(mask_next)::value) mask_scores(s, xmap(u + 1));
-        } else {
-          const float mx = rowmax(s, xmap(u + 1), mask_next);
-          maybe_rescale(s, mx, mask_next);
-        }
-        probs(s, pf);
-        fence();
-        // Publish sub-tile u+3 once every wave has passed this point.
-        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((kRing - 4) * LDPS) : "memory");
-        fence();
-      };
-
-      // Steady state in blocks of kRing steps, so that each step's ring slots
-      // (V of u+1 at (u+1-xb) mod 8, K of u+2 at (u+2-xb) mod 8) are constants;
-      // a block runs while all its steps read real sub-tiles and none needs the
-      // mask. The remaining steps address the ring at run time and mask.
-      if constexpr (G::kJit) {
-#pragma unroll
-        for (int f = 0; f < 4; ++f) fr[f] = xread(f, rslot(min(xb + 1, xe - 1)), 0);
-      }
-      if (role) bar();
-      int u = xb;
-      for (; u + kRing <= min(xe - 2, x_mask - 1); u += kRing) {
-        // Steps u + k, k = 0..kRing-1: V of sub-tile u+k+1 in slot (k+1) mod
-        // kRing, K of u+k+2 in slot (k+2) mod kRing (and V of u+k, K of u+k+1).
-        for_each_index(std::make_integer_sequence<int, kRing>{}, [&](auto k) {
-          constexpr int K = decltype(k)::value;
-          step(u + K, NoMask{}, std::integral_constant<int, (K + 1) % kRing>{},
-               std::integral_constant<int, (K + 2) % kRing>{}, std::integral_constant<int, K % kRing>{},
-               std::integral_constant<int, (K + 1) % kRing>{});
-        });
-      }
-      for (; u < xe - 1; ++u) step(u, Mask{}, rslot(u + 1), rslot(min(u + 2, xe - 1)), rslot(u), rslot(u + 1));
-      // Last X phase: PV of the last sub-tile only.
-      if constexpr (G::kJit) {
-        const int vs = rslot(xe - 1);
-#pragma unroll
-        for (int i = 0; i < NF; ++i)
-          acc[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vread(vs, i), pf[i & 1], acc[i >> 1], 0, 0, 0);
-      } else {
-#pragma unroll
-        for (int i = 0; i < NF; ++i) acc[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf[i & 1], acc[i >> 1], 0, 0, 0);
-      }
-    };
-    if (bounded) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) msplat[r] = -m_run;
-      run_tile(std::true_type{});
-    } else {
-      run_tile(std::false_type{});
-    }
-    if (!role) bar();
-    // The ring holds refills that nobody reads; let them retire so no LDS
-    // write is pending when the workgroup ends or the next segment starts.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
   if (rec < 0) {
     // A row that saw no key (frame window only) has l = 0 and is written as 0.
@@ -2048,24 +1757,26 @@ __global__ __launch_bounds__(Geo<D>::NW * 64) void attn_merge_kernel(AttnArgs a)
   };
   const uint16_t* gate_row = a.gate ? a.gate + (int64_t)b * a.Sq * a.H + h : nullptr;
   if constexpr (G::kM16) {
-    // Records in the 16x16 layout: 2 query tiles x D/16 tiles x 4
-    // registers, then the two rows' offsets and the two partial sums.
+    // Records in the 16x16 layout: QT query tiles x D/16 tiles x 4
+    // registers, then the QT rows' offsets and the QT partial sums.
     constexpr int NT16 = D / 16;
-    f32x4_t acc[2][NT16];
-    float M[2], l[2] = {0.f, 0.f};
+    constexpr int QT = G::QT;
+    f32x4_t acc[QT][NT16];
+    float M[QT], l[QT];
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+    for (int qt = 0; qt < QT; ++qt) {
       M[qt] = -INFINITY;
-      for (int j = j0; j <= j1; ++j) M[qt] = fmaxf(M[qt], record(j)[(G::kRecM + qt) * T]);
+      l[qt] = 0.f;
+      for (int j = j0; j <= j1; ++j) M[qt] = fmaxf(M[qt], record(j)[(G::kRecA + qt) * T]);
 #pragma unroll
       for (int ct = 0; ct < NT16; ++ct) acc[qt][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
     for (int j = j0; j <= j1; ++j) {
       const float* pr = record(j);
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        const float w = __builtin_amdgcn_exp2f(pr[(G::kRecM + qt) * T] - M[qt]);
-        l[qt] += w * pr[(G::kRecM + 2 + qt) * T];
+      for (int qt = 0; qt < QT; ++qt) {
+        const float w = __builtin_amdgcn_exp2f(pr[(G::kRecA + qt) * T] - M[qt]);
+        l[qt] += w * pr[(G::kRecA + QT + qt) * T];
 #pragma unroll
         for (int ct = 0; ct < NT16; ++ct)
 #pragma unroll
@@ -2074,11 +1785,11 @@ __global__ __launch_bounds__(Geo<D>::NW * 64) void attn_merge_kernel(AttnArgs a)
     }
     const int l16 = lane & 15, g4 = lane >> 4;
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+    for (int qt = 0; qt < QT; ++qt) {
       const uint32_t u = __builtin_bit_cast(uint32_t, l[qt]);
       const auto sw = __builtin_amdgcn_permlane16_swap(u, u, false, false);
       const float lr = sum_lane_pair(__builtin_bit_cast(float, (uint32_t)sw[0]) + __builtin_bit_cast(float, (uint32_t)sw[1]));
-      store_row16<D>(a, obase, q0 + wave * 32 + qt * 16 + l16, g4, acc[qt], 1.0f / lr, a.q_valid, gate_row);
+      store_row16<D>(a, obase, q0 + wave * G::WROWS + qt * 16 + l16, g4, acc[qt], 1.0f / lr, a.q_valid, gate_row);
     }
   } else {
   float M = -INFINITY;

@@ -10,11 +10,14 @@
 namespace h3 {
 
 // Attention tiling by head dim D (64, 128 or 256): a workgroup of
-// attn_threads(D) / 64 waves (32 query rows each) owns attn_rows(D) query
-// rows of one (b, h) and walks the keys in kAttnSub-key sub-tiles.
+// attn_threads(D) / 64 waves owns attn_rows(D) query rows of one (b, h) and
+// walks the keys in kAttnSub-key sub-tiles. At head dims 64 and 128 each
+// wave holds attn_query_tiles(D) 16-row query tiles (64 and 32 rows); at 256
+// each of four waves holds one 32-row tile.
 constexpr int kAttnSub = 32;
 constexpr int attn_threads(int D) { return D <= 128 ? 512 : 256; }
-constexpr int attn_rows(int D) { return attn_threads(D) / 2; }
+constexpr int attn_query_tiles(int D) { return D == 64 ? 4 : 2; }
+constexpr int attn_rows(int D) { return D <= 128 ? attn_threads(D) / 64 * 16 * attn_query_tiles(D) : attn_threads(D) / 2; }
 
 // Load balancing of the last, partial round of query tiles (stream-K): those
 // tiles' sub-tile steps are split evenly over up to kSplitMaxBlocks
@@ -24,10 +27,13 @@ constexpr int attn_rows(int D) { return attn_threads(D) / 2; }
 // values per lane) plus the lane's running max and partial row sum.
 constexpr int kSplitMaxBlocks = 256;
 constexpr int kSplitMinSteps = 16;
-// Floats per partial record: the accumulator registers of every thread, then
-// each thread's row offsets and partial sums (two of each at head dim 128,
-// whose waves hold their rows as two 16-row tiles).
-constexpr int attn_part_floats(int D) { return (D / 2 + (D == 128 ? 4 : 2)) * attn_threads(D); }
+// Floats per partial record: the accumulator registers of every thread (its
+// share of rows x D), then each thread's row offsets and partial sums, one
+// of each per query tile.
+constexpr int attn_part_floats(int D) {
+  return D <= 128 ? (attn_rows(D) * D / attn_threads(D) + 2 * attn_query_tiles(D)) * attn_threads(D)
+                  : (D / 2 + 2) * attn_threads(D);
+}
 
 // Partial records the forward workspace reserves for these sizes: two per
 // split workgroup, for the largest split the launcher can choose.

@@ -90,7 +90,8 @@ bool workspace_layout(int32_t B, int32_t Sq, int32_t Sk, int32_t Hq, int32_t Hkv
                       WorkspaceLayout* w) {
   if (B < 1 || Sq < 1 || Sk < 1 || Hq < 1 || Hkv < 1) return false;
   if (D != 64 && D != 128 && D != 256) return false;
-  w->Sq_pad = round_up(Sq, h3::kRowPad);
+  // Query rows pad to whole query blocks (512 rows at head dim 64).
+  w->Sq_pad = round_up(Sq, h3::attn_rows(D) > h3::kRowPad ? h3::attn_rows(D) : h3::kRowPad);
   w->Sk_pad = round_up(Sk, h3::kRowPad);
   const unsigned row = 2u * (unsigned)D;
   const unsigned __int128 qb = (unsigned __int128)B * (unsigned __int128)Hq * (unsigned __int128)w->Sq_pad * row;

@@ -206,15 +206,16 @@ def test_forward_ex_workspace_bytes(lib):
         2 * (4 * 1024 + 2 * 1 * 512) * 256 + kn(2)
     assert h3attn.forward_ex_workspace_bytes(1, 104448, 104448, 6, 6, window=True) == \
         3 * 6 * 104448 * 256 + kn(6 * 26)
-    # rows of 2 * head_dim bytes; split records per lane of 512: at head dim 64, 64 accumulators (64
-    # query rows x 64 channels over 64 lanes) and four row offsets and sums; at 256 (one lane of 256 per
-    # row pair), 128 accumulators and one of each. Query rows pad to 512 at head dim 64.
+    # rows of 2 * head_dim bytes; split records per lane of 512: 64 accumulators (at head dim 64, 64
+    # query rows x 64 channels over 64 lanes; at 256, 32 rows x 128 channels, each wave of a pair
+    # holding half of the channels) and one row offset and one sum per 16-row query tile (four at 64,
+    # two at 256). Query rows pad to 512 at head dim 64.
     assert h3attn.forward_ex_workspace_bytes(1, 4096, 4096, 8, 8, head_dim=64) == \
         3 * 8 * 4096 * 128 + 2 * 256 * (64 + 8) * 512 * 4 + kn(8)
     assert h3attn.forward_ex_workspace_bytes(1, 4100, 4100, 8, 8, head_dim=64) == \
         (8 * 4608 + 2 * 8 * 4352) * 128 + 2 * 256 * (64 + 8) * 512 * 4 + kn(8 * 2)
     assert h3attn.forward_ex_workspace_bytes(1, 4096, 4096, 8, 8, head_dim=256) == \
-        3 * 8 * 4096 * 512 + 2 * 256 * (128 + 2) * 256 * 4 + kn(8)
+        3 * 8 * 4096 * 512 + 2 * 256 * (64 + 4) * 512 * 4 + kn(8)
     assert h3attn.forward_ex_workspace_bytes(1, 8, 8, 4, 4, head_dim=96) == 0
     assert h3attn.forward_ex_workspace_bytes(1, 8, 8, 6, 4) == 0      # 6 heads do not group into 4
     assert h3attn.forward_ex_workspace_bytes(1, 8, 8, 4, 0) == 0

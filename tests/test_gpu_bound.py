@@ -142,14 +142,16 @@ def test_weights_either_side_of_the_limit(h3, w):
     check_metrics(oracle.compare(got, ref), f"weights {w}")
 
 
-@pytest.mark.parametrize("D,Sk", [(64, 2048), (128, 2048), (128, 300)])
+@pytest.mark.parametrize("D,Sk", [(64, 2048), (128, 2048), (128, 300), (256, 2048)])
 def test_data_bound_mixes_paths_within_a_workgroup(h3, D, Sk):
     """Without the norm the bound is |q_i| max_j |k_j| per row, decided per
     wave. Key 7 gets a norm above 100 on channel 5, which every query has at
     zero (its scores stay those of a plain key), so max_j |k_j| > 100; the
-    query rows of every other 32-row wave are scaled by 1/16 (exactly), so
+    query rows of every other 32-row block are scaled by 1/16 (exactly), so
     those waves have m_i below the limit and run the bounded path while
-    their neighbours in the same workgroup run the online maximum."""
+    their neighbours in the same workgroup run the online maximum. At head
+    dim 256 the workgroup takes one decision (a max pass, then exact row
+    maxima as offsets) as soon as one of its waves is over the limit."""
     B, S, H = 1, 2048, 2
     base = workloads.make_inputs(B, S, Sk, H, seed=930 + D, D=D)
     q = base.q.copy()

@@ -18,17 +18,14 @@ SRC = os.path.join(ROOT, "tests", "sched_check.cpp")
 
 
 def record_floats(D):
-    """Floats per partial record, per thread: the accumulators of its share
-    of the workgroup's query rows x D channels, then one row offset and one
-    partial sum per 16-row query tile it holds (four at head dim 64, whose
-    waves hold 64 rows; two at 128, 32 rows), over the 512 threads of a
-    head-dim-64/128 workgroup; at 256, D/2 accumulators and one of each over
-    256 threads (32 rows per wave of 64 lanes)."""
-    if D <= 128:
-        tiles = 4 if D == 64 else 2
-        rows = 8 * 16 * tiles
-        return (rows * D // 512 + 2 * tiles) * 512
-    return (D // 2 + 2) * 256
+    """Floats per partial record, over the 512 threads of a workgroup: per
+    thread the accumulators of its share of the workgroup's query rows x D
+    channels, then one row offset and one partial sum per 16-row query tile
+    it holds (four at head dim 64, whose waves hold 64 rows; two at 128 and
+    256, 32 rows; at 256 the two waves of a pair share their rows and split
+    the channels)."""
+    tiles = 4 if D == 64 else 2
+    return (query_rows(D) * D // 512 + 2 * tiles) * 512
 
 
 def query_rows(D):

@@ -173,49 +173,49 @@ constexpr float kBoundMax = 60.0f;
 constexpr float kBoundSlack = 1.0f + 1.0f / 1024.0f;
 constexpr int kSub = 32;                       // keys per sub-tile
 
-// Tiling by head dim D (64, 128 or 256). D <= 128: eight waves per
-// workgroup, two per SIMD, an eight-slot ring, and 16x16x32 matrix-core
-// instructions on QT 16-row query tiles per wave (four at 64, so 512 rows per
-// workgroup; two at 128, 256 rows). D = 256 holds twice the accumulators and
-// fragments of a 32-row tile, so one wave per SIMD (four waves, 128 rows)
-// with the whole register file, 32x32x16 instructions, and a K ring and a
-// V^T ring of four 16 KB slots each.
+// Tiling by head dim D (64, 128 or 256): eight waves per workgroup, two per
+// SIMD, 16x16x32 matrix-core instructions on QT 16-row query tiles per wave
+// (four at 64, so 512 rows per workgroup; two at 128, 256 rows). At 256 the
+// waves work in pairs (kCS): both waves of a pair hold the same 32 query
+// rows; each computes the scores of half of every sub-tile's keys and the
+// output of half of the channels, so that its accumulators and fragment
+// reads are those of head dim 128, and the pair exchanges probabilities
+// through LDS (128 rows per workgroup).
 template <int D>
 struct Geo {
   static_assert(D == 64 || D == 128 || D == 256, "head dim");
-  static constexpr int NW = D <= 128 ? 8 : 4;           // waves per workgroup
-  static constexpr int WPE = D <= 128 ? 2 : 1;          // waves per SIMD
-  // kM16: the two-wave ping-pong on 16x16x32 matrix-core instructions with
-  // QT 16-row query tiles per wave; otherwise (D = 256) the
-  // software-pipelined step (kPipe) on 32x32x16, one wave per SIMD.
-  static constexpr bool kM16 = D <= 128;
-  static constexpr bool kPipe = D == 256;
-  static constexpr int QT = attn_query_tiles(D);        // 16-row query tiles per wave (kM16)
-  static constexpr int WROWS = kM16 ? 16 * QT : 32;     // query rows per wave
-  static constexpr int BM = NW * WROWS;                 // query rows per workgroup
-  static constexpr int kRing = D <= 128 ? 8 : 4;        // ring depth (sub-tiles; per operand when kPipe)
+  static constexpr int NW = 8;                          // waves per workgroup
+  static constexpr int WPE = 2;                         // waves per SIMD
+  static constexpr bool kCS = D == 256;                 // channel-split wave pairs
+  static constexpr int DW = kCS ? D / 2 : D;            // channels per wave
+  static constexpr int QT = attn_query_tiles(D);        // 16-row query tiles per wave
+  static constexpr int WROWS = 16 * QT;                 // query rows per wave (per pair when kCS)
+  static constexpr int BM = (kCS ? NW / 2 : NW) * WROWS;   // query rows per workgroup
+  static constexpr int kRing = D <= 128 ? 8 : 4;        // ring depth (sub-tiles)
   static constexpr int kKBytes = kSub * D * 2;          // K sub-tile: 32 rows x 2D bytes
   static constexpr int kVBytes = D * kSub * 2;          // V^T sub-tile: D rows x 64 B
   static constexpr int kBufBytes = kKBytes + kVBytes;   // one ring slot
-  static constexpr int NF = D / 16;                     // 16-channel (QK) / 16-key (PV) fragments
-  static constexpr int NT = D / 32;                     // 32-channel output tiles
   static constexpr int kSwz = (D / 8 < 16 ? D / 8 : 16) - 1;   // K chunk swizzle mask
   static constexpr int nK = kKBytes / 1024;             // 1 KB direct loads per sub-tile (K)
   static constexpr int LDPS = (kKBytes + kVBytes) / 1024 / NW;   // per wave per sub-tile
-  // Partial record layout per thread: kRecA accumulator floats, then the row
-  // offsets and partial sums (QT of each for kM16; one each at 256, at
-  // kRecM and kRecL).
-  static constexpr int kRecA = kM16 ? WROWS * D / 64 : NT * 16;
-  static constexpr int kRecM = kRecA, kRecL = kRecA + 1;
-  // LDS: the ring and one int per wave (its SIMD) for D <= 128; at 256 the
-  // two operand rings fill 128 KB.
-  static constexpr int kLdsBytes = kPipe ? 2 * kRing * kKBytes : kRing * kBufBytes + NW * 4;
+  // LDS: the ring (K sub-tiles, then V^T sub-tiles), for kCS the pairs'
+  // exchange areas (row maxima and sums: 512 B per wave; probabilities: 1 KB
+  // per wave), then one int per wave (its SIMD).
+  static constexpr int kXOff = kRing * kBufBytes;
+  static constexpr int kXScores = kCS ? NW * 512 : 0;
+  static constexpr int kXProbs = kCS ? NW * 1024 : 0;
+  static constexpr int kSimdOff = kXOff + kXScores + kXProbs;
+  static constexpr int kLdsBytes = kSimdOff + NW * 4;
+  // Partial record layout per thread: kRecA accumulator floats, then QT row
+  // offsets and QT partial sums.
+  static constexpr int kRecA = WROWS * DW / 64;
   static_assert(LDPS * NW * 1024 == kKBytes + kVBytes, "tile split");
   static_assert(kLdsBytes <= 160 * 1024, "LDS");
   static_assert(BM == attn_rows(D) && NW * 64 == attn_threads(D), "tiling constants");
+  static_assert(kRing * kKBytes <= 65536, "K sub-tiles within the first 64 KB");
   // Floats each thread writes to a partial record fill exactly the record
   // size the host reserves per record.
-  static_assert((kM16 ? kRecA + 2 * QT : kRecL + 1) * NW * 64 == attn_part_floats(D), "partial record size");
+  static_assert((kRecA + 2 * QT) * NW * 64 == attn_part_floats(D), "partial record size");
 };
 
 // LDS layouts (no padding; XOR swizzles keep every 8-lane group of a
@@ -223,38 +223,13 @@ struct Geo {
 //   K:   row r (key), 16-byte chunk c (channels 8c..8c+7) at r*2D + (c ^ (r & kSwz))*16
 //   V^T: row d (channel), chunk c (positions 8c..8c+7) at d*64 + (c ^ ((d >> 2) & 3))*16
 
-// Writes one query row of a finished tile: o = acc * inv rounded to bf16, or
-// +0.0 for rows at or past q_valid. With a gate (gate_row: the head's gate
-// column of the batch item, stride H) the row is also multiplied by
-// sigmoid(gate), the softmax gate epilogue. Lane (l, register r of acc[dt])
-// holds channel dt*32 + 8*(r/4) + 4*(l/32) + r%4 of its row.
-template <int D>
-__device__ inline void store_row(const AttnArgs& a, uint16_t* obase, int q, int g, const f32x16_t* acc,
-                                 float inv, int q_valid, const uint16_t* gate_row) {
-  if (q >= a.Sq) return;
-  uint16_t* op = obase + q * ((int64_t)a.H * D);
-  const bool live = q < q_valid;
-  if (gate_row && live) {
-    const float gv = __uint_as_float((uint32_t)gate_row[(int64_t)q * a.H] << 16);
-    inv *= 1.0f / (1.0f + __expf(-gv));
-  }
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      const int d0 = dt * 32 + rq * 8 + g * 4;
-      uint2 val = make_uint2(0u, 0u);
-      if (live) {
-        val.x = pack_bf16x2(acc[dt][rq * 4 + 0] * inv, acc[dt][rq * 4 + 1] * inv);
-        val.y = pack_bf16x2(acc[dt][rq * 4 + 2] * inv, acc[dt][rq * 4 + 3] * inv);
-      }
-      *reinterpret_cast<uint2*>(op + d0) = val;
-    }
-}
-
-// store_row for the 16x16 output layout: lane (l, register r of acc[ct])
-// holds channel 16 ct + 4 (l/16) + r of its row (g4 = l/16).
-template <int D>
+// Writes NT16 x 16 channels of one query row of a finished tile (obase
+// points at the first of them): o = acc * inv rounded to bf16, or +0.0 for
+// rows at or past q_valid. With a gate (gate_row: the head's gate column of
+// the batch item, stride H) the row is also multiplied by sigmoid(gate), the
+// softmax gate epilogue. In the 16x16 output layout lane (l, register r of
+// acc[ct]) holds channel 16 ct + 4 (l/16) + r (g4 = l/16).
+template <int D, int NT16>
 __device__ inline void store_row16(const AttnArgs& a, uint16_t* obase, int q, int g4, const f32x4_t* acc,
                                    float inv, int q_valid, const uint16_t* gate_row) {
   if (q >= a.Sq) return;
@@ -265,7 +240,7 @@ __device__ inline void store_row16(const AttnArgs& a, uint16_t* obase, int q, in
     inv *= 1.0f / (1.0f + __expf(-gv));
   }
 #pragma unroll
-  for (int ct = 0; ct < D / 16; ++ct) {
+  for (int ct = 0; ct < NT16; ++ct) {
     uint2 val = make_uint2(0u, 0u);
     if (live) {
       val.x = pack_bf16x2(acc[ct][0] * inv, acc[ct][1] * inv);
@@ -275,10 +250,10 @@ __device__ inline void store_row16(const AttnArgs& a, uint16_t* obase, int q, in
   }
 }
 
-// Partial record of a split tile, per thread t of the T-thread workgroup
-// (fp32, thread-contiguous so every access is coalesced): accumulator
-// register r at [r * T + t] (D/2 of them), then the row offset m at
-// [kRecM * T + t] and this lane's row-sum share at [kRecL * T + t].
+// Partial record of a split tile, per logical thread t (64 lwave + lane) of
+// the workgroup (fp32, thread-contiguous so every access is coalesced):
+// accumulator register r at [r * 512 + t] (kRecA of them), then the QT row
+// offsets and the QT partial row sums.
 
 // f(integral_constant<int, K>) for each K of the sequence, in order.
 template <int... K, typename F>
@@ -306,8 +281,6 @@ void attn_fwd_kernel(AttnArgs a) {
   constexpr int kRing = G::kRing;
   constexpr int kKBytes = G::kKBytes;
   constexpr int kBufBytes = G::kBufBytes;
-  constexpr int NF = G::NF;
-  constexpr int NT = G::NT;
   // One LDS object only: the ring, then the per-wave SIMD ids. (With a
   // second LDS variable the compiler can no longer tell fragment reads from
   // the ring's DMA writes and waits for every load in flight before each.)
@@ -316,22 +289,45 @@ void attn_fwd_kernel(AttnArgs a) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int lq = lane & 31;
-  const int g = lane >> 5;
 
   // Role of this wave among the waves that share its SIMD (HW_ID bits 5:4
-  // name the SIMD): the second one of each SIMD runs one phase behind. (At
-  // head dim 256 every wave has its SIMD to itself.)
-  int role = 0;
-  if constexpr (!G::kPipe) {
-    int* simd_of = reinterpret_cast<int*>(lds + kRing * kBufBytes);
+  // name the SIMD): the second one of each SIMD runs one phase behind.
+  // Channel-split pairs (head dim 256) must run in the same phase: when every
+  // SIMD holds two waves, the waves of one role (one per SIMD) pair up by
+  // SIMD (0 with 1, 2 with 3); otherwise every wave takes role 0 (no phase
+  // offset) and waves 2p and 2p + 1 pair up. pair: the wave's (or pair's)
+  // query rows; half: its channel half.
+  int role = 0, pair = wave, half = 0;
+  {
+    int* simd_of = reinterpret_cast<int*>(lds + G::kSimdOff);
     if (lane == 0) simd_of[wave] = (int)(__builtin_amdgcn_s_getreg((1 << 11) | (4 << 6) | 4) & 3);
     __syncthreads();
     const int mine = simd_of[wave];
+    int on_simd[4] = {0, 0, 0, 0};
 #pragma unroll
-    for (int w = 0; w < NW; ++w) role += (w < wave && simd_of[w] == mine) ? 1 : 0;
+    for (int w = 0; w < NW; ++w) {
+      role += (w < wave && simd_of[w] == mine) ? 1 : 0;
+      on_simd[simd_of[w] & 3] += 1;
+    }
     role = __builtin_amdgcn_readfirstlane(role & 1);
+    if constexpr (G::kCS) {
+      const bool regular = on_simd[0] == 2 && on_simd[1] == 2 && on_simd[2] == 2 && on_simd[3] == 2;
+      if (regular) {
+        pair = 2 * role + (mine >> 1);
+        half = mine & 1;
+      } else {
+        role = 0;
+        pair = wave >> 1;
+        half = wave & 1;
+      }
+      pair = __builtin_amdgcn_readfirstlane(pair);
+      half = __builtin_amdgcn_readfirstlane(half);
+      role = __builtin_amdgcn_readfirstlane(role);
+    }
   }
+  // Logical wave: the position of this wave's rows and channels in the
+  // workgroup's tile, which indexes its share of a partial record.
+  const int lwave = G::kCS ? 2 * pair + half : wave;
 
   const int n_qblocks = (a.Sq + BM - 1) / BM;
   const int bid = blockIdx.x;
@@ -489,15 +485,6 @@ void attn_fwd_kernel(AttnArgs a) {
     q01 = (g1 - bh1 * a.nqv) * BM;
   }
 
-  // Per-lane LDS byte addresses of the matrix-core operand reads. K fragment
-  // kk of a sub-tile is at kbase ^ (32 kk): its chunk is 2kk + g, stored at
-  // (2kk + g) ^ (lq & kSwz) = 2kk ^ (g ^ (lq & kSwz)), and 32 kk stays below
-  // the row size, so one register serves every fragment of the row.
-  const uint32_t kbase = lq * (2 * D) + ((g ^ (lq & G::kSwz)) * 16);
-  uint32_t vaddr[2];
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) vaddr[ks] = kKBytes + lq * 64 + ((((2 * ks) | g) ^ ((lq >> 2) & 3)) * 16);
-
 #pragma nounroll
   for (int si = 0; si < nseg; ++si) {
   const int bh = si ? bh1 : bh0;
@@ -511,21 +498,32 @@ void attn_fwd_kernel(AttnArgs a) {
   const int bh_kv = b * a.Hkv + h / (a.H / a.Hkv);
   uint16_t* obase = a.o + ((int64_t)b * a.Sq * a.H + h) * D;
   const uint16_t* gate_row = a.gate ? a.gate + (int64_t)b * a.Sq * a.H + h : nullptr;
-  if constexpr (G::kM16) {
-  // Head dims 64 and 128 on v_mfma_f32_16x16x32_bf16 (A 16 x 32: lane l
-  // supplies row l%16, k = 8(l/16) .. +7; B 32 x 16: column l%16, the same k;
-  // D 16 x 16: lane l register r holds row 4(l/16) + r, column l%16). The
-  // smaller shape sustains more flops at the chip's power limit. Each wave
-  // keeps its 16 QT query rows as QT 16-row tiles qt: QK^T is 2 key tiles x
-  // QT query tiles x D/32 channel chunks (each K fragment serves every query
-  // tile), so lane l holds, for query row 16 qt + l%16, the 8 keys 16 kt + 4
-  // g4 + r (g4 = l/16, r < 4); a row's 32 keys are spread over the four lanes
-  // l%16 + 16 j. PV takes those 8 keys as positions 8 g4 .. 8 g4 + 7 of the
-  // sub-tile, with V^T's keys permuted to match (position 8g + j holds key 16
-  // (j/4) + 4g + j%4), and is D/16 channel tiles x QT query tiles (each V^T
-  // fragment serves every query tile). Head dim 64 holds four query tiles
-  // (64 rows) per wave, so that each fragment read and each step's softmax
-  // feed as many matrix-core cycles as at 128.
+  // All head dims on v_mfma_f32_16x16x32_bf16 (A 16 x 32: lane l supplies
+  // row l%16, k = 8(l/16) .. +7; B 32 x 16: column l%16, the same k; D 16 x
+  // 16: lane l register r holds row 4(l/16) + r, column l%16). The smaller
+  // shape sustains more flops at the chip's power limit. Each wave keeps its
+  // 16 QT query rows as QT 16-row tiles qt and works on DW channels: QK^T is 2
+  // key tiles x QT query tiles x DW/32 channel chunks (each K fragment serves
+  // every query tile), so lane l holds, for query row 16 qt + l%16, the 8
+  // keys 16 kt + 4 g4 + r (g4 = l/16, r < 4); a row's 32 keys are spread over
+  // the four lanes l%16 + 16 j. PV takes those 8 keys as positions 8 g4 .. 8
+  // g4 + 7 of the sub-tile, with V^T's keys permuted to match (position 8g + j
+  // holds key 16 (j/4) + 4g + j%4), and is DW/16 channel tiles x QT query
+  // tiles (each V^T fragment serves every query tile). Head dim 64 holds four
+  // query tiles (64 rows) per wave, so that each fragment read and each
+  // step's softmax feed as many matrix-core cycles as at 128.
+  //
+  // Head dim 256 (CS): the two waves of a pair hold the same 32 rows. Wave
+  // `half` computes the full scores (all 256 channels) of key tile kt = half
+  // of each sub-tile and their probabilities, and the output of its channel
+  // half (DW = 128) from all 32 keys: it writes its 16 keys' probabilities to
+  // LDS and reads the partner's 16 before its PV. So each wave holds the Q
+  // of every channel but only half of the accumulators, issues as many
+  // matrix-core instructions and fragment reads per step as at head dim 128,
+  // and computes half of the exponentials. The pair runs in one phase of the
+  // ping-pong, so the barriers that separate the phases also order the
+  // exchange: probabilities are written in Y and read at the start of the
+  // next X.
   //
   // Schedule (ping-pong): the two waves of a SIMD alternate an X phase
   // (matrix-core work only: QK^T of sub-tile u+1 and PV of sub-tile u, the
@@ -533,14 +531,18 @@ void attn_fwd_kernel(AttnArgs a) {
   // phase (softmax of u+1, the first fragment reads of the next X, one ring
   // refill), separated by workgroup barriers, so one wave feeds the matrix
   // core while the other computes the softmax.
-  constexpr int NC = D / 32;       // 32-channel chunks
-  constexpr int NT16 = D / 16;     // 16-channel output tiles
+  constexpr bool CS = G::kCS;
+  constexpr int DW = G::DW;          // channels of this wave
+  constexpr int NC = DW / 32;        // 32-channel chunks of this wave's output channels
+  constexpr int NCQ = CS ? D / 32 : NC;   // 32-channel chunks of its QK^T
+  constexpr int NKF = CS ? NCQ : 2 * NC;  // K fragments per sub-tile (CS: one key tile)
+  constexpr int NT16 = DW / 16;      // 16-channel output tiles
   const int l16 = lane & 15, g4 = lane >> 4;
-  constexpr int QT = G::QT;        // 16-row query tiles per wave
+  constexpr int QT = G::QT;          // 16-row query tiles per wave
   int rowq[QT], limq[QT];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    rowq[qt] = q0 + wave * G::WROWS + qt * 16 + l16;
+    rowq[qt] = q0 + pair * G::WROWS + qt * 16 + l16;
     limq[qt] = a.causal ? min(rowq[qt], kvv_t - 1) : kvv_t - 1;
   }
   auto xmap = [&](int v) __attribute__((always_inline)) {
@@ -562,20 +564,22 @@ void attn_fwd_kernel(AttnArgs a) {
 
   // Q fragments (B operand of S^T = K Q^T): query row 16 qt + l%16 of the
   // wave, channels 32 cc + 8 g4 .. +7. Loaded before the ring fill.
-  bf16x8_t qf[QT][NC];
+  bf16x8_t qf[QT][NCQ];
   {
-    const uint16_t* qp = a.qw + ((int64_t)bh * a.Sq_pad + q0 + wave * G::WROWS + l16) * D + g4 * 8;
+    const uint16_t* qp = a.qw + ((int64_t)bh * a.Sq_pad + q0 + pair * G::WROWS + l16) * D + g4 * 8;
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
-      for (int cc = 0; cc < NC; ++cc) qf[qt][cc] = *reinterpret_cast<const bf16x8_t*>(qp + qt * 16 * D + cc * 32);
+      for (int cc = 0; cc < NCQ; ++cc) qf[qt][cc] = *reinterpret_cast<const bf16x8_t*>(qp + qt * 16 * D + cc * 32);
   }
 
-  // Direct loads: the same sub-tile layouts as the 32x32 path, but the ring
-  // keeps all K sub-tiles in its first 64 KB and all V^T sub-tiles in the
-  // second (slot s: K at s * kKBytes, V^T at kRing * kKBytes + s * kKBytes),
-  // so every fragment offset fits the instruction's 16-bit field from one
-  // base register per operand.
+  // Direct loads: the ring keeps all K sub-tiles in its first kRing kKBytes
+  // and all V^T sub-tiles after them (slot s: K at s * kKBytes, V^T at kRing
+  // * kKBytes + s * kKBytes), so every fragment offset fits the instruction's
+  // 16-bit field from one base register per operand. Load i of this wave
+  // fills LDS bytes [1024 j, 1024 j + 1024) of the slot's K (j < nK) or V^T
+  // (j - nK), j = wave + NW i; the lane that fills LDS chunk Q fetches the
+  // logical chunk the swizzle puts there.
   const uint16_t* kw = a.kw + (int64_t)bh_kv * a.Sk_pad * D;
   const uint16_t* vt = a.vt + (int64_t)bh_kv * a.Sk_pad * D;
   int loff[LDPS];
@@ -592,21 +596,53 @@ void attn_fwd_kernel(AttnArgs a) {
       loff[i] = (d * kSub + ((p ^ ((d >> 2) & 3)) * 8)) * 2;
     }
   }
-  auto issue_loads = [&](int x) __attribute__((always_inline)) {
+  // Loads of sub-tile x into its slot: i in [i0, i1) of this wave's LDPS
+  // loads (the first LDPS / 2 fill K, the others V^T, as j = wave + NW i).
+  auto issue_part = [&](int x, int i0, int i1) __attribute__((always_inline)) {
     const int sl = (x - xb) & (kRing - 1);
     const bool live = x < xe;
     const int xs = live ? xmap(x) : 0;
     const uint16_t* kx = kw + (int64_t)xs * (kSub * D);
     const uint16_t* vx = vt + (int64_t)xs * (kSub * D);
 #pragma unroll
-    for (int i = 0; i < LDPS; ++i) {
+    for (int i = i0; i < i1; ++i) {
       const int j = wave + NW * i;
       uint8_t* dst = j < G::nK ? lds + sl * kKBytes + j * 1024 : lds + (kRing + sl) * kKBytes + (j - G::nK) * 1024;
       load_lds16(j < G::nK ? kx : vx, live ? kKBytes : 0, loff[i], dst);
     }
   };
+  static_assert(G::nK == NW * LDPS / 2, "half of each wave's loads fill K");
+  auto issue_loads = [&](int x) __attribute__((always_inline)) { issue_part(x, 0, LDPS); };
+  auto issue_k = [&](int x) __attribute__((always_inline)) { issue_part(x, 0, LDPS / 2); };
+  auto issue_v = [&](int x) __attribute__((always_inline)) { issue_part(x, LDPS / 2, LDPS); };
+  // Ring refills. Sub-tile x is first read in the Y phase of step x - 2 (K)
+  // and x - 1 (V^T); its slot's K part is free once every wave has done
+  // step x - kRing - 1's X phase, its V^T part one step later.
+  // Head dims 64 and 128 (eight slots): step u refills the slot of u - 1
+  // with u - 1 + kRing and each Y phase ends waiting for the loads of u + 3.
+  // Head dim 256 (four slots) refills K a step ahead of V^T: in step u the
+  // waves of role 0 load K(u + 4) and V^T(u + 3) and, at the end of each X
+  // phase, wait for the loads of two steps before; the waves of role 1, which
+  // run a phase later, load K(u + 5) and V^T(u + 4) and wait at the end of
+  // each Y phase for the loads of two steps before. Either way every wave's
+  // share of a sub-tile has landed at the barrier before its first read, and
+  // each load has two to three phases to land.
+  const bool early = CS && role;
+  auto fill_ring = [&]() __attribute__((always_inline)) {
+    if constexpr (CS) {
+      // Role 0: K and V^T of xb .. xb + 2, K of xb + 3; role 1: K and V^T of
+      // xb .. xb + 3 (its K of xb + 4 follows once the prologue has read K of
+      // xb).
 #pragma unroll
-  for (int i = 0; i < kRing - 1; ++i) issue_loads(xb + i);
+      for (int i = 0; i < kRing - 1; ++i) issue_loads(xb + i);
+      if (early) issue_loads(xb + kRing - 1);
+      else issue_k(xb + kRing - 1);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kRing - 1; ++i) issue_loads(xb + i);
+    }
+  };
+  fill_ring();
 
   // Accumulator tiles (qt, ct) live as 4-register slices of 16-register
   // tuples (tile i = qt NT16 + ct in tuple i/4, slice i%4): with the tiles as
@@ -639,13 +675,25 @@ void attn_fwd_kernel(AttnArgs a) {
   for (int qt = 0; qt < QT; ++qt) {
     m_run[qt] = l_run[qt] = 0.f;
     seen[qt] = true;
+    msplat[qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
   auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
 
-  // Sets this lane's scores of query tile qt in sub-tile x that its row does
-  // not see to -inf.
-  auto mask16 = [&](f32x4_t* sq, int x, int qt) __attribute__((always_inline)) {
+  // Pair exchange areas (CS): row values (maxima, sums) that wave (pair, h)
+  // reads at xs(pair, h) (its partner writes them there), probabilities that
+  // wave (pair, h) writes at xp(pair, h); per lane QT floats and 8 bf16.
+  uint8_t* const xs_out = lds + G::kXOff + (pair * 2 + (1 - half)) * 512 + lane * 8;
+  const uint8_t* const xs_in = lds + G::kXOff + (pair * 2 + half) * 512 + lane * 8;
+  uint8_t* const xp_out = lds + G::kXOff + G::kXScores + (pair * 2 + half) * 1024 + lane * 16;
+  const uint8_t* const xp_in = lds + G::kXOff + G::kXScores + (pair * 2 + (1 - half)) * 1024 + lane * 16;
+  // Barrier with this wave's LDS writes complete (the pair's exchanges at
+  // points where every wave of the workgroup is in step).
+  auto pair_sync = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+
+  // Sets this lane's scores of key tile kt of query tile qt in sub-tile x
+  // that its row does not see to -inf.
+  auto mask_kt = [&](f32x4_t& sk, int x, int qt, int kt) __attribute__((always_inline)) {
     int a_end = 0x7fffffff, w_lo = 0, w_hi = 0;
     if constexpr (WIN) {
       if (c_row[qt] >= 0) {
@@ -655,17 +703,21 @@ void attn_fwd_kernel(AttnArgs a) {
       }
     }
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = x * kSub + kt * 16 + g4 * 4 + r;
-        if constexpr (WIN) {
-          const bool hidden = (key > limq[qt]) | ((key >= a_end) & ((key < w_lo) | (key >= w_hi)));
-          sq[kt][r] = hidden ? -INFINITY : sq[kt][r];
-        } else {
-          if (key > limq[qt]) sq[kt][r] = -INFINITY;
-        }
+    for (int r = 0; r < 4; ++r) {
+      const int key = x * kSub + kt * 16 + g4 * 4 + r;
+      if constexpr (WIN) {
+        // Bitwise, not short-circuit, so it compiles to compares and one
+        // select instead of branches.
+        const bool hidden = (key > limq[qt]) | ((key >= a_end) & ((key < w_lo) | (key >= w_hi)));
+        sk[r] = hidden ? -INFINITY : sk[r];
+      } else {
+        if (key > limq[qt]) sk[r] = -INFINITY;
       }
+    }
+  };
+  auto mask16 = [&](f32x4_t* sq, int x, int qt) __attribute__((always_inline)) {
+    mask_kt(sq[0], x, qt, 0);
+    mask_kt(sq[1], x, qt, 1);
   };
   // This lane's maximum of the 8 scores of query tile qt in sub-tile x; with
   // MASK, keys its row does not see are set to -inf first.
@@ -700,7 +752,9 @@ void attn_fwd_kernel(AttnArgs a) {
   // Without the norm, the bound comes from the data: row i's scores lie in
   // [-m_i, m_i] with m_i = |q_i| max_j |k_j| (Cauchy-Schwarz on the bf16
   // rows the matrix core reads; q carries c already), each row taking its own
-  // m_i as its offset when every row of the wave has m_i <= kBoundMax.
+  // m_i as its offset when every row of the wave has m_i <= kBoundMax (at
+  // head dim 256 both waves of a pair hold every channel of their rows, so
+  // they take the same offsets).
   bool bounded = false;
   if (a.wq != nullptr) {
     auto wmax = [&](const float* w) __attribute__((always_inline)) {
@@ -718,18 +772,34 @@ void attn_fwd_kernel(AttnArgs a) {
     }
   } else if (a.knorm != nullptr) {
     const float kmax = key_norm_max(a, bh_kv);
-    float m[QT];
+    float ss[QT], m[QT];
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
-      float ss = 0.f;
+      ss[qt] = 0.f;
 #pragma unroll
-      for (int cc = 0; cc < NC; ++cc) ss = sum_sq(qf[qt][cc], ss);
-      m[qt] = sqrtf(sum_row16(ss)) * kmax * kBoundSlack;
+      for (int cc = 0; cc < NCQ; ++cc) ss[qt] = sum_sq(qf[qt][cc], ss[qt]);
+      ss[qt] = sum_row16(ss[qt]);
     }
     bool over = false;
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) over = over | !(m[qt] <= kBoundMax);
+    for (int qt = 0; qt < QT; ++qt) {
+      m[qt] = sqrtf(ss[qt]) * kmax * kBoundSlack;
+      over = over | !(m[qt] <= kBoundMax);
+    }
     bounded = __builtin_amdgcn_ballot_w64(over) == 0;
+    if constexpr (CS) {
+      // Without the bound the pairs run an extra pass with barriers of its
+      // own, so the whole workgroup takes one decision: bounded only if
+      // every wave is. (The SIMD-id slots are free after the kernel start;
+      // the next segment writes them after a barrier.)
+      int* flag = reinterpret_cast<int*>(lds + G::kSimdOff);
+      if (lane == 0) flag[wave] = bounded ? 1 : 0;
+      pair_sync();
+      int all = 1;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) all &= flag[w];
+      bounded = __builtin_amdgcn_readfirstlane(all) != 0;
+    }
     if (bounded) {
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
@@ -796,142 +866,242 @@ void attn_fwd_kernel(AttnArgs a) {
     }
   };
 
-  // Fragment reads. K fragment (kt, cc): key row 16 kt + l%16, chunk 4 cc +
-  // g4, stored at (4 cc + g4) ^ s = (g4 ^ s) ^ 4 cc, so one address
-  // register per cc (the swizzle takes l%16 & kSwz); V^T fragment ct:
-  // channel row 16 ct + l%16, chunk g4. The V^T base (kRing K sub-tiles in)
-  // is hidden from the compiler so that it stays in the register and out of
-  // the offset field.
-  static_assert(kRing * kKBytes <= 65536, "K sub-tiles within the first 64 KB");
+  // Fragment reads. K fragment (kt, cc): key row 16 kt + l%16 (CS: kt =
+  // half), chunk 4 cc + g4, stored at (4 cc + g4) ^ s = (g4 ^ s) ^ 4 cc (s =
+  // l%16 & kSwz), so one address register per cc; V^T fragment ct: channel
+  // row half DW + 16 ct + l%16, chunk g4. The V^T base (kRing K sub-tiles
+  // in) is hidden from the compiler so that it stays in the register and out
+  // of the offset field.
   bf16x8_t pf[QT];
-  const uint32_t kb16 = l16 * (2 * D) + ((g4 ^ (l16 & G::kSwz)) * 16);
-  uint32_t ka[NC];
+  const uint32_t kb16 = (l16 + (CS ? 16 * half : 0)) * (2 * D) + ((g4 ^ (l16 & G::kSwz)) * 16);
+  uint32_t ka[NCQ];
 #pragma unroll
-  for (int cc = 0; cc < NC; ++cc) ka[cc] = kb16 ^ (64u * cc);
-  uint32_t va = kRing * kKBytes + l16 * 64 + ((g4 ^ ((l16 >> 2) & 3)) * 16);
+  for (int cc = 0; cc < NCQ; ++cc) ka[cc] = kb16 ^ (64u * cc);
+  uint32_t va = kRing * kKBytes + half * (DW * 64) + l16 * 64 + ((g4 ^ ((l16 >> 2) & 3)) * 16);
   asm("" : "+v"(va));
-  // Fragment g of a step: g < 2 NC is K fragment (kt, cc) = (g % 2, g / 2)
-  // of the sub-tile in slot_k, the others V^T fragment ct = g - 2 NC of the
-  // one in slot_v. Each feeds two matrix-core instructions (both query tiles).
+  // Fragment g of a step: g < NKF is K fragment (kt, cc) = (g % 2, g / 2)
+  // (CS: (half, g)) of the sub-tile in slot_k, the others V^T fragment ct =
+  // g - NKF of the one in slot_v. Each feeds QT matrix-core instructions.
   auto frag = [&](int g, auto slot_k, auto slot_v) __attribute__((always_inline)) -> bf16x8_t {
     int sk, sv;
     if constexpr (std::is_integral_v<decltype(slot_k)>) sk = slot_k;
     else sk = decltype(slot_k)::value;
     if constexpr (std::is_integral_v<decltype(slot_v)>) sv = slot_v;
     else sv = decltype(slot_v)::value;
-    if (g < 2 * NC)
-      return *reinterpret_cast<const bf16x8_t*>(lds + sk * kKBytes + (g & 1) * (16 * 2 * D) + ka[g >> 1]);
-    return *reinterpret_cast<const bf16x8_t*>(lds + sv * kKBytes + (g - 2 * NC) * 1024 + va);
+    if (g < NKF) {
+      if constexpr (CS) return *reinterpret_cast<const bf16x8_t*>(lds + sk * kKBytes + ka[g]);
+      else return *reinterpret_cast<const bf16x8_t*>(lds + sk * kKBytes + (g & 1) * (16 * 2 * D) + ka[g >> 1]);
+    }
+    return *reinterpret_cast<const bf16x8_t*>(lds + sv * kKBytes + (g - NKF) * 1024 + va);
   };
-  constexpr int NG = 2 * NC + NT16;   // fragments per step
+  constexpr int NG = NKF + NT16;   // fragments per step
   auto rslot = [&](int x) { return (x - xb) & (kRing - 1); };
-  // One X phase: QK^T into s (K fragments of slot_k) and PV into acc (V^T
-  // fragments of slot_v, probabilities pf), in fenced groups of the two
+  // One X phase: QK^T into s (K fragments of slot_k) and, with PV, PV into
+  // acc (V^T fragments of slot_v, probabilities pf), in fenced groups of the
   // instructions that use fragment g and the read of fragment g + 4; fr holds
   // the first four fragments, read by the caller.
   bf16x8_t fr[4];
-  auto xphase = [&](f32x4_t (&s)[QT][2], auto slot_k, auto slot_v, bool do_qk) __attribute__((always_inline)) {
+  auto xphase = [&](f32x4_t (&s)[QT][2], auto slot_k, auto slot_v, auto pv, auto hf) __attribute__((always_inline)) {
+    constexpr bool PV = decltype(pv)::value;
+    constexpr int H = decltype(hf)::value;
+    constexpr int NGX = PV ? NG : NKF;
     bf16x8_t gf[NG];
 #pragma unroll
     for (int g = 0; g < 4; ++g) gf[g] = fr[g];
-    for_each_index(std::make_integer_sequence<int, NG>{}, [&](auto gc) __attribute__((always_inline)) {
+    for_each_index(std::make_integer_sequence<int, NGX>{}, [&](auto gc) __attribute__((always_inline)) {
       constexpr int g = decltype(gc)::value;
-      if constexpr (g + 4 < NG) gf[g + 4] = frag(g + 4, slot_k, slot_v);
-      if constexpr (g < 2 * NC) {
-        if (do_qk) {
+      if constexpr (g + 4 < NGX) gf[g + 4] = frag(g + 4, slot_k, slot_v);
+      if constexpr (g < NKF) {
 #pragma unroll
-          for (int qt = 0; qt < QT; ++qt)
-            s[qt][g & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gf[g], qf[qt][g >> 1], s[qt][g & 1], 0, 0, 0);
+        for (int qt = 0; qt < QT; ++qt) {
+          if constexpr (CS) s[qt][H] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gf[g], qf[qt][g], s[qt][H], 0, 0, 0);
+          else s[qt][g & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gf[g], qf[qt][g >> 1], s[qt][g & 1], 0, 0, 0);
         }
       } else {
 #pragma unroll
-        for (int qt = 0; qt < QT; ++qt) acc_mfma(qt, g - 2 * NC, gf[g], pf[qt]);
+        for (int qt = 0; qt < QT; ++qt) acc_mfma(qt, g - NKF, gf[g], pf[qt]);
       }
       fence();
     });
   };
 
-  // The rest of the tile, for the online maximum (BND false) or the fixed
-  // bounded offset (BND true); the bounded steps have no row maximum, no
-  // wave-wide check and no rescale.
-  auto run_tile = [&](auto bnd) __attribute__((always_inline)) {
-  constexpr bool BND = decltype(bnd)::value;
+  // Probabilities of key tile H (elements 4H .. 4H + 3 of each query tile's
+  // PV operand) and this lane's share of the sums; written for the partner.
+  auto probs_own = [&](const f32x4_t (&s)[QT][2], auto hf) __attribute__((always_inline)) {
+    constexpr int H = decltype(hf)::value;
+    uint32_t w[QT * 2];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pf[qt][4 * H + j] = (__bf16)__builtin_amdgcn_exp2f(s[qt][H][j]);
+#pragma unroll
+      for (int j = 0; j < 4; j += 2) {
+        const bf16x2_t pp = {pf[qt][4 * H + j], pf[qt][4 * H + j + 1]};
+        l_run[qt] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_run[qt], false);
+        w[qt * 2 + j / 2] = __builtin_bit_cast(uint32_t, pp);
+      }
+    }
+    static_assert(!CS || QT == 2, "one 16-byte exchange per lane");
+    *reinterpret_cast<u32x4_t*>(xp_out) = u32x4_t{w[0], w[1], w[2], w[3]};
+  };
+  // The partner's probabilities (key tile 1 - H) into the PV operands.
+  auto probs_in = [&](auto hf) __attribute__((always_inline)) {
+    constexpr int H = decltype(hf)::value;
+    const u32x4_t w = *reinterpret_cast<const u32x4_t*>(xp_in);
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      u32x4_t p = __builtin_bit_cast(u32x4_t, pf[qt]);
+      p[2 * (1 - H)] = w[2 * qt];
+      p[2 * (1 - H) + 1] = w[2 * qt + 1];
+      pf[qt] = __builtin_bit_cast(bf16x8_t, p);
+    }
+  };
+  // Largest score of key tile H per lane (the max pass).
+  auto max_own = [&](const f32x4_t (&s)[QT][2], float* mx, auto hf) __attribute__((always_inline)) {
+    constexpr int H = decltype(hf)::value;
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) mx[qt] = fmaxf(mx[qt], fmaxf(max3(s[qt][H][0], s[qt][H][1], s[qt][H][2]), s[qt][H][3]));
+  };
+
+  // The rest of the tile. MODE 0: the online maximum with lazy rescale;
+  // MODE 1: the fixed offsets msplat (a bound, or the exact row maxima), no
+  // row maximum, wave-wide check or rescale in the steps; MODE 2 (CS only):
+  // the max pass, QK^T only, each row's largest visible score into mxp.
+  // hf: this wave's channel half (CS; 0 otherwise).
+  float mxp[QT];
+  auto run_tile = [&](auto mode, auto hf, auto rf) __attribute__((always_inline)) {
+    constexpr int MODE = decltype(mode)::value;
+    constexpr int H = decltype(hf)::value;
+    // Role as a constant (CS: the pair's waits and refills depend on it, and
+    // branches on it would split the unrolled steps into many blocks).
+    constexpr int RF = decltype(rf)::value;
+    const bool role1 = CS ? RF == 1 : role != 0;
+    constexpr bool ONLINE = MODE == 0, MAXP = MODE == 2;
+    static_assert(!(CS && ONLINE) && (CS || !MAXP), "modes");
+    // QK^T accumulators start from -m: scores arrive relative to the row
+    // offset.
+    auto s_init = [&](int qt) __attribute__((always_inline)) -> f32x4_t {
+      if constexpr (ONLINE) return f32x4_t{0.f, 0.f, 0.f, 0.f};
+      else return msplat[qt];
+    };
     // Prologue: scores of xb set each row's offset to its exact maximum
-    // (online path), or start from the fixed offset (bounded path).
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kRing - 4) * LDPS) : "memory");
+    // (online path), or start from the fixed offset.
+    // Wait for K and V^T of xb and xb + 1 (and, in role 1, K of xb + 2).
+    if constexpr (CS) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * LDPS / 2) : "memory");
+    else asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kRing - 4) * LDPS) : "memory");
     __syncthreads();
     f32x4_t s[QT][2];
     {
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) s[qt][kt] = BND ? msplat[qt] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int kt = 0; kt < 2; ++kt) s[qt][kt] = s_init(qt);
 #pragma unroll
-      for (int g = 0; g < 2 * NC; ++g) {
+      for (int g = 0; g < NKF; ++g) {
         const bf16x8_t kfr = frag(g, 0, 0);
 #pragma unroll
-        for (int qt = 0; qt < QT; ++qt)
-          s[qt][g & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfr, qf[qt][g >> 1], s[qt][g & 1], 0, 0, 0);
-      }
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        if constexpr (BND) {
-          mask16(s[qt], xmap(xb), qt);
-        } else {
-          m_run[qt] = max_row16(rowmax16(s[qt], xmap(xb), qt, Mask{}));
-          if constexpr (WIN) {
-            seen[qt] = m_run[qt] != -INFINITY;
-            if (!seen[qt]) m_run[qt] = 0.f;
-          }
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            s[qt][0][r] -= m_run[qt];
-            s[qt][1][r] -= m_run[qt];
-            msplat[qt][r] = -m_run[qt];
-          }
+        for (int qt = 0; qt < QT; ++qt) {
+          if constexpr (CS) s[qt][H] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfr, qf[qt][g], s[qt][H], 0, 0, 0);
+          else s[qt][g & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfr, qf[qt][g >> 1], s[qt][g & 1], 0, 0, 0);
         }
       }
-      probs16(s, pf);
+      if constexpr (CS) {
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) mask_kt(s[qt][H], xmap(xb), qt, H);
+        if constexpr (MAXP) {
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt) mxp[qt] = -INFINITY;
+          max_own(s, mxp, hf);
+        } else {
+          probs_own(s, hf);
+        }
+        pair_sync();
+        if constexpr (RF == 1) issue_k(xb + kRing);   // every wave has read K of xb
+        if constexpr (!MAXP) probs_in(hf);
+      } else {
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+          if constexpr (!ONLINE) {
+            mask16(s[qt], xmap(xb), qt);
+          } else {
+            m_run[qt] = max_row16(rowmax16(s[qt], xmap(xb), qt, Mask{}));
+            if constexpr (WIN) {
+              seen[qt] = m_run[qt] != -INFINITY;
+              if (!seen[qt]) m_run[qt] = 0.f;
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              s[qt][0][r] -= m_run[qt];
+              s[qt][1][r] -= m_run[qt];
+              msplat[qt][r] = -m_run[qt];
+            }
+          }
+        }
+        probs16(s, pf);
+      }
     }
     // The first fragments of the first X phase: K(xb+1), V(xb).
 #pragma unroll
     for (int g = 0; g < 4; ++g) fr[g] = frag(g, rslot(min(xb + 1, xe - 1)), 0);
 
     // Step u: X = QK^T of u+1 and PV of u; Y = fragment reads of K(u+2) and
-    // V(u+1), the refill of the slot of u-1, the softmax of u+1 (as the
-    // 32x32 path).
+    // V(u+1), a ring refill, the softmax of u+1.
     // slot_vc, slot_kc: V(u) and K(u+1), read by this X phase; slot_vn,
     // slot_kn: V(u+1) and K(u+2), whose first fragments the Y phase reads.
     auto step = [&](int u, auto mask_next, auto slot_vn, auto slot_kn, auto slot_vc, auto slot_kc) __attribute__((always_inline)) {
       fence();
+      if constexpr (CS && !MAXP) probs_in(hf);
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) s[qt][kt] = msplat[qt];
-      xphase(s, slot_kc, slot_vc, true);
-      bar();
+        for (int kt = 0; kt < 2; ++kt) s[qt][kt] = CS ? s_init(qt) : msplat[qt];
+      xphase(s, slot_kc, slot_vc, std::integral_constant<bool, !MAXP>{}, hf);
+      if constexpr (CS && RF == 0) asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(LDPS) : "memory");
+      else bar();
       fence();
 #pragma unroll
       for (int g = 0; g < 4; ++g) fr[g] = frag(g, slot_kn, slot_vn);
-      issue_loads(u - 1 + kRing);
-      if constexpr (BND) {
-        if constexpr (decltype(mask_next)::value) {
-#pragma unroll
-          for (int qt = 0; qt < QT; ++qt) mask16(s[qt], xmap(u + 1), qt);
+      if constexpr (CS) {
+        if constexpr (RF == 1) {
+          issue_k(u + kRing + 1);
+          issue_v(u + kRing);
+        } else {
+          issue_k(u + kRing);
+          issue_v(u + kRing - 1);
         }
       } else {
-        float mx[QT];
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) mx[qt] = rowmax16(s[qt], xmap(u + 1), qt, mask_next);
-        maybe_rescale16(s, mx, mask_next);
+        issue_loads(u - 1 + kRing);
       }
-      probs16(s, pf);
-      fence();
-      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((kRing - 4) * LDPS) : "memory");
+      if constexpr (CS) {
+        if constexpr (decltype(mask_next)::value) {
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt) mask_kt(s[qt][H], xmap(u + 1), qt, H);
+        }
+        if constexpr (MAXP) max_own(s, mxp, hf);
+        else probs_own(s, hf);
+        fence();
+        if constexpr (RF == 1) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * LDPS) : "memory");
+        else asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      } else {
+        if constexpr (!ONLINE) {
+          if constexpr (decltype(mask_next)::value) {
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt) mask16(s[qt], xmap(u + 1), qt);
+          }
+        } else {
+          float mx[QT];
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt) mx[qt] = rowmax16(s[qt], xmap(u + 1), qt, mask_next);
+          maybe_rescale16(s, mx, mask_next);
+        }
+        probs16(s, pf);
+        fence();
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((kRing - 4) * LDPS) : "memory");
+      }
       fence();
     };
 
-    if (role) bar();
+    if (role1) bar();
     int u = xb;
     for (; u + kRing <= min(xe - 2, x_mask - 1); u += kRing) {
       for_each_index(std::make_integer_sequence<int, kRing>{}, [&](auto k) __attribute__((always_inline)) {
@@ -943,7 +1113,8 @@ void attn_fwd_kernel(AttnArgs a) {
     }
     for (; u < xe - 1; ++u) step(u, Mask{}, rslot(u + 1), rslot(min(u + 2, xe - 1)), rslot(u), rslot(u + 1));
     // Last X phase: PV of the last sub-tile only.
-    {
+    if constexpr (!MAXP) {
+      if constexpr (CS) probs_in(hf);
       const int vs = rslot(xe - 1);
 #pragma unroll
       for (int ct = 0; ct < NT16; ++ct) {
@@ -952,11 +1123,58 @@ void attn_fwd_kernel(AttnArgs a) {
         for (int qt = 0; qt < QT; ++qt) acc_mfma(qt, ct, vfr, pf[qt]);
       }
     }
+    if (!role1) bar();
+    // The ring holds refills that nobody reads; let them retire so no LDS
+    // write is pending when the workgroup ends or the ring restarts.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   };
-  if (bounded) run_tile(std::true_type{});
-  else run_tile(std::false_type{});
-  if (!role) bar();
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if constexpr (CS) {
+    // Without a usable bound, a max pass over the keys finds each row's
+    // largest score first (the pair's two key tiles combined), and the
+    // second pass runs with those exact maxima as fixed offsets.
+    auto both = [&](auto hf, auto rf) __attribute__((always_inline)) {
+      if (!bounded) {
+        run_tile(std::integral_constant<int, 2>{}, hf, rf);
+        float mr[QT];
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) mr[qt] = max_row16(mxp[qt]);
+        __syncthreads();
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) reinterpret_cast<float*>(xs_out)[qt] = mr[qt];
+        pair_sync();
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+          float m = fmaxf(mr[qt], reinterpret_cast<const float*>(xs_in)[qt]);
+          m = m == -INFINITY ? 0.f : m;   // a row that sees no key: l = 0, written as 0
+          m_run[qt] = m;
+          msplat[qt] = f32x4_t{-m, -m, -m, -m};
+        }
+        pair_sync();
+        fill_ring();
+      }
+      run_tile(std::integral_constant<int, 1>{}, hf, rf);
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    if (role) {
+      if (half) both(I1{}, I1{});
+      else both(I0{}, I1{});
+    } else {
+      if (half) both(I1{}, I0{});
+      else both(I0{}, I0{});
+    }
+    // Each lane's row-sum share over both key tiles: add the partner's.
+    __syncthreads();
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) reinterpret_cast<float*>(xs_out)[qt] = l_run[qt];
+    pair_sync();
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) l_run[qt] += reinterpret_cast<const float*>(xs_in)[qt];
+  } else {
+    using I0 = std::integral_constant<int, 0>;
+    if (bounded) run_tile(std::integral_constant<int, 1>{}, I0{}, I0{});
+    else run_tile(std::integral_constant<int, 0>{}, I0{}, I0{});
+  }
 
   if (rec < 0) {
 #pragma unroll
@@ -965,10 +1183,11 @@ void attn_fwd_kernel(AttnArgs a) {
       f32x4_t at[NT16];
 #pragma unroll
       for (int ct = 0; ct < NT16; ++ct) at[ct] = acc_get(qt, ct);
-      store_row16<D>(a, obase, rowq[qt], g4, at, (!WIN || l > 0.f) ? 1.0f / l : 0.f, qv_seg, gate_row);
+      store_row16<D, NT16>(a, obase + half * DW, rowq[qt], g4, at, (!WIN || l > 0.f) ? 1.0f / l : 0.f, qv_seg,
+                           gate_row);
     }
   } else {
-    float* pr = a.part + (int64_t)rec * attn_part_floats(D) + tid;
+    float* pr = a.part + (int64_t)rec * attn_part_floats(D) + lwave * 64 + lane;
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
 #pragma unroll
@@ -978,489 +1197,6 @@ void attn_fwd_kernel(AttnArgs a) {
       pr[(G::kRecA + qt) * T] = m_run[qt];
       pr[(G::kRecA + QT + qt) * T] = l_run[qt];
     }
-  }
-  } else {
-  // Masking: lane's last visible key (its query row under the causal mask,
-  // capped by the valid keys), and the first sub-tile in which some lane of
-  // the workgroup may see a masked key; steps before it skip the mask.
-  const int row = q0 + wave * 32 + lq;
-  const int lim = a.causal ? min(row, kvv_t - 1) : kvv_t - 1;
-  // Sub-tile of virtual step v (the identity unless a frame window skips
-  // the keys between its two ranges).
-  auto xmap = [&](int v) {
-    if constexpr (WIN) return v < wn1 ? v : v + ws2;
-    else return v;
-  };
-  int x_mask = min(a.causal ? q0 / kSub : 0x7fffffff, (kvv_t % kSub) ? kvv_t / kSub : 0x7fffffff);
-  // Frame window, per lane: the chunk of the lane's row, or -1 for a row of
-  // an anchor frame (a dense row). Masked steps derive the row's window from
-  // it, so the steady state keeps one register for the window.
-  int c_row = -1;
-  if constexpr (WIN) {
-    const int f = row / a.win_F;
-    c_row = f < a.win_A ? -1 : (f - a.win_A) / a.win_C;
-    // Uniform tiles mask only a partial last sub-tile; the others mask every
-    // step.
-    x_mask = !win_fast ? 0 : ((kvv_t % kSub) && xmap(xe - 1) == kvv_t / kSub ? xe - 1 : 0x7fffffff);
-  }
-
-  // Q fragments (B operand of S^T = K Q^T): the lane holds query row
-  // 32*wave + lq, channels 16*kk + 8*g .. +7. Loaded before the ring fill so
-  // the in-order load counter covers them.
-  bf16x8_t qf[NF];
-  {
-    const uint16_t* qp = a.qw + ((int64_t)bh * a.Sq_pad + q0 + wave * 32 + lq) * D + g * 8;
-#pragma unroll
-    for (int kk = 0; kk < NF; ++kk) qf[kk] = *reinterpret_cast<const bf16x8_t*>(qp + kk * 16);
-  }
-
-  f32x16_t acc[NT];
-#pragma unroll
-  for (int dt = 0; dt < NT; ++dt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
-  float m_run = 0.f;       // row offset (exp2 units), shared by the lane pair
-  float l_run = 0.f;       // this lane's share of the row sum of bf16 probabilities
-  bool seen = true;        // the row has met a visible key (m_run is its offset)
-  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-
-  // The a priori bound of the 32x32 paths (head dims 64 and 256; H3's norm
-  // is defined on 128 channels only, so the bound comes from the data): row
-  // i's scores lie in [-m_i, m_i], m_i = |q_i| max_j |k_j| (the lane pair
-  // holds the row's channels in qf); when every row of the wave has m_i <=
-  // kBoundMax, m_i is its fixed offset and the steps keep no row maximum.
-  bool bounded = false;
-  {
-    if (a.knorm != nullptr) {
-      float ss = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < NF; ++kk) ss = sum_sq(qf[kk], ss);
-      const float m = sqrtf(sum_lane_pair(ss)) * key_norm_max(a, bh_kv) * kBoundSlack;
-      bounded = __builtin_amdgcn_ballot_w64(!(m <= kBoundMax)) == 0;
-      if (bounded) m_run = m;
-    }
-  }
-
-  // Sets this lane's scores of sub-tile x that its row does not see (past
-  // its last visible key, or outside its frame window) to -inf (a no-op in
-  // sub-tiles without such keys).
-  auto mask_scores = [&](f32x16_t& s, int x) {
-    // Window rows see keys below a_end (the anchor frames) and in
-    // [w_lo, w_hi) (the chunks within R of theirs); dense rows see all.
-    int a_end = 0x7fffffff, w_lo = 0, w_hi = 0;
-    if constexpr (WIN) {
-      if (c_row >= 0) {
-        // The launcher clamps F, C, R, A to the sequence (which is below
-        // 2^28 rows), so these products stay below 2^31.
-        a_end = a.win_A * a.win_F;
-        w_lo = (a.win_A + a.win_C * max(c_row - a.win_R, 0)) * a.win_F;
-        w_hi = (a.win_A + a.win_C * min(c_row + a.win_R + 1, win_cap)) * a.win_F;
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = x * kSub + (r >> 2) * 8 + g * 4 + (r & 3);
-      if constexpr (WIN) {
-        // Bitwise, not short-circuit, so it compiles to compares and one
-        // select instead of branches.
-        const bool hidden = (key > lim) | ((key >= a_end) & ((key < w_lo) | (key >= w_hi)));
-        s[r] = hidden ? -INFINITY : s[r];
-      } else {
-        if (key > lim) s[r] = -INFINITY;
-      }
-    }
-  };
-  // Row max of this lane's 16 scores of sub-tile x; with MASK, the keys the
-  // lane's row does not see are set to -inf first.
-  auto rowmax = [&](f32x16_t& s, int x, auto mask) {
-    if constexpr (decltype(mask)::value) mask_scores(s, x);
-    // Depth-3 tree over the 16 values.
-    const float m0 = max3(s[0], s[1], s[2]), m1 = max3(s[3], s[4], s[5]), m2 = max3(s[6], s[7], s[8]);
-    const float m3 = max3(s[9], s[10], s[11]), m4 = max3(s[12], s[13], s[14]);
-    return fmaxf(max3(m0, m1, m2), max3(m3, m4, s[15]));
-  };
-  using NoMask = std::integral_constant<bool, false>;
-  using Mask = std::integral_constant<bool, true>;
-  // sched_barrier(0) fences keep the compiler from moving instructions
-  // across them (phase boundaries, interleave groups).
-  auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
-  if constexpr (G::kPipe) {
-    // Head dim 256 runs one wave per SIMD, so no second wave covers the
-    // softmax: each wave overlaps it with its own matrix-core work. Step u
-    // sends QK^T of sub-tile u+2 and PV of sub-tile u to the matrix core and
-    // computes, between those instructions, the softmax of sub-tile u+1,
-    // whose scores the previous step produced. K and V^T have rings of their
-    // own, kRing slots of one 16 KB sub-tile each (128 KB, which keeps every
-    // fragment offset inside the 16-bit field): K(x) is read at step x-2 and
-    // V^T(x) at step x, and each slot is refilled the step after its last
-    // read. A step's end waits for the loads of the step before, so a load
-    // has one step and more to land (load latency is not the limit here:
-    // waiting a step earlier, and rings of two and three slots, measured the
-    // same), and the next step's first fragments can be read before the
-    // barrier.
-    constexpr int kS = kKBytes;                 // one K or V^T sub-tile
-    constexpr int kV0 = kRing * kS;             // V^T ring base
-    constexpr int LPS = kS / 1024 / NW;         // 1 KB loads per wave per sub-tile and operand
-    constexpr int kWait = (2 * kRing - 6) * LPS;   // loads that may stay in flight at a step's end
-    int loffK[LPS], loffV[LPS];
-#pragma unroll
-    for (int i = 0; i < LPS; ++i) {
-      const int Q = (wave + NW * i) * 64 + lane;
-      const int r = Q / (D / 8), p = Q % (D / 8);
-      loffK[i] = (r * D + ((p ^ (r & G::kSwz)) * 8)) * 2;
-      const int d = Q >> 2, pv = Q & 3;
-      loffV[i] = (d * kSub + ((pv ^ ((d >> 2) & 3)) * 8)) * 2;
-    }
-    const uint16_t* kw = a.kw + (int64_t)bh_kv * a.Sk_pad * D;
-    const uint16_t* vt = a.vt + (int64_t)bh_kv * a.Sk_pad * D;
-    auto slot_of = [&](int x) { return (x - xb) % kRing; };
-    // Loads of sub-tile x into its ring slot; past the last sub-tile the
-    // range is empty (zeros, no memory access) and the slot is never read.
-    auto issue_k = [&](int x) __attribute__((always_inline)) {
-      const bool live = x < xe;
-      const uint16_t* src = kw + (int64_t)(live ? xmap(x) : 0) * (kSub * D);
-      uint8_t* dst = lds + slot_of(x) * kS;
-#pragma unroll
-      for (int i = 0; i < LPS; ++i) load_lds16(src, live ? kS : 0, loffK[i], dst + (wave + NW * i) * 1024);
-    };
-    auto issue_v = [&](int x) __attribute__((always_inline)) {
-      const bool live = x < xe;
-      const uint16_t* src = vt + (int64_t)(live ? xmap(x) : 0) * (kSub * D);
-      uint8_t* dst = lds + kV0 + slot_of(x) * kS;
-#pragma unroll
-      for (int i = 0; i < LPS; ++i) load_lds16(src, live ? kS : 0, loffV[i], dst + (wave + NW * i) * 1024);
-    };
-    // Fragment reads. K fragments kk and kk + 8 differ only in bit 4 of the
-    // chunk index, which the swizzle leaves alone (256 bytes apart).
-    // The V^T addresses hold the ring base (64 KB or more, past the offset
-    // field), hidden from the compiler so it stays out of the per-read offsets.
-    uint32_t ka[8], va[2];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) ka[k] = kbase ^ (32u * k);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      va[ks] = vaddr[ks] - kKBytes + kV0;
-      asm("" : "+v"(va[ks]));
-    }
-    auto kfrag = [&](int slot, int kk) __attribute__((always_inline)) {
-      return *reinterpret_cast<const bf16x8_t*>(lds + slot * kS + (kk >> 3) * 256 + ka[kk & 7]);
-    };
-    auto vfrag = [&](int slot, int i) __attribute__((always_inline)) {
-      return *reinterpret_cast<const bf16x8_t*>(lds + slot * kS + (i >> 1) * 2048 + va[i & 1]);
-    };
-
-    // p = exp2(s) of scores already relative to the row offset, as the two
-    // B operands of PV, and this lane's share of their sum added to ls.
-    auto probs256 = [&](const f32x16_t& s, bf16x8_t* pn, float& ls) __attribute__((always_inline)) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) pn[ks][i] = (__bf16)__builtin_amdgcn_exp2f(s[ks * 8 + i]);
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int i = 0; i < 8; i += 2) {
-          const bf16x2_t pp = {pn[ks][i], pn[ks][i + 1]};
-          ls = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ls, false);
-        }
-    };
-    // Raises the row offset by the lane pair's excess mx over it (under a
-    // frame window, a row meeting its first visible keys takes their maximum
-    // as its offset), rescales the accumulator and the running sum, and
-    // returns the change of the offset.
-    auto rescale256 = [&](float mx, auto mask) __attribute__((always_inline)) -> float {
-      float delta = max_lane_pair(mx);
-      float alpha;
-      if constexpr (WIN && decltype(mask)::value) {
-        const bool fresh = !seen && delta != -INFINITY;
-        seen = seen || fresh;
-        delta = fresh ? delta : fmaxf(delta, 0.f);
-        // A fresh row's accumulator and sum are still zero.
-        alpha = fresh ? 1.f : __builtin_amdgcn_exp2f(-delta);
-      } else {
-        delta = fmaxf(delta, 0.f);
-        alpha = __builtin_amdgcn_exp2f(-delta);
-      }
-      m_run += delta;
-      l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < NT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
-      return delta;
-    };
-
-    // Prologue. Ring fill in the order of first use: K(xb), K(xb+1), then
-    // V^T(xb+t), K(xb+2+t) for t < kRing-2. The scores of xb set each row's
-    // offset to its exact maximum (so the row keeps one probability of 1).
-    // Q fragments live in the accumulation registers (the matrix core reads
-    // its operands from either file), leaving the vector registers to the
-    // fragments in flight and the softmax.
-    if constexpr (G::WPE == 1) {
-#pragma unroll
-      for (int kk = 0; kk < NF; ++kk) asm volatile("" : "+a"(qf[kk]));
-    }
-    issue_k(xb);
-    issue_k(xb + 1);
-#pragma unroll
-    for (int t = 0; t < kRing - 2; ++t) {
-      issue_v(xb + t);
-      issue_k(xb + 2 + t);
-    }
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((2 * kRing - 4) * LPS) : "memory");
-    __syncthreads();
-    // The rest of the tile, with the online maximum (BND false) or the
-    // fixed per-row bounds (BND true: no row maximum, no rescale).
-    auto run_tile = [&](auto bnd) __attribute__((always_inline)) {
-    constexpr bool BND = decltype(bnd)::value;
-      const f32x16_t zero16 = {};
-      f32x16_t s_nx, msplat;
-      if constexpr (BND) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) msplat[r] = -m_run;
-      }
-      f32x16_t s0 = BND ? msplat : zero16;
-#pragma unroll
-      for (int kk = 0; kk < NF; ++kk) s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(0, kk), qf[kk], s0, 0, 0, 0);
-      bf16x8_t pf[2];
-      float dprev = 0.f;
-      if constexpr (BND) {
-        mask_scores(s0, xmap(xb));
-        probs256(s0, pf, l_run);
-      } else {
-        m_run = max_lane_pair(rowmax(s0, xmap(xb), Mask{}));
-        // A row with no visible key here (possible only under a frame window)
-        // starts from offset 0 and takes its offset from the first keys it sees.
-        if constexpr (WIN) {
-          seen = m_run != -INFINITY;
-          if (!seen) m_run = 0.f;
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          s0[r] -= m_run;
-          msplat[r] = -m_run;
-        }
-        probs256(s0, pf, l_run);
-      }
-      s_nx = msplat;
-#pragma unroll
-      for (int kk = 0; kk < NF; ++kk) s_nx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(1, kk), qf[kk], s_nx, 0, 0, 0);
-      // Every wave has read K slots 0 and 1: the refills of the first step
-      // before it, then the wait for K(xb+2), V^T(xb), K(xb+3) and V^T(xb+1).
-      bar();
-      issue_k(xb + kRing);
-      issue_v(xb + kRing - 2);
-      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kWait) : "memory");
-      // The first four fragments of the first step (K(xb+2) 0, V^T(xb) 0,
-      // K(xb+2) 1, V^T(xb) 1); each step without a mask reads those of the next.
-      bf16x8_t nf[4];
-#pragma unroll
-      for (int f = 0; f < 4; ++f) nf[f] = (f & 1) ? vfrag(0, f >> 1) : kfrag(2, f >> 1);
-
-      // Step u: refills of the slots read last step (K(u+1), V^T(u-1)); QK^T
-      // of u+2 (when it exists) and PV of u; the softmax of u+1. At the end,
-      // K(u+4) and V^T(u+2) have landed for every wave; a step without a mask
-      // has read the first fragments of K(u+3) and V^T(u+1), which landed a
-      // step earlier, before that wait, so the next step's first matrix-core
-      // instruction does not wait on LDS. Without the mask the
-      // step has no data-dependent branch before its last instruction: each row
-      // raises its offset by its excess when that passes 2^kRescaleLog2 and the
-      // running sum takes the factor at once, while the accumulator, which PV of
-      // u (still relative to the old offset) is updating, is scaled after it in
-      // the rare step where some row raised, together with the probabilities,
-      // which the block computed with the old offset. So the matrix-core and
-      // vector work form one block that the scheduler interleaves: one fragment
-      // read and a few vector instructions per matrix-core instruction.
-      // Scores leave QK^T relative to the row offset (the accumulator starts at
-      // msplat = -offset); scores computed before a raise are shifted at the
-      // next step's start, in the same rare case.
-      auto step256 = [&](int u, auto mask, auto kslot, auto vslot, auto with_qk, int nkslot = 0, int nvslot = 0) __attribute__((always_inline)) {
-        constexpr bool kMask = decltype(mask)::value;
-        issue_k(u + 1 + kRing);
-        issue_v(u - 1 + kRing);
-        f32x16_t s = s_nx;
-        // s came out of last step's QK^T relative to the offset before that
-        // step raised it by dprev (rare).
-        if constexpr (!BND) {
-          if (__builtin_amdgcn_ballot_w64(dprev != 0.f) != 0) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              s[r] -= dprev;
-              msplat[r] -= dprev;
-            }
-          }
-        }
-        bf16x8_t pn[2];
-        float ls = 0.f;
-        if constexpr (!kMask && decltype(with_qk)::value) {
-          // The 32 matrix-core instructions f (even: QK^T fragment f/2, odd: PV
-          // fragment f/2) each with the LDS read of fragment f+4 and a slice of
-          // the softmax, in groups the compiler keeps in this order.
-          auto frag = [&](int f) __attribute__((always_inline)) {
-            return (f & 1) ? vfrag(vslot, f >> 1) : kfrag(kslot, f >> 1);
-          };
-          bf16x8_t fr[2 * NF];
-          f32x16_t sn = msplat;
-          float m0, m1, m2, m3, m4, mx, delta, alpha;
-          uint32_t pk[8];
-#pragma unroll
-          for (int f = 0; f < 4; ++f) fr[f] = nf[f];
-          fence();
-          for_each_index(std::make_integer_sequence<int, 2 * NF>{}, [&](auto fc) __attribute__((always_inline)) {
-            constexpr int f = decltype(fc)::value;
-            if constexpr (f + 4 < 2 * NF) fr[f + 4] = frag(f + 4);
-            if constexpr (f & 1)
-              acc[f >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[f], pf[(f >> 1) & 1], acc[f >> 2], 0, 0, 0);
-            else
-              sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[f], qf[f >> 1], sn, 0, 0, 0);
-            // The softmax in 24 slices, slice i in group i (2 NF = 32) or
-            // spread in order over the 16 groups (2 NF = 16). Each slice's
-            // result is pinned in its group by an empty asm use: the fences
-            // bind the scheduler, not the passes that move pure arithmetic
-            // towards its first use. With the fixed offsets (BND) the first
-            // eight slices (row maximum, offset raise) do not exist and the
-            // other sixteen spread over the groups.
-            for_each_index(std::make_integer_sequence<int, 24>{}, [&](auto ic) __attribute__((always_inline)) {
-              constexpr int i = decltype(ic)::value;
-              constexpr int grp = BND ? (i < 8 ? -1 : (i - 8) * 2 * NF / 16) : (2 * NF >= 24 ? i : i * 2 * NF / 24);
-              if constexpr (grp == f) {
-                if constexpr (i < 5) {
-                  const float t = max3(s[3 * i], s[3 * i + 1], s[3 * i + 2]);
-                  asm volatile("" ::"v"(t));
-                  if constexpr (i == 0) m0 = t;
-                  else if constexpr (i == 1) m1 = t;
-                  else if constexpr (i == 2) m2 = t;
-                  else if constexpr (i == 3) m3 = t;
-                  else m4 = t;
-                } else if constexpr (i == 5) {
-                  mx = fmaxf(max3(m0, m1, m2), max3(m3, m4, s[15]));
-                  asm volatile("" ::"v"(mx));
-                } else if constexpr (i == 6) {
-                  mx = max_lane_pair(mx);
-                  asm volatile("" ::"v"(mx));
-                } else if constexpr (i == 7) {
-                  // Each row raises its offset by its excess when that passes
-                  // 2^kRescaleLog2; the sum takes the factor now, the
-                  // accumulator after this step's PV.
-                  delta = mx > kRescaleLog2 ? mx : 0.f;
-                  m_run += delta;
-                  alpha = __builtin_amdgcn_exp2f(-delta);
-                  l_run *= alpha;
-                  asm volatile("" ::"v"(m_run), "v"(l_run), "v"(alpha));
-                } else if constexpr (i < 16) {
-                  constexpr int e = 2 * (i - 8);
-                  pk[i - 8] = pack_bf16x2(__builtin_amdgcn_exp2f(s[e]), __builtin_amdgcn_exp2f(s[e + 1]));
-                  asm volatile("" ::"v"(pk[i - 8]));
-                } else {
-                  ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[i - 16]), ones, ls, false);
-                  asm volatile("" ::"v"(ls));
-                }
-              }
-            });
-            fence();
-          });
-          s_nx = sn;
-          if (!BND && __builtin_amdgcn_ballot_w64(delta != 0.f) != 0) {
-#pragma unroll
-            for (int dt = 0; dt < NT; ++dt)
-#pragma unroll
-              for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s[r] -= delta;
-            ls = 0.f;
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                pk[4 * ks + i] = pack_bf16x2(__builtin_amdgcn_exp2f(s[8 * ks + 2 * i]), __builtin_amdgcn_exp2f(s[8 * ks + 2 * i + 1]));
-                ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[4 * ks + i]), ones, ls, false);
-              }
-          }
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks)
-            pn[ks] = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]});
-          if constexpr (!BND) dprev = delta;
-        } else {
-          if constexpr (decltype(with_qk)::value) {
-            f32x16_t sn = msplat;
-#pragma unroll
-            for (int m = 0; m < NF; ++m) {
-              sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(kslot, m), qf[m], sn, 0, 0, 0);
-              acc[m >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag(vslot, m), pf[m & 1], acc[m >> 1], 0, 0, 0);
-            }
-            s_nx = sn;
-          } else {
-#pragma unroll
-            for (int m = 0; m < NF; ++m)
-              acc[m >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag(vslot, m), pf[m & 1], acc[m >> 1], 0, 0, 0);
-          }
-          if constexpr (BND) {
-            if constexpr (kMask) mask_scores(s, xmap(u + 1));
-          } else {
-            const float mx = rowmax(s, xmap(u + 1), mask);
-            bool trigger = mx > kRescaleLog2;
-            if constexpr (WIN && kMask) trigger = trigger || (!seen && mx != -INFINITY);
-            dprev = 0.f;
-            if (__builtin_amdgcn_ballot_w64(trigger) != 0) {
-              dprev = rescale256(mx, mask);
-#pragma unroll
-              for (int r = 0; r < 16; ++r) s[r] -= dprev;
-            }
-          }
-          probs256(s, pn, ls);
-        }
-        l_run += ls;
-        pf[0] = pn[0];
-        pf[1] = pn[1];
-        if constexpr (!kMask && decltype(with_qk)::value) {
-#pragma unroll
-          for (int f = 0; f < 4; ++f) nf[f] = (f & 1) ? vfrag(nvslot, f >> 1) : kfrag(nkslot, f >> 1);
-        }
-        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kWait) : "memory");
-      };
-
-      // Steady state in blocks of kRing steps (ring slots as constants) while
-      // the steps have a QK^T and need no mask; the rest address the ring at
-      // run time and mask.
-      int u = xb;
-      for (; u + kRing <= min(xe - 2, x_mask - 1); u += kRing) {
-        for_each_index(std::make_integer_sequence<int, kRing>{}, [&](auto k) {
-          constexpr int K = decltype(k)::value;
-          step256(u + K, NoMask{}, (K + 2) % kRing, K, std::true_type{}, (K + 3) % kRing, (K + 1) % kRing);
-        });
-      }
-      for (; u < xe - 2; ++u) step256(u, Mask{}, slot_of(u + 2), slot_of(u), std::true_type{});
-      if (u == xe - 2) {
-        step256(u, Mask{}, 0, slot_of(u), std::false_type{});
-        ++u;
-      }
-      // PV of the last sub-tile.
-      {
-        const int vs = slot_of(xe - 1);
-#pragma unroll
-        for (int m = 0; m < NF; ++m)
-          acc[m >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag(vs, m), pf[m & 1], acc[m >> 1], 0, 0, 0);
-      }
-    };
-    if (bounded) run_tile(std::true_type{});
-    else run_tile(std::false_type{});
-    // Let the refills nobody reads retire before the workgroup ends or the
-    // next segment refills the rings.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  }
-  if (rec < 0) {
-    // A row that saw no key (frame window only) has l = 0 and is written as 0.
-    const float l = sum_lane_pair(l_run);
-    store_row<D>(a, obase, q0 + wave * 32 + lq, g, acc, (!WIN || l > 0.f) ? 1.0f / l : 0.f, qv_seg, gate_row);
-  } else {
-    float* pr = a.part + (int64_t)rec * attn_part_floats(D) + tid;
-#pragma unroll
-    for (int dt = 0; dt < NT; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) pr[(dt * 16 + r) * T] = acc[dt][r];
-    pr[G::kRecM * T] = m_run;
-    pr[G::kRecL * T] = l_run;
-  }
   }
   if (si + 1 < nseg) __syncthreads();   // the next segment refills the LDS ring
   }
@@ -1722,7 +1458,7 @@ void attn_resident_kernel(AttnArgs a, int32_t G) {
     }
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt)
-      store_row16<D>(a, obase, t * BM + wave * 32 + qt * 16 + l16, g4, acc[qt], 1.0f / sum_row16(l_run[qt]), a.q_valid,
+      store_row16<D, NT16>(a, obase, t * BM + wave * 32 + qt * 16 + l16, g4, acc[qt], 1.0f / sum_row16(l_run[qt]), a.q_valid,
                      gate_row);
   }
 }
@@ -1736,9 +1472,11 @@ __global__ __launch_bounds__(Geo<D>::NW * 64) void attn_merge_kernel(AttnArgs a)
   using G = Geo<D>;
   constexpr int BM = G::BM;
   constexpr int T = G::NW * 64;
-  constexpr int NT = G::NT;
+  constexpr int QT = G::QT;
+  constexpr int NT16 = G::DW / 16;   // 16-channel output tiles per thread
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int lw = tid >> 6;           // logical wave: its rows (and channel half at 256)
+  const int pair = G::kCS ? lw >> 1 : lw, half = G::kCS ? lw & 1 : 0;
   const int lane = tid & 63;
   const int t = blockIdx.x;
   const int NU = (a.kv_valid + kSub - 1) / kSub;
@@ -1747,7 +1485,7 @@ __global__ __launch_bounds__(Geo<D>::NW * 64) void attn_merge_kernel(AttnArgs a)
   const int q0 = (tg - bh * a.nqv) * BM;
   const int b = bh / a.H;
   const int h = bh - b * a.H;
-  uint16_t* obase = a.o + ((int64_t)b * a.Sq * a.H + h) * D;
+  uint16_t* obase = a.o + ((int64_t)b * a.Sq * a.H + h) * D + half * G::DW;
 
   // The blocks j0 .. j1 that touch tile t, and block j's record for it.
   int j0, j1;
@@ -1756,70 +1494,46 @@ __global__ __launch_bounds__(Geo<D>::NW * 64) void attn_merge_kernel(AttnArgs a)
     return a.part + (int64_t)merge_record(j, t, a.n_split, NU, a.n_split_blocks) * attn_part_floats(D) + tid;
   };
   const uint16_t* gate_row = a.gate ? a.gate + (int64_t)b * a.Sq * a.H + h : nullptr;
-  if constexpr (G::kM16) {
-    // Records in the 16x16 layout: QT query tiles x D/16 tiles x 4
-    // registers, then the QT rows' offsets and the QT partial sums.
-    constexpr int NT16 = D / 16;
-    constexpr int QT = G::QT;
-    f32x4_t acc[QT][NT16];
-    float M[QT], l[QT];
+  // Records in the 16x16 layout: QT query tiles x NT16 tiles x 4 registers,
+  // then the QT rows' offsets and the QT partial sums.
+  f32x4_t acc[QT][NT16];
+  float M[QT], l[QT];
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      M[qt] = -INFINITY;
-      l[qt] = 0.f;
-      for (int j = j0; j <= j1; ++j) M[qt] = fmaxf(M[qt], record(j)[(G::kRecA + qt) * T]);
+  for (int qt = 0; qt < QT; ++qt) {
+    M[qt] = -INFINITY;
+    l[qt] = 0.f;
+    for (int j = j0; j <= j1; ++j) M[qt] = fmaxf(M[qt], record(j)[(G::kRecA + qt) * T]);
 #pragma unroll
-      for (int ct = 0; ct < NT16; ++ct) acc[qt][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
-    for (int j = j0; j <= j1; ++j) {
-      const float* pr = record(j);
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        const float w = __builtin_amdgcn_exp2f(pr[(G::kRecA + qt) * T] - M[qt]);
-        l[qt] += w * pr[(G::kRecA + QT + qt) * T];
-#pragma unroll
-        for (int ct = 0; ct < NT16; ++ct)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[qt][ct][r] += w * pr[((qt * NT16 + ct) * 4 + r) * T];
-      }
-    }
-    const int l16 = lane & 15, g4 = lane >> 4;
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      const uint32_t u = __builtin_bit_cast(uint32_t, l[qt]);
-      const auto sw = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-      const float lr = sum_lane_pair(__builtin_bit_cast(float, (uint32_t)sw[0]) + __builtin_bit_cast(float, (uint32_t)sw[1]));
-      store_row16<D>(a, obase, q0 + wave * G::WROWS + qt * 16 + l16, g4, acc[qt], 1.0f / lr, a.q_valid, gate_row);
-    }
-  } else {
-  float M = -INFINITY;
-  for (int j = j0; j <= j1; ++j) M = fmaxf(M, record(j)[G::kRecM * T]);
-  f32x16_t acc[NT];
-#pragma unroll
-  for (int dt = 0; dt < NT; ++dt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
-  float l = 0.f;
+    for (int ct = 0; ct < NT16; ++ct) acc[qt][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
   for (int j = j0; j <= j1; ++j) {
     const float* pr = record(j);
-    const float w = __builtin_amdgcn_exp2f(pr[G::kRecM * T] - M);
-    l += w * pr[G::kRecL * T];
 #pragma unroll
-    for (int dt = 0; dt < NT; ++dt)
+    for (int qt = 0; qt < QT; ++qt) {
+      const float w = __builtin_amdgcn_exp2f(pr[(G::kRecA + qt) * T] - M[qt]);
+      l[qt] += w * pr[(G::kRecA + QT + qt) * T];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[dt][r] += w * pr[(dt * 16 + r) * T];
+      for (int ct = 0; ct < NT16; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[qt][ct][r] += w * pr[((qt * NT16 + ct) * 4 + r) * T];
+    }
   }
-  store_row<D>(a, obase, q0 + wave * 32 + (lane & 31), lane >> 5, acc, 1.0f / sum_lane_pair(l), a.q_valid, gate_row);
+  const int l16 = lane & 15, g4 = lane >> 4;
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, l[qt]);
+    const auto sw = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const float lr = sum_lane_pair(__builtin_bit_cast(float, (uint32_t)sw[0]) + __builtin_bit_cast(float, (uint32_t)sw[1]));
+    store_row16<D, NT16>(a, obase, q0 + pair * G::WROWS + qt * 16 + l16, g4, acc[qt], 1.0f / lr, a.q_valid, gate_row);
   }
 }
 
-// Key held at position p (< 32) of a V^T sub-tile: sigma (bits 2 and 3 of
-// p swapped) for the 32x32 PV operand; for the 16x16x32 path (kM16),
-// position 8g + j holds key 16 (j/4) + 4g + j%4.
+// Key held at position p (< 32) of a V^T sub-tile: position 8g + j holds
+// key 16 (j/4) + 4g + j%4, the keys whose probabilities lane group g of the
+// 16x16x32 PV operand supplies.
 template <int D>
 __device__ inline int key_of_position(int p) {
-  if constexpr (Geo<D>::kM16) return ((p & 4) << 2) | ((p & 0x18) >> 1) | (p & 3);
-  else return (p & ~0xC) | ((p & 4) << 1) | ((p & 8) >> 1);
+  return ((p & 4) << 2) | ((p & 0x18) >> 1) | (p & 3);
 }
 
 // Transposed, key-blocked copy of v for the PV operand: a block moves 64 keys

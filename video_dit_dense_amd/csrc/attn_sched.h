@@ -9,15 +9,15 @@
 
 namespace h3 {
 
-// Attention tiling by head dim D (64, 128 or 256): a workgroup of
-// attn_threads(D) / 64 waves owns attn_rows(D) query rows of one (b, h) and
-// walks the keys in kAttnSub-key sub-tiles. At head dims 64 and 128 each
-// wave holds attn_query_tiles(D) 16-row query tiles (64 and 32 rows); at 256
-// each of four waves holds one 32-row tile.
+// Attention tiling by head dim D (64, 128 or 256): a workgroup of eight
+// waves owns attn_rows(D) query rows of one (b, h) and walks the keys in
+// kAttnSub-key sub-tiles. Each wave holds attn_query_tiles(D) 16-row query
+// tiles (64 rows at head dim 64, 32 at 128); at 256 the waves work in pairs
+// that share 32 rows, each wave holding half of the channels.
 constexpr int kAttnSub = 32;
-constexpr int attn_threads(int D) { return D <= 128 ? 512 : 256; }
+constexpr int attn_threads(int) { return 512; }
 constexpr int attn_query_tiles(int D) { return D == 64 ? 4 : 2; }
-constexpr int attn_rows(int D) { return D <= 128 ? attn_threads(D) / 64 * 16 * attn_query_tiles(D) : attn_threads(D) / 2; }
+constexpr int attn_rows(int D) { return attn_threads(D) / 64 * 16 * attn_query_tiles(D) / (D == 256 ? 2 : 1); }
 
 // Load balancing of the last, partial round of query tiles (stream-K): those
 // tiles' sub-tile steps are split evenly over up to kSplitMaxBlocks
@@ -31,8 +31,7 @@ constexpr int kSplitMinSteps = 16;
 // share of rows x D), then each thread's row offsets and partial sums, one
 // of each per query tile.
 constexpr int attn_part_floats(int D) {
-  return D <= 128 ? (attn_rows(D) * D / attn_threads(D) + 2 * attn_query_tiles(D)) * attn_threads(D)
-                  : (D / 2 + 2) * attn_threads(D);
+  return (attn_rows(D) * D / attn_threads(D) + 2 * attn_query_tiles(D)) * attn_threads(D);
 }
 
 // Partial records the forward workspace reserves for these sizes: two per

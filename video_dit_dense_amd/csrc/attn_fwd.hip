@@ -1059,20 +1059,11 @@ void attn_fwd_kernel(AttnArgs a) {
       if constexpr (CS && RF == 0) asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(LDPS) : "memory");
       else bar();
       fence();
-#pragma unroll
-      for (int g = 0; g < 4; ++g) fr[g] = frag(g, slot_kn, slot_vn);
       if constexpr (CS) {
-        if constexpr (RF == 1) {
-          issue_k(u + kRing + 1);
-          issue_v(u + kRing);
-        } else {
-          issue_k(u + kRing);
-          issue_v(u + kRing - 1);
-        }
-      } else {
-        issue_loads(u - 1 + kRing);
-      }
-      if constexpr (CS) {
+        // The probabilities go out first, then the next X phase's first
+        // fragment reads: LDS operations complete in order, so waiting until
+        // at most those four reads are outstanding publishes the write at
+        // the barrier while the reads stay in flight.
         if constexpr (decltype(mask_next)::value) {
 #pragma unroll
           for (int qt = 0; qt < QT; ++qt) mask_kt(s[qt][H], xmap(u + 1), qt, H);
@@ -1080,9 +1071,22 @@ void attn_fwd_kernel(AttnArgs a) {
         if constexpr (MAXP) max_own(s, mxp, hf);
         else probs_own(s, hf);
         fence();
-        if constexpr (RF == 1) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * LDPS) : "memory");
-        else asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+        for (int g = 0; g < 4; ++g) fr[g] = frag(g, slot_kn, slot_vn);
+        if constexpr (RF == 1) {
+          issue_k(u + kRing + 1);
+          issue_v(u + kRing);
+        } else {
+          issue_k(u + kRing);
+          issue_v(u + kRing - 1);
+        }
+        fence();
+        if constexpr (RF == 1) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(4)\n\ts_barrier" ::"n"(2 * LDPS) : "memory");
+        else asm volatile("s_waitcnt lgkmcnt(4)\n\ts_barrier" ::: "memory");
       } else {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) fr[g] = frag(g, slot_kn, slot_vn);
+        issue_loads(u - 1 + kRing);
         if constexpr (!ONLINE) {
           if constexpr (decltype(mask_next)::value) {
 #pragma unroll

@@ -49,6 +49,14 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
     if verbose and out.strip():
         print(out)
+    # The library must resolve every symbol: a kernel whose host-side launch
+    # stub the compiler dropped (device-only builtins in its body) links but
+    # fails to load.
+    chk = subprocess.run([sys.executable, "-c", f"import ctypes; ctypes.CDLL({tmp!r})"],
+                         capture_output=True, text=True)
+    if chk.returncode != 0:
+        os.remove(tmp)
+        raise RuntimeError(f"built library does not load:\n{chk.stderr.strip()[-2000:]}")
     os.replace(tmp, LIB)
     return LIB
 

@@ -105,6 +105,14 @@ __device__ __forceinline__ void load_lds16(const void* base, int bytes, int byte
       byte_off, 0, 0, 0);
 }
 
+// The same load with the buffer's sub-block in the scalar offset: base and
+// bytes fixed for a whole segment, so the resource is built once.
+__device__ __forceinline__ void load_lds16_soff(const void* base, int bytes, int byte_off, int soff, uint8_t* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufferRsrcWord3), (lds_void_t*)dst, 16,
+      byte_off, soff, 0, 0);
+}
+
 __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
   bf16x2_t v = {(__bf16)lo, (__bf16)hi};
   return __builtin_bit_cast(uint32_t, v);
@@ -596,19 +604,31 @@ void attn_fwd_kernel(AttnArgs a) {
       loff[i] = (d * kSub + ((p ^ ((d >> 2) & 3)) * 8)) * 2;
     }
   }
+  // Head dims 64 and 128 build one buffer resource per operand for the
+  // segment (the head's prepared K or V^T, Sk_pad keys; the host keeps that
+  // below 2 GB) and give a load's sub-tile as its scalar offset; a load past
+  // the segment's last sub-tile re-reads sub-tile 0 into a slot that is never
+  // read, so every access stays inside the head's rows. Head dim 256 builds a
+  // resource per sub-tile instead (an empty one past the end): its loop has
+  // no scalar registers to spare for two resources held across the segment,
+  // and the spills cost more than the per-load set-up.
+  const int kv_bytes = a.Sk_pad * D * 2;
   // Loads of sub-tile x into its slot: i in [i0, i1) of this wave's LDPS
   // loads (the first LDPS / 2 fill K, the others V^T, as j = wave + NW i).
   auto issue_part = [&](int x, int i0, int i1) __attribute__((always_inline)) {
     const int sl = (x - xb) & (kRing - 1);
     const bool live = x < xe;
     const int xs = live ? xmap(x) : 0;
-    const uint16_t* kx = kw + (int64_t)xs * (kSub * D);
-    const uint16_t* vx = vt + (int64_t)xs * (kSub * D);
 #pragma unroll
     for (int i = i0; i < i1; ++i) {
       const int j = wave + NW * i;
       uint8_t* dst = j < G::nK ? lds + sl * kKBytes + j * 1024 : lds + (kRing + sl) * kKBytes + (j - G::nK) * 1024;
-      load_lds16(j < G::nK ? kx : vx, live ? kKBytes : 0, loff[i], dst);
+      if constexpr (G::kCS) {
+        const uint16_t* src = (j < G::nK ? kw : vt) + (int64_t)xs * (kSub * D);
+        load_lds16(src, live ? kKBytes : 0, loff[i], dst);
+      } else {
+        load_lds16_soff(j < G::nK ? kw : vt, kv_bytes, loff[i], xs * kKBytes, dst);
+      }
     }
   };
   static_assert(G::nK == NW * LDPS / 2, "half of each wave's loads fill K");

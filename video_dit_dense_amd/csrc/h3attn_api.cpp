@@ -289,6 +289,8 @@ int check_forward(const h3attn_forward_args* a, size_t workspace_bytes, const vo
   if (!workspace_layout(B, Sq, Sk, Hq, Hkv, uniform_schedule(a), D, wl)) return H3ATTN_ERR_BAD_SHAPE;
   if ((int64_t)B * Hq * wl->Sq_pad >= (1ll << 31) || (int64_t)B * Hkv * wl->Sk_pad >= (1ll << 31))
     return H3ATTN_ERR_BAD_SHAPE;
+  // One head's prepared keys are addressed with 32-bit byte offsets.
+  if ((int64_t)wl->Sk_pad * D * 2 >= (1ll << 31)) return H3ATTN_ERR_BAD_SHAPE;
   if ((int64_t)B * Sq * Hq >= (1ll << 31) || (int64_t)B * Sk * Hkv >= (1ll << 31)) return H3ATTN_ERR_BAD_SHAPE;
   Range rq, rk, rv;
   if (!view_range(a->q, qs, B, Sq, Hq, D, &rq) || !view_range(a->k, ks, B, Sk, Hkv, D, &rk) ||

@@ -289,6 +289,10 @@ int h3attn_forward_stages(const uint16_t* q, const uint16_t* k, const uint16_t* 
  * h3attn_forward_ex_workspace_bytes() gives the workspace these arguments
  * need (0 if a size is invalid); stages are those of h3attn_forward_stages
  * (an ATTEND-only call must follow a PREPARE call with the same arguments).
+ * Size limits (BAD_SHAPE past them): B * Hq <= 65535; Sq, Sk <= 2^30;
+ * B * S * H < 2^31 for q and for k; and one head's prepared keys, Sk rounded
+ * up to a multiple of 256 times head_dim * 2 bytes, below 2^31 bytes (the
+ * attention kernel addresses them with 32-bit offsets).
  * Errors: NULL_POINTER, BAD_SHAPE, BAD_ALIGNMENT (pointers, strides),
  * ALIASING, BAD_VALUE (causal not 0/1, stages, scale, eps), WORKSPACE,
  * UNSUPPORTED_DEVICE, HIP.

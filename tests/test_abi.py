@@ -222,6 +222,13 @@ def test_forward_ex_workspace_bytes(lib):
     assert lib.h3attn_forward_ex_workspace_bytes(None) == 0
 
 
+def far_apart(Sk):
+    """Fields of an Sk-key call whose fake buffers are far enough apart not
+    to overlap (the rotary tables grow with the key count)."""
+    return dict(Sk=Sk, rope_rows=Sk, k=1 << 40, v=1 << 41, o=1 << 42, rope_cos=1 << 43, rope_sin=1 << 44,
+                ws=1 << 45, wsb=1 << 40)
+
+
 def test_forward_ex_validation(lib):
     assert lib.h3attn_forward_ex(None, P(16 * A), 1 << 20, 3, None) == NULLP
     assert fwd_ex(lib, v=None) == NULLP
@@ -253,11 +260,14 @@ def test_forward_ex_validation(lib):
     assert fwd_ex(lib, head_dim=256, q_norm_w=None, k_norm_w=None, wsb=1 << 30) == SHAPE   # rotary still given
     assert fwd_ex(lib, gate=9 * A + 1) == ALIGN
     assert fwd_ex(lib, gate=4 * A + 256) == ALIAS               # gate inside o
+    # one head's prepared keys reach 2 GB: past the 32-bit load offsets
+    assert fwd_ex(lib, **far_apart(1 << 23)) == SHAPE
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="device gate is checked on a machine without a GPU")
 def test_forward_ex_device_gate_without_gpu(lib):
     assert fwd_ex(lib) == DEVICE
+    assert fwd_ex(lib, **far_apart((1 << 23) - 512)) == DEVICE   # just under the per-head key limit
     assert fwd_ex(lib, causal=1) == DEVICE
     assert fwd_ex(lib, valid_lengths=9 * A, kv_valid=0) == DEVICE   # per-item lengths replace kv_valid
     assert fwd_ex(lib, q_stride=[8 * 12 * 128, 12 * 128, 128], k_stride=[8 * 12 * 128, 12 * 128, 128]) == DEVICE

@@ -162,22 +162,31 @@ def attention_bytes(wl) -> int:
 # Most key sub-tiles (32 keys each) whose K and V^T stay resident in LDS:
 # dense head-dim-128 attention over at most this many runs in one kernel
 # with no ring (the launcher's rule in attn_fwd.hip).
-RESIDENT_MAX_SUBTILES = 10
+def attend_schedule(wl, cus: int = 0) -> dict:
+    """The launcher's schedule of the attend stage for workload wl on a
+    device with `cus` compute units (0: this device), from the library."""
+    from video_dit_dense_amd import h3attn
+    return h3attn.schedule(wl.B, wl.Sq, wl.Sk, wl.H, wl.kv_heads, wl.head_dim,
+                           -1 if wl.lengths else wl.q_valid, -1 if wl.lengths else wl.kv_valid,
+                           causal=wl.causal, per_item_lengths=bool(wl.lengths), window=wl.window or None, cus=cus)
 
 
-def attend_kernels(wl) -> str:
-    """The kernels the attend stage launches for a workload, by the
-    launcher's dispatch: the general mode (causal mask, per-item lengths,
-    frame window) runs one tile per workgroup with no split; dense
-    head-dim-128 attention over at most RESIDENT_MAX_SUBTILES key sub-tiles
-    keeps its keys in LDS; every other dense launch may split the last
-    partial round of tiles and merge it."""
+def attend_kernels(wl, plan: dict) -> str:
+    """The kernels the attend stage launches for workload wl under `plan`
+    (attend_schedule): the general mode (causal mask, per-item lengths,
+    frame window) runs one tile per workgroup with no split; the resident-key
+    kernel serves short key ranges; every other launch runs whole rounds and
+    merges the split last round, if any."""
     D = wl.head_dim
-    if wl.causal or wl.lengths or wl.window:
-        return f"attn_fwd_kernel<{D}, {'true' if wl.window else 'false'}> (general mode)"
-    if D == 128 and (wl.kv_valid + 31) // 32 <= RESIDENT_MAX_SUBTILES:
+    if plan["kernel"] == "resident":
         return "attn_resident_kernel (keys resident in LDS)"
-    return f"attn_fwd_kernel<{D}, false> + attn_merge_kernel<{D}> (when the last round is split)"
+    qt = plan["query_tiles"]
+    name = f"attn_fwd_kernel<{D}, {qt}, {'true' if wl.window else 'false'}>"
+    if wl.causal or wl.lengths or wl.window:
+        return name + " (general mode)"
+    if plan["split_tiles"]:
+        return f"{name} + attn_merge_kernel<{D}, {qt}> ({plan['split_tiles']} tiles split)"
+    return name
 
 
 def window_keys_per_row(wl, rows):
@@ -709,6 +718,7 @@ def main() -> int:
     # The attend stage against both rooflines; the one whose time at peak is
     # longer bounds it.
     abytes = attention_bytes(wl)
+    plan = attend_schedule(wl)
     tflops = flops / (attn_avg * 1e-3) / 1e12
     gbs = abytes / (attn_avg * 1e-3) / 1e9
     mfma_roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -719,7 +729,8 @@ def main() -> int:
     main_roof, other_roof = (hbm_roof, mfma_roof) if hbm_bound else (mfma_roof, hbm_roof)
     roofline = {
         **{k: v for k, v in main_roof.items() if k != "work"},
-        "kernel": attend_kernels(wl) + ", attend stage",
+        "kernel": attend_kernels(wl, plan) + ", attend stage",
+        "schedule": plan,
         "traffic": measured_traffic(wl.name),
         "avg_ms": round(attn_avg, 4),
         "work_per_launch": main_roof["work"],

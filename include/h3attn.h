@@ -148,7 +148,7 @@ int h3attn_qkv_pack(const uint16_t* q, const uint16_t* k, const uint16_t* v,
  * normalised q and k and a key-major copy of v, each padded to whole tiles,
  * then room for the partial results of query tiles whose keys the forward
  * splits over several workgroups (it does so when the last round of tiles
- * would leave compute units idle; two fp32 records of 136 KB per split
+ * would leave compute units idle; two fp32 records of 204 KB per split
  * workgroup, at most 512 records), then one fp32 per (b, head, 4096 keys):
  * the largest key norm of each chunk, which bounds the scores when q and k
  * are not normalised. Returns 0 when a size is < 1 or the result would
@@ -278,13 +278,17 @@ int h3attn_forward_stages(const uint16_t* q, const uint16_t* k, const uint16_t* 
  *   BAD_SHAPE. Hq must be a multiple of Hkv. Norm, rotary and softmax_scale
  *   arguments are those of h3attn_forward; the rotary table rows serve
  *   sequence positions of q and k alike.
- * Work split: no causal mask, no valid_lengths and no window uses the
- *   schedule of h3attn_forward (whole rounds of query tiles, the last
- *   round's key steps split over all compute units; at head_dim 128 with
- *   at most 320 valid keys, the keys stay resident in LDS and each
- *   workgroup streams several query tiles past them); otherwise one
- *   workgroup per (b, h, query block of 256 rows, 128 at head_dim 256), the
- *   longest first under the causal mask and the frame window.
+ * Work split: the attention kernel's workgroup owns a query block of one
+ *   (b, h): 512 rows at head_dim 64, 256 or 384 at 128 (two or three 16-row
+ *   tiles per wave, chosen per launch from the schedule each gives; see
+ *   query_tiles), 128 at 256. No causal mask, no valid_lengths and no
+ *   window uses the schedule of h3attn_forward (whole rounds of query
+ *   blocks, the last round's key steps split over all compute units; at
+ *   head_dim 128 with at most 320 valid keys, the keys stay resident in LDS
+ *   and each workgroup streams several 256-row blocks past them); otherwise
+ *   one workgroup per (b, h, query block), the longest first under the
+ *   causal mask and the frame window. h3attn_forward_ex_plan() reports the
+ *   schedule a call takes.
  *
  * h3attn_forward_ex_workspace_bytes() gives the workspace these arguments
  * need (0 if a size is invalid); stages are those of h3attn_forward_stages
@@ -338,11 +342,43 @@ typedef struct h3attn_forward_args {
    * sigmoid(gate[b, i, h]) = 1 / (1 + exp(-gate)) before its bf16 rounding.
    * Rows at or past q_valid stay +0.0. */
   const uint16_t* gate;
+  /* Query tiles per wave of the attention kernel: 0 (a zeroed descriptor)
+   * lets the library choose; otherwise 2 or 3 at head_dim 128 and the one
+   * count of the other head dims (4 at 64, 2 at 256), else BAD_VALUE. An
+   * override for tuning and tests: every row's arithmetic is the same at
+   * either count, so tiles that run whole give bit-identical rows; the
+   * split last round divides its keys differently (same accuracy). Ignored
+   * when the keys are resident in LDS. The workspace does not depend on
+   * it. */
+  int32_t query_tiles;
 } h3attn_forward_args;
 
 size_t h3attn_forward_ex_workspace_bytes(const h3attn_forward_args* args);
 int h3attn_forward_ex(const h3attn_forward_args* args, void* workspace, size_t workspace_bytes,
                       uint32_t stages, void* stream);
+
+/*
+ * The schedule h3attn_forward_ex(args) launches on a device with `cus`
+ * compute units (cus <= 0: the current device's), written to *plan. Host
+ * arithmetic only: nothing is enqueued, and with cus > 0 no device is
+ * needed. Arguments are checked as for h3attn_forward_ex, except the
+ * workspace and the device (pointers are not dereferenced).
+ * Errors: NULL_POINTER (plan or args), the argument errors of
+ * h3attn_forward_ex, UNSUPPORTED_DEVICE or HIP when cus <= 0 and there is no
+ * usable device.
+ */
+typedef struct h3attn_plan {
+  int32_t kernel;         /* 0: the ring kernel; 1: keys resident in LDS */
+  int32_t query_tiles;    /* 16-row query tiles per wave */
+  int32_t rows_per_tile;  /* query rows per workgroup tile */
+  int32_t reserved;       /* 0 */
+  int64_t tiles;          /* tiles with valid rows (every tile in general mode) */
+  int64_t whole_tiles;    /* uniform schedule: tiles run whole */
+  int64_t split_tiles;    /* uniform schedule: last-round tiles split over split_blocks workgroups */
+  int64_t split_blocks;
+  int64_t grid;           /* workgroups of the attention kernel */
+} h3attn_plan;
+int h3attn_forward_ex_plan(const h3attn_forward_args* args, int32_t cus, h3attn_plan* plan);
 
 /*
  * Fused RMSNorm + indexed AdaLN scale/shift, the DiT block's norm before the

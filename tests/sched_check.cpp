@@ -170,8 +170,8 @@ struct Shape {
   int B, Sq, Sk, H, qv, kvv;
 };
 
-static int64_t check_split(const Shape& s, int D, int cus) {
-  const int BM = attn_rows(D);
+static int64_t check_split(const Shape& s, int D, int QT, int cus) {
+  const int BM = attn_rows(D, QT);
   const int64_t part_slots = split_part_slots(s.B, s.Sq, s.Sk, s.H, D);
   const int64_t nqv = (s.qv + BM - 1) / BM;
   const int64_t n_valid = (int64_t)s.B * s.H * nqv;
@@ -301,15 +301,29 @@ int main() {
   int n_split_cases = 0;
   for (size_t i = 0; i < shapes.size(); ++i) {
     int64_t max_rec = -1;
+    const int D = shapes[i].second;
+    const Shape& s = shapes[i].first;
     for (int cus : cus_list) {
-      const int64_t m = check_split(shapes[i].first, shapes[i].second, cus);
-      if (m >= 0) ++n_split_cases;
-      max_rec = std::max(max_rec, m);
+      for (int QT = attn_qt_min(D); QT <= attn_qt_max(D); ++QT) {
+        const int64_t m = check_split(s, D, QT, cus);
+        if (m >= 0) ++n_split_cases;
+        max_rec = std::max(max_rec, m);
+      }
+      // The launcher's choice is one of the head dim's tilings in both modes.
+      const int64_t NU = (s.kvv + kAttnSub - 1) / kAttnSub;
+      const int64_t slots = split_part_slots(s.B, s.Sq, s.Sk, s.H, D);
+      for (int general = 0; general < 2; ++general) {
+        const int qt = choose_query_tiles(D, general != 0, (int64_t)s.B * s.H, general ? s.Sq : s.qv, NU, cus, slots);
+        REQUIRE(qt >= attn_qt_min(D) && qt <= attn_qt_max(D), "D=%d: %d query tiles", D, qt);
+      }
     }
     if ((int)i < n_fixed) {
-      const Shape& s = shapes[i].first;
-      std::printf("WS %d %d %d %d %d %lld %lld\n", s.B, s.Sq, s.Sk, s.H, shapes[i].second,
-                  (long long)split_part_slots(s.B, s.Sq, s.Sk, s.H, shapes[i].second), (long long)max_rec);
+      std::printf("WS %d %d %d %d %d %lld %lld\n", s.B, s.Sq, s.Sk, s.H, D,
+                  (long long)split_part_slots(s.B, s.Sq, s.Sk, s.H, D), (long long)max_rec);
+      const int64_t NU = (s.kvv + kAttnSub - 1) / kAttnSub;
+      std::printf("QT %d %d %d %d %d %d %d %d\n", s.B, s.Sq, s.Sk, s.H, D, s.qv, s.kvv,
+                  choose_query_tiles(D, false, (int64_t)s.B * s.H, s.qv, NU, 256,
+                                     split_part_slots(s.B, s.Sq, s.Sk, s.H, D)));
     }
   }
   std::printf("OK %lld checks, %zu split shapes x %zu CU counts (%d split)\n", g_checks, shapes.size(),

@@ -51,21 +51,24 @@ def test_status_strings(lib):
 
 
 def test_workspace_bytes(lib):
-    # q, k, v each padded to 256 rows, bf16, 128 channels
-    # q, k and v^T rows padded to 256, 256 bytes each, then partial records
-    # for split tiles: 2 per split block, blocks = min(256, tiles*steps/16)
-    # with 256-row tiles and 32-key steps; a record is (64 + 4) x 512 floats
-    # (the accumulators, then two row offsets and two partial sums per lane:
-    # head dim 128 holds each wave's rows as two 16-row tiles).
-    # Then the key-norm maxima: one fp32 per 4096 padded keys of each
-    # (b, head), padded to 256 bytes.
-    rec = (64 + 4) * 512 * 4
+    # q rows padded to whole query blocks of every tiling a head-dim-128
+    # launch may take (256 and 384 rows: the larger of the two round-ups),
+    # k and v^T rows to 256; 256 bytes per row (bf16, 128 channels). Then
+    # partial records for split tiles: 2 per split block, blocks =
+    # min(256, tiles * steps / 16) counted with the smaller, 256-row tiles
+    # and 32-key steps; a record is (96 + 6) x 512 floats, the larger
+    # tiling's (each wave's 48 rows as three 16-row tiles: 48 x 128
+    # accumulators over 64 lanes, then three row offsets and three partial
+    # sums per lane). Then the key-norm maxima: one fp32 per 4096 padded keys
+    # of each (b, head), padded to 256 bytes.
+    rec = (96 + 6) * 512 * 4
     kn = lambda n: (n * 4 + 255) // 256 * 256   # noqa: E731
+    # 104448 rows are whole blocks of both 256 and 384
     assert lib.h3attn_forward_workspace_bytes(1, 104448, 104448, 6) == 6 * 104448 * 256 * 3 + 2 * 256 * rec + kn(6 * 26)
-    # 6 heads x 4 tiles x 10 steps = 240 steps -> 15 blocks
-    assert lib.h3attn_forward_workspace_bytes(2, 1000, 300, 3) == 6 * (1024 + 2 * 512) * 256 + 2 * 15 * rec + kn(6)
-    # 1 tile x 1 step: no split blocks
-    assert lib.h3attn_forward_workspace_bytes(1, 1, 1, 1) == 3 * 256 * 256 + kn(1)
+    # 1000 query rows: 1024 by 256, 1152 by 384; 6 heads x 4 tiles x 10 steps = 240 steps -> 15 blocks
+    assert lib.h3attn_forward_workspace_bytes(2, 1000, 300, 3) == 6 * (1152 + 2 * 512) * 256 + 2 * 15 * rec + kn(6)
+    # 1 tile x 1 step: no split blocks; one query row pads to 384
+    assert lib.h3attn_forward_workspace_bytes(1, 1, 1, 1) == (384 + 2 * 256) * 256 + kn(1)
     assert lib.h3attn_forward_workspace_bytes(0, 1, 1, 1) == 0
     assert lib.h3attn_forward_workspace_bytes(1, -5, 1, 1) == 0
 
@@ -193,17 +196,18 @@ def fwd_ex(lib, stages=3, ws=16 * A, wsb=None, **kw):
 def test_forward_ex_workspace_bytes(lib):
     # q rows for Hq heads, k and v^T rows for Hkv heads, partial records only
     # for the uniform schedule (no causal mask, no per-item lengths); at head
-    # dim 128 a record holds two row offsets and two partial sums per lane;
-    # then the key-norm maxima, one fp32 per 4096 padded keys of each
-    # (b, kv head), padded to 256 bytes
-    rec = (64 + 4) * 512 * 4
+    # dim 128 a record is sized for three query tiles per wave (96
+    # accumulators, three row offsets and three partial sums per lane); then
+    # the key-norm maxima, one fp32 per 4096 padded keys of each (b, kv
+    # head), padded to 256 bytes
+    rec = (96 + 6) * 512 * 4
     kn = lambda n: (n * 4 + 255) // 256 * 256   # noqa: E731
     assert h3attn.forward_ex_workspace_bytes(1, 104448, 104448, 6, 2) == \
         (6 + 2 * 2) * 104448 * 256 + 2 * 256 * rec + kn(2 * 26)
     assert h3attn.forward_ex_workspace_bytes(1, 104448, 104448, 6, 2, causal=True) == \
         (6 + 2 * 2) * 104448 * 256 + kn(2 * 26)
     assert h3attn.forward_ex_workspace_bytes(2, 1000, 300, 4, 1, per_item_lengths=True) == \
-        2 * (4 * 1024 + 2 * 1 * 512) * 256 + kn(2)
+        2 * (4 * 1152 + 2 * 1 * 512) * 256 + kn(2)
     assert h3attn.forward_ex_workspace_bytes(1, 104448, 104448, 6, 6, window=True) == \
         3 * 6 * 104448 * 256 + kn(6 * 26)
     # rows of 2 * head_dim bytes; split records per lane of 512: 64 accumulators (at head dim 64, 64
@@ -415,3 +419,40 @@ def test_pack_validation(lib):
         assert pack(lib) == DEVICE
         assert pack(lib, off=2, rows=10) == DEVICE
         assert pack(lib, wq=0, wk=0, rc=0, rs=0, rows=0, off=1000) == DEVICE   # no rotary: any offset
+
+
+def test_forward_ex_plan(lib):
+    """The schedule query: host arithmetic on a checked descriptor, no device
+    needed when the CU count is given."""
+    sch = h3attn.schedule
+    full = sch(1, 104448, 104448, 6, cus=256)
+    assert full == {"kernel": "ring", "query_tiles": 3, "rows_per_tile": 384, "tiles": 1632, "whole_tiles": 1536,
+                    "split_tiles": 96, "split_blocks": 256, "grid": 1792}
+    # the same launch forced to two tiles per wave: 408 blocks of 256 rows per head
+    two = sch(1, 104448, 104448, 6, query_tiles=2, cus=256)
+    assert (two["rows_per_tile"], two["tiles"], two["whole_tiles"], two["split_tiles"]) == (256, 2448, 2304, 144)
+    assert sch(1, 8192, 8192, 8, cus=256)["query_tiles"] == 2                 # one whole round of 256 tiles
+    padded = sch(1, 32768, 32768, 8, q_valid=30720, kv_valid=30720, cus=256)
+    assert (padded["query_tiles"], padded["tiles"], padded["grid"]) == (3, 640, 512 + 256 + 8 * 6)
+    assert sch(1, 32760, 512, 8, kv_valid=300, cus=256)["kernel"] == "resident"
+    causal = sch(1, 104448, 104448, 6, causal=True, cus=256)
+    assert (causal["query_tiles"], causal["tiles"], causal["split_tiles"]) == (3, 1632, 0)
+    assert sch(1, 104448, 104448, 12, head_dim=64, cus=256)["rows_per_tile"] == 512
+    assert sch(1, 104448, 104448, 3, head_dim=256, cus=256)["rows_per_tile"] == 128
+    # errors: no plan, a query-tile count the head dim does not have, bad sizes
+    a = h3attn.ForwardArgs()
+    a.q, a.k, a.v, a.o = A, 2 * A, 3 * A, 4 * A
+    a.B, a.Sq, a.Sk, a.Hq, a.Hkv, a.head_dim = 1, 8, 8, 2, 2, 128
+    a.q_valid, a.kv_valid, a.softmax_scale = -1, -1, 0.0883
+    p = h3attn.Plan()
+    assert lib.h3attn_forward_ex_plan(ctypes.byref(a), 256, None) == NULLP
+    assert lib.h3attn_forward_ex_plan(None, 256, ctypes.byref(p)) == NULLP
+    assert lib.h3attn_forward_ex_plan(ctypes.byref(a), 256, ctypes.byref(p)) == 0
+    for qt, want in ((1, VALUE), (4, VALUE), (2, 0), (3, 0)):
+        a.query_tiles = qt
+        assert lib.h3attn_forward_ex_plan(ctypes.byref(a), 256, ctypes.byref(p)) == want, qt
+    a.head_dim, a.query_tiles = 64, 3
+    assert lib.h3attn_forward_ex_plan(ctypes.byref(a), 256, ctypes.byref(p)) == VALUE
+    a.head_dim, a.query_tiles = 96, 0
+    assert lib.h3attn_forward_ex_plan(ctypes.byref(a), 256, ctypes.byref(p)) == SHAPE
+    assert fwd_ex(lib, query_tiles=5) == VALUE

@@ -70,18 +70,22 @@ def test_timing_stats():
 
 
 def test_attend_kernel_names_follow_the_launcher():
-    """The bench names the kernels the launcher dispatches; its resident-key
-    limit is the kernel source's."""
-    import re
-    src = open(os.path.join(ROOT, "video_dit_dense_amd", "csrc", "attn_fwd.hip")).read()
-    assert int(re.search(r"constexpr int kResMaxSub = (\d+);", src).group(1)) == bench.RESIDENT_MAX_SUBTILES
+    """The bench names the kernels from the library's own schedule of each
+    workload (256 compute units)."""
     W = {**workloads.WORKLOADS, **workloads.VARIANT_WORKLOADS}
-    assert bench.attend_kernels(W["cross"]).startswith("attn_resident_kernel")
-    assert bench.attend_kernels(W["full"]).startswith("attn_fwd_kernel<128, false> + attn_merge_kernel")
-    assert bench.attend_kernels(W["full_causal"]) == "attn_fwd_kernel<128, false> (general mode)"
-    assert bench.attend_kernels(W["full_window"]) == "attn_fwd_kernel<128, true> (general mode)"
-    assert bench.attend_kernels(W["full_d64"]).startswith("attn_fwd_kernel<64, false>")
+
+    def name(wl):
+        return bench.attend_kernels(wl, bench.attend_schedule(wl, cus=256))
+
+    assert name(W["cross"]).startswith("attn_resident_kernel")
+    assert name(W["full"]) == "attn_fwd_kernel<128, 3, false> + attn_merge_kernel<128, 3> (96 tiles split)"
+    assert name(W["mid"]) == "attn_fwd_kernel<128, 2, false>"
+    assert name(W["tiny"]) == "attn_fwd_kernel<128, 2, false>"
+    assert name(W["full_causal"]) == "attn_fwd_kernel<128, 3, false> (general mode)"
+    assert name(W["full_window"]) == "attn_fwd_kernel<128, 3, true> (general mode)"
+    assert name(W["full_d64"]).startswith("attn_fwd_kernel<64, 4, false>")
+    assert name(W["full_d256"]).startswith("attn_fwd_kernel<256, 2, false>")
     wl = workloads.Workload("w", 1, 4096, 321, 2, 4096, 321, True, False, 0)
-    assert bench.attend_kernels(wl).startswith("attn_fwd_kernel<128")      # 11 sub-tiles: the ring kernel
+    assert name(wl).startswith("attn_fwd_kernel<128")      # 11 sub-tiles: the ring kernel
     wl = workloads.Workload("w", 1, 4096, 320, 2, 4096, 320, True, False, 0)
-    assert bench.attend_kernels(wl).startswith("attn_resident_kernel")
+    assert name(wl).startswith("attn_resident_kernel")

@@ -181,22 +181,24 @@ constexpr float kBoundMax = 60.0f;
 constexpr float kBoundSlack = 1.0f + 1.0f / 1024.0f;
 constexpr int kSub = 32;                       // keys per sub-tile
 
-// Tiling by head dim D (64, 128 or 256): eight waves per workgroup, two per
-// SIMD, 16x16x32 matrix-core instructions on QT 16-row query tiles per wave
-// (four at 64, so 512 rows per workgroup; two at 128, 256 rows). At 256 the
+// Tiling by head dim D (64, 128 or 256) and query tiles per wave QT_: eight
+// waves per workgroup, two per SIMD, 16x16x32 matrix-core instructions on QT
+// 16-row query tiles per wave (four at 64, so 512 rows per workgroup; two or
+// three at 128, 256 or 384 rows; two at 256). At 256 the
 // waves work in pairs (kCS): both waves of a pair hold the same 32 query
 // rows; each computes the scores of half of every sub-tile's keys and the
 // output of half of the channels, so that its accumulators and fragment
 // reads are those of head dim 128, and the pair exchanges probabilities
 // through LDS (128 rows per workgroup).
-template <int D>
+template <int D, int QT_>
 struct Geo {
   static_assert(D == 64 || D == 128 || D == 256, "head dim");
+  static_assert(QT_ >= attn_qt_min(D) && QT_ <= attn_qt_max(D), "query tiles per wave");
   static constexpr int NW = 8;                          // waves per workgroup
   static constexpr int WPE = 2;                         // waves per SIMD
   static constexpr bool kCS = D == 256;                 // channel-split wave pairs
   static constexpr int DW = kCS ? D / 2 : D;            // channels per wave
-  static constexpr int QT = attn_query_tiles(D);        // 16-row query tiles per wave
+  static constexpr int QT = QT_;                        // 16-row query tiles per wave
   static constexpr int WROWS = 16 * QT;                 // query rows per wave (per pair when kCS)
   static constexpr int BM = (kCS ? NW / 2 : NW) * WROWS;   // query rows per workgroup
   static constexpr int kRing = D <= 128 ? 8 : 4;        // ring depth (sub-tiles)
@@ -219,11 +221,13 @@ struct Geo {
   static constexpr int kRecA = WROWS * DW / 64;
   static_assert(LDPS * NW * 1024 == kKBytes + kVBytes, "tile split");
   static_assert(kLdsBytes <= 160 * 1024, "LDS");
-  static_assert(BM == attn_rows(D) && NW * 64 == attn_threads(D), "tiling constants");
+  static_assert(BM == attn_rows(D, QT) && NW * 64 == attn_threads(D), "tiling constants");
   static_assert(kRing * kKBytes <= 65536, "K sub-tiles within the first 64 KB");
   // Floats each thread writes to a partial record fill exactly the record
   // size the host reserves per record.
-  static_assert((kRecA + 2 * QT) * NW * 64 == attn_part_floats(D), "partial record size");
+  static constexpr int kRecFloats = attn_part_floats(D, QT);
+  static_assert((kRecA + 2 * QT) * NW * 64 == kRecFloats && kRecFloats <= attn_part_floats_max(D),
+                "partial record size");
 };
 
 // LDS layouts (no padding; XOR swizzles keep every 8-lane group of a
@@ -274,14 +278,15 @@ __device__ __forceinline__ void for_each_index(std::integer_sequence<int, K...>,
 // keeps the compiler from moving memory operations across it.
 __device__ __forceinline__ void bar() { asm volatile("s_barrier" ::: "memory"); }
 
-// D: the head dim. WIN: the frame-window variant (general mode with
-// a.win_F > 0); the other modes are compiled without its per-lane window
-// bounds and first-key bookkeeping, which would cost registers in the
-// steady state.
-template <int D, bool WIN>
-__global__ __launch_bounds__(Geo<D>::NW * 64) __attribute__((amdgpu_waves_per_eu(Geo<D>::WPE, Geo<D>::WPE)))
+// D: the head dim. QT_: query tiles per wave. WIN: the frame-window variant
+// (general mode with a.win_F > 0); the other modes are compiled without its
+// per-lane window bounds and first-key bookkeeping, which would cost
+// registers in the steady state.
+template <int D, int QT_, bool WIN>
+__global__ __launch_bounds__((Geo<D, QT_>::NW * 64))
+__attribute__((amdgpu_waves_per_eu(Geo<D, QT_>::WPE, Geo<D, QT_>::WPE)))
 void attn_fwd_kernel(AttnArgs a) {
-  using G = Geo<D>;
+  using G = Geo<D, QT_>;
   constexpr int NW = G::NW;
   constexpr int BM = G::BM;
   constexpr int T = NW * 64;
@@ -1211,7 +1216,7 @@ void attn_fwd_kernel(AttnArgs a) {
                            gate_row);
     }
   } else {
-    float* pr = a.part + (int64_t)rec * attn_part_floats(D) + lwave * 64 + lane;
+    float* pr = a.part + (int64_t)rec * G::kRecFloats + lwave * 64 + lane;
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
 #pragma unroll
@@ -1242,12 +1247,13 @@ void attn_fwd_kernel(AttnArgs a) {
 // the ring slots' (K rows and V^T rows swizzled as there), filled by plain
 // loads and stores.
 constexpr int kResMaxSub = 10;
+constexpr int kResRows = 256;   // query rows per tile: eight waves of two 16-row tiles
 
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_resident_kernel(AttnArgs a, int32_t G) {
   constexpr int D = 128;
-  using Gm = Geo<D>;
-  constexpr int BM = Gm::BM, T = Gm::NW * 64, NC = D / 32, NT16 = D / 16;
+  using Gm = Geo<D, 2>;
+  constexpr int BM = kResRows, T = Gm::NW * 64, NC = D / 32, NT16 = D / 16;
   constexpr int kKB = Gm::kKBytes;                 // one K or V^T sub-tile (8 KB)
   constexpr int kVBase = kResMaxSub * kKB;         // V^T region
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kResMaxSub * kKB];
@@ -1491,9 +1497,9 @@ void attn_resident_kernel(AttnArgs a, int32_t G) {
 // meet the tile each left one partial record (O_i, m_i, l_i) with O_i and l_i
 // relative to their own offset m_i; with M = max m_i the tile's result is
 // sum 2^(m_i - M) O_i / sum 2^(m_i - M) l_i (scores are in exp2 units).
-template <int D>
-__global__ __launch_bounds__(Geo<D>::NW * 64) void attn_merge_kernel(AttnArgs a) {
-  using G = Geo<D>;
+template <int D, int QT_>
+__global__ __launch_bounds__((Geo<D, QT_>::NW * 64)) void attn_merge_kernel(AttnArgs a) {
+  using G = Geo<D, QT_>;
   constexpr int BM = G::BM;
   constexpr int T = G::NW * 64;
   constexpr int QT = G::QT;
@@ -1515,7 +1521,7 @@ __global__ __launch_bounds__(Geo<D>::NW * 64) void attn_merge_kernel(AttnArgs a)
   int j0, j1;
   merge_blocks(t, a.n_split, NU, a.n_split_blocks, j0, j1);
   auto record = [&](int j) {
-    return a.part + (int64_t)merge_record(j, t, a.n_split, NU, a.n_split_blocks) * attn_part_floats(D) + tid;
+    return a.part + (int64_t)merge_record(j, t, a.n_split, NU, a.n_split_blocks) * G::kRecFloats + tid;
   };
   const uint16_t* gate_row = a.gate ? a.gate + (int64_t)b * a.Sq * a.H + h : nullptr;
   // Records in the 16x16 layout: QT query tiles x NT16 tiles x 4 registers,
@@ -1671,73 +1677,108 @@ bool win_longest_first(const AttnArgs& a, int BM, int64_t nq, int cus) {
   return last;
 }
 
-template <int D>
-hipError_t launch_attention_d(AttnArgs a, hipStream_t stream) {
-  constexpr int NW = Geo<D>::NW;
-  constexpr int BM = Geo<D>::BM;
-  static_assert(BM == attn_rows(D) && NW * 64 == attn_threads(D) && kAttnSub == kSub, "tiling constants");
-  const int64_t nq = (a.Sq + BM - 1) / BM;
-  a.general = (a.causal || a.lengths != nullptr || a.win_F > 0) ? 1 : 0;
+// The launch at QT query tiles per wave, on the schedule plan_attention
+// made: general mode, or the uniform schedule of whole rounds and a split
+// last round.
+template <int D, int QT>
+hipError_t launch_attention_q(AttnArgs a, const AttnPlan& p, hipStream_t stream) {
+  using G = Geo<D, QT>;
+  constexpr int NW = G::NW;
+  static_assert(kAttnSub == kSub, "tiling constants");
+  if (p.rows != G::BM || p.grid > 0x7fffffffLL || p.nqv > 0x7fffffffLL) return hipErrorInvalidValue;
+  a.nqv = (int32_t)p.nqv;
+  a.n_whole = (int32_t)p.n_whole;
+  a.n_split = (int32_t)p.n_split;
+  a.n_split_blocks = (int32_t)p.n_blocks;
   if (a.general) {
-    // One block per (b, h, query block); each finds its own valid rows and
-    // key range, so nothing is split.
-    const int64_t grid = (int64_t)a.B * a.H * nq;
-    if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-    a.nqv = (int32_t)nq;
-    a.n_whole = a.n_split = a.n_split_blocks = 0;
-    a.win_longest_first = a.win_F > 0 && win_longest_first(a, BM, nq, device_cus()) ? 1 : 0;
-    if (grid > 0) {
+    a.win_longest_first = a.win_F > 0 && win_longest_first(a, G::BM, p.nqv, device_cus()) ? 1 : 0;
+    if (p.grid > 0) {
       if (a.win_F > 0)
-        attn_fwd_kernel<D, true><<<dim3((unsigned)grid), NW * 64, 0, stream>>>(a);
+        attn_fwd_kernel<D, QT, true><<<dim3((unsigned)p.grid), NW * 64, 0, stream>>>(a);
       else
-        attn_fwd_kernel<D, false><<<dim3((unsigned)grid), NW * 64, 0, stream>>>(a);
+        attn_fwd_kernel<D, QT, false><<<dim3((unsigned)p.grid), NW * 64, 0, stream>>>(a);
     }
     return hipGetLastError();
   }
-  const int64_t nqv = (a.q_valid + BM - 1) / BM;
-  const int64_t n_valid = (int64_t)a.B * a.H * nqv;
-  const int64_t n_zero = (int64_t)a.B * a.H * (nq - nqv);
-  const int64_t NU = (a.kv_valid + kSub - 1) / kSub;
+  if (p.grid > 0) attn_fwd_kernel<D, QT, false><<<dim3((unsigned)p.grid), NW * 64, 0, stream>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.n_split == 0) return e;
+  attn_merge_kernel<D, QT><<<dim3((unsigned)p.n_split), NW * 64, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_attention_d(const AttnArgs& a, const AttnPlan& p, hipStream_t stream) {
   if constexpr (D == 128) {
-    if (NU <= kResMaxSub) {
-      // Keys resident in LDS: one workgroup per (b, h) and residue class of
-      // its query tiles, G classes per head so that the grid covers the CUs.
-      const int64_t cus = std::max(device_cus(), 1);
-      const int64_t bh = (int64_t)a.B * a.H;
-      const int64_t G = std::max<int64_t>(1, std::min<int64_t>(nq, (cus + bh - 1) / bh));
-      if (bh * G > 0x7fffffffLL) return hipErrorInvalidValue;
-      a.nqv = (int32_t)nqv;
-      a.n_whole = a.n_split = a.n_split_blocks = 0;
-      attn_resident_kernel<<<dim3((unsigned)(bh * G)), NW * 64, 0, stream>>>(a, (int32_t)G);
+    if (p.resident) {
+      if (p.grid > 0x7fffffffLL) return hipErrorInvalidValue;
+      attn_resident_kernel<<<dim3((unsigned)p.grid), Geo<D, 2>::NW * 64, 0, stream>>>(a, (int32_t)(p.grid / ((int64_t)a.B * a.H)));
       return hipGetLastError();
     }
   }
-  // One tile per CU at a time: the last round holds n_valid % cus tiles. When
-  // that round is partial, split its tiles' steps over more blocks (at most
-  // one per CU, each at least kSplitMinSteps steps, and more blocks than
-  // tiles so no block spans more than two tiles).
-  const SplitPlan sp = split_plan(n_valid, NU, device_cus(), a.part_slots);
-  const int64_t n_whole = sp.n_whole, n_split = sp.n_split, n_blocks = sp.n_blocks;
-  const int64_t grid = n_whole + n_blocks + n_zero;
-  if (grid > 0x7fffffffLL || nqv > 0x7fffffffLL) return hipErrorInvalidValue;
-  a.nqv = (int32_t)nqv;
-  a.n_whole = (int32_t)n_whole;
-  a.n_split = (int32_t)n_split;
-  a.n_split_blocks = (int32_t)n_blocks;
-  if (grid > 0) attn_fwd_kernel<D, false><<<dim3((unsigned)grid), NW * 64, 0, stream>>>(a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || n_split == 0) return e;
-  attn_merge_kernel<D><<<dim3((unsigned)n_split), NW * 64, 0, stream>>>(a);
-  return hipGetLastError();
+  constexpr int lo = attn_qt_min(D), hi = attn_qt_max(D);
+  if (p.query_tiles == hi) return launch_attention_q<D, hi>(a, p, stream);
+  if constexpr (lo != hi) {
+    if (p.query_tiles == lo) return launch_attention_q<D, lo>(a, p, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
+AttnPlan plan_attention(const AttnArgs& a, int cus) {
+  AttnPlan p{};
+  const bool general = a.causal || a.lengths != nullptr || a.win_F > 0;
+  const int64_t NU = (a.kv_valid + kSub - 1) / kSub;
+  const int64_t bh = (int64_t)a.B * a.H;
+  if (a.D == 128 && !general && NU <= kResMaxSub) {
+    // Keys resident in LDS: one workgroup per (b, h) and residue class of its
+    // query tiles, G classes per head so that the grid covers the CUs.
+    const int64_t nq = (a.Sq + kResRows - 1) / kResRows;
+    const int64_t G = std::max<int64_t>(1, std::min<int64_t>(nq, (std::max(cus, 1) + bh - 1) / bh));
+    p.resident = 1;
+    p.query_tiles = 2;
+    p.rows = kResRows;
+    p.nqv = (a.q_valid + kResRows - 1) / kResRows;
+    p.tiles = bh * p.nqv;
+    p.grid = bh * G;
+    return p;
+  }
+  p.query_tiles = a.query_tiles != 0 ? a.query_tiles
+                                     : choose_query_tiles(a.D, general, bh, general ? a.Sq : a.q_valid, NU, cus,
+                                                          a.part_slots);
+  p.rows = attn_rows(a.D, p.query_tiles);
+  const int64_t nq = (a.Sq + p.rows - 1) / p.rows;
+  if (general) {
+    // One block per (b, h, query block); each finds its own valid rows and
+    // key range, so nothing is split.
+    p.nqv = nq;
+    p.tiles = bh * nq;
+    p.grid = p.tiles;
+    return p;
+  }
+  // One tile per CU at a time: the last round holds n_valid % cus tiles. When
+  // that round is partial, split its tiles' steps over more blocks (at most
+  // one per CU, each at least kSplitMinSteps steps, and more blocks than
+  // tiles so no block spans more than two tiles). Tiles wholly past q_valid
+  // only write zeros.
+  p.nqv = (a.q_valid + p.rows - 1) / p.rows;
+  p.tiles = bh * p.nqv;
+  const SplitPlan sp = split_plan(p.tiles, NU, cus, a.part_slots);
+  p.n_whole = sp.n_whole;
+  p.n_split = sp.n_split;
+  p.n_blocks = sp.n_blocks;
+  p.grid = sp.n_whole + sp.n_blocks + bh * (nq - p.nqv);
+  return p;
+}
+
 hipError_t launch_attention(AttnArgs a, hipStream_t stream) {
+  a.general = (a.causal || a.lengths != nullptr || a.win_F > 0) ? 1 : 0;
+  const AttnPlan p = plan_attention(a, device_cus());
   switch (a.D) {
-    case 64: return launch_attention_d<64>(a, stream);
-    case 128: return launch_attention_d<128>(a, stream);
-    case 256: return launch_attention_d<256>(a, stream);
+    case 64: return launch_attention_d<64>(a, p, stream);
+    case 128: return launch_attention_d<128>(a, p, stream);
+    case 256: return launch_attention_d<256>(a, p, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -10,14 +10,16 @@
 namespace h3 {
 
 // Attention tiling by head dim D (64, 128 or 256): a workgroup of eight
-// waves owns attn_rows(D) query rows of one (b, h) and walks the keys in
-// kAttnSub-key sub-tiles. Each wave holds attn_query_tiles(D) 16-row query
-// tiles (64 rows at head dim 64, 32 at 128); at 256 the waves work in pairs
-// that share 32 rows, each wave holding half of the channels.
+// waves owns attn_rows(D, QT) query rows of one (b, h) and walks the keys in
+// kAttnSub-key sub-tiles. Each wave holds QT 16-row query tiles: four at head
+// dim 64 (64 rows), two or three at 128 (32 or 48 rows, chosen per launch by
+// choose_query_tiles), two at 256, where the waves work in pairs that share
+// 32 rows, each wave holding half of the channels.
 constexpr int kAttnSub = 32;
 constexpr int attn_threads(int) { return 512; }
-constexpr int attn_query_tiles(int D) { return D == 64 ? 4 : 2; }
-constexpr int attn_rows(int D) { return attn_threads(D) / 64 * 16 * attn_query_tiles(D) / (D == 256 ? 2 : 1); }
+constexpr int attn_qt_min(int D) { return D == 64 ? 4 : 2; }
+constexpr int attn_qt_max(int D) { return D == 64 ? 4 : D == 128 ? 3 : 2; }
+constexpr int attn_rows(int D, int QT) { return attn_threads(D) / 64 * 16 * QT / (D == 256 ? 2 : 1); }
 
 // Load balancing of the last, partial round of query tiles (stream-K): those
 // tiles' sub-tile steps are split evenly over up to kSplitMaxBlocks
@@ -29,15 +31,19 @@ constexpr int kSplitMaxBlocks = 256;
 constexpr int kSplitMinSteps = 16;
 // Floats per partial record: the accumulator registers of every thread (its
 // share of rows x D), then each thread's row offsets and partial sums, one
-// of each per query tile.
-constexpr int attn_part_floats(int D) {
-  return (attn_rows(D) * D / attn_threads(D) + 2 * attn_query_tiles(D)) * attn_threads(D);
+// of each per query tile. The workspace sizes every record for the largest
+// query-tile count of the head dim.
+constexpr int attn_part_floats(int D, int QT) {
+  return (attn_rows(D, QT) * D / attn_threads(D) + 2 * QT) * attn_threads(D);
 }
+constexpr int attn_part_floats_max(int D) { return attn_part_floats(D, attn_qt_max(D)); }
 
 // Partial records the forward workspace reserves for these sizes: two per
-// split workgroup, for the largest split the launcher can choose.
+// split workgroup, for the largest split the launcher can choose (the most
+// tiles: the fewest query tiles per wave).
 inline int64_t split_part_slots(int32_t B, int32_t Sq, int32_t Sk, int32_t H, int32_t D) {
-  const int64_t tiles = (int64_t)B * H * ((Sq + attn_rows(D) - 1) / attn_rows(D));
+  const int rows = attn_rows(D, attn_qt_min(D));
+  const int64_t tiles = (int64_t)B * H * ((Sq + rows - 1) / rows);
   const int64_t steps = tiles * ((Sk + kAttnSub - 1) / kAttnSub);
   const int64_t blocks = steps / kSplitMinSteps < kSplitMaxBlocks ? steps / kSplitMinSteps : kSplitMaxBlocks;
   return 2 * blocks;
@@ -119,6 +125,52 @@ inline SplitPlan split_plan(int64_t n_valid, int64_t NU, int64_t cus, int64_t pa
     p.n_blocks = blocks;
   }
   return p;
+}
+
+// Query tiles per wave for one launch (head dim 128 has two choices; the
+// others one). Three tiles feed each fragment read and each direct load to a
+// third more matrix-core instructions, about 5% faster per unit of work, but
+// their 384-row tiles fill the rounds of the chip differently. Uniform mode
+// compares the two schedules' busy time per CU (split_plan: whole rounds of
+// NU steps, then the split round's steps per block, plus a fixed cost of
+// kSplitOverheadSteps for its records and merge), each step weighted by its
+// rows and that efficiency. General mode (tiles of unequal length, no split)
+// takes three tiles when they make at least two rounds. cus <= 0 (unknown)
+// takes the largest count.
+constexpr int kSplitOverheadSteps = 64;
+inline int choose_query_tiles(int D, bool general, int64_t BH, int64_t q_valid, int64_t NU, int64_t cus,
+                              int64_t part_slots) {
+  const int lo = attn_qt_min(D), hi = attn_qt_max(D);
+  if (lo == hi || cus <= 0) return hi;
+  const int64_t c = cus < kSplitMaxBlocks ? cus : kSplitMaxBlocks;
+  if (general) {
+    const int64_t rows = attn_rows(D, hi);
+    return BH * ((q_valid + rows - 1) / rows) >= 2 * c ? hi : lo;
+  }
+  // Busy time num / den in units of (one step of a 16-row query tile) / 20:
+  // a step of QT tiles costs 20 QT at three tiles and 21 QT at two. The
+  // busiest CU's steps are scaled by n_blocks so the split round's share is
+  // whole.
+  struct Cost {
+    int64_t num, den;
+  };
+  auto cost = [&](int QT) {
+    const int64_t rows = attn_rows(D, QT);
+    const int64_t n = BH * ((q_valid + rows - 1) / rows);
+    const SplitPlan p = split_plan(n, NU, cus, part_slots);
+    Cost r;
+    if (p.n_blocks > 0) {
+      r.num = (p.n_whole / c * NU + kSplitOverheadSteps) * p.n_blocks + p.n_split * NU;
+      r.den = p.n_blocks;
+    } else {
+      r.num = (n + c - 1) / c * NU;
+      r.den = 1;
+    }
+    r.num *= (int64_t)QT * (QT == 3 ? 20 : 21);
+    return r;
+  };
+  const Cost a = cost(lo), b = cost(hi);
+  return (__int128)b.num * a.den <= (__int128)a.num * b.den ? hi : lo;
 }
 
 // The work of split workgroup j (0 <= j < n_blocks): of the U = n_split * NU

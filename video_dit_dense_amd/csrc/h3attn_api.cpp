@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
@@ -90,14 +91,17 @@ bool workspace_layout(int32_t B, int32_t Sq, int32_t Sk, int32_t Hq, int32_t Hkv
                       WorkspaceLayout* w) {
   if (B < 1 || Sq < 1 || Sk < 1 || Hq < 1 || Hkv < 1) return false;
   if (D != 64 && D != 128 && D != 256) return false;
-  // Query rows pad to whole query blocks (512 rows at head dim 64).
-  w->Sq_pad = round_up(Sq, h3::attn_rows(D) > h3::kRowPad ? h3::attn_rows(D) : h3::kRowPad);
+  // Query rows pad to whole query blocks of every tiling a launch may take:
+  // the ring kernel's (512 rows at head dim 64, 256 or 384 at 128, 128 at
+  // 256) and the resident-key kernel's (256).
+  w->Sq_pad = std::max({round_up(Sq, h3::attn_rows(D, h3::attn_qt_min(D))),
+                        round_up(Sq, h3::attn_rows(D, h3::attn_qt_max(D))), round_up(Sq, h3::kRowPad)});
   w->Sk_pad = round_up(Sk, h3::kRowPad);
   const unsigned row = 2u * (unsigned)D;
   const unsigned __int128 qb = (unsigned __int128)B * (unsigned __int128)Hq * (unsigned __int128)w->Sq_pad * row;
   const unsigned __int128 kb = (unsigned __int128)B * (unsigned __int128)Hkv * (unsigned __int128)w->Sk_pad * row;
   w->part_slots = uniform ? h3::split_part_slots(B, Sq, Sk, Hq, D) : 0;
-  const unsigned __int128 pb = (unsigned __int128)w->part_slots * (sizeof(float) * h3::attn_part_floats(D));
+  const unsigned __int128 pb = (unsigned __int128)w->part_slots * (sizeof(float) * h3::attn_part_floats_max(D));
   // Key-norm maxima (fp32 per chunk of keys of each (b, kv head)), padded to 256 bytes.
   w->kn_chunks = h3::key_norm_chunks(w->Sk_pad);
   const unsigned __int128 nb = ((unsigned __int128)B * Hkv * w->kn_chunks * sizeof(float) + 255) / 256 * 256;
@@ -274,6 +278,8 @@ int check_forward(const h3attn_forward_args* a, size_t workspace_bytes, const vo
     if (qv < 0 || qv > Sq || kvv < 1 || kvv > Sk) return H3ATTN_ERR_BAD_SHAPE;
   }
   if (!std::isfinite(a->softmax_scale) || !(a->softmax_scale > 0.f)) return H3ATTN_ERR_BAD_VALUE;
+  if (a->query_tiles != 0 && (a->query_tiles < h3::attn_qt_min(a->head_dim) || a->query_tiles > h3::attn_qt_max(a->head_dim)))
+    return H3ATTN_ERR_BAD_VALUE;
   if (int st = check_prologue_args(Sq, Sk, a->q_norm_w, a->k_norm_w, a->eps, a->rope_cos, a->rope_sin, a->rope_rows))
     return st;
   for (int i = 0; i < 3; ++i)
@@ -324,6 +330,47 @@ int check_forward(const h3attn_forward_args* a, size_t workspace_bytes, const vo
   return with_workspace ? check_device() : H3ATTN_OK;
 }
 
+// The attention kernel's arguments for a checked forward, less the
+// workspace pointers and the key-norm maxima.
+h3::AttnArgs attn_args(const h3attn_forward_args* a, const WorkspaceLayout& wl) {
+  const int32_t Sq = a->Sq, Sk = a->Sk;
+  h3::AttnArgs at{};
+  at.D = a->head_dim;
+  at.o = a->o;
+  at.part_slots = wl.part_slots;
+  at.B = a->B;
+  at.H = a->Hq;
+  at.Sq = Sq;
+  at.Sk = Sk;
+  at.Sq_pad = (int32_t)wl.Sq_pad;
+  at.Sk_pad = (int32_t)wl.Sk_pad;
+  at.q_valid = a->valid_lengths ? Sq : (a->q_valid == -1 ? Sq : a->q_valid);
+  at.kv_valid = a->valid_lengths ? Sk : (a->kv_valid == -1 ? Sk : a->kv_valid);
+  at.Hkv = a->Hkv;
+  at.causal = a->causal;
+  at.lengths = a->valid_lengths;
+  if (a->window_frame_rows > 0) {
+    // Clamp the geometry to the sequence without changing which keys a row
+    // sees: a frame longer than the sequence is one frame, and counts of
+    // anchor frames, chunk frames or radius chunks beyond the sequence's
+    // frames cover everything. With S < 2^28 the kernel's products
+    // (A + C*(c + R + 1)) * F then stay below 2^31.
+    const int32_t S = std::max(Sq, Sk);
+    const int32_t F = std::min(a->window_frame_rows, S);
+    const int32_t n_frames = (S + F - 1) / F;
+    at.win_F = F;
+    at.win_C = std::min(a->window_chunk_frames, n_frames);
+    at.win_R = std::min(a->window_radius, n_frames);
+    at.win_A = std::min(a->window_anchor_frames, n_frames);
+  }
+  at.gate = a->gate;
+  at.wq = a->q_norm_w;
+  at.wk = a->k_norm_w;
+  at.kn_chunks = (int32_t)wl.kn_chunks;
+  at.query_tiles = a->query_tiles;
+  return at;
+}
+
 int run_forward(const h3attn_forward_args* a, void* workspace, size_t workspace_bytes, uint32_t stages,
                 void* stream) {
   int64_t qs[3], ks[3], vs[3];
@@ -370,45 +417,13 @@ int run_forward(const h3attn_forward_args* a, void* workspace, size_t workspace_
   }
   if (!(stages & H3ATTN_STAGE_ATTEND)) return H3ATTN_OK;
 
-  h3::AttnArgs at{};
-  at.D = D;
+  h3::AttnArgs at = attn_args(a, wl);
   at.qw = qw;
   at.kw = kw;
   at.vt = vt;
-  at.o = a->o;
   at.part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + wl.part_off);
-  at.part_slots = wl.part_slots;
-  at.B = B;
-  at.H = Hq;
-  at.Sq = Sq;
-  at.Sk = Sk;
-  at.Sq_pad = (int32_t)wl.Sq_pad;
-  at.Sk_pad = (int32_t)wl.Sk_pad;
-  at.q_valid = q_valid;
-  at.kv_valid = kv_valid;
-  at.Hkv = Hkv;
-  at.causal = a->causal;
-  at.lengths = a->valid_lengths;
-  if (a->window_frame_rows > 0) {
-    // Clamp the geometry to the sequence without changing which keys a row
-    // sees: a frame longer than the sequence is one frame, and counts of
-    // anchor frames, chunk frames or radius chunks beyond the sequence's
-    // frames cover everything. With S < 2^28 the kernel's products
-    // (A + C*(c + R + 1)) * F then stay below 2^31.
-    const int32_t S = std::max(Sq, Sk);
-    const int32_t F = std::min(a->window_frame_rows, S);
-    const int32_t n_frames = (S + F - 1) / F;
-    at.win_F = F;
-    at.win_C = std::min(a->window_chunk_frames, n_frames);
-    at.win_R = std::min(a->window_radius, n_frames);
-    at.win_A = std::min(a->window_anchor_frames, n_frames);
-  }
-  at.gate = a->gate;
-  at.wq = a->q_norm_w;
-  at.wk = a->k_norm_w;
   at.c_log2 = c;
   at.knorm = a->k_norm_w == nullptr ? kn : nullptr;
-  at.kn_chunks = (int32_t)wl.kn_chunks;
   return status_from(h3::launch_attention(at, s));
 }
 
@@ -501,6 +516,32 @@ H3_API size_t h3attn_forward_ex_workspace_bytes(const h3attn_forward_args* args)
 H3_API int h3attn_forward_ex(const h3attn_forward_args* args, void* workspace, size_t workspace_bytes,
                              uint32_t stages, void* stream) {
   return run_forward(args, workspace, workspace_bytes, stages, stream);
+}
+
+H3_API int h3attn_forward_ex_plan(const h3attn_forward_args* args, int32_t cus, h3attn_plan* plan) {
+  if (!plan) return H3ATTN_ERR_NULL_POINTER;
+  int64_t qs[3], ks[3], vs[3];
+  WorkspaceLayout wl;
+  if (int st = check_forward(args, 0, nullptr, H3ATTN_STAGE_PREPARE | H3ATTN_STAGE_ATTEND, qs, ks, vs, &wl, false))
+    return st;
+  if (cus <= 0) {
+    if (int st = check_device()) return st;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return H3ATTN_ERR_HIP;
+  }
+  const h3::AttnPlan p = h3::plan_attention(attn_args(args, wl), cus);
+  plan->kernel = p.resident;
+  plan->query_tiles = p.query_tiles;
+  plan->rows_per_tile = p.rows;
+  plan->reserved = 0;
+  plan->tiles = p.tiles;
+  plan->whole_tiles = p.n_whole;
+  plan->split_tiles = p.n_split;
+  plan->split_blocks = p.n_blocks;
+  plan->grid = p.grid;
+  return H3ATTN_OK;
 }
 
 H3_API int h3attn_rmsnorm_scale_shift(const uint16_t* x, uint16_t* y, int32_t B, int32_t S, int32_t D,

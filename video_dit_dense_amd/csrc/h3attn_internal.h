@@ -160,6 +160,9 @@ struct AttnArgs {
   // which the kernel bounds each row's scores by |q_i| max_j |k_j|.
   const float* knorm;
   int32_t kn_chunks;
+  // Query tiles per wave (2 or 3 at head dim 128, the only count elsewhere),
+  // or 0: the launcher chooses (choose_query_tiles in attn_sched.h).
+  int32_t query_tiles;
   // Schedule, filled in by launch_attention. Uniform mode (no causal mask,
   // no per-item lengths): valid tiles (query block below q_valid) are
   // numbered g = (b*H + h) * nqv + query block; tiles g < n_whole run whole,
@@ -173,6 +176,18 @@ struct AttnArgs {
   // (set by the launcher when that shortens the schedule), else 0.
   int32_t win_longest_first;
 };
+
+// The schedule of one attention launch on a device with `cus` compute units
+// (host arithmetic only): which kernel, its query tiles per wave and rows
+// per tile, the valid query blocks per (b, h), the tiles with work, the
+// uniform schedule's whole tiles, split tiles and split blocks, and the grid.
+struct AttnPlan {
+  int32_t resident;      // 1: keys resident in LDS (attn_resident_kernel)
+  int32_t query_tiles;
+  int32_t rows;
+  int64_t nqv, tiles, n_whole, n_split, n_blocks, grid;
+};
+AttnPlan plan_attention(const AttnArgs& a, int cus);
 
 // Enqueues the attention kernel (and, when the schedule splits tiles, the
 // merge of their partial records) on `stream`.

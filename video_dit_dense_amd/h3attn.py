@@ -63,11 +63,21 @@ class ForwardArgs(ctypes.Structure):
         ("q_valid", _I), ("kv_valid", _I), ("valid_lengths", _P), ("causal", _I),
         ("softmax_scale", _F),
         ("window_frame_rows", _I), ("window_chunk_frames", _I), ("window_radius", _I),
-        ("window_anchor_frames", _I), ("gate", _P),
+        ("window_anchor_frames", _I), ("gate", _P), ("query_tiles", _I),
+    ]
+
+
+class Plan(ctypes.Structure):
+    """Mirror of h3attn_plan (include/h3attn.h)."""
+    _fields_ = [
+        ("kernel", _I), ("query_tiles", _I), ("rows_per_tile", _I), ("reserved", _I),
+        ("tiles", ctypes.c_int64), ("whole_tiles", ctypes.c_int64), ("split_tiles", ctypes.c_int64),
+        ("split_blocks", ctypes.c_int64), ("grid", ctypes.c_int64),
     ]
 
 
 SIGNATURES["h3attn_forward_ex_workspace_bytes"] = (ctypes.c_size_t, [ctypes.POINTER(ForwardArgs)])
+SIGNATURES["h3attn_forward_ex_plan"] = (ctypes.c_int, [ctypes.POINTER(ForwardArgs), _I, ctypes.POINTER(Plan)])
 SIGNATURES["h3attn_forward_ex"] = (ctypes.c_int, [ctypes.POINTER(ForwardArgs), _P, ctypes.c_size_t,
                                                   ctypes.c_uint32, _P])
 SIGNATURES["h3attn_rmsnorm_scale_shift"] = (ctypes.c_int, [_P, _P, _I, _I, _I, _P, _F, _P, _P, _I, _P, _P])
@@ -234,7 +244,7 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
             stages: int = STAGE_PREPARE | STAGE_ATTEND, causal: bool = False,
             valid_lengths: torch.Tensor | None = None, window: tuple | None = None,
-            gate: torch.Tensor | None = None) -> torch.Tensor:
+            gate: torch.Tensor | None = None, query_tiles: int = 0) -> torch.Tensor:
     """The attention step: prologue on q/k (if weights/tables given), then
     softmax attention with key padding (kv_valid) and a zeroed query tail
     (q_valid). Returns o [B, Sq, Hq, D] bf16. D is 128 (H3), 64 or 256; the
@@ -249,10 +259,69 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     prepare call with the same arguments. `window` = (frame_rows,
     chunk_frames, radius, anchor_frames) restricts each row to its frame
     window (anchor-frame rows see every key); `gate`, a bf16 GPU tensor
-    [B, Sq, Hq], multiplies each output row by sigmoid(gate). Dense inputs
-    without the variants go through h3attn_forward_stages, everything else
-    through h3attn_forward_ex."""
+    [B, Sq, Hq], multiplies each output row by sigmoid(gate). `query_tiles`
+    (0: the library chooses) sets the attention kernel's 16-row query tiles
+    per wave, 2 or 3 at head dim 128. Dense inputs without the variants go
+    through h3attn_forward_stages, everything else through h3attn_forward_ex."""
     lib = load_library()
+    a, o, plain = _forward_args(q, k, v, w_q, w_k, eps, rope_cos, rope_sin, q_valid, kv_valid, scale, out,
+                                causal, valid_lengths, window, gate, query_tiles)
+    if stages != (STAGE_PREPARE | STAGE_ATTEND) and workspace is None:
+        raise ValueError("a single stage needs a caller-kept workspace")
+    if plain:
+        B, Sq, H, D = q.shape
+        ws = make_workspace(B, Sq, k.shape[1], H, q.device) if workspace is None else workspace
+        st = lib.h3attn_forward_stages(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, Sq, k.shape[1], H, D,
+                                       _ptr(w_q), _ptr(w_k), float(eps), _ptr(rope_cos), _ptr(rope_sin),
+                                       a.rope_rows, a.q_valid, a.kv_valid, a.softmax_scale, _ptr(ws),
+                                       ws.numel() * ws.element_size(), int(stages), _stream(q.device))
+        _check(st, "h3attn_forward_stages")
+        return o
+    if workspace is None:
+        n = int(lib.h3attn_forward_ex_workspace_bytes(ctypes.byref(a)))
+        if n == 0:
+            raise ValueError("bad sizes for the workspace")
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
+    st = lib.h3attn_forward_ex(ctypes.byref(a), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                               int(stages), _stream(q.device))
+    _check(st, "h3attn_forward_ex")
+    return o
+
+
+def schedule(B: int, Sq: int, Sk: int, Hq: int, Hkv: int | None = None, head_dim: int = HEAD_DIM,
+             q_valid: int = -1, kv_valid: int = -1, causal: bool = False, per_item_lengths: bool = False,
+             window: tuple | None = None, query_tiles: int = 0, cus: int = 0) -> dict:
+    """The schedule forward() launches for these sizes and variant on a
+    device with `cus` compute units (0: the current device), from
+    h3attn_forward_ex_plan: the kernel ("ring" or "resident"), query tiles
+    per wave, rows per tile, the tiles with work, the uniform schedule's
+    whole tiles, split tiles and split blocks, and the grid. Host arithmetic
+    only; the descriptor's buffers are placeholders that are never touched."""
+    a = ForwardArgs()
+    a.q, a.k, a.v, a.o = 1 << 44, 2 << 44, 3 << 44, 4 << 44
+    a.B, a.Sq, a.Sk, a.Hq, a.Hkv, a.head_dim = B, Sq, Sk, Hq, Hkv or Hq, head_dim
+    a.eps, a.softmax_scale = 1e-6, 1.0 / math.sqrt(head_dim)
+    a.q_valid, a.kv_valid = q_valid, kv_valid
+    a.valid_lengths = (5 << 44) if per_item_lengths else None
+    a.causal = 1 if causal else 0
+    if window:
+        a.window_frame_rows, a.window_chunk_frames, a.window_radius, a.window_anchor_frames = (
+            int(x) for x in window)
+    a.query_tiles = int(query_tiles)
+    p = Plan()
+    _check(load_library().h3attn_forward_ex_plan(ctypes.byref(a), int(cus), ctypes.byref(p)),
+           "h3attn_forward_ex_plan")
+    return {"kernel": "resident" if p.kernel else "ring", "query_tiles": p.query_tiles,
+            "rows_per_tile": p.rows_per_tile, "tiles": p.tiles, "whole_tiles": p.whole_tiles,
+            "split_tiles": p.split_tiles, "split_blocks": p.split_blocks, "grid": p.grid}
+
+
+def _forward_args(q, k, v, w_q=None, w_k=None, eps=1e-6, rope_cos=None, rope_sin=None, q_valid=None,
+                  kv_valid=None, scale=None, out=None, causal=False, valid_lengths=None, window=None,
+                  gate=None, query_tiles=0):
+    """Checks forward()'s arguments and fills h3attn_forward_args. Returns the
+    descriptor, the output tensor (allocated when out is None) and whether the
+    call is the plain dense one that h3attn_forward_stages takes."""
     for name, t in (("q", q), ("k", k), ("v", v)):
         _check_bshd(name, t, view=True, dims=HEAD_DIMS)
     if q.shape[-1] != HEAD_DIM and any(x is not None for x in (w_q, w_k, rope_cos, rope_sin)):
@@ -279,20 +348,9 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     _check_bshd("out", o, dims=(D,))
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     rows = 0 if rope_cos is None else rope_cos.shape[0]
-    if stages != (STAGE_PREPARE | STAGE_ATTEND) and workspace is None:
-        raise ValueError("a single stage needs a caller-kept workspace")
     plain = (D == HEAD_DIM and Hkv == H and not causal and valid_lengths is None and window is None
-             and gate is None and q.is_contiguous() and k.is_contiguous() and v.is_contiguous())
-    if plain:
-        ws = make_workspace(B, Sq, Sk, H, q.device) if workspace is None else workspace
-        st = lib.h3attn_forward_stages(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, Sq, Sk, H, D,
-                                       _ptr(w_q), _ptr(w_k), float(eps), _ptr(rope_cos), _ptr(rope_sin), rows,
-                                       -1 if q_valid is None else int(q_valid),
-                                       -1 if kv_valid is None else int(kv_valid),
-                                       scale, _ptr(ws), ws.numel() * ws.element_size(), int(stages),
-                                       _stream(q.device))
-        _check(st, "h3attn_forward_stages")
-        return o
+             and gate is None and not query_tiles and q.is_contiguous() and k.is_contiguous()
+             and v.is_contiguous())
     a = ForwardArgs()
     a.q, a.k, a.v, a.o = q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr()
     for field, t in (("q_stride", q), ("k_stride", k), ("v_stride", v)):
@@ -313,15 +371,8 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         a.window_frame_rows, a.window_chunk_frames, a.window_radius, a.window_anchor_frames = (
             int(x) for x in window)
     a.gate = None if gate is None else gate.data_ptr()
-    if workspace is None:
-        n = int(lib.h3attn_forward_ex_workspace_bytes(ctypes.byref(a)))
-        if n == 0:
-            raise ValueError("bad sizes for the workspace")
-        workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
-    st = lib.h3attn_forward_ex(ctypes.byref(a), _ptr(workspace), workspace.numel() * workspace.element_size(),
-                               int(stages), _stream(q.device))
-    _check(st, "h3attn_forward_ex")
-    return o
+    a.query_tiles = int(query_tiles)
+    return a, o, plain
 
 
 def forward_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,

@@ -203,9 +203,9 @@ int h3attn_forward(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint
  * workspace and workspace_bytes. Sizes whose workspace
  * (h3attn_forward_workspace_bytes) exceeds H3ATTN_NOALLOC_SCRATCH_BYTES are
  * rejected with H3ATTN_ERR_WORKSPACE before anything is enqueued: the tiny,
- * mid (8192 x 8 heads, 122 MB) and cross-attention (32760 x 8 heads against
- * 512 keys, 141 MB) shapes fit; padded (32768 x 8, 273 MB) and the full
- * 104448 x 6 share (550 MB) do not.
+ * mid (8192 x 8 heads, 158 MB) and cross-attention (32760 x 8 heads against
+ * 512 keys, 177 MB) shapes fit; padded (32768 x 8, 309 MB) and the full
+ * 104448 x 6 share (588 MB) do not.
  *
  * Every call on one GPU uses that GPU's one array, which keeps the last
  * call's contents; nothing in it needs to start at zero (every call writes

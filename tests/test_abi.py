@@ -379,8 +379,8 @@ def test_noalloc_validation(lib):
     assert noalloc(lib, scale=-1.0) == VALUE
     assert noalloc(lib, o=4 * A + 8) == ALIGN
     assert noalloc(lib, o=2 * A) == ALIAS
-    # Sizes whose workspace exceeds the static array: padded (273 MB) and the
-    # full 104448 x 6 share (550 MB) are rejected before anything else runs.
+    # Sizes whose workspace exceeds the static array: padded (309 MB) and the
+    # full 104448 x 6 share (588 MB) are rejected before anything else runs.
     big = dict(q=G, k=2 * G, v=3 * G, o=4 * G, wq=5 * G, wk=5 * G + 512, rc=6 * G, rs=7 * G)
     assert lib.h3attn_forward_workspace_bytes(1, 32768, 32768, 8) > h3attn.NOALLOC_SCRATCH_BYTES
     assert noalloc(lib, B=1, Sq=32768, Sk=32768, H=8, rows=32768, **big) == WS

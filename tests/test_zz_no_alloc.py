@@ -25,10 +25,10 @@ def h3():
     return h3attn
 
 
-# (B, Sq, Sk, H, q_valid, kv_valid, rope): the mid configuration (122 MB of
+# (B, Sq, Sk, H, q_valid, kv_valid, rope): the mid configuration (158 MB of
 # workspace, whole rounds of tiles), then a smaller ragged shape whose last
 # round is split (partial records in the array) and whose valid lengths cut
-# both ends; then cross-attention (141 MB) and a tiny one.
+# both ends; then cross-attention (177 MB) and a tiny one.
 PAIRS = [
     ((1, 8192, 8192, 8, 8192, 8192, True), (2, 3000, 2500, 3, 2900, 2333, True)),
     ((1, 32760, 512, 8, 32760, 300, False), (1, 700, 300, 2, 650, 1, True)),

@@ -214,9 +214,14 @@ def step_flops(wl) -> float:
 
 
 def cpu_baseline(wl, inp, target_s: float):
-    """Time the fp64 oracle (as it stands) on one head and a seeded sample of
-    query rows against all keys; scale the row count so the run takes about
-    `target_s` seconds. Reports attention TFLOP/s of that sample."""
+    """Time the fp64 oracle (as it stands) on a bounded sample of the
+    workload that takes about `target_s` seconds, and report attention
+    TFLOP/s of that sample. The unit of work is one (item, query head): its
+    valid query rows against its visible keys, prologue included. When one
+    unit takes longer than target_s, the sample is a seeded subset of item
+    0, head 0's query rows, sized from two probes; otherwise whole units in
+    order (items, then heads), cycling over the workload again if it is
+    done first, until target_s has passed."""
     import numpy as np
     import oracle
     import workloads
@@ -226,34 +231,59 @@ def cpu_baseline(wl, inp, target_s: float):
         threads = max([d.get("num_threads", 1) for d in info if d.get("user_api") == "blas"] or [1])
     except Exception:  # noqa: BLE001
         threads = None
-    # Item 0, query head 0 and the key/value head it reads (head 0).
-    q1, k1, v1 = inp.q[:1, :, :1].copy(), inp.k[:1, :, :1].copy(), inp.v[:1, :, :1].copy()
-    gate1 = workloads.make_gate(wl.B, wl.Sq, wl.H, seed=wl.seed)[:1, :, :1].copy() if wl.gate else None
     theta = wl.theta if wl.rope else None
-    qv0, kvv0 = wl.item_lengths()[0]
+    lengths = wl.item_lengths()
+    gate_all = workloads.make_gate(wl.B, wl.Sq, wl.H, seed=wl.seed) if wl.gate else None
+    group = wl.H // wl.kv_heads
 
-    def run(n_rows):
-        rows = np.sort(np.random.default_rng(99).choice(qv0, size=n_rows, replace=False))
+    def run(b, h, rows):
+        """Oracle on query head h of item b for `rows`: (seconds, flops)."""
+        kvh = h // group
+        q1 = inp.q[b:b + 1, :, h:h + 1].copy()
+        k1, v1 = inp.k[b:b + 1, :, kvh:kvh + 1].copy(), inp.v[b:b + 1, :, kvh:kvh + 1].copy()
+        gate1 = gate_all[b:b + 1, :, h:h + 1].copy() if gate_all is not None else None
+        qv, kvv = lengths[b]
         t0 = time.perf_counter()
-        oracle.forward(q1, k1, v1, inp.w_q, inp.w_k, wl.eps, theta, wl.scale, qv0, kvv0,
+        oracle.forward(q1, k1, v1, inp.w_q, inp.w_k, wl.eps, theta, wl.scale, qv, kvv,
                        norm=wl.norm, rows=rows, causal=wl.causal, window=wl.window or None,
                        gate_bits=gate1)
-        return time.perf_counter() - t0, rows
+        t = time.perf_counter() - t0
+        if wl.window:
+            keys = window_keys_per_row(wl, rows)
+        else:
+            keys = np.minimum(rows + 1, kvv) if wl.causal else np.full(len(rows), kvv)
+        return t, 4.0 * float(np.minimum(keys, kvv).sum()) * wl.head_dim
+
+    qv0 = lengths[0][0]
+
+    def sample(n):
+        return np.sort(np.random.default_rng(99).choice(qv0, size=n, replace=False))
 
     # Fixed cost (prologue over all rows of the head) plus a per-row cost:
-    # fit t(n) = t0 + t1*n from two probes, then size the timed run.
-    n1, n2 = 128, 512
-    ta, _ = run(n1)
-    tb, _ = run(n2)
-    per_row = max((tb - ta) / (n2 - n1), 1e-6)
+    # fit t(n) = t0 + t1*n from two probes.
+    n1, n2 = min(128, qv0), min(512, qv0)
+    ta, _ = run(0, 0, sample(n1))
+    tb, _ = run(0, 0, sample(n2))
+    per_row = max((tb - ta) / max(n2 - n1, 1), 1e-7)
     fixed = max(ta - per_row * n1, 0.0)
     n = int(min(qv0, max(n2, (target_s - fixed) / per_row)))
-    t, rows = run(n)
-    if wl.window:
-        keys = window_keys_per_row(wl, rows)
+    if n < qv0:
+        t, flops = run(0, 0, sample(n))
+        what = f"item 0, head 0 of {wl.H}, {n} of {qv0} query rows"
+        units = 1
     else:
-        keys = np.minimum(rows + 1, kvv0) if wl.causal else np.full(len(rows), kvv0)
-    flops = 4.0 * float(keys.sum()) * wl.head_dim
+        units = []
+        order = [(b, h) for b in range(wl.B) for h in range(wl.H) if lengths[b][0] > 0]
+        t = flops = 0.0
+        while t < target_s and len(units) < 100000:
+            b, h = order[len(units) % len(order)]
+            dt, df = run(b, h, np.arange(lengths[b][0]))
+            t, flops = t + dt, flops + df
+            units.append((b, h))
+        per = len(order)
+        what = (f"{len(units)} whole (item, head) units of the {per} with valid rows"
+                + (f" ({len(units) / per:.1f} passes over the workload)" if len(units) > per else ""))
+        units = len(units)
     return {
         "value": flops / t / 1e12,
         "unit": "TFLOP/s",
@@ -261,11 +291,11 @@ def cpu_baseline(wl, inp, target_s: float):
         "cores_meaning": "BLAS threads of the one oracle process (its matrix products); the rest runs on one",
         **host_info(),
         "kind": "oracle",
-        "sample": f"fp64 NumPy oracle, item 0, head 0 of {wl.H}, {n} of {qv0} query rows against "
-                  f"{'their causal prefix of ' if wl.causal else 'their frame window of ' if wl.window else 'all '}"
-                  f"{kvv0} keys, prologue included, "
-                  f"{t:.1f} s wall",
+        "sample": f"fp64 NumPy oracle, {what}, each against "
+                  f"{'its causal prefix of the' if wl.causal else 'its frame window of the' if wl.window else 'all'}"
+                  f" valid keys, prologue included, {t:.1f} s wall",
         "seconds": t,
+        "units": units,
     }
 
 

@@ -136,16 +136,16 @@ def test_head_dim_256_key_lengths(h3, Sk):
     check(oracle.compare(got, ref(inp, 256)), f"D=256 Sk={Sk} per-item lengths")
 
 
-@pytest.mark.parametrize("D", [64, 128, 256])
-def test_rising_row_maxima(h3, D):
+@pytest.mark.parametrize("D,qt", [(64, 0), (128, 0), (128, 3), (256, 0)])
+def test_rising_row_maxima(h3, D, qt):
     """Keys whose magnitude grows along the sequence, so each row's running
     maximum rises by many units at several steps and the accumulator is
     rescaled there. q has entries in {-1, 0, 1} and key j entries in
     {-c, 0, c} with c = 1 + j // 256, and the scale is ln 2: q * scale *
     log2(e) stays an exact small integer in bf16, so the scores (exp2 units)
     are exact integers however large, and only v and the output are
-    rounded."""
-    say("rising row maxima", D)
+    rounded. At head dim 128 also with three query tiles per wave forced."""
+    say("rising row maxima", D, qt)
     Sq, Sk, H = 512, 2048, 2
     rng = np.random.default_rng(330 + D)
     qv = rng.integers(-1, 2, size=(1, Sq, H, D)).astype(np.float32)
@@ -156,7 +156,7 @@ def test_rising_row_maxima(h3, D):
     q, k = bits(qv), bits(kv)
     scale = math.log(2.0)
     d = DevInputs(workloads.Inputs(q, k, inp.v, inp.w_q, inp.w_k))
-    o = h3.forward(d.q, d.k, d.v, scale=scale)
+    o = h3.forward(d.q, d.k, d.v, scale=scale, query_tiles=qt)
     torch.cuda.synchronize()
     want = oracle.forward(q, k, inp.v, None, None, 1e-6, None, scale, norm=False)
-    check(oracle.compare(to_host(o), want), f"D={D} rising maxima")
+    check(oracle.compare(to_host(o), want), f"D={D} rising maxima, query tiles {qt or 'auto'}")

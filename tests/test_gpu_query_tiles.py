@@ -18,7 +18,7 @@ import torch
 
 import oracle
 import workloads
-from gpu_util import DevInputs, check_metrics, say, to_host
+from gpu_util import DevInputs, check_metrics, say, to_dev, to_host
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -108,3 +108,41 @@ def test_automatic_choice_is_one_of_the_tilings(h3):
     qt = plan(h3, inp, 0, causal=True)["query_tiles"]
     assert qt in (2, 3)
     assert np.array_equal(run(h3, d, 0, causal=True), run(h3, d, qt, causal=True))
+
+
+# (B, Sq, Sk, H, kwargs): the ring kernel's online path (norm weights whose
+# score bound is over the limit) in the uniform schedule with a split last
+# round, with ragged valid lengths, under the causal mask, and in the frame
+# window with the gate.
+ONLINE = [
+    (1, 3000, 3000, 3, {}),
+    (2, 1000, 777, 2, {"q_valid": 900, "kv_valid": 700}),
+    (1, 1500, 1500, 2, {"causal": True}),
+    (1, 2000, 2000, 2, {"window": (100, 3, 1, 2), "gate": True}),
+]
+
+
+@pytest.mark.parametrize("qt", [2, 3])
+@pytest.mark.parametrize("B,Sq,Sk,H,kw", ONLINE)
+def test_online_path_at_both_counts(h3, B, Sq, Sk, H, kw, qt):
+    """Weights large enough that the a priori bound exceeds its limit (one
+    channel's weight 4, zeroed in the data so the scores stay moderate): the
+    running maximum and the rescale run, at either tiling."""
+    kw = dict(kw)
+    base = workloads.make_inputs(B, Sq, Sk, H, seed=980 + Sq)
+    w_q, w_k = base.w_q.copy(), base.w_k.copy()
+    w_q[3] = w_k[100] = 4.0
+    q, k = base.q.copy(), base.k.copy()
+    q[..., 3] = 0
+    k[..., 100] = 0
+    inp = workloads.Inputs(q, k, base.v, w_q, w_k)
+    gate_bits = workloads.make_gate(B, Sq, H, seed=Sq) if kw.pop("gate", False) else None
+    say("online path", qt, B, Sq, Sk, H, kw)
+    d = DevInputs(inp)
+    cos, sin = h3.rope_tables(max(Sq, Sk))
+    gate = None if gate_bits is None else to_dev(gate_bits)
+    o = h3.forward(d.q, d.k, d.v, d.w_q, d.w_k, 1e-6, cos, sin, scale=SCALE, gate=gate, query_tiles=qt, **kw)
+    torch.cuda.synchronize()
+    want = oracle.forward(inp.q, inp.k, inp.v, w_q, w_k, 1e-6, 1e4, SCALE, kw.get("q_valid"), kw.get("kv_valid"),
+                          causal=kw.get("causal", False), window=kw.get("window"), gate_bits=gate_bits)
+    check_metrics(oracle.compare(to_host(o), want), f"online path, {qt} query tiles, {B}x{Sq}x{Sk}x{H} {kw}")

@@ -3,11 +3,10 @@
 // Computes, per (b, h) and query row i < q_valid,
 //   o_i = sum_{j visible to i} softmax_j(scale * q_i . k_j) v_j
 // flash-style: key/value blocks stream through LDS, scores never reach HBM,
-// and a running max / running sum per query row rescales the accumulator
-// (online softmax). QK^T and PV are bf16 matrix-core contractions
-// accumulated in fp32 (v_mfma_f32_16x16x32_bf16 at head dim 128, whose
-// layout is described where it is built; v_mfma_f32_32x32x16_bf16 at 64 and
-// 256, described below); the softmax is fp32.
+// and each row's softmax offset is either an a priori bound of its scores or
+// a running maximum that rescales the accumulator (online softmax). QK^T and
+// PV are bf16 matrix-core contractions (v_mfma_f32_16x16x32_bf16, wave64)
+// accumulated in fp32; the softmax is fp32.
 // The main step is the dense attention of FastVideo PR #1832 ("Summary":
 // BSHD, head_dim 128, dense non-causal) with the valid-front / zero-tail
 // layout of TeleFuser PR #37 (sections 2.3 and 2.4): key j is visible to
@@ -16,51 +15,46 @@
 // #1799, "Implementation"), and a frame window with anchor frames (SGLang PR
 // #37903, "Modifications", hybrid_window_attn_h3), whose optional softmax
 // gate multiplies each output row by sigmoid(g). Head dims 64, 128 and 256
-// share the code through the Geo<D> tiling constants.
+// share the code through the Geo<D, QT> tiling constants.
 //
-// Orientation (32x32x16 paths). Each wave owns 32 query rows and computes S^T = K Q^T, so the
-// matrix-core result puts one query per lane column: lane l holds 16 of the
-// 32 keys of a 32x32 score block for query l%32, and lane l^32 holds the
-// other 16. P^T then feeds O^T = V^T P^T straight from registers: the keys a
-// lane holds are exactly the keys its B operand needs, provided V^T's key
-// order inside each 16-key group is permuted by sigma (swap bits 2 and 3 of
-// the key index). The v relayout kernel below writes V^T in that order.
+// Orientation. Each wave owns QT 16-row query tiles (four at head dim 64;
+// two or three at 128, chosen per launch; at 256 a pair of waves shares two)
+// and computes S^T = K Q^T: K comes from LDS as the A operand and Q stays in
+// registers as the B operand, so each lane holds 8 scores of each query
+// tile, and P^T feeds O^T = V^T P^T straight from registers. V^T's keys are
+// permuted inside each 32-key sub-tile (key_of_position) so that the keys a
+// lane holds are the ones its PV operand needs. The operand layouts are
+// described where the fragments are built.
 //
-// Matrix-core operand layouts used (32x32x16, wave64):
-//   A (32 x 16): lane l supplies row l%32, k = 8*(l/32) .. 8*(l/32)+7
-//   B (16 x 32): lane l supplies column l%32, k = 8*(l/32) .. +7
-//   D (32 x 32): lane l register r holds row 8*(r/4) + 4*(l/32) + r%4, col l%32
-//
-// Schedule (head dims 64 and 128; 256 runs its own software-pipelined step,
-// described where it is built). A workgroup is eight waves (256 query rows), one
-// workgroup per CU, so every SIMD runs two waves and each K/V byte brought
-// into LDS serves 256 queries. Keys are processed in 32-key sub-tiles u, and step u is split
-// by workgroup barriers into two phases:
-//   X: matrix-core work only: QK^T of sub-tile u+1 and PV of sub-tile u,
-//      all operands already in registers;
-//   Y: vector and LDS work: the row maxima of u+1, the exponentials and row
-//      sums that turn them into the PV operand, the LDS reads of the next
-//      X phase's fragments and one ring refill.
+// Schedule. A workgroup is eight waves, one workgroup per CU, so every SIMD
+// runs two waves. Keys are processed in 32-key sub-tiles u, and step u is
+// split by workgroup barriers into two phases:
+//   X: matrix-core work only: QK^T of sub-tile u+1 and PV of sub-tile u;
+//   Y: vector and LDS work: the exponentials and row sums that turn the
+//      scores of u+1 into the next PV operand (and, on the online path, the
+//      row maxima), the first fragment reads of the next X phase and the
+//      ring refills.
 // The two waves of a SIMD run the phases in opposition (the second passes
 // one extra barrier first), so while one feeds the matrix core the other does
 // the softmax: a ping-pong. Both run the same instructions in the same
 // order, so the result does not depend on which wave runs which phase.
-// Sub-tiles land in an eight-slot LDS ring (128 KB) through direct
-// buffer->LDS loads issued up to seven sub-tiles ahead; the loads use a
-// buffer resource held in scalar registers, so they cost no vector
-// instructions. The chip runs this kernel at its power limit, so every
-// vector instruction and LDS byte per step costs clock: the step keeps them
-// few.
+// Sub-tiles land in an LDS ring (eight slots at head dims 64 and 128, four
+// at 256) through direct buffer->LDS loads issued several sub-tiles ahead;
+// the loads use buffer resources in scalar registers, so they cost no
+// vector instructions. The chip runs this kernel at its power limit, so
+// every vector instruction and LDS byte per step costs clock: the step
+// keeps them few.
 //
 // Chip schedule. A workgroup owns one (b, h, query block) tile and one CU,
 // so tiles run in rounds of one per CU. In the uniform mode (no causal mask,
 // per-item lengths or window), when the last round is only partly full, its
 // tiles are not run whole: their 32-key steps are divided evenly over up to
 // one workgroup per CU, each workgroup writes an fp32 partial result
-// (un-normalised accumulator, running max, row sum) per tile it touches, and
+// (un-normalised accumulator, offset, row sum) per tile it touches, and
 // attn_merge_kernel combines them. Tiles wholly past q_valid only write
 // zeros. The general mode (the other variants) runs one workgroup per tile,
-// each finding its own key ranges.
+// each finding its own key ranges. Short key ranges at head dim 128 keep
+// their keys resident in LDS instead (attn_resident_kernel).
 //
 // Exponent arithmetic. q arrives pre-multiplied by softmax_scale*log2(e)
 // (applied in fp32 by the prologue before its single bf16 rounding), so
@@ -69,7 +63,7 @@
 // Workspace layouts read here (written by the prologue and the relayout):
 //   qw [B*H][Sq_pad][D]            rows >= q_valid zero
 //   kw [B*Hkv][Sk_pad][D]          rows >= kv_valid zero
-//   vt [B*Hkv][Sk_pad/32][D][32]   vt[.., x, d, p] = v[key 32x + sigma(p)][d], zero past kv_valid
+//   vt [B*Hkv][Sk_pad/32][D][32]   vt[.., x, d, p] = v[key 32x + key_of_position(p)][d], zero past kv_valid
 #include "h3attn_internal.h"
 
 #include <algorithm>
@@ -524,7 +518,11 @@ void attn_fwd_kernel(AttnArgs a) {
   // holds key 16 (j/4) + 4g + j%4), and is DW/16 channel tiles x QT query
   // tiles (each V^T fragment serves every query tile). Head dim 64 holds four
   // query tiles (64 rows) per wave, so that each fragment read and each
-  // step's softmax feed as many matrix-core cycles as at 128.
+  // step's softmax feed as many matrix-core cycles as at 128. Head dim 128
+  // holds two or three (the launcher picks per launch): three feed each
+  // fragment read and each direct load to a third more matrix-core
+  // instructions, in 384-row query blocks that fill the chip's rounds
+  // differently from 256-row ones.
   //
   // Head dim 256 (CS): the two waves of a pair hold the same 32 rows. Wave
   // `half` computes the full scores (all 256 channels) of key tile kt = half

@@ -20,11 +20,9 @@ FLAGS = [
     "-fno-honor-nans",
     # No packed fp32 VALU ops anywhere in device code.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # Matrix-core results in vector registers. Only the head-dim-256 attention
-    # kernel (one wave per SIMD) would otherwise get accumulation registers;
-    # there the softmax reads its scores without copies and the QK^T
-    # accumulator starts from the row offset in place. No other kernel's code
-    # changes.
+    # Matrix-core results in architectural vector registers, where the softmax
+    # reads its scores without copies and the QK^T accumulator starts from
+    # the row offset in place.
     "-mllvm", "-amdgpu-mfma-vgpr-form=true",
     "-Wno-unused-command-line-argument",
 ]

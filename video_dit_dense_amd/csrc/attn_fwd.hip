@@ -275,6 +275,35 @@ __device__ inline void store_row16(const AttnArgs& a, uint16_t* obase, int q, in
   }
 }
 
+// store_row16 through a buffer resource covering the batch item's output rows
+// [0, Sq): rows at or past Sq fall outside it and the hardware drops their
+// stores, so the stores need no branch. ob: byte offset of the head's
+// channel 0 in row 0; gmul: the row's gate factor sigmoid(g), or 1. Without
+// a branch around them the stores leave the compiler's count of outstanding
+// memory operations exact, so a later wait for loads issued before them does
+// not also wait for the stores.
+template <int D, int NT16>
+__device__ inline void store_row16_rsrc(const AttnArgs& a, __amdgpu_buffer_rsrc_t rsrc, uint32_t ob, int q, int g4,
+                                        const f32x4_t* acc, float inv, int q_valid) {
+  const uint32_t orow = ob + (uint32_t)q * (uint32_t)(a.H * D * 2);
+  const bool live = q < q_valid;
+#pragma unroll
+  for (int m = 0; m < NT16 / 2; ++m) {
+    uint32_t e0 = 0u, e1 = 0u, o0 = 0u, o1 = 0u;
+    if (live) {
+      e0 = pack_bf16x2(acc[2 * m][0] * inv, acc[2 * m][1] * inv);
+      e1 = pack_bf16x2(acc[2 * m][2] * inv, acc[2 * m][3] * inv);
+      o0 = pack_bf16x2(acc[2 * m + 1][0] * inv, acc[2 * m + 1][1] * inv);
+      o1 = pack_bf16x2(acc[2 * m + 1][2] * inv, acc[2 * m + 1][3] * inv);
+    }
+    const auto s0 = __builtin_amdgcn_permlane16_swap(e0, o0, false, false);
+    const auto s1 = __builtin_amdgcn_permlane16_swap(e1, o1, false, false);
+    const int ch = 16 * (2 * m + (g4 & 1)) + 8 * (g4 >> 1);
+    const u32x4_t val = {(uint32_t)s0[0], (uint32_t)s1[0], (uint32_t)s0[1], (uint32_t)s1[1]};
+    __builtin_amdgcn_raw_buffer_store_b128(val, rsrc, orow + ch * 2, 0, 0);
+  }
+}
+
 // Partial record of a split tile, per logical thread t (64 lwave + lane) of
 // the workgroup (fp32, thread-contiguous so every access is coalesced):
 // accumulator register r at [r * 512 + t] (kRecA of them), then the QT row
@@ -1282,7 +1311,10 @@ void attn_resident_kernel(AttnArgs a, int32_t G) {
   const int bh_kv = b * a.Hkv + h / (a.H / a.Hkv);
   const int kvv = a.kv_valid, NU = (kvv + kSub - 1) / kSub;
   const int nq = (a.Sq + BM - 1) / BM, nqv = (a.q_valid + BM - 1) / BM;
-  uint16_t* obase = a.o + ((int64_t)b * a.Sq * a.H + h) * D;
+  // The batch item's output rows; the host keeps Sq * H * D * 2 below 2^31.
+  const __amdgpu_buffer_rsrc_t orsrc =
+      __builtin_amdgcn_make_buffer_rsrc(a.o + (int64_t)b * a.Sq * a.H * D, 0, (int)((int64_t)a.Sq * a.H * D * 2),
+                                        kBufferRsrcWord3);
   const uint16_t* gate_row = a.gate ? a.gate + (int64_t)b * a.Sq * a.H + h : nullptr;
 
   // Resident keys: LDS byte P of sub-tile x (K at x kKB, V^T at kVBase + x
@@ -1369,7 +1401,8 @@ void attn_resident_kernel(AttnArgs a, int32_t G) {
       constexpr int CPR = D / 8;
       for (int idx = tid; idx < BM * CPR; idx += T) {
         const int q = t * BM + idx / CPR;
-        if (q < a.Sq) *reinterpret_cast<u32x4_t*>(obase + (int64_t)q * a.H * D + (idx % CPR) * 8) = u32x4_t{0u, 0u, 0u, 0u};
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{0u, 0u, 0u, 0u}, orsrc,
+                                               (uint32_t)(((q * a.H + h) * D + (idx % CPR) * 8) * 2), 0, 0);
       }
       continue;
     }
@@ -1378,7 +1411,19 @@ void attn_resident_kernel(AttnArgs a, int32_t G) {
     for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
       for (int cc = 0; cc < NC; ++cc) qf[qt][cc] = qn[qt][cc];
-    if (t + G < nqv) load_q(t + G);
+    // The next tile's Q (this tile's again when there is none, from L2): the
+    // load is issued on every path, so the wait for it at the next tile
+    // counts only this tile's stores after it.
+    load_q(t + G < nqv ? t + G : t);
+    // Gate values of this wave's two rows (rows past q_valid read the last
+    // valid row's and are written as zeros), loaded with the Q prefetch and
+    // first used at the stores.
+    uint32_t graw[2] = {0u, 0u};
+    if (gate_row) {
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+        graw[qt] = gate_row[(int64_t)min(t * BM + wave * 32 + qt * 16 + l16, a.q_valid - 1) * a.H];
+    }
 
     // QK^T of sub-tile x into s (initial value sinit); keys at or past kvv set to -inf.
     auto scores = [&](int x, const f32x4_t* sinit, f32x4_t (&s)[2][2]) __attribute__((always_inline)) {
@@ -1468,12 +1513,12 @@ void attn_resident_kernel(AttnArgs a, int32_t G) {
           s[qt][g & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[g], qf[qt][g >> 1], s[qt][g & 1], 0, 0, 0);
     };
     f32x4_t s[2][2];
+    bf16x8_t vf[NT16];
     read_k(0);
+#pragma unroll
+    for (int ct = 0; ct < NT16; ++ct) vf[ct] = vfrag(0, ct);
     qk(s);
     for (int x = 0; x < NU; ++x) {
-      bf16x8_t vf[NT16];
-#pragma unroll
-      for (int ct = 0; ct < NT16; ++ct) vf[ct] = vfrag(x, ct);
       if (x == NU - 1 && (kvv % kSub) != 0) {
         const int lim = kvv - x * kSub - g4 * 4;
 #pragma unroll
@@ -1506,12 +1551,19 @@ void attn_resident_kernel(AttnArgs a, int32_t G) {
           l_run[qt] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_run[qt], false);
         }
       __builtin_amdgcn_sched_barrier(0);
-      if (x + 1 < NU) qk(s);
+      if (x + 1 < NU) {
+#pragma unroll
+        for (int ct = 0; ct < NT16; ++ct) vf[ct] = vfrag(x + 1, ct);
+        qk(s);
+      }
     }
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
-      store_row16<D, NT16>(a, obase, t * BM + wave * 32 + qt * 16 + l16, g4, acc[qt], 1.0f / sum_row16(l_run[qt]), a.q_valid,
-                     gate_row);
+    for (int qt = 0; qt < 2; ++qt) {
+      float inv = 1.0f / sum_row16(l_run[qt]);
+      if (gate_row) inv *= 1.0f / (1.0f + __expf(-__uint_as_float(graw[qt] << 16)));
+      store_row16_rsrc<D, NT16>(a, orsrc, (uint32_t)(h * D * 2), t * BM + wave * 32 + qt * 16 + l16, g4, acc[qt], inv,
+                                a.q_valid);
+    }
   }
 }
 
@@ -1753,7 +1805,7 @@ AttnPlan plan_attention(const AttnArgs& a, int cus) {
   const bool general = a.causal || a.lengths != nullptr || a.win_F > 0;
   const int64_t NU = (a.kv_valid + kSub - 1) / kSub;
   const int64_t bh = (int64_t)a.B * a.H;
-  if (a.D == 128 && !general && NU <= kResMaxSub) {
+  if (a.D == 128 && !general && NU <= kResMaxSub && (int64_t)a.Sq * a.H * 128 * 2 < (1ll << 31)) {
     // Keys resident in LDS: one workgroup per (b, h) and residue class of its
     // query tiles, G classes per head so that the grid covers the CUs.
     const int64_t nq = (a.Sq + kResRows - 1) / kResRows;

@@ -1572,17 +1572,21 @@ void attn_resident_kernel(AttnArgs a, int32_t G) {
 // relative to their own offset m_i; with M = max m_i the tile's result is
 // sum 2^(m_i - M) O_i / sum 2^(m_i - M) l_i (scores are in exp2 units).
 template <int D, int QT_>
-__global__ __launch_bounds__((Geo<D, QT_>::NW * 64)) void attn_merge_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
+  // One workgroup per (split tile, logical wave): a single wave merges the
+  // rows (and at head dim 256 the channel half) that logical wave lw of the
+  // split blocks held, so the grid has NW workgroups per split tile.
   using G = Geo<D, QT_>;
   constexpr int BM = G::BM;
   constexpr int T = G::NW * 64;
   constexpr int QT = G::QT;
   constexpr int NT16 = G::DW / 16;   // 16-channel output tiles per thread
-  const int tid = threadIdx.x;
-  const int lw = tid >> 6;           // logical wave: its rows (and channel half at 256)
+  constexpr int NR = G::kRecA + 2 * QT;   // floats per thread in a record
+  const int lane = threadIdx.x;
+  const int t = blockIdx.x / G::NW;
+  const int lw = blockIdx.x - t * G::NW;   // logical wave: its rows (and channel half at 256)
+  const int tid = lw * 64 + lane;          // its thread index within a record
   const int pair = G::kCS ? lw >> 1 : lw, half = G::kCS ? lw & 1 : 0;
-  const int lane = tid & 63;
-  const int t = blockIdx.x;
   const int NU = (a.kv_valid + kSub - 1) / kSub;
   const int tg = a.n_whole + t;
   const int bh = tg / a.nqv;
@@ -1599,7 +1603,9 @@ __global__ __launch_bounds__((Geo<D, QT_>::NW * 64)) void attn_merge_kernel(Attn
   };
   const uint16_t* gate_row = a.gate ? a.gate + (int64_t)b * a.Sq * a.H + h : nullptr;
   // Records in the 16x16 layout: QT query tiles x NT16 tiles x 4 registers,
-  // then the QT rows' offsets and the QT partial sums.
+  // then the QT rows' offsets and the QT partial sums. Each record is read
+  // whole into registers (all loads in flight together, coalesced across
+  // the wave), then folded into the running result.
   f32x4_t acc[QT][NT16];
   float M[QT], l[QT];
 #pragma unroll
@@ -1612,14 +1618,17 @@ __global__ __launch_bounds__((Geo<D, QT_>::NW * 64)) void attn_merge_kernel(Attn
   }
   for (int j = j0; j <= j1; ++j) {
     const float* pr = record(j);
+    float v[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) v[r] = __builtin_nontemporal_load(pr + r * T);
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
-      const float w = __builtin_amdgcn_exp2f(pr[(G::kRecA + qt) * T] - M[qt]);
-      l[qt] += w * pr[(G::kRecA + QT + qt) * T];
+      const float w = __builtin_amdgcn_exp2f(v[G::kRecA + qt] - M[qt]);
+      l[qt] += w * v[G::kRecA + QT + qt];
 #pragma unroll
       for (int ct = 0; ct < NT16; ++ct)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[qt][ct][r] += w * pr[((qt * NT16 + ct) * 4 + r) * T];
+        for (int r = 0; r < 4; ++r) acc[qt][ct][r] += w * v[(qt * NT16 + ct) * 4 + r];
     }
   }
   const int l16 = lane & 15, g4 = lane >> 4;
@@ -1777,7 +1786,7 @@ hipError_t launch_attention_q(AttnArgs a, const AttnPlan& p, hipStream_t stream)
   if (p.grid > 0) attn_fwd_kernel<D, QT, false><<<dim3((unsigned)p.grid), NW * 64, 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_split == 0) return e;
-  attn_merge_kernel<D, QT><<<dim3((unsigned)p.n_split), NW * 64, 0, stream>>>(a);
+  attn_merge_kernel<D, QT><<<dim3((unsigned)(p.n_split * NW)), 64, 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -137,6 +137,25 @@ def test_gate_in_uniform_schedule(h3):
                                                     gate_bits=g)), "gate on split tiles")
 
 
+def test_gate_on_resident_keys(h3):
+    """The gate on the resident-key kernel (300 valid text keys stay in LDS;
+    the gate values are read with each tile's query prefetch), two batch
+    items, a zero tail and a partial last query tile."""
+    say("gate, resident keys")
+    B, Sq, Sk, H = 2, 1000, 512, 3
+    inp = workloads.make_inputs(B, Sq, Sk, H, seed=86)
+    g = workloads.make_gate(B, Sq, H, seed=86)
+    assert h3.schedule(B, Sq, Sk, H, q_valid=900, kv_valid=300)["kernel"] == "resident"
+    d = DevInputs(inp)
+    o = h3.forward(d.q, d.k, d.v, d.w_q, d.w_k, 1e-6, None, None, q_valid=900, kv_valid=300, scale=SCALE,
+                   gate=to_dev(g))
+    torch.cuda.synchronize()
+    got = to_host(o)
+    check(oracle.compare(got, oracle.forward(inp.q, inp.k, inp.v, inp.w_q, inp.w_k, 1e-6, None, SCALE,
+                                             q_valid=900, kv_valid=300, gate_bits=g)), "gate on resident keys")
+    assert np.all(got[:, 900:] == 0), "rows past q_valid are +0.0"
+
+
 def test_window_repeatable(h3):
     inp = workloads.make_inputs(1, 2000, 2000, 2, seed=84)
     g = workloads.make_gate(1, 2000, 2, seed=84)

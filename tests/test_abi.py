@@ -435,6 +435,10 @@ def test_forward_ex_plan(lib):
     padded = sch(1, 32768, 32768, 8, q_valid=30720, kv_valid=30720, cus=256)
     assert (padded["query_tiles"], padded["tiles"], padded["grid"]) == (3, 640, 512 + 256 + 8 * 6)
     assert sch(1, 32760, 512, 8, kv_valid=300, cus=256)["kernel"] == "resident"
+    # the resident kernel stores through a 32-bit buffer range per item: an item's output of 2^31 bytes or
+    # more (here 1048576 rows x 8 heads x 256 B) takes the ring kernel instead
+    assert sch(2, 1048575, 512, 8, kv_valid=300, cus=256)["kernel"] == "resident"
+    assert sch(1, 1048576, 512, 8, kv_valid=300, cus=256)["kernel"] == "ring"
     causal = sch(1, 104448, 104448, 6, causal=True, cus=256)
     assert (causal["query_tiles"], causal["tiles"], causal["split_tiles"]) == (3, 1632, 0)
     assert sch(1, 104448, 104448, 12, head_dim=64, cus=256)["rows_per_tile"] == 512

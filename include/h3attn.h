@@ -284,8 +284,9 @@ int h3attn_forward_stages(const uint16_t* q, const uint16_t* k, const uint16_t* 
  *   query_tiles), 128 at 256. No causal mask, no valid_lengths and no
  *   window uses the schedule of h3attn_forward (whole rounds of query
  *   blocks, the last round's key steps split over all compute units; at
- *   head_dim 128 with at most 320 valid keys, the keys stay resident in LDS
- *   and each workgroup streams several 256-row blocks past them); otherwise
+ *   head_dim 128 with at most 320 valid keys and an item's output below
+ *   2^31 bytes, the keys stay resident in LDS and each workgroup streams
+ *   several 256-row blocks past them); otherwise
  *   one workgroup per (b, h, query block), the longest first under the
  *   causal mask and the frame window. h3attn_forward_ex_plan() reports the
  *   schedule a call takes.

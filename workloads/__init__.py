@@ -230,6 +230,28 @@ def make_inputs(B: int, Sq: int, Sk: int, H: int, seed: int,
     return Inputs(q, k, v, w[0], w[1])
 
 
+def normal_bf16_rows(B: int, S: int, H: int, seed: int, D: int = HEAD_DIM,
+                     chunk_rows: int = 1 << 16) -> np.ndarray:
+    """A [B, S, H, D] tensor ~ N(0,1) (float32, then RNE to bf16 bits) for
+    tensors of several GiB: each chunk of chunk_rows sequence rows of each
+    item is drawn from its own PCG64 stream, spawned in order from `seed`
+    (numpy's SeedSequence), on a thread pool. No float32 draw is held whole."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+
+    out = np.empty((B, S, H, D), dtype=np.uint16)
+    spans = [(b, s0, min(S, s0 + chunk_rows)) for b in range(B) for s0 in range(0, S, chunk_rows)]
+    seeds = np.random.SeedSequence(seed).spawn(len(spans))
+
+    def draw(i):
+        b, s0, s1 = spans[i]
+        out[b, s0:s1] = _normal_bf16(np.random.default_rng(seeds[i]), (s1 - s0, H, D))
+
+    with ThreadPoolExecutor(max(1, min(16, len(os.sched_getaffinity(0))))) as ex:
+        list(ex.map(draw, range(len(spans))))
+    return out
+
+
 def make_workload_inputs(wl: Workload, seed: int | None = None) -> Inputs:
     return make_inputs(wl.B, wl.Sq, wl.Sk, wl.H, wl.seed if seed is None else seed, Hkv=wl.kv_heads,
                        D=wl.head_dim)

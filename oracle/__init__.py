@@ -39,7 +39,10 @@ attention):
 Readings where the pages are silent (each pinned by a test in tests/):
 per-head norm with one [128] weight shared by all heads, eps inside the square
 root, weight multiplied as given; rotary frequency theta^(-2j/96) over the 96
-rotated channels; 1-D positions 0..S-1; no rounding between steps.
+rotated channels; 1-D positions 0..S-1; no rounding between steps. The same
+holds for the frame-window geometry and the pack's chunk layout below. These
+pins are worked by hand from the reading: the pages print no value for them,
+so agreement with H3's own implementation on these points is parity unpinned.
 
 The fused RMSNorm + indexed AdaLN scale/shift step has its own module,
 `oracle.scale_shift`, with bf16 rounding boundaries instead of fp64 results.

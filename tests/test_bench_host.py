@@ -85,6 +85,7 @@ def test_attend_kernel_names_follow_the_launcher():
     assert name(W["full_window"]) == "attn_fwd_kernel<128, 3, true> (general mode)"
     assert name(W["full_d64"]).startswith("attn_fwd_kernel<64, 4, false>")
     assert name(W["full_d256"]).startswith("attn_fwd_kernel<256, 2, false>")
+    assert name(W["full_window_d64"]) == "attn_fwd_kernel<64, 4, true> (general mode)"
     wl = workloads.Workload("w", 1, 4096, 321, 2, 4096, 321, True, False, 0)
     assert name(wl).startswith("attn_fwd_kernel<128")      # 11 sub-tiles: the ring kernel
     wl = workloads.Workload("w", 1, 4096, 320, 2, 4096, 320, True, False, 0)

@@ -3,8 +3,8 @@ size and in the launch configuration it times, against the fp64 oracle.
 
 Coverage:
 - padded and cross: every row of every head (the oracle takes seconds);
-- full, full_causal, full_gqa, full_window, full_d64, full_d256 and
-  batch_varlen: seeded rows in every (item, head, query block) tile of the
+- full, full_causal, full_gqa, full_window, full_d64, full_d256,
+  full_window_d64 and batch_varlen: seeded rows in every (item, head, query block) tile of the
   launch: one in every 128-row block, so at least one in every query block
   of whichever tiling the launch takes (128 to 512 rows), plus the
   first, last, last-valid and first-tail rows (and frame edges for the
@@ -95,7 +95,7 @@ def test_every_row(h3, name):
 
 @pytest.mark.parametrize("name,per_tile", [
     ("full", 1), ("full_causal", 1), ("full_gqa", 1), ("full_window", 1),
-    ("full_d64", 1), ("full_d256", 1), ("batch_varlen", 1),
+    ("full_d64", 1), ("full_d256", 1), ("full_window_d64", 1), ("batch_varlen", 1),
 ])
 def test_every_tile(h3, name, per_tile):
     wl = ALL[name]

@@ -132,6 +132,12 @@ VARIANT_WORKLOADS = {
                          description="full sequence at head dim 64, 12 heads, no prologue", head_dim=64),
     "full_d256": Workload("full_d256", 1, 104448, 104448, 3, 104448, 104448, False, False, 7,
                           description="full sequence at head dim 256, 3 heads, no prologue", head_dim=256),
+    # The frame window and gate at head dim 64 (12 heads, no prologue): the
+    # window kernel holds four query tiles' window bounds per wave there.
+    "full_window_d64": Workload("full_window_d64", 1, 104448, 104448, 12, 104448, 104448, False, False, 8,
+                                description="full sequence at head dim 64, 12 heads, no prologue, the "
+                                            "full_window frame window and gate",
+                                window=(3072, 5, 1, 1), gate=True, head_dim=64),
     "batch_varlen": Workload("batch_varlen", 4, 32768, 32768, 8, 32768, 32768, True, True, 5,
                              description="B=4 padded to 32768 rows, items valid for 32768, 24576, "
                                          "16384 and 8192 query rows and keys, H=8",
